@@ -1,0 +1,326 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+Every test here runs on the CPU. Each one is chosen so that a plausible slip in
+the oracle (a dropped window, a wrong tie rule, an off-by-one in the causal
+mask, a transposed operand) fails at least one of them.
+
+Source of the method: "Long-Context Fine-Tuning with Limited VRAM", section 2.1.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def tiny_cfg(**kw):
+    base = dict(L=256, n_q=256, hq=2, hkv=1, d=8, chunk=16, group=4, q_block=16,
+                top_chunks=3, top_groups=5, sink=16, local=16, dtype="f32", rope_theta=None,
+                shared_rank=0, shared_scale=0.0, n_plant_chunks=0, groups_per_plant_chunk=1,
+                plant_chunks=(1, 2), alpha=0.0, beta=0.0, tier_split=0, cfg_id=50)
+    base.update(kw)
+    return base
+
+
+def rand_qkv(cfg, seed=0):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((cfg["hq"], cfg["n_q"], cfg["d"]))
+    k = rng.standard_normal((cfg["hkv"], cfg["L"], cfg["d"]))
+    v = rng.standard_normal((cfg["hkv"], cfg["L"], cfg["d"]))
+    return q, k, v
+
+
+def dense_causal(cfg, q, k, v):
+    """Textbook dense causal attention (full score matrix, masked softmax)."""
+    G = cfg["hq"] // cfg["hkv"]
+    q0 = cfg["L"] - cfg["n_q"]
+    scale = cfg.get("softmax_scale") or 1.0 / math.sqrt(cfg["d"])
+    out = np.empty_like(q)
+    lse = np.empty(q.shape[:2])
+    pos_q = np.arange(q0, cfg["L"])[:, None]
+    pos_k = np.arange(cfg["L"])[None, :]
+    for hq in range(cfg["hq"]):
+        s = scale * (q[hq] @ k[hq // G].T)
+        s = np.where(pos_k <= pos_q, s, -np.inf)
+        m = s.max(axis=1, keepdims=True)
+        p = np.exp(s - m)
+        den = p.sum(axis=1, keepdims=True)
+        out[hq] = (p / den) @ v[hq // G]
+        lse[hq] = (m + np.log(den))[:, 0]
+    return out, lse
+
+
+def oracle_full(cfg, q, k, v):
+    """Run the oracle on every item; return out [Hq][n_q][d], lse, and the routing."""
+    res = oracle.run(cfg, q, k, v)
+    G, B = cfg["hq"] // cfg["hkv"], cfg["q_block"]
+    out = np.empty((cfg["hq"], cfg["n_q"], cfg["d"]))
+    lse = np.empty((cfg["hq"], cfg["n_q"]))
+    for n, (b, h) in enumerate(oracle.all_items(cfg)):
+        for r in range(G):
+            out[h * G + r, b * B:(b + 1) * B] = res["out"][n, r]
+            lse[h * G + r, b * B:(b + 1) * B] = res["lse"][n, r]
+    return out, lse, res
+
+
+# ------------------------------------------------------------------ step 1
+def test_summaries_closed_form_ramp():
+    """Keys K[h][t][e] = (h+1) t + e/2: group j's mean is (h+1)(g j + (g-1)/2) + e/2."""
+    cfg = tiny_cfg(hkv=2, hq=2, L=128, n_q=64)
+    L, d, g, c = cfg["L"], cfg["d"], cfg["group"], cfg["chunk"]
+    t = np.arange(L)[None, :, None]
+    h = np.arange(2)[:, None, None]
+    e = np.arange(d)[None, None, :]
+    k = (h + 1) * t + 0.5 * e + 0.0 * t
+    gs, cs = oracle.summaries(cfg, k)
+    j = np.arange(L // g)[None, :, None]
+    m = np.arange(L // c)[None, :, None]
+    np.testing.assert_array_equal(gs, (h + 1) * (g * j + (g - 1) / 2) + 0.5 * e)
+    np.testing.assert_array_equal(cs, (h + 1) * (c * m + (c - 1) / 2) + 0.5 * e)
+
+
+def test_summaries_constant_and_chunk_is_mean_of_groups():
+    cfg = tiny_cfg()
+    k = np.full((1, cfg["L"], cfg["d"]), 0.375)
+    gs, cs = oracle.summaries(cfg, k)
+    assert np.all(gs == 0.375) and np.all(cs == 0.375)
+    _, k, _ = rand_qkv(cfg, 3)
+    gs, cs = oracle.summaries(cfg, k)
+    per = cfg["chunk"] // cfg["group"]
+    np.testing.assert_allclose(cs, gs.reshape(1, -1, per, cfg["d"]).mean(axis=2), rtol=0, atol=1e-15)
+
+
+# ------------------------------------------------------------------ hand-worked example
+def test_hand_worked_example():
+    fx = json.load(open(os.path.join(GOLDEN, "hand_worked_L20.json")))
+    cfg = tiny_cfg(**fx["config"])
+    k = np.array(fx["k"], float)[None]
+    q = np.array(fx["q"], float)[None]
+    v = np.stack([np.arange(cfg["L"], dtype=float), np.ones(cfg["L"])], axis=1)[None]
+    ci, gi, ns, dg = oracle.route(cfg, q, k, [(0, 0)])
+    exp = fx["expected"]
+    assert ci[0].tolist() == exp["chunk_idx"]
+    assert gi[0].tolist() == exp["group_idx"]
+    assert ns[0].tolist() == exp["n_sel"]
+    assert oracle.token_set(cfg, 0, gi[0], ns[0, 1]).tolist() == exp["token_set"]
+    out, lse = oracle.attend(cfg, q, k, v, [(0, 0)], gi, ns[:, 1])
+    env = {"exp": math.exp, "log": math.log}
+    for pos, expr in exp["out_0_closed_form"].items():
+        i = int(pos) - 16
+        assert out[0, 0, i, 0] == pytest.approx(eval(expr, env), rel=1e-14)
+        assert out[0, 0, i, 1] == pytest.approx(1.0, rel=1e-14)
+    for pos, expr in exp["lse_closed_form"].items():
+        assert lse[0, 0, int(pos) - 16] == pytest.approx(eval(expr, env), rel=1e-14)
+
+
+# ------------------------------------------------------------------ steps 4, 5: selection
+def _designed_chunk_scores(cfg, weights):
+    """Queries all equal e_0, chunk m keys all equal weights[m] e_0: score_m = weights[m]."""
+    L, d, c = cfg["L"], cfg["d"], cfg["chunk"]
+    q = np.zeros((cfg["hq"], cfg["n_q"], d)); q[..., 0] = 1.0
+    k = np.zeros((1, L, d))
+    for m in range(L // c):
+        k[0, m * c:(m + 1) * c, 0] = weights[m]
+    return q, k
+
+
+def test_chunk_stage_closed_form_scores():
+    cfg = tiny_cfg(n_q=16, top_chunks=4, top_groups=0)
+    nc = cfg["L"] // cfg["chunk"]            # 16 chunks; the block is chunk 15
+    rng = np.random.default_rng(7)
+    w = rng.permutation(nc).astype(float)
+    q, k = _designed_chunk_scores(cfg, w)
+    ci, gi, ns, dg = oracle.route(cfg, q, k, [(0, 0)])
+    cand = [m for m in range(nc - 1) if m != 0 and m != nc - 2]   # sink 0, local 14
+    expect = sorted(sorted(cand, key=lambda m: -w[m])[:4])
+    assert ci[0].tolist() == expect
+    assert ns[0, 0] == 4 and dg[0, oracle.DG_NCAND_C] == len(cand)
+
+
+def test_exact_ties_go_to_lower_index():
+    cfg = tiny_cfg(n_q=16, top_chunks=3, top_groups=4)
+    q = np.ones((cfg["hq"], 16, cfg["d"]))
+    k = np.ones((1, cfg["L"], cfg["d"]))
+    ci, gi, ns, _ = oracle.route(cfg, q, k, [(0, 0)])
+    assert ci[0].tolist() == [1, 2, 3]          # chunk 0 is the sink
+    assert gi[0].tolist() == [4, 5, 6, 7]       # the first 4 groups of chunk 1
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_matches_exhaustive_subset_search(seed):
+    """For small candidate counts, enumerate every k-subset: the kept set is the
+    unique subset where each kept item beats each dropped one (higher score, or
+    an equal score and a lower index)."""
+    cfg = tiny_cfg(L=176, n_q=16, top_chunks=3, top_groups=4, d=4)
+    rng = np.random.default_rng(100 + seed)
+    q = rng.standard_normal((cfg["hq"], 16, cfg["d"]))
+    k = rng.integers(-2, 3, size=(1, cfg["L"], cfg["d"])).astype(float)   # frequent ties
+    ci, gi, ns, dg = oracle.route(cfg, q, k, [(0, 0)])
+    # decision score: float64 block-mean query against the float32-rounded summary
+    qbar = q[:, :16].reshape(-1, cfg["d"]).mean(axis=0)
+    gs, cs = oracle.summaries(cfg, k)
+
+    def score(vec):
+        return float(np.dot(qbar, vec.astype(np.float32).astype(np.float64)))
+
+    def beats(x, y, sc):
+        return sc[x] > sc[y] or (sc[x] == sc[y] and x < y)
+
+    def brute(cands, sc, kk):
+        kk = min(kk, len(cands))
+        good = [S for S in itertools.combinations(cands, kk)
+                if all(beats(x, y, sc) for x in S for y in cands if y not in S)]
+        assert len(good) == 1
+        return sorted(good[0])
+
+    nc = cfg["L"] // cfg["chunk"]
+    cands = [m for m in range(1, nc - 2)]
+    scc = {m: score(cs[0, m]) for m in cands}
+    selc = brute(cands, scc, 3)
+    assert ci[0].tolist() == selc
+    gcands = [m * 4 + u for m in selc for u in range(4)]
+    scg = {j: score(gs[0, j]) for j in gcands}
+    assert gi[0].tolist() == brute(gcands, scg, 4)
+
+
+def test_selection_is_permutation_equivariant():
+    """Swapping the contents of two candidate chunks swaps them in the selection."""
+    cfg = tiny_cfg(n_q=16, top_chunks=4, top_groups=6)
+    q, k, _ = rand_qkv(cfg, 11)
+    q += 0.5
+    k[0, 16 * 9:16 * 10] += 1.0
+    ci, gi, ns, _ = oracle.route(cfg, q, k, [(0, 0)])
+    a, b = 3, 9
+    k2 = k.copy()
+    k2[0, 16 * a:16 * (a + 1)], k2[0, 16 * b:16 * (b + 1)] = k[0, 16 * b:16 * (b + 1)], k[0, 16 * a:16 * (a + 1)]
+    ci2, gi2, _, _ = oracle.route(cfg, q, k2, [(0, 0)])
+    sw = {a: b, b: a}
+    assert sorted(sw.get(m, m) for m in ci[0]) == ci2[0].tolist()
+    gmap = lambda j: sw.get(j // 4, j // 4) * 4 + j % 4
+    assert sorted(gmap(j) for j in gi[0]) == gi2[0].tolist()
+
+
+# ------------------------------------------------------------------ step 7: attention
+@pytest.mark.parametrize("hq,hkv,ragged", [(1, 1, False), (4, 2, False), (6, 3, True)])
+def test_dense_equivalence_when_budget_covers_everything(hq, hkv, ragged):
+    """With kc >= every candidate and kg >= all their groups, routed attention is
+    dense causal attention (the token set is every earlier token)."""
+    L = 176 if ragged else 256
+    cfg = tiny_cfg(L=L, n_q=L - 32, hq=hq, hkv=hkv, top_chunks=L // 16, top_groups=L // 4)
+    q, k, v = rand_qkv(cfg, 5)
+    out, lse, res = oracle_full(cfg, q, k, v)
+    ref, rlse = dense_causal(cfg, q, k, v)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, rlse, rtol=0, atol=1e-12)
+
+
+def test_no_routing_budget_is_block_diagonal_attention():
+    cfg = tiny_cfg(sink=0, local=0, top_chunks=0, top_groups=0, hq=2, hkv=1)
+    q, k, v = rand_qkv(cfg, 6)
+    out, lse, _ = oracle_full(cfg, q, k, v)
+    B = cfg["q_block"]
+    for b in range(cfg["n_q"] // B):
+        sub = tiny_cfg(L=B, n_q=B, hq=2, hkv=1)
+        ref, rlse = dense_causal(sub, q[:, b * B:(b + 1) * B], k[:, b * B:(b + 1) * B], v[:, b * B:(b + 1) * B])
+        np.testing.assert_allclose(out[:, b * B:(b + 1) * B], ref, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[:, b * B:(b + 1) * B], rlse, rtol=0, atol=1e-12)
+
+
+def test_constant_values_and_uniform_weights():
+    """Constant V gives O = V; Q = 0 gives uniform weights, so O is the mean of V
+    over the visible kept tokens and LSE = log(count)."""
+    cfg = tiny_cfg()
+    q, k, v = rand_qkv(cfg, 8)
+    vc = np.full_like(v, -1.25)
+    out, _, _ = oracle_full(cfg, q, k, vc)
+    np.testing.assert_allclose(out, -1.25, rtol=0, atol=1e-13)
+    q0 = np.zeros_like(q)
+    out, lse, res = oracle_full(cfg, q0, k, v)
+    B = cfg["q_block"]
+    for n, (b, h) in enumerate(oracle.all_items(cfg)):
+        T = oracle.token_set(cfg, b, res["group_idx"][n], res["n_sel"][n, 1])
+        for i in (0, 5, B - 1):
+            pos = b * B + i
+            vis = T[T <= pos]
+            np.testing.assert_allclose(out[0, pos], v[0, vis].mean(axis=0), atol=1e-13)
+            assert lse[0, pos] == pytest.approx(math.log(len(vis)), abs=1e-13)
+
+
+def test_causality_future_keys_do_not_change_past_outputs():
+    cfg = tiny_cfg(top_chunks=2, top_groups=3)
+    q, k, v = rand_qkv(cfg, 9)
+    out, lse, _ = oracle_full(cfg, q, k, v)
+    rng = np.random.default_rng(1)
+    for p in (37, 100, 170, 250):
+        k2, v2 = k.copy(), v.copy()
+        k2[:, p + 1:] += rng.standard_normal(k2[:, p + 1:].shape) * 3
+        v2[:, p + 1:] -= 2.0
+        o2, l2, _ = oracle_full(cfg, q, k2, v2)
+        np.testing.assert_array_equal(o2[:, :p + 1], out[:, :p + 1])
+        np.testing.assert_array_equal(l2[:, :p + 1], lse[:, :p + 1])
+        assert not np.array_equal(o2[:, p + 1:], out[:, p + 1:])
+
+
+# ------------------------------------------------------------------ step 6 invariants
+@pytest.mark.parametrize("cfg_over", [dict(), dict(sink=32, local=48, top_chunks=4, top_groups=7),
+                                      dict(sink=0, local=16, top_chunks=1, top_groups=4, n_q=128)])
+def test_routing_and_token_set_invariants(cfg_over):
+    cfg = tiny_cfg(**cfg_over)
+    q, k, v = rand_qkv(cfg, 12)
+    items = oracle.all_items(cfg)
+    ci, gi, ns, dg = oracle.route(cfg, q, k, items)
+    c, g, B = cfg["chunk"], cfg["group"], cfg["q_block"]
+    q0 = cfg["L"] - cfg["n_q"]
+    for n, (b, h) in enumerate(items):
+        s = q0 + b * B
+        ms = s // c
+        fixed = {m for m in range(ms) if m < cfg["sink"] // c or m >= ms - cfg["local"] // c}
+        cand = [m for m in range(ms) if m not in fixed]
+        nsc, nsg = ns[n]
+        assert nsc == min(cfg["top_chunks"], len(cand))
+        assert nsg == min(cfg["top_groups"], nsc * (c // g))
+        selc = ci[n, :nsc].tolist()
+        assert all(x == -1 for x in ci[n, nsc:]) and all(x == -1 for x in gi[n, nsg:])
+        assert selc == sorted(set(selc)) and not (set(selc) & fixed)
+        selg = gi[n, :nsg].tolist()
+        assert selg == sorted(set(selg))
+        assert all(j // (c // g) in selc for j in selg)
+        assert all((j + 1) * g <= s for j in selg)
+        T = oracle.token_set(cfg, b, gi[n], nsg)
+        assert T.tolist() == sorted(set(T.tolist()))
+        assert T.max() == s + B - 1
+        expect = set(range(s, s + B))
+        for m in fixed:
+            expect |= set(range(m * c, (m + 1) * c))
+        for j in selg:
+            expect |= set(range(j * g, (j + 1) * g))
+        assert set(T.tolist()) == expect
+        assert len(T) == c * len(fixed) + g * nsg + B
+
+
+# ------------------------------------------------------------------ planted workloads
+def test_planted_margins_tiny_workload():
+    """The tiny fp32 workload: 4 planted groups; wherever all planted chunks are
+    candidates, the kept chunks are exactly them with a score margin >= 0.5, and
+    the planted groups are kept."""
+    cfg = synth.config(0)
+    x = synth.make_inputs(cfg)
+    q, k = synth.to_f64(x["q"], "f32"), synth.to_f64(x["k"], "f32")
+    ci, gi, ns, dg = oracle.route(cfg, q, k)
+    planted = x["planted"][0]
+    pch = sorted({j // 8 for j in planted})
+    n_checked = 0
+    for b in range(cfg["n_q"] // 64):
+        if b - 2 >= max(pch):
+            n_checked += 1
+            assert ci[b].tolist() == pch
+            assert dg[b, oracle.DG_GAP_C] >= 0.5
+            assert set(planted) <= set(gi[b].tolist())
+    assert n_checked >= 2
