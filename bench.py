@@ -1,0 +1,259 @@
+"""Benchmark of the HGA routed-attention forward on one MI355X.
+
+A step is one pass of the whole path over one layer of one synthetic input:
+hga_build_summaries (group and chunk summaries of every key), hga_route
+(block queries, chunk stage, group stage) and hga_attend (exact routed
+attention), all on one stream with every input already in HBM.
+
+The workload is the 16,384-token training-segment shape (Qwen3-8B heads:
+32 query / 8 KV heads, head_dim 128, bf16, 2,048 active queries over a
+14,336-token history, top-16 chunks, top-64 groups, sink 64, local 128).
+The same line also reports the 65,536-token Qwen3-30B-A3B-shaped layer with
+its history in HBM and, separately, with its history in pinned host memory
+(that rate includes the PCIe transfer of the routed set).
+
+Output: one JSON line (see the keys below). ``roofline`` covers the attention
+kernel, whose duration is measured with HIP events on the launch stream over
+the timed steps; ``cpu_baseline`` is the CPU oracle on a bounded sample of the
+same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
+PEAK_BF16 = 2.5e15         # flop/s, MI355X dense bf16 MFMA
+PEAK_F32_MFMA = 157.3e12
+
+METRIC = "routed-attn query-tokens/sec per layer at 16K/64K; % of HBM or MFMA peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2, help="workload index (default: the 16K segment)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the 64K lines")
+    return ap.parse_args()
+
+
+def algorithmic(cfg, n_sel):
+    """Attention flops and bytes of one launch from the kept selection.
+
+    flops = 4 d x (attended query-key pairs) over all query heads;
+    bytes = Q read + O write + per-(block, KV head) K/V rows of its token set.
+    """
+    d, G, hkv = cfg["d"], cfg["hq"] // cfg["hkv"], cfg["hkv"]
+    nb = cfg["n_q"] // 64
+    q0 = cfg["L"] - cfg["n_q"]
+    esz = 2 if cfg["dtype"] == "bf16" else 4
+    ns = n_sel.reshape(nb, hkv, 2)
+    pairs = 0
+    kv_rows = 0
+    for b in range(nb):
+        s = q0 + 64 * b
+        ms = s // 64
+        a = min(cfg["sink"] // 64, ms)
+        bb = max(ms - cfg["local"] // 64, a)
+        fixed = 64 * (a + ms - bb)
+        for h in range(hkv):
+            hist = fixed + cfg["group"] * int(ns[b, h, 1])
+            pairs += G * (64 * hist + 64 * 65 // 2)
+            kv_rows += hist + 64
+    flops = 4.0 * d * pairs
+    qo = 2.0 * cfg["hq"] * cfg["n_q"] * d * esz
+    byts = qo + 2.0 * kv_rows * d * esz
+    return flops, byts, pairs
+
+
+def to_dev(a, dtype, dev):
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+
+class Workload:
+    """Device buffers and one step of the path for one configuration."""
+
+    def __init__(self, cfg_id, split=0):
+        import torch
+
+        import hierarchical_sparse_attention_hga_amd as hga
+        import synth
+        from hierarchical_sparse_attention_hga_amd.memory import split_to_host
+
+        self.torch, self.hga = torch, hga
+        self.cfg = cfg = synth.config(cfg_id)
+        self.x = x = synth.make_inputs(cfg)
+        self.c = hga.make_config(cfg["hq"], cfg["hkv"], cfg["d"], cfg["top_chunks"], cfg["top_groups"],
+                                 cfg["sink"], cfg["local"], dtype=cfg["dtype"], group_size=cfg["group"])
+        DEV = torch.device("cuda:0")
+        L, nq, hkv, d = cfg["L"], cfg["n_q"], cfg["hkv"], cfg["d"]
+        self.L, self.nq, self.q0 = L, nq, L - nq
+        nb = nq // 64
+        self.q, k, v = (to_dev(x[n], cfg["dtype"], DEV) for n in ("q", "k", "v"))
+        self.gs = torch.empty(hkv, L // cfg["group"], d, device=DEV)
+        self.cs = torch.empty(hkv, L // 64, d, device=DEV)
+        self.ci = torch.empty(nb, hkv, cfg["top_chunks"], dtype=torch.int32, device=DEV)
+        self.gi = torch.empty(nb, hkv, cfg["top_groups"], dtype=torch.int32, device=DEV)
+        self.ns = torch.empty(nb, hkv, 2, dtype=torch.int32, device=DEV)
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty(cfg["hq"], nq, device=DEV)
+        self.k_full = k
+        self.split = split
+        self.pins = []
+        self.ws, self.wsb = None, 0
+        if split > 0:
+            hga.hga_build_summaries(self.c, k, L, self.gs, self.cs)
+            torch.cuda.synchronize()
+            gpin, _, gs_t = split_to_host(self.gs, split // cfg["group"])
+            self.gs_t = (gs_t[0], gs_t[1], split)
+            kpin, _, self.k_t = split_to_host(k, split)
+            vpin, _, self.v_t = split_to_host(v, split)
+            self.pins = [gpin, kpin, vpin]
+            self.wsb = hga.hga_workspace_size(self.c, L, nq, hga.HGA_WS_ATTEND_TIERED)
+            self.ws = torch.empty(self.wsb, dtype=torch.uint8, device=DEV)
+        else:
+            self.gs_t, self.k_t, self.v_t = self.gs, k, v
+
+    def step(self, ev=None):
+        hga, c = self.hga, self.c
+        if ev:
+            ev[0].record()
+        if self.split == 0:
+            hga.hga_build_summaries(c, self.k_full, self.L, self.gs, self.cs)
+        if ev:
+            ev[1].record()
+        hga.hga_route(c, self.q, self.q0, self.nq, self.L, self.cs, self.gs_t, self.ci, self.gi, self.ns)
+        if ev:
+            ev[2].record()
+        hga.hga_attend(c, self.q, self.q0, self.nq, self.L, self.k_t, self.v_t, self.gi, self.ns,
+                       self.out, self.lse, self.ws, self.wsb)
+        if ev:
+            ev[3].record()
+
+    def run(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        stage = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs]) * 1e3  # us
+        return wall, stage
+
+    def free(self):
+        for p in self.pins:
+            p.free()
+
+
+def roofline(cfg, n_sel, attend_us):
+    flops, byts, _ = algorithmic(cfg, n_sel)
+    t_mfma = flops / PEAK_BF16
+    t_hbm = byts / PEAK_HBM
+    t = attend_us * 1e-6
+    if t_mfma >= t_hbm:
+        return {"bound": "mfma", "achieved": flops / t / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                "frac": flops / t / PEAK_BF16, "traffic": None,
+                "algorithmic_flops": flops, "algorithmic_bytes": byts}
+    return {"bound": "hbm", "achieved": byts / t / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+            "frac": byts / t / PEAK_HBM, "traffic": None,
+            "algorithmic_flops": flops, "algorithmic_bytes": byts}
+
+
+def cpu_baseline(cfg_id):
+    """The oracle on a bounded sample: summaries of every key, then routing and
+    attention of a few query blocks for every KV head, scaled to the layer."""
+    import oracle
+    import synth
+    cfg = synth.config(cfg_id)
+    x = synth.make_inputs(cfg)
+    f = {n: synth.to_f64(x[n], cfg["dtype"]) for n in ("q", "k", "v")}
+    nb = cfg["n_q"] // 64
+    blocks = [nb - 1] if cfg_id >= 3 else [0, nb - 1]
+    items = [(b, h) for b in blocks for h in range(cfg["hkv"])]
+    t0 = time.perf_counter()
+    sums = (oracle.summaries(cfg, f["k"]), oracle.abs_summaries(cfg, f["k"]))
+    t1 = time.perf_counter()
+    ci, gi, ns, dg = oracle.route(cfg, f["q"], f["k"], items, sums=sums)
+    oracle.attend(cfg, f["q"], f["k"], f["v"], items, gi, ns[:, 1])
+    t2 = time.perf_counter()
+    per_layer = (t1 - t0) + (t2 - t1) * nb / len(blocks)
+    return {"value": cfg["n_q"] / per_layer, "unit": "query-tokens/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"float64 C oracle: summaries of all {cfg['L']} keys ({t1 - t0:.2f} s), then routing "
+                      f"and attention of query blocks {blocks} for all {cfg['hkv']} KV heads "
+                      f"({t2 - t1:.2f} s), scaled to the {nb} blocks of the layer"}
+
+
+def measure(cfg_id, steps, warmup, split=0):
+    w = Workload(cfg_id, split)
+    wall, stage = w.run(steps, warmup)
+    ns = w.ns.cpu().numpy()
+    cfg = w.cfg
+    w.free()
+    med = np.median(stage, axis=0)
+    mean = stage.mean(axis=0)
+    return cfg, ns, wall, med, mean
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by KV head with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    torch.cuda.init()
+    cfg, ns, wall, med, mean = measure(args.config, args.steps, args.warmup)
+    value = args.steps * cfg["n_q"] / wall
+    rl = roofline(cfg, ns, mean[2])
+    line = {
+        "metric": METRIC, "value": value, "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg["dtype"],
+        "data": "synthetic (seeded; Qwen3-shaped heads, rank-8 shared component, planted groups)",
+        "config": {"workload": cfg["name"], "seq_len": cfg["L"], "n_q": cfg["n_q"], "q_heads": cfg["hq"],
+                   "kv_heads": cfg["hkv"], "head_dim": cfg["d"], "top_chunks": cfg["top_chunks"],
+                   "top_groups": cfg["top_groups"], "sink": cfg["sink"], "local": cfg["local"],
+                   "kv_residency": "hbm"},
+        "stages_us_mean": {"summaries": mean[0], "route": mean[1], "attend": mean[2]},
+        "stages_us_median": {"summaries": med[0], "route": med[1], "attend": med[2]},
+        "roofline": rl,
+    }
+    if not args.no_extra and args.config != 3:
+        extra = {}
+        c3, ns3, wall3, med3, mean3 = measure(3, max(args.steps // 2, 5), args.warmup)
+        extra["64k_hbm"] = {"value": max(args.steps // 2, 5) * c3["n_q"] / wall3, "unit": "query-tokens/s",
+                            "stages_us_mean": {"summaries": mean3[0], "route": mean3[1], "attend": mean3[2]},
+                            "roofline": roofline(c3, ns3, mean3[2])}
+        c3h, _, wallh, medh, meanh = measure(3, 5, 2, split=c3["tier_split"])
+        extra["64k_host_tier_pcie_inclusive"] = {
+            "value": 5 * c3h["n_q"] / wallh, "unit": "query-tokens/s",
+            "note": "history K/V and group summaries in pinned host memory; routed rows cross PCIe each step",
+            "stages_us_mean": {"route": meanh[1], "gather_and_attend": meanh[2]}}
+        line["also"] = extra
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args.config)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,190 @@
+// C ABI of the HGA routed-attention library: argument validation on the host,
+// then kernel launches on the caller's stream. See include/hga.h for the
+// contract of each entry point.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "hga_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+hga_status fail(hga_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+hga_status ok() {
+  g_err[0] = '\0';
+  return HGA_OK;
+}
+
+hga_status device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(HGA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Validate the config and the sequence geometry; fill the derived shape.
+hga_status make_shape(const hga_config* cfg, int64_t seq_len, int64_t q_start, int64_t n_q,
+                      hga::Shape* s) {
+  using namespace hga;
+  if (!cfg) return fail(HGA_ERR_INVALID_ARGUMENT, "cfg is NULL");
+  if (cfg->n_q_heads < 1 || cfg->n_kv_heads < 1 || cfg->n_q_heads % cfg->n_kv_heads != 0)
+    return fail(HGA_ERR_INVALID_ARGUMENT, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)",
+                cfg->n_q_heads, cfg->n_kv_heads);
+  if (cfg->dtype != HGA_F32 && cfg->dtype != HGA_BF16)
+    return fail(HGA_ERR_INVALID_ARGUMENT, "unknown dtype %d", cfg->dtype);
+  if (cfg->summary_op != HGA_SUMMARY_MEAN)
+    return fail(HGA_ERR_INVALID_ARGUMENT, "unknown summary_op %d", cfg->summary_op);
+  if (cfg->head_dim < 1) return fail(HGA_ERR_INVALID_ARGUMENT, "head_dim must be positive");
+  if (cfg->chunk_size < 1 || cfg->group_size < 1 || cfg->q_block < 1)
+    return fail(HGA_ERR_INVALID_ARGUMENT, "chunk_size, group_size and q_block must be positive");
+  if (cfg->chunk_size % cfg->group_size != 0)
+    return fail(HGA_ERR_INVALID_ARGUMENT, "group_size (%d) must divide chunk_size (%d)", cfg->group_size,
+                cfg->chunk_size);
+  if (cfg->top_chunks < 0 || cfg->top_groups < 0 || cfg->sink_tokens < 0 || cfg->local_tokens < 0)
+    return fail(HGA_ERR_INVALID_ARGUMENT, "budgets and window sizes must be >= 0");
+  if (!(cfg->softmax_scale >= 0.0f) || !isfinite(cfg->softmax_scale))
+    return fail(HGA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
+  if (seq_len < 0 || q_start < 0 || n_q < 0 || q_start + n_q > seq_len)
+    return fail(HGA_ERR_INVALID_ARGUMENT, "need 0 <= q_start, 0 <= n_q, q_start + n_q <= seq_len");
+  if (cfg->chunk_size != kChunk || cfg->q_block != kChunk)
+    return fail(HGA_ERR_UNSUPPORTED, "chunk_size and q_block must both be %d", kChunk);
+  if (cfg->sink_tokens % kChunk || cfg->local_tokens % kChunk)
+    return fail(HGA_ERR_UNSUPPORTED, "sink_tokens and local_tokens must be multiples of %d", kChunk);
+  if (seq_len % kChunk || q_start % kChunk || n_q % kChunk)
+    return fail(HGA_ERR_UNSUPPORTED, "seq_len, q_start and n_q must be multiples of %d", kChunk);
+  const int d = cfg->head_dim;
+  if (cfg->dtype == HGA_BF16 && d != 64 && d != 128)
+    return fail(HGA_ERR_UNSUPPORTED, "bfloat16 needs head_dim 64 or 128 (got %d)", d);
+  if (cfg->dtype == HGA_F32 && !(d == 4 || d == 8 || d == 16 || d == 32 || d == 64 || d == 128))
+    return fail(HGA_ERR_UNSUPPORTED, "float32 needs head_dim in {4, 8, 16, 32, 64, 128} (got %d)", d);
+  if (seq_len / kChunk > kMaxCand)
+    return fail(HGA_ERR_UNSUPPORTED, "seq_len above %lld", (long long)kMaxCand * kChunk);
+  const int gpc = kChunk / cfg->group_size;
+  if (cfg->top_chunks > kMaxKeptChunks || (int64_t)cfg->top_chunks * gpc > kMaxCand)
+    return fail(HGA_ERR_UNSUPPORTED, "top_chunks too large (at most %d and %d groups)", kMaxKeptChunks,
+                kMaxCand);
+  if (cfg->top_groups > kMaxRouted)
+    return fail(HGA_ERR_UNSUPPORTED, "top_groups above %d", kMaxRouted);
+  s->hq = cfg->n_q_heads;
+  s->hkv = cfg->n_kv_heads;
+  s->G = s->hq / s->hkv;
+  s->d = d;
+  s->c = kChunk;
+  s->g = cfg->group_size;
+  s->B = kChunk;
+  s->kc = cfg->top_chunks;
+  s->kg = cfg->top_groups;
+  s->sink_chunks = cfg->sink_tokens / kChunk;
+  s->local_chunks = cfg->local_tokens / kChunk;
+  s->dtype = cfg->dtype;
+  s->scale = cfg->softmax_scale > 0.0f ? cfg->softmax_scale : 1.0f / sqrtf((float)d);
+  s->L = seq_len;
+  s->q0 = q_start;
+  s->nq = n_q;
+  s->nb = n_q / kChunk;
+  return HGA_OK;
+}
+
+hga_status check_tier(const hga_tiered* t, const char* name, int64_t seq_len, int64_t q_start) {
+  if (!t) return fail(HGA_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (t->split < 0 || t->split > q_start)
+    return fail(HGA_ERR_INVALID_ARGUMENT, "%s.split must be in [0, q_start]", name);
+  if (t->split % hga::kChunk) return fail(HGA_ERR_UNSUPPORTED, "%s.split must be a multiple of 64", name);
+  if (t->split > 0 && !t->host) return fail(HGA_ERR_INVALID_ARGUMENT, "%s.host is NULL", name);
+  if (t->split < seq_len && !t->dev) return fail(HGA_ERR_INVALID_ARGUMENT, "%s.dev is NULL", name);
+  return HGA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hga_workspace_size(const hga_config* cfg, int64_t seq_len, int64_t n_q, int32_t which) {
+  hga::Shape s;
+  if (make_shape(cfg, seq_len, seq_len - n_q, n_q, &s) != HGA_OK) return (size_t)-1;
+  switch (which) {
+    case HGA_WS_ROUTE: return 0;
+    case HGA_WS_ATTEND: return 0;
+    case HGA_WS_ATTEND_TIERED: return hga::staging_bytes(s);
+    default: fail(HGA_ERR_INVALID_ARGUMENT, "unknown workspace kind %d", which); return (size_t)-1;
+  }
+}
+
+hga_status hga_build_summaries(const hga_config* cfg, const void* k, int64_t seq_len, float* group_sum,
+                               float* chunk_sum, void* stream) {
+  hga::Shape s;
+  hga_status st = make_shape(cfg, seq_len, 0, 0, &s);
+  if (st != HGA_OK) return st;
+  if (seq_len == 0) return ok();
+  if (!k || !group_sum || !chunk_sum)
+    return fail(HGA_ERR_INVALID_ARGUMENT, "k, group_sum and chunk_sum must be non-NULL");
+  return device_status(hga::launch_summaries(s, k, group_sum, chunk_sum, (hipStream_t)stream),
+                       "hga_build_summaries launch");
+}
+
+hga_status hga_route(const hga_config* cfg, const void* q, int64_t q_start, int64_t n_q, int64_t seq_len,
+                     const float* chunk_sum, const hga_tiered* group_sum, int32_t* chunk_idx,
+                     int32_t* group_idx, int32_t* n_sel, void* workspace, size_t ws_bytes, void* stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  hga::Shape s;
+  hga_status st = make_shape(cfg, seq_len, q_start, n_q, &s);
+  if (st != HGA_OK) return st;
+  if (n_q == 0) return ok();
+  if (!q || !chunk_sum || !n_sel || (s.kc > 0 && !chunk_idx) || (s.kg > 0 && !group_idx))
+    return fail(HGA_ERR_INVALID_ARGUMENT, "q, chunk_sum, n_sel, chunk_idx and group_idx must be non-NULL");
+  if ((st = check_tier(group_sum, "group_sum", seq_len, q_start)) != HGA_OK) return st;
+  return device_status(
+      hga::launch_route(s, q, chunk_sum, static_cast<const float*>(group_sum->host),
+                        static_cast<const float*>(group_sum->dev), group_sum->split, chunk_idx, group_idx,
+                        n_sel, (hipStream_t)stream),
+      "hga_route launch");
+}
+
+hga_status hga_attend(const hga_config* cfg, const void* q, int64_t q_start, int64_t n_q, int64_t seq_len,
+                      const hga_tiered* k, const hga_tiered* v, const int32_t* group_idx,
+                      const int32_t* n_sel, void* out, float* lse, void* workspace, size_t ws_bytes,
+                      void* stream) {
+  hga::Shape s;
+  hga_status st = make_shape(cfg, seq_len, q_start, n_q, &s);
+  if (st != HGA_OK) return st;
+  if (n_q == 0) return ok();
+  if (!q || !out || !n_sel || (s.kg > 0 && !group_idx))
+    return fail(HGA_ERR_INVALID_ARGUMENT, "q, out, n_sel and group_idx must be non-NULL");
+  if ((st = check_tier(k, "k", seq_len, q_start)) != HGA_OK) return st;
+  if ((st = check_tier(v, "v", seq_len, q_start)) != HGA_OK) return st;
+  if (k->split != v->split) return fail(HGA_ERR_INVALID_ARGUMENT, "k.split and v.split differ");
+  if (k->split > 0) {
+    const size_t need = hga::staging_bytes(s);
+    if (!workspace || ws_bytes < need)
+      return fail(HGA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                  workspace ? ws_bytes : (size_t)0);
+  }
+  hga::KVSrc kv{k->host, k->dev, v->host, v->dev, k->split};
+  return device_status(hga::launch_attend(s, q, kv, group_idx, n_sel, out, lse, workspace, (hipStream_t)stream),
+                       "hga_attend launch");
+}
+
+const char* hga_status_string(hga_status status) {
+  switch (status) {
+    case HGA_OK: return "ok";
+    case HGA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case HGA_ERR_UNSUPPORTED: return "unsupported";
+    case HGA_ERR_WORKSPACE: return "workspace too small";
+    case HGA_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* hga_last_error(void) { return g_err; }
+
+int32_t hga_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// Internal declarations of the gfx950 HGA routed-attention library.
+// Kernel sources and the C-ABI layer include this; nothing outside csrc/ does.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hga.h"
+
+namespace hga {
+
+// Chunk and query-block size the kernels are built for (the pages' 64-token
+// chunks; a query block is one chunk).
+constexpr int kChunk = 64;
+// Largest number of routing candidates of one stage for one (block, KV head).
+constexpr int kMaxCand = 4096;
+// Largest number of routed groups an attention workgroup keeps in LDS.
+constexpr int kMaxRouted = 4096;
+// Most chunks the router may keep per item (LDS list of the group stage).
+constexpr int kMaxKeptChunks = 2048;
+
+// Validated problem shape shared by the launchers.
+struct Shape {
+  int hq, hkv, G, d;
+  int c, g, B;          // chunk, group, query block
+  int kc, kg;           // top chunks, top groups
+  int sink_chunks, local_chunks;
+  int dtype;            // hga_dtype
+  float scale;          // softmax scale (resolved)
+  int64_t L, q0, nq, nb;
+};
+
+// Fixed sink/local windows of a block whose first token is in chunk ms: the
+// fixed chunks are [0, a) and [bb, ms) with a <= bb <= ms; the chunk-stage
+// candidates are [a, bb).
+__host__ __device__ inline void fixed_windows(int64_t ms, int sink_chunks, int local_chunks,
+                                              int64_t* a, int64_t* bb) {
+  int64_t aa = sink_chunks < ms ? sink_chunks : ms;
+  int64_t lo = ms - local_chunks;
+  *a = aa;
+  *bb = lo > aa ? lo : aa;
+}
+
+// Number of 64-token tiles of one item's token set: fixed chunks, routed
+// groups packed 64/g per tile, and the block's own tile.
+__host__ __device__ inline int64_t max_tiles(const Shape& s) {
+  return (int64_t)s.sink_chunks + s.local_chunks + ((int64_t)s.kg * s.g + kChunk - 1) / kChunk + 1;
+}
+
+hipError_t launch_summaries(const Shape& s, const void* k, float* gs, float* cs, hipStream_t st);
+
+hipError_t launch_route(const Shape& s, const void* q, const float* cs, const float* gs_host,
+                        const float* gs_dev, int64_t split, int32_t* chunk_idx, int32_t* group_idx,
+                        int32_t* n_sel, hipStream_t st);
+
+// K/V sources of the attention: device rows [split, L) and host rows [0, split).
+struct KVSrc {
+  const void* k_host;
+  const void* k_dev;
+  const void* v_host;
+  const void* v_dev;
+  int64_t split;
+};
+
+// Bytes of the staging buffer the tiered path gathers into.
+size_t staging_bytes(const Shape& s);
+
+hipError_t launch_attend(const Shape& s, const void* q, const KVSrc& kv, const int32_t* group_idx,
+                         const int32_t* n_sel, void* out, float* lse, void* staging, hipStream_t st);
+
+}  // namespace hga

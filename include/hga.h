@@ -1,0 +1,183 @@
+/*
+ * hga.h -- C ABI of the MI355X (gfx950) HGA routed-attention forward.
+ *
+ * Hierarchical Global Attention (HGA) replaces dense causal attention. The
+ * operation follows "Long-Context Fine-Tuning with Limited VRAM", section 2.1
+ * "Exact-token hierarchical routing", and the base HGA abstract:
+ *
+ *   hga_build_summaries  key summaries of every 8-token group and every closed
+ *                        64-token chunk, built from the model's projected,
+ *                        RoPE-applied keys (section 2.1, first paragraph;
+ *                        abstract: "compact RoPE-aware summaries"). The
+ *                        operator is the mean of the post-RoPE keys.
+ *   hga_route            per query block and KV head: score chunk summaries
+ *                        with the block's mean query, keep the top chunks in
+ *                        addition to fixed sink and local windows, open them
+ *                        into groups and keep the top groups (section 2.1,
+ *                        "Chunk selection" and "Group selection"). Indices
+ *                        only; no gradient (section 2.1, last paragraph).
+ *   hga_attend           exact causal softmax attention of each query over
+ *                        the exact token K/V of the kept groups, the fixed
+ *                        windows and its own block (section 2.1, "Exact-token
+ *                        attention"); summaries are never attended.
+ *
+ * Conventions shared by every entry point
+ *   Layout     head-major, row-major: Q and O are [Hq][n_q][d], K and V are
+ *              [Hkv][seq_len][d]; query row i of Q holds position q_start + i.
+ *              Query head r reads KV head r / (Hq / Hkv).
+ *   Element    Q, K, V and O use cfg->dtype (float32 or bfloat16);
+ *              summaries are float32; indices are int32.
+ *   Ownership  the caller allocates every buffer and the workspace and keeps
+ *              them alive until the work on `stream` has finished. The library
+ *              allocates nothing and keeps no state between calls.
+ *   Memory     "device" pointers are GPU memory of the current HIP device;
+ *              "host" pointers of an hga_tiered are pinned host memory
+ *              allocated with hipHostMalloc (mapped, readable by kernels).
+ *   Streams    `stream` is a hipStream_t (NULL = the default stream). All work
+ *              is enqueued on it; nothing synchronizes.
+ *   Errors     arguments are validated on the host before any launch; on an
+ *              error nothing is enqueued and a status other than HGA_OK is
+ *              returned. hga_last_error() gives a message (thread-local).
+ *              Kernel launch failures return HGA_ERR_DEVICE.
+ *   Support    chunk_size == q_block == 64; group_size divides 64; sink and
+ *              local sizes are multiples of chunk_size; q_start, n_q and
+ *              seq_len are multiples of chunk_size. bfloat16 needs
+ *              head_dim 64 or 128; float32 needs head_dim % 4 == 0 and
+ *              head_dim <= 128. Anything else returns HGA_ERR_UNSUPPORTED.
+ */
+#ifndef HGA_H
+#define HGA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HGA_OK = 0,
+  HGA_ERR_INVALID_ARGUMENT = 1,  /* null pointer, negative or inconsistent size */
+  HGA_ERR_UNSUPPORTED = 2,       /* valid, but outside what this build implements */
+  HGA_ERR_WORKSPACE = 3,         /* workspace missing or smaller than hga_workspace_size */
+  HGA_ERR_DEVICE = 4             /* a HIP launch or runtime call failed */
+} hga_status;
+
+typedef enum { HGA_F32 = 0, HGA_BF16 = 1 } hga_dtype;
+
+/* Summary operator. The pages call the chunk summaries "RoPE-aware" without
+ * defining them; the mean of the post-RoPE keys is the operator built here. */
+typedef enum { HGA_SUMMARY_MEAN = 0 } hga_summary_op;
+
+typedef struct {
+  int32_t n_q_heads;     /* Hq >= 1, a multiple of n_kv_heads */
+  int32_t n_kv_heads;    /* Hkv >= 1 */
+  int32_t head_dim;      /* d */
+  int32_t chunk_size;    /* tokens per chunk (64) */
+  int32_t group_size;    /* tokens per group (8); divides chunk_size */
+  int32_t q_block;       /* queries per routing block (== chunk_size) */
+  int32_t top_chunks;    /* kc >= 0: routed chunks kept per block and KV head */
+  int32_t top_groups;    /* kg >= 0: routed groups kept per block and KV head */
+  int32_t sink_tokens;   /* S: the first S tokens are always attended */
+  int32_t local_tokens;  /* W: the W tokens before the block are always attended */
+  int32_t summary_op;    /* hga_summary_op */
+  int32_t dtype;         /* hga_dtype of Q, K, V and O */
+  float softmax_scale;   /* 0 selects 1/sqrt(head_dim) */
+} hga_config;
+
+/* A [H][seq_len][width] tensor split between two tiers at token `split`:
+ * rows [0, split) live in `host` as [H][split][width] (pinned host memory),
+ * rows [split, seq_len) live in `dev` as [H][seq_len - split][width].
+ * split == 0 means everything is in `dev` (then `host` may be NULL). For group
+ * summaries the split is counted in tokens and the rows are groups. */
+typedef struct {
+  const void* host;
+  const void* dev;
+  int64_t split;
+} hga_tiered;
+
+enum { HGA_WS_ROUTE = 0, HGA_WS_ATTEND = 1, HGA_WS_ATTEND_TIERED = 2 };
+
+/* Bytes of device workspace that hga_route (which = HGA_WS_ROUTE) or
+ * hga_attend (HGA_WS_ATTEND with everything on the device,
+ * HGA_WS_ATTEND_TIERED with K/V split at a token > 0) needs for this shape.
+ * Returns 0 when no workspace is needed, and (size_t)-1 when the config or
+ * sizes are invalid. */
+size_t hga_workspace_size(const hga_config* cfg, int64_t seq_len, int64_t n_q, int32_t which);
+
+/* Key summaries (section 2.1, first paragraph).
+ *   k          device, [Hkv][seq_len][d] of cfg->dtype, post-RoPE keys.
+ *   group_sum  device, [Hkv][seq_len / group_size][d] float32: the mean of
+ *              each group's keys, rounded once to float32.
+ *   chunk_sum  device, [Hkv][seq_len / chunk_size][d] float32: the mean of
+ *              each chunk's keys, rounded once to float32.
+ * Means are accumulated in float64 before the single rounding. */
+hga_status hga_build_summaries(const hga_config* cfg, const void* k, int64_t seq_len,
+                               float* group_sum, float* chunk_sum, void* stream);
+
+/* Two-level routing (section 2.1, "Chunk selection", "Group selection").
+ * For query block b (positions s = q_start + 64 b .. s + 63) and KV head h:
+ *   block query   mean of Q over the block's 64 positions and the
+ *                 Hq/Hkv query heads of h (float64 accumulation);
+ *   fixed chunks  sink: chunks before sink_tokens; local: the chunks holding
+ *                 the local_tokens before s (only chunks that end by s);
+ *   chunk stage   candidates are the chunks ending by s that are not fixed;
+ *                 score = block query . chunk_sum (float64 dot of the float32
+ *                 summary); keep the top_chunks highest, ties to the lower
+ *                 chunk index;
+ *   group stage   candidates are the groups of the kept chunks; score =
+ *                 block query . group_sum; keep the top_groups highest, ties to
+ *                 the lower group index.
+ *   q          device, [Hq][n_q][d] of cfg->dtype.
+ *   chunk_sum  device, as written by hga_build_summaries.
+ *   group_sum  group summaries, tiered at a token split (a multiple of
+ *              chunk_size, <= q_start); host rows are read only when the group
+ *              stage must choose (top_groups < groups of the kept chunks).
+ *   chunk_idx  device, [n_q/64][Hkv][top_chunks] int32, ascending, -1 padded.
+ *   group_idx  device, [n_q/64][Hkv][top_groups] int32, ascending, -1 padded.
+ *   n_sel      device, [n_q/64][Hkv][2] int32: kept chunks, kept groups.
+ *   workspace  unused (hga_workspace_size returns 0); may be NULL. */
+hga_status hga_route(const hga_config* cfg, const void* q, int64_t q_start, int64_t n_q,
+                     int64_t seq_len, const float* chunk_sum, const hga_tiered* group_sum,
+                     int32_t* chunk_idx, int32_t* group_idx, int32_t* n_sel,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+/* Exact-token routed attention (section 2.1, "Exact-token attention").
+ * Query at position p of block b attends, with causal masking t <= p, to the
+ * token set: the fixed sink and local chunks, the kept groups, and the block's
+ * own 64 tokens. out = softmax(scale * q . k_t) @ v_t; lse = log-sum-exp of the
+ * scaled scores (natural log).
+ *   q          device, [Hq][n_q][d] of cfg->dtype.
+ *   k, v       [Hkv][seq_len][d] of cfg->dtype, tiered at a token split
+ *              (a multiple of chunk_size, <= q_start). With split > 0 the
+ *              routed rows are first gathered into the workspace.
+ *   group_idx  device, [n_q/64][Hkv][top_groups] as written by hga_route.
+ *              An entry is usable when it is >= 0, its group ends by the block
+ *              start and it lies outside the sink and local chunks; a usable
+ *              entry that is not greater than every earlier usable entry of
+ *              its row is skipped, so each token counts once and an ascending
+ *              row is taken whole.
+ *   n_sel      device, [n_q/64][Hkv][2]; the second value (clamped to
+ *              [0, top_groups]) is how many entries of the row to read.
+ *   out        device, [Hq][n_q][d] of cfg->dtype.
+ *   lse        device, [Hq][n_q] float32, or NULL.
+ *   workspace  device, at least hga_workspace_size(...) bytes. */
+hga_status hga_attend(const hga_config* cfg, const void* q, int64_t q_start, int64_t n_q,
+                      int64_t seq_len, const hga_tiered* k, const hga_tiered* v,
+                      const int32_t* group_idx, const int32_t* n_sel,
+                      void* out, float* lse, void* workspace, size_t ws_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* hga_status_string(hga_status status);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* hga_last_error(void);
+
+/* ABI version of this library (major * 100 + minor). */
+int32_t hga_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HGA_H */

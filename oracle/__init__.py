@@ -58,6 +58,7 @@ def _load():
         lib.orc_token_set.argtypes = [C.POINTER(_Cfg), C.c_int, P, C.c_int, P, C.c_int64]
         lib.orc_token_set.restype = C.c_int64
         assert lib.orc_diag_width() == 8
+        lib.orc_threads.restype = C.c_int
         _lib = lib
     return _lib
 
@@ -154,6 +155,11 @@ def token_set(cfg, b, group_idx, n_groups):
     buf = np.empty(cap, np.int32)
     n = lib.orc_token_set(C.byref(make_cfg(cfg)), int(b), _ptr(gi), int(n_groups), _ptr(buf), cap)
     return buf[:n].copy()
+
+
+def threads() -> int:
+    """OpenMP threads the oracle runs on."""
+    return int(_load().orc_threads())
 
 
 def certified(diag_row, stage: str) -> bool:

@@ -329,3 +329,11 @@ int orc_attend(const orc_cfg* c, const double* q, const double* k, const double*
 }
 
 int orc_diag_width(void) { return DG_NUM; }
+
+/* Threads the OpenMP loops use. */
+#ifdef _OPENMP
+#include <omp.h>
+int orc_threads(void) { return omp_get_max_threads(); }
+#else
+int orc_threads(void) { return 1; }
+#endif

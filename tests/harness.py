@@ -1,0 +1,141 @@
+"""Shared helpers of the GPU tests: device upload, pinned host tiers, one call
+of the whole path through the C ABI, and the comparison rules."""
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+import torch
+
+import hierarchical_sparse_attention_hga_amd as hga
+from hierarchical_sparse_attention_hga_amd.memory import split_to_host
+import oracle
+import synth
+
+DEV = torch.device("cuda:0")
+
+# Output tolerances against the float64 oracle. bfloat16: the workload's
+# stated bar (max-abs 2e-2, mean-abs 1e-3). float32: scores and softmax in
+# float32 over at most a few thousand tokens keep the relative error near
+# 1e-6; the bar leaves two orders of magnitude of room.
+TOL = {"bf16": dict(max_abs=2e-2, mean_abs=1e-3, lse_abs=1e-3),
+       "f32": dict(max_abs=1e-4, mean_abs=1e-5, lse_abs=1e-4)}
+
+
+def to_dev(a, dtype):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def hga_cfg(cfg):
+    return hga.make_config(cfg["hq"], cfg["hkv"], cfg["d"], cfg["top_chunks"], cfg["top_groups"],
+                           cfg["sink"], cfg["local"], dtype=cfg["dtype"], group_size=cfg["group"],
+                           softmax_scale=cfg.get("softmax_scale") or 0.0)
+
+
+def gpu_run(cfg, x, split=0, group_idx=None, n_sel=None, q_start=None, seq_len=None):
+    """Run summaries, routing and attention through the C ABI.
+
+    ``group_idx``/``n_sel`` (numpy, [nb][hkv][kg] / [nb][hkv][2]) replace the
+    GPU routing as the attention's input when given. Returns numpy arrays.
+    """
+    c = hga_cfg(cfg)
+    dt = cfg["dtype"]
+    L = cfg["L"] if seq_len is None else seq_len
+    nq = cfg["n_q"]
+    q0 = L - nq if q_start is None else q_start
+    nb, hkv, d, g = nq // 64, cfg["hkv"], cfg["d"], cfg["group"]
+    q, k, v = to_dev(x["q"], dt), to_dev(x["k"], dt), to_dev(x["v"], dt)
+    gs = torch.empty(hkv, L // g, d, device=DEV)
+    cs = torch.empty(hkv, L // 64, d, device=DEV)
+    ci = torch.full((nb, hkv, cfg["top_chunks"]), -7, dtype=torch.int32, device=DEV)
+    gi = torch.full((nb, hkv, cfg["top_groups"]), -7, dtype=torch.int32, device=DEV)
+    ns = torch.full((nb, hkv, 2), -7, dtype=torch.int32, device=DEV)
+    out = torch.empty_like(q)
+    lse = torch.empty(cfg["hq"], nq, device=DEV)
+    hga.hga_build_summaries(c, k, L, gs, cs)
+    pins = []
+    if split > 0:
+        gpin, _, gs_t = split_to_host(gs, split // g)
+        gs_t = (gs_t[0], gs_t[1], split)          # the group-summary split is counted in tokens
+        kpin, _, k_t = split_to_host(k, split)
+        vpin, _, v_t = split_to_host(v, split)
+        pins = [gpin, kpin, vpin]
+    else:
+        gs_t, k_t, v_t = gs, k, v
+    hga.hga_route(c, q, q0, nq, L, cs, gs_t, ci, gi, ns)
+    if group_idx is not None:
+        gi_in = torch.from_numpy(np.ascontiguousarray(group_idx, dtype=np.int32)).to(DEV)
+        ns_in = torch.from_numpy(np.ascontiguousarray(n_sel, dtype=np.int32)).to(DEV)
+    else:
+        gi_in, ns_in = gi, ns
+    ws = None
+    wsb = 0
+    if split > 0:
+        wsb = hga.hga_workspace_size(c, L, nq, hga.HGA_WS_ATTEND_TIERED)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    hga.hga_attend(c, q, q0, nq, L, k_t, v_t, gi_in, ns_in, out, lse, ws, wsb)
+    torch.cuda.synchronize()
+    res = dict(gs=gs.cpu().numpy(), cs=cs.cpu().numpy(), chunk_idx=ci.cpu().numpy(),
+               group_idx=gi.cpu().numpy(), n_sel=ns.cpu().numpy(),
+               out=out.float().cpu().numpy().astype(np.float64), lse=lse.cpu().numpy().astype(np.float64))
+    for p in pins:
+        p.free()
+    return res
+
+
+@functools.lru_cache(maxsize=4)
+def inputs(cfg_id, **over):
+    cfg = synth.config(cfg_id, **over)
+    x = synth.make_inputs(cfg)
+    f = {n: synth.to_f64(x[n], cfg["dtype"]) for n in ("q", "k", "v")}
+    return cfg, x, f
+
+
+def oracle_route(cfg, f):
+    sums = (oracle.summaries(cfg, f["k"]), oracle.abs_summaries(cfg, f["k"]))
+    return oracle.route(cfg, f["q"], f["k"], sums=sums)
+
+
+def check_routing(cfg, gpu, ref):
+    """Certified boundaries must match exactly. Returns (items, uncertified, mismatches)."""
+    ci_r, gi_r, ns_r, dg = ref
+    kc, kg = cfg["top_chunks"], cfg["top_groups"]
+    n_items = ci_r.shape[0]
+    ci_g = gpu["chunk_idx"].reshape(n_items, kc)
+    gi_g = gpu["group_idx"].reshape(n_items, kg)
+    ns_g = gpu["n_sel"].reshape(n_items, 2)
+    uncert = mism = 0
+    for n in range(ci_r.shape[0]):
+        cc, cg = oracle.certified(dg[n], "chunk"), oracle.certified(dg[n], "group")
+        same_c = np.array_equal(ci_g[n], ci_r[n]) and ns_g[n, 0] == ns_r[n, 0]
+        same_g = np.array_equal(gi_g[n], gi_r[n]) and ns_g[n, 1] == ns_r[n, 1]
+        if not (cc and cg):
+            uncert += 1
+        if cc:
+            assert same_c, f"item {n}: certified chunk set differs: {ci_g[n]} vs {ci_r[n]}"
+            if cg:
+                assert same_g, f"item {n}: certified group set differs: {gi_g[n]} vs {gi_r[n]}"
+        mism += int(not (same_c and same_g))
+    return ci_r.shape[0], uncert, mism
+
+
+def item_rows(cfg, out, items):
+    """Gather [n][G][B][d] rows of a [Hq][n_q][d] array for (b, h) items."""
+    G = cfg["hq"] // cfg["hkv"]
+    return np.stack([np.stack([out[h * G + r, b * 64:(b + 1) * 64] for r in range(G)]) for b, h in items])
+
+
+def check_outputs(cfg, gpu, items, ref_out, ref_lse):
+    tol = TOL[cfg["dtype"]]
+    o = item_rows(cfg, gpu["out"], items)
+    l = item_rows(cfg, gpu["lse"][..., None], items)[..., 0]
+    err = np.abs(o - ref_out)
+    assert np.isfinite(o).all()
+    max_abs, mean_abs = float(err.max()), float(err.mean())
+    lerr = float(np.abs(l - ref_lse).max())
+    assert max_abs <= tol["max_abs"], f"max abs error {max_abs}"
+    assert mean_abs <= tol["mean_abs"], f"mean abs error {mean_abs}"
+    assert lerr <= tol["lse_abs"], f"lse error {lerr}"
+    return max_abs, mean_abs, lerr

@@ -1,0 +1,134 @@
+"""The C ABI on the CPU: the library loads, exports every entry point that
+include/hga.h declares, and every validation path returns its status before
+anything is launched (no GPU is touched by these calls)."""
+import os
+import re
+
+import pytest
+
+import hierarchical_sparse_attention_hga_amd as hga
+from hierarchical_sparse_attention_hga_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000          # never dereferenced: validation fails before any use
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return hga.load()
+
+
+def cfg(**kw):
+    base = dict(n_q_heads=32, n_kv_heads=8, head_dim=128, top_chunks=16, top_groups=64,
+                sink_tokens=64, local_tokens=128, dtype="bf16")
+    base.update(kw)
+    return hga.make_config(**base)
+
+
+def test_every_declared_entry_point_is_exported(lib):
+    header = open(os.path.join(ROOT, "include", "hga.h")).read()
+    declared = set(re.findall(r"^\S[^\n;]*?\b(hga_\w+)\(", header, flags=re.M))
+    assert declared == set(B.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name)
+    assert hga.hga_version() == 100
+
+
+def test_status_strings(lib):
+    for st in range(5):
+        assert hga.hga_status_string(st)
+    assert hga.hga_status_string(99) == "unknown status"
+
+
+def test_workspace_sizes():
+    c = cfg()
+    assert hga.hga_workspace_size(c, 16384, 2048, hga.HGA_WS_ROUTE) == 0
+    assert hga.hga_workspace_size(c, 16384, 2048, hga.HGA_WS_ATTEND) == 0
+    # staging: K and V, every (block, KV head) item, max tiles of 64 rows of d bf16
+    tiles = 1 + 2 + (64 * 8 + 63) // 64 + 1
+    assert hga.hga_workspace_size(c, 16384, 2048, hga.HGA_WS_ATTEND_TIERED) == 2 * 32 * 8 * tiles * 64 * 128 * 2
+    assert hga.hga_workspace_size(c, 16384, 2048, 7) == 2**64 - 1
+    assert hga.hga_workspace_size(cfg(head_dim=96), 16384, 2048, 0) == 2**64 - 1
+
+
+def _status(fn, *args):
+    with pytest.raises(hga.HgaError) as ei:
+        fn(*args)
+    return ei.value.status
+
+
+BAD_CONFIGS = [
+    (dict(n_q_heads=30), hga.HGA_ERR_INVALID_ARGUMENT),
+    (dict(n_kv_heads=0), hga.HGA_ERR_INVALID_ARGUMENT),
+    (dict(dtype=5), hga.HGA_ERR_INVALID_ARGUMENT),
+    (dict(summary_op=3), hga.HGA_ERR_INVALID_ARGUMENT),
+    (dict(top_chunks=-1), hga.HGA_ERR_INVALID_ARGUMENT),
+    (dict(local_tokens=-64), hga.HGA_ERR_INVALID_ARGUMENT),
+    (dict(group_size=7), hga.HGA_ERR_INVALID_ARGUMENT),
+    (dict(softmax_scale=float("nan")), hga.HGA_ERR_INVALID_ARGUMENT),
+    (dict(softmax_scale=-1.0), hga.HGA_ERR_INVALID_ARGUMENT),
+    (dict(chunk_size=32, q_block=32), hga.HGA_ERR_UNSUPPORTED),
+    (dict(q_block=128), hga.HGA_ERR_UNSUPPORTED),
+    (dict(sink_tokens=32), hga.HGA_ERR_UNSUPPORTED),
+    (dict(head_dim=96), hga.HGA_ERR_UNSUPPORTED),
+    (dict(head_dim=48, dtype="f32"), hga.HGA_ERR_UNSUPPORTED),
+    (dict(top_chunks=4096), hga.HGA_ERR_UNSUPPORTED),
+    (dict(top_groups=5000), hga.HGA_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("over,status", BAD_CONFIGS)
+def test_config_validation(over, status):
+    c = cfg(**over)
+    assert _status(hga.hga_build_summaries, c, FAKE, 16384, FAKE, FAKE) == status
+    assert _status(hga.hga_route, c, FAKE, 14336, 2048, 16384, FAKE, FAKE, FAKE, FAKE, FAKE) == status
+    assert _status(hga.hga_attend, c, FAKE, 14336, 2048, 16384, FAKE, FAKE, FAKE, FAKE, FAKE) == status
+    assert hga.hga_last_error()
+
+
+@pytest.mark.parametrize("q_start,n_q,seq_len,status", [
+    (14336, 2048, 16000, hga.HGA_ERR_INVALID_ARGUMENT),   # q_start + n_q > seq_len
+    (-64, 64, 16384, hga.HGA_ERR_INVALID_ARGUMENT),
+    (14300, 2048, 16384, hga.HGA_ERR_UNSUPPORTED),       # not a multiple of 64
+    (14336, 2000, 16384, hga.HGA_ERR_UNSUPPORTED),
+    (0, 64, 64 * 4097, hga.HGA_ERR_UNSUPPORTED),         # too many chunk candidates
+])
+def test_geometry_validation(q_start, n_q, seq_len, status):
+    c = cfg()
+    assert _status(hga.hga_route, c, FAKE, q_start, n_q, seq_len, FAKE, FAKE, FAKE, FAKE, FAKE) == status
+    assert _status(hga.hga_attend, c, FAKE, q_start, n_q, seq_len, FAKE, FAKE, FAKE, FAKE, FAKE) == status
+
+
+def test_null_pointers():
+    c = cfg()
+    E = hga.HGA_ERR_INVALID_ARGUMENT
+    assert _status(hga.hga_build_summaries, c, None, 16384, FAKE, FAKE) == E
+    assert _status(hga.hga_route, c, None, 14336, 2048, 16384, FAKE, FAKE, FAKE, FAKE, FAKE) == E
+    assert _status(hga.hga_route, c, FAKE, 14336, 2048, 16384, FAKE, FAKE, FAKE, FAKE, None) == E
+    assert _status(hga.hga_route, c, FAKE, 14336, 2048, 16384, FAKE, None, FAKE, FAKE, FAKE) == E
+    assert _status(hga.hga_attend, c, FAKE, 14336, 2048, 16384, FAKE, FAKE, FAKE, FAKE, None) == E
+    assert _status(hga.hga_attend, c, FAKE, 14336, 2048, 16384, None, FAKE, FAKE, FAKE, FAKE) == E
+
+
+def test_tier_validation():
+    c = cfg()
+    E = hga.HGA_ERR_INVALID_ARGUMENT
+    args = (c, FAKE, 14336, 2048, 16384)
+    assert _status(hga.hga_route, *args, FAKE, (FAKE, FAKE, 14400), FAKE, FAKE, FAKE) == E   # split > q_start
+    assert _status(hga.hga_route, *args, FAKE, (None, FAKE, 1024), FAKE, FAKE, FAKE) == E    # host NULL
+    assert _status(hga.hga_route, *args, FAKE, (FAKE, FAKE, 1000), FAKE, FAKE, FAKE) == hga.HGA_ERR_UNSUPPORTED
+    assert _status(hga.hga_attend, *args, (FAKE, FAKE, 1024), (FAKE, FAKE, 2048), FAKE, FAKE, FAKE) == E
+    # tiered K/V needs the staging workspace
+    need = hga.hga_workspace_size(c, 16384, 2048, hga.HGA_WS_ATTEND_TIERED)
+    tier = (FAKE, FAKE, 1024)
+    assert _status(hga.hga_attend, *args, tier, tier, FAKE, FAKE, FAKE, None, None, 0) == hga.HGA_ERR_WORKSPACE
+    assert _status(hga.hga_attend, *args, tier, tier, FAKE, FAKE, FAKE, None, FAKE, need - 1) == \
+        hga.HGA_ERR_WORKSPACE
+
+
+def test_empty_query_range_is_a_no_op():
+    c = cfg()
+    hga.hga_route(c, FAKE, 16384, 0, 16384, FAKE, FAKE, FAKE, FAKE, FAKE)
+    hga.hga_attend(c, FAKE, 16384, 0, 16384, FAKE, FAKE, FAKE, FAKE, FAKE)
+    hga.hga_build_summaries(c, None, 0, None, None)
+    assert hga.hga_last_error() == ""

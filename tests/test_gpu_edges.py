@@ -1,0 +1,117 @@
+"""GPU edge cases against the oracle on small shapes (several tiles, ragged
+routed tiles, degenerate budgets and windows, other GQA ratios, head sizes
+and group sizes, float32, invalid selection entries, empty query range)."""
+import numpy as np
+import pytest
+import torch
+
+import hierarchical_sparse_attention_hga_amd as hga
+import oracle
+import synth
+from harness import DEV, check_outputs, check_routing, gpu_run, hga_cfg, oracle_route, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def small(**kw):
+    base = dict(name="edge", L=1024, n_q=512, hq=8, hkv=2, d=128, dtype="bf16", rope_theta=1e4,
+                chunk=64, group=8, q_block=64, top_chunks=4, top_groups=12, sink=64, local=128,
+                shared_rank=0, shared_scale=0.0, n_plant_chunks=2, groups_per_plant_chunk=1,
+                plant_chunks=(1, 6), alpha=1.0, beta=16.0, tier_split=0, cfg_id=60)
+    base.update(kw)
+    return synth.config(base)
+
+
+CASES = {
+    "base": dict(),
+    "gqa1": dict(hq=2, hkv=2),
+    "gqa2": dict(hq=4, hkv=2),
+    "gqa6": dict(hq=12, hkv=2),
+    "gqa8": dict(hq=16, hkv=2),
+    "d64": dict(d=64),
+    "group4": dict(group=4, top_groups=20),
+    "group16": dict(group=16, top_groups=6),
+    "group64": dict(group=64, top_groups=3),
+    "group1": dict(group=1, top_groups=70),
+    "no_routing": dict(top_chunks=0, top_groups=0),
+    "no_groups": dict(top_groups=0),
+    "no_windows": dict(sink=0, local=0),
+    "ragged13": dict(top_groups=13),
+    "budget_covers_all": dict(top_chunks=16, top_groups=128),
+    "wide_windows": dict(sink=192, local=256),
+    "single_block": dict(n_q=64),
+    "from_zero": dict(L=512, n_q=512),
+    "one_chunk": dict(L=64, n_q=64),
+    "f32_d64": dict(dtype="f32", d=64, rope_theta=None),
+    "f32_d128_g3": dict(dtype="f32", d=128, hq=6, hkv=2, rope_theta=None),
+    "f32_d32_group4": dict(dtype="f32", d=32, group=4, top_groups=9, rope_theta=None),
+    "f32_d4": dict(dtype="f32", d=4, rope_theta=None, n_plant_chunks=0),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_edge_case_end_to_end(name):
+    cfg = small(**CASES[name])
+    print(f"[edge] {name}", flush=True)
+    x = synth.make_inputs(cfg)
+    f = {n: synth.to_f64(x[n], cfg["dtype"]) for n in ("q", "k", "v")}
+    gpu = gpu_run(cfg, x)
+    ref = oracle_route(cfg, f)
+    n, uncert, mism = check_routing(cfg, gpu, ref)
+    assert mism <= uncert
+    items = oracle.all_items(cfg)
+    ro, rl = oracle.attend(cfg, f["q"], f["k"], f["v"], items, ref[1], ref[2][:, 1])
+    check_outputs(cfg, gpu, items, ro, rl)
+
+
+def test_queries_before_the_end_of_the_keys():
+    """q_start + n_q < seq_len: keys past the last query are never read."""
+    cfg = small(L=1024, n_q=256)
+    x = synth.make_inputs(cfg)
+    gpu = gpu_run(cfg, x, q_start=512, seq_len=1024)
+    sub = dict(cfg, L=768)
+    f = {"q": synth.to_f64(x["q"], "bf16"), "k": synth.to_f64(x["k"], "bf16")[:, :768],
+         "v": synth.to_f64(x["v"], "bf16")[:, :768]}
+    ref = oracle_route(sub, f)
+    check_routing(sub, gpu, ref)
+    items = oracle.all_items(sub)
+    ro, rl = oracle.attend(sub, f["q"], f["k"], f["v"], items, ref[1], ref[2][:, 1])
+    check_outputs(sub, gpu, items, ro, rl)
+
+
+def test_invalid_selection_entries_are_skipped():
+    """Negative, duplicate, fixed-chunk and not-yet-closed entries mixed into an
+    ascending selection change nothing."""
+    cfg = small(top_groups=8)
+    x = synth.make_inputs(cfg)
+    f = {n: synth.to_f64(x[n], "bf16") for n in ("q", "k", "v")}
+    ref = oracle_route(cfg, f)
+    nb, hkv = cfg["n_q"] // 64, cfg["hkv"]
+    wide = dict(cfg, top_groups=24)
+    gi = np.full((nb * hkv, 24), -1, np.int32)
+    ns = np.zeros((nb * hkv, 2), np.int32)
+    for n, (b, h) in enumerate(oracle.all_items(cfg)):
+        s = cfg["L"] - cfg["n_q"] + 64 * b
+        row = [-5, 0]                                   # negative; a group of the sink chunk
+        for j in ref[1][n][: ref[2][n, 1]]:
+            row += [int(j), int(j)]                     # duplicates
+        row += [s // 8, s // 8 + 3, 10**6]              # groups not closed before the block
+        gi[n, :len(row)] = row
+        ns[n] = (ref[2][n, 0], len(row))
+    gpu = gpu_run(wide, x, group_idx=gi.reshape(nb, hkv, 24), n_sel=ns.reshape(nb, hkv, 2))
+    items = oracle.all_items(cfg)
+    ro, rl = oracle.attend(cfg, f["q"], f["k"], f["v"], items, ref[1], ref[2][:, 1])
+    check_outputs(cfg, gpu, items, ro, rl)
+
+
+def test_empty_query_range_writes_nothing():
+    cfg = small()
+    x = synth.make_inputs(cfg)
+    c = hga_cfg(cfg)
+    q, k = to_dev(x["q"], "bf16"), to_dev(x["k"], "bf16")
+    out = torch.full_like(q, 3.0)
+    ns = torch.full((1, 2, 2), -7, dtype=torch.int32, device=DEV)
+    hga.hga_route(c, q, 1024, 0, 1024, k, k, ns, ns, ns)
+    hga.hga_attend(c, q, 1024, 0, 1024, k, k, ns, ns, out)
+    torch.cuda.synchronize()
+    assert (ns == -7).all() and (out == 3.0).all()

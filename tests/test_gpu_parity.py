@@ -1,0 +1,105 @@
+"""GPU parity of the HIP path with the CPU oracle, through the C ABI.
+
+Bars: routing index sets bit-exact wherever the oracle certifies the boundary
+(every boundary of the planted workloads is certified); summaries bit-exact
+for bfloat16 keys (their float64 sums are exact, then rounded once) and
+within one float32 ulp for float32 keys; outputs within the tolerances of
+tests/harness.py. Workloads are the five seeded synthetic configurations at
+full size; attention is compared element by element on sampled items.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from harness import check_outputs, check_routing, gpu_run, inputs, oracle_route
+
+pytestmark = pytest.mark.gpu
+
+# items compared element by element per workload (first, last and spread blocks)
+SAMPLE_BLOCKS = {0: None, 1: [0, 1, 2, 31, 62, 63], 2: [0, 13, 31], 3: [0, 40, 63], 4: [0, 31]}
+
+
+def sampled_items(cfg, cfg_id):
+    nb = cfg["n_q"] // 64
+    blocks = SAMPLE_BLOCKS[cfg_id] or list(range(nb))
+    return [(b, h) for b in blocks for h in range(cfg["hkv"])]
+
+
+@pytest.mark.parametrize("cfg_id", [0, 1, 2, 3, 4])
+def test_summaries(cfg_id):
+    cfg, x, f = inputs(cfg_id)
+    print(f"[summaries] {cfg['name']}", flush=True)
+    gpu = gpu_run(cfg, x)
+    gs, cs = oracle.summaries(cfg, f["k"])
+    gs32, cs32 = gs.astype(np.float32), cs.astype(np.float32)
+    if cfg["dtype"] == "bf16":
+        np.testing.assert_array_equal(gpu["gs"], gs32)
+        np.testing.assert_array_equal(gpu["cs"], cs32)
+    else:
+        for a, b in ((gpu["gs"], gs32), (gpu["cs"], cs32)):
+            ulp = np.abs(np.spacing(b))
+            assert (np.abs(a - b) <= ulp).all()
+
+
+@pytest.mark.parametrize("cfg_id", [0, 1, 2, 3, 4])
+def test_routing_and_attention_end_to_end(cfg_id):
+    """GPU route + GPU attend against the oracle's own routing and attention."""
+    cfg, x, f = inputs(cfg_id)
+    print(f"[end-to-end] {cfg['name']}", flush=True)
+    gpu = gpu_run(cfg, x)
+    ref = oracle_route(cfg, f)
+    n, uncert, mism = check_routing(cfg, gpu, ref)
+    assert uncert == 0, f"{uncert} uncertified boundaries in a planted workload"
+    assert mism == 0
+    items = sampled_items(cfg, cfg_id)
+    idx = [b * cfg["hkv"] + h for b, h in items]
+    ro, rl = oracle.attend(cfg, f["q"], f["k"], f["v"], items, ref[1][idx], ref[2][idx, 1])
+    mx, mean, lerr = check_outputs(cfg, gpu, items, ro, rl)
+    print(f"  items={n} max_abs={mx:.3g} mean_abs={mean:.3g} lse={lerr:.3g}", flush=True)
+
+
+@pytest.mark.parametrize("cfg_id", [3, 4])
+def test_host_tier_matches_device_resident(cfg_id):
+    """History K/V and group summaries in pinned host memory (split at the first
+    query): indices and outputs are bit-identical to the all-HBM run."""
+    cfg, x, f = inputs(cfg_id)
+    print(f"[host tier] {cfg['name']} split={cfg['tier_split']}", flush=True)
+    a = gpu_run(cfg, x)
+    b = gpu_run(cfg, x, split=cfg["tier_split"])
+    for key in ("chunk_idx", "group_idx", "n_sel"):
+        np.testing.assert_array_equal(a[key], b[key])
+    np.testing.assert_array_equal(a["out"], b["out"])
+    np.testing.assert_array_equal(a["lse"], b["lse"])
+
+
+def test_host_tier_group_stage_reads_host_summaries():
+    """A tiered run whose group stage must choose (top_groups < groups of the kept
+    chunks), so group summaries are read from pinned host memory."""
+    cfg, x, f = inputs(2)
+    split = 8192
+    print(f"[host tier, choosing group stage] split={split}", flush=True)
+    a = gpu_run(cfg, x)
+    b = gpu_run(cfg, x, split=split)
+    for key in ("chunk_idx", "group_idx", "n_sel", "out", "lse"):
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+def test_deterministic_reruns():
+    cfg, x, f = inputs(2)
+    a = gpu_run(cfg, x)
+    b = gpu_run(cfg, x)
+    for key in ("gs", "cs", "chunk_idx", "group_idx", "n_sel", "out", "lse"):
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+@pytest.mark.parametrize("cfg_id", [1, 2])
+def test_attention_with_oracle_selection(cfg_id):
+    """hga_attend fed the oracle's own selection, compared on sampled items."""
+    cfg, x, f = inputs(cfg_id)
+    ref = oracle_route(cfg, f)
+    nb, hkv = cfg["n_q"] // 64, cfg["hkv"]
+    gpu = gpu_run(cfg, x, group_idx=ref[1].reshape(nb, hkv, -1), n_sel=ref[2].reshape(nb, hkv, 2))
+    items = sampled_items(cfg, cfg_id)
+    idx = [b * hkv + h for b, h in items]
+    ro, rl = oracle.attend(cfg, f["q"], f["k"], f["v"], items, ref[1][idx], ref[2][idx, 1])
+    check_outputs(cfg, gpu, items, ro, rl)
