@@ -45,7 +45,21 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload index (default: the 16K segment)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the 64K lines")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (counter calibration)")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    """A plain copy kernel of known size, to scale the HBM byte counters."""
+    import torch
+    n = mib * 1024 * 1024 // 4
+    src = torch.arange(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4}), flush=True)
 
 
 def algorithmic(cfg, n_sel):
@@ -222,6 +236,9 @@ def main():
         sys.exit(2)
     import torch
     torch.cuda.init()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     cfg, ns, wall, med, mean = measure(args.config, args.steps, args.warmup)
     value = args.steps * cfg["n_q"] / wall
     rl = roofline(cfg, ns, mean[2])

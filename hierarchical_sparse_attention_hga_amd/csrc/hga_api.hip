@@ -72,6 +72,8 @@ hga_status make_shape(const hga_config* cfg, int64_t seq_len, int64_t q_start, i
                 kMaxCand);
   if (cfg->top_groups > kMaxRouted)
     return fail(HGA_ERR_UNSUPPORTED, "top_groups above %d", kMaxRouted);
+  if (cfg->dtype == HGA_BF16 && cfg->top_groups > kMaxRoutedAttn)
+    return fail(HGA_ERR_UNSUPPORTED, "top_groups above %d for bfloat16", kMaxRoutedAttn);
   s->hq = cfg->n_q_heads;
   s->hkv = cfg->n_kv_heads;
   s->G = s->hq / s->hkv;

@@ -37,6 +37,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -97,7 +99,7 @@ __device__ int block_scan(int v, int* lds, int* total) {
 // it is greater than every earlier usable entry of the row, so each token is
 // used once and ascending rows are taken whole.
 __device__ Plan make_plan(const Shape& S, int b, int h, const int32_t* gidx, const int32_t* nsel,
-                          int* runs, int* lds) {
+                          int* runs, int* lds, int cap) {
   Plan P;
   P.s = S.q0 + (int64_t)b * S.B;
   const int64_t ms = P.s / S.c;
@@ -121,11 +123,11 @@ __device__ Plan make_plan(const Shape& S, int b, int h, const int32_t* gidx, con
     const bool ok = usable && j > pm;
     int tot;
     const int pos = block_scan<false>(ok ? 1 : 0, lds, &tot);
-    if (ok && count + pos < kMaxRouted) runs[count + pos] = j * S.g;
+    if (ok && count + pos < cap) runs[count + pos] = j * S.g;
     carry_max = bmax > carry_max ? bmax : carry_max;
     count += tot;
   }
-  P.nrouted = count < kMaxRouted ? count : kMaxRouted;
+  P.nrouted = count < cap ? count : cap;
   const int per_tile = kChunk / S.g;
   P.nrt = (P.nrouted + per_tile - 1) / per_tile;
   P.ntiles = P.nfix + P.nrt + 1;
@@ -178,30 +180,83 @@ __device__ inline void item_of_block(const Shape& S, int wpi, int* b, int* h, in
 }
 
 // ------------------------------------------------------------ bf16 MFMA kernel
+// Token of slot sl of tile t (-1 for an empty slot of the last routed tile).
+// Group sizes divide 64, so they are powers of two: lg = log2(g).
+__device__ inline int slot_token(const Plan& P, const int* runs, int lg, int t, int sl) {
+  if (t < P.nfix) return (int)((t < P.a ? t : P.bb + (t - P.a)) * kChunk) + sl;
+  if (t < P.nfix + P.nrt) {
+    const int run = ((t - P.nfix) << (6 - lg)) + (sl >> lg);
+    return run < P.nrouted ? runs[run] + (sl & ((1 << lg) - 1)) : -1;
+  }
+  return (int)P.s + sl;
+}
+
+// The running max used by the exponentials is raised only when a row's new
+// scores exceed it by more than 2^8 (in the log2 domain): probabilities then
+// stay below 256, exact in float32 and in bfloat16's range, and the O/l
+// rescale runs only when some row of the wave needs it.
+constexpr float kRescaleSlack = 8.0f;
+
+// bfloat16 attention workgroup: 8 waves of 32 query rows (256 rows: the G
+// heads x 64 positions of one item for G = 4). K/V tiles stream through a ring
+// of kAttnStages LDS stages filled by direct global-to-LDS loads, so the
+// gathered rows of the next tiles are in flight while a tile is computed.
+constexpr int kAttnThreads = 512;
+constexpr int kAttnWaves = kAttnThreads / 64;
+constexpr int kAttnStages = 3;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Element offset of the 4 bf16 at (row r, column c, c % 4 == 0) of a tile
+// whose rows hold their 16-byte pieces XOR-swizzled: piece p of row r sits at
+// position p ^ (r % NP).
+template <int D>
+__device__ inline int swz(int r, int c) {
+  constexpr int NP = D / 8;
+  return r * D + ((((c >> 3) ^ (r & (NP - 1))) << 3) | (c & 7));
+}
+
+// Direct global-to-LDS copy of 16 bytes per lane: lane i's 16 bytes at src
+// land at LDS byte address lds_base + 16 i (lds_base uniform across the wave).
+// The instruction writes no register, so the compiler never waits on it; the
+// kernel waits for it itself (s_waitcnt vmcnt) before the barrier that
+// publishes a stage.
+__device__ inline void lds_dma16(const void* src, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "memory", "m0");
+}
+
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 template <int D, bool kStaged>
-__global__ __launch_bounds__(512) void attend_bf16_kernel(AttnArgs A) {
-  constexpr int NT = 512;
-  constexpr int KROW = D + 8;          // bf16 per LDS row of K (16 B pad: conflict-free 16 B reads)
-  constexpr int VROW = kChunk + 4;     // bf16 per LDS row of V^T (8 B pad: conflict-free 8 B reads)
-  constexpr int DP = D / 8;            // 16-byte pieces per token row
-  constexpr int KPT = kChunk * DP / NT;        // K pieces per thread per tile
-  constexpr int VPAIRS = kChunk / 2;           // token pairs per tile
-  constexpr int VTHREADS = VPAIRS * DP;        // threads that load V
-  static_assert(KPT >= 1 && VTHREADS <= NT, "tile shape");
-  __shared__ __align__(16) uint16_t sK[2][kChunk * KROW];
-  __shared__ __align__(16) uint16_t sV[2][D * VROW];
-  __shared__ int sRuns[kMaxRouted];
+__global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(AttnArgs A) {
+  constexpr int NP = D / 8;                   // 16-byte pieces per token row
+  constexpr int RPI = 64 / NP;                // rows per direct-to-LDS wave load
+  constexpr int RPW = kChunk / kAttnWaves;    // rows each wave loads per tile
+  constexpr int KI = RPW / RPI;               // loads per wave per tensor per tile
+  constexpr int kPerTile = 2 * KI;            // K and V
+  static_assert(KI >= 1 && kPerTile <= 15, "tile shape");
+  __shared__ __align__(16) uint16_t sK[kAttnStages][kChunk * D];
+  __shared__ __align__(16) uint16_t sV[kAttnStages][kChunk * D];
+  __shared__ int sRuns[kMaxRoutedAttn];
   __shared__ int sScan[16];
 
   const Shape& S = A.s;
   int b, h, z;
   item_of_block(S, A.wg_per_item, &b, &h, &z);
-  const Plan P = make_plan(S, b, h, A.gidx, A.nsel, sRuns, sScan);
+  const Plan P = make_plan(S, b, h, A.gidx, A.nsel, sRuns, sScan, kMaxRoutedAttn);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5;                  // lane half
   const int col = lane & 31;                 // query column of this lane
-  const int rb = z * 8 + wave;               // 32-row block of the item
+  const int rb = z * kAttnWaves + wave;      // 32-row block of the item
   const bool active = rb < 2 * S.G;
   const int head = h * S.G + (rb >> 1);
   const int qi = (rb & 1) * 32 + col;        // position within the block
@@ -217,59 +272,33 @@ __global__ __launch_bounds__(512) void attend_bf16_kernel(AttnArgs A) {
       qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 16 * ks));
   }
 
-  // tile loader: K as pieces (token sl, 8 dims), V as token pairs (2 sl, 8 dims)
-  u32x4 kreg[KPT], vreg[2];
-  auto load_tile = [&](int t) {
-#pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-      const int p = tid + NT * r, sl = p / DP, dp = p % DP;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (kStaged) {
-        x = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(A.k_stage) +
-                                           ((item_lin * A.tiles_per_item + t) * kChunk + sl) * D + dp * 8);
-      } else {
-        const int64_t tok = tile_token(P, sRuns, S.g, t, sl);
-        if (tok >= 0)
-          x = *reinterpret_cast<const u32x4*>(
-              kv_row<uint16_t>(A.kv.k_host, A.kv.k_dev, A.kv.split, S.L, D, h, tok) + dp * 8);
-      }
-      kreg[r] = x;
-    }
-    if (tid < VTHREADS) {
-      const int sp = tid % VPAIRS, dp = tid / VPAIRS;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int sl = 2 * sp + u;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (kStaged) {
-          x = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(A.v_stage) +
-                                             ((item_lin * A.tiles_per_item + t) * kChunk + sl) * D + dp * 8);
-        } else {
-          const int64_t tok = tile_token(P, sRuns, S.g, t, sl);
-          if (tok >= 0)
-            x = *reinterpret_cast<const u32x4*>(
-                kv_row<uint16_t>(A.kv.v_host, A.kv.v_dev, A.kv.split, S.L, D, h, tok) + dp * 8);
-        }
-        vreg[u] = x;
-      }
-    }
+  const int lg = __ffs(S.g) - 1;
+  const uint16_t* kbase = static_cast<const uint16_t*>(kStaged ? A.k_stage : A.kv.k_dev);
+  const uint16_t* vbase = static_cast<const uint16_t*>(kStaged ? A.v_stage : A.kv.v_dev);
+  if (!kStaged) {
+    kbase += (int64_t)h * S.L * D;
+    vbase += (int64_t)h * S.L * D;
+  }
+  // Row of slot sl of tile t in kbase/vbase. Empty slots read token 0: their
+  // probabilities are exactly zero, so any finite row will do.
+  auto slot_row = [&](int t, int sl) -> int64_t {
+    if (kStaged) return (item_lin * A.tiles_per_item + t) * kChunk + sl;
+    const int tok = slot_token(P, sRuns, lg, t, sl);
+    return tok >= 0 ? tok : 0;
   };
-  auto store_tile = [&](int buf) {
+  // Wave w copies rows [RPW w, RPW w + RPW) of tile t into its stage; each
+  // lane moves one 16-byte piece, written at its swizzled position.
+  const uint32_t k_lds = lds_addr(&sK[0][0]), v_lds = lds_addr(&sV[0][0]);
+  auto issue = [&](int t) {
+    const uint32_t stage_off = (uint32_t)((t % kAttnStages) * kChunk * D * 2);
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-      const int p = tid + NT * r, sl = p / DP, dp = p % DP;
-      *reinterpret_cast<u32x4*>(&sK[buf][sl * KROW + dp * 8]) = kreg[r];
-    }
-    if (tid < VTHREADS) {
-      const int sp = tid % VPAIRS, dp = tid / VPAIRS;
-      uint32_t* vt = reinterpret_cast<uint32_t*>(&sV[buf][0]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t w0 = vreg[0][e >> 1], w1 = vreg[1][e >> 1];
-        const uint32_t lo = (e & 1) ? (w0 >> 16) : (w0 & 0xffffu);
-        const uint32_t hi = (e & 1) ? (w1 & 0xffff0000u) : (w1 << 16);
-        vt[((dp * 8 + e) * VROW + 2 * sp) >> 1] = lo | hi;
-      }
+    for (int i = 0; i < KI; ++i) {
+      const int row0 = wave * RPW + i * RPI;
+      const int rr = row0 + lane / NP;
+      const int piece = (lane % NP) ^ (rr & (NP - 1));
+      const int64_t off = slot_row(t, rr) * D + piece * 8;
+      lds_dma16(kbase + off, k_lds + stage_off + (uint32_t)(row0 * D * 2));
+      lds_dma16(vbase + off, v_lds + stage_off + (uint32_t)(row0 * D * 2));
     }
   };
 
@@ -279,75 +308,99 @@ __global__ __launch_bounds__(512) void attend_bf16_kernel(AttnArgs A) {
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  // lanes' part of the transposed V reads: group of 16 lanes g, lane j in it
+  const int vj = lane & 15, vg = lane >> 4;
+  const int vcol = 16 * (vg & 1) + 4 * (vj & 3);   // + 32 db
+  const int vrow = 4 * hl + (vj >> 2);             // + 32 tb + 16 mm (+ 8)
+
+#pragma unroll
+  for (int t = 0; t < kAttnStages - 1; ++t)
+    if (t < P.ntiles) issue(t);
   for (int t = 0; t < P.ntiles; ++t) {
-    const int cur = t & 1;
-    if (t + 1 < P.ntiles) load_tile(t + 1);
-    if (active) {
-      // S^T = K Q^T: two 32-token blocks
-      f32x16 sacc[2];
+    // this thread's loads of tile t are done once at most one newer tile is pending
+    if (t + 1 < P.ntiles)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kPerTile);   // vmcnt(kPerTile)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
+    __syncthreads();   // every wave's loads of tile t landed; tile t - 1 is free
+    if (t + kAttnStages - 1 < P.ntiles) issue(t + kAttnStages - 1);
+    if (!active) continue;
+    const uint16_t* kt = sK[t % kAttnStages];
+    const uint16_t* vt = sV[t % kAttnStages];
+    // S^T = K Q^T for both 32-token halves of the tile
+    f32x16 sacc[2];
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        sacc[tb] = f32x16{};
-        const uint16_t* kp = &sK[cur][(32 * tb + col) * KROW + 8 * hl];
+    for (int tb = 0; tb < 2; ++tb) {
+      const int r = 32 * tb + col;
+      bf16x8 kf[D / 16];
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + 16 * ks));
-          sacc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[tb], 0, 0, 0);
-        }
-      }
-      // scale, mask, online softmax (this lane: query column qi, 32 tokens)
-      const bool diag = t == P.ntiles - 1;
-      const int lim = tile_limit(P, S.g, t);
-      float mx = -INFINITY;
+      for (int ks = 0; ks < D / 16; ++ks)
+        kf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kt + swz<D>(r, 16 * ks + 8 * hl)));
+      sacc[tb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+        sacc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], sacc[tb], 0, 0, 0);
+    }
+    // masking only on the block's own tile and on a partial routed tile;
+    // slot of accumulator r of half tb: 32 tb + 8 (r >> 2) + 4 hl + (r & 3)
+    const bool diag = t == P.ntiles - 1;
+    const int lim = tile_limit(P, S.g, t);
+    if (diag || lim < kChunk) {
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int slot = 32 * tb + 8 * (r >> 2) + 4 * hl + (r & 3);
-          float zz = sacc[tb][r] * sl2;
-          if (slot >= lim || (diag && slot > qi)) zz = -INFINITY;
-          sacc[tb][r] = zz;
-          mx = fmaxf(mx, zz);
+          if (slot >= lim || (diag && slot > qi)) sacc[tb][r] = -INFINITY;
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
+    }
+    float mx = fmaxf(sacc[0][0], sacc[1][0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(sacc[0][r], sacc[1][r]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+    const bool upd = mx > m_run + kRescaleSlack;
+    if (__ballot(upd)) {
+      const float m_new = upd ? mx : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      float psum = 0.0f;
-      bf16x8 pf[2][2];
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(sacc[tb][r] - m_new);
-          psum += p;
-          pf[tb][r >> 3][r & 7] = (__bf16)p;
-        }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-      // O^T += V^T P^T: token slot of (half hl, element e) in 16-token step mm
-      // of block tb is 32 tb + 16 mm + 4 hl + (e & 3) + 8 (e >> 2)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const uint16_t* vp = &sV[cur][(32 * db + col) * VROW + 4 * hl];
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-          for (int mm = 0; mm < 2; ++mm) {
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(vp + 32 * tb + 16 * mm);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 32 * tb + 16 * mm + 8);
-            const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[tb][mm],
-                                                             o[db], 0, 0, 0);
-          }
-      }
+      m_run = m_new;
     }
-    if (t + 1 < P.ntiles) store_tile(cur ^ 1);
-    __syncthreads();
+    const float neg_m = -m_run;   // finite: the first slot of every tile is visible to every row
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      bf16x8 pf[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[tb][r], sl2, neg_m));
+        l_run += p;
+        pf[r >> 3][r & 7] = (__bf16)p;
+      }
+      // O^T += V^T P^T. The A operand of lane (half hl, column kd) holds V at
+      // tokens 32 tb + 16 mm + 4 hl + {0..3, 8..11}: two transposing LDS reads,
+      // in which lane j of each 16-lane group points at row 4 hl + j / 4 (+ 8)
+      // and columns 16 (g % 2) + 4 (j % 4) .. + 3, and receives its column's
+      // four tokens.
+      bf16x8 vf[D / 32][2];
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          const int r0 = 32 * tb + 16 * mm + vrow, c0 = 32 * db + vcol;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(vt + swz<D>(r0, c0)));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(vt + swz<D>(r0 + 8, c0)));
+          const s16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          vf[db][mm] = __builtin_bit_cast(bf16x8, w);
+        }
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm)
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db][mm], pf[mm], o[db], 0, 0, 0);
+    }
   }
 
   if (active) {
@@ -384,7 +437,7 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttnArgs A) {
   const Shape& S = A.s;
   int b, h, z;
   item_of_block(S, A.wg_per_item, &b, &h, &z);
-  const Plan P = make_plan(S, b, h, A.gidx, A.nsel, sRuns, sScan);
+  const Plan P = make_plan(S, b, h, A.gidx, A.nsel, sRuns, sScan, kMaxRouted);
   const int tid = threadIdx.x;
   const int row = z * ROWS + tid / TPR;       // row of the item: head-local * 64 + qi
   const int part = tid % TPR;
@@ -476,7 +529,7 @@ __global__ __launch_bounds__(256) void gather_kernel(AttnArgs A) {
   const Shape& S = A.s;
   const int64_t item_lin = blockIdx.x;            // h * nb + b
   const int h = (int)(item_lin / S.nb), b = (int)(item_lin % S.nb);
-  const Plan P = make_plan(S, b, h, A.gidx, A.nsel, sRuns, sScan);
+  const Plan P = make_plan(S, b, h, A.gidx, A.nsel, sRuns, sScan, kMaxRouted);
   const int d = S.d;
   constexpr int EPV = 16 / sizeof(T);             // elements per 16-byte piece
   const int pieces = kChunk * d / EPV;
@@ -499,7 +552,7 @@ __global__ __launch_bounds__(256) void gather_kernel(AttnArgs A) {
 
 template <int D, bool kStaged>
 hipError_t launch_bf16(const AttnArgs& a, int64_t items, hipStream_t st) {
-  attend_bf16_kernel<D, kStaged><<<dim3((unsigned)(items * a.wg_per_item)), dim3(512), 0, st>>>(a);
+  attend_bf16_kernel<D, kStaged><<<dim3((unsigned)(items * a.wg_per_item)), dim3(kAttnThreads), 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -550,7 +603,7 @@ hipError_t launch_attend(const Shape& s, const void* q, const KVSrc& kv, const i
     if (e != hipSuccess) return e;
   }
   if (s.dtype == HGA_BF16) {
-    a.wg_per_item = (2 * s.G + 7) / 8;
+    a.wg_per_item = (2 * s.G + kAttnWaves - 1) / kAttnWaves;
     if (s.d == 128) return staged ? launch_bf16<128, true>(a, items, st) : launch_bf16<128, false>(a, items, st);
     if (s.d == 64) return staged ? launch_bf16<64, true>(a, items, st) : launch_bf16<64, false>(a, items, st);
     return hipErrorInvalidValue;

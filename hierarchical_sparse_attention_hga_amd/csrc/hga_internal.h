@@ -14,8 +14,11 @@ namespace hga {
 constexpr int kChunk = 64;
 // Largest number of routing candidates of one stage for one (block, KV head).
 constexpr int kMaxCand = 4096;
-// Largest number of routed groups an attention workgroup keeps in LDS.
+// Largest number of routed groups per (block, KV head) the library accepts.
 constexpr int kMaxRouted = 4096;
+// Routed groups the bfloat16 attention workgroup keeps in LDS (bounds
+// top_groups for bfloat16).
+constexpr int kMaxRoutedAttn = 2048;
 // Most chunks the router may keep per item (LDS list of the group stage).
 constexpr int kMaxKeptChunks = 2048;
 
