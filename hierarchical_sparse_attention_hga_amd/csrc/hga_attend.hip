@@ -207,14 +207,18 @@ constexpr int kAttnStages = 3;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// Element offset of the 4 bf16 at (row r, column c, c % 4 == 0) of a tile
-// whose rows hold their 16-byte pieces XOR-swizzled: piece p of row r sits at
-// position p ^ (r % NP).
+// Tiles live in LDS row-major (one token row of D bf16 per row) with the
+// 16-byte pieces of each row permuted by XOR:
+//   K: piece p of row r at position p ^ (r % NP). The QK^T reads take one
+//      piece from 16 consecutive rows at once: all 16 positions differ.
+//   V: piece p of row r at position p ^ (4 (r % 4) % NP). The transposing reads
+//      take an aligned block of 4 pieces from 4 consecutive rows at once: the
+//      4 rows land in 4 different blocks.
+// Both keep every LDS read of the tile loop free of bank conflicts.
 template <int D>
-__device__ inline int swz(int r, int c) {
-  constexpr int NP = D / 8;
-  return r * D + ((((c >> 3) ^ (r & (NP - 1))) << 3) | (c & 7));
-}
+__device__ inline int k_swizzle(int r) { return r & (D / 8 - 1); }
+template <int D>
+__device__ inline int v_swizzle(int r) { return ((r & 3) << 2) & (D / 8 - 1); }
 
 // Direct global-to-LDS copy of 16 bytes per lane: lane i's 16 bytes at src
 // land at LDS byte address lds_base + 16 i (lds_base uniform across the wave).
@@ -295,10 +299,9 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(AttnArgs A) {
     for (int i = 0; i < KI; ++i) {
       const int row0 = wave * RPW + i * RPI;
       const int rr = row0 + lane / NP;
-      const int piece = (lane % NP) ^ (rr & (NP - 1));
-      const int64_t off = slot_row(t, rr) * D + piece * 8;
-      lds_dma16(kbase + off, k_lds + stage_off + (uint32_t)(row0 * D * 2));
-      lds_dma16(vbase + off, v_lds + stage_off + (uint32_t)(row0 * D * 2));
+      const int64_t row = slot_row(t, rr) * D;
+      lds_dma16(kbase + row + ((lane % NP) ^ k_swizzle<D>(rr)) * 8, k_lds + stage_off + (uint32_t)(row0 * D * 2));
+      lds_dma16(vbase + row + ((lane % NP) ^ v_swizzle<D>(rr)) * 8, v_lds + stage_off + (uint32_t)(row0 * D * 2));
     }
   };
 
@@ -308,10 +311,30 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(AttnArgs A) {
 #pragma unroll
   for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
 
-  // lanes' part of the transposed V reads: group of 16 lanes g, lane j in it
-  const int vj = lane & 15, vg = lane >> 4;
-  const int vcol = 16 * (vg & 1) + 4 * (vj & 3);   // + 32 db
-  const int vrow = 4 * hl + (vj >> 2);             // + 32 tb + 16 mm (+ 8)
+  // Per-lane byte offsets of the tile-loop LDS reads inside a stage. K: lane
+  // (col, hl) reads piece 2 ks + hl of row col (+ 32 for the second half).
+  // V (transposing reads): lane j of 16-lane group g points at row
+  // vrow = 4 hl + j / 4 (+ 32 tb + 16 mm, + 8 for the upper four tokens) and
+  // columns vcol = 16 (g % 2) + 4 (j % 4) (+ 32 db), and receives its column's
+  // four tokens. The row additions are multiples of 4 and leave both swizzles
+  // unchanged, so they fold into the instructions' constant offsets.
+  constexpr int RB = D * 2;                        // bytes per LDS row
+  uint32_t koff[D / 16], voff[D / 32];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    koff[ks] = (uint32_t)(col * RB + (((2 * ks + hl) ^ k_swizzle<D>(col)) << 4));
+  {
+    const int vj = lane & 15, vg = lane >> 4;
+    const int vcol = 16 * (vg & 1) + 4 * (vj & 3);
+    const int vrow = 4 * hl + (vj >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int c = 32 * db + vcol;
+      voff[db] = (uint32_t)(vrow * RB + ((((c >> 3) ^ v_swizzle<D>(vrow))) << 4) + ((c & 7) << 1));
+    }
+  }
+  const char* sKb = reinterpret_cast<const char*>(&sK[0][0]);
+  const char* sVb = reinterpret_cast<const char*>(&sV[0][0]);
 
 #pragma unroll
   for (int t = 0; t < kAttnStages - 1; ++t)
@@ -325,17 +348,17 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(AttnArgs A) {
     __syncthreads();   // every wave's loads of tile t landed; tile t - 1 is free
     if (t + kAttnStages - 1 < P.ntiles) issue(t + kAttnStages - 1);
     if (!active) continue;
-    const uint16_t* kt = sK[t % kAttnStages];
-    const uint16_t* vt = sV[t % kAttnStages];
+    const uint32_t stage = (uint32_t)((t % kAttnStages) * kChunk * RB);
+    const char* kt = sKb + stage;
+    const char* vt = sVb + stage;
     // S^T = K Q^T for both 32-token halves of the tile
     f32x16 sacc[2];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      const int r = 32 * tb + col;
       bf16x8 kf[D / 16];
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks)
-        kf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kt + swz<D>(r, 16 * ks + 8 * hl)));
+        kf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kt + koff[ks] + 32 * tb * RB));
       sacc[tb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks)
@@ -356,7 +379,7 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(AttnArgs A) {
     }
     float mx = fmaxf(sacc[0][0], sacc[1][0]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(sacc[0][r], sacc[1][r]));
+    for (int r = 1; r < 16; ++r) mx = __builtin_fmaxf(__builtin_fmaxf(mx, sacc[0][r]), sacc[1][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
     const bool upd = mx > m_run + kRescaleSlack;
     if (__ballot(upd)) {
@@ -378,20 +401,16 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(AttnArgs A) {
         pf[r >> 3][r & 7] = (__bf16)p;
       }
       // O^T += V^T P^T. The A operand of lane (half hl, column kd) holds V at
-      // tokens 32 tb + 16 mm + 4 hl + {0..3, 8..11}: two transposing LDS reads,
-      // in which lane j of each 16-lane group points at row 4 hl + j / 4 (+ 8)
-      // and columns 16 (g % 2) + 4 (j % 4) .. + 3, and receives its column's
-      // four tokens.
+      // tokens 32 tb + 16 mm + 4 hl + {0..3, 8..11}: two transposing reads.
       bf16x8 vf[D / 32][2];
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
-          const int r0 = 32 * tb + 16 * mm + vrow, c0 = 32 * db + vcol;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(vt + swz<D>(r0, c0)));
+          const char* vp = vt + voff[db] + (32 * tb + 16 * mm) * RB;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)vp);
           const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(vt + swz<D>(r0 + 8, c0)));
+              (__attribute__((address_space(3))) s16x4*)(vp + 8 * RB));
           const s16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           vf[db][mm] = __builtin_bit_cast(bf16x8, w);
         }
