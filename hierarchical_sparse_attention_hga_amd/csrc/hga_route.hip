@@ -1,25 +1,28 @@
 // Two-level HGA router ("Long-Context Fine-Tuning with Limited VRAM",
 // section 2.1, "Chunk selection" and "Group selection").
 //
-// One 512-thread workgroup routes one (query block, KV head) item:
+// One 512-thread workgroup routes one (query block, KV head) item. Every
+// phase is a chain of dependent memory round trips, so each issues all of
+// its loads before using any:
 //   1. block query: mean of the block's queries over its 64 positions and the
 //      G query heads of the KV head, accumulated in float64 (exact for
-//      bfloat16 inputs, so independent of the summation order); every thread
-//      issues all of its 16-byte row loads before adding;
+//      bfloat16 inputs, so independent of the summation order);
 //   2. chunk stage: the candidates are the closed chunks before the block
-//      that are neither sink nor local (a contiguous range); each score is the
-//      float64 dot of the block query with the float32 chunk summary, eight
-//      lanes per candidate, two candidates per lane group in flight;
-//   3. exact top-k by an 8-pass radix select (8 bits per pass, MSB first) on
-//      64-bit order keys (ascending key = descending score): it finds the k-th
-//      key T; the kept set is every key below T plus the first keys equal to
-//      T in candidate order, which is the lower-index tie rule because
-//      candidates are laid out in ascending index order. A block-wide scan
-//      then compacts the kept positions, so the output is ascending;
-//   4. group stage: the groups of the kept chunks (ascending) are scored the
-//      same way against the group summaries (device or pinned host memory)
-//      and selected the same way; when the budget covers every group of the
-//      kept chunks, all are kept and their summaries are never read.
+//      that are neither sink nor local, a range [lo, hi); eight lanes score a
+//      summary row (four rows per lane group in flight), each score the
+//      float64 dot of the block query with the float32 chunk summary, stored
+//      as a 64-bit order key (ascending key = descending score);
+//   3. exact top-k by one wave with no block barrier: an 8-pass
+//      radix select (8 bits per pass, MSB first, stopping as soon as the
+//      boundary bucket is taken whole) finds the k-th key T; the kept set is
+//      every key below T plus the first keys equal to T in candidate order,
+//      which is the lower-index tie rule because candidates are laid out in
+//      ascending index order; a wave scan compacts the kept positions, so
+//      the output is ascending;
+//   4. group stage: the groups of the kept chunks (ascending) are
+//      scored the same way against the group summaries (device or pinned host
+//      memory) and selected the same way; when the budget covers every group
+//      of the kept chunks, all are kept and their summaries are never read.
 // Outputs are ascending and -1 padded.
 #include "hga_internal.h"
 
@@ -29,6 +32,7 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kLanesPerCand = 8;
+constexpr int kRowsInFlight = 4;   // summary rows per lane group per round
 
 template <typename T>
 struct Slice;  // one 16-byte slice of a query row
@@ -64,38 +68,101 @@ __device__ inline unsigned long long order_key(double sc) {
 }
 
 struct RouteSmem {
-  unsigned long long key[kMaxCand];    // order keys; also stages block-query partial sums
-  int chunks[kMaxKeptChunks];          // kept chunks, ascending
-  int hist[256];
-  int scan[kWaves];
-  int misc[2];
+  unsigned long long key[kMaxCand];      // order keys; also stages block-query partial sums
+  int chunks[kMaxKeptChunks];            // kept chunks, ascending
+  int hist[256];                         // radix histogram of the selecting wave
   double qbar[128];
 };
 
-// Block-wide exclusive prefix sum of one int per thread; *total gets the sum.
-__device__ int block_exclusive_sum(int v, int* scan, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Wave-level exclusive prefix sum; *total gets the wave's sum.
+__device__ inline int wave_exclusive_sum(int v, int* total) {
+  const int lane = threadIdx.x & 63;
   int x = v;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const int y = __shfl_up(x, off);
     if (lane >= off) x += y;
   }
-  if (lane == 63) scan[wave] = x;
-  __syncthreads();
-  int pre = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const int t = scan[w];
-    pre += w < wave ? t : 0;
-    tot += t;
-  }
-  __syncthreads();
-  *total = tot;
-  return pre + x - v;
+  *total = __shfl(x, 63);
+  return x - v;
 }
 
-// Score candidates c in [0, n): row(c) points at d float32 values.
+// One wave keeps the k smallest of key[0..n) in (key, position) order
+// (0 < k < n) and calls emit(rank, position) for each kept position, ranks
+// ascending with the position. hist is a 256-bin array private to the wave.
+template <typename EmitFn>
+__device__ void wave_select(const unsigned long long* key, int n, int k, int* hist, EmitFn emit) {
+  const int lane = threadIdx.x & 63;
+  unsigned long long prefix = 0ull, mask = 0ull;
+  int kk = k;
+  for (int pass = 0; pass < 8; ++pass) {
+    const int shift = 56 - 8 * pass;
+    for (int i = lane; i < 256; i += 64) hist[i] = 0;
+    for (int base = 0; base < n; base += 64) {
+      const int i = base + lane;
+      unsigned long long x = 0ull;
+      bool act = false;
+      if (i < n) {
+        x = key[i];
+        act = (x & mask) == prefix;
+      }
+      const int dg = (int)((x >> shift) & 255);
+      const unsigned long long am = __ballot(act);
+      if (am) {
+        // a wave whose matching keys share one digit adds them in one atomic
+        const int first = __ffsll(am) - 1;
+        const int d0 = __shfl(dg, first);
+        if (__ballot(act && dg == d0) == am) {
+          if (lane == first) atomicAdd(&hist[d0], __popcll(am));
+        } else if (act) {
+          atomicAdd(&hist[dg], 1);
+        }
+      }
+    }
+    // the bucket holding the kk-th smallest matching key
+    const int h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+    const int sum = h0 + h1 + h2 + h3;
+    int tot;
+    const int excl = wave_exclusive_sum(sum, &tot);
+    const bool mine = excl < kk && kk <= excl + sum;
+    int r = kk - excl, dg = 4 * lane, cnt = h0;
+    if (r > h0) { r -= h0; ++dg; cnt = h1; if (r > h1) { r -= h1; ++dg; cnt = h2; if (r > h2) { r -= h2; ++dg; cnt = h3; } } }
+    const int owner = __ffsll(__ballot(mine)) - 1;
+    dg = __shfl(dg, owner);
+    r = __shfl(r, owner);
+    cnt = __shfl(cnt, owner);
+    prefix |= (unsigned long long)dg << shift;
+    mask |= 255ull << shift;
+    kk = r;
+    if (kk == cnt) break;   // the whole bucket is kept: no finer digit is needed
+  }
+  // kept: masked key below the prefix, or equal to it among the first kk by position
+  const int per = (n + 63) / 64;
+  const int lo = lane * per, hi = lo + per < n ? lo + per : n;
+  int eq = 0, kept = 0;
+  for (int i = lo; i < hi; ++i) eq += (key[i] & mask) == prefix;
+  int tot;
+  const int eq_before = wave_exclusive_sum(eq, &tot);
+  {
+    int e = eq_before;
+    for (int i = lo; i < hi; ++i) {
+      const unsigned long long x = key[i] & mask;
+      if (x < prefix || (x == prefix && e++ < kk)) ++kept;
+    }
+  }
+  int rank = wave_exclusive_sum(kept, &tot);
+  {
+    int e = eq_before;
+    for (int i = lo; i < hi; ++i) {
+      const unsigned long long x = key[i] & mask;
+      if (x < prefix || (x == prefix && e++ < kk)) emit(rank++, i);
+    }
+  }
+}
+
+// Score summary rows c in [0, n) against the block query: row(c) points at d
+// float32 values; the order key goes to key[c]. Eight lanes per row,
+// kRowsInFlight rows per lane group per round, all loads issued first.
 template <typename RowFn>
 __device__ void score_rows(const double* qbar, int d, int n, RowFn row, unsigned long long* key) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -103,97 +170,37 @@ __device__ void score_rows(const double* qbar, int d, int n, RowFn row, unsigned
   constexpr int per_wave = 64 / kLanesPerCand;
   constexpr int per_round = kWaves * per_wave;
   const int quads = d / 4;
-  for (int base = 0; base < n; base += 2 * per_round) {
-    const int c0 = base + wave * per_wave + sub, c1 = c0 + per_round;
-    double a0 = 0.0, a1 = 0.0;
-    const float* r0 = c0 < n ? row(c0) : nullptr;
-    const float* r1 = c1 < n ? row(c1) : nullptr;
+  for (int base = 0; base < n; base += kRowsInFlight * per_round) {
+    int c[kRowsInFlight];
+    const float* r[kRowsInFlight];
+    double acc[kRowsInFlight];
+#pragma unroll
+    for (int u = 0; u < kRowsInFlight; ++u) {
+      c[u] = base + u * per_round + wave * per_wave + sub;
+      r[u] = c[u] < n ? row(c[u]) : nullptr;
+      acc[u] = 0.0;
+    }
     for (int q4 = lic; q4 < quads; q4 += kLanesPerCand) {
-      float4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
-      if (r0) v0 = *reinterpret_cast<const float4*>(r0 + 4 * q4);
-      if (r1) v1 = *reinterpret_cast<const float4*>(r1 + 4 * q4);
-      const double* qb = qbar + 4 * q4;
-      a0 += qb[0] * (double)v0.x; a0 += qb[1] * (double)v0.y; a0 += qb[2] * (double)v0.z; a0 += qb[3] * (double)v0.w;
-      a1 += qb[0] * (double)v1.x; a1 += qb[1] * (double)v1.y; a1 += qb[2] * (double)v1.z; a1 += qb[3] * (double)v1.w;
-    }
+      float4 v[kRowsInFlight];
 #pragma unroll
-    for (int off = kLanesPerCand / 2; off > 0; off >>= 1) {
-      a0 += __shfl_xor(a0, off, kLanesPerCand);
-      a1 += __shfl_xor(a1, off, kLanesPerCand);
-    }
-    if (lic == 0) {
-      if (c0 < n) key[c0] = order_key(a0);
-      if (c1 < n) key[c1] = order_key(a1);
-    }
-  }
-}
-
-// Keep the k smallest of key[0..n) in (key, position) order (0 < k < n) and
-// call emit(rank, position) for each kept position, ranks ascending with the
-// position. Ends with a barrier.
-template <typename EmitFn>
-__device__ void select_smallest(const unsigned long long* key, int n, int k, RouteSmem& sm, EmitFn emit) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  unsigned long long prefix = 0ull, mask = 0ull;
-  int kk = k;
-  for (int pass = 0; pass < 8; ++pass) {
-    const int shift = 56 - 8 * pass;
-    for (int i = tid; i < 256; i += kThreads) sm.hist[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += kThreads) {
-      const unsigned long long x = key[i];
-      if ((x & mask) == prefix) atomicAdd(&sm.hist[(x >> shift) & 255], 1);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      const int h0 = sm.hist[4 * lane], h1 = sm.hist[4 * lane + 1];
-      const int h2 = sm.hist[4 * lane + 2], h3 = sm.hist[4 * lane + 3];
-      const int sum = h0 + h1 + h2 + h3;
-      int incl = sum;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
+      for (int u = 0; u < kRowsInFlight; ++u) {
+        v[u] = float4{0.f, 0.f, 0.f, 0.f};
+        if (r[u]) v[u] = *reinterpret_cast<const float4*>(r[u] + 4 * q4);
       }
-      const int excl = incl - sum;
-      if (excl < kk && kk <= incl) {
-        int r = kk - excl, dg = 4 * lane;
-        if (r > h0) { r -= h0; ++dg; if (r > h1) { r -= h1; ++dg; if (r > h2) { r -= h2; ++dg; } } }
-        sm.misc[0] = dg;
-        sm.misc[1] = r;
+      const double q0 = qbar[4 * q4], q1 = qbar[4 * q4 + 1], q2 = qbar[4 * q4 + 2], q3 = qbar[4 * q4 + 3];
+#pragma unroll
+      for (int u = 0; u < kRowsInFlight; ++u) {
+        acc[u] += q0 * (double)v[u].x; acc[u] += q1 * (double)v[u].y;
+        acc[u] += q2 * (double)v[u].z; acc[u] += q3 * (double)v[u].w;
       }
     }
-    __syncthreads();
-    prefix |= (unsigned long long)sm.misc[0] << shift;
-    mask |= 255ull << shift;
-    kk = sm.misc[1];
-    __syncthreads();
-  }
-  // kept: key < T, or key == T among the first kk such keys by position
-  const unsigned long long T = prefix;
-  const int per = (n + kThreads - 1) / kThreads;
-  const int lo = tid * per, hi = lo + per < n ? lo + per : n;
-  int eq = 0;
-  for (int i = lo; i < hi; ++i) eq += key[i] == T;
-  int tot;
-  int eq_before = block_exclusive_sum(eq, sm.scan, &tot);
-  int kept = 0;
-  {
-    int e = eq_before;
-    for (int i = lo; i < hi; ++i) {
-      const unsigned long long x = key[i];
-      if (x < T || (x == T && e++ < kk)) ++kept;
+#pragma unroll
+    for (int u = 0; u < kRowsInFlight; ++u) {
+#pragma unroll
+      for (int off = kLanesPerCand / 2; off > 0; off >>= 1) acc[u] += __shfl_xor(acc[u], off, kLanesPerCand);
+      if (lic == 0 && c[u] < n) key[c[u]] = order_key(acc[u]);
     }
   }
-  int rank = block_exclusive_sum(kept, sm.scan, &tot);
-  {
-    int e = eq_before;
-    for (int i = lo; i < hi; ++i) {
-      const unsigned long long x = key[i];
-      if (x < T || (x == T && e++ < kk)) emit(rank++, i);
-    }
-  }
-  __syncthreads();
 }
 
 struct RouteArgs {
@@ -212,46 +219,48 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   __shared__ RouteSmem sm;
   constexpr int E = Slice<T>::E;
+  constexpr int kRowsPerThread = 8;   // block-query rows loaded per thread per round
   const Shape& S = a.s;
-  const int b = blockIdx.x / S.hkv;
-  const int h = blockIdx.x % S.hkv;
+  // the workgroups of one KV head stay on one XCD (block id x runs on XCD
+  // x % 8), so its summaries stay in that XCD's L2
+  const int nwg = (int)(S.nb * S.hkv);
+  int lid = blockIdx.x;
+  if (nwg % 8 == 0) lid = (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8;
+  const int h = lid / (int)S.nb;
+  const int b = lid % (int)S.nb;
   const int d = S.d;
   const int64_t s = S.q0 + (int64_t)b * S.B;
   const int64_t ms = s / S.c;
   const int gpc = S.c / S.g;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   // ---- 1. block query (float64)
   {
-    const int P = d / E;                   // 16-byte slices per row
+    const int P = d / E;                       // 16-byte slices per row
     const int phases = kThreads / P;
     const int p = tid % P, ph = tid / P;
     double* part = reinterpret_cast<double*>(sm.key);   // [phases][d]
     const int nrows = S.G * S.B;
+    const T* qbase = static_cast<const T*>(a.q);
     double acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.0;
-    const T* qbase = static_cast<const T*>(a.q);
-    int r = ph;
-    for (; r + 3 * phases < nrows; r += 4 * phases) {
-      uint4 v[4];
+    for (int r = ph; r < nrows; r += kRowsPerThread * phases) {
+      uint4 v[kRowsPerThread];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kRowsPerThread; ++u) {
         const int rr = r + u * phases;
-        const int64_t row = (int64_t)(h * S.G + rr / S.B) * S.nq + (s - S.q0) + rr % S.B;
-        v[u] = *reinterpret_cast<const uint4*>(qbase + row * d + p * E);
+        v[u] = uint4{0u, 0u, 0u, 0u};
+        if (rr < nrows) {
+          const int64_t row = (int64_t)(h * S.G + rr / S.B) * S.nq + (s - S.q0) + rr % S.B;
+          v[u] = *reinterpret_cast<const uint4*>(qbase + row * d + p * E);
+        }
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) Slice<T>::add(v[u], acc);
+      for (int u = 0; u < kRowsPerThread; ++u) Slice<T>::add(v[u], acc);
     }
-    for (; r < nrows; r += phases) {
-      const int64_t row = (int64_t)(h * S.G + r / S.B) * S.nq + (s - S.q0) + r % S.B;
-      Slice<T>::add(*reinterpret_cast<const uint4*>(qbase + row * d + p * E), acc);
-    }
-    if (ph < phases) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) part[ph * d + p * E + e] = acc[e];
-    }
+    for (int e = 0; e < E; ++e) part[ph * d + p * E + e] = acc[e];
     __syncthreads();
     if (tid < d) {
       double t = 0.0;
@@ -271,11 +280,11 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
     const float* csh = a.cs + (int64_t)h * (S.L / S.c) * d;
     score_rows(sm.qbar, d, ncand, [&](int c) { return csh + (lo + c) * d; }, sm.key);
     __syncthreads();
-    select_smallest(sm.key, ncand, nsc, sm, [&](int rank, int pos) { sm.chunks[rank] = (int)(lo + pos); });
+    if (wave == 0) wave_select(sm.key, ncand, nsc, sm.hist, [&](int rank, int pos) { sm.chunks[rank] = (int)(lo + pos); });
   } else {
     for (int i = tid; i < nsc; i += kThreads) sm.chunks[i] = (int)(lo + i);
-    __syncthreads();
   }
+  __syncthreads();
   for (int i = tid; i < S.kc; i += kThreads) a.chunk_idx[orow * S.kc + i] = i < nsc ? sm.chunks[i] : -1;
 
   // ---- 4. group stage over the groups of the kept chunks (ascending order)
@@ -292,7 +301,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
                         : a.gs_dev + ((int64_t)h * (ngl - gsplit) + (j - gsplit)) * d;
     }, sm.key);
     __syncthreads();
-    select_smallest(sm.key, ngc, nsg, sm, [&](int rank, int pos) { gout[rank] = group_of(pos); });
+    if (wave == 0) wave_select(sm.key, ngc, nsg, sm.hist, [&](int rank, int pos) { gout[rank] = group_of(pos); });
   } else {
     for (int i = tid; i < nsg; i += kThreads) gout[i] = group_of(i);
   }
