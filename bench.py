@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload index (default: the 16K segment)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the 64K lines")
+    ap.add_argument("--traffic-kib", type=float, nargs=2, default=None, metavar=("FETCH", "WRITE"),
+                    help="attention kernel FETCH_SIZE and WRITE_SIZE per dispatch (KiB, as rocprofv3 "
+                         "reports them) for the roofline traffic field")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (counter calibration)")
     return ap.parse_args()
@@ -178,43 +181,59 @@ class Workload:
             p.free()
 
 
+def measured_traffic(workload):
+    """HBM bytes per attention launch from the committed rocprofv3 counter runs
+    (profiles/attend_bf16_<workload>.traffic.json), or None when they are
+    missing or were taken on different attention kernel sources."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"attend_bf16_{workload}.traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = b"".join(open(os.path.join(ROOT, "hierarchical_sparse_attention_hga_amd", "csrc", f), "rb").read()
+                   for f in ("hga_attend.hip", "hga_internal.h"))
+    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+        return None
+    return 1024.0 * (rec["fetch_kib"] * rec["fetch_factor"] + rec["write_kib"] * rec["write_factor"])
+
+
 def roofline(cfg, n_sel, attend_us):
     flops, byts, _ = algorithmic(cfg, n_sel)
+    traffic = measured_traffic(cfg["name"])
     t_mfma = flops / PEAK_BF16
     t_hbm = byts / PEAK_HBM
     t = attend_us * 1e-6
     if t_mfma >= t_hbm:
         return {"bound": "mfma", "achieved": flops / t / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
-                "frac": flops / t / PEAK_BF16, "traffic": None,
+                "frac": flops / t / PEAK_BF16, "traffic": traffic, "traffic_unit": "HBM bytes per launch",
                 "algorithmic_flops": flops, "algorithmic_bytes": byts}
     return {"bound": "hbm", "achieved": byts / t / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-            "frac": byts / t / PEAK_HBM, "traffic": None,
+            "frac": byts / t / PEAK_HBM, "traffic": traffic, "traffic_unit": "HBM bytes per launch",
             "algorithmic_flops": flops, "algorithmic_bytes": byts}
 
 
-def cpu_baseline(cfg_id):
-    """The oracle on a bounded sample: summaries of every key, then routing and
-    attention of a few query blocks for every KV head, scaled to the layer."""
+def cpu_baseline(cfg_id, min_seconds=10.0):
+    """The oracle timed on the host cores: summaries, routing and attention of
+    every (block, KV head) of the layer, repeated until at least min_seconds
+    of CPU work have run."""
     import oracle
     import synth
     cfg = synth.config(cfg_id)
     x = synth.make_inputs(cfg)
     f = {n: synth.to_f64(x[n], cfg["dtype"]) for n in ("q", "k", "v")}
-    nb = cfg["n_q"] // 64
-    blocks = [nb - 1] if cfg_id >= 3 else [0, nb - 1]
-    items = [(b, h) for b in blocks for h in range(cfg["hkv"])]
-    t0 = time.perf_counter()
-    sums = (oracle.summaries(cfg, f["k"]), oracle.abs_summaries(cfg, f["k"]))
-    t1 = time.perf_counter()
-    ci, gi, ns, dg = oracle.route(cfg, f["q"], f["k"], items, sums=sums)
-    oracle.attend(cfg, f["q"], f["k"], f["v"], items, gi, ns[:, 1])
-    t2 = time.perf_counter()
-    per_layer = (t1 - t0) + (t2 - t1) * nb / len(blocks)
-    return {"value": cfg["n_q"] / per_layer, "unit": "query-tokens/s", "cores": oracle.threads(),
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        sums = (oracle.summaries(cfg, f["k"]), oracle.abs_summaries(cfg, f["k"]))
+        ci, gi, ns, dg = oracle.route(cfg, f["q"], f["k"], sums=sums)
+        oracle.attend(cfg, f["q"], f["k"], f["v"], oracle.all_items(cfg), gi, ns[:, 1])
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": reps * cfg["n_q"] / el, "unit": "query-tokens/s", "cores": oracle.threads(),
             "kind": "oracle",
-            "sample": f"float64 C oracle: summaries of all {cfg['L']} keys ({t1 - t0:.2f} s), then routing "
-                      f"and attention of query blocks {blocks} for all {cfg['hkv']} KV heads "
-                      f"({t2 - t1:.2f} s), scaled to the {nb} blocks of the layer"}
+            "sample": f"float64 C oracle, whole layer ({cfg['n_q']} queries, all {cfg['hkv']} KV heads: "
+                      f"summaries, routing, attention) repeated {reps}x in {el:.1f} s"}
 
 
 def measure(cfg_id, steps, warmup, split=0):
