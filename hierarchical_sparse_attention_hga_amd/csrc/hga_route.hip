@@ -12,13 +12,13 @@
 //      summary row (four rows per lane group in flight), each score the
 //      float64 dot of the block query with the float32 chunk summary, stored
 //      as a 64-bit order key (ascending key = descending score);
-//   3. exact top-k by one wave with no block barrier: an 8-pass
-//      radix select (8 bits per pass, MSB first, stopping as soon as the
-//      boundary bucket is taken whole) finds the k-th key T; the kept set is
-//      every key below T plus the first keys equal to T in candidate order,
+//   3. exact top-k by one wave with no block barrier, keys in registers: an
+//      8-pass radix select (8 bits per pass, MSB first, stopping as soon as
+//      the boundary bucket is taken whole) finds the k-th key T; the kept set
+//      is every key below T plus the first keys equal to T in candidate order,
 //      which is the lower-index tie rule because candidates are laid out in
-//      ascending index order; a wave scan compacts the kept positions, so
-//      the output is ascending;
+//      ascending index order; ranks from ballots compact the kept positions,
+//      so the output is ascending;
 //   4. group stage: the groups of the kept chunks (ascending) are
 //      scored the same way against the group summaries (device or pinned host
 //      memory) and selected the same way; when the budget covers every group
@@ -88,25 +88,26 @@ __device__ inline int wave_exclusive_sum(int v, int* total) {
 }
 
 // One wave keeps the k smallest of key[0..n) in (key, position) order
-// (0 < k < n) and calls emit(rank, position) for each kept position, ranks
-// ascending with the position. hist is a 256-bin array private to the wave.
-template <typename EmitFn>
-__device__ void wave_select(const unsigned long long* key, int n, int k, int* hist, EmitFn emit) {
+// (0 < k < n <= 64 KPL) and calls emit(rank, position) for each kept
+// position, ranks ascending with the position. Lane l holds the keys at
+// positions l + 64 j in registers; hist is a 256-bin array private to the wave.
+template <int KPL, typename EmitFn>
+__device__ void wave_select_kpl(const unsigned long long* key, int n, int k, int* hist, EmitFn emit) {
   const int lane = threadIdx.x & 63;
+  const unsigned long long lt = (1ull << lane) - 1ull;   // lanes below this one
+  unsigned long long x[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) x[j] = lane + 64 * j < n ? key[lane + 64 * j] : ~0ull;
+  auto valid = [&](int j) { return lane + 64 * j < n; };
   unsigned long long prefix = 0ull, mask = 0ull;
   int kk = k;
   for (int pass = 0; pass < 8; ++pass) {
     const int shift = 56 - 8 * pass;
-    for (int i = lane; i < 256; i += 64) hist[i] = 0;
-    for (int base = 0; base < n; base += 64) {
-      const int i = base + lane;
-      unsigned long long x = 0ull;
-      bool act = false;
-      if (i < n) {
-        x = key[i];
-        act = (x & mask) == prefix;
-      }
-      const int dg = (int)((x >> shift) & 255);
+    *reinterpret_cast<int4*>(&hist[4 * lane]) = int4{0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const bool act = valid(j) && (x[j] & mask) == prefix;
+      const int dg = (int)((x[j] >> shift) & 255);
       const unsigned long long am = __ballot(act);
       if (am) {
         // a wave whose matching keys share one digit adds them in one atomic
@@ -120,13 +121,18 @@ __device__ void wave_select(const unsigned long long* key, int n, int k, int* hi
       }
     }
     // the bucket holding the kk-th smallest matching key
-    const int h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
-    const int sum = h0 + h1 + h2 + h3;
-    int tot;
-    const int excl = wave_exclusive_sum(sum, &tot);
-    const bool mine = excl < kk && kk <= excl + sum;
-    int r = kk - excl, dg = 4 * lane, cnt = h0;
-    if (r > h0) { r -= h0; ++dg; cnt = h1; if (r > h1) { r -= h1; ++dg; cnt = h2; if (r > h2) { r -= h2; ++dg; cnt = h3; } } }
+    const int4 hv = *reinterpret_cast<const int4*>(&hist[4 * lane]);
+    const int sum = hv.x + hv.y + hv.z + hv.w;
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    const int excl = incl - sum;
+    const bool mine = excl < kk && kk <= incl;
+    int r = kk - excl, dg = 4 * lane, cnt = hv.x;
+    if (r > hv.x) { r -= hv.x; ++dg; cnt = hv.y; if (r > hv.y) { r -= hv.y; ++dg; cnt = hv.z; if (r > hv.z) { r -= hv.z; ++dg; cnt = hv.w; } } }
     const int owner = __ffsll(__ballot(mine)) - 1;
     dg = __shfl(dg, owner);
     r = __shfl(r, owner);
@@ -136,28 +142,32 @@ __device__ void wave_select(const unsigned long long* key, int n, int k, int* hi
     kk = r;
     if (kk == cnt) break;   // the whole bucket is kept: no finer digit is needed
   }
-  // kept: masked key below the prefix, or equal to it among the first kk by position
-  const int per = (n + 63) / 64;
-  const int lo = lane * per, hi = lo + per < n ? lo + per : n;
-  int eq = 0, kept = 0;
-  for (int i = lo; i < hi; ++i) eq += (key[i] & mask) == prefix;
-  int tot;
-  const int eq_before = wave_exclusive_sum(eq, &tot);
-  {
-    int e = eq_before;
-    for (int i = lo; i < hi; ++i) {
-      const unsigned long long x = key[i] & mask;
-      if (x < prefix || (x == prefix && e++ < kk)) ++kept;
-    }
+  // kept: masked key below the prefix, or equal to it among the first kk in
+  // position order; ranks in position order from ballots (row j before row
+  // j + 1, lanes ascending within a row)
+  int eq_seen = 0, kept_seen = 0;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const unsigned long long xm = x[j] & mask;
+    const bool eq = valid(j) && xm == prefix;
+    const unsigned long long em = __ballot(eq);
+    const bool keep = valid(j) && (xm < prefix || (eq && eq_seen + __popcll(em & lt) < kk));
+    const unsigned long long km = __ballot(keep);
+    if (keep) emit(kept_seen + __popcll(km & lt), lane + 64 * j);
+    eq_seen += __popcll(em);
+    kept_seen += __popcll(km);
   }
-  int rank = wave_exclusive_sum(kept, &tot);
-  {
-    int e = eq_before;
-    for (int i = lo; i < hi; ++i) {
-      const unsigned long long x = key[i] & mask;
-      if (x < prefix || (x == prefix && e++ < kk)) emit(rank++, i);
-    }
-  }
+}
+
+template <typename EmitFn>
+__device__ void wave_select(const unsigned long long* key, int n, int k, int* hist, EmitFn emit) {
+  if (n <= 64) wave_select_kpl<1>(key, n, k, hist, emit);
+  else if (n <= 128) wave_select_kpl<2>(key, n, k, hist, emit);
+  else if (n <= 256) wave_select_kpl<4>(key, n, k, hist, emit);
+  else if (n <= 512) wave_select_kpl<8>(key, n, k, hist, emit);
+  else if (n <= 1024) wave_select_kpl<16>(key, n, k, hist, emit);
+  else if (n <= 2048) wave_select_kpl<32>(key, n, k, hist, emit);
+  else wave_select_kpl<64>(key, n, k, hist, emit);
 }
 
 // Score summary rows c in [0, n) against the block query: row(c) points at d
