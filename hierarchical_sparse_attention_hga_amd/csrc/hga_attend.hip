@@ -203,7 +203,7 @@ constexpr float kRescaleSlack = 8.0f;
 // gathered rows of the next tiles are in flight while a tile is computed.
 constexpr int kAttnThreads = 512;
 constexpr int kAttnWaves = kAttnThreads / 64;
-constexpr int kAttnStages = 3;
+constexpr int kAttnStages = 2;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -225,6 +225,10 @@ __device__ inline int v_swizzle(int r) { return ((r & 3) << 2) & (D / 8 - 1); }
 // The instruction writes no register, so the compiler never waits on it; the
 // kernel waits for it itself (s_waitcnt vmcnt) before the barrier that
 // publishes a stage.
+// M0 is declared clobbered so the compiler sets it again before its own uses;
+// clang warns about clobbering a reserved register, which is the intent here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ inline void lds_dma16(const void* src, uint32_t lds_base) {
   asm volatile(
       "s_mov_b32 m0, %1\n\t"
@@ -234,6 +238,13 @@ __device__ inline void lds_dma16(const void* src, uint32_t lds_base) {
       : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
       : "memory", "m0");
 }
+#pragma clang diagnostic pop
+
+// s_waitcnt immediate that waits for vector memory only: vmcnt(n) with the
+// LDS and export counters left at their "don't wait" maxima. vmcnt is split
+// over bits 3:0 and 15:14.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+static_assert(vmcnt_imm(5) == (0x0F70 | 5), "waitcnt encoding");
 
 __device__ inline uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -246,7 +257,8 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(AttnArgs A) {
   constexpr int RPW = kChunk / kAttnWaves;    // rows each wave loads per tile
   constexpr int KI = RPW / RPI;               // loads per wave per tensor per tile
   constexpr int kPerTile = 2 * KI;            // K and V
-  static_assert(KI >= 1 && kPerTile <= 15, "tile shape");
+  constexpr int kAhead = kAttnStages - 2;     // tiles in flight beyond t at the top of iteration t
+  static_assert(KI >= 1 && kPerTile * kAhead <= 63, "tile shape");
   __shared__ __align__(16) uint16_t sK[kAttnStages][kChunk * D];
   __shared__ __align__(16) uint16_t sV[kAttnStages][kChunk * D];
   __shared__ int sRuns[kMaxRoutedAttn];
@@ -340,11 +352,13 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(AttnArgs A) {
   for (int t = 0; t < kAttnStages - 1; ++t)
     if (t < P.ntiles) issue(t);
   for (int t = 0; t < P.ntiles; ++t) {
-    // this thread's loads of tile t are done once at most one newer tile is pending
-    if (t + 1 < P.ntiles)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | kPerTile);   // vmcnt(kPerTile)
+    // this thread's loads of tile t are done once only newer tiles are pending
+    if (kAhead >= 2 && t + 2 < P.ntiles)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPerTile));
+    else if (kAhead >= 1 && t + 1 < P.ntiles)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPerTile));
     else
-      __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();   // every wave's loads of tile t landed; tile t - 1 is free
     if (t + kAttnStages - 1 < P.ntiles) issue(t + kAttnStages - 1);
     if (!active) continue;

@@ -33,6 +33,7 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kLanesPerCand = 8;
 constexpr int kRowsInFlight = 4;   // summary rows per lane group per round
+constexpr int kQuadsPerLane = 128 / 4 / kLanesPerCand;   // float4s per lane and row (d <= 128)
 
 template <typename T>
 struct Slice;  // one 16-byte slice of a query row
@@ -74,17 +75,18 @@ struct RouteSmem {
   double qbar[128];
 };
 
-// Wave-level exclusive prefix sum; *total gets the wave's sum.
-__device__ inline int wave_exclusive_sum(int v, int* total) {
-  const int lane = threadIdx.x & 63;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  *total = __shfl(x, 63);
-  return x - v;
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: a
+// Hillis-Steele scan inside each row of 16 lanes, then the row totals
+// (lane 15 of a row to the next row, lane 31 to the upper two rows).
+__device__ inline int wave_inclusive_sum(int x) {
+  constexpr int kRowShr = 0x110, kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+  x += __builtin_amdgcn_update_dpp(0, x, kRowShr | 1, 0xf, 0xf, true);
+  x += __builtin_amdgcn_update_dpp(0, x, kRowShr | 2, 0xf, 0xf, true);
+  x += __builtin_amdgcn_update_dpp(0, x, kRowShr | 4, 0xf, 0xf, true);
+  x += __builtin_amdgcn_update_dpp(0, x, kRowShr | 8, 0xf, 0xf, true);
+  x += __builtin_amdgcn_update_dpp(0, x, kRowBcast15, 0xa, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kRowBcast31, 0xc, 0xf, false);
+  return x;
 }
 
 // One wave keeps the k smallest of key[0..n) in (key, position) order
@@ -112,7 +114,7 @@ __device__ void wave_select_kpl(const unsigned long long* key, int n, int k, int
       if (am) {
         // a wave whose matching keys share one digit adds them in one atomic
         const int first = __ffsll(am) - 1;
-        const int d0 = __shfl(dg, first);
+        const int d0 = __builtin_amdgcn_readlane(dg, first);
         if (__ballot(act && dg == d0) == am) {
           if (lane == first) atomicAdd(&hist[d0], __popcll(am));
         } else if (act) {
@@ -123,20 +125,15 @@ __device__ void wave_select_kpl(const unsigned long long* key, int n, int k, int
     // the bucket holding the kk-th smallest matching key
     const int4 hv = *reinterpret_cast<const int4*>(&hist[4 * lane]);
     const int sum = hv.x + hv.y + hv.z + hv.w;
-    int incl = sum;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off);
-      if (lane >= off) incl += y;
-    }
+    const int incl = wave_inclusive_sum(sum);
     const int excl = incl - sum;
     const bool mine = excl < kk && kk <= incl;
     int r = kk - excl, dg = 4 * lane, cnt = hv.x;
     if (r > hv.x) { r -= hv.x; ++dg; cnt = hv.y; if (r > hv.y) { r -= hv.y; ++dg; cnt = hv.z; if (r > hv.z) { r -= hv.z; ++dg; cnt = hv.w; } } }
     const int owner = __ffsll(__ballot(mine)) - 1;
-    dg = __shfl(dg, owner);
-    r = __shfl(r, owner);
-    cnt = __shfl(cnt, owner);
+    dg = __builtin_amdgcn_readlane(dg, owner);
+    r = __builtin_amdgcn_readlane(r, owner);
+    cnt = __builtin_amdgcn_readlane(cnt, owner);
     prefix |= (unsigned long long)dg << shift;
     mask |= 255ull << shift;
     kk = r;
@@ -190,18 +187,25 @@ __device__ void score_rows(const double* qbar, int d, int n, RowFn row, unsigned
       r[u] = c[u] < n ? row(c[u]) : nullptr;
       acc[u] = 0.0;
     }
-    for (int q4 = lic; q4 < quads; q4 += kLanesPerCand) {
-      float4 v[kRowsInFlight];
+    // every load of the round is issued before the first use
+    float4 v[kQuadsPerLane][kRowsInFlight];
+#pragma unroll
+    for (int i = 0; i < kQuadsPerLane; ++i)
 #pragma unroll
       for (int u = 0; u < kRowsInFlight; ++u) {
-        v[u] = float4{0.f, 0.f, 0.f, 0.f};
-        if (r[u]) v[u] = *reinterpret_cast<const float4*>(r[u] + 4 * q4);
+        const int q4 = lic + i * kLanesPerCand;
+        v[i][u] = float4{0.f, 0.f, 0.f, 0.f};
+        if (r[u] && q4 < quads) v[i][u] = *reinterpret_cast<const float4*>(r[u] + 4 * q4);
       }
+#pragma unroll
+    for (int i = 0; i < kQuadsPerLane; ++i) {
+      const int q4 = lic + i * kLanesPerCand;
+      if (q4 >= quads) break;
       const double q0 = qbar[4 * q4], q1 = qbar[4 * q4 + 1], q2 = qbar[4 * q4 + 2], q3 = qbar[4 * q4 + 3];
 #pragma unroll
       for (int u = 0; u < kRowsInFlight; ++u) {
-        acc[u] += q0 * (double)v[u].x; acc[u] += q1 * (double)v[u].y;
-        acc[u] += q2 * (double)v[u].z; acc[u] += q3 * (double)v[u].w;
+        acc[u] += q0 * (double)v[i][u].x; acc[u] += q1 * (double)v[i][u].y;
+        acc[u] += q2 * (double)v[i][u].z; acc[u] += q3 * (double)v[i][u].w;
       }
     }
 #pragma unroll
@@ -242,14 +246,14 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   const int64_t s = S.q0 + (int64_t)b * S.B;
   const int64_t ms = s / S.c;
   const int gpc = S.c / S.g;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, wave = tid >> 6;
 
   // ---- 1. block query (float64)
   {
     const int P = d / E;                       // 16-byte slices per row
     const int phases = kThreads / P;
     const int p = tid % P, ph = tid / P;
-    double* part = reinterpret_cast<double*>(sm.key);   // [phases][d]
+    double* part = reinterpret_cast<double*>(sm.key);   // [waves][d]
     const int nrows = S.G * S.B;
     const T* qbase = static_cast<const T*>(a.q);
     double acc[E];
@@ -269,12 +273,19 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
 #pragma unroll
       for (int u = 0; u < kRowsPerThread; ++u) Slice<T>::add(v[u], acc);
     }
+    // lanes of a wave with the same slice are P apart: fold them, then the
+    // 8 wave partials through LDS
+    for (int off = P; off < 64; off <<= 1)
 #pragma unroll
-    for (int e = 0; e < E; ++e) part[ph * d + p * E + e] = acc[e];
+      for (int e = 0; e < E; ++e) acc[e] += __shfl_xor(acc[e], off);
+    if ((tid & 63) < P)
+#pragma unroll
+      for (int e = 0; e < E; ++e) part[wave * d + p * E + e] = acc[e];
     __syncthreads();
     if (tid < d) {
       double t = 0.0;
-      for (int q = 0; q < phases; ++q) t += part[q * d + tid];
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) t += part[w * d + tid];
       sm.qbar[tid] = t / nrows;
     }
     __syncthreads();
