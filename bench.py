@@ -1,9 +1,11 @@
 """Benchmark of the HGA routed-attention forward on one MI355X.
 
 A step is one pass of the whole path over one layer of one synthetic input:
-hga_build_summaries (group and chunk summaries of every key), hga_route
-(block queries, chunk stage, group stage) and hga_attend (exact routed
-attention), all on one stream with every input already in HBM.
+hga_build_summaries (group and chunk summaries of every key), then
+hga_route_attend (block queries, chunk stage, group stage and exact routed
+attention, one kernel), all on one stream with every input already in HBM.
+The same step through the separate hga_route and hga_attend calls is
+reported alongside.
 
 The workload is the 16,384-token training-segment shape (Qwen3-8B heads:
 32 query / 8 KV heads, head_dim 128, bf16, 2,048 active queries over a
@@ -12,10 +14,10 @@ The same line also reports the 65,536-token Qwen3-30B-A3B-shaped layer with
 its history in HBM and, separately, with its history in pinned host memory
 (that rate includes the PCIe transfer of the routed set).
 
-Output: one JSON line (see the keys below). ``roofline`` covers the attention
-kernel, whose duration is measured with HIP events on the launch stream over
-the timed steps; ``cpu_baseline`` is the CPU oracle on a bounded sample of the
-same workload.
+Output: one JSON line (see the keys below). ``roofline`` covers the
+route-and-attend kernel (the attention's flops over that kernel's duration,
+measured with HIP events on the launch stream over the timed steps);
+``cpu_baseline`` is the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -104,7 +106,7 @@ def to_dev(a, dtype, dev):
 class Workload:
     """Device buffers and one step of the path for one configuration."""
 
-    def __init__(self, cfg_id, split=0):
+    def __init__(self, cfg_id, split=0, fused=True):
         import torch
 
         import hierarchical_sparse_attention_hga_amd as hga
@@ -130,6 +132,8 @@ class Workload:
         self.lse = torch.empty(cfg["hq"], nq, device=DEV)
         self.k_full = k
         self.split = split
+        self.fused = fused
+        self.n_stages = 2 if fused else 3
         self.pins = []
         self.ws, self.wsb = None, 0
         if split > 0:
@@ -153,27 +157,31 @@ class Workload:
             hga.hga_build_summaries(c, self.k_full, self.L, self.gs, self.cs)
         if ev:
             ev[1].record()
-        hga.hga_route(c, self.q, self.q0, self.nq, self.L, self.cs, self.gs_t, self.ci, self.gi, self.ns)
+        if self.fused:
+            hga.hga_route_attend(c, self.q, self.q0, self.nq, self.L, self.cs, self.gs_t, self.k_t, self.v_t,
+                                 self.ci, self.gi, self.ns, self.out, self.lse, self.ws, self.wsb)
+        else:
+            hga.hga_route(c, self.q, self.q0, self.nq, self.L, self.cs, self.gs_t, self.ci, self.gi, self.ns)
+            if ev:
+                ev[2].record()
+            hga.hga_attend(c, self.q, self.q0, self.nq, self.L, self.k_t, self.v_t, self.gi, self.ns,
+                           self.out, self.lse, self.ws, self.wsb)
         if ev:
-            ev[2].record()
-        hga.hga_attend(c, self.q, self.q0, self.nq, self.L, self.k_t, self.v_t, self.gi, self.ns,
-                       self.out, self.lse, self.ws, self.wsb)
-        if ev:
-            ev[3].record()
+            ev[self.n_stages].record()
 
     def run(self, steps, warmup):
         torch = self.torch
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(self.n_stages + 1)] for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
             self.step(evs[i])
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        stage = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs]) * 1e3  # us
+        stage = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(self.n_stages)] for e in evs]) * 1e3  # us
         return wall, stage
 
     def free(self):
@@ -181,25 +189,33 @@ class Workload:
             p.free()
 
 
-def measured_traffic(workload):
-    """HBM bytes per attention launch from the committed rocprofv3 counter runs
-    (profiles/attend_bf16_<workload>.traffic.json), or None when they are
-    missing or were taken on different attention kernel sources."""
+KERNEL_SOURCES = ("hga_attend.hip", "hga_route_impl.h", "hga_internal.h")
+
+
+def source_sha256():
+    """Digest of the sources of the route-and-attend kernel."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"attend_bf16_{workload}.traffic.json")
+    src = b"".join(open(os.path.join(ROOT, "hierarchical_sparse_attention_hga_amd", "csrc", f), "rb").read()
+                   for f in KERNEL_SOURCES)
+    return hashlib.sha256(src).hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per route-and-attend launch from the committed rocprofv3
+    counter runs (profiles/route_attend_bf16_<workload>.traffic.json), or None
+    when they are missing or were taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"route_attend_bf16_{workload}.traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = b"".join(open(os.path.join(ROOT, "hierarchical_sparse_attention_hga_amd", "csrc", f), "rb").read()
-                   for f in ("hga_attend.hip", "hga_internal.h"))
-    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+    if source_sha256() != rec["source_sha256"]:
         return None
     return 1024.0 * (rec["fetch_kib"] * rec["fetch_factor"] + rec["write_kib"] * rec["write_factor"])
 
 
-def roofline(cfg, n_sel, attend_us):
+def roofline(cfg, n_sel, attend_us, with_traffic=True):
     flops, byts, _ = algorithmic(cfg, n_sel)
-    traffic = measured_traffic(cfg["name"])
+    traffic = measured_traffic(cfg["name"]) if with_traffic else None
     t_mfma = flops / PEAK_BF16
     t_hbm = byts / PEAK_HBM
     t = attend_us * 1e-6
@@ -236,8 +252,8 @@ def cpu_baseline(cfg_id, min_seconds=10.0):
                       f"summaries, routing, attention) repeated {reps}x in {el:.1f} s"}
 
 
-def measure(cfg_id, steps, warmup, split=0):
-    w = Workload(cfg_id, split)
+def measure(cfg_id, steps, warmup, split=0, fused=True):
+    w = Workload(cfg_id, split, fused)
     wall, stage = w.run(steps, warmup)
     ns = w.ns.cpu().numpy()
     cfg = w.cfg
@@ -260,7 +276,7 @@ def main():
         return
     cfg, ns, wall, med, mean = measure(args.config, args.steps, args.warmup)
     value = args.steps * cfg["n_q"] / wall
-    rl = roofline(cfg, ns, mean[2])
+    rl = roofline(cfg, ns, mean[1])
     line = {
         "metric": METRIC, "value": value, "unit": "query-tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3,
@@ -270,21 +286,30 @@ def main():
                    "kv_heads": cfg["hkv"], "head_dim": cfg["d"], "top_chunks": cfg["top_chunks"],
                    "top_groups": cfg["top_groups"], "sink": cfg["sink"], "local": cfg["local"],
                    "kv_residency": "hbm"},
-        "stages_us_mean": {"summaries": mean[0], "route": mean[1], "attend": mean[2]},
-        "stages_us_median": {"summaries": med[0], "route": med[1], "attend": med[2]},
+        "stages_us_mean": {"summaries": mean[0], "route_attend": mean[1]},
+        "stages_us_median": {"summaries": med[0], "route_attend": med[1]},
         "roofline": rl,
     }
-    if not args.no_extra and args.config != 3:
+    if not args.no_extra:
         extra = {}
-        c3, ns3, wall3, med3, mean3 = measure(3, max(args.steps // 2, 5), args.warmup)
-        extra["64k_hbm"] = {"value": max(args.steps // 2, 5) * c3["n_q"] / wall3, "unit": "query-tokens/s",
-                            "stages_us_mean": {"summaries": mean3[0], "route": mean3[1], "attend": mean3[2]},
-                            "roofline": roofline(c3, ns3, mean3[2])}
-        c3h, _, wallh, medh, meanh = measure(3, 5, 2, split=c3["tier_split"])
-        extra["64k_host_tier_pcie_inclusive"] = {
-            "value": 5 * c3h["n_q"] / wallh, "unit": "query-tokens/s",
-            "note": "history K/V and group summaries in pinned host memory; routed rows cross PCIe each step",
-            "stages_us_mean": {"route": meanh[1], "gather_and_attend": meanh[2]}}
+        half = max(args.steps // 2, 5)
+        cs_, nss, walls, meds, means = measure(args.config, half, args.warmup, fused=False)
+        extra["separate_calls"] = {
+            "value": half * cs_["n_q"] / walls, "unit": "query-tokens/s",
+            "note": "same step through hga_route then hga_attend; roofline of the attention kernel alone",
+            "stages_us_mean": {"summaries": means[0], "route": means[1], "attend": means[2]},
+            "roofline": roofline(cs_, nss, means[2], with_traffic=False)}
+        if args.config != 3:
+            c3, ns3, wall3, med3, mean3 = measure(3, half, args.warmup)
+            extra["64k_hbm"] = {"value": half * c3["n_q"] / wall3, "unit": "query-tokens/s",
+                                "stages_us_mean": {"summaries": mean3[0], "route_attend": mean3[1]},
+                                "roofline": roofline(c3, ns3, mean3[1])}
+            c3h, _, wallh, medh, meanh = measure(3, 5, 2, split=c3["tier_split"])
+            extra["64k_host_tier_pcie_inclusive"] = {
+                "value": 5 * c3h["n_q"] / wallh, "unit": "query-tokens/s",
+                "note": "history K/V and group summaries in pinned host memory; routed rows cross PCIe each "
+                        "step (routing, then gather and attention)",
+                "stages_us_mean": {"route_gather_attend": meanh[1]}}
         line["also"] = extra
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.config)

@@ -20,7 +20,7 @@ HGA_SUMMARY_MEAN = 0
 HGA_WS_ROUTE, HGA_WS_ATTEND, HGA_WS_ATTEND_TIERED = 0, 1, 2
 
 # Every exported entry point of include/hga.h.
-EXPORTS = ("hga_workspace_size", "hga_build_summaries", "hga_route", "hga_attend",
+EXPORTS = ("hga_workspace_size", "hga_build_summaries", "hga_route", "hga_attend", "hga_route_attend",
            "hga_status_string", "hga_last_error", "hga_version")
 
 
@@ -59,7 +59,8 @@ def load():
         lib.hga_build_summaries.argtypes = [cfgp, P, I64, P, P, P]
         lib.hga_route.argtypes = [cfgp, P, I64, I64, I64, P, tierp, P, P, P, P, SZ, P]
         lib.hga_attend.argtypes = [cfgp, P, I64, I64, I64, tierp, tierp, P, P, P, P, P, SZ, P]
-        for f in ("hga_build_summaries", "hga_route", "hga_attend"):
+        lib.hga_route_attend.argtypes = [cfgp, P, I64, I64, I64, P, tierp, tierp, tierp, P, P, P, P, P, P, SZ, P]
+        for f in ("hga_build_summaries", "hga_route", "hga_attend", "hga_route_attend"):
             getattr(lib, f).restype = C.c_int
         lib.hga_status_string.argtypes = [C.c_int]
         lib.hga_status_string.restype = C.c_char_p
@@ -139,6 +140,14 @@ def hga_attend(cfg, q, q_start, n_q, seq_len, k, v, group_idx, n_sel, out, lse=N
     _check(load().hga_attend(C.byref(cfg), _ptr(q), q_start, n_q, seq_len, C.byref(kt), C.byref(vt),
                              _ptr(group_idx), _ptr(n_sel), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                              _stream(stream)))
+
+
+def hga_route_attend(cfg, q, q_start, n_q, seq_len, chunk_sum, group_sum, k, v, chunk_idx, group_idx, n_sel,
+                     out, lse=None, workspace=None, ws_bytes=0, stream=None):
+    gt, kt, vt = _tier(group_sum), _tier(k), _tier(v)
+    _check(load().hga_route_attend(C.byref(cfg), _ptr(q), q_start, n_q, seq_len, _ptr(chunk_sum), C.byref(gt),
+                                   C.byref(kt), C.byref(vt), _ptr(chunk_idx), _ptr(group_idx), _ptr(n_sel),
+                                   _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def hga_status_string(status):

@@ -174,6 +174,43 @@ hga_status hga_attend(const hga_config* cfg, const void* q, int64_t q_start, int
                        "hga_attend launch");
 }
 
+hga_status hga_route_attend(const hga_config* cfg, const void* q, int64_t q_start, int64_t n_q, int64_t seq_len,
+                            const float* chunk_sum, const hga_tiered* group_sum, const hga_tiered* k,
+                            const hga_tiered* v, int32_t* chunk_idx, int32_t* group_idx, int32_t* n_sel,
+                            void* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  hga::Shape s;
+  hga_status st = make_shape(cfg, seq_len, q_start, n_q, &s);
+  if (st != HGA_OK) return st;
+  if (n_q == 0) return ok();
+  if (!q || !chunk_sum || !n_sel || !out || (s.kc > 0 && !chunk_idx) || (s.kg > 0 && !group_idx))
+    return fail(HGA_ERR_INVALID_ARGUMENT,
+                "q, chunk_sum, n_sel, out, chunk_idx and group_idx must be non-NULL");
+  if ((st = check_tier(group_sum, "group_sum", seq_len, q_start)) != HGA_OK) return st;
+  if ((st = check_tier(k, "k", seq_len, q_start)) != HGA_OK) return st;
+  if ((st = check_tier(v, "v", seq_len, q_start)) != HGA_OK) return st;
+  if (k->split != v->split) return fail(HGA_ERR_INVALID_ARGUMENT, "k.split and v.split differ");
+  if (k->split > 0) {
+    const size_t need = hga::staging_bytes(s);
+    if (!workspace || ws_bytes < need)
+      return fail(HGA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                  workspace ? ws_bytes : (size_t)0);
+  }
+  const hipStream_t hs = (hipStream_t)stream;
+  const float* gs_host = static_cast<const float*>(group_sum->host);
+  const float* gs_dev = static_cast<const float*>(group_sum->dev);
+  hga::KVSrc kv{k->host, k->dev, v->host, v->dev, k->split};
+  if (hga::fused_route_attend_supported(s, k->split))
+    return device_status(hga::launch_route_attend(s, q, chunk_sum, gs_host, gs_dev, group_sum->split, kv,
+                                                  chunk_idx, group_idx, n_sel, out, lse, hs),
+                         "hga_route_attend launch");
+  st = device_status(hga::launch_route(s, q, chunk_sum, gs_host, gs_dev, group_sum->split, chunk_idx, group_idx,
+                                       n_sel, hs),
+                     "hga_route_attend routing launch");
+  if (st != HGA_OK) return st;
+  return device_status(hga::launch_attend(s, q, kv, group_idx, n_sel, out, lse, workspace, hs),
+                       "hga_route_attend attention launch");
+}
+
 const char* hga_status_string(hga_status status) {
   switch (status) {
     case HGA_OK: return "ok";
@@ -187,6 +224,6 @@ const char* hga_status_string(hga_status status) {
 
 const char* hga_last_error(void) { return g_err; }
 
-int32_t hga_version(void) { return 100; }
+int32_t hga_version(void) { return 101; }
 
 }  // extern "C"

@@ -27,7 +27,7 @@
 // then read the staged tiles contiguously.
 #include <limits.h>
 
-#include "hga_internal.h"
+#include "hga_route_impl.h"
 
 namespace hga {
 namespace {
@@ -250,24 +250,77 @@ __device__ inline uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
+// Max and sum of x over lanes l and l ^ 32, by one swap of the wave's halves:
+// the two results of the swap are this lane's value and its partner's.
+__device__ inline float pair_max(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ inline float pair_sum(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+// Shared memory of the bfloat16 attention: the K and V stage rings and the
+// item's routed run list.
+template <int D>
+struct AttnSmem {
+  uint16_t k[kAttnStages][kChunk * D];
+  uint16_t v[kAttnStages][kChunk * D];
+  int runs[kMaxRoutedAttn];
+  int scan[16];
+};
+
+// K/V row bases of KV head h: the staged tiles of the host-tier path, or the
+// head's device rows.
 template <int D, bool kStaged>
-__global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(AttnArgs A) {
+__device__ inline void kv_bases(const AttnArgs& A, int h, const uint16_t** kb, const uint16_t** vb) {
+  const uint16_t* k = static_cast<const uint16_t*>(kStaged ? A.k_stage : A.kv.k_dev);
+  const uint16_t* v = static_cast<const uint16_t*>(kStaged ? A.v_stage : A.kv.v_dev);
+  if (!kStaged) {
+    k += (int64_t)h * A.s.L * D;
+    v += (int64_t)h * A.s.L * D;
+  }
+  *kb = k;
+  *vb = v;
+}
+
+// This wave's share of one tile load: rows [RPW w, RPW w + RPW) of the tile,
+// each lane one 16-byte piece of K and of V written at its swizzled position
+// in the stage at LDS byte addresses k_lds / v_lds. row(sl) is the tensor row
+// of slot sl.
+template <int D, typename RowFn>
+__device__ inline void issue_tile(const uint16_t* kbase, const uint16_t* vbase, uint32_t k_lds, uint32_t v_lds,
+                                  RowFn row) {
   constexpr int NP = D / 8;                   // 16-byte pieces per token row
   constexpr int RPI = 64 / NP;                // rows per direct-to-LDS wave load
   constexpr int RPW = kChunk / kAttnWaves;    // rows each wave loads per tile
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < RPW / RPI; ++i) {
+    const int row0 = wave * RPW + i * RPI;
+    const int rr = row0 + lane / NP;
+    const int64_t r = row(rr) * D;
+    lds_dma16(kbase + r + ((lane % NP) ^ k_swizzle<D>(rr)) * 8, k_lds + (uint32_t)(row0 * D * 2));
+    lds_dma16(vbase + r + ((lane % NP) ^ v_swizzle<D>(rr)) * 8, v_lds + (uint32_t)(row0 * D * 2));
+  }
+}
+
+// Attention of item (b, h), workgroup slot z, over the token set of plan P
+// (runs in sm.runs). With tile0_issued the caller has already issued tile
+// 0's loads into stage 0.
+template <int D, bool kStaged>
+__device__ void attend_bf16_body(const AttnArgs& A, int b, int h, int z, const Plan& P, AttnSmem<D>& sm,
+                                 bool tile0_issued) {
+  constexpr int NP = D / 8;
+  constexpr int RPI = 64 / NP;
+  constexpr int RPW = kChunk / kAttnWaves;
   constexpr int KI = RPW / RPI;               // loads per wave per tensor per tile
   constexpr int kPerTile = 2 * KI;            // K and V
   constexpr int kAhead = kAttnStages - 2;     // tiles in flight beyond t at the top of iteration t
   static_assert(KI >= 1 && kPerTile * kAhead <= 63, "tile shape");
-  __shared__ __align__(16) uint16_t sK[kAttnStages][kChunk * D];
-  __shared__ __align__(16) uint16_t sV[kAttnStages][kChunk * D];
-  __shared__ int sRuns[kMaxRoutedAttn];
-  __shared__ int sScan[16];
-
   const Shape& S = A.s;
-  int b, h, z;
-  item_of_block(S, A.wg_per_item, &b, &h, &z);
-  const Plan P = make_plan(S, b, h, A.gidx, A.nsel, sRuns, sScan, kMaxRoutedAttn);
+  const int nt = P.ntiles;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5;                  // lane half
@@ -289,32 +342,17 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(AttnArgs A) {
   }
 
   const int lg = __ffs(S.g) - 1;
-  const uint16_t* kbase = static_cast<const uint16_t*>(kStaged ? A.k_stage : A.kv.k_dev);
-  const uint16_t* vbase = static_cast<const uint16_t*>(kStaged ? A.v_stage : A.kv.v_dev);
-  if (!kStaged) {
-    kbase += (int64_t)h * S.L * D;
-    vbase += (int64_t)h * S.L * D;
-  }
+  const uint16_t *kbase, *vbase;
+  kv_bases<D, kStaged>(A, h, &kbase, &vbase);
   // Row of slot sl of tile t in kbase/vbase. Empty slots read token 0: their
   // probabilities are exactly zero, so any finite row will do.
-  auto slot_row = [&](int t, int sl) -> int64_t {
-    if (kStaged) return (item_lin * A.tiles_per_item + t) * kChunk + sl;
-    const int tok = slot_token(P, sRuns, lg, t, sl);
-    return tok >= 0 ? tok : 0;
-  };
-  // Wave w copies rows [RPW w, RPW w + RPW) of tile t into its stage; each
-  // lane moves one 16-byte piece, written at its swizzled position.
-  const uint32_t k_lds = lds_addr(&sK[0][0]), v_lds = lds_addr(&sV[0][0]);
   auto issue = [&](int t) {
-    const uint32_t stage_off = (uint32_t)((t % kAttnStages) * kChunk * D * 2);
-#pragma unroll
-    for (int i = 0; i < KI; ++i) {
-      const int row0 = wave * RPW + i * RPI;
-      const int rr = row0 + lane / NP;
-      const int64_t row = slot_row(t, rr) * D;
-      lds_dma16(kbase + row + ((lane % NP) ^ k_swizzle<D>(rr)) * 8, k_lds + stage_off + (uint32_t)(row0 * D * 2));
-      lds_dma16(vbase + row + ((lane % NP) ^ v_swizzle<D>(rr)) * 8, v_lds + stage_off + (uint32_t)(row0 * D * 2));
-    }
+    const uint32_t off = (uint32_t)((t % kAttnStages) * kChunk * D * 2);
+    issue_tile<D>(kbase, vbase, lds_addr(&sm.k[0][0]) + off, lds_addr(&sm.v[0][0]) + off, [&](int sl) -> int64_t {
+      if (kStaged) return (item_lin * A.tiles_per_item + t) * kChunk + sl;
+      const int tok = slot_token(P, sm.runs, lg, t, sl);
+      return tok >= 0 ? tok : 0;
+    });
   };
 
   const float sl2 = S.scale * kLog2e;
@@ -345,22 +383,22 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(AttnArgs A) {
       voff[db] = (uint32_t)(vrow * RB + ((((c >> 3) ^ v_swizzle<D>(vrow))) << 4) + ((c & 7) << 1));
     }
   }
-  const char* sKb = reinterpret_cast<const char*>(&sK[0][0]);
-  const char* sVb = reinterpret_cast<const char*>(&sV[0][0]);
+  const char* sKb = reinterpret_cast<const char*>(&sm.k[0][0]);
+  const char* sVb = reinterpret_cast<const char*>(&sm.v[0][0]);
 
 #pragma unroll
   for (int t = 0; t < kAttnStages - 1; ++t)
-    if (t < P.ntiles) issue(t);
-  for (int t = 0; t < P.ntiles; ++t) {
+    if (t < nt && !(t == 0 && tile0_issued)) issue(t);
+  for (int t = 0; t < nt; ++t) {
     // this thread's loads of tile t are done once only newer tiles are pending
-    if (kAhead >= 2 && t + 2 < P.ntiles)
+    if (kAhead >= 2 && t + 2 < nt)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPerTile));
-    else if (kAhead >= 1 && t + 1 < P.ntiles)
+    else if (kAhead >= 1 && t + 1 < nt)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPerTile));
     else
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();   // every wave's loads of tile t landed; tile t - 1 is free
-    if (t + kAttnStages - 1 < P.ntiles) issue(t + kAttnStages - 1);
+    if (t + kAttnStages - 1 < nt) issue(t + kAttnStages - 1);
     if (!active) continue;
     const uint32_t stage = (uint32_t)((t % kAttnStages) * kChunk * RB);
     const char* kt = sKb + stage;
@@ -379,22 +417,24 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(AttnArgs A) {
         sacc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], sacc[tb], 0, 0, 0);
     }
     // masking only on the block's own tile and on a partial routed tile;
-    // slot of accumulator r of half tb: 32 tb + 8 (r >> 2) + 4 hl + (r & 3)
-    const bool diag = t == P.ntiles - 1;
+    // slot of accumulator r of half tb: 32 tb + 8 (r >> 2) + 4 hl + (r & 3).
+    // A slot is masked when it reaches the tile's limit or, on the block's
+    // own tile, passes the query's position; thr is that bound shifted by
+    // this lane's 4 hl.
+    const bool diag = t == nt - 1;
     const int lim = tile_limit(P, S.g, t);
     if (diag || lim < kChunk) {
+      const int thr = (diag && qi + 1 < lim ? qi + 1 : lim) - 4 * hl;
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int slot = 32 * tb + 8 * (r >> 2) + 4 * hl + (r & 3);
-          if (slot >= lim || (diag && slot > qi)) sacc[tb][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (32 * tb + 8 * (r >> 2) + (r & 3) >= thr) sacc[tb][r] = -INFINITY;
     }
-    float mx = fmaxf(sacc[0][0], sacc[1][0]);
+    float mx = __builtin_fmaxf(sacc[0][0], sacc[1][0]);
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = __builtin_fmaxf(__builtin_fmaxf(mx, sacc[0][r]), sacc[1][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+    mx = pair_max(mx) * sl2;
     const bool upd = mx > m_run + kRescaleSlack;
     if (__ballot(upd)) {
       const float m_new = upd ? mx : m_run;
@@ -437,7 +477,7 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(AttnArgs A) {
   }
 
   if (active) {
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = pair_sum(l_run);
     const float inv = 1.0f / l_tot;
     uint16_t* op = static_cast<uint16_t*>(A.out) + ((int64_t)head * S.nq + qrow) * D;
 #pragma unroll
@@ -451,6 +491,61 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(AttnArgs A) {
       }
     if (A.lse && hl == 0) A.lse[(int64_t)head * S.nq + qrow] = (m_run + __log2f(l_tot)) * kLn2;
   }
+}
+
+// bfloat16 attention of items whose kept groups come from group_idx.
+template <int D, bool kStaged>
+__global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(AttnArgs A) {
+  __shared__ AttnSmem<D> sm;
+  int b, h, z;
+  item_of_block(A.s, A.wg_per_item, &b, &h, &z);
+  const Plan P = make_plan(A.s, b, h, A.gidx, A.nsel, sm.runs, sm.scan, kMaxRoutedAttn);
+  attend_bf16_body<D, kStaged>(A, b, h, z, P, sm, false);
+}
+
+// Route, then attend, in one workgroup per (item, slot): the router's kept
+// groups go straight into the run list (they are ascending and every one is
+// usable, so the run list is exactly the one built from the router's output),
+// and the loads of the first fixed tile, which needs no routing, are in
+// flight while the router runs. Slot 0 writes the router's outputs.
+struct FusedArgs {
+  route::RouteArgs r;
+  AttnArgs a;
+};
+
+template <int D>
+__global__ __launch_bounds__(kAttnThreads) void route_attend_bf16_kernel(FusedArgs F) {
+  static_assert(kAttnThreads == route::kThreads, "one workgroup size for both phases");
+  __shared__ AttnSmem<D> sm;
+  __shared__ route::RouteSmem rsm;
+  const Shape& S = F.a.s;
+  int b, h, z;
+  item_of_block(S, F.a.wg_per_item, &b, &h, &z);
+  Plan P;
+  P.s = S.q0 + (int64_t)b * S.B;
+  const int64_t ms = P.s / S.c;
+  fixed_windows(ms, S.sink_chunks, S.local_chunks, &P.a, &P.bb);
+  P.nfix = (int)(P.a + (ms - P.bb));
+  const bool pre = P.nfix > 0;
+  if (pre) {
+    const uint16_t *kbase, *vbase;
+    kv_bases<D, false>(F.a, h, &kbase, &vbase);
+    const int64_t m0 = P.a > 0 ? 0 : P.bb;      // chunk of fixed tile 0
+    issue_tile<D>(kbase, vbase, lds_addr(&sm.k[0][0]), lds_addr(&sm.v[0][0]),
+                  [&](int sl) -> int64_t { return m0 * kChunk + sl; });
+  }
+  const bool wr = z == 0;
+  int32_t* gout = F.r.group_idx + ((int64_t)b * S.hkv + h) * S.kg;
+  const int g = S.g;
+  const int nsg = route::route_item<uint16_t>(F.r, b, h, rsm, wr, [&](int rank, int group) {
+    sm.runs[rank] = group * g;
+    if (wr) gout[rank] = group;
+  });
+  __syncthreads();
+  P.nrouted = nsg;
+  P.nrt = (nsg + kChunk / g - 1) / (kChunk / g);
+  P.ntiles = P.nfix + P.nrt + 1;
+  attend_bf16_body<D, false>(F.a, b, h, z, P, sm, pre);
 }
 
 // ------------------------------------------------------------ float32 SIMT kernel
@@ -645,6 +740,32 @@ hipError_t launch_attend(const Shape& s, const void* q, const KVSrc& kv, const i
   const int rows = 256 / tpr;
   a.wg_per_item = (s.G * s.B + rows - 1) / rows;
   return staged ? dispatch_f32<true>(a, items, st) : dispatch_f32<false>(a, items, st);
+}
+
+// One kernel when one workgroup holds every query row of an item (2 G <= 8
+// waves of 32 rows): with more, each of an item's workgroups would route it
+// again, and the separate router is cheaper.
+bool fused_route_attend_supported(const Shape& s, int64_t kv_split) {
+  return s.dtype == HGA_BF16 && kv_split == 0 && (s.d == 128 || s.d == 64) && 2 * s.G <= kAttnWaves;
+}
+
+hipError_t launch_route_attend(const Shape& s, const void* q, const float* cs, const float* gs_host,
+                               const float* gs_dev, int64_t gs_split, const KVSrc& kv, int32_t* chunk_idx,
+                               int32_t* group_idx, int32_t* n_sel, void* out, float* lse, hipStream_t st) {
+  const int64_t items = s.nb * s.hkv;
+  if (items == 0) return hipSuccess;
+  if (!fused_route_attend_supported(s, kv.split)) return hipErrorInvalidValue;
+  FusedArgs f{};
+  f.r = route::RouteArgs{q, cs, gs_host, gs_dev, gs_split, chunk_idx, group_idx, n_sel, s};
+  f.a.q = q; f.a.kv = kv; f.a.out = out; f.a.lse = lse; f.a.s = s;
+  f.a.tiles_per_item = max_tiles(s);
+  f.a.wg_per_item = (2 * s.G + kAttnWaves - 1) / kAttnWaves;
+  const dim3 grid((unsigned)(items * f.a.wg_per_item)), block(kAttnThreads);
+  if (s.d == 128)
+    route_attend_bf16_kernel<128><<<grid, block, 0, st>>>(f);
+  else
+    route_attend_bf16_kernel<64><<<grid, block, 0, st>>>(f);
+  return hipGetLastError();
 }
 
 }  // namespace hga

@@ -71,4 +71,10 @@ size_t staging_bytes(const Shape& s);
 hipError_t launch_attend(const Shape& s, const void* q, const KVSrc& kv, const int32_t* group_idx,
                          const int32_t* n_sel, void* out, float* lse, void* staging, hipStream_t st);
 
+// Routing and attention in one kernel (bfloat16, K/V all on the device).
+bool fused_route_attend_supported(const Shape& s, int64_t kv_split);
+hipError_t launch_route_attend(const Shape& s, const void* q, const float* cs, const float* gs_host,
+                               const float* gs_dev, int64_t gs_split, const KVSrc& kv, int32_t* chunk_idx,
+                               int32_t* group_idx, int32_t* n_sel, void* out, float* lse, hipStream_t st);
+
 }  // namespace hga

@@ -167,6 +167,22 @@ hga_status hga_attend(const hga_config* cfg, const void* q, int64_t q_start, int
                       const int32_t* group_idx, const int32_t* n_sel,
                       void* out, float* lse, void* workspace, size_t ws_bytes, void* stream);
 
+/* Routing and attention of the same query rows in one call (section 2.1,
+ * "Chunk selection", "Group selection" and "Exact-token attention" in
+ * sequence): the results are those of hga_route followed by hga_attend on
+ * its chunk_idx / group_idx / n_sel, which are written as well. Arguments
+ * have the meaning, layout and ownership they have in those two calls; the
+ * workspace is the one hga_attend needs for this K/V split. With bfloat16,
+ * K/V entirely on the device (split 0) and at most 4 query heads per KV head,
+ * both steps run in one kernel, each workgroup routing its own query block
+ * before attending over the groups it kept; otherwise the call runs the two
+ * steps one after the other. Errors are those of either call. */
+hga_status hga_route_attend(const hga_config* cfg, const void* q, int64_t q_start, int64_t n_q,
+                            int64_t seq_len, const float* chunk_sum, const hga_tiered* group_sum,
+                            const hga_tiered* k, const hga_tiered* v,
+                            int32_t* chunk_idx, int32_t* group_idx, int32_t* n_sel,
+                            void* out, float* lse, void* workspace, size_t ws_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* hga_status_string(hga_status status);
 

@@ -34,12 +34,14 @@ def hga_cfg(cfg):
                            softmax_scale=cfg.get("softmax_scale") or 0.0)
 
 
-def gpu_run(cfg, x, split=0, group_idx=None, n_sel=None, q_start=None, seq_len=None):
+def gpu_run(cfg, x, split=0, group_idx=None, n_sel=None, q_start=None, seq_len=None, fused=False):
     """Run summaries, routing and attention through the C ABI.
 
     ``group_idx``/``n_sel`` (numpy, [nb][hkv][kg] / [nb][hkv][2]) replace the
-    GPU routing as the attention's input when given. Returns numpy arrays.
+    GPU routing as the attention's input when given. With ``fused`` routing
+    and attention run through hga_route_attend. Returns numpy arrays.
     """
+    assert not (fused and group_idx is not None)
     c = hga_cfg(cfg)
     dt = cfg["dtype"]
     L = cfg["L"] if seq_len is None else seq_len
@@ -64,18 +66,20 @@ def gpu_run(cfg, x, split=0, group_idx=None, n_sel=None, q_start=None, seq_len=N
         pins = [gpin, kpin, vpin]
     else:
         gs_t, k_t, v_t = gs, k, v
-    hga.hga_route(c, q, q0, nq, L, cs, gs_t, ci, gi, ns)
-    if group_idx is not None:
-        gi_in = torch.from_numpy(np.ascontiguousarray(group_idx, dtype=np.int32)).to(DEV)
-        ns_in = torch.from_numpy(np.ascontiguousarray(n_sel, dtype=np.int32)).to(DEV)
-    else:
-        gi_in, ns_in = gi, ns
     ws = None
     wsb = 0
     if split > 0:
         wsb = hga.hga_workspace_size(c, L, nq, hga.HGA_WS_ATTEND_TIERED)
         ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
-    hga.hga_attend(c, q, q0, nq, L, k_t, v_t, gi_in, ns_in, out, lse, ws, wsb)
+    if fused:
+        hga.hga_route_attend(c, q, q0, nq, L, cs, gs_t, k_t, v_t, ci, gi, ns, out, lse, ws, wsb)
+    else:
+        hga.hga_route(c, q, q0, nq, L, cs, gs_t, ci, gi, ns)
+        gi_in, ns_in = gi, ns
+        if group_idx is not None:
+            gi_in = torch.from_numpy(np.ascontiguousarray(group_idx, dtype=np.int32)).to(DEV)
+            ns_in = torch.from_numpy(np.ascontiguousarray(n_sel, dtype=np.int32)).to(DEV)
+        hga.hga_attend(c, q, q0, nq, L, k_t, v_t, gi_in, ns_in, out, lse, ws, wsb)
     torch.cuda.synchronize()
     res = dict(gs=gs.cpu().numpy(), cs=cs.cpu().numpy(), chunk_idx=ci.cpu().numpy(),
                group_idx=gi.cpu().numpy(), n_sel=ns.cpu().numpy(),

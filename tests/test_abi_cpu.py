@@ -31,7 +31,7 @@ def test_every_declared_entry_point_is_exported(lib):
     assert declared == set(B.EXPORTS)
     for name in declared:
         assert hasattr(lib, name)
-    assert hga.hga_version() == 100
+    assert hga.hga_version() == 101
 
 
 def test_status_strings(lib):
@@ -83,6 +83,7 @@ def test_config_validation(over, status):
     assert _status(hga.hga_build_summaries, c, FAKE, 16384, FAKE, FAKE) == status
     assert _status(hga.hga_route, c, FAKE, 14336, 2048, 16384, FAKE, FAKE, FAKE, FAKE, FAKE) == status
     assert _status(hga.hga_attend, c, FAKE, 14336, 2048, 16384, FAKE, FAKE, FAKE, FAKE, FAKE) == status
+    assert _status(hga.hga_route_attend, c, FAKE, 14336, 2048, 16384, *[FAKE] * 8) == status
     assert hga.hga_last_error()
 
 
@@ -97,6 +98,7 @@ def test_geometry_validation(q_start, n_q, seq_len, status):
     c = cfg()
     assert _status(hga.hga_route, c, FAKE, q_start, n_q, seq_len, FAKE, FAKE, FAKE, FAKE, FAKE) == status
     assert _status(hga.hga_attend, c, FAKE, q_start, n_q, seq_len, FAKE, FAKE, FAKE, FAKE, FAKE) == status
+    assert _status(hga.hga_route_attend, c, FAKE, q_start, n_q, seq_len, *[FAKE] * 8) == status
 
 
 def test_null_pointers():
@@ -108,6 +110,12 @@ def test_null_pointers():
     assert _status(hga.hga_route, c, FAKE, 14336, 2048, 16384, FAKE, None, FAKE, FAKE, FAKE) == E
     assert _status(hga.hga_attend, c, FAKE, 14336, 2048, 16384, FAKE, FAKE, FAKE, FAKE, None) == E
     assert _status(hga.hga_attend, c, FAKE, 14336, 2048, 16384, None, FAKE, FAKE, FAKE, FAKE) == E
+    # route_attend: q, chunk_sum, k, v, chunk_idx, group_idx, n_sel, out
+    for i in range(8):
+        args = [FAKE] * 9
+        args[[0, 1, 3, 4, 5, 6, 7, 8][i]] = None
+        q, cs, gs, k, v, ci, gi, ns, out = args
+        assert _status(hga.hga_route_attend, c, q, 14336, 2048, 16384, cs, gs, k, v, ci, gi, ns, out) == E
 
 
 def test_tier_validation():
@@ -124,11 +132,18 @@ def test_tier_validation():
     assert _status(hga.hga_attend, *args, tier, tier, FAKE, FAKE, FAKE, None, None, 0) == hga.HGA_ERR_WORKSPACE
     assert _status(hga.hga_attend, *args, tier, tier, FAKE, FAKE, FAKE, None, FAKE, need - 1) == \
         hga.HGA_ERR_WORKSPACE
+    ra = (c, FAKE, 14336, 2048, 16384, FAKE)
+    assert _status(hga.hga_route_attend, *ra, (FAKE, FAKE, 14400), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE) == E
+    assert _status(hga.hga_route_attend, *ra, FAKE, (FAKE, FAKE, 1024), (FAKE, FAKE, 2048),
+                   FAKE, FAKE, FAKE, FAKE) == E
+    assert _status(hga.hga_route_attend, *ra, FAKE, tier, tier, FAKE, FAKE, FAKE, FAKE, None, None, 0) == \
+        hga.HGA_ERR_WORKSPACE
 
 
 def test_empty_query_range_is_a_no_op():
     c = cfg()
     hga.hga_route(c, FAKE, 16384, 0, 16384, FAKE, FAKE, FAKE, FAKE, FAKE)
     hga.hga_attend(c, FAKE, 16384, 0, 16384, FAKE, FAKE, FAKE, FAKE, FAKE)
+    hga.hga_route_attend(c, FAKE, 16384, 0, 16384, *[FAKE] * 8)
     hga.hga_build_summaries(c, None, 0, None, None)
     assert hga.hga_last_error() == ""
