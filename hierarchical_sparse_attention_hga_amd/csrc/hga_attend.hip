@@ -537,8 +537,9 @@ __global__ __launch_bounds__(kAttnThreads) void route_attend_bf16_kernel(FusedAr
   const bool wr = z == 0;
   int32_t* gout = F.r.group_idx + ((int64_t)b * S.hkv + h) * S.kg;
   const int g = S.g;
-  const int nsg = route::route_item<uint16_t>(F.r, b, h, rsm, wr, [&](int rank, int group) {
-    sm.runs[rank] = group * g;
+  int* runs = sm.runs;
+  const int nsg = route::route_item<uint16_t>(F.r, b, h, rsm, wr, [runs, wr, gout, g](int rank, int group) {
+    runs[rank] = group * g;
     if (wr) gout[rank] = group;
   });
   __syncthreads();

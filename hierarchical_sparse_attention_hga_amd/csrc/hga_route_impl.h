@@ -172,54 +172,72 @@ __device__ void wave_select(const unsigned long long* key, int n, int k, int* hi
 
 // Score summary rows c in [0, n) against the block query: row(c) points at d
 // float32 values; the order key goes to key[c]. Eight lanes per row,
-// kRowsInFlight rows per lane group per round, all loads issued first.
+// kRowsInFlight rows per lane group per round; a round's loads are all
+// issued before any is used, and the first round's may be issued early
+// (before the block query exists) by load_round.
+struct ScoreRound {
+  int c[kRowsInFlight];
+  float4 v[kQuadsPerLane][kRowsInFlight];
+};
+
 template <typename RowFn>
-__device__ void score_rows(const double* qbar, int d, int n, RowFn row, unsigned long long* key) {
+__device__ void load_round(int base, int d, int n, RowFn row, ScoreRound& rd) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane / kLanesPerCand, lic = lane % kLanesPerCand;
   constexpr int per_wave = 64 / kLanesPerCand;
   constexpr int per_round = kWaves * per_wave;
-  const int quads = d / 4;
-  for (int base = 0; base < n; base += kRowsInFlight * per_round) {
-    int c[kRowsInFlight];
-    const float* r[kRowsInFlight];
-    double acc[kRowsInFlight];
+  const float* r[kRowsInFlight];
+#pragma unroll
+  for (int u = 0; u < kRowsInFlight; ++u) {
+    rd.c[u] = base + u * per_round + wave * per_wave + sub;
+    r[u] = rd.c[u] < n ? row(rd.c[u]) : nullptr;
+  }
+#pragma unroll
+  for (int i = 0; i < kQuadsPerLane; ++i)
 #pragma unroll
     for (int u = 0; u < kRowsInFlight; ++u) {
-      c[u] = base + u * per_round + wave * per_wave + sub;
-      r[u] = c[u] < n ? row(c[u]) : nullptr;
-      acc[u] = 0.0;
-    }
-    // every load of the round is issued before the first use
-    float4 v[kQuadsPerLane][kRowsInFlight];
-#pragma unroll
-    for (int i = 0; i < kQuadsPerLane; ++i)
-#pragma unroll
-      for (int u = 0; u < kRowsInFlight; ++u) {
-        const int q4 = lic + i * kLanesPerCand;
-        v[i][u] = float4{0.f, 0.f, 0.f, 0.f};
-        if (r[u] && q4 < quads) v[i][u] = *reinterpret_cast<const float4*>(r[u] + 4 * q4);
-      }
-#pragma unroll
-    for (int i = 0; i < kQuadsPerLane; ++i) {
       const int q4 = lic + i * kLanesPerCand;
-      if (q4 >= quads) break;
-      const double q0 = qbar[4 * q4], q1 = qbar[4 * q4 + 1], q2 = qbar[4 * q4 + 2], q3 = qbar[4 * q4 + 3];
-#pragma unroll
-      for (int u = 0; u < kRowsInFlight; ++u) {
-        acc[u] += q0 * (double)v[i][u].x; acc[u] += q1 * (double)v[i][u].y;
-        acc[u] += q2 * (double)v[i][u].z; acc[u] += q3 * (double)v[i][u].w;
-      }
+      rd.v[i][u] = float4{0.f, 0.f, 0.f, 0.f};
+      if (r[u] && q4 < d / 4) rd.v[i][u] = *reinterpret_cast<const float4*>(r[u] + 4 * q4);
     }
+}
+
+__device__ inline void finish_round(const ScoreRound& rd, const double* qbar, int d, int n,
+                                    unsigned long long* key) {
+  const int lic = (threadIdx.x & 63) % kLanesPerCand;
+  double acc[kRowsInFlight];
+#pragma unroll
+  for (int u = 0; u < kRowsInFlight; ++u) acc[u] = 0.0;
+#pragma unroll
+  for (int i = 0; i < kQuadsPerLane; ++i) {
+    const int q4 = lic + i * kLanesPerCand;
+    if (q4 >= d / 4) break;
+    const double q0 = qbar[4 * q4], q1 = qbar[4 * q4 + 1], q2 = qbar[4 * q4 + 2], q3 = qbar[4 * q4 + 3];
 #pragma unroll
     for (int u = 0; u < kRowsInFlight; ++u) {
-#pragma unroll
-      for (int off = kLanesPerCand / 2; off > 0; off >>= 1) acc[u] += __shfl_xor(acc[u], off, kLanesPerCand);
-      if (lic == 0 && c[u] < n) key[c[u]] = order_key(acc[u]);
+      acc[u] += q0 * (double)rd.v[i][u].x; acc[u] += q1 * (double)rd.v[i][u].y;
+      acc[u] += q2 * (double)rd.v[i][u].z; acc[u] += q3 * (double)rd.v[i][u].w;
     }
+  }
+#pragma unroll
+  for (int u = 0; u < kRowsInFlight; ++u) {
+#pragma unroll
+    for (int off = kLanesPerCand / 2; off > 0; off >>= 1) acc[u] += __shfl_xor(acc[u], off, kLanesPerCand);
+    if (lic == 0 && rd.c[u] < n) key[rd.c[u]] = order_key(acc[u]);
   }
 }
 
+constexpr int kRoundRows = kRowsInFlight * kWaves * (64 / kLanesPerCand);   // rows per round
+
+// Rounds from row `from` on (a multiple of kRoundRows).
+template <typename RowFn>
+__device__ void score_rows(const double* qbar, int d, int n, RowFn row, unsigned long long* key, int from = 0) {
+  for (int base = from; base < n; base += kRoundRows) {
+    ScoreRound rd;
+    load_round(base, d, n, row, rd);
+    finish_round(rd, qbar, d, n, key);
+  }
+}
 
 struct RouteArgs {
   const void* q;
@@ -249,6 +267,18 @@ __device__ int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm, bool 
   const int64_t ms = s / S.c;
   const int gpc = S.c / S.g;
   const int tid = threadIdx.x, wave = tid >> 6;
+
+  // chunk-stage candidates [lo, hi); the first round of their summaries is
+  // requested now, so its latency overlaps the block query's
+  int64_t lo, hi;
+  fixed_windows(ms, S.sink_chunks, S.local_chunks, &lo, &hi);
+  const int ncand = (int)(hi - lo);
+  const int nsc = ncand < S.kc ? ncand : S.kc;
+  const bool chunk_select = nsc > 0 && nsc < ncand;
+  const float* csh = a.cs + (int64_t)h * (S.L / S.c) * d;
+  auto chunk_row = [&](int c) { return csh + (lo + c) * d; };
+  ScoreRound first;
+  if (chunk_select) load_round(0, d, ncand, chunk_row, first);
 
   // ---- 1. block query (float64)
   {
@@ -295,15 +325,16 @@ __device__ int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm, bool 
 
   const int64_t orow = (int64_t)b * S.hkv + h;
   // ---- 2-3. chunk stage
-  int64_t lo, hi;
-  fixed_windows(ms, S.sink_chunks, S.local_chunks, &lo, &hi);
-  const int ncand = (int)(hi - lo);
-  const int nsc = ncand < S.kc ? ncand : S.kc;
-  if (nsc > 0 && nsc < ncand) {
-    const float* csh = a.cs + (int64_t)h * (S.L / S.c) * d;
-    score_rows(sm.qbar, d, ncand, [&](int c) { return csh + (lo + c) * d; }, sm.key);
+  if (chunk_select) {
+    finish_round(first, sm.qbar, d, ncand, sm.key);
+    score_rows(sm.qbar, d, ncand, chunk_row, sm.key, kRoundRows);
     __syncthreads();
-    if (wave == 0) wave_select(sm.key, ncand, nsc, sm.hist, [&](int rank, int pos) { sm.chunks[rank] = (int)(lo + pos); });
+    // the functors handed to the select capture by value: a by-reference
+    // capture would keep the captured locals in scratch memory
+    int* kept = sm.chunks;
+    const int first_cand = (int)lo;
+    if (wave == 0)
+      wave_select(sm.key, ncand, nsc, sm.hist, [kept, first_cand](int rank, int pos) { kept[rank] = first_cand + pos; });
   } else {
     for (int i = tid; i < nsc; i += kThreads) sm.chunks[i] = (int)(lo + i);
   }
@@ -315,7 +346,8 @@ __device__ int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm, bool 
   const int ngc = nsc * gpc;
   const int nsg = ngc < S.kg ? ngc : S.kg;
   int32_t* gout = a.group_idx + orow * S.kg;   // written only with write_out
-  auto group_of = [&](int c) { return (int)((int64_t)sm.chunks[c / gpc] * gpc + c % gpc); };
+  const int* kept_chunks = sm.chunks;
+  auto group_of = [kept_chunks, gpc](int c) { return kept_chunks[c / gpc] * gpc + c % gpc; };
   if (nsg > 0 && nsg < ngc) {
     const int64_t gsplit = a.split / S.g;          // groups held in host memory
     const int64_t ngl = S.L / S.g;
@@ -325,7 +357,7 @@ __device__ int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm, bool 
                         : a.gs_dev + ((int64_t)h * (ngl - gsplit) + (j - gsplit)) * d;
     }, sm.key);
     __syncthreads();
-    if (wave == 0) wave_select(sm.key, ngc, nsg, sm.hist, [&](int rank, int pos) { emit(rank, group_of(pos)); });
+    if (wave == 0) wave_select(sm.key, ngc, nsg, sm.hist, [emit, group_of](int rank, int pos) { emit(rank, group_of(pos)); });
   } else {
     for (int i = tid; i < nsg; i += kThreads) emit(i, group_of(i));
   }
