@@ -180,16 +180,6 @@ __device__ inline void item_of_block(const Shape& S, int wpi, int* b, int* h, in
 }
 
 // ------------------------------------------------------------ bf16 MFMA kernel
-// Token of slot sl of tile t (-1 for an empty slot of the last routed tile).
-// Group sizes divide 64, so they are powers of two: lg = log2(g).
-__device__ inline int slot_token(const Plan& P, const int* runs, int lg, int t, int sl) {
-  if (t < P.nfix) return (int)((t < P.a ? t : P.bb + (t - P.a)) * kChunk) + sl;
-  if (t < P.nfix + P.nrt) {
-    const int run = ((t - P.nfix) << (6 - lg)) + (sl >> lg);
-    return run < P.nrouted ? runs[run] + (sl & ((1 << lg) - 1)) : -1;
-  }
-  return (int)P.s + sl;
-}
 
 // The running max used by the exponentials is raised only when a row's new
 // scores exceed it by more than 2^8 (in the log2 domain): probabilities then
@@ -287,20 +277,22 @@ __device__ inline void kv_bases(const AttnArgs& A, int h, const uint16_t** kb, c
 
 // This wave's share of one tile load: rows [RPW w, RPW w + RPW) of the tile,
 // each lane one 16-byte piece of K and of V written at its swizzled position
-// in the stage at LDS byte addresses k_lds / v_lds. row(sl) is the tensor row
-// of slot sl.
+// in the stage at LDS byte addresses k_lds / v_lds. row(i, sl) is the tensor
+// row of slot sl, the row of this lane in the wave's i-th load.
 template <int D, typename RowFn>
 __device__ inline void issue_tile(const uint16_t* kbase, const uint16_t* vbase, uint32_t k_lds, uint32_t v_lds,
                                   RowFn row) {
   constexpr int NP = D / 8;                   // 16-byte pieces per token row
   constexpr int RPI = 64 / NP;                // rows per direct-to-LDS wave load
   constexpr int RPW = kChunk / kAttnWaves;    // rows each wave loads per tile
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is made scalar, so the LDS destinations are scalar
+  // arithmetic and each load needs no lane-to-scalar move before setting M0
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int i = 0; i < RPW / RPI; ++i) {
     const int row0 = wave * RPW + i * RPI;
     const int rr = row0 + lane / NP;
-    const int64_t r = row(rr) * D;
+    const int64_t r = row(i, rr) * D;
     lds_dma16(kbase + r + ((lane % NP) ^ k_swizzle<D>(rr)) * 8, k_lds + (uint32_t)(row0 * D * 2));
     lds_dma16(vbase + r + ((lane % NP) ^ v_swizzle<D>(rr)) * 8, v_lds + (uint32_t)(row0 * D * 2));
   }
@@ -322,7 +314,7 @@ __device__ void attend_bf16_body(const AttnArgs& A, int b, int h, int z, const P
   const Shape& S = A.s;
   const int nt = P.ntiles;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5;                  // lane half
   const int col = lane & 31;                 // query column of this lane
   const int rb = z * kAttnWaves + wave;      // 32-row block of the item
@@ -346,12 +338,27 @@ __device__ void attend_bf16_body(const AttnArgs& A, int b, int h, int z, const P
   kv_bases<D, kStaged>(A, h, &kbase, &vbase);
   // Row of slot sl of tile t in kbase/vbase. Empty slots read token 0: their
   // probabilities are exactly zero, so any finite row will do.
+  // The run-table entries the rows of a tile need are read one tile ahead,
+  // unconditionally at a clamped index, and only used when that tile's loads
+  // issue (after a barrier): the reads never stall the loop.
+  constexpr int KIr = (kChunk / kAttnWaves) / (64 / (D / 8));   // loads per wave per tensor per tile
+  int raw[KIr];
+  auto run_of = [&](int t, int sl) { return ((t - P.nfix) << (6 - lg)) + (sl >> lg); };
+  auto fetch = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < KIr; ++i) {
+      const int rr = wave * (kChunk / kAttnWaves) + i * (64 / (D / 8)) + lane / (D / 8);
+      raw[i] = sm.runs[run_of(t, rr) & (kMaxRoutedAttn - 1)];
+    }
+  };
   auto issue = [&](int t) {
     const uint32_t off = (uint32_t)((t % kAttnStages) * kChunk * D * 2);
-    issue_tile<D>(kbase, vbase, lds_addr(&sm.k[0][0]) + off, lds_addr(&sm.v[0][0]) + off, [&](int sl) -> int64_t {
+    issue_tile<D>(kbase, vbase, lds_addr(&sm.k[0][0]) + off, lds_addr(&sm.v[0][0]) + off,
+                  [&](int i, int sl) -> int64_t {
       if (kStaged) return (item_lin * A.tiles_per_item + t) * kChunk + sl;
-      const int tok = slot_token(P, sm.runs, lg, t, sl);
-      return tok >= 0 ? tok : 0;
+      if (t < P.nfix) return (int64_t)((t < P.a ? t : P.bb + (t - P.a)) * kChunk) + sl;
+      if (t < P.nfix + P.nrt) return run_of(t, sl) < P.nrouted ? raw[i] + (sl & ((1 << lg) - 1)) : 0;
+      return P.s + sl;
     });
   };
 
@@ -386,9 +393,12 @@ __device__ void attend_bf16_body(const AttnArgs& A, int b, int h, int z, const P
   const char* sKb = reinterpret_cast<const char*>(&sm.k[0][0]);
   const char* sVb = reinterpret_cast<const char*>(&sm.v[0][0]);
 
-#pragma unroll
-  for (int t = 0; t < kAttnStages - 1; ++t)
-    if (t < nt && !(t == 0 && tile0_issued)) issue(t);
+  static_assert(kAttnStages == 2, "the run-table prefetch runs one tile ahead");
+  if (!tile0_issued) {
+    fetch(0);
+    issue(0);
+  }
+  fetch(1);
   for (int t = 0; t < nt; ++t) {
     // this thread's loads of tile t are done once only newer tiles are pending
     if (kAhead >= 2 && t + 2 < nt)
@@ -398,7 +408,10 @@ __device__ void attend_bf16_body(const AttnArgs& A, int b, int h, int z, const P
     else
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();   // every wave's loads of tile t landed; tile t - 1 is free
-    if (t + kAttnStages - 1 < nt) issue(t + kAttnStages - 1);
+    if (t + 1 < nt) {
+      issue(t + 1);
+      fetch(t + 2);
+    }
     if (!active) continue;
     const uint32_t stage = (uint32_t)((t % kAttnStages) * kChunk * RB);
     const char* kt = sKb + stage;
@@ -532,7 +545,7 @@ __global__ __launch_bounds__(kAttnThreads) void route_attend_bf16_kernel(FusedAr
     kv_bases<D, false>(F.a, h, &kbase, &vbase);
     const int64_t m0 = P.a > 0 ? 0 : P.bb;      // chunk of fixed tile 0
     issue_tile<D>(kbase, vbase, lds_addr(&sm.k[0][0]), lds_addr(&sm.v[0][0]),
-                  [&](int sl) -> int64_t { return m0 * kChunk + sl; });
+                  [&](int, int sl) -> int64_t { return m0 * kChunk + sl; });
   }
   const bool wr = z == 0;
   int32_t* gout = F.r.group_idx + ((int64_t)b * S.hkv + h) * S.kg;
