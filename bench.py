@@ -3,9 +3,11 @@
 A step is one pass of the whole path over one layer of one synthetic input:
 hga_build_summaries (group and chunk summaries of every key), then
 hga_route_attend (block queries, chunk stage, group stage and exact routed
-attention, one kernel), all on one stream with every input already in HBM.
-The same step through the separate hga_route and hga_attend calls is
-reported alongside.
+attention), all on one stream with every input already in HBM. With at most
+4 query heads per KV head hga_route_attend is one kernel; with more (the 64K
+layer's 8) the step runs the router and the attention kernels, timed apart.
+The 16K step through the separate hga_route and hga_attend calls is reported
+alongside.
 
 The workload is the 16,384-token training-segment shape (Qwen3-8B heads:
 32 query / 8 KV heads, head_dim 128, bf16, 2,048 active queries over a
@@ -14,10 +16,12 @@ The same line also reports the 65,536-token Qwen3-30B-A3B-shaped layer with
 its history in HBM and, separately, with its history in pinned host memory
 (that rate includes the PCIe transfer of the routed set).
 
-Output: one JSON line (see the keys below). ``roofline`` covers the
-route-and-attend kernel (the attention's flops over that kernel's duration,
-measured with HIP events on the launch stream over the timed steps);
-``cpu_baseline`` is the CPU oracle on a bounded sample of the same workload.
+Output: one JSON line (see the keys below). ``roofline`` covers the kernel
+that does the attention (the route-and-attend kernel, or the attention kernel
+where routing runs apart): the attention's algorithmic flops or bytes over
+that kernel's mean duration, measured with HIP events on the launch stream
+over the timed steps; ``cpu_baseline`` is the CPU oracle on a bounded sample
+of the same workload.
 """
 from __future__ import annotations
 
@@ -42,7 +46,7 @@ METRIC = "routed-attn query-tokens/sec per layer at 16K/64K; % of HBM or MFMA pe
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload index (default: the 16K segment)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -106,7 +110,7 @@ def to_dev(a, dtype, dev):
 class Workload:
     """Device buffers and one step of the path for one configuration."""
 
-    def __init__(self, cfg_id, split=0, fused=True):
+    def __init__(self, cfg_id, split=0, fused=None):
         import torch
 
         import hierarchical_sparse_attention_hga_amd as hga
@@ -132,6 +136,11 @@ class Workload:
         self.lse = torch.empty(cfg["hq"], nq, device=DEV)
         self.k_full = k
         self.split = split
+        # one kernel exactly where hga_route_attend fuses (bf16, K/V on the
+        # device, at most 4 query heads per KV head); otherwise the two calls
+        # are timed apart
+        if fused is None:
+            fused = cfg["dtype"] == "bf16" and split == 0 and cfg["hq"] // hkv <= 4
         self.fused = fused
         self.n_stages = 2 if fused else 3
         self.pins = []
@@ -149,39 +158,51 @@ class Workload:
         else:
             self.gs_t, self.k_t, self.v_t = self.gs, k, v
 
-    def step(self, ev=None):
+    def step(self, ev=None, timed=-1):
+        """One step; with ev, HIP events on the launch stream bracket stage
+        `timed` (0 summaries, 1 routing or routing + attention, 2 attention)."""
         hga, c = self.hga, self.c
-        if ev:
-            ev[0].record()
+
+        def mark(stage, k):
+            if ev is not None and stage == timed:
+                ev[k].record()
+        mark(0, 0)
         if self.split == 0:
             hga.hga_build_summaries(c, self.k_full, self.L, self.gs, self.cs)
-        if ev:
-            ev[1].record()
+        mark(0, 1)
+        mark(1, 0)
         if self.fused:
             hga.hga_route_attend(c, self.q, self.q0, self.nq, self.L, self.cs, self.gs_t, self.k_t, self.v_t,
                                  self.ci, self.gi, self.ns, self.out, self.lse, self.ws, self.wsb)
+            mark(1, 1)
         else:
             hga.hga_route(c, self.q, self.q0, self.nq, self.L, self.cs, self.gs_t, self.ci, self.gi, self.ns)
-            if ev:
-                ev[2].record()
+            mark(1, 1)
+            mark(2, 0)
             hga.hga_attend(c, self.q, self.q0, self.nq, self.L, self.k_t, self.v_t, self.gi, self.ns,
                            self.out, self.lse, self.ws, self.wsb)
-        if ev:
-            ev[self.n_stages].record()
+            mark(2, 1)
 
     def run(self, steps, warmup):
+        """Time `steps` steps. A timing event drains the queue, so each stage
+        is bracketed on one step of every 2 x n_stages (its own subset) and
+        half of the steps carry no event; stage times are means over their
+        subset."""
         torch = self.torch
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(self.n_stages + 1)] for _ in range(steps)]
+        cycle = 2 * self.n_stages
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        which = [i % cycle // 2 if i % 2 == 0 else -1 for i in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
-            self.step(evs[i])
+            self.step(evs[i], which[i])
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        stage = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(self.n_stages)] for e in evs]) * 1e3  # us
+        stage = [[evs[i][0].elapsed_time(evs[i][1]) * 1e3 for i in range(steps) if which[i] == j]
+                 for j in range(self.n_stages)]   # us
         return wall, stage
 
     def free(self):
@@ -200,11 +221,12 @@ def source_sha256():
     return hashlib.sha256(src).hexdigest()
 
 
-def measured_traffic(workload):
-    """HBM bytes per route-and-attend launch from the committed rocprofv3
-    counter runs (profiles/route_attend_bf16_<workload>.traffic.json), or None
-    when they are missing or were taken on different kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"route_attend_bf16_{workload}.traffic.json")
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` ("route_attend_bf16" or "attend_bf16")
+    from the committed rocprofv3 counter runs
+    (profiles/<kernel>_<workload>.traffic.json), or None when they are missing
+    or were taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}.traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -213,17 +235,17 @@ def measured_traffic(workload):
     return 1024.0 * (rec["fetch_kib"] * rec["fetch_factor"] + rec["write_kib"] * rec["write_factor"])
 
 
-def roofline(cfg, n_sel, attend_us, with_traffic=True):
+def roofline(cfg, n_sel, attend_us, kernel, with_traffic=True):
     flops, byts, _ = algorithmic(cfg, n_sel)
-    traffic = measured_traffic(cfg["name"]) if with_traffic else None
+    traffic = measured_traffic(cfg["name"], kernel) if with_traffic else None
     t_mfma = flops / PEAK_BF16
     t_hbm = byts / PEAK_HBM
     t = attend_us * 1e-6
     if t_mfma >= t_hbm:
-        return {"bound": "mfma", "achieved": flops / t / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+        return {"kernel": kernel, "bound": "mfma", "achieved": flops / t / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
                 "frac": flops / t / PEAK_BF16, "traffic": traffic, "traffic_unit": "HBM bytes per launch",
                 "algorithmic_flops": flops, "algorithmic_bytes": byts}
-    return {"bound": "hbm", "achieved": byts / t / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+    return {"kernel": kernel, "bound": "hbm", "achieved": byts / t / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
             "frac": byts / t / PEAK_HBM, "traffic": traffic, "traffic_unit": "HBM bytes per launch",
             "algorithmic_flops": flops, "algorithmic_bytes": byts}
 
@@ -252,15 +274,34 @@ def cpu_baseline(cfg_id, min_seconds=10.0):
                       f"summaries, routing, attention) repeated {reps}x in {el:.1f} s"}
 
 
-def measure(cfg_id, steps, warmup, split=0, fused=True):
+class Result:
+    """Timing of one workload: wall time of the timed steps and per-stage
+    means and medians (us)."""
+
+    def __init__(self, w, wall, stage):
+        self.cfg, self.fused, self.wall = w.cfg, w.fused, wall
+        self.ns = w.ns.cpu().numpy()
+        self.mean = [float(np.mean(x)) if x else float("nan") for x in stage]
+        self.med = [float(np.median(x)) if x else float("nan") for x in stage]
+
+    def stages(self, which):
+        v = self.mean if which == "mean" else self.med
+        if self.fused:
+            return {"summaries": v[0], "route_attend": v[1]}
+        return {"summaries": v[0], "route": v[1], "attend": v[2]}
+
+    def roofline(self, with_traffic=True):
+        if self.fused:
+            return roofline(self.cfg, self.ns, self.mean[1], "route_attend_bf16", with_traffic)
+        return roofline(self.cfg, self.ns, self.mean[2], "attend_bf16", with_traffic)
+
+
+def measure(cfg_id, steps, warmup, split=0, fused=None):
     w = Workload(cfg_id, split, fused)
     wall, stage = w.run(steps, warmup)
-    ns = w.ns.cpu().numpy()
-    cfg = w.cfg
+    r = Result(w, wall, stage)
     w.free()
-    med = np.median(stage, axis=0)
-    mean = stage.mean(axis=0)
-    return cfg, ns, wall, med, mean
+    return r
 
 
 def main():
@@ -274,42 +315,41 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
-    cfg, ns, wall, med, mean = measure(args.config, args.steps, args.warmup)
-    value = args.steps * cfg["n_q"] / wall
-    rl = roofline(cfg, ns, mean[1])
+    main_r = measure(args.config, args.steps, args.warmup)
+    cfg = main_r.cfg
+    value = args.steps * cfg["n_q"] / main_r.wall
     line = {
         "metric": METRIC, "value": value, "unit": "query-tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_r.wall / args.steps * 1e3,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg["dtype"],
         "data": "synthetic (seeded; Qwen3-shaped heads, rank-8 shared component, planted groups)",
         "config": {"workload": cfg["name"], "seq_len": cfg["L"], "n_q": cfg["n_q"], "q_heads": cfg["hq"],
                    "kv_heads": cfg["hkv"], "head_dim": cfg["d"], "top_chunks": cfg["top_chunks"],
                    "top_groups": cfg["top_groups"], "sink": cfg["sink"], "local": cfg["local"],
                    "kv_residency": "hbm"},
-        "stages_us_mean": {"summaries": mean[0], "route_attend": mean[1]},
-        "stages_us_median": {"summaries": med[0], "route_attend": med[1]},
-        "roofline": rl,
+        "stages_us_mean": main_r.stages("mean"),
+        "stages_us_median": main_r.stages("median"),
+        "roofline": main_r.roofline(),
     }
     if not args.no_extra:
         extra = {}
         half = max(args.steps // 2, 5)
-        cs_, nss, walls, meds, means = measure(args.config, half, args.warmup, fused=False)
-        extra["separate_calls"] = {
-            "value": half * cs_["n_q"] / walls, "unit": "query-tokens/s",
-            "note": "same step through hga_route then hga_attend; roofline of the attention kernel alone",
-            "stages_us_mean": {"summaries": means[0], "route": means[1], "attend": means[2]},
-            "roofline": roofline(cs_, nss, means[2], with_traffic=False)}
+        if main_r.fused:
+            sep = measure(args.config, half, args.warmup, fused=False)
+            extra["separate_calls"] = {
+                "value": half * sep.cfg["n_q"] / sep.wall, "unit": "query-tokens/s",
+                "note": "same step through hga_route then hga_attend; roofline of the attention kernel alone",
+                "stages_us_mean": sep.stages("mean"), "roofline": sep.roofline(with_traffic=False)}
         if args.config != 3:
-            c3, ns3, wall3, med3, mean3 = measure(3, half, args.warmup)
-            extra["64k_hbm"] = {"value": half * c3["n_q"] / wall3, "unit": "query-tokens/s",
-                                "stages_us_mean": {"summaries": mean3[0], "route_attend": mean3[1]},
-                                "roofline": roofline(c3, ns3, mean3[1])}
-            c3h, _, wallh, medh, meanh = measure(3, 5, 2, split=c3["tier_split"])
+            r3 = measure(3, half, args.warmup)
+            extra["64k_hbm"] = {"value": half * r3.cfg["n_q"] / r3.wall, "unit": "query-tokens/s",
+                                "stages_us_mean": r3.stages("mean"), "roofline": r3.roofline()}
+            rh = measure(3, 5, 2, split=r3.cfg["tier_split"])
             extra["64k_host_tier_pcie_inclusive"] = {
-                "value": 5 * c3h["n_q"] / wallh, "unit": "query-tokens/s",
+                "value": 5 * rh.cfg["n_q"] / rh.wall, "unit": "query-tokens/s",
                 "note": "history K/V and group summaries in pinned host memory; routed rows cross PCIe each "
                         "step (routing, then gather and attention)",
-                "stages_us_mean": {"route_gather_attend": meanh[1]}}
+                "stages_us_mean": rh.stages("mean")}
         line["also"] = extra
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.config)
