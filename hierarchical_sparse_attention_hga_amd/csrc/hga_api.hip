@@ -104,6 +104,21 @@ hga_status check_tier(const hga_tiered* t, const char* name, int64_t seq_len, in
   return HGA_OK;
 }
 
+// K and V tiers of one call: same split; with a host part, a bounded number
+// of fixed chunks and the workspace of the host-tier cache.
+hga_status check_kv_tier(const hga::Shape& s, const hga_tiered* k, const hga_tiered* v, void* workspace,
+                         size_t ws_bytes) {
+  if (k->split != v->split) return fail(HGA_ERR_INVALID_ARGUMENT, "k.split and v.split differ");
+  if (k->split == 0) return HGA_OK;
+  if (s.sink_chunks + s.local_chunks > hga::kMaxFixedTiered)
+    return fail(HGA_ERR_UNSUPPORTED, "with a host tier, sink and local windows may span at most %d chunks",
+                hga::kMaxFixedTiered);
+  const size_t need = hga::tier_cache_bytes(s, k->split);
+  if (!workspace || ws_bytes < need)
+    return fail(HGA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : (size_t)0);
+  return HGA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -114,7 +129,7 @@ size_t hga_workspace_size(const hga_config* cfg, int64_t seq_len, int64_t n_q, i
   switch (which) {
     case HGA_WS_ROUTE: return 0;
     case HGA_WS_ATTEND: return 0;
-    case HGA_WS_ATTEND_TIERED: return hga::staging_bytes(s);
+    case HGA_WS_ATTEND_TIERED: return hga::tier_cache_bytes(s, seq_len - n_q);
     default: fail(HGA_ERR_INVALID_ARGUMENT, "unknown workspace kind %d", which); return (size_t)-1;
   }
 }
@@ -162,13 +177,7 @@ hga_status hga_attend(const hga_config* cfg, const void* q, int64_t q_start, int
     return fail(HGA_ERR_INVALID_ARGUMENT, "q, out, n_sel and group_idx must be non-NULL");
   if ((st = check_tier(k, "k", seq_len, q_start)) != HGA_OK) return st;
   if ((st = check_tier(v, "v", seq_len, q_start)) != HGA_OK) return st;
-  if (k->split != v->split) return fail(HGA_ERR_INVALID_ARGUMENT, "k.split and v.split differ");
-  if (k->split > 0) {
-    const size_t need = hga::staging_bytes(s);
-    if (!workspace || ws_bytes < need)
-      return fail(HGA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
-                  workspace ? ws_bytes : (size_t)0);
-  }
+  if ((st = check_kv_tier(s, k, v, workspace, ws_bytes)) != HGA_OK) return st;
   hga::KVSrc kv{k->host, k->dev, v->host, v->dev, k->split};
   return device_status(hga::launch_attend(s, q, kv, group_idx, n_sel, out, lse, workspace, (hipStream_t)stream),
                        "hga_attend launch");
@@ -188,13 +197,7 @@ hga_status hga_route_attend(const hga_config* cfg, const void* q, int64_t q_star
   if ((st = check_tier(group_sum, "group_sum", seq_len, q_start)) != HGA_OK) return st;
   if ((st = check_tier(k, "k", seq_len, q_start)) != HGA_OK) return st;
   if ((st = check_tier(v, "v", seq_len, q_start)) != HGA_OK) return st;
-  if (k->split != v->split) return fail(HGA_ERR_INVALID_ARGUMENT, "k.split and v.split differ");
-  if (k->split > 0) {
-    const size_t need = hga::staging_bytes(s);
-    if (!workspace || ws_bytes < need)
-      return fail(HGA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
-                  workspace ? ws_bytes : (size_t)0);
-  }
+  if ((st = check_kv_tier(s, k, v, workspace, ws_bytes)) != HGA_OK) return st;
   const hipStream_t hs = (hipStream_t)stream;
   const float* gs_host = static_cast<const float*>(group_sum->host);
   const float* gs_dev = static_cast<const float*>(group_sum->dev);

@@ -22,9 +22,14 @@
 // float32 path (attend_f32_kernel): SIMT, a few lanes per query row, for the
 // float32 configurations.
 //
-// Host-tier path: K/V rows in pinned host memory are first gathered tile by
-// tile into a device staging buffer (gather_kernel); the attention kernels
-// then read the staged tiles contiguously.
+// Host-tier path (history rows [0, split) in pinned host memory): the chunks
+// of the history that any item of the call needs (its fixed windows and the
+// chunks of its kept groups) are marked, given slots in an HBM cache in the
+// caller's workspace, and copied there once each, so a chunk shared by many
+// query blocks crosses the host link once per call (the pages' VRAM cache of
+// routed sets shared across query blocks, "Long-Context Fine-Tuning with
+// Limited VRAM", section 2.1). The attention kernels then read history rows
+// from the cache and the rest from HBM.
 #include <limits.h>
 
 #include "hga_route_impl.h"
@@ -46,16 +51,23 @@ constexpr float kLn2 = 0.6931471805599453f;
 struct AttnArgs {
   const void* q;
   KVSrc kv;
-  const void* k_stage;     // staged tiles [item][tile][64][d] (host-tier path)
-  const void* v_stage;
+  const void* k_cache;     // host-tier path: cached history chunks, [Hkv][nch][64][d] by slot
+  const void* v_cache;
+  const int32_t* slot;     // [Hkv][nch]: cache slot of history chunk m of head h (-1: not needed)
+  int nch;                 // chunks in the host tier (split / 64)
   const int32_t* gidx;
   const int32_t* nsel;
   void* out;
   float* lse;
-  int64_t tiles_per_item;  // staging stride in tiles
   int wg_per_item;
   Shape s;
 };
+
+// Source rows of the host-tier path are encoded in one int: with kCacheFlag
+// set, a row of the cache ((h nch + slot) 64 + offset); without it, a row of
+// the head's device part (token - split). Without a host tier a source row is
+// the token itself.
+constexpr int kCacheFlag = 1 << 30;
 
 // ------------------------------------------------------------ token-set plan
 struct Plan {
@@ -135,17 +147,20 @@ __device__ Plan make_plan(const Shape& S, int b, int h, const int32_t* gidx, con
   return P;
 }
 
-// Token position of slot `slot` of tile t, or -1 for an empty slot.
-__device__ inline int64_t tile_token(const Plan& P, const int* runs, int g, int t, int slot) {
+// Source row of slot sl of tile t (see kCacheFlag), or -1 for an empty slot.
+// runs hold the kept groups' first rows and fixsrc the fixed chunks' first
+// rows (both encoded on the host-tier path, see translate_plan).
+__device__ inline int tile_src(const Plan& P, const int* runs, const int* fixsrc, int g, bool tiered, int64_t split,
+                               int t, int sl) {
   if (t < P.nfix) {
-    const int64_t m = t < P.a ? t : P.bb + (t - P.a);
-    return m * kChunk + slot;
+    if (tiered) return fixsrc[t] + sl;
+    return (int)((t < P.a ? t : P.bb + (t - P.a)) * kChunk) + sl;
   }
   if (t < P.nfix + P.nrt) {
-    const int r = (t - P.nfix) * (kChunk / g) + slot / g;
-    return r < P.nrouted ? (int64_t)runs[r] + slot % g : -1;
+    const int r = (t - P.nfix) * (kChunk / g) + sl / g;
+    return r < P.nrouted ? runs[r] + sl % g : -1;
   }
-  return P.s + slot;
+  return (int)(tiered ? P.s - split : P.s) + sl;
 }
 
 // Number of leading valid slots of tile t (the rest are empty).
@@ -157,12 +172,32 @@ __device__ inline int tile_limit(const Plan& P, int g, int t) {
   return kChunk;
 }
 
-// Address of the d-wide row of token `tok` of KV head h in a tiered tensor.
+// Host-tier path: rewrite the kept groups' first tokens in runs[] and the
+// fixed chunks' first tokens into encoded source rows (fixsrc[t] for fixed
+// tile t). Every history chunk used here was marked and given a slot.
+__device__ void translate_plan(const AttnArgs& A, int h, const Plan& P, int* runs, int* fixsrc) {
+  const int64_t split = A.kv.split;
+  const int nch = A.nch;
+  auto enc = [&](int64_t tok) -> int {
+    if (tok < split) {
+      const int64_t m = tok / kChunk;
+      const int sl = A.slot[(int64_t)h * nch + m];
+      // every chunk used here was marked; an unmarked one would read device
+      // row 0 rather than outside the cache
+      return sl >= 0 ? kCacheFlag | (int)(((int64_t)h * nch + sl) * kChunk + tok % kChunk) : 0;
+    }
+    return (int)(tok - split);
+  };
+  for (int i = threadIdx.x; i < P.nrouted; i += blockDim.x) runs[i] = enc(runs[i]);
+  for (int t = threadIdx.x; t < P.nfix; t += blockDim.x)
+    fixsrc[t] = enc((t < P.a ? t : P.bb + (t - P.a)) * kChunk);
+  __syncthreads();
+}
+
+// K or V row of a source row: the cache, or the head's device rows.
 template <typename T>
-__device__ inline const T* kv_row(const void* host, const void* dev, int64_t split, int64_t L, int d,
-                                  int h, int64_t tok) {
-  if (tok < split) return static_cast<const T*>(host) + ((int64_t)h * split + tok) * d;
-  return static_cast<const T*>(dev) + ((int64_t)h * (L - split) + (tok - split)) * d;
+__device__ inline const T* src_ptr(const T* dev_head, const T* cache, int src, int d) {
+  return (src & kCacheFlag) ? cache + (int64_t)(src & ~kCacheFlag) * d : dev_head + (int64_t)src * d;
 }
 
 // Item and workgroup slot of this workgroup. Consecutive items of one KV head
@@ -251,37 +286,37 @@ __device__ inline float pair_sum(float x) {
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
-// Shared memory of the bfloat16 attention: the K and V stage rings and the
-// item's routed run list.
+// Shared memory of the bfloat16 attention: the K and V stage rings, the
+// item's routed run list and, after it, the fixed chunks' source rows of the
+// host-tier path.
 template <int D>
 struct AttnSmem {
   uint16_t k[kAttnStages][kChunk * D];
   uint16_t v[kAttnStages][kChunk * D];
-  int runs[kMaxRoutedAttn];
+  int runs[kMaxRoutedAttn + kMaxFixedTiered];
   int scan[16];
 };
 
-// K/V row bases of KV head h: the staged tiles of the host-tier path, or the
-// head's device rows.
-template <int D, bool kStaged>
-__device__ inline void kv_bases(const AttnArgs& A, int h, const uint16_t** kb, const uint16_t** vb) {
-  const uint16_t* k = static_cast<const uint16_t*>(kStaged ? A.k_stage : A.kv.k_dev);
-  const uint16_t* v = static_cast<const uint16_t*>(kStaged ? A.v_stage : A.kv.v_dev);
-  if (!kStaged) {
-    k += (int64_t)h * A.s.L * D;
-    v += (int64_t)h * A.s.L * D;
-  }
-  *kb = k;
-  *vb = v;
+// K/V rows of KV head h: its device rows (rows [split, L) on the host-tier
+// path), and the cache of the host-tier path.
+struct KVRows {
+  const uint16_t *k_dev, *v_dev, *k_cache, *v_cache;
+};
+template <int D, bool kTiered>
+__device__ inline KVRows kv_rows(const AttnArgs& A, int h) {
+  const int64_t per_head = kTiered ? A.s.L - A.kv.split : A.s.L;
+  return KVRows{static_cast<const uint16_t*>(A.kv.k_dev) + (int64_t)h * per_head * D,
+                static_cast<const uint16_t*>(A.kv.v_dev) + (int64_t)h * per_head * D,
+                static_cast<const uint16_t*>(A.k_cache), static_cast<const uint16_t*>(A.v_cache)};
 }
 
 // This wave's share of one tile load: rows [RPW w, RPW w + RPW) of the tile,
 // each lane one 16-byte piece of K and of V written at its swizzled position
-// in the stage at LDS byte addresses k_lds / v_lds. row(i, sl) is the tensor
-// row of slot sl, the row of this lane in the wave's i-th load.
-template <int D, typename RowFn>
-__device__ inline void issue_tile(const uint16_t* kbase, const uint16_t* vbase, uint32_t k_lds, uint32_t v_lds,
-                                  RowFn row) {
+// in the stage at LDS byte addresses k_lds / v_lds. src(i, sl) is the source
+// row (see kCacheFlag) of slot sl, the row of this lane in the wave's i-th
+// load.
+template <int D, typename SrcFn>
+__device__ inline void issue_tile(const KVRows& kv, uint32_t k_lds, uint32_t v_lds, SrcFn src) {
   constexpr int NP = D / 8;                   // 16-byte pieces per token row
   constexpr int RPI = 64 / NP;                // rows per direct-to-LDS wave load
   constexpr int RPW = kChunk / kAttnWaves;    // rows each wave loads per tile
@@ -292,16 +327,18 @@ __device__ inline void issue_tile(const uint16_t* kbase, const uint16_t* vbase, 
   for (int i = 0; i < RPW / RPI; ++i) {
     const int row0 = wave * RPW + i * RPI;
     const int rr = row0 + lane / NP;
-    const int64_t r = row(i, rr) * D;
-    lds_dma16(kbase + r + ((lane % NP) ^ k_swizzle<D>(rr)) * 8, k_lds + (uint32_t)(row0 * D * 2));
-    lds_dma16(vbase + r + ((lane % NP) ^ v_swizzle<D>(rr)) * 8, v_lds + (uint32_t)(row0 * D * 2));
+    const int sr = src(i, rr);
+    lds_dma16(src_ptr(kv.k_dev, kv.k_cache, sr, D) + ((lane % NP) ^ k_swizzle<D>(rr)) * 8,
+              k_lds + (uint32_t)(row0 * D * 2));
+    lds_dma16(src_ptr(kv.v_dev, kv.v_cache, sr, D) + ((lane % NP) ^ v_swizzle<D>(rr)) * 8,
+              v_lds + (uint32_t)(row0 * D * 2));
   }
 }
 
 // Attention of item (b, h), workgroup slot z, over the token set of plan P
 // (runs in sm.runs). With tile0_issued the caller has already issued tile
 // 0's loads into stage 0.
-template <int D, bool kStaged>
+template <int D, bool kTiered>
 __device__ void attend_bf16_body(const AttnArgs& A, int b, int h, int z, const Plan& P, AttnSmem<D>& sm,
                                  bool tile0_issued) {
   constexpr int NP = D / 8;
@@ -322,7 +359,6 @@ __device__ void attend_bf16_body(const AttnArgs& A, int b, int h, int z, const P
   const int head = h * S.G + (rb >> 1);
   const int qi = (rb & 1) * 32 + col;        // position within the block
   const int64_t qrow = (int64_t)b * S.B + qi;  // row of Q / O
-  const int64_t item_lin = (int64_t)h * S.nb + b;
 
   // queries of this lane's column as MFMA B operands (d = 16 ks + 8 hl + e)
   bf16x8 qf[D / 16];
@@ -334,12 +370,12 @@ __device__ void attend_bf16_body(const AttnArgs& A, int b, int h, int z, const P
   }
 
   const int lg = __ffs(S.g) - 1;
-  const uint16_t *kbase, *vbase;
-  kv_bases<D, kStaged>(A, h, &kbase, &vbase);
-  // Row of slot sl of tile t in kbase/vbase. Empty slots read token 0: their
-  // probabilities are exactly zero, so any finite row will do.
-  // The run-table entries the rows of a tile need are read one tile ahead,
-  // unconditionally at a clamped index, and only used when that tile's loads
+  const KVRows kv = kv_rows<D, kTiered>(A, h);
+  // Source row of slot sl of tile t (see kCacheFlag). Empty slots read row 0
+  // of the head's device rows: their probabilities are exactly zero, so any
+  // finite row will do. The table entry a row needs (a kept group's first
+  // row, or on the host-tier path a fixed chunk's) is read one tile ahead, at
+  // an index clamped into the table, and only used when that tile's loads
   // issue (after a barrier): the reads never stall the loop.
   constexpr int KIr = (kChunk / kAttnWaves) / (64 / (D / 8));   // loads per wave per tensor per tile
   int raw[KIr];
@@ -348,17 +384,18 @@ __device__ void attend_bf16_body(const AttnArgs& A, int b, int h, int z, const P
 #pragma unroll
     for (int i = 0; i < KIr; ++i) {
       const int rr = wave * (kChunk / kAttnWaves) + i * (64 / (D / 8)) + lane / (D / 8);
-      raw[i] = sm.runs[run_of(t, rr) & (kMaxRoutedAttn - 1)];
+      const int idx = kTiered && t < P.nfix ? kMaxRoutedAttn + (t & (kMaxFixedTiered - 1))
+                                            : run_of(t, rr) & (kMaxRoutedAttn - 1);
+      raw[i] = sm.runs[idx];
     }
   };
+  const int64_t diag0 = kTiered ? P.s - A.kv.split : P.s;   // source row of the block's first token
   auto issue = [&](int t) {
     const uint32_t off = (uint32_t)((t % kAttnStages) * kChunk * D * 2);
-    issue_tile<D>(kbase, vbase, lds_addr(&sm.k[0][0]) + off, lds_addr(&sm.v[0][0]) + off,
-                  [&](int i, int sl) -> int64_t {
-      if (kStaged) return (item_lin * A.tiles_per_item + t) * kChunk + sl;
-      if (t < P.nfix) return (int64_t)((t < P.a ? t : P.bb + (t - P.a)) * kChunk) + sl;
+    issue_tile<D>(kv, lds_addr(&sm.k[0][0]) + off, lds_addr(&sm.v[0][0]) + off, [&](int i, int sl) -> int {
+      if (t < P.nfix) return kTiered ? raw[i] + sl : (int)((t < P.a ? t : P.bb + (t - P.a)) * kChunk) + sl;
       if (t < P.nfix + P.nrt) return run_of(t, sl) < P.nrouted ? raw[i] + (sl & ((1 << lg) - 1)) : 0;
-      return P.s + sl;
+      return (int)diag0 + sl;
     });
   };
 
@@ -507,13 +544,14 @@ __device__ void attend_bf16_body(const AttnArgs& A, int b, int h, int z, const P
 }
 
 // bfloat16 attention of items whose kept groups come from group_idx.
-template <int D, bool kStaged>
+template <int D, bool kTiered>
 __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(AttnArgs A) {
   __shared__ AttnSmem<D> sm;
   int b, h, z;
   item_of_block(A.s, A.wg_per_item, &b, &h, &z);
   const Plan P = make_plan(A.s, b, h, A.gidx, A.nsel, sm.runs, sm.scan, kMaxRoutedAttn);
-  attend_bf16_body<D, kStaged>(A, b, h, z, P, sm, false);
+  if (kTiered) translate_plan(A, h, P, sm.runs, sm.runs + kMaxRoutedAttn);
+  attend_bf16_body<D, kTiered>(A, b, h, z, P, sm, false);
 }
 
 // Route, then attend, in one workgroup per (item, slot): the router's kept
@@ -541,11 +579,9 @@ __global__ __launch_bounds__(kAttnThreads) void route_attend_bf16_kernel(FusedAr
   P.nfix = (int)(P.a + (ms - P.bb));
   const bool pre = P.nfix > 0;
   if (pre) {
-    const uint16_t *kbase, *vbase;
-    kv_bases<D, false>(F.a, h, &kbase, &vbase);
-    const int64_t m0 = P.a > 0 ? 0 : P.bb;      // chunk of fixed tile 0
-    issue_tile<D>(kbase, vbase, lds_addr(&sm.k[0][0]), lds_addr(&sm.v[0][0]),
-                  [&](int, int sl) -> int64_t { return m0 * kChunk + sl; });
+    const int m0 = P.a > 0 ? 0 : (int)P.bb;    // chunk of fixed tile 0
+    issue_tile<D>(kv_rows<D, false>(F.a, h), lds_addr(&sm.k[0][0]), lds_addr(&sm.v[0][0]),
+                  [&](int, int sl) -> int { return m0 * kChunk + sl; });
   }
   const bool wr = z == 0;
   int32_t* gout = F.r.group_idx + ((int64_t)b * S.hkv + h) * S.kg;
@@ -564,7 +600,7 @@ __global__ __launch_bounds__(kAttnThreads) void route_attend_bf16_kernel(FusedAr
 
 // ------------------------------------------------------------ float32 SIMT kernel
 // 256 threads; TPR lanes per query row, each owning D / TPR dimensions.
-template <int D, bool kStaged>
+template <int D, bool kTiered>
 __global__ __launch_bounds__(256) void attend_f32_kernel(AttnArgs A) {
   constexpr int NT = 256;
   constexpr int TPR = D <= 32 ? 1 : D / 32;   // lanes per row
@@ -573,13 +609,19 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttnArgs A) {
   constexpr int HALF = 32;                    // tokens per LDS sub-tile
   __shared__ __align__(16) float sK[HALF * D];
   __shared__ __align__(16) float sV[HALF * D];
-  __shared__ int sRuns[kMaxRouted];
+  __shared__ int sRuns[kMaxRouted + kMaxFixedTiered];
   __shared__ int sScan[16];
 
   const Shape& S = A.s;
   int b, h, z;
   item_of_block(S, A.wg_per_item, &b, &h, &z);
   const Plan P = make_plan(S, b, h, A.gidx, A.nsel, sRuns, sScan, kMaxRouted);
+  if (kTiered) translate_plan(A, h, P, sRuns, sRuns + kMaxRouted);
+  const int64_t per_head = kTiered ? S.L - A.kv.split : S.L;
+  const float* kdev = static_cast<const float*>(A.kv.k_dev) + (int64_t)h * per_head * D;
+  const float* vdev = static_cast<const float*>(A.kv.v_dev) + (int64_t)h * per_head * D;
+  const float* kc = static_cast<const float*>(A.k_cache);
+  const float* vc = static_cast<const float*>(A.v_cache);
   const int tid = threadIdx.x;
   const int row = z * ROWS + tid / TPR;       // row of the item: head-local * 64 + qi
   const int part = tid % TPR;
@@ -587,7 +629,6 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttnArgs A) {
   const int head = h * S.G + row / S.B;
   const int qi = row % S.B;
   const int64_t qrow = (int64_t)b * S.B + qi;
-  const int64_t item_lin = (int64_t)h * S.nb + b;
 
   float q[DPT], o[DPT];
 #pragma unroll
@@ -607,16 +648,10 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttnArgs A) {
         const int sl = i / (D / 4), e4 = i % (D / 4);
         const int slot = half * HALF + sl;
         float4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
-        if (kStaged) {
-          const int64_t off = ((item_lin * A.tiles_per_item + t) * kChunk + slot) * D + 4 * e4;
-          kx = *reinterpret_cast<const float4*>(static_cast<const float*>(A.k_stage) + off);
-          vx = *reinterpret_cast<const float4*>(static_cast<const float*>(A.v_stage) + off);
-        } else {
-          const int64_t tok = tile_token(P, sRuns, S.g, t, slot);
-          if (tok >= 0) {
-            kx = *reinterpret_cast<const float4*>(kv_row<float>(A.kv.k_host, A.kv.k_dev, A.kv.split, S.L, D, h, tok) + 4 * e4);
-            vx = *reinterpret_cast<const float4*>(kv_row<float>(A.kv.v_host, A.kv.v_dev, A.kv.split, S.L, D, h, tok) + 4 * e4);
-          }
+        const int src = tile_src(P, sRuns, sRuns + kMaxRouted, S.g, kTiered, A.kv.split, t, slot);
+        if (src >= 0) {
+          kx = *reinterpret_cast<const float4*>(src_ptr(kdev, kc, src, D) + 4 * e4);
+          vx = *reinterpret_cast<const float4*>(src_ptr(vdev, vc, src, D) + 4 * e4);
         }
         *reinterpret_cast<float4*>(&sK[sl * D + 4 * e4]) = kx;
         *reinterpret_cast<float4*>(&sV[sl * D + 4 * e4]) = vx;
@@ -661,99 +696,165 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttnArgs A) {
   }
 }
 
-// ------------------------------------------------------------ host-tier gather
-// One workgroup per (item, tile): copies the tile's 64 K and V rows (empty
-// slots as zeros) from pinned host or device memory into the staging buffer.
-template <typename T>
-__global__ __launch_bounds__(256) void gather_kernel(AttnArgs A) {
+// ------------------------------------------------------------ host-tier cache
+__global__ __launch_bounds__(256) void fill_zero_kernel(int32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+// Mark the history chunks (below split) item (b, h) needs: its fixed chunks
+// and the chunks of its usable kept groups. One workgroup per item; every
+// writer stores the same 1.
+__global__ __launch_bounds__(256) void mark_kernel(AttnArgs A, int32_t* need) {
   __shared__ int sRuns[kMaxRouted];
   __shared__ int sScan[16];
   const Shape& S = A.s;
-  const int64_t item_lin = blockIdx.x;            // h * nb + b
-  const int h = (int)(item_lin / S.nb), b = (int)(item_lin % S.nb);
+  const int h = (int)(blockIdx.x / S.nb), b = (int)(blockIdx.x % S.nb);
   const Plan P = make_plan(S, b, h, A.gidx, A.nsel, sRuns, sScan, kMaxRouted);
-  const int d = S.d;
+  int32_t* nh = need + (int64_t)h * A.nch;
+  for (int i = threadIdx.x; i < P.nrouted; i += blockDim.x)
+    if (sRuns[i] < A.kv.split) nh[sRuns[i] / kChunk] = 1;
+  for (int t = threadIdx.x; t < P.nfix; t += blockDim.x) {
+    const int64_t m = t < P.a ? t : P.bb + (t - P.a);
+    if (m < A.nch) nh[m] = 1;
+  }
+}
+
+// Cache slots of the marked chunks: per head (one workgroup each), an
+// exclusive scan of the flags in chunk order; -1 for unmarked chunks.
+__global__ __launch_bounds__(1024) void slot_kernel(const int32_t* need, int32_t* slot, int nch) {
+  __shared__ int sScan[16];
+  constexpr int kPer = kMaxCand / 1024;
+  const int32_t* nh = need + (int64_t)blockIdx.x * nch;
+  int32_t* sh = slot + (int64_t)blockIdx.x * nch;
+  const int c0 = threadIdx.x * kPer;
+  int f[kPer], cnt = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    f[k] = c0 + k < nch ? nh[c0 + k] : 0;
+    cnt += f[k];
+  }
+  int tot;
+  int next = block_scan<false>(cnt, sScan, &tot);
+#pragma unroll
+  for (int k = 0; k < kPer; ++k)
+    if (c0 + k < nch) {
+      sh[c0 + k] = f[k] ? next : -1;
+      next += f[k];
+    }
+}
+
+// Copy each marked history chunk of K and V (64 rows) from pinned host memory
+// into its cache slot. One workgroup per (chunk, KV head); unmarked chunks
+// return at once. Every thread issues all its loads before its stores.
+template <typename T>
+__global__ __launch_bounds__(256) void copy_kernel(AttnArgs A) {
+  const int m = blockIdx.x, h = blockIdx.y;
+  const int sl = A.slot[(int64_t)h * A.nch + m];
+  if (sl < 0) return;
+  const int d = A.s.d;
+  const int64_t split = A.kv.split;
   constexpr int EPV = 16 / sizeof(T);             // elements per 16-byte piece
+  constexpr int kPer = 8;
   const int pieces = kChunk * d / EPV;
-  for (int t = blockIdx.y; t < P.ntiles; t += gridDim.y) {
-    T* kd = static_cast<T*>(const_cast<void*>(A.k_stage)) + (item_lin * A.tiles_per_item + t) * kChunk * d;
-    T* vd = static_cast<T*>(const_cast<void*>(A.v_stage)) + (item_lin * A.tiles_per_item + t) * kChunk * d;
-    for (int p = threadIdx.x; p < pieces; p += blockDim.x) {
-      const int sl = p / (d / EPV), dp = p % (d / EPV);
-      const int64_t tok = tile_token(P, sRuns, S.g, t, sl);
-      u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-      if (tok >= 0) {
-        kx = *reinterpret_cast<const u32x4*>(kv_row<T>(A.kv.k_host, A.kv.k_dev, A.kv.split, S.L, d, h, tok) + dp * EPV);
-        vx = *reinterpret_cast<const u32x4*>(kv_row<T>(A.kv.v_host, A.kv.v_dev, A.kv.split, S.L, d, h, tok) + dp * EPV);
+  const T* ks = static_cast<const T*>(A.kv.k_host) + ((int64_t)h * split + (int64_t)m * kChunk) * d;
+  const T* vs = static_cast<const T*>(A.kv.v_host) + ((int64_t)h * split + (int64_t)m * kChunk) * d;
+  T* kd = static_cast<T*>(const_cast<void*>(A.k_cache)) + ((int64_t)h * A.nch + sl) * kChunk * d;
+  T* vd = static_cast<T*>(const_cast<void*>(A.v_cache)) + ((int64_t)h * A.nch + sl) * kChunk * d;
+  for (int base = threadIdx.x; base < pieces; base += blockDim.x * kPer) {
+    u32x4 kx[kPer], vx[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int p = base + u * blockDim.x;
+      if (p < pieces) {
+        kx[u] = *reinterpret_cast<const u32x4*>(ks + (int64_t)p * EPV);
+        vx[u] = *reinterpret_cast<const u32x4*>(vs + (int64_t)p * EPV);
       }
-      *reinterpret_cast<u32x4*>(kd + (int64_t)sl * d + dp * EPV) = kx;
-      *reinterpret_cast<u32x4*>(vd + (int64_t)sl * d + dp * EPV) = vx;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int p = base + u * blockDim.x;
+      if (p < pieces) {
+        *reinterpret_cast<u32x4*>(kd + (int64_t)p * EPV) = kx[u];
+        *reinterpret_cast<u32x4*>(vd + (int64_t)p * EPV) = vx[u];
+      }
     }
   }
 }
 
-template <int D, bool kStaged>
+template <int D, bool kTiered>
 hipError_t launch_bf16(const AttnArgs& a, int64_t items, hipStream_t st) {
-  attend_bf16_kernel<D, kStaged><<<dim3((unsigned)(items * a.wg_per_item)), dim3(kAttnThreads), 0, st>>>(a);
+  attend_bf16_kernel<D, kTiered><<<dim3((unsigned)(items * a.wg_per_item)), dim3(kAttnThreads), 0, st>>>(a);
   return hipGetLastError();
 }
 
-template <int D, bool kStaged>
+template <int D, bool kTiered>
 hipError_t launch_f32(const AttnArgs& a, int64_t items, hipStream_t st) {
-  attend_f32_kernel<D, kStaged><<<dim3((unsigned)(items * a.wg_per_item)), dim3(256), 0, st>>>(a);
+  attend_f32_kernel<D, kTiered><<<dim3((unsigned)(items * a.wg_per_item)), dim3(256), 0, st>>>(a);
   return hipGetLastError();
 }
 
-template <bool kStaged>
+template <bool kTiered>
 hipError_t dispatch_f32(const AttnArgs& a, int64_t items, hipStream_t st) {
   switch (a.s.d) {
-    case 4: return launch_f32<4, kStaged>(a, items, st);
-    case 8: return launch_f32<8, kStaged>(a, items, st);
-    case 16: return launch_f32<16, kStaged>(a, items, st);
-    case 32: return launch_f32<32, kStaged>(a, items, st);
-    case 64: return launch_f32<64, kStaged>(a, items, st);
-    case 128: return launch_f32<128, kStaged>(a, items, st);
+    case 4: return launch_f32<4, kTiered>(a, items, st);
+    case 8: return launch_f32<8, kTiered>(a, items, st);
+    case 16: return launch_f32<16, kTiered>(a, items, st);
+    case 32: return launch_f32<32, kTiered>(a, items, st);
+    case 64: return launch_f32<64, kTiered>(a, items, st);
+    case 128: return launch_f32<128, kTiered>(a, items, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-size_t staging_bytes(const Shape& s) {
+size_t tier_cache_bytes(const Shape& s, int64_t split) {
+  const int64_t nch = split / kChunk;
   const size_t esz = s.dtype == HGA_BF16 ? 2 : 4;
-  return 2 * (size_t)(s.nb * s.hkv) * (size_t)max_tiles(s) * kChunk * (size_t)s.d * esz;
+  const size_t flags = ((2 * (size_t)s.hkv * nch * sizeof(int32_t)) + 255) & ~(size_t)255;
+  return flags + 2 * (size_t)s.hkv * nch * kChunk * (size_t)s.d * esz;
 }
 
 hipError_t launch_attend(const Shape& s, const void* q, const KVSrc& kv, const int32_t* group_idx,
-                         const int32_t* n_sel, void* out, float* lse, void* staging, hipStream_t st) {
+                         const int32_t* n_sel, void* out, float* lse, void* workspace, hipStream_t st) {
   const int64_t items = s.nb * s.hkv;
   if (items == 0) return hipSuccess;
   AttnArgs a{};
   a.q = q; a.kv = kv; a.gidx = group_idx; a.nsel = n_sel; a.out = out; a.lse = lse; a.s = s;
-  a.tiles_per_item = max_tiles(s);
-  const bool staged = kv.split > 0;
-  if (staged) {
+  const bool tiered = kv.split > 0;
+  if (tiered) {
+    // workspace: [need][slot] int32 [Hkv][nch], then the K and V caches
+    const int nch = (int)(kv.split / kChunk);
     const size_t esz = s.dtype == HGA_BF16 ? 2 : 4;
-    a.k_stage = staging;
-    a.v_stage = static_cast<char*>(staging) + (size_t)items * a.tiles_per_item * kChunk * s.d * esz;
-    const int64_t ty = a.tiles_per_item < 64 ? a.tiles_per_item : 64;
+    int32_t* need = static_cast<int32_t*>(workspace);
+    int32_t* slot = need + (int64_t)s.hkv * nch;
+    char* cache = static_cast<char*>(workspace) + (((2 * (size_t)s.hkv * nch * sizeof(int32_t)) + 255) & ~(size_t)255);
+    a.slot = slot;
+    a.nch = nch;
+    a.k_cache = cache;
+    a.v_cache = cache + (size_t)s.hkv * nch * kChunk * s.d * esz;
+    const int64_t nflags = (int64_t)s.hkv * nch;
+    fill_zero_kernel<<<dim3((unsigned)((nflags + 255) / 256)), dim3(256), 0, st>>>(need, nflags);
+    mark_kernel<<<dim3((unsigned)items), dim3(256), 0, st>>>(a, need);
+    slot_kernel<<<dim3((unsigned)s.hkv), dim3(1024), 0, st>>>(need, slot, nch);
     if (s.dtype == HGA_BF16)
-      gather_kernel<uint16_t><<<dim3((unsigned)items, (unsigned)ty), dim3(256), 0, st>>>(a);
+      copy_kernel<uint16_t><<<dim3((unsigned)nch, (unsigned)s.hkv), dim3(256), 0, st>>>(a);
     else
-      gather_kernel<float><<<dim3((unsigned)items, (unsigned)ty), dim3(256), 0, st>>>(a);
+      copy_kernel<float><<<dim3((unsigned)nch, (unsigned)s.hkv), dim3(256), 0, st>>>(a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (s.dtype == HGA_BF16) {
     a.wg_per_item = (2 * s.G + kAttnWaves - 1) / kAttnWaves;
-    if (s.d == 128) return staged ? launch_bf16<128, true>(a, items, st) : launch_bf16<128, false>(a, items, st);
-    if (s.d == 64) return staged ? launch_bf16<64, true>(a, items, st) : launch_bf16<64, false>(a, items, st);
+    if (s.d == 128) return tiered ? launch_bf16<128, true>(a, items, st) : launch_bf16<128, false>(a, items, st);
+    if (s.d == 64) return tiered ? launch_bf16<64, true>(a, items, st) : launch_bf16<64, false>(a, items, st);
     return hipErrorInvalidValue;
   }
   const int tpr = s.d <= 32 ? 1 : s.d / 32;
   const int rows = 256 / tpr;
   a.wg_per_item = (s.G * s.B + rows - 1) / rows;
-  return staged ? dispatch_f32<true>(a, items, st) : dispatch_f32<false>(a, items, st);
+  return tiered ? dispatch_f32<true>(a, items, st) : dispatch_f32<false>(a, items, st);
 }
 
 // One kernel when one workgroup holds every query row of an item (2 G <= 8
@@ -772,7 +873,6 @@ hipError_t launch_route_attend(const Shape& s, const void* q, const float* cs, c
   FusedArgs f{};
   f.r = route::RouteArgs{q, cs, gs_host, gs_dev, gs_split, chunk_idx, group_idx, n_sel, s};
   f.a.q = q; f.a.kv = kv; f.a.out = out; f.a.lse = lse; f.a.s = s;
-  f.a.tiles_per_item = max_tiles(s);
   f.a.wg_per_item = (2 * s.G + kAttnWaves - 1) / kAttnWaves;
   const dim3 grid((unsigned)(items * f.a.wg_per_item)), block(kAttnThreads);
   if (s.d == 128)

@@ -21,6 +21,9 @@ constexpr int kMaxRouted = 4096;
 constexpr int kMaxRoutedAttn = 2048;
 // Most chunks the router may keep per item (LDS list of the group stage).
 constexpr int kMaxKeptChunks = 2048;
+// Most fixed (sink + local) chunks per item when the history is in host
+// memory (LDS table of their cached source rows).
+constexpr int kMaxFixedTiered = 256;
 
 // Validated problem shape shared by the launchers.
 struct Shape {
@@ -44,12 +47,6 @@ __host__ __device__ inline void fixed_windows(int64_t ms, int sink_chunks, int l
   *bb = lo > aa ? lo : aa;
 }
 
-// Number of 64-token tiles of one item's token set: fixed chunks, routed
-// groups packed 64/g per tile, and the block's own tile.
-__host__ __device__ inline int64_t max_tiles(const Shape& s) {
-  return (int64_t)s.sink_chunks + s.local_chunks + ((int64_t)s.kg * s.g + kChunk - 1) / kChunk + 1;
-}
-
 hipError_t launch_summaries(const Shape& s, const void* k, float* gs, float* cs, hipStream_t st);
 
 hipError_t launch_route(const Shape& s, const void* q, const float* cs, const float* gs_host,
@@ -65,11 +62,13 @@ struct KVSrc {
   int64_t split;
 };
 
-// Bytes of the staging buffer the tiered path gathers into.
-size_t staging_bytes(const Shape& s);
+// Workspace bytes of the host-tier path for a history of `split` tokens in
+// host memory: chunk flags and slots, and an HBM cache able to hold every
+// history chunk of K and V.
+size_t tier_cache_bytes(const Shape& s, int64_t split);
 
 hipError_t launch_attend(const Shape& s, const void* q, const KVSrc& kv, const int32_t* group_idx,
-                         const int32_t* n_sel, void* out, float* lse, void* staging, hipStream_t st);
+                         const int32_t* n_sel, void* out, float* lse, void* workspace, hipStream_t st);
 
 // Routing and attention in one kernel (bfloat16, K/V all on the device).
 bool fused_route_attend_supported(const Shape& s, int64_t kv_split);

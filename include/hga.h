@@ -99,10 +99,13 @@ typedef struct {
 enum { HGA_WS_ROUTE = 0, HGA_WS_ATTEND = 1, HGA_WS_ATTEND_TIERED = 2 };
 
 /* Bytes of device workspace that hga_route (which = HGA_WS_ROUTE) or
- * hga_attend (HGA_WS_ATTEND with everything on the device,
+ * hga_attend / hga_route_attend (HGA_WS_ATTEND with everything on the device,
  * HGA_WS_ATTEND_TIERED with K/V split at a token > 0) needs for this shape.
- * Returns 0 when no workspace is needed, and (size_t)-1 when the config or
- * sizes are invalid. */
+ * The tiered figure holds for every split <= seq_len - n_q: it covers chunk
+ * flags and slots and an HBM cache as large as the whole host part of K and V
+ * (the attention copies each history chunk any query block needs into it once
+ * per call). Returns 0 when no workspace is needed, and (size_t)-1 when the
+ * config or sizes are invalid. */
 size_t hga_workspace_size(const hga_config* cfg, int64_t seq_len, int64_t n_q, int32_t which);
 
 /* Key summaries (section 2.1, first paragraph).
@@ -150,7 +153,13 @@ hga_status hga_route(const hga_config* cfg, const void* q, int64_t q_start, int6
  *   q          device, [Hq][n_q][d] of cfg->dtype.
  *   k, v       [Hkv][seq_len][d] of cfg->dtype, tiered at a token split
  *              (a multiple of chunk_size, <= q_start). With split > 0 the
- *              routed rows are first gathered into the workspace.
+ *              history chunks that any query block of the call needs (its
+ *              sink and local chunks, the chunks of its kept groups) are
+ *              copied once each into an HBM cache in the workspace, and the
+ *              attention reads history rows from there (the pages' VRAM cache
+ *              of routed sets shared across query blocks, section 2.1); sink
+ *              and local windows may then span at most 256 chunks
+ *              (HGA_ERR_UNSUPPORTED otherwise).
  *   group_idx  device, [n_q/64][Hkv][top_groups] as written by hga_route.
  *              An entry is usable when it is >= 0, its group ends by the block
  *              start and it lies outside the sink and local chunks; a usable

@@ -44,9 +44,11 @@ def test_workspace_sizes():
     c = cfg()
     assert hga.hga_workspace_size(c, 16384, 2048, hga.HGA_WS_ROUTE) == 0
     assert hga.hga_workspace_size(c, 16384, 2048, hga.HGA_WS_ATTEND) == 0
-    # staging: K and V, every (block, KV head) item, max tiles of 64 rows of d bf16
-    tiles = 1 + 2 + (64 * 8 + 63) // 64 + 1
-    assert hga.hga_workspace_size(c, 16384, 2048, hga.HGA_WS_ATTEND_TIERED) == 2 * 32 * 8 * tiles * 64 * 128 * 2
+    # host-tier cache: int32 flags and slots per (KV head, history chunk), padded to
+    # 256 bytes, then K and V rows of every history chunk (history <= seq_len - n_q)
+    nch = (16384 - 2048) // 64
+    flags = (2 * 8 * nch * 4 + 255) // 256 * 256
+    assert hga.hga_workspace_size(c, 16384, 2048, hga.HGA_WS_ATTEND_TIERED) == flags + 2 * 8 * nch * 64 * 128 * 2
     assert hga.hga_workspace_size(c, 16384, 2048, 7) == 2**64 - 1
     assert hga.hga_workspace_size(cfg(head_dim=96), 16384, 2048, 0) == 2**64 - 1
 
@@ -126,12 +128,18 @@ def test_tier_validation():
     assert _status(hga.hga_route, *args, FAKE, (None, FAKE, 1024), FAKE, FAKE, FAKE) == E    # host NULL
     assert _status(hga.hga_route, *args, FAKE, (FAKE, FAKE, 1000), FAKE, FAKE, FAKE) == hga.HGA_ERR_UNSUPPORTED
     assert _status(hga.hga_attend, *args, (FAKE, FAKE, 1024), (FAKE, FAKE, 2048), FAKE, FAKE, FAKE) == E
-    # tiered K/V needs the staging workspace
-    need = hga.hga_workspace_size(c, 16384, 2048, hga.HGA_WS_ATTEND_TIERED)
+    # tiered K/V needs the host-tier cache workspace: for a split of 1024 tokens
+    # (16 chunks), flags and slots (1 KiB) and K/V of 16 chunks per KV head
     tier = (FAKE, FAKE, 1024)
+    need = 1024 + 2 * 8 * 16 * 64 * 128 * 2
+    assert need <= hga.hga_workspace_size(c, 16384, 2048, hga.HGA_WS_ATTEND_TIERED)
     assert _status(hga.hga_attend, *args, tier, tier, FAKE, FAKE, FAKE, None, None, 0) == hga.HGA_ERR_WORKSPACE
     assert _status(hga.hga_attend, *args, tier, tier, FAKE, FAKE, FAKE, None, FAKE, need - 1) == \
         hga.HGA_ERR_WORKSPACE
+    # the host-tier cache bounds the fixed windows (sink + local chunks)
+    wide = cfg(sink_tokens=64 * 200, local_tokens=64 * 100)
+    assert _status(hga.hga_attend, wide, FAKE, 14336, 2048, 16384, tier, tier, FAKE, FAKE, FAKE, None, FAKE,
+                   need) == hga.HGA_ERR_UNSUPPORTED
     ra = (c, FAKE, 14336, 2048, 16384, FAKE)
     assert _status(hga.hga_route_attend, *ra, (FAKE, FAKE, 14400), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE) == E
     assert _status(hga.hga_route_attend, *ra, FAKE, (FAKE, FAKE, 1024), (FAKE, FAKE, 2048),

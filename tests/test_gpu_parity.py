@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 import oracle
+import synth
 from harness import check_outputs, check_routing, gpu_run, inputs, oracle_route
 
 pytestmark = pytest.mark.gpu
@@ -103,3 +104,34 @@ def test_attention_with_oracle_selection(cfg_id):
     idx = [b * hkv + h for b, h in items]
     ro, rl = oracle.attend(cfg, f["q"], f["k"], f["v"], items, ref[1][idx], ref[2][idx, 1])
     check_outputs(cfg, gpu, items, ro, rl)
+
+
+@pytest.mark.parametrize("case", ["f32", "bf16_d64_g4", "split_below_q_start", "wide_windows"])
+def test_host_tier_cache_small_shapes(case):
+    """The host-tier path (history chunks marked, given cache slots and copied
+    once each) is bit-identical to the all-HBM run on small shapes: fp32,
+    d = 64 with 4-token groups, a split well below the first query (the local
+    windows and some kept groups then come from HBM), wide sink/local windows."""
+    from test_gpu_edges import small
+    over = {"f32": dict(dtype="f32", d=64, rope_theta=None),
+            "bf16_d64_g4": dict(d=64, group=4, top_groups=20),
+            "split_below_q_start": dict(L=2048, n_q=512),
+            "wide_windows": dict(L=2048, n_q=512, sink=192, local=256)}[case]
+    cfg = small(**over)
+    x = synth.make_inputs(cfg)
+    split = {"split_below_q_start": 768, "wide_windows": 1024}.get(case, cfg["L"] - cfg["n_q"])
+    print(f"[host tier cache] {case} split={split}", flush=True)
+    a = gpu_run(cfg, x)
+    b = gpu_run(cfg, x, split=split)
+    for key in ("chunk_idx", "group_idx", "n_sel", "out", "lse"):
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+def test_host_tier_cache_keys_past_the_last_query():
+    from test_gpu_edges import small
+    cfg = small(L=1024, n_q=256)
+    x = synth.make_inputs(cfg)
+    a = gpu_run(cfg, x, q_start=512, seq_len=1024)
+    b = gpu_run(cfg, x, q_start=512, seq_len=1024, split=384)
+    for key in ("chunk_idx", "group_idx", "n_sel", "out", "lse"):
+        np.testing.assert_array_equal(a[key], b[key])
