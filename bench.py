@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload index (default: the 16K segment)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the 64K lines")
+    ap.add_argument("--host-tier", action="store_true",
+                    help="main line with the history (tokens before the first query) in pinned host memory")
     ap.add_argument("--traffic-kib", type=float, nargs=2, default=None, metavar=("FETCH", "WRITE"),
                     help="attention kernel FETCH_SIZE and WRITE_SIZE per dispatch (KiB, as rocprofv3 "
                          "reports them) for the roofline traffic field")
@@ -250,6 +252,26 @@ def roofline(cfg, n_sel, attend_us, kernel, with_traffic=True):
             "algorithmic_flops": flops, "algorithmic_bytes": byts}
 
 
+def host_link_bytes(cfg, n_sel, group_idx, split):
+    """Bytes one step moves across the host link on the host-tier path: K and V
+    of every history chunk (below split) that some (block, KV head) needs (its
+    sink and local chunks, the chunks of its kept groups), each once."""
+    nb, hkv, g = cfg["n_q"] // 64, cfg["hkv"], cfg["group"]
+    q0 = cfg["L"] - cfg["n_q"]
+    ns = n_sel.reshape(nb, hkv, 2)
+    gi = group_idx.reshape(nb, hkv, -1)
+    need = [set() for _ in range(hkv)]
+    for b in range(nb):
+        ms = (q0 + 64 * b) // 64
+        a = min(cfg["sink"] // 64, ms)
+        bb = max(ms - cfg["local"] // 64, a)
+        for h in range(hkv):
+            need[h].update(m for m in list(range(a)) + list(range(bb, ms)) if m * 64 < split)
+            need[h].update(int(j) * g // 64 for j in gi[b, h, :int(ns[b, h, 1])] if j >= 0 and int(j) * g < split)
+    esz = 2 if cfg["dtype"] == "bf16" else 4
+    return sum(len(n) for n in need) * 64 * cfg["d"] * esz * 2
+
+
 def cpu_baseline(cfg_id, min_seconds=10.0):
     """The oracle timed on the host cores: summaries, routing and attention of
     every (block, KV head) of the layer, repeated until at least min_seconds
@@ -281,6 +303,8 @@ class Result:
     def __init__(self, w, wall, stage):
         self.cfg, self.fused, self.wall = w.cfg, w.fused, wall
         self.ns = w.ns.cpu().numpy()
+        self.split = w.split
+        self.host_bytes = host_link_bytes(w.cfg, self.ns, w.gi.cpu().numpy(), w.split) if w.split else 0
         self.mean = [float(np.mean(x)) if x else float("nan") for x in stage]
         self.med = [float(np.median(x)) if x else float("nan") for x in stage]
 
@@ -315,7 +339,12 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
-    main_r = measure(args.config, args.steps, args.warmup)
+    split = 0
+    if args.host_tier:
+        import synth
+        split = synth.config(args.config)["tier_split"] or (synth.config(args.config)["L"] -
+                                                            synth.config(args.config)["n_q"])
+    main_r = measure(args.config, args.steps, args.warmup, split=split)
     cfg = main_r.cfg
     value = args.steps * cfg["n_q"] / main_r.wall
     line = {
@@ -326,13 +355,21 @@ def main():
         "config": {"workload": cfg["name"], "seq_len": cfg["L"], "n_q": cfg["n_q"], "q_heads": cfg["hq"],
                    "kv_heads": cfg["hkv"], "head_dim": cfg["d"], "top_chunks": cfg["top_chunks"],
                    "top_groups": cfg["top_groups"], "sink": cfg["sink"], "local": cfg["local"],
-                   "kv_residency": "hbm"},
+                   "kv_residency": "host-pinned history" if split else "hbm"},
         "stages_us_mean": main_r.stages("mean"),
         "stages_us_median": main_r.stages("median"),
         "roofline": main_r.roofline(),
     }
+    if split:
+        line["host_link_bytes_per_step"] = main_r.host_bytes
     if not args.no_extra:
         extra = {}
+        # the rate with the summaries prebuilt (kept resident, as the pages do):
+        # query tokens over the routing + gather + attention stage times
+        rest = sum(main_r.mean[1:])
+        extra["summaries_prebuilt"] = {
+            "value": cfg["n_q"] / (rest * 1e-6), "unit": "query-tokens/s",
+            "note": "n_q / (mean routing + gather + attention stage time); summary build excluded"}
         half = max(args.steps // 2, 5)
         if main_r.fused:
             sep = measure(args.config, half, args.warmup, fused=False)
@@ -344,11 +381,12 @@ def main():
             r3 = measure(3, half, args.warmup)
             extra["64k_hbm"] = {"value": half * r3.cfg["n_q"] / r3.wall, "unit": "query-tokens/s",
                                 "stages_us_mean": r3.stages("mean"), "roofline": r3.roofline()}
-            rh = measure(3, 5, 2, split=r3.cfg["tier_split"])
+            rh = measure(3, 10, 2, split=r3.cfg["tier_split"])
             extra["64k_host_tier_pcie_inclusive"] = {
-                "value": 5 * rh.cfg["n_q"] / rh.wall, "unit": "query-tokens/s",
-                "note": "history K/V and group summaries in pinned host memory; routed rows cross PCIe each "
-                        "step (routing, then gather and attention)",
+                "value": 10 * rh.cfg["n_q"] / rh.wall, "unit": "query-tokens/s",
+                "note": "history K/V and group summaries in pinned host memory; each history chunk any block "
+                        "needs crosses the host link once per step into an HBM cache, then attention",
+                "host_link_bytes_per_step": rh.host_bytes,
                 "stages_us_mean": rh.stages("mean")}
         line["also"] = extra
     if not args.no_cpu_baseline:
