@@ -336,11 +336,11 @@ __device__ inline void issue_tile(const KVRows& kv, uint32_t k_lds, uint32_t v_l
 }
 
 // Attention of item (b, h), workgroup slot z, over the token set of plan P
-// (runs in sm.runs). With tile0_issued the caller has already issued tile
-// 0's loads into stage 0.
+// (runs in sm.runs). The caller has already issued the loads of the first
+// pre_tiles tiles (at most kAttnStages), tile t into stage t.
 template <int D, bool kTiered>
 __device__ void attend_bf16_body(const AttnArgs& A, int b, int h, int z, const Plan& P, AttnSmem<D>& sm,
-                                 bool tile0_issued) {
+                                 int pre_tiles) {
   constexpr int NP = D / 8;
   constexpr int RPI = 64 / NP;
   constexpr int RPW = kChunk / kAttnWaves;
@@ -431,7 +431,7 @@ __device__ void attend_bf16_body(const AttnArgs& A, int b, int h, int z, const P
   const char* sVb = reinterpret_cast<const char*>(&sm.v[0][0]);
 
   static_assert(kAttnStages == 2, "the run-table prefetch runs one tile ahead");
-  if (!tile0_issued) {
+  if (pre_tiles < 1) {
     fetch(0);
     issue(0);
   }
@@ -446,7 +446,7 @@ __device__ void attend_bf16_body(const AttnArgs& A, int b, int h, int z, const P
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();   // every wave's loads of tile t landed; tile t - 1 is free
     if (t + 1 < nt) {
-      issue(t + 1);
+      if (t + 1 >= pre_tiles) issue(t + 1);
       fetch(t + 2);
     }
     if (!active) continue;
@@ -551,13 +551,13 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(AttnArgs A) {
   item_of_block(A.s, A.wg_per_item, &b, &h, &z);
   const Plan P = make_plan(A.s, b, h, A.gidx, A.nsel, sm.runs, sm.scan, kMaxRoutedAttn);
   if (kTiered) translate_plan(A, h, P, sm.runs, sm.runs + kMaxRoutedAttn);
-  attend_bf16_body<D, kTiered>(A, b, h, z, P, sm, false);
+  attend_bf16_body<D, kTiered>(A, b, h, z, P, sm, 0);
 }
 
 // Route, then attend, in one workgroup per (item, slot): the router's kept
 // groups go straight into the run list (they are ascending and every one is
 // usable, so the run list is exactly the one built from the router's output),
-// and the loads of the first fixed tile, which needs no routing, are in
+// and the loads of the first fixed tiles, which need no routing, are in
 // flight while the router runs. Slot 0 writes the router's outputs.
 struct FusedArgs {
   route::RouteArgs r;
@@ -577,11 +577,14 @@ __global__ __launch_bounds__(kAttnThreads) void route_attend_bf16_kernel(FusedAr
   const int64_t ms = P.s / S.c;
   fixed_windows(ms, S.sink_chunks, S.local_chunks, &P.a, &P.bb);
   P.nfix = (int)(P.a + (ms - P.bb));
-  const bool pre = P.nfix > 0;
-  if (pre) {
-    const int m0 = P.a > 0 ? 0 : (int)P.bb;    // chunk of fixed tile 0
-    issue_tile<D>(kv_rows<D, false>(F.a, h), lds_addr(&sm.k[0][0]), lds_addr(&sm.v[0][0]),
-                  [&](int, int sl) -> int { return m0 * kChunk + sl; });
+  // fixed tiles need no routing: the first two (one per stage) load while
+  // the router runs
+  const int pre = P.nfix < kAttnStages ? P.nfix : kAttnStages;
+  for (int t = 0; t < pre; ++t) {
+    const int m = t < P.a ? t : (int)(P.bb + (t - P.a));   // chunk of fixed tile t
+    const uint32_t off = (uint32_t)(t * kChunk * D * 2);
+    issue_tile<D>(kv_rows<D, false>(F.a, h), lds_addr(&sm.k[0][0]) + off, lds_addr(&sm.v[0][0]) + off,
+                  [&](int, int sl) -> int { return m * kChunk + sl; });
   }
   const bool wr = z == 0;
   int32_t* gout = F.r.group_idx + ((int64_t)b * S.hkv + h) * S.kg;
