@@ -320,6 +320,45 @@ class Result:
         return roofline(self.cfg, self.ns, self.mean[2], "attend_bf16", with_traffic)
 
 
+def stream_line(passes, warmup):
+    """The 16K training-segment sequence with every position querying, run by
+    hga_stream_forward in its 2,048-token segments (each: summaries of the
+    chunks it closes, then routing and attention of its queries); query-tokens
+    per second over whole passes."""
+    import torch
+
+    import hierarchical_sparse_attention_hga_amd as hga
+    import synth
+    cfg = synth.config(2, n_q=16384)
+    x = synth.make_inputs(cfg)
+    DEV = torch.device("cuda:0")
+    L, hkv, d, g = cfg["L"], cfg["hkv"], cfg["d"], cfg["group"]
+    c = hga.make_config(cfg["hq"], hkv, d, cfg["top_chunks"], cfg["top_groups"], cfg["sink"], cfg["local"],
+                        dtype=cfg["dtype"], group_size=g)
+    q, k, v = (to_dev(x[n], cfg["dtype"], DEV) for n in ("q", "k", "v"))
+    gs = torch.empty(hkv, L // g, d, device=DEV)
+    cs = torch.empty(hkv, L // 64, d, device=DEV)
+    ci = torch.empty(L // 64, hkv, cfg["top_chunks"], dtype=torch.int32, device=DEV)
+    gi = torch.empty(L // 64, hkv, cfg["top_groups"], dtype=torch.int32, device=DEV)
+    ns = torch.empty(L // 64, hkv, 2, dtype=torch.int32, device=DEV)
+    out = torch.empty_like(q)
+    lse = torch.empty(cfg["hq"], L, device=DEV)
+
+    def one():
+        hga.hga_stream_forward(c, q, k, v, L, 2048, cs, gs, ci, gi, ns, out, lse)
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(passes):
+        one()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    return {"value": passes * L / el, "unit": "query-tokens/s", "ms_per_pass": el / passes * 1e3,
+            "note": "16,384 positions all querying, 8 segments of 2,048: per segment the summaries of its 32 "
+                    "chunks, then routing and attention of its queries against the committed history"}
+
+
 def measure(cfg_id, steps, warmup, split=0, fused=None):
     w = Workload(cfg_id, split, fused)
     wall, stage = w.run(steps, warmup)
@@ -377,6 +416,8 @@ def main():
                 "value": half * sep.cfg["n_q"] / sep.wall, "unit": "query-tokens/s",
                 "note": "same step through hga_route then hga_attend; roofline of the attention kernel alone",
                 "stages_us_mean": sep.stages("mean"), "roofline": sep.roofline(with_traffic=False)}
+        if args.config == 2:
+            extra["16k_streamed_2048_segments"] = stream_line(max(args.steps // 6, 3), 2)
         if args.config != 3:
             r3 = measure(3, half, args.warmup)
             extra["64k_hbm"] = {"value": half * r3.cfg["n_q"] / r3.wall, "unit": "query-tokens/s",

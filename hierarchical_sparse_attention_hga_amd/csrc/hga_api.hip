@@ -91,6 +91,8 @@ hga_status make_shape(const hga_config* cfg, int64_t seq_len, int64_t q_start, i
   s->q0 = q_start;
   s->nq = n_q;
   s->nb = n_q / kChunk;
+  s->qs = n_q;
+  s->kvs = seq_len;
   return HGA_OK;
 }
 
@@ -142,8 +144,72 @@ hga_status hga_build_summaries(const hga_config* cfg, const void* k, int64_t seq
   if (seq_len == 0) return ok();
   if (!k || !group_sum || !chunk_sum)
     return fail(HGA_ERR_INVALID_ARGUMENT, "k, group_sum and chunk_sum must be non-NULL");
-  return device_status(hga::launch_summaries(s, k, group_sum, chunk_sum, (hipStream_t)stream),
+  return device_status(hga::launch_summaries(s, k, group_sum, chunk_sum, 0, seq_len / hga::kChunk,
+                                             (hipStream_t)stream),
                        "hga_build_summaries launch");
+}
+
+hga_status hga_build_summaries_range(const hga_config* cfg, const void* k, int64_t seq_len, int64_t chunk_begin,
+                                     int64_t chunk_end, float* group_sum, float* chunk_sum, void* stream) {
+  hga::Shape s;
+  hga_status st = make_shape(cfg, seq_len, 0, 0, &s);
+  if (st != HGA_OK) return st;
+  if (chunk_begin < 0 || chunk_begin > chunk_end || chunk_end > seq_len / hga::kChunk)
+    return fail(HGA_ERR_INVALID_ARGUMENT, "need 0 <= chunk_begin <= chunk_end <= seq_len / 64");
+  if (chunk_begin == chunk_end) return ok();
+  if (!k || !group_sum || !chunk_sum)
+    return fail(HGA_ERR_INVALID_ARGUMENT, "k, group_sum and chunk_sum must be non-NULL");
+  return device_status(hga::launch_summaries(s, k, group_sum, chunk_sum, chunk_begin, chunk_end, (hipStream_t)stream),
+                       "hga_build_summaries_range launch");
+}
+
+hga_status hga_stream_forward(const hga_config* cfg, const void* q, const void* k, const void* v, int64_t seq_len,
+                              int64_t segment, float* chunk_sum, float* group_sum, int32_t* chunk_idx,
+                              int32_t* group_idx, int32_t* n_sel, void* out, float* lse, void* stream) {
+  hga::Shape full;
+  hga_status st = make_shape(cfg, seq_len, 0, seq_len, &full);
+  if (st != HGA_OK) return st;
+  if (segment <= 0 || segment % hga::kChunk)
+    return fail(HGA_ERR_INVALID_ARGUMENT, "segment must be a positive multiple of 64");
+  if (seq_len == 0) return ok();
+  if (!q || !k || !v || !chunk_sum || !group_sum || !n_sel || !out || (full.kc > 0 && !chunk_idx) ||
+      (full.kg > 0 && !group_idx))
+    return fail(HGA_ERR_INVALID_ARGUMENT,
+                "q, k, v, chunk_sum, group_sum, n_sel, out, chunk_idx and group_idx must be non-NULL");
+  const hipStream_t hs = (hipStream_t)stream;
+  const size_t esz = full.dtype == HGA_BF16 ? 2 : 4;
+  const hga::KVSrc kv{nullptr, k, nullptr, v, 0};
+  for (int64_t s0 = 0; s0 < seq_len; s0 += segment) {
+    const int64_t s1 = s0 + segment < seq_len ? s0 + segment : seq_len;
+    // the segment's chunks close: their summaries join the history's
+    st = device_status(hga::launch_summaries(full, k, group_sum, chunk_sum, s0 / hga::kChunk, s1 / hga::kChunk, hs),
+                       "hga_stream_forward summary launch");
+    if (st != HGA_OK) return st;
+    // the segment's queries against the committed history and themselves
+    hga::Shape seg;
+    if ((st = make_shape(cfg, s1, s0, s1 - s0, &seg)) != HGA_OK) return st;
+    seg.qs = seq_len;
+    seg.kvs = seq_len;
+    const void* qs = static_cast<const char*>(q) + (size_t)s0 * full.d * esz;
+    void* os = static_cast<char*>(out) + (size_t)s0 * full.d * esz;
+    float* ls = lse ? lse + s0 : nullptr;
+    const int64_t b0 = s0 / hga::kChunk;
+    int32_t* ci = full.kc > 0 ? chunk_idx + b0 * full.hkv * full.kc : chunk_idx;
+    int32_t* gi = full.kg > 0 ? group_idx + b0 * full.hkv * full.kg : group_idx;
+    int32_t* ns = n_sel + b0 * full.hkv * 2;
+    if (hga::fused_route_attend_supported(seg, 0)) {
+      st = device_status(hga::launch_route_attend(seg, qs, chunk_sum, nullptr, group_sum, 0, kv, ci, gi, ns, os, ls, hs),
+                         "hga_stream_forward launch");
+    } else {
+      st = device_status(hga::launch_route(seg, qs, chunk_sum, nullptr, group_sum, 0, ci, gi, ns, hs),
+                         "hga_stream_forward routing launch");
+      if (st == HGA_OK)
+        st = device_status(hga::launch_attend(seg, qs, kv, gi, ns, os, ls, nullptr, hs),
+                           "hga_stream_forward attention launch");
+    }
+    if (st != HGA_OK) return st;
+  }
+  return ok();
 }
 
 hga_status hga_route(const hga_config* cfg, const void* q, int64_t q_start, int64_t n_q, int64_t seq_len,

@@ -304,7 +304,7 @@ struct KVRows {
 };
 template <int D, bool kTiered>
 __device__ inline KVRows kv_rows(const AttnArgs& A, int h) {
-  const int64_t per_head = kTiered ? A.s.L - A.kv.split : A.s.L;
+  const int64_t per_head = kTiered ? A.s.kvs - A.kv.split : A.s.kvs;
   return KVRows{static_cast<const uint16_t*>(A.kv.k_dev) + (int64_t)h * per_head * D,
                 static_cast<const uint16_t*>(A.kv.v_dev) + (int64_t)h * per_head * D,
                 static_cast<const uint16_t*>(A.k_cache), static_cast<const uint16_t*>(A.v_cache)};
@@ -363,7 +363,7 @@ __device__ void attend_bf16_body(const AttnArgs& A, int b, int h, int z, const P
   // queries of this lane's column as MFMA B operands (d = 16 ks + 8 hl + e)
   bf16x8 qf[D / 16];
   if (active) {
-    const uint16_t* qp = static_cast<const uint16_t*>(A.q) + ((int64_t)head * S.nq + qrow) * D + 8 * hl;
+    const uint16_t* qp = static_cast<const uint16_t*>(A.q) + ((int64_t)head * S.qs + qrow) * D + 8 * hl;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
       qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 16 * ks));
@@ -529,7 +529,7 @@ __device__ void attend_bf16_body(const AttnArgs& A, int b, int h, int z, const P
   if (active) {
     const float l_tot = pair_sum(l_run);
     const float inv = 1.0f / l_tot;
-    uint16_t* op = static_cast<uint16_t*>(A.out) + ((int64_t)head * S.nq + qrow) * D;
+    uint16_t* op = static_cast<uint16_t*>(A.out) + ((int64_t)head * S.qs + qrow) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -539,7 +539,7 @@ __device__ void attend_bf16_body(const AttnArgs& A, int b, int h, int z, const P
         for (int ii = 0; ii < 4; ++ii) v4[ii] = (__bf16)(o[db][4 * jj + ii] * inv);
         *reinterpret_cast<u32x2*>(op + 32 * db + 8 * jj + 4 * hl) = __builtin_bit_cast(u32x2, v4);
       }
-    if (A.lse && hl == 0) A.lse[(int64_t)head * S.nq + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+    if (A.lse && hl == 0) A.lse[(int64_t)head * S.qs + qrow] = (m_run + __log2f(l_tot)) * kLn2;
   }
 }
 
@@ -620,7 +620,7 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttnArgs A) {
   item_of_block(S, A.wg_per_item, &b, &h, &z);
   const Plan P = make_plan(S, b, h, A.gidx, A.nsel, sRuns, sScan, kMaxRouted);
   if (kTiered) translate_plan(A, h, P, sRuns, sRuns + kMaxRouted);
-  const int64_t per_head = kTiered ? S.L - A.kv.split : S.L;
+  const int64_t per_head = kTiered ? S.kvs - A.kv.split : S.kvs;
   const float* kdev = static_cast<const float*>(A.kv.k_dev) + (int64_t)h * per_head * D;
   const float* vdev = static_cast<const float*>(A.kv.v_dev) + (int64_t)h * per_head * D;
   const float* kc = static_cast<const float*>(A.k_cache);
@@ -636,7 +636,7 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttnArgs A) {
   float q[DPT], o[DPT];
 #pragma unroll
   for (int e = 0; e < DPT; ++e) {
-    q[e] = active ? static_cast<const float*>(A.q)[((int64_t)head * S.nq + qrow) * D + part * DPT + e] : 0.0f;
+    q[e] = active ? static_cast<const float*>(A.q)[((int64_t)head * S.qs + qrow) * D + part * DPT + e] : 0.0f;
     o[e] = 0.0f;
   }
   const float sl2 = S.scale * kLog2e;
@@ -692,10 +692,10 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttnArgs A) {
   }
   if (active) {
     const float inv = 1.0f / l_run;
-    float* op = static_cast<float*>(A.out) + ((int64_t)head * S.nq + qrow) * D + part * DPT;
+    float* op = static_cast<float*>(A.out) + ((int64_t)head * S.qs + qrow) * D + part * DPT;
 #pragma unroll
     for (int e = 0; e < DPT; ++e) op[e] = o[e] * inv;
-    if (A.lse && part == 0) A.lse[(int64_t)head * S.nq + qrow] = (m_run + log2f(l_run)) * kLn2;
+    if (A.lse && part == 0) A.lse[(int64_t)head * S.qs + qrow] = (m_run + log2f(l_run)) * kLn2;
   }
 }
 

@@ -34,6 +34,9 @@ struct Shape {
   int dtype;            // hga_dtype
   float scale;          // softmax scale (resolved)
   int64_t L, q0, nq, nb;
+  int64_t qs;           // rows per head of Q, O and LSE (n_q; more when they cover a longer sequence)
+  int64_t kvs;          // rows per head of K and V, and of the summaries in tokens (L; more when
+                        // the tensors hold a longer sequence than the one attended)
 };
 
 // Fixed sink/local windows of a block whose first token is in chunk ms: the
@@ -47,7 +50,9 @@ __host__ __device__ inline void fixed_windows(int64_t ms, int sink_chunks, int l
   *bb = lo > aa ? lo : aa;
 }
 
-hipError_t launch_summaries(const Shape& s, const void* k, float* gs, float* cs, hipStream_t st);
+// Summaries of chunks [c0, c1) of every KV head.
+hipError_t launch_summaries(const Shape& s, const void* k, float* gs, float* cs, int64_t c0, int64_t c1,
+                            hipStream_t st);
 
 hipError_t launch_route(const Shape& s, const void* q, const float* cs, const float* gs_host,
                         const float* gs_dev, int64_t split, int32_t* chunk_idx, int32_t* group_idx,

@@ -275,7 +275,7 @@ __device__ int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm, bool 
   const int ncand = (int)(hi - lo);
   const int nsc = ncand < S.kc ? ncand : S.kc;
   const bool chunk_select = nsc > 0 && nsc < ncand;
-  const float* csh = a.cs + (int64_t)h * (S.L / S.c) * d;
+  const float* csh = a.cs + (int64_t)h * (S.kvs / S.c) * d;
   auto chunk_row = [&](int c) { return csh + (lo + c) * d; };
   ScoreRound first;
   if (chunk_select) load_round(0, d, ncand, chunk_row, first);
@@ -298,7 +298,7 @@ __device__ int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm, bool 
         const int rr = r + u * phases;
         v[u] = uint4{0u, 0u, 0u, 0u};
         if (rr < nrows) {
-          const int64_t row = (int64_t)(h * S.G + rr / S.B) * S.nq + (s - S.q0) + rr % S.B;
+          const int64_t row = (int64_t)(h * S.G + rr / S.B) * S.qs + (s - S.q0) + rr % S.B;
           v[u] = *reinterpret_cast<const uint4*>(qbase + row * d + p * E);
         }
       }
@@ -350,7 +350,7 @@ __device__ int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm, bool 
   auto group_of = [kept_chunks, gpc](int c) { return kept_chunks[c / gpc] * gpc + c % gpc; };
   if (nsg > 0 && nsg < ngc) {
     const int64_t gsplit = a.split / S.g;          // groups held in host memory
-    const int64_t ngl = S.L / S.g;
+    const int64_t ngl = S.kvs / S.g;
     score_rows(sm.qbar, d, ngc, [&](int c) -> const float* {
       const int64_t j = group_of(c);
       return j < gsplit ? a.gs_host + ((int64_t)h * gsplit + j) * d

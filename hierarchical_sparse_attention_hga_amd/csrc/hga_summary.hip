@@ -39,24 +39,26 @@ struct Slice<uint16_t> {
   }
 };
 
+// Rows per head of k, gs and cs: kvs, kvs / g, kvs / 64; block x covers chunk c0 + x.
 template <typename T>
 __global__ __launch_bounds__(1024) void summary_kernel(const T* __restrict__ k, float* __restrict__ gs,
-                                                       float* __restrict__ cs, int64_t L, int d, int g) {
+                                                       float* __restrict__ cs, int64_t kvs, int64_t c0, int d,
+                                                       int g) {
   constexpr int E = Slice<T>::E;
   extern __shared__ double part[];   // [groups per chunk][d] group sums
   const int P = d / E;               // slices per row
   const int gpc = kChunk / g;
-  const int64_t m = blockIdx.x, h = blockIdx.y;
-  const int64_t nchunk = L / kChunk;
+  const int64_t m = c0 + blockIdx.x, h = blockIdx.y;
+  const int64_t nchunk = kvs / kChunk;
   for (int w = threadIdx.x; w < gpc * P; w += blockDim.x) {
     const int p = w % P, u = w / P;
-    const T* src = k + (h * L + m * kChunk + (int64_t)u * g) * d + p * E;
+    const T* src = k + (h * kvs + m * kChunk + (int64_t)u * g) * d + p * E;
     double acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.0;
 #pragma unroll 8
     for (int t = 0; t < g; ++t) Slice<T>::add(src + (int64_t)t * d, acc);
-    float* dst = gs + (h * (L / g) + m * gpc + u) * d + p * E;
+    float* dst = gs + (h * (kvs / g) + m * gpc + u) * d + p * E;
 #pragma unroll
     for (int e = 0; e < E; e += 4) {
       float4 o;
@@ -77,20 +79,21 @@ __global__ __launch_bounds__(1024) void summary_kernel(const T* __restrict__ k, 
 
 }  // namespace
 
-hipError_t launch_summaries(const Shape& s, const void* k, float* gs, float* cs, hipStream_t st) {
-  const int64_t nchunk = s.L / kChunk;
-  if (nchunk == 0) return hipSuccess;
+hipError_t launch_summaries(const Shape& s, const void* k, float* gs, float* cs, int64_t c0, int64_t c1,
+                            hipStream_t st) {
+  const int64_t nchunk = c1 - c0;
+  if (nchunk <= 0) return hipSuccess;
   const int gpc = kChunk / s.g;
   const size_t lds = (size_t)gpc * s.d * sizeof(double);
   const dim3 grid((unsigned)nchunk, (unsigned)s.hkv);
   if (s.dtype == HGA_BF16) {
     const int threads = gpc * (s.d / 8) < 1024 ? gpc * (s.d / 8) : 1024;
-    summary_kernel<uint16_t><<<grid, dim3(threads), lds, st>>>(static_cast<const uint16_t*>(k), gs, cs, s.L,
-                                                              s.d, s.g);
+    summary_kernel<uint16_t><<<grid, dim3(threads), lds, st>>>(static_cast<const uint16_t*>(k), gs, cs, s.kvs,
+                                                              c0, s.d, s.g);
   } else {
     const int threads = gpc * (s.d / 4) < 1024 ? gpc * (s.d / 4) : 1024;
-    summary_kernel<float><<<grid, dim3(threads), lds, st>>>(static_cast<const float*>(k), gs, cs, s.L, s.d,
-                                                           s.g);
+    summary_kernel<float><<<grid, dim3(threads), lds, st>>>(static_cast<const float*>(k), gs, cs, s.kvs, c0,
+                                                           s.d, s.g);
   }
   return hipGetLastError();
 }

@@ -118,6 +118,15 @@ size_t hga_workspace_size(const hga_config* cfg, int64_t seq_len, int64_t n_q, i
 hga_status hga_build_summaries(const hga_config* cfg, const void* k, int64_t seq_len,
                                float* group_sum, float* chunk_sum, void* stream);
 
+/* Summaries of chunks [chunk_begin, chunk_end) only (section 2.1, first
+ * paragraph: summaries are kept resident and a chunk's are built once, when it
+ * closes). Layouts as in hga_build_summaries; rows of other chunks are left
+ * untouched. 0 <= chunk_begin <= chunk_end <= seq_len / chunk_size, else
+ * HGA_ERR_INVALID_ARGUMENT; an empty range is a no-op. */
+hga_status hga_build_summaries_range(const hga_config* cfg, const void* k, int64_t seq_len,
+                                     int64_t chunk_begin, int64_t chunk_end,
+                                     float* group_sum, float* chunk_sum, void* stream);
+
 /* Two-level routing (section 2.1, "Chunk selection", "Group selection").
  * For query block b (positions s = q_start + 64 b .. s + 63) and KV head h:
  *   block query   mean of Q over the block's 64 positions and the
@@ -191,6 +200,27 @@ hga_status hga_route_attend(const hga_config* cfg, const void* q, int64_t q_star
                             const hga_tiered* k, const hga_tiered* v,
                             int32_t* chunk_idx, int32_t* group_idx, int32_t* n_sel,
                             void* out, float* lse, void* workspace, size_t ws_bytes, void* stream);
+
+/* Forward pass over a whole sequence in segments, in the pages' execution
+ * order (section 2.1 with the segment-by-segment processing of section 2.2):
+ * for each segment [s0, s0 + segment) in turn (the last may be shorter), the
+ * summaries of the chunks it closes are built, then its queries are routed
+ * and attended against the committed history and the segment itself
+ * (hga_route_attend with q_start = s0 and seq_len = the segment's end). The
+ * results equal one hga_build_summaries over the sequence followed by one
+ * hga_route_attend over all of its queries.
+ *   q, out     device, [Hq][seq_len][d] of cfg->dtype (every position queries).
+ *   k, v       device, [Hkv][seq_len][d] of cfg->dtype.
+ *   chunk_sum, group_sum   device, as written by hga_build_summaries (every
+ *              row is written).
+ *   chunk_idx, group_idx, n_sel   device, [seq_len/64][Hkv][...] as in hga_route.
+ *   lse        device, [Hq][seq_len] float32, or NULL.
+ *   segment    a positive multiple of chunk_size, else HGA_ERR_INVALID_ARGUMENT.
+ * Everything is on the device (no host tier); no workspace is needed. */
+hga_status hga_stream_forward(const hga_config* cfg, const void* q, const void* k, const void* v,
+                              int64_t seq_len, int64_t segment, float* chunk_sum, float* group_sum,
+                              int32_t* chunk_idx, int32_t* group_idx, int32_t* n_sel,
+                              void* out, float* lse, void* stream);
 
 /* Static description of a status code. */
 const char* hga_status_string(hga_status status);

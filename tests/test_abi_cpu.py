@@ -148,6 +148,26 @@ def test_tier_validation():
         hga.HGA_ERR_WORKSPACE
 
 
+def test_summary_range_and_stream_validation():
+    c = cfg()
+    E = hga.HGA_ERR_INVALID_ARGUMENT
+    # chunk range outside [0, seq_len / 64]
+    assert _status(hga.hga_build_summaries_range, c, FAKE, 16384, -1, 4, FAKE, FAKE) == E
+    assert _status(hga.hga_build_summaries_range, c, FAKE, 16384, 5, 4, FAKE, FAKE) == E
+    assert _status(hga.hga_build_summaries_range, c, FAKE, 16384, 0, 257, FAKE, FAKE) == E
+    assert _status(hga.hga_build_summaries_range, c, None, 16384, 0, 4, FAKE, FAKE) == E
+    hga.hga_build_summaries_range(c, None, 16384, 7, 7, None, None)   # empty range: no-op
+    # segment must be a positive multiple of 64; pointers non-NULL
+    sf = (c, FAKE, FAKE, FAKE, 4096)
+    assert _status(hga.hga_stream_forward, *sf, 0, *[FAKE] * 7) == E
+    assert _status(hga.hga_stream_forward, *sf, 100, *[FAKE] * 7) == E
+    assert _status(hga.hga_stream_forward, c, FAKE, None, FAKE, 4096, 1024, *[FAKE] * 7) == E
+    assert _status(hga.hga_stream_forward, *sf, 1024, FAKE, FAKE, FAKE, FAKE, FAKE, None) == E
+    assert _status(hga.hga_stream_forward, c, FAKE, FAKE, FAKE, 4000, 1024, *[FAKE] * 7) == \
+        hga.HGA_ERR_UNSUPPORTED
+    hga.hga_stream_forward(c, None, None, None, 0, 1024, *[None] * 7)   # empty sequence: no-op
+
+
 def test_empty_query_range_is_a_no_op():
     c = cfg()
     hga.hga_route(c, FAKE, 16384, 0, 16384, FAKE, FAKE, FAKE, FAKE, FAKE)
