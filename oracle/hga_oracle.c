@@ -23,7 +23,10 @@
  *                 fixed; keep the top kc by (score desc, chunk index asc).
  *   5. group stage  open the kept chunks into groups; keep the top kg by
  *                 (score desc, group index asc).
- *   6. token set  fixed chunks + kept groups + the block's own tokens.
+ *   6. token set  fixed chunks + kept groups + the block's own chunk up to
+ *                 the block's last position (reading: the open chunk has no
+ *                 summary, so its earlier tokens are kept whole; for a block
+ *                 of one whole chunk this is the block's own tokens).
  *   7. attention  exact causal softmax attention over the token set.
  *
  * Steps 4 and 5 are decisions. Summaries are stored in float32 (the mean
@@ -250,7 +253,12 @@ int orc_route(const orc_cfg* c, const double* q, const double* ga, const double*
 /* ------------------------------------------------------------------ step 6 */
 /* Mark the token set of block b in mask[0 .. s+B). Entries of group_idx that
  * are out of range, inside a fixed chunk or not closed are ignored, so the
- * result is always a set. */
+ * result is always a set. The block's own chunk ms is still open (it has no
+ * summary, so it is neither a candidate nor a fixed window): its tokens from
+ * the chunk start up to the block's last position are kept whole. For a block
+ * that is a whole chunk these are exactly the block's own tokens; for a
+ * smaller block (one token when decoding) they add the open chunk's earlier
+ * tokens. */
 static void token_mask(const orc_cfg* c, int b, const int32_t* group_idx, int n_groups, unsigned char* mask) {
   const int64_t s = q_start(c) + (int64_t)b * c->q_block, ms = s / c->chunk;
   memset(mask, 0, (size_t)(s + c->q_block));
@@ -263,7 +271,7 @@ static void token_mask(const orc_cfg* c, int b, const int32_t* group_idx, int n_
     if (is_fixed(c, j * c->group / c->chunk, ms)) continue;
     for (int64_t t = j * c->group; t < (j + 1) * c->group; ++t) mask[t] = 1;
   }
-  for (int64_t t = s; t < s + c->q_block; ++t) mask[t] = 1;
+  for (int64_t t = ms * c->chunk; t < s + c->q_block; ++t) mask[t] = 1;
 }
 
 int64_t orc_token_set(const orc_cfg* c, int b, const int32_t* group_idx, int n_groups,

@@ -221,6 +221,57 @@ def test_dense_equivalence_when_budget_covers_everything(hq, hkv, ragged):
     np.testing.assert_allclose(lse, rlse, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("q_block,L,n_q", [(1, 183, 1), (1, 256, 40), (4, 180, 72), (8, 256, 104)])
+def test_dense_equivalence_small_query_blocks(q_block, L, n_q):
+    """Blocks smaller than a chunk (q_block = 1 is per-token decoding), with a
+    sequence that may end inside an open chunk: under a budget that covers
+    every candidate the token set is every earlier token, so the result is
+    dense causal attention. Dropping the open chunk's earlier tokens, or taking
+    the windows from the block instead of its chunk, fails this."""
+    cfg = tiny_cfg(L=L, n_q=n_q, q_block=q_block, hq=4, hkv=2, top_chunks=L // 16, top_groups=L // 4)
+    q, k, v = rand_qkv(cfg, 15)
+    out, lse, _ = oracle_full(cfg, q, k, v)
+    ref, rlse = dense_causal(cfg, q, k, v)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, rlse, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("q_block", [1, 4])
+def test_no_routing_budget_small_blocks_is_chunk_diagonal_attention(q_block):
+    """With no windows and no budget a block sees only its own open chunk up to
+    itself: dense causal attention restricted to each chunk."""
+    cfg = tiny_cfg(sink=0, local=0, top_chunks=0, top_groups=0, hq=2, hkv=1, q_block=q_block, n_q=128)
+    q, k, v = rand_qkv(cfg, 16)
+    out, lse, _ = oracle_full(cfg, q, k, v)
+    c, q0 = cfg["chunk"], cfg["L"] - cfg["n_q"]
+    for m in range(q0 // c, cfg["L"] // c):
+        sub = tiny_cfg(L=c, n_q=c, hq=2, hkv=1)
+        sl = slice(m * c, (m + 1) * c)
+        ref, rlse = dense_causal(sub, q[:, m * c - q0:(m + 1) * c - q0], k[:, sl], v[:, sl])
+        np.testing.assert_allclose(out[:, m * c - q0:(m + 1) * c - q0], ref, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[:, m * c - q0:(m + 1) * c - q0], rlse, rtol=0, atol=1e-12)
+
+
+def test_single_token_block_query_is_the_head_mean():
+    """q_block = 1, G = 1: the block query is the query itself, so the kept
+    chunks are the top kc of q . CS[m] over the non-fixed closed chunks (brute
+    force over the float32-rounded summaries, ties to the lower index)."""
+    cfg = tiny_cfg(L=250, n_q=1, q_block=1, hq=1, hkv=1, sink=16, local=32, top_chunks=4, top_groups=6)
+    q, k, v = rand_qkv(cfg, 17)
+    ci, gi, ns, _ = oracle.route(cfg, q, k, [(0, 0)])
+    gs, cs = oracle.summaries(cfg, k)
+    s = 249
+    ms = s // 16
+    cand = [m for m in range(ms) if not (m < 1 or m >= ms - 2)]
+    sc = {m: float(np.dot(q[0, 0], cs[0, m].astype(np.float32).astype(np.float64))) for m in cand}
+    keep = sorted(sorted(cand, key=lambda m: (-sc[m], m))[:4])
+    assert ci[0].tolist() == keep
+    groups = [4 * m + u for m in keep for u in range(4)]
+    gsc = {j: float(np.dot(q[0, 0], gs[0, j].astype(np.float32).astype(np.float64))) for j in groups}
+    assert gi[0].tolist() == sorted(sorted(groups, key=lambda j: (-gsc[j], j))[:6])
+    assert ns[0].tolist() == [4, 6]
+
+
 def test_no_routing_budget_is_block_diagonal_attention():
     cfg = tiny_cfg(sink=0, local=0, top_chunks=0, top_groups=0, hq=2, hkv=1)
     q, k, v = rand_qkv(cfg, 6)
@@ -270,7 +321,9 @@ def test_causality_future_keys_do_not_change_past_outputs():
 
 # ------------------------------------------------------------------ step 6 invariants
 @pytest.mark.parametrize("cfg_over", [dict(), dict(sink=32, local=48, top_chunks=4, top_groups=7),
-                                      dict(sink=0, local=16, top_chunks=1, top_groups=4, n_q=128)])
+                                      dict(sink=0, local=16, top_chunks=1, top_groups=4, n_q=128),
+                                      dict(q_block=1, n_q=40, top_chunks=2, top_groups=5),
+                                      dict(q_block=4, L=252, n_q=100, sink=32, top_chunks=3, top_groups=6)])
 def test_routing_and_token_set_invariants(cfg_over):
     cfg = tiny_cfg(**cfg_over)
     q, k, v = rand_qkv(cfg, 12)
@@ -296,13 +349,13 @@ def test_routing_and_token_set_invariants(cfg_over):
         T = oracle.token_set(cfg, b, gi[n], nsg)
         assert T.tolist() == sorted(set(T.tolist()))
         assert T.max() == s + B - 1
-        expect = set(range(s, s + B))
+        expect = set(range(ms * c, s + B))   # the block's open chunk up to the block's end
         for m in fixed:
             expect |= set(range(m * c, (m + 1) * c))
         for j in selg:
             expect |= set(range(j * g, (j + 1) * g))
         assert set(T.tolist()) == expect
-        assert len(T) == c * len(fixed) + g * nsg + B
+        assert len(T) == c * len(fixed) + g * nsg + (s + B - ms * c)
 
 
 # ------------------------------------------------------------------ planted workloads
