@@ -53,12 +53,16 @@ hga_status make_shape(const hga_config* cfg, int64_t seq_len, int64_t q_start, i
     return fail(HGA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite and >= 0");
   if (seq_len < 0 || q_start < 0 || n_q < 0 || q_start + n_q > seq_len)
     return fail(HGA_ERR_INVALID_ARGUMENT, "need 0 <= q_start, 0 <= n_q, q_start + n_q <= seq_len");
-  if (cfg->chunk_size != kChunk || cfg->q_block != kChunk)
-    return fail(HGA_ERR_UNSUPPORTED, "chunk_size and q_block must both be %d", kChunk);
+  if (cfg->chunk_size != kChunk)
+    return fail(HGA_ERR_UNSUPPORTED, "chunk_size must be %d", kChunk);
+  if (cfg->q_block > kChunk || kChunk % cfg->q_block)
+    return fail(HGA_ERR_UNSUPPORTED, "q_block must divide %d (got %d)", kChunk, cfg->q_block);
   if (cfg->sink_tokens % kChunk || cfg->local_tokens % kChunk)
     return fail(HGA_ERR_UNSUPPORTED, "sink_tokens and local_tokens must be multiples of %d", kChunk);
-  if (seq_len % kChunk || q_start % kChunk || n_q % kChunk)
-    return fail(HGA_ERR_UNSUPPORTED, "seq_len, q_start and n_q must be multiples of %d", kChunk);
+  if (seq_len % kChunk)
+    return fail(HGA_ERR_UNSUPPORTED, "seq_len must be a multiple of %d", kChunk);
+  if (q_start % cfg->q_block || n_q % cfg->q_block)
+    return fail(HGA_ERR_UNSUPPORTED, "q_start and n_q must be multiples of q_block (%d)", cfg->q_block);
   const int d = cfg->head_dim;
   if (cfg->dtype == HGA_BF16 && d != 64 && d != 128)
     return fail(HGA_ERR_UNSUPPORTED, "bfloat16 needs head_dim 64 or 128 (got %d)", d);
@@ -80,7 +84,7 @@ hga_status make_shape(const hga_config* cfg, int64_t seq_len, int64_t q_start, i
   s->d = d;
   s->c = kChunk;
   s->g = cfg->group_size;
-  s->B = kChunk;
+  s->B = cfg->q_block;
   s->kc = cfg->top_chunks;
   s->kg = cfg->top_groups;
   s->sink_chunks = cfg->sink_tokens / kChunk;
@@ -90,7 +94,7 @@ hga_status make_shape(const hga_config* cfg, int64_t seq_len, int64_t q_start, i
   s->L = seq_len;
   s->q0 = q_start;
   s->nq = n_q;
-  s->nb = n_q / kChunk;
+  s->nb = n_q / cfg->q_block;
   s->qs = n_q;
   s->kvs = seq_len;
   return HGA_OK;
@@ -193,7 +197,7 @@ hga_status hga_stream_forward(const hga_config* cfg, const void* q, const void* 
     const void* qs = static_cast<const char*>(q) + (size_t)s0 * full.d * esz;
     void* os = static_cast<char*>(out) + (size_t)s0 * full.d * esz;
     float* ls = lse ? lse + s0 : nullptr;
-    const int64_t b0 = s0 / hga::kChunk;
+    const int64_t b0 = s0 / full.B;   // first query block of the segment
     int32_t* ci = full.kc > 0 ? chunk_idx + b0 * full.hkv * full.kc : chunk_idx;
     int32_t* gi = full.kg > 0 ? group_idx + b0 * full.hkv * full.kg : group_idx;
     int32_t* ns = n_sel + b0 * full.hkv * 2;
@@ -293,6 +297,6 @@ const char* hga_status_string(hga_status status) {
 
 const char* hga_last_error(void) { return g_err; }
 
-int32_t hga_version(void) { return 101; }
+int32_t hga_version(void) { return 102; }
 
 }  // extern "C"

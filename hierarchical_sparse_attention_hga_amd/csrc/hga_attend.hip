@@ -5,12 +5,16 @@
 //
 // Token set of one (query block b, KV head h) item, as 64-token tiles:
 //   [fixed sink/local chunks, one tile each][kept groups, 64/g per tile,
-//    the last tile possibly partial][the block's own chunk, causal].
+//    the last tile possibly partial][the block's own chunk from its first
+//    token up to the block's last position, causal]. A block smaller than a
+//    chunk (one token when decoding) lies inside a chunk that is still open:
+//    it has no summary, so the chunk's earlier tokens are kept whole.
 // The order of tiles does not change the result (softmax is a sum over the
 // set); each tile is one LDS-staged K/V tile of the flash-style loop.
 //
-// bfloat16 path (attend_bf16_kernel): one 512-thread workgroup per item and
-// 256 query rows (G heads x 64 positions); each of the 8 waves owns 32 rows.
+// bfloat16 path (attend_bf16_kernel): 512-thread workgroups, each of the 8
+// waves owning 32 of the item's G B query rows (G heads x B positions; 256
+// rows for G = 4 and B = 64, one workgroup).
 // Per 64-token tile a wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
 // (K from LDS as the A operand, its queries held in registers as B), keeps the
 // online-softmax state of its own query column per lane, and accumulates
@@ -72,12 +76,26 @@ constexpr int kCacheFlag = 1 << 30;
 // ------------------------------------------------------------ token-set plan
 struct Plan {
   int64_t s;      // first position of the block
+  int64_t c0;     // first token of the block's chunk ms (the last tile's first token)
+  int off;        // s - c0: the block's first slot in the last tile
+  int dlim;       // off + B: slots of the last tile at or after it are empty
   int64_t a, bb;  // fixed chunks are [0, a) and [bb, ms)
   int nfix;       // fixed chunks (tiles)
   int nrouted;    // kept groups after validation (their first tokens in runs[])
   int nrt;        // routed tiles
   int ntiles;
 };
+
+// The parts of the plan of block b that need no routing.
+__device__ inline void plan_windows(const Shape& S, int b, Plan* P) {
+  P->s = S.q0 + (int64_t)b * S.B;
+  const int64_t ms = P->s / S.c;
+  P->c0 = ms * S.c;
+  P->off = (int)(P->s - P->c0);
+  P->dlim = P->off + S.B;
+  fixed_windows(ms, S.sink_chunks, S.local_chunks, &P->a, &P->bb);
+  P->nfix = (int)(P->a + (ms - P->bb));
+}
 
 // Block-wide exclusive scan (sum or max) of one int per thread.
 template <bool kMax>
@@ -113,10 +131,7 @@ __device__ int block_scan(int v, int* lds, int* total) {
 __device__ Plan make_plan(const Shape& S, int b, int h, const int32_t* gidx, const int32_t* nsel,
                           int* runs, int* lds, int cap) {
   Plan P;
-  P.s = S.q0 + (int64_t)b * S.B;
-  const int64_t ms = P.s / S.c;
-  fixed_windows(ms, S.sink_chunks, S.local_chunks, &P.a, &P.bb);
-  P.nfix = (int)(P.a + (ms - P.bb));
+  plan_windows(S, b, &P);
   const int64_t row = (int64_t)b * S.hkv + h;
   int n = nsel[row * 2 + 1];
   n = n < 0 ? 0 : (n > S.kg ? S.kg : n);
@@ -160,7 +175,8 @@ __device__ inline int tile_src(const Plan& P, const int* runs, const int* fixsrc
     const int r = (t - P.nfix) * (kChunk / g) + sl / g;
     return r < P.nrouted ? runs[r] + sl % g : -1;
   }
-  return (int)(tiered ? P.s - split : P.s) + sl;
+  // the last tile: empty slots (past the block) read the chunk's first row
+  return (int)(tiered ? P.c0 - split : P.c0) + (sl < P.dlim ? sl : 0);
 }
 
 // Number of leading valid slots of tile t (the rest are empty).
@@ -169,7 +185,7 @@ __device__ inline int tile_limit(const Plan& P, int g, int t) {
     const int rem = P.nrouted * g - (t - P.nfix) * kChunk;
     return rem < kChunk ? rem : kChunk;
   }
-  return kChunk;
+  return t == P.ntiles - 1 ? P.dlim : kChunk;
 }
 
 // Host-tier path: rewrite the kept groups' first tokens in runs[] and the
@@ -354,15 +370,24 @@ __device__ void attend_bf16_body(const AttnArgs& A, int b, int h, int z, const P
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5;                  // lane half
   const int col = lane & 31;                 // query column of this lane
+  // item rows are head-major (row = B * head-local index + position); wave
+  // rb owns rows [32 rb, 32 rb + 32), lane column col row 32 rb + col
+  const int nrows = S.G * S.B;
   const int rb = z * kAttnWaves + wave;      // 32-row block of the item
-  const bool active = rb < 2 * S.G;
-  const int head = h * S.G + (rb >> 1);
-  const int qi = (rb & 1) * 32 + col;        // position within the block
+  const bool active = 32 * rb < nrows;       // the wave has rows of the item
+  const int row = 32 * rb + col;
+  const bool live = row < nrows;             // this lane's column is a query row
+  const int lgB = __ffs(S.B) - 1;
+  const int head = h * S.G + (row >> lgB);
+  const int qi = row & (S.B - 1);            // position within the block
   const int64_t qrow = (int64_t)b * S.B + qi;  // row of Q / O
 
-  // queries of this lane's column as MFMA B operands (d = 16 ks + 8 hl + e)
+  // queries of this lane's column as MFMA B operands (d = 16 ks + 8 hl + e);
+  // zero on the columns past the item's rows
   bf16x8 qf[D / 16];
-  if (active) {
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) qf[ks] = bf16x8{};
+  if (live) {
     const uint16_t* qp = static_cast<const uint16_t*>(A.q) + ((int64_t)head * S.qs + qrow) * D + 8 * hl;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
@@ -389,13 +414,14 @@ __device__ void attend_bf16_body(const AttnArgs& A, int b, int h, int z, const P
       raw[i] = sm.runs[idx];
     }
   };
-  const int64_t diag0 = kTiered ? P.s - A.kv.split : P.s;   // source row of the block's first token
+  const int diag0 = (int)(kTiered ? P.c0 - A.kv.split : P.c0);   // source row of the last tile's first slot
+  const int dlim = P.dlim;
   auto issue = [&](int t) {
     const uint32_t off = (uint32_t)((t % kAttnStages) * kChunk * D * 2);
     issue_tile<D>(kv, lds_addr(&sm.k[0][0]) + off, lds_addr(&sm.v[0][0]) + off, [&](int i, int sl) -> int {
       if (t < P.nfix) return kTiered ? raw[i] + sl : (int)((t < P.a ? t : P.bb + (t - P.a)) * kChunk) + sl;
       if (t < P.nfix + P.nrt) return run_of(t, sl) < P.nrouted ? raw[i] + (sl & ((1 << lg) - 1)) : 0;
-      return (int)diag0 + sl;
+      return diag0 + (sl < dlim ? sl : 0);   // empty slots past the block read the chunk's first row
     });
   };
 
@@ -469,12 +495,12 @@ __device__ void attend_bf16_body(const AttnArgs& A, int b, int h, int z, const P
     // masking only on the block's own tile and on a partial routed tile;
     // slot of accumulator r of half tb: 32 tb + 8 (r >> 2) + 4 hl + (r & 3).
     // A slot is masked when it reaches the tile's limit or, on the block's
-    // own tile, passes the query's position; thr is that bound shifted by
-    // this lane's 4 hl.
+    // own tile, passes the query's position (slot off + qi); thr is that
+    // bound shifted by this lane's 4 hl.
     const bool diag = t == nt - 1;
     const int lim = tile_limit(P, S.g, t);
     if (diag || lim < kChunk) {
-      const int thr = (diag && qi + 1 < lim ? qi + 1 : lim) - 4 * hl;
+      const int thr = (diag ? P.off + qi + 1 : lim) - 4 * hl;
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
@@ -528,6 +554,7 @@ __device__ void attend_bf16_body(const AttnArgs& A, int b, int h, int z, const P
 
   if (active) {
     const float l_tot = pair_sum(l_run);
+    if (!live) return;
     const float inv = 1.0f / l_tot;
     uint16_t* op = static_cast<uint16_t*>(A.out) + ((int64_t)head * S.qs + qrow) * D;
 #pragma unroll
@@ -573,10 +600,7 @@ __global__ __launch_bounds__(kAttnThreads) void route_attend_bf16_kernel(FusedAr
   int b, h, z;
   item_of_block(S, F.a.wg_per_item, &b, &h, &z);
   Plan P;
-  P.s = S.q0 + (int64_t)b * S.B;
-  const int64_t ms = P.s / S.c;
-  fixed_windows(ms, S.sink_chunks, S.local_chunks, &P.a, &P.bb);
-  P.nfix = (int)(P.a + (ms - P.bb));
+  plan_windows(S, b, &P);
   // fixed tiles need no routing: the first two (one per stage) load while
   // the router runs
   const int pre = P.nfix < kAttnStages ? P.nfix : kAttnStages;
@@ -626,7 +650,7 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttnArgs A) {
   const float* kc = static_cast<const float*>(A.k_cache);
   const float* vc = static_cast<const float*>(A.v_cache);
   const int tid = threadIdx.x;
-  const int row = z * ROWS + tid / TPR;       // row of the item: head-local * 64 + qi
+  const int row = z * ROWS + tid / TPR;       // row of the item: head-local * B + qi
   const int part = tid % TPR;
   const bool active = row < S.G * S.B;
   const int head = h * S.G + row / S.B;
@@ -671,7 +695,7 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttnArgs A) {
         for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, TPR);
         const int slot = half * HALF + sl;
         float v = acc * sl2;
-        if (slot >= lim || (diag && slot > qi)) v = -INFINITY;
+        if (slot >= lim || (diag && slot > P.off + qi)) v = -INFINITY;
         zz[sl] = v;
         mx = fmaxf(mx, v);
       }
@@ -819,6 +843,12 @@ size_t tier_cache_bytes(const Shape& s, int64_t split) {
   return flags + 2 * (size_t)s.hkv * nch * kChunk * (size_t)s.d * esz;
 }
 
+// Workgroups of the bfloat16 kernels per item: one wave per 32 query rows.
+static int bf16_wg_per_item(const Shape& s) {
+  const int waves = (s.G * s.B + 31) / 32;
+  return (waves + kAttnWaves - 1) / kAttnWaves;
+}
+
 hipError_t launch_attend(const Shape& s, const void* q, const KVSrc& kv, const int32_t* group_idx,
                          const int32_t* n_sel, void* out, float* lse, void* workspace, hipStream_t st) {
   const int64_t items = s.nb * s.hkv;
@@ -849,7 +879,7 @@ hipError_t launch_attend(const Shape& s, const void* q, const KVSrc& kv, const i
     if (e != hipSuccess) return e;
   }
   if (s.dtype == HGA_BF16) {
-    a.wg_per_item = (2 * s.G + kAttnWaves - 1) / kAttnWaves;
+    a.wg_per_item = bf16_wg_per_item(s);
     if (s.d == 128) return tiered ? launch_bf16<128, true>(a, items, st) : launch_bf16<128, false>(a, items, st);
     if (s.d == 64) return tiered ? launch_bf16<64, true>(a, items, st) : launch_bf16<64, false>(a, items, st);
     return hipErrorInvalidValue;
@@ -860,11 +890,11 @@ hipError_t launch_attend(const Shape& s, const void* q, const KVSrc& kv, const i
   return tiered ? dispatch_f32<true>(a, items, st) : dispatch_f32<false>(a, items, st);
 }
 
-// One kernel when one workgroup holds every query row of an item (2 G <= 8
+// One kernel when one workgroup holds every query row of an item (G B <= 8
 // waves of 32 rows): with more, each of an item's workgroups would route it
 // again, and the separate router is cheaper.
 bool fused_route_attend_supported(const Shape& s, int64_t kv_split) {
-  return s.dtype == HGA_BF16 && kv_split == 0 && (s.d == 128 || s.d == 64) && 2 * s.G <= kAttnWaves;
+  return s.dtype == HGA_BF16 && kv_split == 0 && (s.d == 128 || s.d == 64) && bf16_wg_per_item(s) == 1;
 }
 
 hipError_t launch_route_attend(const Shape& s, const void* q, const float* cs, const float* gs_host,
@@ -876,7 +906,7 @@ hipError_t launch_route_attend(const Shape& s, const void* q, const float* cs, c
   FusedArgs f{};
   f.r = route::RouteArgs{q, cs, gs_host, gs_dev, gs_split, chunk_idx, group_idx, n_sel, s};
   f.a.q = q; f.a.kv = kv; f.a.out = out; f.a.lse = lse; f.a.s = s;
-  f.a.wg_per_item = (2 * s.G + kAttnWaves - 1) / kAttnWaves;
+  f.a.wg_per_item = 1;
   const dim3 grid((unsigned)(items * f.a.wg_per_item)), block(kAttnThreads);
   if (s.d == 128)
     route_attend_bf16_kernel<128><<<grid, block, 0, st>>>(f);

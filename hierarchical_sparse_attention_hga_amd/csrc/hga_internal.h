@@ -9,8 +9,8 @@
 
 namespace hga {
 
-// Chunk and query-block size the kernels are built for (the pages' 64-token
-// chunks; a query block is one chunk).
+// Chunk size the kernels are built for (the pages' 64-token chunks). A query
+// block is one chunk or a divisor of it (down to one token when decoding).
 constexpr int kChunk = 64;
 // Largest number of routing candidates of one stage for one (block, KV head).
 constexpr int kMaxCand = 4096;

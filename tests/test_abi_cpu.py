@@ -31,7 +31,7 @@ def test_every_declared_entry_point_is_exported(lib):
     assert declared == set(B.EXPORTS)
     for name in declared:
         assert hasattr(lib, name)
-    assert hga.hga_version() == 101
+    assert hga.hga_version() == 102
 
 
 def test_status_strings(lib):
@@ -71,6 +71,8 @@ BAD_CONFIGS = [
     (dict(softmax_scale=-1.0), hga.HGA_ERR_INVALID_ARGUMENT),
     (dict(chunk_size=32, q_block=32), hga.HGA_ERR_UNSUPPORTED),
     (dict(q_block=128), hga.HGA_ERR_UNSUPPORTED),
+    (dict(q_block=48), hga.HGA_ERR_UNSUPPORTED),       # must divide the 64-token chunk
+    (dict(q_block=0), hga.HGA_ERR_INVALID_ARGUMENT),
     (dict(sink_tokens=32), hga.HGA_ERR_UNSUPPORTED),
     (dict(head_dim=96), hga.HGA_ERR_UNSUPPORTED),
     (dict(head_dim=48, dtype="f32"), hga.HGA_ERR_UNSUPPORTED),
@@ -89,15 +91,18 @@ def test_config_validation(over, status):
     assert hga.hga_last_error()
 
 
-@pytest.mark.parametrize("q_start,n_q,seq_len,status", [
-    (14336, 2048, 16000, hga.HGA_ERR_INVALID_ARGUMENT),   # q_start + n_q > seq_len
-    (-64, 64, 16384, hga.HGA_ERR_INVALID_ARGUMENT),
-    (14300, 2048, 16384, hga.HGA_ERR_UNSUPPORTED),       # not a multiple of 64
-    (14336, 2000, 16384, hga.HGA_ERR_UNSUPPORTED),
-    (0, 64, 64 * 4097, hga.HGA_ERR_UNSUPPORTED),         # too many chunk candidates
+@pytest.mark.parametrize("q_start,n_q,seq_len,status,q_block", [
+    (14336, 2048, 16000, hga.HGA_ERR_INVALID_ARGUMENT, 64),   # q_start + n_q > seq_len
+    (-64, 64, 16384, hga.HGA_ERR_INVALID_ARGUMENT, 64),
+    (14300, 2048, 16384, hga.HGA_ERR_UNSUPPORTED, 64),       # not a multiple of 64
+    (14336, 2000, 16384, hga.HGA_ERR_UNSUPPORTED, 64),
+    (0, 64, 64 * 4097, hga.HGA_ERR_UNSUPPORTED, 64),         # too many chunk candidates
+    (16382, 1, 16383, hga.HGA_ERR_UNSUPPORTED, 1),           # seq_len (the buffers' capacity) not a multiple of 64
+    (14338, 4, 16384, hga.HGA_ERR_UNSUPPORTED, 4),       # q_start not a multiple of q_block
+    (14336, 6, 16384, hga.HGA_ERR_UNSUPPORTED, 4),       # n_q not a multiple of q_block
 ])
-def test_geometry_validation(q_start, n_q, seq_len, status):
-    c = cfg()
+def test_geometry_validation(q_start, n_q, seq_len, status, q_block):
+    c = cfg(q_block=q_block)
     assert _status(hga.hga_route, c, FAKE, q_start, n_q, seq_len, FAKE, FAKE, FAKE, FAKE, FAKE) == status
     assert _status(hga.hga_attend, c, FAKE, q_start, n_q, seq_len, FAKE, FAKE, FAKE, FAKE, FAKE) == status
     assert _status(hga.hga_route_attend, c, FAKE, q_start, n_q, seq_len, *[FAKE] * 8) == status

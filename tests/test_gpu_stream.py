@@ -21,7 +21,7 @@ def run(cfg, x, segment=None):
     c = hga_cfg(cfg)
     dt, L, d, g, hkv = cfg["dtype"], cfg["L"], cfg["d"], cfg["group"], cfg["hkv"]
     assert cfg["n_q"] == L
-    nb = L // 64
+    nb = L // cfg["q_block"]
     q, k, v = to_dev(x["q"], dt), to_dev(x["k"], dt), to_dev(x["v"], dt)
     gs = torch.full((hkv, L // g, d), float("nan"), device=DEV)
     cs = torch.full((hkv, L // 64, d), float("nan"), device=DEV)
@@ -53,6 +53,8 @@ CASES = {
     "bf16_seg64": (dict(L=512, n_q=512), 64),
     "bf16_gqa8": (dict(L=1024, n_q=1024, hq=16, hkv=2), 256),
     "f32": (dict(L=1024, n_q=1024, dtype="f32", d=64, rope_theta=None), 256),
+    "bf16_block16_seg192": (dict(L=1024, n_q=1024, q_block=16), 192),
+    "bf16_block1_seg64": (dict(L=256, n_q=256, q_block=1), 64),
 }
 
 
