@@ -16,6 +16,11 @@ The same line also reports the 65,536-token Qwen3-30B-A3B-shaped layer with
 its history in HBM and, separately, with its history in pinned host memory
 (that rate includes the PCIe transfer of the routed set).
 
+It also reports one-token decoding (query block of one token, routing over
+the resident summaries of the closed chunks, then attention) at the end of the
+16K and 64K sequences for batches of sequences, as generated tokens per
+second with the fused kernel's HBM roofline.
+
 Output: one JSON line (see the keys below). ``roofline`` covers the kernel
 that does the attention (the route-and-attend kernel, or the attention kernel
 where routing runs apart): the attention's algorithmic flops or bytes over
@@ -51,6 +56,8 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload index (default: the 16K segment)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the 64K lines")
+    ap.add_argument("--decode-batch", type=int, default=0, metavar="B",
+                    help="only the one-token decoding line of --config for a batch of B sequences")
     ap.add_argument("--host-tier", action="store_true",
                     help="main line with the history (tokens before the first query) in pinned host memory")
     ap.add_argument("--traffic-kib", type=float, nargs=2, default=None, metavar=("FETCH", "WRITE"),
@@ -359,6 +366,90 @@ def stream_line(passes, warmup):
                     "chunks, then routing and attention of its queries against the committed history"}
 
 
+def decode_bytes(cfg, pos, n_sel):
+    """HBM bytes one (sequence, KV head) item of a one-token decoding step
+    must move: the chunk summaries it scores (all candidates when the chunk
+    stage selects), the group summaries of its kept chunks (when the group
+    stage selects), K and V of its token set (fixed chunks, kept groups, the
+    open chunk up to the token), its G queries and outputs (with LSE) and its
+    index rows."""
+    d, G, g = cfg["d"], cfg["hq"] // cfg["hkv"], cfg["group"]
+    esz = 2 if cfg["dtype"] == "bf16" else 4
+    ms = pos // 64
+    a = min(cfg["sink"] // 64, ms)
+    bb = max(ms - cfg["local"] // 64, a)
+    ncand = bb - a
+    nsc = int(n_sel[0])
+    nsg = int(n_sel[1])
+    rows = (ncand if 0 < nsc < ncand else 0) + (64 // g * nsc if 0 < nsg < 64 // g * nsc else 0)
+    tokens = 64 * (a + ms - bb) + g * nsg + (pos - 64 * ms + 1)
+    return (4 * d * rows + 2 * esz * d * tokens + 2 * G * d * esz + 4 * G
+            + 4 * (cfg["top_chunks"] + cfg["top_groups"] + 2))
+
+
+def decode_line(cfg_id, batch, steps, warmup):
+    """One-token decoding steps over a batch of sequences at the end of
+    workload cfg_id's sequence (position L - 1, history L - 1 tokens): per
+    step, hga_route_attend with q_block 1 over the resident summaries of the
+    closed chunks. The batch is folded into the heads (sequence-major
+    [batch x heads]); every sequence repeats the workload's K/V and last query
+    at its own addresses. Summaries are built before timing (each closes once
+    per 64 generated tokens). Timed with HIP events around each launch on the
+    launch stream."""
+    import torch
+
+    import hierarchical_sparse_attention_hga_amd as hga
+    import synth
+    base = synth.config(cfg_id)
+    x = synth.make_inputs(base)
+    DEV = torch.device("cuda:0")
+    L, d, g = base["L"], base["d"], base["group"]
+    hq, hkv = batch * base["hq"], batch * base["hkv"]
+    c = hga.make_config(hq, hkv, d, base["top_chunks"], base["top_groups"], base["sink"], base["local"],
+                        dtype=base["dtype"], group_size=g, q_block=1)
+    k = to_dev(x["k"], base["dtype"], DEV).repeat(batch, 1, 1).contiguous()
+    v = to_dev(x["v"], base["dtype"], DEV).repeat(batch, 1, 1).contiguous()
+    q = to_dev(x["q"][:, -1:], base["dtype"], DEV).repeat(batch, 1, 1).contiguous()
+    del x
+    gs = torch.empty(hkv, L // g, d, device=DEV)
+    cs = torch.empty(hkv, L // 64, d, device=DEV)
+    ci = torch.empty(1, hkv, base["top_chunks"], dtype=torch.int32, device=DEV)
+    gi = torch.empty(1, hkv, base["top_groups"], dtype=torch.int32, device=DEV)
+    ns = torch.empty(1, hkv, 2, dtype=torch.int32, device=DEV)
+    out = torch.empty_like(q)
+    lse = torch.empty(hq, 1, device=DEV)
+    pos = L - 1
+    hga.hga_build_summaries_range(c, k, L, 0, pos // 64, gs, cs)
+
+    def one():
+        hga.hga_route_attend(c, q, pos, 1, L, cs, gs, k, v, ci, gi, ns, out, lse)
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if i % 2 == 0:
+            evs[i][0].record()
+        one()
+        if i % 2 == 0:
+            evs[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us = float(np.mean([evs[i][0].elapsed_time(evs[i][1]) * 1e3 for i in range(0, steps, 2)]))
+    nsel = ns.cpu().numpy().reshape(hkv, 2)
+    byts = float(sum(decode_bytes(base, pos, nsel[h]) for h in range(hkv)))
+    del k, v, gs, cs
+    torch.cuda.empty_cache()
+    return {"value": steps * batch / wall, "unit": "generated tokens/s", "kernel_us_mean": us,
+            "ms_per_step": wall / steps * 1e3,
+            "config": {"workload": f"{base['name']}-decode", "batch": batch, "history": pos,
+                       "q_heads": base["hq"], "kv_heads": base["hkv"], "q_block": 1},
+            "roofline": {"kernel": "route_attend_bf16", "bound": "hbm", "achieved": byts / (us * 1e-6) / 1e9,
+                         "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": byts / (us * 1e-6) / PEAK_HBM,
+                         "traffic": None, "algorithmic_bytes": byts}}
+
+
 def measure(cfg_id, steps, warmup, split=0, fused=None):
     w = Workload(cfg_id, split, fused)
     wall, stage = w.run(steps, warmup)
@@ -377,6 +468,9 @@ def main():
     torch.cuda.init()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.decode_batch:
+        print(json.dumps(decode_line(args.config, args.decode_batch, args.steps, args.warmup)), flush=True)
         return
     split = 0
     if args.host_tier:
@@ -429,6 +523,9 @@ def main():
                         "needs crosses the host link once per step into an HBM cache, then attention",
                 "host_link_bytes_per_step": rh.host_bytes,
                 "stages_us_mean": rh.stages("mean")}
+        extra["decode_16k_batch64"] = decode_line(2, 64, 40, 5)
+        extra["decode_16k_single_sequence"] = decode_line(2, 1, 40, 5)
+        extra["decode_64k_batch32"] = decode_line(3, 32, 40, 5)
         line["also"] = extra
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.config)
