@@ -39,9 +39,13 @@
  *              error nothing is enqueued and a status other than HGA_OK is
  *              returned. hga_last_error() gives a message (thread-local).
  *              Kernel launch failures return HGA_ERR_DEVICE.
- *   Support    chunk_size == q_block == 64; group_size divides 64; sink and
- *              local sizes are multiples of chunk_size; q_start, n_q and
- *              seq_len are multiples of chunk_size. bfloat16 needs
+ *   Support    chunk_size == 64; q_block divides 64 (1 routes every token
+ *              on its own, as when decoding); group_size divides 64; sink and
+ *              local sizes are multiples of chunk_size; seq_len is a multiple
+ *              of chunk_size; q_start and n_q are multiples of q_block.
+ *              Rows of K, V and the summaries past q_start + n_q are never
+ *              read, so seq_len may be the capacity of a decoding cache.
+ *              bfloat16 needs
  *              head_dim 64 or 128; float32 needs head_dim % 4 == 0 and
  *              head_dim <= 128. Anything else returns HGA_ERR_UNSUPPORTED.
  */
@@ -75,7 +79,7 @@ typedef struct {
   int32_t head_dim;      /* d */
   int32_t chunk_size;    /* tokens per chunk (64) */
   int32_t group_size;    /* tokens per group (8); divides chunk_size */
-  int32_t q_block;       /* queries per routing block (== chunk_size) */
+  int32_t q_block;       /* B: queries per routing block, a divisor of chunk_size */
   int32_t top_chunks;    /* kc >= 0: routed chunks kept per block and KV head */
   int32_t top_groups;    /* kg >= 0: routed groups kept per block and KV head */
   int32_t sink_tokens;   /* S: the first S tokens are always attended */
@@ -128,12 +132,14 @@ hga_status hga_build_summaries_range(const hga_config* cfg, const void* k, int64
                                      float* group_sum, float* chunk_sum, void* stream);
 
 /* Two-level routing (section 2.1, "Chunk selection", "Group selection").
- * For query block b (positions s = q_start + 64 b .. s + 63) and KV head h:
- *   block query   mean of Q over the block's 64 positions and the
+ * For query block b (positions s = q_start + B b .. s + B - 1, B = q_block)
+ * and KV head h, with c0 = 64 floor(s / 64) the first token of the block's
+ * chunk:
+ *   block query   mean of Q over the block's B positions and the
  *                 Hq/Hkv query heads of h (float64 accumulation);
  *   fixed chunks  sink: chunks before sink_tokens; local: the chunks holding
- *                 the local_tokens before s (only chunks that end by s);
- *   chunk stage   candidates are the chunks ending by s that are not fixed;
+ *                 the local_tokens before c0 (only chunks that end by c0);
+ *   chunk stage   candidates are the chunks ending by c0 that are not fixed;
  *                 score = block query . chunk_sum (float64 dot of the float32
  *                 summary); keep the top_chunks highest, ties to the lower
  *                 chunk index;
@@ -145,9 +151,9 @@ hga_status hga_build_summaries_range(const hga_config* cfg, const void* k, int64
  *   group_sum  group summaries, tiered at a token split (a multiple of
  *              chunk_size, <= q_start); host rows are read only when the group
  *              stage must choose (top_groups < groups of the kept chunks).
- *   chunk_idx  device, [n_q/64][Hkv][top_chunks] int32, ascending, -1 padded.
- *   group_idx  device, [n_q/64][Hkv][top_groups] int32, ascending, -1 padded.
- *   n_sel      device, [n_q/64][Hkv][2] int32: kept chunks, kept groups.
+ *   chunk_idx  device, [n_q/B][Hkv][top_chunks] int32, ascending, -1 padded.
+ *   group_idx  device, [n_q/B][Hkv][top_groups] int32, ascending, -1 padded.
+ *   n_sel      device, [n_q/B][Hkv][2] int32: kept chunks, kept groups.
  *   workspace  unused (hga_workspace_size returns 0); may be NULL. */
 hga_status hga_route(const hga_config* cfg, const void* q, int64_t q_start, int64_t n_q,
                      int64_t seq_len, const float* chunk_sum, const hga_tiered* group_sum,
@@ -156,8 +162,10 @@ hga_status hga_route(const hga_config* cfg, const void* q, int64_t q_start, int6
 
 /* Exact-token routed attention (section 2.1, "Exact-token attention").
  * Query at position p of block b attends, with causal masking t <= p, to the
- * token set: the fixed sink and local chunks, the kept groups, and the block's
- * own 64 tokens. out = softmax(scale * q . k_t) @ v_t; lse = log-sum-exp of the
+ * token set: the fixed sink and local chunks, the kept groups, and the
+ * block's own chunk from its first token c0 up to the block's last position
+ * (for B = 64 the block itself; for smaller blocks the chunk is still open,
+ * has no summary, and its earlier tokens are kept whole). out = softmax(scale * q . k_t) @ v_t; lse = log-sum-exp of the
  * scaled scores (natural log).
  *   q          device, [Hq][n_q][d] of cfg->dtype.
  *   k, v       [Hkv][seq_len][d] of cfg->dtype, tiered at a token split
@@ -169,13 +177,13 @@ hga_status hga_route(const hga_config* cfg, const void* q, int64_t q_start, int6
  *              of routed sets shared across query blocks, section 2.1); sink
  *              and local windows may then span at most 256 chunks
  *              (HGA_ERR_UNSUPPORTED otherwise).
- *   group_idx  device, [n_q/64][Hkv][top_groups] as written by hga_route.
- *              An entry is usable when it is >= 0, its group ends by the block
- *              start and it lies outside the sink and local chunks; a usable
+ *   group_idx  device, [n_q/B][Hkv][top_groups] as written by hga_route.
+ *              An entry is usable when it is >= 0, its group ends by the
+ *              block start and it lies outside the sink and local chunks; a usable
  *              entry that is not greater than every earlier usable entry of
  *              its row is skipped, so each token counts once and an ascending
  *              row is taken whole.
- *   n_sel      device, [n_q/64][Hkv][2]; the second value (clamped to
+ *   n_sel      device, [n_q/B][Hkv][2]; the second value (clamped to
  *              [0, top_groups]) is how many entries of the row to read.
  *   out        device, [Hq][n_q][d] of cfg->dtype.
  *   lse        device, [Hq][n_q] float32, or NULL.
@@ -191,8 +199,8 @@ hga_status hga_attend(const hga_config* cfg, const void* q, int64_t q_start, int
  * its chunk_idx / group_idx / n_sel, which are written as well. Arguments
  * have the meaning, layout and ownership they have in those two calls; the
  * workspace is the one hga_attend needs for this K/V split. With bfloat16,
- * K/V entirely on the device (split 0) and at most 4 query heads per KV head,
- * both steps run in one kernel, each workgroup routing its own query block
+ * K/V entirely on the device (split 0) and at most 256 query rows per block
+ * and KV head (Hq/Hkv x q_block), both steps run in one kernel, each workgroup routing its own query block
  * before attending over the groups it kept; otherwise the call runs the two
  * steps one after the other. Errors are those of either call. */
 hga_status hga_route_attend(const hga_config* cfg, const void* q, int64_t q_start, int64_t n_q,
@@ -213,7 +221,7 @@ hga_status hga_route_attend(const hga_config* cfg, const void* q, int64_t q_star
  *   k, v       device, [Hkv][seq_len][d] of cfg->dtype.
  *   chunk_sum, group_sum   device, as written by hga_build_summaries (every
  *              row is written).
- *   chunk_idx, group_idx, n_sel   device, [seq_len/64][Hkv][...] as in hga_route.
+ *   chunk_idx, group_idx, n_sel   device, [seq_len/B][Hkv][...] as in hga_route.
  *   lse        device, [Hq][seq_len] float32, or NULL.
  *   segment    a positive multiple of chunk_size, else HGA_ERR_INVALID_ARGUMENT.
  * Everything is on the device (no host tier); no workspace is needed. */
