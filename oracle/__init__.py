@@ -55,6 +55,7 @@ def _load():
         lib.orc_abs_summaries.argtypes = [C.POINTER(_Cfg), P, P, P]
         lib.orc_route.argtypes = [C.POINTER(_Cfg), P, P, P, P, P, C.c_int, P, P, P, P, P]
         lib.orc_attend.argtypes = [C.POINTER(_Cfg), P, P, P, C.c_int, P, P, P, P, P]
+        lib.orc_attend_backward.argtypes = [C.POINTER(_Cfg), P, P, P, P, P, P, P, P, P]
         lib.orc_token_set.argtypes = [C.POINTER(_Cfg), C.c_int, P, C.c_int, P, C.c_int64]
         lib.orc_token_set.restype = C.c_int64
         assert lib.orc_diag_width() == 8
@@ -145,6 +146,26 @@ def attend(cfg, q64, k64, v64, items, group_idx, n_groups):
     lib.orc_attend(C.byref(make_cfg(cfg)), _ptr(_f64(q64)), _ptr(_f64(k64)), _ptr(_f64(v64)), n,
                    _ptr(it), _ptr(gi), _ptr(ng), _ptr(out), _ptr(lse))
     return out, lse
+
+
+def attend_backward(cfg, q64, k64, v64, dout64, group_idx, n_groups):
+    """Backward of step 7 with the routing fixed, over every (block, KV head).
+
+    group_idx [nb][hkv][kg], n_groups [nb][hkv]; dout [Hq][n_q][d]. Returns dq
+    [Hq][n_q][d] and dk, dv [Hkv][L][d] (float64; every key row, zero where no
+    query attends it).
+    """
+    lib = _load()
+    nb, hkv, kg = cfg["n_q"] // cfg["q_block"], cfg["hkv"], cfg["top_groups"]
+    gi = np.ascontiguousarray(np.asarray(group_idx, dtype=np.int32).reshape(nb, hkv, kg))
+    ng = np.ascontiguousarray(np.asarray(n_groups, dtype=np.int32).reshape(nb, hkv))
+    q64, k64, v64, dout64 = _f64(q64), _f64(k64), _f64(v64), _f64(dout64)
+    dq = np.empty_like(q64)
+    dk = np.empty_like(k64)
+    dv = np.empty_like(v64)
+    lib.orc_attend_backward(C.byref(make_cfg(cfg)), _ptr(q64), _ptr(k64), _ptr(v64), _ptr(dout64),
+                            _ptr(gi), _ptr(ng), _ptr(dq), _ptr(dk), _ptr(dv))
+    return dq, dk, dv
 
 
 def token_set(cfg, b, group_idx, n_groups):

@@ -28,6 +28,8 @@
  *                 summary, so its earlier tokens are kept whole; for a block
  *                 of one whole chunk this is the block's own tokens).
  *   7. attention  exact causal softmax attention over the token set.
+ *   7'. backward  gradients of step 7 with respect to Q, K and V, the
+ *                 routing held fixed (see orc_attend_backward).
  *
  * Steps 4 and 5 are decisions. Summaries are stored in float32 (the mean
  * rounded to nearest); a decision score is the float64 dot of the float64
@@ -333,6 +335,85 @@ int orc_attend(const orc_cfg* c, const double* q, const double* k, const double*
     attend_item(c, q, k, v, items[2 * it], items[2 * it + 1],
                 group_idx + (int64_t)it * c->top_groups, n_groups[it],
                 out + (int64_t)it * G * B * c->d, lse + (int64_t)it * G * B);
+  return 0;
+}
+
+/* ------------------------------------------------------------------ backward of step 7 */
+/* Gradients of step 7 with the routing held fixed: the pages keep routing out
+ * of the gradient (no-grad selection) while the gather and the exact-token
+ * attention stay differentiable ("Long-Context Fine-Tuning with Limited
+ * VRAM", section 2.1). For one query row with token set T (causal, t <= p),
+ * scores z_t = scale q . k_t and weights P_t = softmax(z)_t, and the output
+ * gradient g = dO:
+ *   dP_t = g . v_t,   D = sum_t P_t dP_t,   dS_t = P_t (dP_t - D),
+ *   dq  = scale sum_t dS_t k_t,
+ *   dk_t += scale dS_t q,   dv_t += P_t g.
+ * Keys and values collect the contributions of every row of every block that
+ * attends them. Items of different KV heads touch disjoint rows, so heads run
+ * in parallel and the blocks of one head in order. */
+static void backward_item(const orc_cfg* c, const double* q, const double* k, const double* v,
+                          const double* dout, int b, int h, const int32_t* group_idx, int n_groups,
+                          double* dq, double* dk, double* dv) {
+  const int64_t L = c->seq_len, d = c->d, q0 = q_start(c);
+  const int G = c->hq / c->hkv, B = c->q_block;
+  const int64_t s = q0 + (int64_t)b * B;
+  int32_t* T = (int32_t*)malloc(sizeof(int32_t) * (size_t)(s + B));
+  const int64_t nt = orc_token_set(c, b, group_idx, n_groups, T, s + B);
+  double* z = (double*)malloc(sizeof(double) * (size_t)nt);
+  double* dp = (double*)malloc(sizeof(double) * (size_t)nt);
+  for (int r = 0; r < G; ++r)
+    for (int i = 0; i < B; ++i) {
+      const int64_t pos = s + i, row = (int64_t)(h * G + r) * c->n_q + (pos - q0);
+      const double* qi = q + row * d;
+      const double* gi = dout + row * d;
+      double mx = -INFINITY;
+      int64_t nv = 0;
+      for (int64_t a = 0; a < nt && T[a] <= pos; ++a) {
+        const double* kt = k + ((int64_t)h * L + T[a]) * d;
+        const double* vt = v + ((int64_t)h * L + T[a]) * d;
+        double dot = 0.0, gdot = 0.0;
+        for (int64_t e = 0; e < d; ++e) { dot += qi[e] * kt[e]; gdot += gi[e] * vt[e]; }
+        z[a] = c->scale * dot;
+        dp[a] = gdot;
+        if (z[a] > mx) mx = z[a];
+        nv = a + 1;
+      }
+      double den = 0.0;
+      for (int64_t a = 0; a < nv; ++a) den += exp(z[a] - mx);
+      double D = 0.0;
+      for (int64_t a = 0; a < nv; ++a) D += exp(z[a] - mx) / den * dp[a];
+      double* dqi = dq + row * d;
+      for (int64_t e = 0; e < d; ++e) dqi[e] = 0.0;
+      for (int64_t a = 0; a < nv; ++a) {
+        const double P = exp(z[a] - mx) / den;
+        const double dS = P * (dp[a] - D);
+        const double* kt = k + ((int64_t)h * L + T[a]) * d;
+        double* dkt = dk + ((int64_t)h * L + T[a]) * d;
+        double* dvt = dv + ((int64_t)h * L + T[a]) * d;
+        for (int64_t e = 0; e < d; ++e) {
+          dqi[e] += c->scale * dS * kt[e];
+          dkt[e] += c->scale * dS * qi[e];
+          dvt[e] += P * gi[e];
+        }
+      }
+    }
+  free(dp); free(z); free(T);
+}
+
+/* dq [Hq][n_q][d]; dk, dv [Hkv][L][d] (every key row, zero where no query
+ * attends it). group_idx [nb][Hkv][kg] and n_groups [nb][Hkv] as the forward
+ * takes them. */
+int orc_attend_backward(const orc_cfg* c, const double* q, const double* k, const double* v,
+                        const double* dout, const int32_t* group_idx, const int32_t* n_groups,
+                        double* dq, double* dk, double* dv) {
+  const int64_t nb = c->n_q / c->q_block;
+  memset(dk, 0, sizeof(double) * (size_t)(c->hkv * c->seq_len * c->d));
+  memset(dv, 0, sizeof(double) * (size_t)(c->hkv * c->seq_len * c->d));
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int h = 0; h < c->hkv; ++h)
+    for (int64_t b = 0; b < nb; ++b)
+      backward_item(c, q, k, v, dout, (int)b, h, group_idx + (b * c->hkv + h) * c->top_groups,
+                    n_groups[b * c->hkv + h], dq, dk, dv);
   return 0;
 }
 

@@ -377,3 +377,104 @@ def test_planted_margins_tiny_workload():
             assert dg[b, oracle.DG_GAP_C] >= 0.5
             assert set(planted) <= set(gi[b].tolist())
     assert n_checked >= 2
+
+
+# ------------------------------------------------------------------ backward of step 7
+def _routing(cfg, q, k):
+    items = oracle.all_items(cfg)
+    ci, gi, ns, _ = oracle.route(cfg, q, k, items)
+    nb, hkv = cfg["n_q"] // cfg["q_block"], cfg["hkv"]
+    return items, gi.reshape(nb, hkv, -1), ns[:, 1].reshape(nb, hkv)
+
+
+def _forward_full(cfg, q, k, v, items, gi, ng):
+    """Forward output [Hq][n_q][d] for fixed routing."""
+    G, B = cfg["hq"] // cfg["hkv"], cfg["q_block"]
+    flat_gi = gi.reshape(len(items), -1)
+    flat_ng = ng.reshape(len(items))
+    out, _ = oracle.attend(cfg, q, k, v, items, flat_gi, flat_ng)
+    full = np.empty_like(q)
+    for n, (b, h) in enumerate(items):
+        for r in range(G):
+            full[h * G + r, b * B:(b + 1) * B] = out[n, r]
+    return full
+
+
+@pytest.mark.parametrize("q_block,n_q", [(16, 48), (4, 36)])
+def test_backward_matches_finite_differences(q_block, n_q):
+    """Central differences of L = sum(dO * O) with the routing held fixed, for
+    every element of Q, K and V (history keys included)."""
+    cfg = tiny_cfg(L=64, n_q=n_q, hq=2, hkv=1, d=4, q_block=q_block, sink=16, local=0,
+                   top_chunks=1, top_groups=2)
+    q, k, v = rand_qkv(cfg, 21)
+    dout = np.random.default_rng(22).standard_normal(q.shape)
+    items, gi, ng = _routing(cfg, q, k)
+    assert ng.max() > 0          # some block keeps routed groups
+    dq, dk, dv = oracle.attend_backward(cfg, q, k, v, dout, gi, ng)
+    eps = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args = {"q": q, "k": k, "v": v}
+            fp = _forward_full(cfg, **{**args, name: xp}, items=items, gi=gi, ng=ng)
+            fm = _forward_full(cfg, **{**args, name: xm}, items=items, gi=gi, ng=ng)
+            num[idx] = ((fp - fm) * dout).sum() / (2 * eps)
+        np.testing.assert_allclose(g, num, rtol=0, atol=1e-7, err_msg=name)
+    assert np.abs(dk[:, :16]).max() > 0   # the sink chunk (history) receives gradient
+
+
+def _dense_backward(cfg, q, k, v, dout):
+    """Matrix-form backward of dense causal attention: P = softmax(S),
+    dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(P * dP)), dQ = s dS K,
+    dK = s dS^T Q (summed over the query heads of each KV head)."""
+    G = cfg["hq"] // cfg["hkv"]
+    q0 = cfg["L"] - cfg["n_q"]
+    scale = 1.0 / math.sqrt(cfg["d"])
+    mask = np.arange(cfg["L"])[None, :] <= np.arange(q0, cfg["L"])[:, None]
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for hq in range(cfg["hq"]):
+        h = hq // G
+        S = np.where(mask, scale * q[hq] @ k[h].T, -np.inf)
+        P = np.exp(S - S.max(axis=1, keepdims=True))
+        P /= P.sum(axis=1, keepdims=True)
+        dP = dout[hq] @ v[h].T
+        dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+        dq[hq] = scale * dS @ k[h]
+        dk[h] += scale * dS.T @ q[hq]
+        dv[h] += P.T @ dout[hq]
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("q_block,L,n_q", [(16, 256, 224), (1, 183, 40), (8, 176, 176)])
+def test_backward_dense_equivalence(q_block, L, n_q):
+    """A budget covering every candidate makes the token set every earlier
+    token: the gradients are those of dense causal attention."""
+    cfg = tiny_cfg(L=L, n_q=n_q, hq=4, hkv=2, q_block=q_block, top_chunks=L // 16, top_groups=L // 4)
+    q, k, v = rand_qkv(cfg, 23)
+    dout = np.random.default_rng(24).standard_normal(q.shape)
+    _, gi, ng = _routing(cfg, q, k)
+    got = oracle.attend_backward(cfg, q, k, v, dout, gi, ng)
+    ref = _dense_backward(cfg, q, k, v, dout)
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-11, err_msg=name)
+
+
+def test_backward_invariants():
+    """Shifting every key of a head by one vector moves each row's scores by a
+    constant, so the key gradients of a head sum to zero; each row's weights
+    sum to one, so the value gradients of a head sum to the output gradients
+    of its query heads."""
+    cfg = tiny_cfg(hq=4, hkv=2, top_chunks=2, top_groups=3)
+    q, k, v = rand_qkv(cfg, 25)
+    dout = np.random.default_rng(26).standard_normal(q.shape)
+    _, gi, ng = _routing(cfg, q, k)
+    dq, dk, dv = oracle.attend_backward(cfg, q, k, v, dout, gi, ng)
+    G = cfg["hq"] // cfg["hkv"]
+    for h in range(cfg["hkv"]):
+        np.testing.assert_allclose(dk[h].sum(axis=0), 0.0, atol=1e-11)
+        np.testing.assert_allclose(dv[h].sum(axis=0), dout[h * G:(h + 1) * G].sum(axis=(0, 1)), atol=1e-11)
+    # keys after the last query and outside every token set get nothing
+    assert np.abs(dq).max() > 0
