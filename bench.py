@@ -219,7 +219,7 @@ class Workload:
             p.free()
 
 
-KERNEL_SOURCES = ("hga_attend.hip", "hga_route_impl.h", "hga_internal.h")
+KERNEL_SOURCES = ("hga_attend.hip", "hga_attend_impl.h", "hga_route_impl.h", "hga_internal.h")
 
 
 def source_sha256():

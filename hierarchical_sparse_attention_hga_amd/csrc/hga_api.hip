@@ -136,6 +136,7 @@ size_t hga_workspace_size(const hga_config* cfg, int64_t seq_len, int64_t n_q, i
     case HGA_WS_ROUTE: return 0;
     case HGA_WS_ATTEND: return 0;
     case HGA_WS_ATTEND_TIERED: return hga::tier_cache_bytes(s, seq_len - n_q);
+    case HGA_WS_BACKWARD: return hga::backward_workspace_bytes(s);
     default: fail(HGA_ERR_INVALID_ARGUMENT, "unknown workspace kind %d", which); return (size_t)-1;
   }
 }
@@ -284,6 +285,26 @@ hga_status hga_route_attend(const hga_config* cfg, const void* q, int64_t q_star
                        "hga_route_attend attention launch");
 }
 
+hga_status hga_attend_backward(const hga_config* cfg, const void* q, int64_t q_start, int64_t n_q,
+                               int64_t seq_len, const void* k, const void* v, const int32_t* group_idx,
+                               const int32_t* n_sel, const void* out, const float* lse, const void* dout,
+                               void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes, void* stream) {
+  hga::Shape s;
+  hga_status st = make_shape(cfg, seq_len, q_start, n_q, &s);
+  if (st != HGA_OK) return st;
+  if (s.dtype != HGA_BF16) return fail(HGA_ERR_UNSUPPORTED, "the backward is built for bfloat16 only");
+  if (n_q == 0) return ok();
+  if (!q || !k || !v || !n_sel || !out || !lse || !dout || !dq || !dk || !dv || (s.kg > 0 && !group_idx))
+    return fail(HGA_ERR_INVALID_ARGUMENT,
+                "q, k, v, group_idx, n_sel, out, lse, dout, dq, dk and dv must be non-NULL");
+  const size_t need = hga::backward_workspace_bytes(s);
+  if (!workspace || ws_bytes < need)
+    return fail(HGA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : (size_t)0);
+  return device_status(hga::launch_attend_backward(s, q, k, v, group_idx, n_sel, out, lse, dout, dq, dk, dv,
+                                                   workspace, (hipStream_t)stream),
+                       "hga_attend_backward launch");
+}
+
 const char* hga_status_string(hga_status status) {
   switch (status) {
     case HGA_OK: return "ok";
@@ -297,6 +318,6 @@ const char* hga_status_string(hga_status status) {
 
 const char* hga_last_error(void) { return g_err; }
 
-int32_t hga_version(void) { return 102; }
+int32_t hga_version(void) { return 103; }
 
 }  // extern "C"

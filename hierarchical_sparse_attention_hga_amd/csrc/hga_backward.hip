@@ -1,0 +1,566 @@
+// Backward of the HGA exact-token attention ("Long-Context Fine-Tuning with
+// Limited VRAM", section 2.1: the selection is not differentiated, the gather
+// and the exact-token attention are; section 2.2: only the active segment is
+// differentiable, the history's K and V are detached, so gradients are formed
+// for the call's queries and for the keys and values at the call's own
+// positions).
+//
+// The token set of every (query block, KV head) item is fixed by the kept
+// groups the forward used. For a query row with weights P_t (recomputed
+// exactly from the forward's log-sum-exp) and output gradient dO:
+//   dP_t = dO . v_t,   D = dO . O,   dS_t = P_t (dP_t - D),
+//   dQ = scale sum_t dS_t k_t,   dK_t = scale sum dS_t q,   dV_t = sum P_t dO.
+// Three kernels run on the call's stream:
+//   bwd_prep_kernel  per item: the usable kept groups (the forward plan's
+//                    validation, so both passes see the forward's token set)
+//                    and D = dO . O of each of its rows, into the workspace;
+//   bwd_dq_kernel    per item, laid out like the forward kernel: the item's
+//                    K/V tiles stream through LDS; S^T = K Q^T, P^T from the
+//                    LSE, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T, all with
+//                    v_mfma_f32_32x32x16_bf16 (K read both row-wise and
+//                    transposed, hence kv_swizzle);
+//   bwd_dkv_kernel   per (KV head, chunk holding positions of the call): the
+//                    chunk's K and V stay in registers as MFMA operands while
+//                    the query rows of every block that attends the chunk
+//                    stream through LDS in 64-row tiles (Q and dO, with their
+//                    LSE and D): S = Q K^T, P, dP = dO V^T, dS, then
+//                    dV^T += dO^T P and dK^T += Q^T dS. A key's gradient is
+//                    summed inside one workgroup, in block order: no atomics,
+//                    and the result does not depend on scheduling.
+#include "hga_attend_impl.h"
+
+namespace hga {
+namespace {
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const float* lse;
+  const void* dout;
+  const int32_t* gidx;
+  const int32_t* nsel;
+  float* dd;          // workspace [Hq][n_q]: D = dO . O
+  int32_t* used;      // workspace [nb][Hkv][kg]: usable kept groups, ascending
+  int32_t* nused;     // workspace [nb][Hkv]
+  void* dq;
+  void* dk;
+  void* dv;
+  int wg_per_item;    // bwd_dq_kernel workgroups per item
+  int64_t m0;         // first chunk holding a position of the call
+  int nchunks;        // chunks holding positions of the call
+  Shape s;
+};
+
+__device__ inline float bf16_bits_to_float(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+// ------------------------------------------------------------ preparation
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs A) {
+  __shared__ int sRuns[kMaxRouted];
+  __shared__ int sScan[16];
+  const Shape& S = A.s;
+  const int h = (int)(blockIdx.x / S.nb), b = (int)(blockIdx.x % S.nb);
+  const Plan P = make_plan(S, b, h, A.gidx, A.nsel, sRuns, sScan, kMaxRouted);
+  const int64_t it = (int64_t)b * S.hkv + h;
+  for (int i = threadIdx.x; i < P.nrouted; i += blockDim.x) A.used[it * S.kg + i] = sRuns[i] / S.g;
+  if (threadIdx.x == 0) A.nused[it] = P.nrouted;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nrows = S.G * S.B;
+  const uint16_t* o = static_cast<const uint16_t*>(A.out);
+  const uint16_t* g = static_cast<const uint16_t*>(A.dout);
+  for (int r = wave; r < nrows; r += blockDim.x >> 6) {
+    const int64_t row = (int64_t)(h * S.G + r / S.B) * S.qs + (int64_t)b * S.B + r % S.B;
+    float acc = 0.0f;
+    for (int e = lane; e < S.d; e += 64)
+      acc += bf16_bits_to_float(o[row * S.d + e]) * bf16_bits_to_float(g[row * S.d + e]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0) A.dd[row] = acc;
+  }
+}
+
+// ------------------------------------------------------------ dQ
+template <int D>
+struct BwdQSmem {
+  uint16_t k[2][kChunk * D];   // kv_swizzle: read row-wise and transposed
+  uint16_t v[2][kChunk * D];   // k_swizzle: read row-wise
+  int runs[kMaxRoutedAttn];
+};
+
+// One workgroup slot z of item (b, h): 8 waves of 32 query rows, the item's
+// token-set tiles in the forward's order through a 2-stage LDS ring.
+template <int D>
+__global__ __launch_bounds__(kAttnThreads) void bwd_dq_kernel(BwdArgs A) {
+  __shared__ BwdQSmem<D> sm;
+  constexpr int NP = D / 8;
+  constexpr int RPI = 64 / NP;
+  constexpr int RPW = kChunk / kAttnWaves;
+  constexpr int KI = RPW / RPI;   // loads per wave per tensor per tile
+  const Shape& S = A.s;
+  int b, h, z;
+  item_of_block(S, A.wg_per_item, &b, &h, &z);
+  Plan P;
+  plan_windows(S, b, &P);
+  const int64_t it = (int64_t)b * S.hkv + h;
+  const int nr = A.nused[it];
+  for (int i = threadIdx.x; i < nr; i += kAttnThreads) sm.runs[i] = A.used[it * S.kg + i] * S.g;
+  P.nrouted = nr;
+  P.nrt = (nr + kChunk / S.g - 1) / (kChunk / S.g);
+  P.ntiles = P.nfix + P.nrt + 1;
+  __syncthreads();
+  const int nt = P.ntiles;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5, col = lane & 31;
+  const int nrows = S.G * S.B;
+  const int rb = z * kAttnWaves + wave;
+  const bool active = 32 * rb < nrows;
+  const int row = 32 * rb + col;
+  const bool live = row < nrows;
+  const int lgB = __ffs(S.B) - 1;
+  const int head = h * S.G + (row >> lgB);
+  const int qi = row & (S.B - 1);
+  const int64_t qrow = (int64_t)head * S.qs + (int64_t)b * S.B + qi;
+
+  // queries and output gradients of this lane's column as MFMA B operands
+  // (d = 16 ks + 8 hl + e); zero on columns past the item's rows
+  bf16x8 qf[D / 16], gf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) qf[ks] = gf[ks] = bf16x8{};
+  float lse2 = 0.0f, dterm = 0.0f;
+  if (live) {
+    const uint16_t* qp = static_cast<const uint16_t*>(A.q) + qrow * D + 8 * hl;
+    const uint16_t* gp = static_cast<const uint16_t*>(A.dout) + qrow * D + 8 * hl;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 16 * ks));
+      gf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(gp + 16 * ks));
+    }
+    lse2 = A.lse[qrow] * kLog2e;
+    dterm = A.dd[qrow];
+  }
+
+  const int lg = __ffs(S.g) - 1;
+  const KVRows kv{static_cast<const uint16_t*>(A.k) + (int64_t)h * S.kvs * D,
+                  static_cast<const uint16_t*>(A.v) + (int64_t)h * S.kvs * D, nullptr, nullptr};
+  // run-table entries one tile ahead, as in the forward
+  int raw[KI];
+  auto run_of = [&](int t, int sl) { return ((t - P.nfix) << (6 - lg)) + (sl >> lg); };
+  auto fetch = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int rr = wave * RPW + i * RPI + lane / NP;
+      raw[i] = sm.runs[run_of(t, rr) & (kMaxRoutedAttn - 1)];
+    }
+  };
+  const int diag0 = (int)P.c0;
+  const int dlim = P.dlim;
+  auto issue = [&](int t) {
+    const uint32_t off = (uint32_t)((t & 1) * kChunk * D * 2);
+    issue_tile<D, 2, 0>(kv, lds_addr(&sm.k[0][0]) + off, lds_addr(&sm.v[0][0]) + off, [&](int i, int sl) -> int {
+      if (t < P.nfix) return (int)((t < P.a ? t : P.bb + (t - P.a)) * kChunk) + sl;
+      if (t < P.nfix + P.nrt) return run_of(t, sl) < P.nrouted ? raw[i] + (sl & ((1 << lg) - 1)) : 0;
+      return diag0 + (sl < dlim ? sl : 0);
+    });
+  };
+
+  constexpr int RB = D * 2;
+  // row reads of K (kv_swizzle) and V (k_swizzle): lane (col, hl) reads piece
+  // 2 ks + hl of row col (+ 32 for the second half)
+  uint32_t koff[D / 16], voff[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    koff[ks] = (uint32_t)(col * RB + (((2 * ks + hl) ^ kv_swizzle<D>(col)) << 4));
+    voff[ks] = (uint32_t)(col * RB + (((2 * ks + hl) ^ k_swizzle<D>(col)) << 4));
+  }
+  // transposing reads of K: lane j of 16-lane group g reads row vrow (lo) and
+  // vrow + 8 (hi), columns vcol (+ 32 db); kv_swizzle differs between the two
+  // rows, and is unchanged by the row additions (multiples of 16)
+  uint32_t tlo[D / 32], thi[D / 32];
+  {
+    const int vj = lane & 15, vg = lane >> 4;
+    const int vcol = 16 * (vg & 1) + 4 * (vj & 3);
+    const int vrow = 4 * hl + (vj >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int c = 32 * db + vcol;
+      tlo[db] = (uint32_t)(vrow * RB + (((c >> 3) ^ kv_swizzle<D>(vrow)) << 4) + ((c & 7) << 1));
+      thi[db] = (uint32_t)((vrow + 8) * RB + (((c >> 3) ^ kv_swizzle<D>(vrow + 8)) << 4) + ((c & 7) << 1));
+    }
+  }
+  const char* sKb = reinterpret_cast<const char*>(&sm.k[0][0]);
+  const char* sVb = reinterpret_cast<const char*>(&sm.v[0][0]);
+  const float sl2 = S.scale * kLog2e;
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
+
+  fetch(0);
+  issue(0);
+  fetch(1);
+  for (int t = 0; t < nt; ++t) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();   // every wave's loads of tile t landed; tile t - 1 is free
+    if (t + 1 < nt) {
+      issue(t + 1);
+      fetch(t + 2);
+    }
+    if (!active) continue;
+    const uint32_t stage = (uint32_t)((t & 1) * kChunk * RB);
+    const char* kt = sKb + stage;
+    const char* vt = sVb + stage;
+    f32x16 sacc[2], pacc[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        kf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kt + koff[ks] + 32 * tb * RB));
+        vf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vt + voff[ks] + 32 * tb * RB));
+      }
+      sacc[tb] = f32x16{};
+      pacc[tb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        sacc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], sacc[tb], 0, 0, 0);
+        pacc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks], gf[ks], pacc[tb], 0, 0, 0);
+      }
+    }
+    // the forward's masks: slot of accumulator r of half tb is
+    // 32 tb + 8 (r >> 2) + 4 hl + (r & 3)
+    const bool diag = t == nt - 1;
+    const int lim = tile_limit(P, S.g, t);
+    if (diag || lim < kChunk) {
+      const int thr = (diag ? P.off + qi + 1 : lim) - 4 * hl;
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * tb + 8 * (r >> 2) + (r & 3) >= thr) sacc[tb][r] = -INFINITY;
+    }
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      bf16x8 sf[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[tb][r], sl2, -lse2));
+        sf[r >> 3][r & 7] = (__bf16)(p * (pacc[tb][r] - dterm));
+      }
+      // dQ^T += K^T dS^T: the A operand of lane (half hl, column kd) holds K
+      // at tokens 32 tb + 16 mm + 4 hl + {0..3, 8..11}
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          const char* base = kt + (32 * tb + 16 * mm) * RB;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(base + tlo[db]));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(base + thi[db]));
+          const s16x8 w = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), sf[mm], acc[db], 0, 0, 0);
+        }
+    }
+  }
+  if (!live) return;
+  uint16_t* op = static_cast<uint16_t*>(A.dq) + qrow * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      bf16x4 v4;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) v4[ii] = (__bf16)(acc[db][4 * jj + ii] * S.scale);
+      *reinterpret_cast<u32x2*>(op + 32 * db + 8 * jj + 4 * hl) = __builtin_bit_cast(u32x2, v4);
+    }
+}
+
+// ------------------------------------------------------------ dK, dV
+constexpr int kKVThreads = 256;
+constexpr int kKVWaves = kKVThreads / 64;
+constexpr int kKVListCap = kKVThreads;   // attending blocks listed per pass
+constexpr int kDiagBit = 1 << 30;        // list entry flag: the block lies in the chunk
+
+template <int D>
+struct BwdKVSmem {
+  uint16_t q[2][kChunk * D];   // 64-row tiles of Q and dO (kv_swizzle), 2 stages;
+  uint16_t g[2][kChunk * D];   // after the loop, the cross-wave reduction buffer
+  float lse[2][kChunk];
+  float dd[2][kChunk];
+  float spare[2][kChunk];      // target of the per-row word loads of waves 2 and 3
+  int lb[kKVListCap];          // attending block, | kDiagBit for the chunk's own blocks
+  unsigned long long lmask[kKVListCap];   // tokens of the chunk in the block's token set
+  int scan[16];
+};
+
+// One workgroup per (KV head h, chunk m holding positions of the call).
+// Waves: token half th = wave & 1 (tokens 32 th .. 32 th + 31 of the chunk,
+// this lane's token is column col), row half rw = wave >> 1 of each 64-row
+// query tile. dK^T and dV^T of the wave's tokens accumulate over the tiles
+// of every attending block; the two row halves are summed at the end.
+template <int D>
+__global__ __launch_bounds__(kKVThreads) void bwd_dkv_kernel(BwdArgs A) {
+  __shared__ BwdKVSmem<D> sm;
+  static_assert(2 * 2 * (D / 32) * 16 * 64 * sizeof(float) <= sizeof(sm.q) + sizeof(sm.g),
+                "the row-half reduction fits in the Q and dO stages");
+  constexpr int NP = D / 8;
+  constexpr int RPI = 64 / NP;
+  constexpr int RPW = kChunk / kKVWaves;   // tile rows each wave loads
+  constexpr int KI = RPW / RPI;
+  constexpr int RB = D * 2;
+  const Shape& S = A.s;
+  const int h = (int)(blockIdx.x / A.nchunks);
+  const int64_t m = A.m0 + blockIdx.x % A.nchunks;
+  const int64_t t0 = m * kChunk;
+  const int64_t lq = S.q0 + S.nq;          // no query of the call attends a token at or past lq
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5, col = lane & 31;
+  const int th = wave & 1, rw = wave >> 1;
+  const int tok = 32 * th + col;
+  const int64_t tpos = t0 + tok;
+
+  // K and V of this lane's token as MFMA B operands (d = 16 ks + 8 hl + e);
+  // zero past lq, where rows may hold anything
+  bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) kf[ks] = vf[ks] = bf16x8{};
+  if (tpos < lq) {
+    const uint16_t* kp = static_cast<const uint16_t*>(A.k) + ((int64_t)h * S.kvs + tpos) * D + 8 * hl;
+    const uint16_t* vp = static_cast<const uint16_t*>(A.v) + ((int64_t)h * S.kvs + tpos) * D + 8 * hl;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      kf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + 16 * ks));
+      vf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vp + 16 * ks));
+    }
+  }
+
+  // LDS offsets. Row reads of a Q or dO tile: lane (col, hl) reads piece
+  // 2 ks + hl of row col (+ 32 rw). Transposing reads: rows vrow and vrow + 8
+  // (+ 32 rw + 16 mm), columns vcol (+ 32 db).
+  uint32_t qoff[D / 16], tlo[D / 32], thi[D / 32];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) qoff[ks] = (uint32_t)(col * RB + (((2 * ks + hl) ^ kv_swizzle<D>(col)) << 4));
+  {
+    const int vj = lane & 15, vg = lane >> 4;
+    const int vcol = 16 * (vg & 1) + 4 * (vj & 3);
+    const int vrow = 4 * hl + (vj >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int c = 32 * db + vcol;
+      tlo[db] = (uint32_t)(vrow * RB + (((c >> 3) ^ kv_swizzle<D>(vrow)) << 4) + ((c & 7) << 1));
+      thi[db] = (uint32_t)((vrow + 8) * RB + (((c >> 3) ^ kv_swizzle<D>(vrow + 8)) << 4) + ((c & 7) << 1));
+    }
+  }
+  const char* sQb = reinterpret_cast<const char*>(&sm.q[0][0]);
+  const char* sGb = reinterpret_cast<const char*>(&sm.g[0][0]);
+  const uint16_t* qg = static_cast<const uint16_t*>(A.q);
+  const uint16_t* gg = static_cast<const uint16_t*>(A.dout);
+  const int nrows = S.G * S.B;
+  const int ntl = (nrows + kChunk - 1) / kChunk;   // 64-row query tiles per attending block
+  const int gpc = kChunk / S.g;
+  const unsigned long long gmask = S.g >= 64 ? ~0ull : ((1ull << S.g) - 1ull);
+  const float sl2 = S.scale * kLog2e;
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) dk[i] = dv[i] = f32x16{};
+
+  // source row (in Q / dO / LSE / D) of row ir of block bq; rows past the
+  // item's read its first row (masked)
+  auto src_row = [&](int bq, int ir) -> int64_t {
+    const int r = ir < nrows ? ir : 0;
+    return (int64_t)(h * S.G + r / S.B) * S.qs + (int64_t)bq * S.B + r % S.B;
+  };
+  auto issue = [&](int u) {
+    const int e = u / ntl, pt = u - e * ntl;
+    const int bq = sm.lb[e] & (kDiagBit - 1);
+    const uint32_t off = (uint32_t)((u & 1) * kChunk * D * 2);
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int row0 = wave * RPW + i * RPI;
+      const int rr = row0 + lane / NP;
+      const int64_t sr = src_row(bq, kChunk * pt + rr);
+      const int pc = ((lane % NP) ^ kv_swizzle<D>(rr)) * 8;
+      lds_dma16(qg + sr * D + pc, lds_addr(&sm.q[0][0]) + off + (uint32_t)(row0 * RB));
+      lds_dma16(gg + sr * D + pc, lds_addr(&sm.g[0][0]) + off + (uint32_t)(row0 * RB));
+    }
+    // one word per row: LSE (wave 0), D (wave 1); waves 2 and 3 load the LSE
+    // again into a spare row so that every wave issues the same loads
+    const int64_t sr = src_row(bq, kChunk * pt + lane);
+    const float* src = wave == 1 ? A.dd + sr : A.lse + sr;
+    float* dst = wave == 0 ? &sm.lse[u & 1][0] : wave == 1 ? &sm.dd[u & 1][0] : &sm.spare[u & 1][0];
+    lds_dma4(src, lds_addr(dst));
+  };
+
+  for (int b0 = 0; b0 < S.nb; b0 += kKVListCap) {
+    // the blocks of [b0, b0 + cap) that attend chunk m, in block order
+    int code = -1;
+    unsigned long long msk = 0ull;
+    const int b = b0 + tid;
+    if (b < S.nb) {
+      const int64_t s = S.q0 + (int64_t)b * S.B, ms = s / kChunk;
+      if (m == ms) {
+        code = b | kDiagBit;
+        msk = ~0ull;
+      } else if (m < ms) {
+        int64_t a, bb;
+        fixed_windows(ms, S.sink_chunks, S.local_chunks, &a, &bb);
+        if (m < a || m >= bb) {
+          code = b;
+          msk = ~0ull;
+        } else {
+          const int64_t it = (int64_t)b * S.hkv + h;
+          const int32_t* u = A.used + it * S.kg;
+          const int n = A.nused[it];
+          const int first = (int)(m * gpc);
+          int lo = 0, hi = n;
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (u[mid] < first) lo = mid + 1; else hi = mid;
+          }
+          for (int i = lo; i < n && u[i] < first + gpc; ++i) msk |= gmask << ((u[i] - first) * S.g);
+          if (msk) code = b;
+        }
+      }
+    }
+    int tot;
+    const int pos = block_scan<false>(code >= 0 ? 1 : 0, sm.scan, &tot);
+    if (code >= 0) {
+      sm.lb[pos] = code;
+      sm.lmask[pos] = msk;
+    }
+    __syncthreads();
+    const int T = tot * ntl;
+    if (T > 0) issue(0);
+    for (int u = 0; u < T; ++u) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __syncthreads();   // tile u landed everywhere; the stage of tile u - 1 is free
+      if (u + 1 < T) issue(u + 1);
+      const int e = u / ntl, pt = u - e * ntl;
+      const int code_e = sm.lb[e];
+      const bool diag = (code_e & kDiagBit) != 0;
+      const int64_t sq = S.q0 + (int64_t)(code_e & (kDiagBit - 1)) * S.B;
+      const bool tok_ok = ((sm.lmask[e] >> tok) & 1ull) && tpos < lq;
+      const uint32_t stage = (uint32_t)((u & 1) * kChunk * RB);
+      const char* qt = sQb + stage + 32 * rw * RB;
+      const char* gt = sGb + stage + 32 * rw * RB;
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qt + qoff[ks]));
+        const bf16x8 c = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(gt + qoff[ks]));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ks], sacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c, vf[ks], pacc, 0, 0, 0);
+      }
+      // accumulator r of this lane: tile row 32 rw + 8 (r >> 2) + 4 hl + (r & 3)
+      float lr[16], dr[16];
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const float4 l4 = *reinterpret_cast<const float4*>(&sm.lse[u & 1][32 * rw + 8 * a4 + 4 * hl]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&sm.dd[u & 1][32 * rw + 8 * a4 + 4 * hl]);
+        lr[4 * a4] = l4.x; lr[4 * a4 + 1] = l4.y; lr[4 * a4 + 2] = l4.z; lr[4 * a4 + 3] = l4.w;
+        dr[4 * a4] = d4.x; dr[4 * a4 + 1] = d4.y; dr[4 * a4 + 2] = d4.z; dr[4 * a4 + 3] = d4.w;
+      }
+      bf16x8 pf[2], sf[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ir = kChunk * pt + 32 * rw + 8 * (r >> 2) + 4 * hl + (r & 3);
+        const bool vis = tok_ok && ir < nrows && (!diag || tpos <= sq + (ir & (S.B - 1)));
+        const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[r], sl2, -lr[r] * kLog2e)) : 0.0f;
+        const float ds = vis ? p * (pacc[r] - dr[r]) : 0.0f;
+        pf[r >> 3][r & 7] = (__bf16)p;
+        sf[r >> 3][r & 7] = (__bf16)ds;
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS: A operands of lane (half hl,
+      // column kd) hold dO / Q at tile rows 32 rw + 16 mm + 4 hl + {0..3, 8..11}
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          const char* gb = gt + 16 * mm * RB;
+          const char* qb = qt + 16 * mm * RB;
+          const s16x4 glo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(gb + tlo[db]));
+          const s16x4 ghi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(gb + thi[db]));
+          const s16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(qb + tlo[db]));
+          const s16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(qb + thi[db]));
+          const s16x8 wg = {glo[0], glo[1], glo[2], glo[3], ghi[0], ghi[1], ghi[2], ghi[3]};
+          const s16x8 wq = {qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wg), pf[mm], dv[db], 0, 0, 0);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wq), sf[mm], dk[db], 0, 0, 0);
+        }
+    }
+    __syncthreads();   // the list and the stages are reused by the next pass
+  }
+
+  // sum the two row halves (row half 1 through LDS), then write the keys of
+  // the call's positions: rows tpos - q0 of dk / dv
+  float* red = reinterpret_cast<float*>(&sm.q[0][0]);   // [th][dk, dv][D/32][16][64 lanes]
+  auto slot = [&](int which, int db, int i) { return (((th * 2 + which) * (D / 32) + db) * 16 + i) * 64 + lane; };
+  if (rw == 1) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        red[slot(0, db, i)] = dk[db][i];
+        red[slot(1, db, i)] = dv[db][i];
+      }
+  }
+  __syncthreads();
+  if (rw == 1 || tpos < S.q0 || tpos >= lq) return;
+  uint16_t* kout = static_cast<uint16_t*>(A.dk) + ((int64_t)h * S.nq + (tpos - S.q0)) * D;
+  uint16_t* vout = static_cast<uint16_t*>(A.dv) + ((int64_t)h * S.nq + (tpos - S.q0)) * D;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      bf16x4 k4, v4;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int i = 4 * jj + ii;
+        k4[ii] = (__bf16)((dk[db][i] + red[slot(0, db, i)]) * S.scale);
+        v4[ii] = (__bf16)(dv[db][i] + red[slot(1, db, i)]);
+      }
+      *reinterpret_cast<u32x2*>(kout + 32 * db + 8 * jj + 4 * hl) = __builtin_bit_cast(u32x2, k4);
+      *reinterpret_cast<u32x2*>(vout + 32 * db + 8 * jj + 4 * hl) = __builtin_bit_cast(u32x2, v4);
+    }
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(const Shape& s) {
+  auto a256 = [](size_t n) { return (n + 255) & ~(size_t)255; };
+  return a256(4 * (size_t)s.hq * s.nq) + a256(4 * (size_t)s.nb * s.hkv * s.kg) + a256(4 * (size_t)s.nb * s.hkv);
+}
+
+hipError_t launch_attend_backward(const Shape& s, const void* q, const void* k, const void* v,
+                                  const int32_t* group_idx, const int32_t* n_sel, const void* out,
+                                  const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                  void* workspace, hipStream_t st) {
+  if (s.nq == 0) return hipSuccess;
+  auto a256 = [](size_t n) { return (n + 255) & ~(size_t)255; };
+  BwdArgs A{};
+  A.q = q; A.k = k; A.v = v; A.out = out; A.lse = lse; A.dout = dout; A.gidx = group_idx; A.nsel = n_sel;
+  A.dq = dq; A.dk = dk; A.dv = dv; A.s = s;
+  char* ws = static_cast<char*>(workspace);
+  A.dd = reinterpret_cast<float*>(ws);
+  A.used = reinterpret_cast<int32_t*>(ws + a256(4 * (size_t)s.hq * s.nq));
+  A.nused = reinterpret_cast<int32_t*>(ws + a256(4 * (size_t)s.hq * s.nq) + a256(4 * (size_t)s.nb * s.hkv * s.kg));
+  const int waves = (s.G * s.B + 31) / 32;
+  A.wg_per_item = (waves + kAttnWaves - 1) / kAttnWaves;
+  A.m0 = s.q0 / kChunk;
+  A.nchunks = (int)((s.q0 + s.nq - 1) / kChunk - A.m0 + 1);
+  const int64_t items = s.nb * s.hkv;
+  bwd_prep_kernel<<<dim3((unsigned)items), dim3(256), 0, st>>>(A);
+  const dim3 gq((unsigned)(items * A.wg_per_item)), gkv((unsigned)(s.hkv * A.nchunks));
+  if (s.d == 128) {
+    bwd_dq_kernel<128><<<gq, dim3(kAttnThreads), 0, st>>>(A);
+    bwd_dkv_kernel<128><<<gkv, dim3(kKVThreads), 0, st>>>(A);
+  } else if (s.d == 64) {
+    bwd_dq_kernel<64><<<gq, dim3(kAttnThreads), 0, st>>>(A);
+    bwd_dkv_kernel<64><<<gkv, dim3(kKVThreads), 0, st>>>(A);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hga

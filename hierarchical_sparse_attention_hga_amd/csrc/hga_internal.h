@@ -81,4 +81,12 @@ hipError_t launch_route_attend(const Shape& s, const void* q, const float* cs, c
                                const float* gs_dev, int64_t gs_split, const KVSrc& kv, int32_t* chunk_idx,
                                int32_t* group_idx, int32_t* n_sel, void* out, float* lse, hipStream_t st);
 
+// Backward of the attention (bfloat16, K/V on the device): workspace bytes,
+// and the launch of its three kernels.
+size_t backward_workspace_bytes(const Shape& s);
+hipError_t launch_attend_backward(const Shape& s, const void* q, const void* k, const void* v,
+                                  const int32_t* group_idx, const int32_t* n_sel, const void* out,
+                                  const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                  void* workspace, hipStream_t st);
+
 }  // namespace hga

@@ -100,7 +100,7 @@ typedef struct {
   int64_t split;
 } hga_tiered;
 
-enum { HGA_WS_ROUTE = 0, HGA_WS_ATTEND = 1, HGA_WS_ATTEND_TIERED = 2 };
+enum { HGA_WS_ROUTE = 0, HGA_WS_ATTEND = 1, HGA_WS_ATTEND_TIERED = 2, HGA_WS_BACKWARD = 3 };
 
 /* Bytes of device workspace that hga_route (which = HGA_WS_ROUTE) or
  * hga_attend / hga_route_attend (HGA_WS_ATTEND with everything on the device,
@@ -108,8 +108,9 @@ enum { HGA_WS_ROUTE = 0, HGA_WS_ATTEND = 1, HGA_WS_ATTEND_TIERED = 2 };
  * The tiered figure holds for every split <= seq_len - n_q: it covers chunk
  * flags and slots and an HBM cache as large as the whole host part of K and V
  * (the attention copies each history chunk any query block needs into it once
- * per call). Returns 0 when no workspace is needed, and (size_t)-1 when the
- * config or sizes are invalid. */
+ * per call). HGA_WS_BACKWARD is the workspace of hga_attend_backward.
+ * Returns 0 when no workspace is needed, and (size_t)-1 when the config or
+ * sizes are invalid. */
 size_t hga_workspace_size(const hga_config* cfg, int64_t seq_len, int64_t n_q, int32_t which);
 
 /* Key summaries (section 2.1, first paragraph).
@@ -229,6 +230,31 @@ hga_status hga_stream_forward(const hga_config* cfg, const void* q, const void* 
                               int64_t seq_len, int64_t segment, float* chunk_sum, float* group_sum,
                               int32_t* chunk_idx, int32_t* group_idx, int32_t* n_sel,
                               void* out, float* lse, void* stream);
+
+/* Backward of the exact-token attention (section 2.1: the routing is not
+ * differentiated, the gather and the attention are; section 2.2: only the
+ * active segment is differentiable, the history's K and V are detached).
+ * With the token sets of hga_attend fixed by group_idx / n_sel, it returns
+ * the gradients of a loss whose gradient with respect to `out` is `dout`:
+ *   dq         for every query row of the call;
+ *   dk, dv     for the keys and values at the call's own positions
+ *              q_start .. q_start + n_q - 1 (the segment): the sums of the
+ *              contributions of every query of the call that attends them.
+ *              Keys before q_start (the history) receive no gradient.
+ * Arguments:
+ *   q, k, v, group_idx, n_sel   as hga_attend took them; k and v are device
+ *              pointers ([Hkv][seq_len][d], no host tier).
+ *   out, lse   device, the forward's outputs for these queries (lse required).
+ *   dout, dq   device, [Hq][n_q][d] of cfg->dtype.
+ *   dk, dv     device, [Hkv][n_q][d] of cfg->dtype: row i is position q_start + i.
+ *   workspace  device, at least hga_workspace_size(..., HGA_WS_BACKWARD) bytes.
+ * Only bfloat16 is built (HGA_ERR_UNSUPPORTED for float32). The gradient of
+ * each key is summed in one workgroup in a fixed order: repeated calls give
+ * identical bits. */
+hga_status hga_attend_backward(const hga_config* cfg, const void* q, int64_t q_start, int64_t n_q,
+                               int64_t seq_len, const void* k, const void* v, const int32_t* group_idx,
+                               const int32_t* n_sel, const void* out, const float* lse, const void* dout,
+                               void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* hga_status_string(hga_status status);

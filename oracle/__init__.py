@@ -55,7 +55,7 @@ def _load():
         lib.orc_abs_summaries.argtypes = [C.POINTER(_Cfg), P, P, P]
         lib.orc_route.argtypes = [C.POINTER(_Cfg), P, P, P, P, P, C.c_int, P, P, P, P, P]
         lib.orc_attend.argtypes = [C.POINTER(_Cfg), P, P, P, C.c_int, P, P, P, P, P]
-        lib.orc_attend_backward.argtypes = [C.POINTER(_Cfg), P, P, P, P, P, P, P, P, P]
+        lib.orc_attend_backward.argtypes = [C.POINTER(_Cfg), P, P, P, P, P, P, P, P, P, P, P, P]
         lib.orc_token_set.argtypes = [C.POINTER(_Cfg), C.c_int, P, C.c_int, P, C.c_int64]
         lib.orc_token_set.restype = C.c_int64
         assert lib.orc_diag_width() == 8
@@ -65,7 +65,7 @@ def _load():
 
 
 def _ptr(a):
-    return a.ctypes.data_as(C.c_void_p)
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
 
 
 def make_cfg(cfg: dict) -> _Cfg:
@@ -148,12 +148,14 @@ def attend(cfg, q64, k64, v64, items, group_idx, n_groups):
     return out, lse
 
 
-def attend_backward(cfg, q64, k64, v64, dout64, group_idx, n_groups):
+def attend_backward(cfg, q64, k64, v64, dout64, group_idx, n_groups, with_abs=False):
     """Backward of step 7 with the routing fixed, over every (block, KV head).
 
     group_idx [nb][hkv][kg], n_groups [nb][hkv]; dout [Hq][n_q][d]. Returns dq
     [Hq][n_q][d] and dk, dv [Hkv][L][d] (float64; every key row, zero where no
-    query attends it).
+    query attends it); with ``with_abs`` also their magnitude companions
+    (dq_abs, dk_abs, dv_abs: the same sums over term magnitudes, see
+    orc_attend_backward), for error bounds.
     """
     lib = _load()
     nb, hkv, kg = cfg["n_q"] // cfg["q_block"], cfg["hkv"], cfg["top_groups"]
@@ -163,9 +165,10 @@ def attend_backward(cfg, q64, k64, v64, dout64, group_idx, n_groups):
     dq = np.empty_like(q64)
     dk = np.empty_like(k64)
     dv = np.empty_like(v64)
+    ab = (np.empty_like(q64), np.empty_like(k64), np.empty_like(v64)) if with_abs else (None, None, None)
     lib.orc_attend_backward(C.byref(make_cfg(cfg)), _ptr(q64), _ptr(k64), _ptr(v64), _ptr(dout64),
-                            _ptr(gi), _ptr(ng), _ptr(dq), _ptr(dk), _ptr(dv))
-    return dq, dk, dv
+                            _ptr(gi), _ptr(ng), _ptr(dq), _ptr(dk), _ptr(dv), *(_ptr(a) for a in ab))
+    return (dq, dk, dv, *ab) if with_abs else (dq, dk, dv)
 
 
 def token_set(cfg, b, group_idx, n_groups):

@@ -350,10 +350,18 @@ int orc_attend(const orc_cfg* c, const double* q, const double* k, const double*
  *   dk_t += scale dS_t q,   dv_t += P_t g.
  * Keys and values collect the contributions of every row of every block that
  * attends them. Items of different KV heads touch disjoint rows, so heads run
- * in parallel and the blocks of one head in order. */
+ * in parallel and the blocks of one head in order.
+ *
+ * For tolerances the same sums are also taken over magnitudes (when the abs
+ * arrays are given), with |dS_t| replaced by P_t (|dP_t| + |D| + W), where
+ * W = sum_e |g_e| |o_e| over the exact output o:
+ *   dq_abs = scale sum_t P_t (|dP_t| + |D| + W) |k_t|,
+ *   dk_abs_t += scale P_t (|dP_t| + |D| + W) |q|,   dv_abs_t += P_t |g|.
+ * A relative perturbation e of each dS_t term, of D by e W, or of each P_t
+ * moves a gradient element by at most e times its companion. */
 static void backward_item(const orc_cfg* c, const double* q, const double* k, const double* v,
                           const double* dout, int b, int h, const int32_t* group_idx, int n_groups,
-                          double* dq, double* dk, double* dv) {
+                          double* dq, double* dk, double* dv, double* dq_abs, double* dk_abs, double* dv_abs) {
   const int64_t L = c->seq_len, d = c->d, q0 = q_start(c);
   const int G = c->hq / c->hkv, B = c->q_block;
   const int64_t s = q0 + (int64_t)b * B;
@@ -382,8 +390,17 @@ static void backward_item(const orc_cfg* c, const double* q, const double* k, co
       for (int64_t a = 0; a < nv; ++a) den += exp(z[a] - mx);
       double D = 0.0;
       for (int64_t a = 0; a < nv; ++a) D += exp(z[a] - mx) / den * dp[a];
+      double W = 0.0;   /* sum_e |g_e| |o_e| */
+      if (dq_abs)
+        for (int64_t e = 0; e < d; ++e) {
+          double o = 0.0;
+          for (int64_t a = 0; a < nv; ++a) o += exp(z[a] - mx) / den * v[((int64_t)h * L + T[a]) * d + e];
+          W += fabs(gi[e]) * fabs(o);
+        }
       double* dqi = dq + row * d;
       for (int64_t e = 0; e < d; ++e) dqi[e] = 0.0;
+      if (dq_abs)
+        for (int64_t e = 0; e < d; ++e) dq_abs[row * d + e] = 0.0;
       for (int64_t a = 0; a < nv; ++a) {
         const double P = exp(z[a] - mx) / den;
         const double dS = P * (dp[a] - D);
@@ -395,6 +412,15 @@ static void backward_item(const orc_cfg* c, const double* q, const double* k, co
           dkt[e] += c->scale * dS * qi[e];
           dvt[e] += P * gi[e];
         }
+        if (dq_abs) {
+          const double m = P * (fabs(dp[a]) + fabs(D) + W);
+          const int64_t kr = ((int64_t)h * L + T[a]) * d;
+          for (int64_t e = 0; e < d; ++e) {
+            dq_abs[row * d + e] += c->scale * m * fabs(kt[e]);
+            dk_abs[kr + e] += c->scale * m * fabs(qi[e]);
+            dv_abs[kr + e] += P * fabs(gi[e]);
+          }
+        }
       }
     }
   free(dp); free(z); free(T);
@@ -402,18 +428,23 @@ static void backward_item(const orc_cfg* c, const double* q, const double* k, co
 
 /* dq [Hq][n_q][d]; dk, dv [Hkv][L][d] (every key row, zero where no query
  * attends it). group_idx [nb][Hkv][kg] and n_groups [nb][Hkv] as the forward
- * takes them. */
+ * takes them. dq_abs, dk_abs, dv_abs (same shapes) may all be NULL. */
 int orc_attend_backward(const orc_cfg* c, const double* q, const double* k, const double* v,
                         const double* dout, const int32_t* group_idx, const int32_t* n_groups,
-                        double* dq, double* dk, double* dv) {
+                        double* dq, double* dk, double* dv, double* dq_abs, double* dk_abs, double* dv_abs) {
   const int64_t nb = c->n_q / c->q_block;
-  memset(dk, 0, sizeof(double) * (size_t)(c->hkv * c->seq_len * c->d));
-  memset(dv, 0, sizeof(double) * (size_t)(c->hkv * c->seq_len * c->d));
+  const size_t kv_bytes = sizeof(double) * (size_t)(c->hkv * c->seq_len * c->d);
+  memset(dk, 0, kv_bytes);
+  memset(dv, 0, kv_bytes);
+  if (dq_abs) {
+    memset(dk_abs, 0, kv_bytes);
+    memset(dv_abs, 0, kv_bytes);
+  }
 #pragma omp parallel for schedule(dynamic, 1)
   for (int h = 0; h < c->hkv; ++h)
     for (int64_t b = 0; b < nb; ++b)
       backward_item(c, q, k, v, dout, (int)b, h, group_idx + (b * c->hkv + h) * c->top_groups,
-                    n_groups[b * c->hkv + h], dq, dk, dv);
+                    n_groups[b * c->hkv + h], dq, dk, dv, dq_abs, dk_abs, dv_abs);
   return 0;
 }
 

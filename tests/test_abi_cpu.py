@@ -31,7 +31,7 @@ def test_every_declared_entry_point_is_exported(lib):
     assert declared == set(B.EXPORTS)
     for name in declared:
         assert hasattr(lib, name)
-    assert hga.hga_version() == 102
+    assert hga.hga_version() == 103
 
 
 def test_status_strings(lib):
@@ -180,3 +180,25 @@ def test_empty_query_range_is_a_no_op():
     hga.hga_route_attend(c, FAKE, 16384, 0, 16384, *[FAKE] * 8)
     hga.hga_build_summaries(c, None, 0, None, None)
     assert hga.hga_last_error() == ""
+
+
+def test_backward_validation():
+    c = cfg()
+    E = hga.HGA_ERR_INVALID_ARGUMENT
+    geo = (14336, 2048, 16384)
+    # workspace: D per query row, the usable kept groups and their counts
+    nb = 2048 // 64
+    need = (4 * 32 * 2048 + 255) // 256 * 256 + (4 * nb * 8 * 64 + 255) // 256 * 256 + (4 * nb * 8 + 255) // 256 * 256
+    assert hga.hga_workspace_size(c, 16384, 2048, hga.HGA_WS_BACKWARD) == need
+    args = [FAKE] * 11   # k, v, group_idx, n_sel, out, lse, dout, dq, dk, dv, workspace
+    def call(cc, a, ws_bytes=need, g=geo):
+        return _status(hga.hga_attend_backward, cc, FAKE, *g, *a[:10], a[10], ws_bytes)
+    assert call(cfg(dtype="f32", head_dim=64), args) == hga.HGA_ERR_UNSUPPORTED
+    for i in range(10):
+        a = list(args)
+        a[i] = None
+        assert call(c, a) == E
+    assert call(c, args[:10] + [None]) == hga.HGA_ERR_WORKSPACE
+    assert call(c, args, need - 1) == hga.HGA_ERR_WORKSPACE
+    assert call(c, args, need, (14300, 2048, 16384)) == hga.HGA_ERR_UNSUPPORTED
+    hga.hga_attend_backward(c, None, 16384, 0, 16384, *[None] * 11, 0)   # no queries: a no-op

@@ -1,0 +1,154 @@
+"""Backward of the exact-token attention on the GPU against the oracle
+("Long-Context Fine-Tuning with Limited VRAM", section 2.1: routing is not
+differentiated; section 2.2: only the active segment's keys and values take
+gradients, the history is detached).
+
+Each case runs the GPU forward (hga_route_attend) for its kept groups, output
+and LSE, draws a seeded output gradient, runs hga_attend_backward, and compares
+dQ (every query row) and dK, dV (the call's own positions) with the float64
+oracle on the same bf16 inputs and the same kept groups.
+
+Tolerance (bf16 gradients), derived from the arithmetic: the kernels round P
+and dS to bfloat16 as MFMA operands (relative 2^-9 each), take D = dO . O from
+the forward's bfloat16 output (O off by 2^-9 relative, its weights by 2^-9
+more), and store the gradients in bfloat16. Each gradient element is a sum of
+terms whose magnitudes the oracle also sums (its companions: dS_t taken as
+P_t (|dP_t| + |D| + W), W = sum |dO| |O|), and every one of these roundings
+moves each term by at most 2^-8 of its companion term. The bar: beyond each
+value's own storage rounding (half a bf16 spacing), every element's error is
+at most 2^-6 of its companion (four times the first-order bound), and the
+mean error at most 2^-9 of the mean companion. A second bar, on the mean
+error beyond storage rounding (at most 2e-3 of the gradient's RMS; observed up
+to 1.2e-3 at head_dim 64 and 3e-4 to 9e-4 at 128), catches a systematic error
+spread thinly over many elements.
+"""
+import numpy as np
+import pytest
+import torch
+
+import hierarchical_sparse_attention_hga_amd as hga
+import oracle
+import synth
+from harness import DEV, bf16_half_spacing, hga_cfg, inputs, to_dev
+from test_gpu_edges import small
+
+pytestmark = pytest.mark.gpu
+
+MAX_REL, MEAN_REL, MEAN_RMS = 2.0 ** -6, 2.0 ** -9, 2e-3
+
+
+def gpu_forward_backward(cfg, x, dout_bits, q_start=None, seq_len=None):
+    c = hga_cfg(cfg)
+    L = cfg["L"] if seq_len is None else seq_len
+    nq, hkv, d, g, B = cfg["n_q"], cfg["hkv"], cfg["d"], cfg["group"], cfg["q_block"]
+    q0 = L - nq if q_start is None else q_start
+    nb = nq // B
+    q, k, v = to_dev(x["q"], "bf16"), to_dev(x["k"], "bf16"), to_dev(x["v"], "bf16")
+    gs = torch.empty(hkv, L // g, d, device=DEV)
+    cs = torch.empty(hkv, L // 64, d, device=DEV)
+    ci = torch.empty(nb, hkv, max(cfg["top_chunks"], 1), dtype=torch.int32, device=DEV)
+    gi = torch.full((nb, hkv, max(cfg["top_groups"], 1)), -1, dtype=torch.int32, device=DEV)
+    ns = torch.empty(nb, hkv, 2, dtype=torch.int32, device=DEV)
+    out = torch.empty_like(q)
+    lse = torch.empty(cfg["hq"], nq, device=DEV)
+    hga.hga_build_summaries(c, k, L, gs, cs)
+    hga.hga_route_attend(c, q, q0, nq, L, cs, gs, k, v, ci, gi, ns, out, lse)
+    dout = to_dev(dout_bits, "bf16")
+    dq = torch.empty_like(q)
+    dk = torch.empty(hkv, nq, d, dtype=torch.bfloat16, device=DEV)
+    dv = torch.empty_like(dk)
+    wsb = hga.hga_workspace_size(c, L, nq, hga.HGA_WS_BACKWARD)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    hga.hga_attend_backward(c, q, q0, nq, L, k, v, gi, ns, out, lse, dout, dq, dk, dv, ws, wsb)
+    torch.cuda.synchronize()
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)
+    return dict(gi=gi.cpu().numpy(), ns=ns.cpu().numpy(), dq=f(dq), dk=f(dk), dv=f(dv),
+                raw=(dq.view(torch.int16).cpu().numpy(), dk.view(torch.int16).cpu().numpy(),
+                     dv.view(torch.int16).cpu().numpy()))
+
+
+def seeded_dout(cfg, seed=7):
+    rng = np.random.default_rng([synth.SEED, 90, seed])
+    return synth.f32_to_bf16_bits(rng.standard_normal((cfg["hq"], cfg["n_q"], cfg["d"])).astype(np.float32))
+
+
+def check_grads(cfg, x, gpu, dout_bits, q_start=None):
+    L, nq = cfg["L"], cfg["n_q"]
+    q0 = L - nq if q_start is None else q_start
+    sub = dict(cfg, L=q0 + nq)   # the oracle's sequence ends at the last query
+    f = {n: synth.to_f64(x[n], "bf16") for n in ("q", "k", "v")}
+    k64, v64 = f["k"][:, :q0 + nq], f["v"][:, :q0 + nq]
+    kg = max(cfg["top_groups"], 1)
+    dq, dk, dv, qa, ka, va = oracle.attend_backward(
+        sub, f["q"], k64, v64, synth.to_f64(dout_bits, "bf16"),
+        gpu["gi"][..., :kg] if cfg["top_groups"] else gpu["gi"][..., :0], gpu["ns"][..., 1], with_abs=True)
+    sl = slice(q0, q0 + nq)
+    res = {}
+    for name, got, ref, comp in (("dq", gpu["dq"], dq, qa), ("dk", gpu["dk"], dk[:, sl], ka[:, sl]),
+                                 ("dv", gpu["dv"], dv[:, sl], va[:, sl])):
+        assert np.isfinite(got).all(), name
+        err = np.maximum(np.abs(got - ref) - bf16_half_spacing(got), 0.0)
+        worst = float((err / np.maximum(comp, 1e-30)).max())
+        mean = float(err.mean() / comp.mean())
+        rms = float(np.sqrt(np.mean(ref ** 2)))
+        res[name] = (worst, mean, float(err.mean()) / rms, rms)
+        assert worst <= MAX_REL, f"{name}: an element's error is {worst:.3g} of its companion"
+        assert mean <= MEAN_REL, f"{name}: mean error {mean:.3g} of the mean companion"
+        assert err.mean() <= MEAN_RMS * rms, f"{name}: mean error {err.mean() / rms:.3g} of the RMS"
+    print("  " + "  ".join(f"{n}: worst={v[0]:.2e} mean={v[1]:.2e} mean/rms={v[2]:.2e} rms={v[3]:.3g}"
+                           for n, v in res.items()), flush=True)
+    return res
+
+
+CASES = {
+    "block64": dict(),
+    "block16_ragged_start": dict(q_block=16, n_q=496),
+    "block1": dict(q_block=1, n_q=40, L=1000 + 24),
+    "gqa8": dict(hq=16, hkv=2),
+    "no_budget": dict(top_chunks=0, top_groups=0),
+    "d64": dict(d=64),
+    "group4": dict(group=4, top_groups=20),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_backward_small(name):
+    cfg = small(**CASES[name])
+    print(f"[backward] {name}", flush=True)
+    x = synth.make_inputs(cfg)
+    dout = seeded_dout(cfg)
+    gpu = gpu_forward_backward(cfg, x, dout)
+    check_grads(cfg, x, gpu, dout)
+
+
+def test_backward_whole_sequence_4k():
+    """Workload qwen3-8b-4k with every position querying (nothing detached:
+    every key takes gradient, the sink chunk from every block)."""
+    cfg, x, _ = inputs(1)
+    print("[backward] qwen3-8b-4k", flush=True)
+    dout = seeded_dout(cfg)
+    check_grads(cfg, x, gpu_forward_backward(cfg, x, dout), dout)
+
+
+@pytest.mark.parametrize("cfg_id,n_q", [(2, 512), (3, 256)])
+def test_backward_segment_end(cfg_id, n_q):
+    """The last n_q positions of the 16K segment and 64K workloads as the
+    active segment (G = 4 and G = 8; 64 and 256 kept groups); the history
+    before it is detached."""
+    full, x, _ = inputs(cfg_id)
+    cfg = dict(full, n_q=n_q, tier_split=0)
+    q0f = full["L"] - full["n_q"]
+    xs = {"q": x["q"][:, full["L"] - n_q - q0f:], "k": x["k"], "v": x["v"]}
+    print(f"[backward] {cfg['name']} n_q={n_q}", flush=True)
+    dout = seeded_dout(cfg)
+    check_grads(cfg, xs, gpu_forward_backward(cfg, xs, dout), dout)
+
+
+def test_backward_is_deterministic():
+    cfg = small(L=2048, n_q=1024)
+    x = synth.make_inputs(cfg)
+    dout = seeded_dout(cfg)
+    a = gpu_forward_backward(cfg, x, dout)
+    b = gpu_forward_backward(cfg, x, dout)
+    for ra, rb in zip(a["raw"], b["raw"]):
+        assert np.array_equal(ra, rb)

@@ -424,6 +424,12 @@ def test_backward_matches_finite_differences(q_block, n_q):
             num[idx] = ((fp - fm) * dout).sum() / (2 * eps)
         np.testing.assert_allclose(g, num, rtol=0, atol=1e-7, err_msg=name)
     assert np.abs(dk[:, :16]).max() > 0   # the sink chunk (history) receives gradient
+    # the magnitude companions bound the gradients (triangle inequality) and
+    # leave the gradients themselves unchanged
+    ab = oracle.attend_backward(cfg, q, k, v, dout, gi, ng, with_abs=True)
+    for g, g2, a in zip((dq, dk, dv), ab[:3], ab[3:]):
+        np.testing.assert_array_equal(g, g2)
+        assert (a >= np.abs(g) - 1e-15).all() and a.max() > 0
 
 
 def _dense_backward(cfg, q, k, v, dout):
