@@ -16,7 +16,9 @@ The same line also reports the 65,536-token Qwen3-30B-A3B-shaped layer with
 its history in HBM and, separately, with its history in pinned host memory
 (that rate includes the PCIe transfer of the routed set).
 
-It also reports one-token decoding (query block of one token, routing over
+It also reports the backward of the attention over the 16K workload's
+2,048-query active segment (hga_attend_backward: dQ, and dK, dV of the
+segment's keys; the history is detached) against bf16 MFMA peak, and one-token decoding (query block of one token, routing over
 the resident summaries of the closed chunks, then attention) at the end of the
 16K and 64K sequences for batches of sequences, as generated tokens per
 second with the fused kernel's HBM roofline.
@@ -56,6 +58,7 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload index (default: the 16K segment)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the 64K lines")
+    ap.add_argument("--backward", action="store_true", help="only the backward line of --config")
     ap.add_argument("--decode-batch", type=int, default=0, metavar="B",
                     help="only the one-token decoding line of --config for a batch of B sequences")
     ap.add_argument("--host-tier", action="store_true",
@@ -450,6 +453,81 @@ def decode_line(cfg_id, batch, steps, warmup):
                          "traffic": None, "algorithmic_bytes": byts}}
 
 
+def backward_flops(cfg, n_sel, group_idx):
+    """Algorithmic flops of one backward call: S and dP once over every
+    attended (query, key) pair, dQ over every pair, and dK, dV over the pairs
+    whose key lies in the call's own positions (history keys are detached):
+    2 d flops per pair and product, so 6 d per pair plus 4 d per segment pair."""
+    d, G, hkv, g = cfg["d"], cfg["hq"] // cfg["hkv"], cfg["hkv"], cfg["group"]
+    nb = cfg["n_q"] // 64
+    q0 = cfg["L"] - cfg["n_q"]
+    ns = n_sel.reshape(nb, hkv, 2)
+    gi = group_idx.reshape(nb, hkv, -1)
+    pairs = pairs_seg = 0
+    for b in range(nb):
+        s = q0 + 64 * b
+        ms = s // 64
+        a = min(cfg["sink"] // 64, ms)
+        bb = max(ms - cfg["local"] // 64, a)
+        fixed = list(range(a)) + list(range(bb, ms))
+        diag = 64 * 65 // 2
+        for h in range(hkv):
+            kept = gi[b, h, :int(ns[b, h, 1])]
+            pairs += G * (64 * (64 * len(fixed) + g * len(kept)) + diag)
+            seg_fixed = sum(1 for m in fixed if 64 * m >= q0)
+            seg_kept = int((kept * g >= q0).sum())
+            pairs_seg += G * (64 * (64 * seg_fixed + g * seg_kept) + diag)
+    return 2.0 * d * (3 * pairs + 2 * pairs_seg)
+
+
+def backward_line(cfg_id, steps, warmup):
+    """hga_attend_backward over the active segment of workload cfg_id (its n_q
+    queries; keys before q_start are detached history), after one forward
+    that provides the kept groups, output and LSE; timed with HIP events on
+    the launch stream around every other call."""
+    import torch
+
+    hga = __import__("hierarchical_sparse_attention_hga_amd")
+    w = Workload(cfg_id)
+    w.step()
+    torch.cuda.synchronize()
+    cfg = w.cfg
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(1337)
+    dout = torch.randn(w.q.shape, generator=gen, device="cuda:0").to(torch.bfloat16)
+    dq = torch.empty_like(w.q)
+    dk = torch.empty(cfg["hkv"], w.nq, cfg["d"], dtype=torch.bfloat16, device="cuda:0")
+    dv = torch.empty_like(dk)
+    wsb = hga.hga_workspace_size(w.c, w.L, w.nq, hga.HGA_WS_BACKWARD)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda:0")
+
+    def one():
+        hga.hga_attend_backward(w.c, w.q, w.q0, w.nq, w.L, w.k_full, w.v_t, w.gi, w.ns, w.out, w.lse, dout,
+                                dq, dk, dv, ws, wsb)
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if i % 2 == 0:
+            evs[i][0].record()
+        one()
+        if i % 2 == 0:
+            evs[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us = float(np.mean([evs[i][0].elapsed_time(evs[i][1]) * 1e3 for i in range(0, steps, 2)]))
+    flops = backward_flops(cfg, w.ns.cpu().numpy(), w.gi.cpu().numpy())
+    w.free()
+    return {"value": steps * cfg["n_q"] / wall, "unit": "query-tokens/s", "call_us_mean": us,
+            "ms_per_step": wall / steps * 1e3,
+            "config": {"workload": f"{cfg['name']}-backward", "n_q": cfg["n_q"], "history": w.q0},
+            "roofline": {"kernel": "hga_attend_backward (bwd_dq_kernel, then bwd_dkv_kernel)", "bound": "mfma",
+                         "achieved": flops / (us * 1e-6) / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                         "frac": flops / (us * 1e-6) / PEAK_BF16, "traffic": None, "algorithmic_flops": flops}}
+
+
 def measure(cfg_id, steps, warmup, split=0, fused=None):
     w = Workload(cfg_id, split, fused)
     wall, stage = w.run(steps, warmup)
@@ -468,6 +546,9 @@ def main():
     torch.cuda.init()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.backward:
+        print(json.dumps(backward_line(args.config, args.steps, args.warmup)), flush=True)
         return
     if args.decode_batch:
         print(json.dumps(decode_line(args.config, args.decode_batch, args.steps, args.warmup)), flush=True)
@@ -523,6 +604,7 @@ def main():
                         "needs crosses the host link once per step into an HBM cache, then attention",
                 "host_link_bytes_per_step": rh.host_bytes,
                 "stages_us_mean": rh.stages("mean")}
+        extra["backward_16k_segment"] = backward_line(2, 40, 5)
         extra["decode_16k_batch64"] = decode_line(2, 64, 40, 5)
         extra["decode_16k_single_sequence"] = decode_line(2, 1, 40, 5)
         extra["decode_64k_batch32"] = decode_line(3, 32, 40, 5)

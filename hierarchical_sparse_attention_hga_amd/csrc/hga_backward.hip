@@ -10,14 +10,14 @@
 // exactly from the forward's log-sum-exp) and output gradient dO:
 //   dP_t = dO . v_t,   D = dO . O,   dS_t = P_t (dP_t - D),
 //   dQ = scale sum_t dS_t k_t,   dK_t = scale sum dS_t q,   dV_t = sum P_t dO.
-// Three kernels run on the call's stream:
-//   bwd_prep_kernel  per item: the usable kept groups (the forward plan's
-//                    validation, so both passes see the forward's token set)
-//                    and D = dO . O of each of its rows, into the workspace;
-//   bwd_dq_kernel    per item, laid out like the forward kernel: the item's
-//                    K/V tiles stream through LDS; S^T = K Q^T, P^T from the
-//                    LSE, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T, all with
-//                    v_mfma_f32_32x32x16_bf16 (K read both row-wise and
+// Two kernels run on the call's stream:
+//   bwd_dq_kernel    per item, laid out like the forward kernel: it validates
+//                    the kept groups as the forward does (so both see the
+//                    same token set), computes D = dO . O of its rows, and
+//                    leaves both in the workspace for the second kernel; the
+//                    item's K/V tiles stream through LDS; S^T = K Q^T, P^T
+//                    from the LSE, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T, all
+//                    with v_mfma_f32_32x32x16_bf16 (K read both row-wise and
 //                    transposed, hence kv_swizzle);
 //   bwd_dkv_kernel   per (KV head, chunk holding positions of the call): the
 //                    chunk's K and V stay in registers as MFMA operands while
@@ -53,39 +53,13 @@ struct BwdArgs {
   Shape s;
 };
 
-__device__ inline float bf16_bits_to_float(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
-
-// ------------------------------------------------------------ preparation
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs A) {
-  __shared__ int sRuns[kMaxRouted];
-  __shared__ int sScan[16];
-  const Shape& S = A.s;
-  const int h = (int)(blockIdx.x / S.nb), b = (int)(blockIdx.x % S.nb);
-  const Plan P = make_plan(S, b, h, A.gidx, A.nsel, sRuns, sScan, kMaxRouted);
-  const int64_t it = (int64_t)b * S.hkv + h;
-  for (int i = threadIdx.x; i < P.nrouted; i += blockDim.x) A.used[it * S.kg + i] = sRuns[i] / S.g;
-  if (threadIdx.x == 0) A.nused[it] = P.nrouted;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nrows = S.G * S.B;
-  const uint16_t* o = static_cast<const uint16_t*>(A.out);
-  const uint16_t* g = static_cast<const uint16_t*>(A.dout);
-  for (int r = wave; r < nrows; r += blockDim.x >> 6) {
-    const int64_t row = (int64_t)(h * S.G + r / S.B) * S.qs + (int64_t)b * S.B + r % S.B;
-    float acc = 0.0f;
-    for (int e = lane; e < S.d; e += 64)
-      acc += bf16_bits_to_float(o[row * S.d + e]) * bf16_bits_to_float(g[row * S.d + e]);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (lane == 0) A.dd[row] = acc;
-  }
-}
-
 // ------------------------------------------------------------ dQ
 template <int D>
 struct BwdQSmem {
   uint16_t k[2][kChunk * D];   // kv_swizzle: read row-wise and transposed
   uint16_t v[2][kChunk * D];   // k_swizzle: read row-wise
   int runs[kMaxRoutedAttn];
+  int scan[16];
 };
 
 // One workgroup slot z of item (b, h): 8 waves of 32 query rows, the item's
@@ -100,15 +74,12 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dq_kernel(BwdArgs A) {
   const Shape& S = A.s;
   int b, h, z;
   item_of_block(S, A.wg_per_item, &b, &h, &z);
-  Plan P;
-  plan_windows(S, b, &P);
-  const int64_t it = (int64_t)b * S.hkv + h;
-  const int nr = A.nused[it];
-  for (int i = threadIdx.x; i < nr; i += kAttnThreads) sm.runs[i] = A.used[it * S.kg + i] * S.g;
-  P.nrouted = nr;
-  P.nrt = (nr + kChunk / S.g - 1) / (kChunk / S.g);
-  P.ntiles = P.nfix + P.nrt + 1;
-  __syncthreads();
+  const Plan P = make_plan(S, b, h, A.gidx, A.nsel, sm.runs, sm.scan, kMaxRoutedAttn);
+  if (z == 0) {   // the usable kept groups, for bwd_dkv_kernel
+    const int64_t it = (int64_t)b * S.hkv + h;
+    for (int i = threadIdx.x; i < P.nrouted; i += kAttnThreads) A.used[it * S.kg + i] = sm.runs[i] / S.g;
+    if (threadIdx.x == 0) A.nused[it] = P.nrouted;
+  }
   const int nt = P.ntiles;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -128,18 +99,24 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dq_kernel(BwdArgs A) {
   bf16x8 qf[D / 16], gf[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) qf[ks] = gf[ks] = bf16x8{};
-  float lse2 = 0.0f, dterm = 0.0f;
+  float lse2 = 0.0f, dpart = 0.0f;
   if (live) {
     const uint16_t* qp = static_cast<const uint16_t*>(A.q) + qrow * D + 8 * hl;
     const uint16_t* gp = static_cast<const uint16_t*>(A.dout) + qrow * D + 8 * hl;
+    const uint16_t* op = static_cast<const uint16_t*>(A.out) + qrow * D + 8 * hl;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 16 * ks));
       gf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(gp + 16 * ks));
+      const bf16x8 of = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(op + 16 * ks));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dpart = fmaf((float)gf[ks][e], (float)of[e], dpart);
     }
     lse2 = A.lse[qrow] * kLog2e;
-    dterm = A.dd[qrow];
   }
+  // D = dO . O of this lane's row: the two lane halves hold the two halves of d
+  const float dterm = active ? pair_sum(dpart) : 0.0f;
+  if (live && hl == 0) A.dd[qrow] = dterm;
 
   const int lg = __ffs(S.g) - 1;
   const KVRows kv{static_cast<const uint16_t*>(A.k) + (int64_t)h * S.kvs * D,
@@ -549,7 +526,6 @@ hipError_t launch_attend_backward(const Shape& s, const void* q, const void* k, 
   A.m0 = s.q0 / kChunk;
   A.nchunks = (int)((s.q0 + s.nq - 1) / kChunk - A.m0 + 1);
   const int64_t items = s.nb * s.hkv;
-  bwd_prep_kernel<<<dim3((unsigned)items), dim3(256), 0, st>>>(A);
   const dim3 gq((unsigned)(items * A.wg_per_item)), gkv((unsigned)(s.hkv * A.nchunks));
   if (s.d == 128) {
     bwd_dq_kernel<128><<<gq, dim3(kAttnThreads), 0, st>>>(A);
