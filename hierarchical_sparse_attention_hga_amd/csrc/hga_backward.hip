@@ -42,8 +42,8 @@ struct BwdArgs {
   const int32_t* gidx;
   const int32_t* nsel;
   float* dd;          // workspace [Hq][n_q]: D = dO . O
-  int32_t* used;      // workspace [nb][Hkv][kg]: usable kept groups, ascending
-  int32_t* nused;     // workspace [nb][Hkv]
+  unsigned long long* cmask;   // workspace [nb][Hkv][nchunks]: tokens of chunk m0 + c kept as
+                               // routed groups of the item (bit t: token 64 (m0 + c) + t)
   void* dq;
   void* dk;
   void* dv;
@@ -75,10 +75,22 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dq_kernel(BwdArgs A) {
   int b, h, z;
   item_of_block(S, A.wg_per_item, &b, &h, &z);
   const Plan P = make_plan(S, b, h, A.gidx, A.nsel, sm.runs, sm.scan, kMaxRoutedAttn);
-  if (z == 0) {   // the usable kept groups, for bwd_dkv_kernel
+  if (z == 0) {
+    // for bwd_dkv_kernel: the item's kept tokens in each chunk of the call's
+    // positions, from the ascending run list (first tokens of the groups)
     const int64_t it = (int64_t)b * S.hkv + h;
-    for (int i = threadIdx.x; i < P.nrouted; i += kAttnThreads) A.used[it * S.kg + i] = sm.runs[i] / S.g;
-    if (threadIdx.x == 0) A.nused[it] = P.nrouted;
+    const unsigned long long gmask = S.g >= 64 ? ~0ull : ((1ull << S.g) - 1ull);
+    for (int c = threadIdx.x; c < A.nchunks; c += kAttnThreads) {
+      const int first = (int)((A.m0 + c) * kChunk);
+      int lo = 0, hi = P.nrouted;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (sm.runs[mid] < first) lo = mid + 1; else hi = mid;
+      }
+      unsigned long long msk = 0ull;
+      for (int i = lo; i < P.nrouted && sm.runs[i] < first + kChunk; ++i) msk |= gmask << (sm.runs[i] - first);
+      A.cmask[it * A.nchunks + c] = msk;
+    }
   }
   const int nt = P.ntiles;
 
@@ -256,14 +268,15 @@ constexpr int kKVThreads = 256;
 constexpr int kKVWaves = kKVThreads / 64;
 constexpr int kKVListCap = kKVThreads;   // attending blocks listed per pass
 constexpr int kDiagBit = 1 << 30;        // list entry flag: the block lies in the chunk
+constexpr int kKVStages = 4;             // query tiles in the LDS ring (up to 3 in flight)
 
 template <int D>
 struct BwdKVSmem {
-  uint16_t q[2][kChunk * D];   // 64-row tiles of Q and dO (kv_swizzle), 2 stages;
-  uint16_t g[2][kChunk * D];   // after the loop, the cross-wave reduction buffer
-  float lse[2][kChunk];
-  float dd[2][kChunk];
-  float spare[2][kChunk];      // target of the per-row word loads of waves 2 and 3
+  uint16_t q[kKVStages][kChunk * D];   // 64-row tiles of Q and dO (kv_swizzle); after
+  uint16_t g[kKVStages][kChunk * D];   // the loop, the cross-wave reduction buffer
+  float lse[kKVStages][kChunk];
+  float dd[kKVStages][kChunk];
+  float spare[kKVStages][kChunk];      // target of the per-row word loads of waves 2 and 3
   int lb[kKVListCap];          // attending block, | kDiagBit for the chunk's own blocks
   unsigned long long lmask[kKVListCap];   // tokens of the chunk in the block's token set
   int scan[16];
@@ -333,8 +346,6 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkv_kernel(BwdArgs A) {
   const uint16_t* gg = static_cast<const uint16_t*>(A.dout);
   const int nrows = S.G * S.B;
   const int ntl = (nrows + kChunk - 1) / kChunk;   // 64-row query tiles per attending block
-  const int gpc = kChunk / S.g;
-  const unsigned long long gmask = S.g >= 64 ? ~0ull : ((1ull << S.g) - 1ull);
   const float sl2 = S.scale * kLog2e;
 
   f32x16 dk[D / 32], dv[D / 32];
@@ -350,7 +361,7 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkv_kernel(BwdArgs A) {
   auto issue = [&](int u) {
     const int e = u / ntl, pt = u - e * ntl;
     const int bq = sm.lb[e] & (kDiagBit - 1);
-    const uint32_t off = (uint32_t)((u & 1) * kChunk * D * 2);
+    const uint32_t off = (uint32_t)((u % kKVStages) * kChunk * D * 2);
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
       const int row0 = wave * RPW + i * RPI;
@@ -364,7 +375,8 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkv_kernel(BwdArgs A) {
     // again into a spare row so that every wave issues the same loads
     const int64_t sr = src_row(bq, kChunk * pt + lane);
     const float* src = wave == 1 ? A.dd + sr : A.lse + sr;
-    float* dst = wave == 0 ? &sm.lse[u & 1][0] : wave == 1 ? &sm.dd[u & 1][0] : &sm.spare[u & 1][0];
+    const int st = u % kKVStages;
+    float* dst = wave == 0 ? &sm.lse[st][0] : wave == 1 ? &sm.dd[st][0] : &sm.spare[st][0];
     lds_dma4(src, lds_addr(dst));
   };
 
@@ -385,16 +397,7 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkv_kernel(BwdArgs A) {
           code = b;
           msk = ~0ull;
         } else {
-          const int64_t it = (int64_t)b * S.hkv + h;
-          const int32_t* u = A.used + it * S.kg;
-          const int n = A.nused[it];
-          const int first = (int)(m * gpc);
-          int lo = 0, hi = n;
-          while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (u[mid] < first) lo = mid + 1; else hi = mid;
-          }
-          for (int i = lo; i < n && u[i] < first + gpc; ++i) msk |= gmask << ((u[i] - first) * S.g);
+          msk = A.cmask[((int64_t)b * S.hkv + h) * A.nchunks + (m - A.m0)];
           if (msk) code = b;
         }
       }
@@ -407,17 +410,28 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkv_kernel(BwdArgs A) {
     }
     __syncthreads();
     const int T = tot * ntl;
-    if (T > 0) issue(0);
+    // tiles 0 .. kKVStages - 2 in flight first; at iteration u, once tile u
+    // has landed (every newer issued tile may still be pending), tile
+    // u + kKVStages - 1 goes into the stage tile u - 1 left
+    constexpr int kPerTile = 2 * KI + 1;   // loads per thread per tile
+    for (int u = 0; u < kKVStages - 1 && u < T; ++u) issue(u);
     for (int u = 0; u < T; ++u) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      const int ahead = T - 1 - u < kKVStages - 2 ? T - 1 - u : kKVStages - 2;
+      if (ahead >= 2)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPerTile));
+      else if (ahead == 1)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPerTile));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();   // tile u landed everywhere; the stage of tile u - 1 is free
-      if (u + 1 < T) issue(u + 1);
+      if (u + kKVStages - 1 < T) issue(u + kKVStages - 1);
       const int e = u / ntl, pt = u - e * ntl;
       const int code_e = sm.lb[e];
       const bool diag = (code_e & kDiagBit) != 0;
       const int64_t sq = S.q0 + (int64_t)(code_e & (kDiagBit - 1)) * S.B;
       const bool tok_ok = ((sm.lmask[e] >> tok) & 1ull) && tpos < lq;
-      const uint32_t stage = (uint32_t)((u & 1) * kChunk * RB);
+      const int su = u % kKVStages;
+      const uint32_t stage = (uint32_t)(su * kChunk * RB);
       const char* qt = sQb + stage + 32 * rw * RB;
       const char* gt = sGb + stage + 32 * rw * RB;
       f32x16 sacc = f32x16{}, pacc = f32x16{};
@@ -432,8 +446,8 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkv_kernel(BwdArgs A) {
       float lr[16], dr[16];
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
-        const float4 l4 = *reinterpret_cast<const float4*>(&sm.lse[u & 1][32 * rw + 8 * a4 + 4 * hl]);
-        const float4 d4 = *reinterpret_cast<const float4*>(&sm.dd[u & 1][32 * rw + 8 * a4 + 4 * hl]);
+        const float4 l4 = *reinterpret_cast<const float4*>(&sm.lse[su][32 * rw + 8 * a4 + 4 * hl]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&sm.dd[su][32 * rw + 8 * a4 + 4 * hl]);
         lr[4 * a4] = l4.x; lr[4 * a4 + 1] = l4.y; lr[4 * a4 + 2] = l4.z; lr[4 * a4 + 3] = l4.w;
         dr[4 * a4] = d4.x; dr[4 * a4 + 1] = d4.y; dr[4 * a4 + 2] = d4.z; dr[4 * a4 + 3] = d4.w;
       }
@@ -503,9 +517,12 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkv_kernel(BwdArgs A) {
 
 }  // namespace
 
+// D per query row, then the kept-token masks per (block, KV head, chunk of
+// the call's positions); the chunk count is bounded for any q_start.
 size_t backward_workspace_bytes(const Shape& s) {
   auto a256 = [](size_t n) { return (n + 255) & ~(size_t)255; };
-  return a256(4 * (size_t)s.hq * s.nq) + a256(4 * (size_t)s.nb * s.hkv * s.kg) + a256(4 * (size_t)s.nb * s.hkv);
+  const size_t nchunks_max = (size_t)(s.nq + kChunk - 1) / kChunk + 1;
+  return a256(4 * (size_t)s.hq * s.nq) + a256(8 * (size_t)s.nb * s.hkv * nchunks_max);
 }
 
 hipError_t launch_attend_backward(const Shape& s, const void* q, const void* k, const void* v,
@@ -519,8 +536,7 @@ hipError_t launch_attend_backward(const Shape& s, const void* q, const void* k, 
   A.dq = dq; A.dk = dk; A.dv = dv; A.s = s;
   char* ws = static_cast<char*>(workspace);
   A.dd = reinterpret_cast<float*>(ws);
-  A.used = reinterpret_cast<int32_t*>(ws + a256(4 * (size_t)s.hq * s.nq));
-  A.nused = reinterpret_cast<int32_t*>(ws + a256(4 * (size_t)s.hq * s.nq) + a256(4 * (size_t)s.nb * s.hkv * s.kg));
+  A.cmask = reinterpret_cast<unsigned long long*>(ws + a256(4 * (size_t)s.hq * s.nq));
   const int waves = (s.G * s.B + 31) / 32;
   A.wg_per_item = (waves + kAttnWaves - 1) / kAttnWaves;
   A.m0 = s.q0 / kChunk;

@@ -186,9 +186,10 @@ def test_backward_validation():
     c = cfg()
     E = hga.HGA_ERR_INVALID_ARGUMENT
     geo = (14336, 2048, 16384)
-    # workspace: D per query row, the usable kept groups and their counts
+    # workspace: D per query row (float32), then a 64-bit kept-token mask per
+    # (block, KV head, chunk of the call's positions; at most n_q / 64 + 1)
     nb = 2048 // 64
-    need = (4 * 32 * 2048 + 255) // 256 * 256 + (4 * nb * 8 * 64 + 255) // 256 * 256 + (4 * nb * 8 + 255) // 256 * 256
+    need = (4 * 32 * 2048 + 255) // 256 * 256 + (8 * nb * 8 * (2048 // 64 + 1) + 255) // 256 * 256
     assert hga.hga_workspace_size(c, 16384, 2048, hga.HGA_WS_BACKWARD) == need
     args = [FAKE] * 11   # k, v, group_idx, n_sel, out, lse, dout, dq, dk, dv, workspace
     def call(cc, a, ws_bytes=need, g=geo):
