@@ -222,20 +222,20 @@ class Workload:
             p.free()
 
 
-KERNEL_SOURCES = ("hga_attend.hip", "hga_attend_impl.h", "hga_route_impl.h", "hga_internal.h")
-
-
 def source_sha256():
-    """Digest of the sources of the route-and-attend kernel."""
+    """Digest of every kernel source (csrc/*.hip and *.h, in name order): a
+    counter run is valid only for the sources it was taken on."""
+    import glob
     import hashlib
-    src = b"".join(open(os.path.join(ROOT, "hierarchical_sparse_attention_hga_amd", "csrc", f), "rb").read()
-                   for f in KERNEL_SOURCES)
-    return hashlib.sha256(src).hexdigest()
+    files = sorted(glob.glob(os.path.join(ROOT, "hierarchical_sparse_attention_hga_amd", "csrc", "*.hip")) +
+                   glob.glob(os.path.join(ROOT, "hierarchical_sparse_attention_hga_amd", "csrc", "*.h")))
+    return hashlib.sha256(b"".join(open(f, "rb").read() for f in files)).hexdigest()
 
 
 def measured_traffic(workload, kernel):
-    """HBM bytes per launch of `kernel` ("route_attend_bf16" or "attend_bf16")
-    from the committed rocprofv3 counter runs
+    """HBM bytes per launch of `kernel` ("route_attend_bf16", "attend_bf16" or
+    "attend_backward", the latter summed over its kernels) from the committed
+    rocprofv3 counter runs
     (profiles/<kernel>_<workload>.traffic.json), or None when they are missing
     or were taken on different kernel sources."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}.traffic.json")
@@ -442,6 +442,7 @@ def decode_line(cfg_id, batch, steps, warmup):
     us = float(np.mean([evs[i][0].elapsed_time(evs[i][1]) * 1e3 for i in range(0, steps, 2)]))
     nsel = ns.cpu().numpy().reshape(hkv, 2)
     byts = float(sum(decode_bytes(base, pos, nsel[h]) for h in range(hkv)))
+    traffic = measured_traffic(f"{base['name']}-decode-b{batch}", "route_attend_bf16")
     del k, v, gs, cs
     torch.cuda.empty_cache()
     return {"value": steps * batch / wall, "unit": "generated tokens/s", "kernel_us_mean": us,
@@ -450,7 +451,7 @@ def decode_line(cfg_id, batch, steps, warmup):
                        "q_heads": base["hq"], "kv_heads": base["hkv"], "q_block": 1},
             "roofline": {"kernel": "route_attend_bf16", "bound": "hbm", "achieved": byts / (us * 1e-6) / 1e9,
                          "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": byts / (us * 1e-6) / PEAK_HBM,
-                         "traffic": None, "algorithmic_bytes": byts}}
+                         "traffic": traffic, "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": byts}}
 
 
 def backward_flops(cfg, n_sel, group_idx):
@@ -525,7 +526,9 @@ def backward_line(cfg_id, steps, warmup):
             "config": {"workload": f"{cfg['name']}-backward", "n_q": cfg["n_q"], "history": w.q0},
             "roofline": {"kernel": "hga_attend_backward (bwd_dq_kernel, then bwd_dkv_kernel)", "bound": "mfma",
                          "achieved": flops / (us * 1e-6) / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
-                         "frac": flops / (us * 1e-6) / PEAK_BF16, "traffic": None, "algorithmic_flops": flops}}
+                         "frac": flops / (us * 1e-6) / PEAK_BF16,
+                         "traffic": measured_traffic(f"{cfg['name']}-backward", "attend_backward"),
+                         "traffic_unit": "HBM bytes per call (both kernels)", "algorithmic_flops": flops}}
 
 
 def measure(cfg_id, steps, warmup, split=0, fused=None):
