@@ -1,9 +1,12 @@
 """Benchmark of the HGA routed-attention forward on one MI355X.
 
 A step is one pass of the whole path over one layer of one synthetic input:
-hga_build_summaries (group and chunk summaries of every key), then
-hga_route_attend (block queries, chunk stage, group stage and exact routed
-attention), all on one stream with every input already in HBM. With at most
+hga_build_summaries_range (group and chunk summaries of the chunks the step's
+own positions close; the history's summaries are resident, built when their
+chunks closed, as the pages keep them), then hga_route_attend (block queries,
+chunk stage, group stage and exact routed attention), all on one stream with
+every input already in HBM. The rate with every chunk's summaries rebuilt
+each step is reported alongside. With at most
 4 query heads per KV head hga_route_attend is one kernel; with more (the 64K
 layer's 8) the step runs the router and the attention kernels, timed apart.
 The 16K step through the separate hga_route and hga_attend calls is reported
@@ -157,9 +160,13 @@ class Workload:
         self.n_stages = 2 if fused else 3
         self.pins = []
         self.ws, self.wsb = None, 0
+        # the history's summaries are resident before the step (built when
+        # their chunks closed); each step builds those of the chunks its own
+        # positions close
+        hga.hga_build_summaries(self.c, k, L, self.gs, self.cs)
+        torch.cuda.synchronize()
+        self.seg_chunks = (self.q0 // 64, L // 64)
         if split > 0:
-            hga.hga_build_summaries(self.c, k, L, self.gs, self.cs)
-            torch.cuda.synchronize()
             gpin, _, gs_t = split_to_host(self.gs, split // cfg["group"])
             self.gs_t = (gs_t[0], gs_t[1], split)
             kpin, _, self.k_t = split_to_host(k, split)
@@ -180,7 +187,7 @@ class Workload:
                 ev[k].record()
         mark(0, 0)
         if self.split == 0:
-            hga.hga_build_summaries(c, self.k_full, self.L, self.gs, self.cs)
+            hga.hga_build_summaries_range(c, self.k_full, self.L, *self.seg_chunks, self.gs, self.cs)
         mark(0, 1)
         mark(1, 0)
         if self.fused:
@@ -531,6 +538,24 @@ def backward_line(cfg_id, steps, warmup):
                          "traffic_unit": "HBM bytes per call (both kernels)", "algorithmic_flops": flops}}
 
 
+def full_summary_us(cfg_id, reps=20):
+    """Mean time of hga_build_summaries over every chunk of workload cfg_id's
+    sequence (HIP events on the launch stream)."""
+    import torch
+    w = Workload(cfg_id)
+    for _ in range(3):
+        w.hga.hga_build_summaries(w.c, w.k_full, w.L, w.gs, w.cs)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        w.hga.hga_build_summaries(w.c, w.k_full, w.L, w.gs, w.cs)
+    e1.record()
+    torch.cuda.synchronize()
+    w.free()
+    return e0.elapsed_time(e1) / reps * 1e3
+
+
 def measure(cfg_id, steps, warmup, split=0, fused=None):
     w = Workload(cfg_id, split, fused)
     wall, stage = w.run(steps, warmup)
@@ -587,6 +612,13 @@ def main():
         extra["summaries_prebuilt"] = {
             "value": cfg["n_q"] / (rest * 1e-6), "unit": "query-tokens/s",
             "note": "n_q / (mean routing + gather + attention stage time); summary build excluded"}
+        if not split:
+            full_us = full_summary_us(args.config)
+            extra["full_summary_rebuild"] = {
+                "value": cfg["n_q"] / ((full_us + rest) * 1e-6), "unit": "query-tokens/s",
+                "summaries_us": full_us,
+                "note": "the step with the summaries of every chunk of the sequence rebuilt (history included) "
+                        "instead of only the chunks the step's positions close"}
         half = max(args.steps // 2, 5)
         if main_r.fused:
             sep = measure(args.config, half, args.warmup, fused=False)
