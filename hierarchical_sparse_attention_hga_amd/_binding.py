@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libhga.so")
 HGA_OK, HGA_ERR_INVALID_ARGUMENT, HGA_ERR_UNSUPPORTED, HGA_ERR_WORKSPACE, HGA_ERR_DEVICE = range(5)
 HGA_F32, HGA_BF16 = 0, 1
 HGA_SUMMARY_MEAN = 0
-HGA_WS_ROUTE, HGA_WS_ATTEND, HGA_WS_ATTEND_TIERED, HGA_WS_BACKWARD = 0, 1, 2, 3
+HGA_WS_ROUTE, HGA_WS_ATTEND, HGA_WS_ATTEND_TIERED, HGA_WS_BACKWARD, HGA_WS_BACKWARD_TIERED = 0, 1, 2, 3, 4
 
 # Every exported entry point of include/hga.h.
 EXPORTS = ("hga_workspace_size", "hga_build_summaries", "hga_build_summaries_range", "hga_route", "hga_attend",
@@ -63,7 +63,7 @@ def load():
         lib.hga_route_attend.argtypes = [cfgp, P, I64, I64, I64, P, tierp, tierp, tierp, P, P, P, P, P, P, SZ, P]
         lib.hga_build_summaries_range.argtypes = [cfgp, P, I64, I64, I64, P, P, P]
         lib.hga_stream_forward.argtypes = [cfgp, P, P, P, I64, I64, P, P, P, P, P, P, P, P]
-        lib.hga_attend_backward.argtypes = [cfgp, P, I64, I64, I64, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+        lib.hga_attend_backward.argtypes = [cfgp, P, I64, I64, I64, tierp, tierp, P, P, P, P, P, P, P, P, P, SZ, P]
         for f in ("hga_build_summaries", "hga_build_summaries_range", "hga_route", "hga_attend",
                   "hga_route_attend", "hga_stream_forward", "hga_attend_backward"):
             getattr(lib, f).restype = C.c_int
@@ -169,7 +169,8 @@ def hga_stream_forward(cfg, q, k, v, seq_len, segment, chunk_sum, group_sum, chu
 
 def hga_attend_backward(cfg, q, q_start, n_q, seq_len, k, v, group_idx, n_sel, out, lse, dout, dq, dk, dv,
                         workspace=None, ws_bytes=0, stream=None):
-    _check(load().hga_attend_backward(C.byref(cfg), _ptr(q), q_start, n_q, seq_len, _ptr(k), _ptr(v),
+    kt, vt = _tier(k), _tier(v)
+    _check(load().hga_attend_backward(C.byref(cfg), _ptr(q), q_start, n_q, seq_len, C.byref(kt), C.byref(vt),
                                       _ptr(group_idx), _ptr(n_sel), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
                                       _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, _stream(stream)))
 

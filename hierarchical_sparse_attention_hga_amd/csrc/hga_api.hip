@@ -137,6 +137,8 @@ size_t hga_workspace_size(const hga_config* cfg, int64_t seq_len, int64_t n_q, i
     case HGA_WS_ATTEND: return 0;
     case HGA_WS_ATTEND_TIERED: return hga::tier_cache_bytes(s, seq_len - n_q);
     case HGA_WS_BACKWARD: return hga::backward_workspace_bytes(s);
+    case HGA_WS_BACKWARD_TIERED:
+      return hga::backward_workspace_bytes(s) + hga::tier_cache_bytes(s, seq_len - n_q);
     default: fail(HGA_ERR_INVALID_ARGUMENT, "unknown workspace kind %d", which); return (size_t)-1;
   }
 }
@@ -286,21 +288,28 @@ hga_status hga_route_attend(const hga_config* cfg, const void* q, int64_t q_star
 }
 
 hga_status hga_attend_backward(const hga_config* cfg, const void* q, int64_t q_start, int64_t n_q,
-                               int64_t seq_len, const void* k, const void* v, const int32_t* group_idx,
-                               const int32_t* n_sel, const void* out, const float* lse, const void* dout,
-                               void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes, void* stream) {
+                               int64_t seq_len, const hga_tiered* k, const hga_tiered* v,
+                               const int32_t* group_idx, const int32_t* n_sel, const void* out, const float* lse,
+                               const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+                               void* stream) {
   hga::Shape s;
   hga_status st = make_shape(cfg, seq_len, q_start, n_q, &s);
   if (st != HGA_OK) return st;
   if (s.dtype != HGA_BF16) return fail(HGA_ERR_UNSUPPORTED, "the backward is built for bfloat16 only");
   if (n_q == 0) return ok();
-  if (!q || !k || !v || !n_sel || !out || !lse || !dout || !dq || !dk || !dv || (s.kg > 0 && !group_idx))
-    return fail(HGA_ERR_INVALID_ARGUMENT,
-                "q, k, v, group_idx, n_sel, out, lse, dout, dq, dk and dv must be non-NULL");
-  const size_t need = hga::backward_workspace_bytes(s);
+  if (!q || !n_sel || !out || !lse || !dout || !dq || !dk || !dv || (s.kg > 0 && !group_idx))
+    return fail(HGA_ERR_INVALID_ARGUMENT, "q, group_idx, n_sel, out, lse, dout, dq, dk and dv must be non-NULL");
+  if ((st = check_tier(k, "k", seq_len, q_start)) != HGA_OK) return st;
+  if ((st = check_tier(v, "v", seq_len, q_start)) != HGA_OK) return st;
+  if (k->split != v->split) return fail(HGA_ERR_INVALID_ARGUMENT, "k.split and v.split differ");
+  if (k->split > 0 && s.sink_chunks + s.local_chunks > hga::kMaxFixedTiered)
+    return fail(HGA_ERR_UNSUPPORTED, "with a host tier, sink and local windows may span at most %d chunks",
+                hga::kMaxFixedTiered);
+  const size_t need = hga::backward_workspace_bytes(s) + (k->split > 0 ? hga::tier_cache_bytes(s, k->split) : 0);
   if (!workspace || ws_bytes < need)
     return fail(HGA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : (size_t)0);
-  return device_status(hga::launch_attend_backward(s, q, k, v, group_idx, n_sel, out, lse, dout, dq, dk, dv,
+  const hga::KVSrc kv{k->host, k->dev, v->host, v->dev, k->split};
+  return device_status(hga::launch_attend_backward(s, q, kv, group_idx, n_sel, out, lse, dout, dq, dk, dv,
                                                    workspace, (hipStream_t)stream),
                        "hga_attend_backward launch");
 }
@@ -318,6 +327,6 @@ const char* hga_status_string(hga_status status) {
 
 const char* hga_last_error(void) { return g_err; }
 
-int32_t hga_version(void) { return 103; }
+int32_t hga_version(void) { return 104; }
 
 }  // extern "C"

@@ -39,27 +39,6 @@
 namespace hga {
 namespace {
 
-// Host-tier path: rewrite the kept groups' first tokens in runs[] and the
-// fixed chunks' first tokens into encoded source rows (fixsrc[t] for fixed
-// tile t). Every history chunk used here was marked and given a slot.
-__device__ void translate_plan(const AttnArgs& A, int h, const Plan& P, int* runs, int* fixsrc) {
-  const int64_t split = A.kv.split;
-  const int nch = A.nch;
-  auto enc = [&](int64_t tok) -> int {
-    if (tok < split) {
-      const int64_t m = tok / kChunk;
-      const int sl = A.slot[(int64_t)h * nch + m];
-      // every chunk used here was marked; an unmarked one would read device
-      // row 0 rather than outside the cache
-      return sl >= 0 ? kCacheFlag | (int)(((int64_t)h * nch + sl) * kChunk + tok % kChunk) : 0;
-    }
-    return (int)(tok - split);
-  };
-  for (int i = threadIdx.x; i < P.nrouted; i += blockDim.x) runs[i] = enc(runs[i]);
-  for (int t = threadIdx.x; t < P.nfix; t += blockDim.x)
-    fixsrc[t] = enc((t < P.a ? t : P.bb + (t - P.a)) * kChunk);
-  __syncthreads();
-}
 
 
 // Attention of item (b, h), workgroup slot z, over the token set of plan P
@@ -323,7 +302,7 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(AttnArgs A) {
   int b, h, z;
   item_of_block(A.s, A.wg_per_item, &b, &h, &z);
   const Plan P = make_plan(A.s, b, h, A.gidx, A.nsel, sm.runs, sm.scan, kMaxRoutedAttn);
-  if (kTiered) translate_plan(A, h, P, sm.runs, sm.runs + kMaxRoutedAttn);
+  if (kTiered) translate_plan(A.kv.split, A.nch, A.slot, h, P, sm.runs, sm.runs + kMaxRoutedAttn);
   attend_bf16_body<D, kTiered>(A, b, h, z, P, sm, 0, nullptr);
 }
 
@@ -392,7 +371,7 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttnArgs A) {
   int b, h, z;
   item_of_block(S, A.wg_per_item, &b, &h, &z);
   const Plan P = make_plan(S, b, h, A.gidx, A.nsel, sRuns, sScan, kMaxRouted);
-  if (kTiered) translate_plan(A, h, P, sRuns, sRuns + kMaxRouted);
+  if (kTiered) translate_plan(A.kv.split, A.nch, A.slot, h, P, sRuns, sRuns + kMaxRouted);
   const int64_t per_head = kTiered ? S.kvs - A.kv.split : S.kvs;
   const float* kdev = static_cast<const float*>(A.kv.k_dev) + (int64_t)h * per_head * D;
   const float* vdev = static_cast<const float*>(A.kv.v_dev) + (int64_t)h * per_head * D;
@@ -598,6 +577,35 @@ static int bf16_wg_per_item(const Shape& s) {
   return (waves + kAttnWaves - 1) / kAttnWaves;
 }
 
+// Host-tier cache of one call (workspace: [need][slot] int32 [Hkv][nch], then
+// the K and V caches): mark the history chunks the call's items need, give
+// them slots, copy them once each.
+hipError_t prepare_tier_cache(const Shape& s, const KVSrc& kv, const int32_t* group_idx, const int32_t* n_sel,
+                              void* workspace, TierCache* tc, hipStream_t st) {
+  const int64_t items = s.nb * s.hkv;
+  AttnArgs a{};
+  a.kv = kv; a.gidx = group_idx; a.nsel = n_sel; a.s = s;
+  const int nch = (int)(kv.split / kChunk);
+  const size_t esz = s.dtype == HGA_BF16 ? 2 : 4;
+  int32_t* need = static_cast<int32_t*>(workspace);
+  int32_t* slot = need + (int64_t)s.hkv * nch;
+  char* cache = static_cast<char*>(workspace) + (((2 * (size_t)s.hkv * nch * sizeof(int32_t)) + 255) & ~(size_t)255);
+  a.slot = slot;
+  a.nch = nch;
+  a.k_cache = cache;
+  a.v_cache = cache + (size_t)s.hkv * nch * kChunk * s.d * esz;
+  *tc = TierCache{slot, nch, a.k_cache, a.v_cache};
+  const int64_t nflags = (int64_t)s.hkv * nch;
+  fill_zero_kernel<<<dim3((unsigned)((nflags + 255) / 256)), dim3(256), 0, st>>>(need, nflags);
+  mark_kernel<<<dim3((unsigned)items), dim3(256), 0, st>>>(a, need);
+  slot_kernel<<<dim3((unsigned)s.hkv), dim3(1024), 0, st>>>(need, slot, nch);
+  if (s.dtype == HGA_BF16)
+    copy_kernel<uint16_t><<<dim3((unsigned)nch, (unsigned)s.hkv), dim3(256), 0, st>>>(a);
+  else
+    copy_kernel<float><<<dim3((unsigned)nch, (unsigned)s.hkv), dim3(256), 0, st>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_attend(const Shape& s, const void* q, const KVSrc& kv, const int32_t* group_idx,
                          const int32_t* n_sel, void* out, float* lse, void* workspace, hipStream_t st) {
   const int64_t items = s.nb * s.hkv;
@@ -606,26 +614,13 @@ hipError_t launch_attend(const Shape& s, const void* q, const KVSrc& kv, const i
   a.q = q; a.kv = kv; a.gidx = group_idx; a.nsel = n_sel; a.out = out; a.lse = lse; a.s = s;
   const bool tiered = kv.split > 0;
   if (tiered) {
-    // workspace: [need][slot] int32 [Hkv][nch], then the K and V caches
-    const int nch = (int)(kv.split / kChunk);
-    const size_t esz = s.dtype == HGA_BF16 ? 2 : 4;
-    int32_t* need = static_cast<int32_t*>(workspace);
-    int32_t* slot = need + (int64_t)s.hkv * nch;
-    char* cache = static_cast<char*>(workspace) + (((2 * (size_t)s.hkv * nch * sizeof(int32_t)) + 255) & ~(size_t)255);
-    a.slot = slot;
-    a.nch = nch;
-    a.k_cache = cache;
-    a.v_cache = cache + (size_t)s.hkv * nch * kChunk * s.d * esz;
-    const int64_t nflags = (int64_t)s.hkv * nch;
-    fill_zero_kernel<<<dim3((unsigned)((nflags + 255) / 256)), dim3(256), 0, st>>>(need, nflags);
-    mark_kernel<<<dim3((unsigned)items), dim3(256), 0, st>>>(a, need);
-    slot_kernel<<<dim3((unsigned)s.hkv), dim3(1024), 0, st>>>(need, slot, nch);
-    if (s.dtype == HGA_BF16)
-      copy_kernel<uint16_t><<<dim3((unsigned)nch, (unsigned)s.hkv), dim3(256), 0, st>>>(a);
-    else
-      copy_kernel<float><<<dim3((unsigned)nch, (unsigned)s.hkv), dim3(256), 0, st>>>(a);
-    const hipError_t e = hipGetLastError();
+    TierCache tc;
+    const hipError_t e = prepare_tier_cache(s, kv, group_idx, n_sel, workspace, &tc, st);
     if (e != hipSuccess) return e;
+    a.slot = tc.slot;
+    a.nch = tc.nch;
+    a.k_cache = tc.k_cache;
+    a.v_cache = tc.v_cache;
   }
   if (s.dtype == HGA_BF16) {
     a.wg_per_item = bf16_wg_per_item(s);

@@ -162,6 +162,29 @@ __device__ inline int tile_limit(const Plan& P, int g, int t) {
 }
 
 
+// Host-tier path: rewrite the kept groups' first tokens in runs[] and the
+// fixed chunks' first tokens into encoded source rows (fixsrc[t] for fixed
+// tile t), given the cache slots (slot[h nch + m], -1: not cached) of the
+// nch history chunks below split. Every history chunk used here was marked
+// and given a slot.
+__device__ void translate_plan(int64_t split, int nch, const int32_t* slot, int h, const Plan& P, int* runs,
+                               int* fixsrc) {
+  auto enc = [&](int64_t tok) -> int {
+    if (tok < split) {
+      const int64_t m = tok / kChunk;
+      const int sl = slot[(int64_t)h * nch + m];
+      // every chunk used here was marked; an unmarked one would read device
+      // row 0 rather than outside the cache
+      return sl >= 0 ? kCacheFlag | (int)(((int64_t)h * nch + sl) * kChunk + tok % kChunk) : 0;
+    }
+    return (int)(tok - split);
+  };
+  for (int i = threadIdx.x; i < P.nrouted; i += blockDim.x) runs[i] = enc(runs[i]);
+  for (int t = threadIdx.x; t < P.nfix; t += blockDim.x)
+    fixsrc[t] = enc((t < P.a ? t : P.bb + (t - P.a)) * kChunk);
+  __syncthreads();
+}
+
 // K or V row of a source row: the cache, or the head's device rows.
 template <typename T>
 __device__ inline const T* src_ptr(const T* dev_head, const T* cache, int src, int d) {

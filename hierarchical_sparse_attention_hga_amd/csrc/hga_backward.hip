@@ -34,8 +34,8 @@ namespace {
 
 struct BwdArgs {
   const void* q;
-  const void* k;
-  const void* v;
+  KVSrc kv;           // K/V: device rows [split, L), host rows [0, split)
+  TierCache tc;       // host-tier cache of the history chunks the call attends (split > 0)
   const void* out;
   const float* lse;
   const void* dout;
@@ -58,13 +58,13 @@ template <int D>
 struct BwdQSmem {
   uint16_t k[2][kChunk * D];   // kv_swizzle: read row-wise and transposed
   uint16_t v[2][kChunk * D];   // k_swizzle: read row-wise
-  int runs[kMaxRoutedAttn];
+  int runs[kMaxRoutedAttn + kMaxFixedTiered];   // kept groups' rows, then (host tier) the fixed chunks'
   int scan[16];
 };
 
 // One workgroup slot z of item (b, h): 8 waves of 32 query rows, the item's
 // token-set tiles in the forward's order through a 2-stage LDS ring.
-template <int D>
+template <int D, bool kTiered>
 __global__ __launch_bounds__(kAttnThreads) void bwd_dq_kernel(BwdArgs A) {
   __shared__ BwdQSmem<D> sm;
   constexpr int NP = D / 8;
@@ -91,6 +91,10 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dq_kernel(BwdArgs A) {
       for (int i = lo; i < P.nrouted && sm.runs[i] < first + kChunk; ++i) msk |= gmask << (sm.runs[i] - first);
       A.cmask[it * A.nchunks + c] = msk;
     }
+  }
+  if (kTiered) {   // rows of the history come from the host-tier cache
+    __syncthreads();   // the masks above read the token runs
+    translate_plan(A.kv.split, A.tc.nch, A.tc.slot, h, P, sm.runs, sm.runs + kMaxRoutedAttn);
   }
   const int nt = P.ntiles;
 
@@ -131,8 +135,10 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dq_kernel(BwdArgs A) {
   if (live && hl == 0) A.dd[qrow] = dterm;
 
   const int lg = __ffs(S.g) - 1;
-  const KVRows kv{static_cast<const uint16_t*>(A.k) + (int64_t)h * S.kvs * D,
-                  static_cast<const uint16_t*>(A.v) + (int64_t)h * S.kvs * D, nullptr, nullptr};
+  const int64_t per_head = S.kvs - A.kv.split;   // device rows per head
+  const KVRows kv{static_cast<const uint16_t*>(A.kv.k_dev) + (int64_t)h * per_head * D,
+                  static_cast<const uint16_t*>(A.kv.v_dev) + (int64_t)h * per_head * D,
+                  static_cast<const uint16_t*>(A.tc.k_cache), static_cast<const uint16_t*>(A.tc.v_cache)};
   // run-table entries one tile ahead, as in the forward
   int raw[KI];
   auto run_of = [&](int t, int sl) { return ((t - P.nfix) << (6 - lg)) + (sl >> lg); };
@@ -140,15 +146,17 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dq_kernel(BwdArgs A) {
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
       const int rr = wave * RPW + i * RPI + lane / NP;
-      raw[i] = sm.runs[run_of(t, rr) & (kMaxRoutedAttn - 1)];
+      const int idx = kTiered && t < P.nfix ? kMaxRoutedAttn + (t & (kMaxFixedTiered - 1))
+                                            : run_of(t, rr) & (kMaxRoutedAttn - 1);
+      raw[i] = sm.runs[idx];
     }
   };
-  const int diag0 = (int)P.c0;
+  const int diag0 = (int)(P.c0 - A.kv.split);   // source row of the last tile's first slot
   const int dlim = P.dlim;
   auto issue = [&](int t) {
     const uint32_t off = (uint32_t)((t & 1) * kChunk * D * 2);
     issue_tile<D, 2, 0>(kv, lds_addr(&sm.k[0][0]) + off, lds_addr(&sm.v[0][0]) + off, [&](int i, int sl) -> int {
-      if (t < P.nfix) return (int)((t < P.a ? t : P.bb + (t - P.a)) * kChunk) + sl;
+      if (t < P.nfix) return kTiered ? raw[i] + sl : (int)((t < P.a ? t : P.bb + (t - P.a)) * kChunk) + sl;
       if (t < P.nfix + P.nrt) return run_of(t, sl) < P.nrouted ? raw[i] + (sl & ((1 << lg) - 1)) : 0;
       return diag0 + (sl < dlim ? sl : 0);
     });
@@ -313,9 +321,10 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkv_kernel(BwdArgs A) {
   bf16x8 kf[D / 16], vf[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) kf[ks] = vf[ks] = bf16x8{};
-  if (tpos < lq) {
-    const uint16_t* kp = static_cast<const uint16_t*>(A.k) + ((int64_t)h * S.kvs + tpos) * D + 8 * hl;
-    const uint16_t* vp = static_cast<const uint16_t*>(A.v) + ((int64_t)h * S.kvs + tpos) * D + 8 * hl;
+  if (tpos < lq) {   // the call's positions lie in the device rows (split <= 64 m0)
+    const int64_t drow = (int64_t)h * (S.kvs - A.kv.split) + (tpos - A.kv.split);
+    const uint16_t* kp = static_cast<const uint16_t*>(A.kv.k_dev) + drow * D + 8 * hl;
+    const uint16_t* vp = static_cast<const uint16_t*>(A.kv.v_dev) + drow * D + 8 * hl;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       kf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + 16 * ks));
@@ -525,14 +534,13 @@ size_t backward_workspace_bytes(const Shape& s) {
   return a256(4 * (size_t)s.hq * s.nq) + a256(8 * (size_t)s.nb * s.hkv * nchunks_max);
 }
 
-hipError_t launch_attend_backward(const Shape& s, const void* q, const void* k, const void* v,
-                                  const int32_t* group_idx, const int32_t* n_sel, const void* out,
-                                  const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                                  void* workspace, hipStream_t st) {
+hipError_t launch_attend_backward(const Shape& s, const void* q, const KVSrc& kv, const int32_t* group_idx,
+                                  const int32_t* n_sel, const void* out, const float* lse, const void* dout,
+                                  void* dq, void* dk, void* dv, void* workspace, hipStream_t st) {
   if (s.nq == 0) return hipSuccess;
   auto a256 = [](size_t n) { return (n + 255) & ~(size_t)255; };
   BwdArgs A{};
-  A.q = q; A.k = k; A.v = v; A.out = out; A.lse = lse; A.dout = dout; A.gidx = group_idx; A.nsel = n_sel;
+  A.q = q; A.kv = kv; A.out = out; A.lse = lse; A.dout = dout; A.gidx = group_idx; A.nsel = n_sel;
   A.dq = dq; A.dk = dk; A.dv = dv; A.s = s;
   char* ws = static_cast<char*>(workspace);
   A.dd = reinterpret_cast<float*>(ws);
@@ -541,13 +549,20 @@ hipError_t launch_attend_backward(const Shape& s, const void* q, const void* k, 
   A.wg_per_item = (waves + kAttnWaves - 1) / kAttnWaves;
   A.m0 = s.q0 / kChunk;
   A.nchunks = (int)((s.q0 + s.nq - 1) / kChunk - A.m0 + 1);
+  const bool tiered = kv.split > 0;
+  if (tiered) {   // the host-tier cache follows the backward's own workspace
+    const hipError_t e = prepare_tier_cache(s, kv, group_idx, n_sel, ws + backward_workspace_bytes(s), &A.tc, st);
+    if (e != hipSuccess) return e;
+  }
   const int64_t items = s.nb * s.hkv;
   const dim3 gq((unsigned)(items * A.wg_per_item)), gkv((unsigned)(s.hkv * A.nchunks));
   if (s.d == 128) {
-    bwd_dq_kernel<128><<<gq, dim3(kAttnThreads), 0, st>>>(A);
+    if (tiered) bwd_dq_kernel<128, true><<<gq, dim3(kAttnThreads), 0, st>>>(A);
+    else bwd_dq_kernel<128, false><<<gq, dim3(kAttnThreads), 0, st>>>(A);
     bwd_dkv_kernel<128><<<gkv, dim3(kKVThreads), 0, st>>>(A);
   } else if (s.d == 64) {
-    bwd_dq_kernel<64><<<gq, dim3(kAttnThreads), 0, st>>>(A);
+    if (tiered) bwd_dq_kernel<64, true><<<gq, dim3(kAttnThreads), 0, st>>>(A);
+    else bwd_dq_kernel<64, false><<<gq, dim3(kAttnThreads), 0, st>>>(A);
     bwd_dkv_kernel<64><<<gkv, dim3(kKVThreads), 0, st>>>(A);
   } else {
     return hipErrorInvalidValue;

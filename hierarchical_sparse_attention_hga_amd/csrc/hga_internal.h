@@ -72,6 +72,18 @@ struct KVSrc {
 // history chunk of K and V.
 size_t tier_cache_bytes(const Shape& s, int64_t split);
 
+// Host-tier cache of one call: the cache slot of each history chunk of each
+// KV head (-1: not needed) and the HBM copies of the needed chunks' K and V,
+// in the workspace (tier_cache_bytes). The copy runs on st.
+struct TierCache {
+  const int32_t* slot;
+  int nch;
+  const void* k_cache;
+  const void* v_cache;
+};
+hipError_t prepare_tier_cache(const Shape& s, const KVSrc& kv, const int32_t* group_idx, const int32_t* n_sel,
+                              void* workspace, TierCache* tc, hipStream_t st);
+
 hipError_t launch_attend(const Shape& s, const void* q, const KVSrc& kv, const int32_t* group_idx,
                          const int32_t* n_sel, void* out, float* lse, void* workspace, hipStream_t st);
 
@@ -81,12 +93,12 @@ hipError_t launch_route_attend(const Shape& s, const void* q, const float* cs, c
                                const float* gs_dev, int64_t gs_split, const KVSrc& kv, int32_t* chunk_idx,
                                int32_t* group_idx, int32_t* n_sel, void* out, float* lse, hipStream_t st);
 
-// Backward of the attention (bfloat16, K/V on the device): workspace bytes,
-// and the launch of its three kernels.
+// Backward of the attention (bfloat16): workspace bytes (without the
+// host-tier cache, which follows them when kv.split > 0), and the launch of
+// its kernels.
 size_t backward_workspace_bytes(const Shape& s);
-hipError_t launch_attend_backward(const Shape& s, const void* q, const void* k, const void* v,
-                                  const int32_t* group_idx, const int32_t* n_sel, const void* out,
-                                  const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                                  void* workspace, hipStream_t st);
+hipError_t launch_attend_backward(const Shape& s, const void* q, const KVSrc& kv, const int32_t* group_idx,
+                                  const int32_t* n_sel, const void* out, const float* lse, const void* dout,
+                                  void* dq, void* dk, void* dv, void* workspace, hipStream_t st);
 
 }  // namespace hga

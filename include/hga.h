@@ -100,7 +100,9 @@ typedef struct {
   int64_t split;
 } hga_tiered;
 
-enum { HGA_WS_ROUTE = 0, HGA_WS_ATTEND = 1, HGA_WS_ATTEND_TIERED = 2, HGA_WS_BACKWARD = 3 };
+enum {
+  HGA_WS_ROUTE = 0, HGA_WS_ATTEND = 1, HGA_WS_ATTEND_TIERED = 2, HGA_WS_BACKWARD = 3, HGA_WS_BACKWARD_TIERED = 4
+};
 
 /* Bytes of device workspace that hga_route (which = HGA_WS_ROUTE) or
  * hga_attend / hga_route_attend (HGA_WS_ATTEND with everything on the device,
@@ -108,7 +110,8 @@ enum { HGA_WS_ROUTE = 0, HGA_WS_ATTEND = 1, HGA_WS_ATTEND_TIERED = 2, HGA_WS_BAC
  * The tiered figure holds for every split <= seq_len - n_q: it covers chunk
  * flags and slots and an HBM cache as large as the whole host part of K and V
  * (the attention copies each history chunk any query block needs into it once
- * per call). HGA_WS_BACKWARD is the workspace of hga_attend_backward.
+ * per call). HGA_WS_BACKWARD is the workspace of hga_attend_backward with K/V
+ * on the device, HGA_WS_BACKWARD_TIERED the same plus that cache (any split).
  * Returns 0 when no workspace is needed, and (size_t)-1 when the config or
  * sizes are invalid. */
 size_t hga_workspace_size(const hga_config* cfg, int64_t seq_len, int64_t n_q, int32_t which);
@@ -242,19 +245,22 @@ hga_status hga_stream_forward(const hga_config* cfg, const void* q, const void* 
  *              contributions of every query of the call that attends them.
  *              Keys before q_start (the history) receive no gradient.
  * Arguments:
- *   q, k, v, group_idx, n_sel   as hga_attend took them; k and v are device
- *              pointers ([Hkv][seq_len][d], no host tier).
+ *   q, k, v, group_idx, n_sel   as hga_attend took them. With a host tier
+ *              (split > 0) the history chunks the call attends are copied
+ *              once each into an HBM cache in the workspace, as in hga_attend.
  *   out, lse   device, the forward's outputs for these queries (lse required).
  *   dout, dq   device, [Hq][n_q][d] of cfg->dtype.
  *   dk, dv     device, [Hkv][n_q][d] of cfg->dtype: row i is position q_start + i.
- *   workspace  device, at least hga_workspace_size(..., HGA_WS_BACKWARD) bytes.
+ *   workspace  device, at least hga_workspace_size(..., HGA_WS_BACKWARD) bytes
+ *              for split 0, HGA_WS_BACKWARD_TIERED with a host tier.
  * Only bfloat16 is built (HGA_ERR_UNSUPPORTED for float32). The gradient of
  * each key is summed in one workgroup in a fixed order: repeated calls give
  * identical bits. */
 hga_status hga_attend_backward(const hga_config* cfg, const void* q, int64_t q_start, int64_t n_q,
-                               int64_t seq_len, const void* k, const void* v, const int32_t* group_idx,
-                               const int32_t* n_sel, const void* out, const float* lse, const void* dout,
-                               void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes, void* stream);
+                               int64_t seq_len, const hga_tiered* k, const hga_tiered* v,
+                               const int32_t* group_idx, const int32_t* n_sel, const void* out, const float* lse,
+                               const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+                               void* stream);
 
 /* Static description of a status code. */
 const char* hga_status_string(hga_status status);

@@ -31,7 +31,7 @@ def test_every_declared_entry_point_is_exported(lib):
     assert declared == set(B.EXPORTS)
     for name in declared:
         assert hasattr(lib, name)
-    assert hga.hga_version() == 103
+    assert hga.hga_version() == 104
 
 
 def test_status_strings(lib):
@@ -191,6 +191,9 @@ def test_backward_validation():
     nb = 2048 // 64
     need = (4 * 32 * 2048 + 255) // 256 * 256 + (8 * nb * 8 * (2048 // 64 + 1) + 255) // 256 * 256
     assert hga.hga_workspace_size(c, 16384, 2048, hga.HGA_WS_BACKWARD) == need
+    # with a host tier, the host-tier cache follows (the forward's, for any split)
+    assert hga.hga_workspace_size(c, 16384, 2048, hga.HGA_WS_BACKWARD_TIERED) == \
+        need + hga.hga_workspace_size(c, 16384, 2048, hga.HGA_WS_ATTEND_TIERED)
     args = [FAKE] * 11   # k, v, group_idx, n_sel, out, lse, dout, dq, dk, dv, workspace
     def call(cc, a, ws_bytes=need, g=geo):
         return _status(hga.hga_attend_backward, cc, FAKE, *g, *a[:10], a[10], ws_bytes)
@@ -202,4 +205,9 @@ def test_backward_validation():
     assert call(c, args[:10] + [None]) == hga.HGA_ERR_WORKSPACE
     assert call(c, args, need - 1) == hga.HGA_ERR_WORKSPACE
     assert call(c, args, need, (14300, 2048, 16384)) == hga.HGA_ERR_UNSUPPORTED
+    # tiers: same split for k and v, host memory present, workspace with the cache
+    t1, t2 = (FAKE, FAKE, 1024), (FAKE, FAKE, 2048)
+    assert call(c, [t1, t2] + args[2:]) == E
+    assert call(c, [(None, FAKE, 1024), (None, FAKE, 1024)] + args[2:]) == E
+    assert call(c, [t1, t1] + args[2:]) == hga.HGA_ERR_WORKSPACE   # the cache needs more than `need`
     hga.hga_attend_backward(c, None, 16384, 0, 16384, *[None] * 11, 0)   # no queries: a no-op

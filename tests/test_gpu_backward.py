@@ -30,6 +30,7 @@ import hierarchical_sparse_attention_hga_amd as hga
 import oracle
 import synth
 from harness import DEV, bf16_half_spacing, hga_cfg, inputs, to_dev
+from hierarchical_sparse_attention_hga_amd.memory import split_to_host
 from test_gpu_edges import small
 
 pytestmark = pytest.mark.gpu
@@ -37,7 +38,7 @@ pytestmark = pytest.mark.gpu
 MAX_REL, MEAN_REL, MEAN_RMS = 2.0 ** -6, 2.0 ** -9, 2e-3
 
 
-def gpu_forward_backward(cfg, x, dout_bits, q_start=None, seq_len=None):
+def gpu_forward_backward(cfg, x, dout_bits, q_start=None, seq_len=None, split=0):
     c = hga_cfg(cfg)
     L = cfg["L"] if seq_len is None else seq_len
     nq, hkv, d, g, B = cfg["n_q"], cfg["hkv"], cfg["d"], cfg["group"], cfg["q_block"]
@@ -57,10 +58,18 @@ def gpu_forward_backward(cfg, x, dout_bits, q_start=None, seq_len=None):
     dq = torch.empty_like(q)
     dk = torch.empty(hkv, nq, d, dtype=torch.bfloat16, device=DEV)
     dv = torch.empty_like(dk)
-    wsb = hga.hga_workspace_size(c, L, nq, hga.HGA_WS_BACKWARD)
+    pins = []
+    k_t, v_t = k, v
+    if split > 0:   # history rows [0, split) of K and V in pinned host memory
+        kpin, _, k_t = split_to_host(k, split)
+        vpin, _, v_t = split_to_host(v, split)
+        pins = [kpin, vpin]
+    wsb = hga.hga_workspace_size(c, L, nq, hga.HGA_WS_BACKWARD_TIERED if split else hga.HGA_WS_BACKWARD)
     ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
-    hga.hga_attend_backward(c, q, q0, nq, L, k, v, gi, ns, out, lse, dout, dq, dk, dv, ws, wsb)
+    hga.hga_attend_backward(c, q, q0, nq, L, k_t, v_t, gi, ns, out, lse, dout, dq, dk, dv, ws, wsb)
     torch.cuda.synchronize()
+    for p in pins:
+        p.free()
     f = lambda t: t.float().cpu().numpy().astype(np.float64)
     return dict(gi=gi.cpu().numpy(), ns=ns.cpu().numpy(), dq=f(dq), dk=f(dk), dv=f(dv),
                 raw=(dq.view(torch.int16).cpu().numpy(), dk.view(torch.int16).cpu().numpy(),
@@ -152,3 +161,27 @@ def test_backward_is_deterministic():
     b = gpu_forward_backward(cfg, x, dout)
     for ra, rb in zip(a["raw"], b["raw"]):
         assert np.array_equal(ra, rb)
+
+
+@pytest.mark.parametrize("case", ["small", "64k"])
+def test_backward_host_tier_is_identical(case):
+    """K and V of the history in pinned host memory (the pages' training
+    setup): the history chunks the call attends go through the host-tier
+    cache; every gradient is bit-identical to the all-HBM call."""
+    if case == "small":
+        cfg = small(L=2048, n_q=512)
+        x = synth.make_inputs(cfg)
+        splits = [1536, 640]
+    else:
+        full, x0, _ = inputs(3)
+        cfg = dict(full, n_q=256, tier_split=0)
+        q0f = full["L"] - full["n_q"]
+        x = {"q": x0["q"][:, full["L"] - 256 - q0f:], "k": x0["k"], "v": x0["v"]}
+        splits = [full["L"] - 256]
+    dout = seeded_dout(cfg)
+    print(f"[backward host tier] {case}", flush=True)
+    a = gpu_forward_backward(cfg, x, dout)
+    for split in splits:
+        b = gpu_forward_backward(cfg, x, dout, split=split)
+        for ra, rb in zip(a["raw"], b["raw"]):
+            assert np.array_equal(ra, rb), f"split {split}"
