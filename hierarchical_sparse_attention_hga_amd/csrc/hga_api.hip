@@ -295,7 +295,6 @@ hga_status hga_attend_backward(const hga_config* cfg, const void* q, int64_t q_s
   hga::Shape s;
   hga_status st = make_shape(cfg, seq_len, q_start, n_q, &s);
   if (st != HGA_OK) return st;
-  if (s.dtype != HGA_BF16) return fail(HGA_ERR_UNSUPPORTED, "the backward is built for bfloat16 only");
   if (n_q == 0) return ok();
   if (!q || !n_sel || !out || !lse || !dout || !dq || !dk || !dv || (s.kg > 0 && !group_idx))
     return fail(HGA_ERR_INVALID_ARGUMENT, "q, group_idx, n_sel, out, lse, dout, dq, dk and dv must be non-NULL");

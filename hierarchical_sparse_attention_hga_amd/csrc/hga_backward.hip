@@ -53,6 +53,63 @@ struct BwdArgs {
   Shape s;
 };
 
+// For the dK/dV pass: the kept routed tokens of item (b, h) in each chunk of
+// the call's positions, from its ascending run list (first tokens of the
+// kept groups, before any host-tier translation).
+__device__ void write_chunk_masks(const BwdArgs& A, int b, int h, const Plan& P, const int* runs) {
+  const Shape& S = A.s;
+  const int64_t it = (int64_t)b * S.hkv + h;
+  const unsigned long long gmask = S.g >= 64 ? ~0ull : ((1ull << S.g) - 1ull);
+  for (int c = threadIdx.x; c < A.nchunks; c += blockDim.x) {
+    const int first = (int)((A.m0 + c) * kChunk);
+    int lo = 0, hi = P.nrouted;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (runs[mid] < first) lo = mid + 1; else hi = mid;
+    }
+    unsigned long long msk = 0ull;
+    for (int i = lo; i < P.nrouted && runs[i] < first + kChunk; ++i) msk |= gmask << (runs[i] - first);
+    A.cmask[it * A.nchunks + c] = msk;
+  }
+}
+
+// The blocks of [b0, b0 + blockDim.x) that attend chunk m of KV head h, in
+// block order, into lb (block, | kDiagBit for the chunk's own blocks) and
+// lmask (the chunk's tokens in the block's token set); returns their count.
+constexpr int kDiagBit = 1 << 30;
+__device__ int list_attending(const BwdArgs& A, int h, int64_t m, int b0, int* lb, unsigned long long* lmask,
+                              int* scan) {
+  const Shape& S = A.s;
+  int code = -1;
+  unsigned long long msk = 0ull;
+  const int b = b0 + threadIdx.x;
+  if (b < S.nb) {
+    const int64_t s = S.q0 + (int64_t)b * S.B, ms = s / kChunk;
+    if (m == ms) {
+      code = b | kDiagBit;
+      msk = ~0ull;
+    } else if (m < ms) {
+      int64_t a, bb;
+      fixed_windows(ms, S.sink_chunks, S.local_chunks, &a, &bb);
+      if (m < a || m >= bb) {
+        code = b;
+        msk = ~0ull;
+      } else {
+        msk = A.cmask[((int64_t)b * S.hkv + h) * A.nchunks + (m - A.m0)];
+        if (msk) code = b;
+      }
+    }
+  }
+  int tot;
+  const int pos = block_scan<false>(code >= 0 ? 1 : 0, scan, &tot);
+  if (code >= 0) {
+    lb[pos] = code;
+    lmask[pos] = msk;
+  }
+  __syncthreads();
+  return tot;
+}
+
 // ------------------------------------------------------------ dQ
 template <int D>
 struct BwdQSmem {
@@ -75,23 +132,7 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dq_kernel(BwdArgs A) {
   int b, h, z;
   item_of_block(S, A.wg_per_item, &b, &h, &z);
   const Plan P = make_plan(S, b, h, A.gidx, A.nsel, sm.runs, sm.scan, kMaxRoutedAttn);
-  if (z == 0) {
-    // for bwd_dkv_kernel: the item's kept tokens in each chunk of the call's
-    // positions, from the ascending run list (first tokens of the groups)
-    const int64_t it = (int64_t)b * S.hkv + h;
-    const unsigned long long gmask = S.g >= 64 ? ~0ull : ((1ull << S.g) - 1ull);
-    for (int c = threadIdx.x; c < A.nchunks; c += kAttnThreads) {
-      const int first = (int)((A.m0 + c) * kChunk);
-      int lo = 0, hi = P.nrouted;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (sm.runs[mid] < first) lo = mid + 1; else hi = mid;
-      }
-      unsigned long long msk = 0ull;
-      for (int i = lo; i < P.nrouted && sm.runs[i] < first + kChunk; ++i) msk |= gmask << (sm.runs[i] - first);
-      A.cmask[it * A.nchunks + c] = msk;
-    }
-  }
+  if (z == 0) write_chunk_masks(A, b, h, P, sm.runs);
   if (kTiered) {   // rows of the history come from the host-tier cache
     __syncthreads();   // the masks above read the token runs
     translate_plan(A.kv.split, A.tc.nch, A.tc.slot, h, P, sm.runs, sm.runs + kMaxRoutedAttn);
@@ -275,7 +316,6 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dq_kernel(BwdArgs A) {
 constexpr int kKVThreads = 256;
 constexpr int kKVWaves = kKVThreads / 64;
 constexpr int kKVListCap = kKVThreads;   // attending blocks listed per pass
-constexpr int kDiagBit = 1 << 30;        // list entry flag: the block lies in the chunk
 constexpr int kKVStages = 4;             // query tiles in the LDS ring (up to 3 in flight)
 
 template <int D>
@@ -390,34 +430,7 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkv_kernel(BwdArgs A) {
   };
 
   for (int b0 = 0; b0 < S.nb; b0 += kKVListCap) {
-    // the blocks of [b0, b0 + cap) that attend chunk m, in block order
-    int code = -1;
-    unsigned long long msk = 0ull;
-    const int b = b0 + tid;
-    if (b < S.nb) {
-      const int64_t s = S.q0 + (int64_t)b * S.B, ms = s / kChunk;
-      if (m == ms) {
-        code = b | kDiagBit;
-        msk = ~0ull;
-      } else if (m < ms) {
-        int64_t a, bb;
-        fixed_windows(ms, S.sink_chunks, S.local_chunks, &a, &bb);
-        if (m < a || m >= bb) {
-          code = b;
-          msk = ~0ull;
-        } else {
-          msk = A.cmask[((int64_t)b * S.hkv + h) * A.nchunks + (m - A.m0)];
-          if (msk) code = b;
-        }
-      }
-    }
-    int tot;
-    const int pos = block_scan<false>(code >= 0 ? 1 : 0, sm.scan, &tot);
-    if (code >= 0) {
-      sm.lb[pos] = code;
-      sm.lmask[pos] = msk;
-    }
-    __syncthreads();
+    const int tot = list_attending(A, h, m, b0, sm.lb, sm.lmask, sm.scan);
     const int T = tot * ntl;
     // tiles 0 .. kKVStages - 2 in flight first; at iteration u, once tile u
     // has landed (every newer issued tile may still be pending), tile
@@ -524,6 +537,207 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkv_kernel(BwdArgs A) {
     }
 }
 
+// ------------------------------------------------------------ float32 (SIMT)
+// The same two passes for float32 inputs, as the float32 forward computes:
+// TPR lanes per query row, each owning D / TPR dimensions, and the token set
+// in 32-token LDS sub-tiles.
+template <int D, bool kTiered>
+__global__ __launch_bounds__(256) void bwd_dq_f32_kernel(BwdArgs A) {
+  constexpr int NT = 256;
+  constexpr int TPR = D <= 32 ? 1 : D / 32;   // lanes per row
+  constexpr int DPT = D / TPR;                // dims per lane
+  constexpr int ROWS = NT / TPR;              // rows per workgroup
+  constexpr int HALF = 32;                    // tokens per LDS sub-tile
+  __shared__ __align__(16) float sK[HALF * D];
+  __shared__ __align__(16) float sV[HALF * D];
+  __shared__ int sRuns[kMaxRouted + kMaxFixedTiered];
+  __shared__ int sScan[16];
+  const Shape& S = A.s;
+  int b, h, z;
+  item_of_block(S, A.wg_per_item, &b, &h, &z);
+  const Plan P = make_plan(S, b, h, A.gidx, A.nsel, sRuns, sScan, kMaxRouted);
+  if (z == 0) write_chunk_masks(A, b, h, P, sRuns);
+  if (kTiered) {
+    __syncthreads();
+    translate_plan(A.kv.split, A.tc.nch, A.tc.slot, h, P, sRuns, sRuns + kMaxRouted);
+  }
+  const int64_t per_head = S.kvs - A.kv.split;
+  const float* kdev = static_cast<const float*>(A.kv.k_dev) + (int64_t)h * per_head * D;
+  const float* vdev = static_cast<const float*>(A.kv.v_dev) + (int64_t)h * per_head * D;
+  const float* kc = static_cast<const float*>(A.tc.k_cache);
+  const float* vc = static_cast<const float*>(A.tc.v_cache);
+  const int tid = threadIdx.x;
+  const int row = z * ROWS + tid / TPR;
+  const int part = tid % TPR;
+  const bool active = row < S.G * S.B;
+  const int head = h * S.G + row / S.B;
+  const int qi = row % S.B;
+  const int64_t qrow = (int64_t)head * S.qs + (int64_t)b * S.B + qi;
+
+  float q[DPT], g[DPT], dq[DPT];
+  float dpart = 0.0f;
+#pragma unroll
+  for (int e = 0; e < DPT; ++e) {
+    const int64_t at = qrow * D + part * DPT + e;
+    q[e] = active ? static_cast<const float*>(A.q)[at] : 0.0f;
+    g[e] = active ? static_cast<const float*>(A.dout)[at] : 0.0f;
+    dpart = fmaf(g[e], active ? static_cast<const float*>(A.out)[at] : 0.0f, dpart);
+    dq[e] = 0.0f;
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) dpart += __shfl_xor(dpart, off, TPR);
+  const float dterm = dpart;
+  if (active && part == 0) A.dd[qrow] = dterm;
+  const float lse2 = active ? A.lse[qrow] * kLog2e : 0.0f;
+  const float sl2 = S.scale * kLog2e;
+
+  for (int t = 0; t < P.ntiles; ++t) {
+    const bool diag = t == P.ntiles - 1;
+    const int lim = tile_limit(P, S.g, t);
+    for (int half = 0; half < 2; ++half) {
+      __syncthreads();
+      for (int i = tid; i < HALF * (D / 4); i += NT) {
+        const int sl = i / (D / 4), e4 = i % (D / 4);
+        const int slot = half * HALF + sl;
+        float4 kx = {0.f, 0.f, 0.f, 0.f}, vx = {0.f, 0.f, 0.f, 0.f};
+        const int src = tile_src(P, sRuns, sRuns + kMaxRouted, S.g, kTiered, A.kv.split, t, slot);
+        if (src >= 0) {
+          kx = *reinterpret_cast<const float4*>(src_ptr(kdev, kc, src, D) + 4 * e4);
+          vx = *reinterpret_cast<const float4*>(src_ptr(vdev, vc, src, D) + 4 * e4);
+        }
+        *reinterpret_cast<float4*>(&sK[sl * D + 4 * e4]) = kx;
+        *reinterpret_cast<float4*>(&sV[sl * D + 4 * e4]) = vx;
+      }
+      __syncthreads();
+      for (int sl = 0; sl < HALF; ++sl) {
+        float sacc = 0.0f, pacc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < DPT; ++e) {
+          sacc = fmaf(q[e], sK[sl * D + part * DPT + e], sacc);
+          pacc = fmaf(g[e], sV[sl * D + part * DPT + e], pacc);
+        }
+#pragma unroll
+        for (int off = TPR / 2; off > 0; off >>= 1) {
+          sacc += __shfl_xor(sacc, off, TPR);
+          pacc += __shfl_xor(pacc, off, TPR);
+        }
+        const int slot = half * HALF + sl;
+        const bool vis = slot < lim && !(diag && slot > P.off + qi);
+        const float p = vis ? exp2f(fmaf(sacc, sl2, -lse2)) : 0.0f;
+        const float ds = p * (pacc - dterm);
+#pragma unroll
+        for (int e = 0; e < DPT; ++e) dq[e] = fmaf(ds, sK[sl * D + part * DPT + e], dq[e]);
+      }
+    }
+  }
+  if (active) {
+    float* op = static_cast<float*>(A.dq) + qrow * D + part * DPT;
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) op[e] = dq[e] * S.scale;
+  }
+}
+
+// Per (KV head, chunk of the call's positions): 4 lanes per token of the
+// chunk, each owning D / 4 dimensions of its key, value and their gradients;
+// the query rows of every attending block stream through LDS 32 at a time.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dkv_f32_kernel(BwdArgs A) {
+  constexpr int TPT = 4;               // lanes per token
+  constexpr int DPT = D / TPT;
+  constexpr int RT = 32;               // query rows per LDS batch
+  static_assert(D % TPT == 0 && kKVThreads == kChunk * TPT, "lane layout");
+  __shared__ __align__(16) float sQ[RT * D];
+  __shared__ __align__(16) float sG[RT * D];
+  __shared__ float sL[RT], sD[RT];
+  __shared__ int lb[kKVListCap];
+  __shared__ unsigned long long lmask[kKVListCap];
+  __shared__ int scan[16];
+  const Shape& S = A.s;
+  const int h = (int)(blockIdx.x / A.nchunks);
+  const int64_t m = A.m0 + blockIdx.x % A.nchunks;
+  const int64_t lq = S.q0 + S.nq;
+  const int tid = threadIdx.x;
+  const int tok = tid / TPT, part = tid % TPT;
+  const int64_t tpos = m * kChunk + tok;
+  float k[DPT], v[DPT], dk[DPT], dv[DPT];
+  const int64_t drow = (int64_t)h * (S.kvs - A.kv.split) + (tpos - A.kv.split);
+#pragma unroll
+  for (int e = 0; e < DPT; ++e) {
+    k[e] = tpos < lq ? static_cast<const float*>(A.kv.k_dev)[drow * D + part * DPT + e] : 0.0f;
+    v[e] = tpos < lq ? static_cast<const float*>(A.kv.v_dev)[drow * D + part * DPT + e] : 0.0f;
+    dk[e] = dv[e] = 0.0f;
+  }
+  const int nrows = S.G * S.B;
+  const float sl2 = S.scale * kLog2e;
+  const float* qg = static_cast<const float*>(A.q);
+  const float* gg = static_cast<const float*>(A.dout);
+  for (int b0 = 0; b0 < S.nb; b0 += kKVListCap) {
+    const int tot = list_attending(A, h, m, b0, lb, lmask, scan);
+    for (int e = 0; e < tot; ++e) {
+      const bool diag = (lb[e] & kDiagBit) != 0;
+      const int bq = lb[e] & (kDiagBit - 1);
+      const int64_t sq = S.q0 + (int64_t)bq * S.B;
+      const bool tok_ok = ((lmask[e] >> tok) & 1ull) && tpos < lq;
+      for (int r0 = 0; r0 < nrows; r0 += RT) {
+        __syncthreads();
+        for (int i = tid; i < RT * (D / 4); i += kKVThreads) {
+          const int rr = i / (D / 4), e4 = i % (D / 4);
+          const int ir = r0 + rr < nrows ? r0 + rr : 0;
+          const int64_t src = (int64_t)(h * S.G + ir / S.B) * S.qs + (int64_t)bq * S.B + ir % S.B;
+          *reinterpret_cast<float4*>(&sQ[rr * D + 4 * e4]) = *reinterpret_cast<const float4*>(qg + src * D + 4 * e4);
+          *reinterpret_cast<float4*>(&sG[rr * D + 4 * e4]) = *reinterpret_cast<const float4*>(gg + src * D + 4 * e4);
+          if (e4 == 0) {
+            sL[rr] = A.lse[src] * kLog2e;
+            sD[rr] = A.dd[src];
+          }
+        }
+        __syncthreads();
+        const int nr = nrows - r0 < RT ? nrows - r0 : RT;
+        for (int rr = 0; rr < nr; ++rr) {
+          float sacc = 0.0f, pacc = 0.0f;
+#pragma unroll
+          for (int e2 = 0; e2 < DPT; ++e2) {
+            sacc = fmaf(k[e2], sQ[rr * D + part * DPT + e2], sacc);
+            pacc = fmaf(v[e2], sG[rr * D + part * DPT + e2], pacc);
+          }
+#pragma unroll
+          for (int off = TPT / 2; off > 0; off >>= 1) {
+            sacc += __shfl_xor(sacc, off, TPT);
+            pacc += __shfl_xor(pacc, off, TPT);
+          }
+          const int ir = r0 + rr;
+          const bool vis = tok_ok && (!diag || tpos <= sq + ir % S.B);
+          const float p = vis ? exp2f(fmaf(sacc, sl2, -sL[rr])) : 0.0f;
+          const float ds = vis ? p * (pacc - sD[rr]) : 0.0f;
+#pragma unroll
+          for (int e2 = 0; e2 < DPT; ++e2) {
+            dk[e2] = fmaf(ds, sQ[rr * D + part * DPT + e2], dk[e2]);
+            dv[e2] = fmaf(p, sG[rr * D + part * DPT + e2], dv[e2]);
+          }
+        }
+      }
+    }
+    __syncthreads();   // the list is rebuilt by the next pass
+  }
+  if (tpos < S.q0 || tpos >= lq) return;
+  float* ko = static_cast<float*>(A.dk) + ((int64_t)h * S.nq + (tpos - S.q0)) * D + part * DPT;
+  float* vo = static_cast<float*>(A.dv) + ((int64_t)h * S.nq + (tpos - S.q0)) * D + part * DPT;
+#pragma unroll
+  for (int e = 0; e < DPT; ++e) {
+    ko[e] = dk[e] * S.scale;
+    vo[e] = dv[e];
+  }
+}
+
+template <int D>
+hipError_t launch_backward_f32(const BwdArgs& A, bool tiered, int64_t items, hipStream_t st) {
+  const dim3 gq((unsigned)(items * A.wg_per_item)), gkv((unsigned)(A.s.hkv * A.nchunks));
+  if (tiered) bwd_dq_f32_kernel<D, true><<<gq, dim3(256), 0, st>>>(A);
+  else bwd_dq_f32_kernel<D, false><<<gq, dim3(256), 0, st>>>(A);
+  bwd_dkv_f32_kernel<D><<<gkv, dim3(kKVThreads), 0, st>>>(A);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // D per query row, then the kept-token masks per (block, KV head, chunk of
@@ -545,8 +759,13 @@ hipError_t launch_attend_backward(const Shape& s, const void* q, const KVSrc& kv
   char* ws = static_cast<char*>(workspace);
   A.dd = reinterpret_cast<float*>(ws);
   A.cmask = reinterpret_cast<unsigned long long*>(ws + a256(4 * (size_t)s.hq * s.nq));
-  const int waves = (s.G * s.B + 31) / 32;
-  A.wg_per_item = (waves + kAttnWaves - 1) / kAttnWaves;
+  if (s.dtype == HGA_BF16) {
+    const int waves = (s.G * s.B + 31) / 32;
+    A.wg_per_item = (waves + kAttnWaves - 1) / kAttnWaves;
+  } else {
+    const int rows = 256 / (s.d <= 32 ? 1 : s.d / 32);
+    A.wg_per_item = (s.G * s.B + rows - 1) / rows;
+  }
   A.m0 = s.q0 / kChunk;
   A.nchunks = (int)((s.q0 + s.nq - 1) / kChunk - A.m0 + 1);
   const bool tiered = kv.split > 0;
@@ -555,6 +774,17 @@ hipError_t launch_attend_backward(const Shape& s, const void* q, const KVSrc& kv
     if (e != hipSuccess) return e;
   }
   const int64_t items = s.nb * s.hkv;
+  if (s.dtype == HGA_F32) {
+    switch (s.d) {
+      case 4: return launch_backward_f32<4>(A, tiered, items, st);
+      case 8: return launch_backward_f32<8>(A, tiered, items, st);
+      case 16: return launch_backward_f32<16>(A, tiered, items, st);
+      case 32: return launch_backward_f32<32>(A, tiered, items, st);
+      case 64: return launch_backward_f32<64>(A, tiered, items, st);
+      case 128: return launch_backward_f32<128>(A, tiered, items, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
   const dim3 gq((unsigned)(items * A.wg_per_item)), gkv((unsigned)(s.hkv * A.nchunks));
   if (s.d == 128) {
     if (tiered) bwd_dq_kernel<128, true><<<gq, dim3(kAttnThreads), 0, st>>>(A);

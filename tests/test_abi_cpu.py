@@ -197,7 +197,7 @@ def test_backward_validation():
     args = [FAKE] * 11   # k, v, group_idx, n_sel, out, lse, dout, dq, dk, dv, workspace
     def call(cc, a, ws_bytes=need, g=geo):
         return _status(hga.hga_attend_backward, cc, FAKE, *g, *a[:10], a[10], ws_bytes)
-    assert call(cfg(dtype="f32", head_dim=64), args) == hga.HGA_ERR_UNSUPPORTED
+    assert call(cfg(dtype="f32", head_dim=96), args) == hga.HGA_ERR_UNSUPPORTED   # head_dim not built
     for i in range(10):
         a = list(args)
         a[i] = None

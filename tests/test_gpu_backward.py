@@ -8,7 +8,7 @@ and LSE, draws a seeded output gradient, runs hga_attend_backward, and compares
 dQ (every query row) and dK, dV (the call's own positions) with the float64
 oracle on the same bf16 inputs and the same kept groups.
 
-Tolerance (bf16 gradients), derived from the arithmetic: the kernels round P
+Tolerance (bf16 gradients; float32 below), derived from the arithmetic: the kernels round P
 and dS to bfloat16 as MFMA operands (relative 2^-9 each), take D = dO . O from
 the forward's bfloat16 output (O off by 2^-9 relative, its weights by 2^-9
 more), and store the gradients in bfloat16. Each gradient element is a sum of
@@ -36,6 +36,10 @@ from test_gpu_edges import small
 pytestmark = pytest.mark.gpu
 
 MAX_REL, MEAN_REL, MEAN_RMS = 2.0 ** -6, 2.0 ** -9, 2e-3
+# float32: every rounding is 2^-24 relative and exp2f is within a few ulp; the
+# bars keep the same shape at 2^-14 of the companion, 2^-18 of the mean
+# companion and 1e-5 of the RMS
+BARS = {"bf16": (MAX_REL, MEAN_REL, MEAN_RMS), "f32": (2.0 ** -14, 2.0 ** -18, 1e-5)}
 
 
 def gpu_forward_backward(cfg, x, dout_bits, q_start=None, seq_len=None, split=0):
@@ -44,7 +48,8 @@ def gpu_forward_backward(cfg, x, dout_bits, q_start=None, seq_len=None, split=0)
     nq, hkv, d, g, B = cfg["n_q"], cfg["hkv"], cfg["d"], cfg["group"], cfg["q_block"]
     q0 = L - nq if q_start is None else q_start
     nb = nq // B
-    q, k, v = to_dev(x["q"], "bf16"), to_dev(x["k"], "bf16"), to_dev(x["v"], "bf16")
+    dt = cfg["dtype"]
+    q, k, v = to_dev(x["q"], dt), to_dev(x["k"], dt), to_dev(x["v"], dt)
     gs = torch.empty(hkv, L // g, d, device=DEV)
     cs = torch.empty(hkv, L // 64, d, device=DEV)
     ci = torch.empty(nb, hkv, max(cfg["top_chunks"], 1), dtype=torch.int32, device=DEV)
@@ -54,9 +59,9 @@ def gpu_forward_backward(cfg, x, dout_bits, q_start=None, seq_len=None, split=0)
     lse = torch.empty(cfg["hq"], nq, device=DEV)
     hga.hga_build_summaries(c, k, L, gs, cs)
     hga.hga_route_attend(c, q, q0, nq, L, cs, gs, k, v, ci, gi, ns, out, lse)
-    dout = to_dev(dout_bits, "bf16")
+    dout = to_dev(dout_bits, dt)
     dq = torch.empty_like(q)
-    dk = torch.empty(hkv, nq, d, dtype=torch.bfloat16, device=DEV)
+    dk = torch.empty(hkv, nq, d, dtype=q.dtype, device=DEV)
     dv = torch.empty_like(dk)
     pins = []
     k_t, v_t = k, v
@@ -71,39 +76,44 @@ def gpu_forward_backward(cfg, x, dout_bits, q_start=None, seq_len=None, split=0)
     for p in pins:
         p.free()
     f = lambda t: t.float().cpu().numpy().astype(np.float64)
+    iv = torch.int16 if dt == "bf16" else torch.int32
     return dict(gi=gi.cpu().numpy(), ns=ns.cpu().numpy(), dq=f(dq), dk=f(dk), dv=f(dv),
-                raw=(dq.view(torch.int16).cpu().numpy(), dk.view(torch.int16).cpu().numpy(),
-                     dv.view(torch.int16).cpu().numpy()))
+                raw=(dq.view(iv).cpu().numpy(), dk.view(iv).cpu().numpy(), dv.view(iv).cpu().numpy()))
 
 
 def seeded_dout(cfg, seed=7):
+    """Output gradient in the storage format of cfg's dtype (bf16 bits or float32)."""
     rng = np.random.default_rng([synth.SEED, 90, seed])
-    return synth.f32_to_bf16_bits(rng.standard_normal((cfg["hq"], cfg["n_q"], cfg["d"])).astype(np.float32))
+    g = rng.standard_normal((cfg["hq"], cfg["n_q"], cfg["d"])).astype(np.float32)
+    return synth.f32_to_bf16_bits(g) if cfg["dtype"] == "bf16" else g
 
 
 def check_grads(cfg, x, gpu, dout_bits, q_start=None):
     L, nq = cfg["L"], cfg["n_q"]
     q0 = L - nq if q_start is None else q_start
     sub = dict(cfg, L=q0 + nq)   # the oracle's sequence ends at the last query
-    f = {n: synth.to_f64(x[n], "bf16") for n in ("q", "k", "v")}
+    dt = cfg["dtype"]
+    f = {n: synth.to_f64(x[n], dt) for n in ("q", "k", "v")}
     k64, v64 = f["k"][:, :q0 + nq], f["v"][:, :q0 + nq]
     kg = max(cfg["top_groups"], 1)
+    max_rel, mean_rel, mean_rms = BARS[dt]
     dq, dk, dv, qa, ka, va = oracle.attend_backward(
-        sub, f["q"], k64, v64, synth.to_f64(dout_bits, "bf16"),
+        sub, f["q"], k64, v64, synth.to_f64(dout_bits, dt),
         gpu["gi"][..., :kg] if cfg["top_groups"] else gpu["gi"][..., :0], gpu["ns"][..., 1], with_abs=True)
     sl = slice(q0, q0 + nq)
     res = {}
     for name, got, ref, comp in (("dq", gpu["dq"], dq, qa), ("dk", gpu["dk"], dk[:, sl], ka[:, sl]),
                                  ("dv", gpu["dv"], dv[:, sl], va[:, sl])):
         assert np.isfinite(got).all(), name
-        err = np.maximum(np.abs(got - ref) - bf16_half_spacing(got), 0.0)
+        own = bf16_half_spacing(got) if dt == "bf16" else np.abs(np.spacing(got.astype(np.float32))) / 2
+        err = np.maximum(np.abs(got - ref) - own, 0.0)
         worst = float((err / np.maximum(comp, 1e-30)).max())
         mean = float(err.mean() / comp.mean())
         rms = float(np.sqrt(np.mean(ref ** 2)))
         res[name] = (worst, mean, float(err.mean()) / rms, rms)
-        assert worst <= MAX_REL, f"{name}: an element's error is {worst:.3g} of its companion"
-        assert mean <= MEAN_REL, f"{name}: mean error {mean:.3g} of the mean companion"
-        assert err.mean() <= MEAN_RMS * rms, f"{name}: mean error {err.mean() / rms:.3g} of the RMS"
+        assert worst <= max_rel, f"{name}: an element's error is {worst:.3g} of its companion"
+        assert mean <= mean_rel, f"{name}: mean error {mean:.3g} of the mean companion"
+        assert err.mean() <= mean_rms * rms, f"{name}: mean error {err.mean() / rms:.3g} of the RMS"
     print("  " + "  ".join(f"{n}: worst={v[0]:.2e} mean={v[1]:.2e} mean/rms={v[2]:.2e} rms={v[3]:.3g}"
                            for n, v in res.items()), flush=True)
     return res
@@ -117,6 +127,8 @@ CASES = {
     "no_budget": dict(top_chunks=0, top_groups=0),
     "d64": dict(d=64),
     "group4": dict(group=4, top_groups=20),
+    "f32": dict(dtype="f32", d=64, rope_theta=None),
+    "f32_block16_d32": dict(dtype="f32", d=32, q_block=16, n_q=496, rope_theta=None),
 }
 
 
@@ -185,3 +197,22 @@ def test_backward_host_tier_is_identical(case):
         b = gpu_forward_backward(cfg, x, dout, split=split)
         for ra, rb in zip(a["raw"], b["raw"]):
             assert np.array_equal(ra, rb), f"split {split}"
+
+
+def test_backward_float32_tiny_workload():
+    """The tiny float32 workload (one query head, head_dim 64), every position
+    querying: the float32 SIMT kernels."""
+    cfg, x, _ = inputs(0)
+    print("[backward] tiny-fp32-1k", flush=True)
+    dout = seeded_dout(cfg)
+    check_grads(cfg, x, gpu_forward_backward(cfg, x, dout), dout)
+
+
+def test_backward_float32_host_tier_is_identical():
+    cfg = small(L=2048, n_q=512, dtype="f32", d=64, rope_theta=None)
+    x = synth.make_inputs(cfg)
+    dout = seeded_dout(cfg)
+    a = gpu_forward_backward(cfg, x, dout)
+    b = gpu_forward_backward(cfg, x, dout, split=1024)
+    for ra, rb in zip(a["raw"], b["raw"]):
+        assert np.array_equal(ra, rb)
