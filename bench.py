@@ -152,8 +152,8 @@ class Workload:
         self.k_full = k
         self.split = split
         # one kernel exactly where hga_route_attend fuses (bf16, K/V on the
-        # device, at most 4 query heads per KV head); otherwise the two calls
-        # are timed apart
+        # device, at most 256 query rows per item: G <= 4 for blocks of 64);
+        # otherwise the two calls are timed apart
         if fused is None:
             fused = cfg["dtype"] == "bf16" and split == 0 and cfg["hq"] // hkv <= 4
         self.fused = fused
