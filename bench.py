@@ -544,6 +544,61 @@ def backward_line(cfg_id, steps, warmup):
                          "traffic_unit": "HBM bytes per call (both kernels)", "algorithmic_flops": flops}}
 
 
+def route_bytes(cfg, n_sel):
+    """HBM bytes of hga_route over every (block, KV head) of the workload: the
+    block's G x 64 query rows, the chunk summaries it scores (all candidates,
+    when the chunk stage selects), the group summaries of its kept chunks
+    (when the group stage selects), and its index rows."""
+    d, G, hkv, g = cfg["d"], cfg["hq"] // cfg["hkv"], cfg["hkv"], cfg["group"]
+    esz = 2 if cfg["dtype"] == "bf16" else 4
+    nb = cfg["n_q"] // 64
+    q0 = cfg["L"] - cfg["n_q"]
+    ns = n_sel.reshape(nb, hkv, 2)
+    rows = 0
+    for b in range(nb):
+        ms = (q0 + 64 * b) // 64
+        a = min(cfg["sink"] // 64, ms)
+        bb = max(ms - cfg["local"] // 64, a)
+        for h in range(hkv):
+            nsc, nsg = int(ns[b, h, 0]), int(ns[b, h, 1])
+            rows += (bb - a if 0 < nsc < bb - a else 0) + (64 // g * nsc if 0 < nsg < 64 // g * nsc else 0)
+    return (nb * hkv * G * 64 * d * esz + 4.0 * d * rows
+            + 4 * nb * hkv * (cfg["top_chunks"] + cfg["top_groups"] + 2))
+
+
+def stage_hbm(cfg_id, reps=20):
+    """Achieved HBM rates of the summary build (every chunk of the sequence)
+    and of the router alone: algorithmic bytes over the mean of reps
+    back-to-back calls (HIP events on the launch stream around all of them)."""
+    import torch
+    w = Workload(cfg_id)
+    cfg, hga = w.cfg, w.hga
+
+    def mean_us(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+    sum_us = mean_us(lambda: hga.hga_build_summaries(w.c, w.k_full, w.L, w.gs, w.cs))
+    route_us = mean_us(lambda: hga.hga_route(w.c, w.q, w.q0, w.nq, w.L, w.cs, w.gs_t, w.ci, w.gi, w.ns))
+    esz = 2 if cfg["dtype"] == "bf16" else 4
+    d, hkv, L = cfg["d"], cfg["hkv"], cfg["L"]
+    sum_bytes = hkv * L * d * esz + 4.0 * hkv * (L // cfg["group"] + L // 64) * d
+    r_bytes = route_bytes(cfg, w.ns.cpu().numpy())
+    w.free()
+    out = {}
+    for name, byts, us in (("summaries_full_build", sum_bytes, sum_us), ("routing", r_bytes, route_us)):
+        out[name] = {"us": us, "algorithmic_bytes": byts, "achieved_GBps": byts / (us * 1e-6) / 1e9,
+                     "frac_of_hbm_peak": byts / (us * 1e-6) / PEAK_HBM}
+    return out
+
+
 def full_summary_us(cfg_id, reps=20):
     """Mean time of hga_build_summaries over every chunk of workload cfg_id's
     sequence (HIP events on the launch stream)."""
@@ -626,6 +681,7 @@ def main():
                 "note": "the step with the summaries of every chunk of the sequence rebuilt (history included) "
                         "instead of only the chunks the step's positions close"}
         half = max(args.steps // 2, 5)
+        extra["stage_hbm"] = stage_hbm(args.config)
         if main_r.fused:
             sep = measure(args.config, half, args.warmup, fused=False)
             extra["separate_calls"] = {
