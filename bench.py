@@ -17,7 +17,8 @@ The workload is the 16,384-token training-segment shape (Qwen3-8B heads:
 14,336-token history, top-16 chunks, top-64 groups, sink 64, local 128).
 The same line also reports the 65,536-token Qwen3-30B-A3B-shaped layer with
 its history in HBM and, separately, with its history in pinned host memory
-(that rate includes the PCIe transfer of the routed set).
+(that rate includes the PCIe transfer of the routed set), and the
+131,072-token long-evaluation layer with its history in pinned host memory.
 
 It also reports the backward of the attention over the 16K workload's
 2,048-query active segment (hga_attend_backward: dQ, and dK, dV of the
@@ -617,6 +618,11 @@ def full_summary_us(cfg_id, reps=20):
     return e0.elapsed_time(e1) / reps * 1e3
 
 
+def synth_config(cfg_id):
+    import synth
+    return synth.config(cfg_id)
+
+
 def measure(cfg_id, steps, warmup, split=0, fused=None):
     w = Workload(cfg_id, split, fused)
     wall, stage = w.run(steps, warmup)
@@ -701,6 +707,15 @@ def main():
                         "needs crosses the host link once per step into an HBM cache, then attention",
                 "host_link_bytes_per_step": rh.host_bytes,
                 "stages_us_mean": rh.stages("mean")}
+            r4 = measure(4, 24, 2, split=synth_config(4)["tier_split"])
+            extra["128k_host_tier_pcie_inclusive"] = {
+                "value": 24 * r4.cfg["n_q"] / r4.wall, "unit": "query-tokens/s",
+                "note": "the 131,072-token long-evaluation layer (Qwen3-8B heads, top-64 chunks, top-512 groups, "
+                        "64 planted needle groups per head): history K/V and group summaries in pinned host "
+                        "memory, the final 2,048 queries in HBM; each history chunk any block needs crosses "
+                        "the host link once per step",
+                "host_link_bytes_per_step": r4.host_bytes,
+                "stages_us_mean": r4.stages("mean")}
         extra["backward_16k_segment"] = backward_line(2, 80, 5)
         extra["decode_16k_batch64"] = decode_line(2, 64, 80, 5)
         extra["decode_16k_single_sequence"] = decode_line(2, 1, 80, 5)
