@@ -39,11 +39,6 @@
 namespace hga {
 namespace {
 
-
-
-// Attention of item (b, h), workgroup slot z, over the token set of plan P
-// (runs in sm.runs). The caller has already issued the loads of the first
-// pre_tiles tiles (at most kAttnStages), tile t into stage t.
 // Queries of this lane's column of item (b, h), slot z, as MFMA B operands
 // (d = 16 ks + 8 hl + e); zero on the columns past the item's rows.
 template <int D>
@@ -65,6 +60,10 @@ __device__ inline void load_q_operands(const AttnArgs& A, int b, int h, int z, b
   }
 }
 
+// Attention of item (b, h), workgroup slot z, over the token set of plan P
+// (runs in sm.runs). The caller has loaded the queries (qpre) and already
+// issued the loads of the first pre_tiles tiles (at most kAttnStages), tile t
+// into stage t.
 template <int D, bool kTiered>
 __device__ __attribute__((always_inline)) void attend_bf16_body(const AttnArgs& A, int b, int h, int z,
                                                                 const Plan& P, AttnSmem<D>& sm, int pre_tiles,
@@ -94,14 +93,10 @@ __device__ __attribute__((always_inline)) void attend_bf16_body(const AttnArgs& 
   const int qi = row & (S.B - 1);            // position within the block
   const int64_t qrow = (int64_t)b * S.B + qi;  // row of Q / O
 
-  // queries of this lane's column (loaded by the caller when qpre is given)
+  // queries of this lane's column, loaded by the caller (load_q_operands)
   bf16x8 qf[D / 16];
-  if (qpre) {
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = qpre[ks];
-  } else {
-    load_q_operands<D>(A, b, h, z, qf);
-  }
+  for (int ks = 0; ks < D / 16; ++ks) qf[ks] = qpre[ks];
 
   const int lg = __ffs(S.g) - 1;
   const KVRows kv = kv_rows<D, kTiered>(A, h);
@@ -127,7 +122,7 @@ __device__ __attribute__((always_inline)) void attend_bf16_body(const AttnArgs& 
   const int dlim = P.dlim;
   auto issue = [&](int t) {
     const uint32_t off = (uint32_t)((t % kAttnStages) * kChunk * D * 2);
-    issue_tile<D>(kv, lds_addr(&sm.k[0][0]) + off, lds_addr(&sm.v[0][0]) + off, [&](int i, int sl) -> int {
+    issue_tile<D, kTiered>(kv, lds_addr(&sm.k[0][0]) + off, lds_addr(&sm.v[0][0]) + off, [&](int i, int sl) -> int {
       if (t < P.nfix) return kTiered ? raw[i] + sl : (int)((t < P.a ? t : P.bb + (t - P.a)) * kChunk) + sl;
       if (t < P.nfix + P.nrt) return run_of(t, sl) < P.nrouted ? raw[i] + (sl & ((1 << lg) - 1)) : 0;
       return diag0 + (sl < dlim ? sl : 0);   // empty slots past the block read the chunk's first row
@@ -277,11 +272,17 @@ __device__ __attribute__((always_inline)) void attend_bf16_body(const AttnArgs& 
     }
   }
 
+  // Output: each wave writes its normalized 32 x D tile to LDS (the stage
+  // ring is free once every wave has left the loop), then stores it back
+  // row by row, 64 / (D / 8) whole rows per instruction, so every store
+  // writes contiguous rows instead of 16 bytes of each of 32 rows. Pieces of
+  // 16 bytes are XOR-swizzled by row in LDS (conflict-free both ways).
+  static_assert(kAttnWaves * 32 * RB <= sizeof(sm.k) + sizeof(sm.v), "output tiles fit in the stage ring");
+  __syncthreads();
   if (active) {
     const float l_tot = pair_sum(l_run);
-    if (!live) return;
-    const float inv = 1.0f / l_tot;
-    uint16_t* op = static_cast<uint16_t*>(A.out) + ((int64_t)head * S.qs + qrow) * D;
+    const float inv = 1.0f / l_tot;   // columns past the item's rows are never stored
+    char* tile = reinterpret_cast<char*>(&sm.k[0][0]) + wave * (32 * RB);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -289,9 +290,23 @@ __device__ __attribute__((always_inline)) void attend_bf16_body(const AttnArgs& 
         bf16x4 v4;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) v4[ii] = (__bf16)(o[db][4 * jj + ii] * inv);
-        *reinterpret_cast<u32x2*>(op + 32 * db + 8 * jj + 4 * hl) = __builtin_bit_cast(u32x2, v4);
+        const int piece = 4 * db + jj;   // dims 8 piece .. 8 piece + 7; this lane holds half 4 hl
+        *reinterpret_cast<u32x2*>(tile + col * RB + ((piece ^ (col & (NP - 1))) << 4) + 8 * hl) =
+            __builtin_bit_cast(u32x2, v4);
       }
-    if (A.lse && hl == 0) A.lse[(int64_t)head * S.qs + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+    constexpr int RPR = 64 / NP;   // rows per store instruction
+    uint16_t* outp = static_cast<uint16_t*>(A.out);
+#pragma unroll
+    for (int i = 0; i < 32 / RPR; ++i) {
+      const int r = i * RPR + lane / NP, pc = lane % NP;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(tile + r * RB + ((pc ^ (r & (NP - 1))) << 4));
+      const int R = 32 * rb + r;   // item row
+      if (R < nrows) {
+        const int64_t orow = (int64_t)(h * S.G + (R >> lgB)) * S.qs + (int64_t)b * S.B + (R & (S.B - 1));
+        *reinterpret_cast<u32x4*>(outp + orow * D + pc * 8) = val;
+      }
+    }
+    if (A.lse && hl == 0 && live) A.lse[(int64_t)head * S.qs + qrow] = (m_run + __log2f(l_tot)) * kLn2;
   }
 }
 
@@ -301,9 +316,25 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(AttnArgs A) {
   __shared__ AttnSmem<D> sm;
   int b, h, z;
   item_of_block(A.s, A.wg_per_item, &b, &h, &z);
+  // the queries and, with every row on the device, the first fixed tiles
+  // (which need no plan) load while the plan is built
+  int pre = 0;
+  if (!kTiered) {
+    Plan W;
+    plan_windows(A.s, b, &W);
+    pre = W.nfix < kAttnStages ? W.nfix : kAttnStages;
+    for (int t = 0; t < pre; ++t) {
+      const int m = t < W.a ? t : (int)(W.bb + (t - W.a));   // chunk of fixed tile t
+      const uint32_t off = (uint32_t)(t * kChunk * D * 2);
+      issue_tile<D, false>(kv_rows<D, false>(A, h), lds_addr(&sm.k[0][0]) + off, lds_addr(&sm.v[0][0]) + off,
+                           [&](int, int sl) -> int { return m * kChunk + sl; });
+    }
+  }
+  bf16x8 qf[D / 16];
+  load_q_operands<D>(A, b, h, z, qf);
   const Plan P = make_plan(A.s, b, h, A.gidx, A.nsel, sm.runs, sm.scan, kMaxRoutedAttn);
   if (kTiered) translate_plan(A.kv.split, A.nch, A.slot, h, P, sm.runs, sm.runs + kMaxRoutedAttn);
-  attend_bf16_body<D, kTiered>(A, b, h, z, P, sm, 0, nullptr);
+  attend_bf16_body<D, kTiered>(A, b, h, z, P, sm, pre, qf);
 }
 
 // Route, then attend, in one workgroup per (item, slot): the router's kept
@@ -332,7 +363,7 @@ __global__ __launch_bounds__(kAttnThreads) void route_attend_bf16_kernel(FusedAr
   for (int t = 0; t < pre; ++t) {
     const int m = t < P.a ? t : (int)(P.bb + (t - P.a));   // chunk of fixed tile t
     const uint32_t off = (uint32_t)(t * kChunk * D * 2);
-    issue_tile<D>(kv_rows<D, false>(F.a, h), lds_addr(&sm.k[0][0]) + off, lds_addr(&sm.v[0][0]) + off,
+    issue_tile<D, false>(kv_rows<D, false>(F.a, h), lds_addr(&sm.k[0][0]) + off, lds_addr(&sm.v[0][0]) + off,
                   [&](int, int sl) -> int { return m * kChunk + sl; });
   }
   // the attention's query operands load while the router runs

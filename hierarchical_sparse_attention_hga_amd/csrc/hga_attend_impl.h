@@ -106,12 +106,14 @@ __device__ Plan make_plan(const Shape& S, int b, int h, const int32_t* gidx, con
   Plan P;
   plan_windows(S, b, &P);
   const int64_t row = (int64_t)b * S.hkv + h;
+  // the first entries load together with the count (one memory round trip)
+  const int j0 = (int)threadIdx.x < S.kg ? gidx[row * S.kg + threadIdx.x] : -1;
   int n = nsel[row * 2 + 1];
   n = n < 0 ? 0 : (n > S.kg ? S.kg : n);
   int carry_max = INT_MIN, count = 0;
   for (int base = 0; base < n; base += blockDim.x) {
     const int i = base + threadIdx.x;
-    const int j = i < n ? gidx[row * S.kg + i] : -1;
+    const int j = i < n ? (base == 0 ? j0 : gidx[row * S.kg + i]) : -1;
     bool usable = i < n && j >= 0 && ((int64_t)j + 1) * S.g <= P.s;
     if (usable) {
       const int64_t m = (int64_t)j * S.g / S.c;
@@ -267,6 +269,18 @@ __device__ inline void lds_dma16(const void* src, uint32_t lds_base) {
       : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
       : "memory", "m0");
 }
+// The same with a uniform 64-bit base in SGPRs and a 32-bit byte offset per
+// lane (the global address is base + off): one vector instruction less per
+// load, and no 64-bit address arithmetic per lane.
+__device__ inline void lds_dma16_off(const void* base, uint32_t off, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "memory", "m0");
+}
 // The same for 4 bytes per lane: lane i's word lands at lds_base + 4 i.
 __device__ inline void lds_dma4(const void* src, uint32_t lds_base) {
   asm volatile(
@@ -329,7 +343,7 @@ __device__ inline KVRows kv_rows(const AttnArgs& A, int h) {
 // (swizzle kinds kKS and kVS, see swizzle) in the stage at LDS byte addresses
 // k_lds / v_lds. src(i, sl) is the source row (see kCacheFlag) of slot sl, the
 // row of this lane in the wave's i-th load.
-template <int D, int kKS = 0, int kVS = 1, typename SrcFn>
+template <int D, bool kTiered, int kKS = 0, int kVS = 1, typename SrcFn>
 __device__ inline void issue_tile(const KVRows& kv, uint32_t k_lds, uint32_t v_lds, SrcFn src) {
   constexpr int NP = D / 8;                   // 16-byte pieces per token row
   constexpr int RPI = 64 / NP;                // rows per direct-to-LDS wave load
@@ -342,10 +356,20 @@ __device__ inline void issue_tile(const KVRows& kv, uint32_t k_lds, uint32_t v_l
     const int row0 = wave * RPW + i * RPI;
     const int rr = row0 + lane / NP;
     const int sr = src(i, rr);
-    lds_dma16(src_ptr(kv.k_dev, kv.k_cache, sr, D) + ((lane % NP) ^ swizzle<D, kKS>(rr)) * 8,
-              k_lds + (uint32_t)(row0 * D * 2));
-    lds_dma16(src_ptr(kv.v_dev, kv.v_cache, sr, D) + ((lane % NP) ^ swizzle<D, kVS>(rr)) * 8,
-              v_lds + (uint32_t)(row0 * D * 2));
+    if (kTiered) {
+      lds_dma16(src_ptr(kv.k_dev, kv.k_cache, sr, D) + ((lane % NP) ^ swizzle<D, kKS>(rr)) * 8,
+                k_lds + (uint32_t)(row0 * D * 2));
+      lds_dma16(src_ptr(kv.v_dev, kv.v_cache, sr, D) + ((lane % NP) ^ swizzle<D, kVS>(rr)) * 8,
+                v_lds + (uint32_t)(row0 * D * 2));
+    } else {
+      // device rows only: byte offsets from the head's rows (a head holds
+      // at most 262,144 rows of at most 256 bytes, well below 2^32)
+      const uint32_t row = (uint32_t)sr * (uint32_t)(D * 2);
+      lds_dma16_off(kv.k_dev, row + ((uint32_t)((lane % NP) ^ swizzle<D, kKS>(rr)) << 4),
+                    k_lds + (uint32_t)(row0 * D * 2));
+      lds_dma16_off(kv.v_dev, row + ((uint32_t)((lane % NP) ^ swizzle<D, kVS>(rr)) << 4),
+                    v_lds + (uint32_t)(row0 * D * 2));
+    }
   }
 }
 

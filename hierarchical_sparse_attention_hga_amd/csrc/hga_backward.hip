@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dq_kernel(BwdArgs A) {
   const int dlim = P.dlim;
   auto issue = [&](int t) {
     const uint32_t off = (uint32_t)((t & 1) * kChunk * D * 2);
-    issue_tile<D, 2, 0>(kv, lds_addr(&sm.k[0][0]) + off, lds_addr(&sm.v[0][0]) + off, [&](int i, int sl) -> int {
+    issue_tile<D, kTiered, 2, 0>(kv, lds_addr(&sm.k[0][0]) + off, lds_addr(&sm.v[0][0]) + off, [&](int i, int sl) -> int {
       if (t < P.nfix) return kTiered ? raw[i] + sl : (int)((t < P.a ? t : P.bb + (t - P.a)) * kChunk) + sl;
       if (t < P.nfix + P.nrt) return run_of(t, sl) < P.nrouted ? raw[i] + (sl & ((1 << lg) - 1)) : 0;
       return diag0 + (sl < dlim ? sl : 0);
