@@ -373,7 +373,7 @@ __global__ __launch_bounds__(kAttnThreads) void route_attend_bf16_kernel(FusedAr
   int32_t* gout = F.r.group_idx + ((int64_t)b * S.hkv + h) * S.kg;
   const int g = S.g;
   int* runs = sm.runs;
-  const int nsg = route::route_item<uint16_t>(F.r, b, h, rsm, wr, [runs, wr, gout, g](int rank, int group) {
+  const int nsg = route::route_item<uint16_t, false>(F.r, b, h, rsm, wr, [runs, wr, gout, g](int rank, int group) {
     runs[rank] = group * g;
     if (wr) gout[rank] = group;
   });

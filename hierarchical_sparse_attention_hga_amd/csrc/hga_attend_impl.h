@@ -272,13 +272,21 @@ __device__ inline void lds_dma16(const void* src, uint32_t lds_base) {
 // The same with a uniform 64-bit base in SGPRs and a 32-bit byte offset per
 // lane (the global address is base + off): one vector instruction less per
 // load, and no 64-bit address arithmetic per lane.
+// base must be the same in every lane; it is taken from the first active
+// lane, so that it is held in scalar registers even where the compiler keeps
+// the pointer in vector registers.
 __device__ inline void lds_dma16_off(const void* base, uint32_t off, uint32_t lds_base) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  // (the builtin returns int: each half goes through uint32_t, so the low
+  // half is not sign-extended into the high one)
+  const uint64_t sbase = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32)) << 32) |
+                         (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);
   asm volatile(
       "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
       "global_load_lds_dwordx4 %0, %1"
       :
-      : "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "v"(off), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
       : "memory", "m0");
 }
 // The same for 4 bytes per lane: lane i's word lands at lds_base + 4 i.

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   const int h = lid / (int)S.nb;
   const int b = lid % (int)S.nb;
   int32_t* gout = a.group_idx + ((int64_t)b * S.hkv + h) * S.kg;
-  route::route_item<T>(a, b, h, sm, true, [gout](int rank, int group) { gout[rank] = group; });
+  route::route_item<T, true>(a, b, h, sm, true, [gout](int rank, int group) { gout[rank] = group; });
 }
 
 }  // namespace

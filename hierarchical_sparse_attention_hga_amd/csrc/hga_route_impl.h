@@ -229,13 +229,30 @@ __device__ inline void finish_round(const ScoreRound& rd, const double* qbar, in
 
 constexpr int kRoundRows = kRowsInFlight * kWaves * (64 / kLanesPerCand);   // rows per round
 
-// Rounds from row `from` on (a multiple of kRoundRows).
-template <typename RowFn>
-__device__ void score_rows(const double* qbar, int d, int n, RowFn row, unsigned long long* key, int from = 0) {
-  for (int base = from; base < n; base += kRoundRows) {
-    ScoreRound rd;
-    load_round(base, d, n, row, rd);
-    finish_round(rd, qbar, d, n, key);
+// Rounds from row `from` on (a multiple of kRoundRows), the loads of round
+// `from` already issued into cur. With kPipelined the next round's loads are
+// issued before a round is scored, so two rounds are in flight (their
+// registers are left to the router kernel: inside the fused kernel they
+// would push the attention's state out to scratch memory).
+template <bool kPipelined, typename RowFn>
+__device__ void score_rows(const double* qbar, int d, int n, RowFn row, unsigned long long* key, ScoreRound& cur,
+                           int from) {
+  if (!kPipelined) {
+    finish_round(cur, qbar, d, n, key);
+    for (int base = from + kRoundRows; base < n; base += kRoundRows) {
+      load_round(base, d, n, row, cur);
+      finish_round(cur, qbar, d, n, key);
+    }
+    return;
+  }
+  ScoreRound nxt;
+  for (int base = from; base < n; base += 2 * kRoundRows) {
+    const bool more = base + kRoundRows < n;
+    if (more) load_round(base + kRoundRows, d, n, row, nxt);
+    finish_round(cur, qbar, d, n, key);
+    if (!more) break;
+    if (base + 2 * kRoundRows < n) load_round(base + 2 * kRoundRows, d, n, row, cur);
+    finish_round(nxt, qbar, d, n, key);
   }
 }
 
@@ -257,7 +274,7 @@ struct RouteArgs {
 // synchronises before reading what it stored. With write_out the item's rows
 // of chunk_idx, group_idx (-1 padding; the kept entries are left to emit) and
 // n_sel are written. Returns the number of kept groups.
-template <typename T, typename GroupEmit>
+template <typename T, bool kPipelined, typename GroupEmit>
 __device__ int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm, bool write_out, GroupEmit emit) {
   constexpr int E = Slice<T>::E;
   constexpr int kRowsPerThread = 8;   // block-query rows loaded per thread per round
@@ -326,8 +343,7 @@ __device__ int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm, bool 
   const int64_t orow = (int64_t)b * S.hkv + h;
   // ---- 2-3. chunk stage
   if (chunk_select) {
-    finish_round(first, sm.qbar, d, ncand, sm.key);
-    score_rows(sm.qbar, d, ncand, chunk_row, sm.key, kRoundRows);
+    score_rows<kPipelined>(sm.qbar, d, ncand, chunk_row, sm.key, first, 0);
     __syncthreads();
     // the functors handed to the select capture by value: a by-reference
     // capture would keep the captured locals in scratch memory
@@ -351,11 +367,14 @@ __device__ int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm, bool 
   if (nsg > 0 && nsg < ngc) {
     const int64_t gsplit = a.split / S.g;          // groups held in host memory
     const int64_t ngl = S.kvs / S.g;
-    score_rows(sm.qbar, d, ngc, [&](int c) -> const float* {
+    auto group_row = [&](int c) -> const float* {
       const int64_t j = group_of(c);
       return j < gsplit ? a.gs_host + ((int64_t)h * gsplit + j) * d
                         : a.gs_dev + ((int64_t)h * (ngl - gsplit) + (j - gsplit)) * d;
-    }, sm.key);
+    };
+    ScoreRound g0;
+    load_round(0, d, ngc, group_row, g0);
+    score_rows<kPipelined>(sm.qbar, d, ngc, group_row, sm.key, g0, 0);
     __syncthreads();
     if (wave == 0) wave_select(sm.key, ngc, nsg, sm.hist, [emit, group_of](int rank, int pos) { emit(rank, group_of(pos)); });
   } else {
