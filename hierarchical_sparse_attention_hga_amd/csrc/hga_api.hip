@@ -304,6 +304,9 @@ hga_status hga_attend_backward(const hga_config* cfg, const void* q, int64_t q_s
   if (k->split > 0 && s.sink_chunks + s.local_chunks > hga::kMaxFixedTiered)
     return fail(HGA_ERR_UNSUPPORTED, "with a host tier, sink and local windows may span at most %d chunks",
                 hga::kMaxFixedTiered);
+  // the dK/dV kernel addresses Q and dO rows by 32-bit byte offsets
+  if ((int64_t)s.hq * s.qs * s.d * (s.dtype == HGA_BF16 ? 2 : 4) > (int64_t)UINT32_MAX)
+    return fail(HGA_ERR_UNSUPPORTED, "q and dout must be under 4 GiB each");
   const size_t need = hga::backward_workspace_bytes(s) + (k->split > 0 ? hga::tier_cache_bytes(s, k->split) : 0);
   if (!workspace || ws_bytes < need)
     return fail(HGA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : (size_t)0);

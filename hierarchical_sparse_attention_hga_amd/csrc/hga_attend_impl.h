@@ -289,6 +289,19 @@ __device__ inline void lds_dma16_off(const void* base, uint32_t off, uint32_t ld
       : "v"(off), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
       : "memory", "m0");
 }
+// The same for 4 bytes per lane, with a uniform base and 32-bit lane offsets.
+__device__ inline void lds_dma4_off(const void* base, uint32_t off, uint32_t lds_base) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint64_t sbase = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32)) << 32) |
+                         (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, %1"
+      :
+      : "v"(off), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "memory", "m0");
+}
 // The same for 4 bytes per lane: lane i's word lands at lds_base + 4 i.
 __device__ inline void lds_dma4(const void* src, uint32_t lds_base) {
   asm volatile(

@@ -299,8 +299,13 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dq_kernel(BwdArgs A) {
         }
     }
   }
-  if (!live) return;
-  uint16_t* op = static_cast<uint16_t*>(A.dq) + qrow * D;
+  // dQ: each wave's 32 x D tile goes through LDS (the stages are free once
+  // every wave has left the loop) and is stored as whole rows, 64 / (D / 8)
+  // rows per instruction; 16-byte pieces XOR-swizzled by row.
+  static_assert(kAttnWaves * 32 * RB <= sizeof(sm.k) + sizeof(sm.v), "dQ tiles fit in the stages");
+  __syncthreads();
+  if (!active) return;
+  char* tile = reinterpret_cast<char*>(&sm.k[0][0]) + wave * (32 * RB);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -308,8 +313,22 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dq_kernel(BwdArgs A) {
       bf16x4 v4;
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) v4[ii] = (__bf16)(acc[db][4 * jj + ii] * S.scale);
-      *reinterpret_cast<u32x2*>(op + 32 * db + 8 * jj + 4 * hl) = __builtin_bit_cast(u32x2, v4);
+      const int piece = 4 * db + jj;
+      *reinterpret_cast<u32x2*>(tile + col * RB + ((piece ^ (col & (NP - 1))) << 4) + 8 * hl) =
+          __builtin_bit_cast(u32x2, v4);
     }
+  constexpr int RPR = 64 / NP;   // rows per store instruction
+  uint16_t* dqp = static_cast<uint16_t*>(A.dq);
+#pragma unroll
+  for (int i = 0; i < 32 / RPR; ++i) {
+    const int r = i * RPR + lane / NP, pc = lane % NP;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(tile + r * RB + ((pc ^ (r & (NP - 1))) << 4));
+    const int R = 32 * rb + r;   // item row
+    if (R < nrows) {
+      const int64_t orow = (int64_t)(h * S.G + (R >> lgB)) * S.qs + (int64_t)b * S.B + (R & (S.B - 1));
+      *reinterpret_cast<u32x4*>(dqp + orow * D + pc * 8) = val;
+    }
+  }
 }
 
 // ------------------------------------------------------------ dK, dV
@@ -402,10 +421,13 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkv_kernel(BwdArgs A) {
   for (int i = 0; i < D / 32; ++i) dk[i] = dv[i] = f32x16{};
 
   // source row (in Q / dO / LSE / D) of row ir of block bq; rows past the
-  // item's read its first row (masked)
-  auto src_row = [&](int bq, int ir) -> int64_t {
+  // item's read its first row (masked). B is a power of two. Rows index
+  // arrays of at most 2^32 bytes (checked by the caller), so byte offsets
+  // from the arrays' bases are 32-bit and the bases stay in scalar registers.
+  const int lgB = __ffs(S.B) - 1;
+  auto src_row = [&](int bq, int ir) -> uint32_t {
     const int r = ir < nrows ? ir : 0;
-    return (int64_t)(h * S.G + r / S.B) * S.qs + (int64_t)bq * S.B + r % S.B;
+    return (uint32_t)(h * S.G + (r >> lgB)) * (uint32_t)S.qs + (uint32_t)((bq << lgB) + (r & (S.B - 1)));
   };
   auto issue = [&](int u) {
     const int e = u / ntl, pt = u - e * ntl;
@@ -415,18 +437,17 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkv_kernel(BwdArgs A) {
     for (int i = 0; i < KI; ++i) {
       const int row0 = wave * RPW + i * RPI;
       const int rr = row0 + lane / NP;
-      const int64_t sr = src_row(bq, kChunk * pt + rr);
-      const int pc = ((lane % NP) ^ kv_swizzle<D>(rr)) * 8;
-      lds_dma16(qg + sr * D + pc, lds_addr(&sm.q[0][0]) + off + (uint32_t)(row0 * RB));
-      lds_dma16(gg + sr * D + pc, lds_addr(&sm.g[0][0]) + off + (uint32_t)(row0 * RB));
+      const uint32_t bo = src_row(bq, kChunk * pt + rr) * (uint32_t)(D * 2) +
+                          ((uint32_t)((lane % NP) ^ kv_swizzle<D>(rr)) << 4);
+      lds_dma16_off(qg, bo, lds_addr(&sm.q[0][0]) + off + (uint32_t)(row0 * RB));
+      lds_dma16_off(gg, bo, lds_addr(&sm.g[0][0]) + off + (uint32_t)(row0 * RB));
     }
     // one word per row: LSE (wave 0), D (wave 1); waves 2 and 3 load the LSE
     // again into a spare row so that every wave issues the same loads
-    const int64_t sr = src_row(bq, kChunk * pt + lane);
-    const float* src = wave == 1 ? A.dd + sr : A.lse + sr;
+    const uint32_t wo = src_row(bq, kChunk * pt + lane) * 4u;
     const int st = u % kKVStages;
     float* dst = wave == 0 ? &sm.lse[st][0] : wave == 1 ? &sm.dd[st][0] : &sm.spare[st][0];
-    lds_dma4(src, lds_addr(dst));
+    lds_dma4_off(wave == 1 ? A.dd : A.lse, wo, lds_addr(dst));
   };
 
   for (int b0 = 0; b0 < S.nb; b0 += kKVListCap) {
@@ -473,13 +494,21 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkv_kernel(BwdArgs A) {
         lr[4 * a4] = l4.x; lr[4 * a4 + 1] = l4.y; lr[4 * a4 + 2] = l4.z; lr[4 * a4 + 3] = l4.w;
         dr[4 * a4] = d4.x; dr[4 * a4 + 1] = d4.y; dr[4 * a4 + 2] = d4.z; dr[4 * a4 + 3] = d4.w;
       }
+      // Accumulator r holds tile row ir = base + cr, cr = 8 (r >> 2) + (r & 3).
+      // The pair is visible when the token is in the block's set, the row
+      // exists, and on the block's own chunk the row's position is at or past
+      // the token's (position sq + (ir & (B - 1)), the token at tpos). A
+      // hidden score becomes -inf, so its probability and dS are zero.
+      const int base = kChunk * pt + 32 * rw + 4 * hl;
+      const int rlim = tok_ok ? nrows - base : 0;
+      const int dpos = diag ? (int)(tpos - sq) : INT_MIN;
       bf16x8 pf[2], sf[2];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int ir = kChunk * pt + 32 * rw + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const bool vis = tok_ok && ir < nrows && (!diag || tpos <= sq + (ir & (S.B - 1)));
-        const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sacc[r], sl2, -lr[r] * kLog2e)) : 0.0f;
-        const float ds = vis ? p * (pacc[r] - dr[r]) : 0.0f;
+        const int cr = 8 * (r >> 2) + (r & 3);
+        const bool vis = cr < rlim && ((base + cr) & (S.B - 1)) >= dpos;
+        const float p = __builtin_amdgcn_exp2f(fmaf(vis ? sacc[r] : -INFINITY, sl2, -lr[r] * kLog2e));
+        const float ds = p * (pacc[r] - dr[r]);
         pf[r >> 3][r & 7] = (__bf16)p;
         sf[r >> 3][r & 7] = (__bf16)ds;
       }
@@ -518,23 +547,41 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkv_kernel(BwdArgs A) {
       }
   }
   __syncthreads();
-  if (rw == 1 || tpos < S.q0 || tpos >= lq) return;
-  uint16_t* kout = static_cast<uint16_t*>(A.dk) + ((int64_t)h * S.nq + (tpos - S.q0)) * D;
-  uint16_t* vout = static_cast<uint16_t*>(A.dv) + ((int64_t)h * S.nq + (tpos - S.q0)) * D;
+  // the sums, as bfloat16 rows of the chunk's 64 tokens, into LDS after the
+  // reduction buffer (16-byte pieces XOR-swizzled by token), then stored as
+  // whole rows by every wave: dK at rows tpos - q0 of dk, dV of dv
+  static_assert(sizeof(float) * 2 * 2 * (D / 32) * 16 * 64 + 2 * kChunk * RB <= sizeof(sm.q) + sizeof(sm.g),
+                "the output tiles fit after the reduction buffer");
+  char* otile = reinterpret_cast<char*>(&sm.q[0][0]) + sizeof(float) * 2 * 2 * (D / 32) * 16 * 64;
+  if (rw == 0) {
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      bf16x4 k4, v4;
+      for (int jj = 0; jj < 4; ++jj) {
+        bf16x4 k4, v4;
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int i = 4 * jj + ii;
-        k4[ii] = (__bf16)((dk[db][i] + red[slot(0, db, i)]) * S.scale);
-        v4[ii] = (__bf16)(dv[db][i] + red[slot(1, db, i)]);
+        for (int ii = 0; ii < 4; ++ii) {
+          const int i = 4 * jj + ii;
+          k4[ii] = (__bf16)((dk[db][i] + red[slot(0, db, i)]) * S.scale);
+          v4[ii] = (__bf16)(dv[db][i] + red[slot(1, db, i)]);
+        }
+        const int off = tok * RB + (((4 * db + jj) ^ (tok & (NP - 1))) << 4) + 8 * hl;
+        *reinterpret_cast<u32x2*>(otile + off) = __builtin_bit_cast(u32x2, k4);
+        *reinterpret_cast<u32x2*>(otile + kChunk * RB + off) = __builtin_bit_cast(u32x2, v4);
       }
-      *reinterpret_cast<u32x2*>(kout + 32 * db + 8 * jj + 4 * hl) = __builtin_bit_cast(u32x2, k4);
-      *reinterpret_cast<u32x2*>(vout + 32 * db + 8 * jj + 4 * hl) = __builtin_bit_cast(u32x2, v4);
-    }
+  }
+  __syncthreads();
+  constexpr int RPR = 64 / NP;   // token rows per store instruction
+#pragma unroll
+  for (int i = 0; i < 2 * kChunk / (kKVWaves * RPR); ++i) {
+    const int rowi = (i * kKVWaves + wave) * RPR + lane / NP;   // 0 .. 127: dK rows, then dV rows
+    const int tk = rowi & (kChunk - 1), pc = lane % NP;
+    const int64_t p = t0 + tk;
+    if (p < S.q0 || p >= lq) continue;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(otile + rowi * RB + ((pc ^ (tk & (NP - 1))) << 4));
+    uint16_t* dst = static_cast<uint16_t*>(rowi < kChunk ? A.dk : A.dv) + ((int64_t)h * S.nq + (p - S.q0)) * D;
+    *reinterpret_cast<u32x4*>(dst + pc * 8) = val;
+  }
 }
 
 // ------------------------------------------------------------ float32 (SIMT)

@@ -253,9 +253,9 @@ hga_status hga_stream_forward(const hga_config* cfg, const void* q, const void* 
  *   dk, dv     device, [Hkv][n_q][d] of cfg->dtype: row i is position q_start + i.
  *   workspace  device, at least hga_workspace_size(..., HGA_WS_BACKWARD) bytes
  *              for split 0, HGA_WS_BACKWARD_TIERED with a host tier.
- * bfloat16 and float32 (head dims as for hga_attend). The gradient of each
- * key is summed in one workgroup in a fixed order: repeated calls give
- * identical bits. */
+ * bfloat16 and float32 (head dims as for hga_attend); q and dout of 4 GiB or
+ * more each return HGA_ERR_UNSUPPORTED. The gradient of each key is summed
+ * in one workgroup in a fixed order: repeated calls give identical bits. */
 hga_status hga_attend_backward(const hga_config* cfg, const void* q, int64_t q_start, int64_t n_q,
                                int64_t seq_len, const hga_tiered* k, const hga_tiered* v,
                                const int32_t* group_idx, const int32_t* n_sel, const void* out, const float* lse,
