@@ -210,4 +210,9 @@ def test_backward_validation():
     assert call(c, [t1, t2] + args[2:]) == E
     assert call(c, [(None, FAKE, 1024), (None, FAKE, 1024)] + args[2:]) == E
     assert call(c, [t1, t1] + args[2:]) == hga.HGA_ERR_WORKSPACE   # the cache needs more than `need`
+    # q of 4 GiB (64 heads x 262,144 rows x 256 bytes): its rows are addressed
+    # by 32-bit byte offsets, so the call is refused before any device work
+    big = cfg(n_q_heads=64)
+    assert call(big, args, 1 << 62, (0, 262144, 262144)) == hga.HGA_ERR_UNSUPPORTED
+    assert "4 GiB" in hga.hga_last_error()
     hga.hga_attend_backward(c, None, 16384, 0, 16384, *[None] * 11, 0)   # no queries: a no-op
