@@ -667,9 +667,17 @@ hipError_t launch_attend(const Shape& s, const void* q, const KVSrc& kv, const i
 
 // One kernel when one workgroup holds every query row of an item (G B <= 8
 // waves of 32 rows): with more, each of an item's workgroups would route it
-// again, and the separate router is cheaper.
+// again, and the separate router is cheaper. Also the separate router when a
+// block has more than two scoring rounds of chunk candidates: the router
+// kernel keeps two rounds in flight, the fused kernel (whose registers hold
+// the attention's state) one, and at 64K and beyond the router kernel then
+// attention kernel are faster (measured: 128K 200 -> 183 us, 64K decoding
+// 83 -> 70 us).
 bool fused_route_attend_supported(const Shape& s, int64_t kv_split) {
-  return s.dtype == HGA_BF16 && kv_split == 0 && (s.d == 128 || s.d == 64) && bf16_wg_per_item(s) == 1;
+  const int64_t last_chunk = (s.q0 + s.nq - 1) / kChunk;   // the last block's chunk
+  const int64_t candidates = last_chunk - s.sink_chunks - s.local_chunks;
+  return s.dtype == HGA_BF16 && kv_split == 0 && (s.d == 128 || s.d == 64) && bf16_wg_per_item(s) == 1 &&
+         candidates <= 2 * route::kRoundRows;
 }
 
 hipError_t launch_route_attend(const Shape& s, const void* q, const float* cs, const float* gs_host,

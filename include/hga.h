@@ -203,10 +203,13 @@ hga_status hga_attend(const hga_config* cfg, const void* q, int64_t q_start, int
  * its chunk_idx / group_idx / n_sel, which are written as well. Arguments
  * have the meaning, layout and ownership they have in those two calls; the
  * workspace is the one hga_attend needs for this K/V split. With bfloat16,
- * K/V entirely on the device (split 0) and at most 256 query rows per block
- * and KV head (Hq/Hkv x q_block), both steps run in one kernel, each workgroup routing its own query block
- * before attending over the groups it kept; otherwise the call runs the two
- * steps one after the other. Errors are those of either call. */
+ * K/V entirely on the device (split 0), at most 256 query rows per block and
+ * KV head (Hq/Hkv x q_block) and at most 512 chunk candidates per block
+ * (closed chunks outside the sink and local windows: sequences up to about
+ * 32K tokens), both steps run in one kernel, each workgroup routing its own
+ * query block before attending over the groups it kept; otherwise the call
+ * runs the two steps one after the other (the results are the same either
+ * way). Errors are those of either call. */
 hga_status hga_route_attend(const hga_config* cfg, const void* q, int64_t q_start, int64_t n_q,
                             int64_t seq_len, const float* chunk_sum, const hga_tiered* group_sum,
                             const hga_tiered* k, const hga_tiered* v,
