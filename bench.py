@@ -455,14 +455,18 @@ def decode_line(cfg_id, batch, steps, warmup):
     us = float(np.mean([evs[i][0].elapsed_time(evs[i][1]) * 1e3 for i in range(0, steps, per)]))
     nsel = ns.cpu().numpy().reshape(hkv, 2)
     byts = float(sum(decode_bytes(base, pos, nsel[h]) for h in range(hkv)))
-    traffic = measured_traffic(f"{base['name']}-decode-b{batch}", "route_attend_bf16")
+    # one kernel unless the block has more than two scoring rounds of chunk
+    # candidates (then the router kernel, then the attention kernel)
+    fused = pos // 64 - base["sink"] // 64 - base["local"] // 64 <= 512 and base["hq"] // base["hkv"] <= 256
+    kname = "route_attend_bf16" if fused else "route_kernel + attend_bf16"
+    traffic = measured_traffic(f"{base['name']}-decode-b{batch}", "route_attend_bf16") if fused else None
     del k, v, gs, cs
     torch.cuda.empty_cache()
     return {"value": steps * batch / wall, "unit": "generated tokens/s", "kernel_us_mean": us,
             "ms_per_step": wall / steps * 1e3,
             "config": {"workload": f"{base['name']}-decode", "batch": batch, "history": pos,
                        "q_heads": base["hq"], "kv_heads": base["hkv"], "q_block": 1},
-            "roofline": {"kernel": "route_attend_bf16", "bound": "hbm", "achieved": byts / (us * 1e-6) / 1e9,
+            "roofline": {"kernel": kname, "bound": "hbm", "achieved": byts / (us * 1e-6) / 1e9,
                          "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": byts / (us * 1e-6) / PEAK_HBM,
                          "traffic": traffic, "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": byts}}
 
