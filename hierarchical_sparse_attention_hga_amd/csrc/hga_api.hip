@@ -329,6 +329,6 @@ const char* hga_status_string(hga_status status) {
 
 const char* hga_last_error(void) { return g_err; }
 
-int32_t hga_version(void) { return 104; }
+int32_t hga_version(void) { return 105; }
 
 }  // extern "C"
