@@ -46,6 +46,11 @@ CASES = {
     "f32_d128_g3": dict(dtype="f32", d=128, hq=6, hkv=2, rope_theta=None),
     "f32_d32_group4": dict(dtype="f32", d=32, group=4, top_groups=9, rope_theta=None),
     "f32_d4": dict(dtype="f32", d=4, rope_theta=None, n_plant_chunks=0),
+    # more than one scoring round (256 summary rows each): about 700 chunk
+    # candidates in three rounds (the router kernel, two in flight), and
+    # 384 groups of 48 kept chunks in two rounds (also inside the fused kernel)
+    "chunk_rounds3": dict(L=64 * 700, n_q=128, top_chunks=8, top_groups=24),
+    "group_rounds2": dict(L=64 * 80, n_q=128, top_chunks=48, top_groups=100),
 }
 
 
