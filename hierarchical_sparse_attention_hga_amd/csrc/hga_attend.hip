@@ -170,7 +170,10 @@ __device__ __attribute__((always_inline)) void attend_bf16_body(const AttnArgs& 
       issue(u);
     }
   fetch(kAttnStages - 1);
-  for (int t = 0; t < nt; ++t) {
+  // One tile per call; the stage is a compile-time constant (the loop below
+  // takes the tiles two at a time), so it folds into the LDS reads' offsets.
+  static_assert(kAttnStages == 2, "the tile loop alternates two stages");
+  auto step = [&](int t, auto stage_c) __attribute__((always_inline)) {
     // this thread's loads of tile t are done once only newer tiles are pending
     const int ahead = nt - 1 - t < kAhead ? nt - 1 - t : kAhead;
     if (kAhead >= 2 && ahead >= 2)
@@ -184,8 +187,8 @@ __device__ __attribute__((always_inline)) void attend_bf16_body(const AttnArgs& 
       if (t + kAttnStages - 1 >= pre_tiles) issue(t + kAttnStages - 1);
       fetch(t + kAttnStages);
     }
-    if (!active) continue;
-    const uint32_t stage = (uint32_t)((t % kAttnStages) * kChunk * RB);
+    if (!active) return;
+    constexpr uint32_t stage = (uint32_t)(decltype(stage_c)::value * kChunk * RB);
     const char* kt = sKb + stage;
     const char* vt = sVb + stage;
     // S^T = K Q^T for both 32-token halves of the tile
@@ -270,6 +273,10 @@ __device__ __attribute__((always_inline)) void attend_bf16_body(const AttnArgs& 
         for (int mm = 0; mm < 2; ++mm)
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfa[tb][db][mm], pf[mm], o[db], 0, 0, 0);
     }
+  };
+  for (int t = 0; t < nt; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < nt) step(t + 1, std::integral_constant<int, 1>{});
   }
 
   // Output: each wave writes its normalized 32 x D tile to LDS (the stage
