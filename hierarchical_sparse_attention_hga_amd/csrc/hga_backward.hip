@@ -73,41 +73,51 @@ __device__ void write_chunk_masks(const BwdArgs& A, int b, int h, const Plan& P,
   }
 }
 
-// The blocks of [b0, b0 + blockDim.x) that attend chunk m of KV head h, in
-// block order, into lb (block, | kDiagBit for the chunk's own blocks) and
-// lmask (the chunk's tokens in the block's token set); returns their count.
+// Whether block b attends chunk m of KV head h: code b (| kDiagBit for the
+// chunk's own blocks) or -1, and the chunk's tokens in the block's token set.
 constexpr int kDiagBit = 1 << 30;
-__device__ int list_attending(const BwdArgs& A, int h, int64_t m, int b0, int* lb, unsigned long long* lmask,
-                              int* scan) {
+struct Attending {
+  int code;
+  unsigned long long msk;
+};
+__device__ Attending attending(const BwdArgs& A, int h, int64_t m, int b) {
   const Shape& S = A.s;
-  int code = -1;
-  unsigned long long msk = 0ull;
-  const int b = b0 + threadIdx.x;
+  Attending x{-1, 0ull};
   if (b < S.nb) {
     const int64_t s = S.q0 + (int64_t)b * S.B, ms = s / kChunk;
     if (m == ms) {
-      code = b | kDiagBit;
-      msk = ~0ull;
+      x = {b | kDiagBit, ~0ull};
     } else if (m < ms) {
       int64_t a, bb;
       fixed_windows(ms, S.sink_chunks, S.local_chunks, &a, &bb);
       if (m < a || m >= bb) {
-        code = b;
-        msk = ~0ull;
+        x = {b, ~0ull};
       } else {
-        msk = A.cmask[((int64_t)b * S.hkv + h) * A.nchunks + (m - A.m0)];
-        if (msk) code = b;
+        x.msk = A.cmask[((int64_t)b * S.hkv + h) * A.nchunks + (m - A.m0)];
+        if (x.msk) x.code = b;
       }
     }
   }
+  return x;
+}
+
+// The attending blocks among one per thread, in thread (block) order, into lb
+// and lmask; returns their count.
+__device__ int list_compact(Attending x, int* lb, unsigned long long* lmask, int* scan) {
   int tot;
-  const int pos = block_scan<false>(code >= 0 ? 1 : 0, scan, &tot);
-  if (code >= 0) {
-    lb[pos] = code;
-    lmask[pos] = msk;
+  const int pos = block_scan<false>(x.code >= 0 ? 1 : 0, scan, &tot);
+  if (x.code >= 0) {
+    lb[pos] = x.code;
+    lmask[pos] = x.msk;
   }
   __syncthreads();
   return tot;
+}
+
+// The blocks of [b0, b0 + blockDim.x) that attend chunk m of KV head h.
+__device__ int list_attending(const BwdArgs& A, int h, int64_t m, int b0, int* lb, unsigned long long* lmask,
+                              int* scan) {
+  return list_compact(attending(A, h, m, b0 + (int)threadIdx.x), lb, lmask, scan);
 }
 
 // ------------------------------------------------------------ dQ
@@ -332,38 +342,43 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dq_kernel(BwdArgs A) {
 }
 
 // ------------------------------------------------------------ dK, dV
-constexpr int kKVThreads = 256;
-constexpr int kKVWaves = kKVThreads / 64;
-constexpr int kKVListCap = kKVThreads;   // attending blocks listed per pass
-constexpr int kKVStages = 4;             // query tiles in the LDS ring (up to 3 in flight)
+constexpr int kKVThreads = 256;                // float32 kernel: 64 tokens x 4 lanes
+constexpr int kKVListCap = kKVThreads;         // float32 kernel: attending blocks listed per pass
+constexpr int kKV16Threads = 512;              // bf16 kernel: 8 waves, two per SIMD
+constexpr int kKV16Waves = kKV16Threads / 64;
+constexpr int kKV16ListCap = kKV16Threads;     // bf16 kernel: attending blocks listed per pass
+constexpr int kKVStages = 3;                   // query tiles in the LDS ring: scored, summed, loading
 
 template <int D>
 struct BwdKVSmem {
   uint16_t q[kKVStages][kChunk * D];   // 64-row tiles of Q and dO (kv_swizzle); after
   uint16_t g[kKVStages][kChunk * D];   // the loop, the cross-wave reduction buffer
+  u32x4 pds[2][4][2][2][64];           // [tile parity][th, rw][P, dS][mm][lane]: bf16 MFMA operands
   float lse[kKVStages][kChunk];
   float dd[kKVStages][kChunk];
-  float spare[kKVStages][kChunk];      // target of the per-row word loads of waves 2 and 3
-  int lb[kKVListCap];          // attending block, | kDiagBit for the chunk's own blocks
-  unsigned long long lmask[kKVListCap];   // tokens of the chunk in the block's token set
+  int lb[kKV16ListCap];        // attending block, | kDiagBit for the chunk's own blocks
+  unsigned long long lmask[kKV16ListCap];   // tokens of the chunk in the block's token set
   int scan[16];
 };
 
-// One workgroup per (KV head h, chunk m holding positions of the call).
-// Waves: token half th = wave & 1 (tokens 32 th .. 32 th + 31 of the chunk,
-// this lane's token is column col), row half rw = wave >> 1 of each 64-row
-// query tile. dK^T and dV^T of the wave's tokens accumulate over the tiles
-// of every attending block; the two row halves are summed at the end.
+// One workgroup per (KV head h, chunk m holding positions of the call), eight
+// waves in two roles, a pipeline over the query tiles of the attending
+// blocks. Wave w: token half th = w & 1 (tokens 32 th .. 32 th + 31 of the
+// chunk, this lane's token is column col), row half rw = (w >> 1) & 1 of each
+// 64-row tile, role w >> 2. At step u the scoring waves (role 0) form S^T and
+// dP^T of tile u for their (th, rw), then P and dS as bf16 MFMA operands in
+// LDS; the summing waves (role 1, sharing a SIMD with the scoring wave of the
+// same (th, rw)) accumulate dV^T += dO^T P and dK^T += Q^T dS of tile u - 1
+// over the whole head dimension. The two row halves are summed at the end.
 template <int D>
-__global__ __launch_bounds__(kKVThreads) void bwd_dkv_kernel(BwdArgs A) {
+__global__ __launch_bounds__(kKV16Threads) void bwd_dkv_kernel(BwdArgs A) {
   __shared__ BwdKVSmem<D> sm;
-  static_assert(2 * 2 * (D / 32) * 16 * 64 * sizeof(float) <= sizeof(sm.q) + sizeof(sm.g),
-                "the row-half reduction fits in the Q and dO stages");
   constexpr int NP = D / 8;
   constexpr int RPI = 64 / NP;
-  constexpr int RPW = kChunk / kKVWaves;   // tile rows each wave loads
+  constexpr int RPW = kChunk / kKV16Waves;   // tile rows each wave loads
   constexpr int KI = RPW / RPI;
   constexpr int RB = D * 2;
+  static_assert(KI >= 1 && KI * RPI == RPW, "tile rows split evenly over the waves");
   const Shape& S = A.s;
   const int h = (int)(blockIdx.x / A.nchunks);
   const int64_t m = A.m0 + blockIdx.x % A.nchunks;
@@ -371,55 +386,16 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkv_kernel(BwdArgs A) {
   const int64_t lq = S.q0 + S.nq;          // no query of the call attends a token at or past lq
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, col = lane & 31;
-  const int th = wave & 1, rw = wave >> 1;
+  const int th = wave & 1, rw = (wave >> 1) & 1, role = wave >> 2, pair = wave & 3;
   const int tok = 32 * th + col;
   const int64_t tpos = t0 + tok;
+  // the first pass's list entry of this thread, read before anything else loads
+  const Attending first = attending(A, h, m, tid);
 
-  // K and V of this lane's token as MFMA B operands (d = 16 ks + 8 hl + e);
-  // zero past lq, where rows may hold anything
-  bf16x8 kf[D / 16], vf[D / 16];
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) kf[ks] = vf[ks] = bf16x8{};
-  if (tpos < lq) {   // the call's positions lie in the device rows (split <= 64 m0)
-    const int64_t drow = (int64_t)h * (S.kvs - A.kv.split) + (tpos - A.kv.split);
-    const uint16_t* kp = static_cast<const uint16_t*>(A.kv.k_dev) + drow * D + 8 * hl;
-    const uint16_t* vp = static_cast<const uint16_t*>(A.kv.v_dev) + drow * D + 8 * hl;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      kf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + 16 * ks));
-      vf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vp + 16 * ks));
-    }
-  }
-
-  // LDS offsets. Row reads of a Q or dO tile: lane (col, hl) reads piece
-  // 2 ks + hl of row col (+ 32 rw). Transposing reads: rows vrow and vrow + 8
-  // (+ 32 rw + 16 mm), columns vcol (+ 32 db).
-  uint32_t qoff[D / 16], tlo[D / 32], thi[D / 32];
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) qoff[ks] = (uint32_t)(col * RB + (((2 * ks + hl) ^ kv_swizzle<D>(col)) << 4));
-  {
-    const int vj = lane & 15, vg = lane >> 4;
-    const int vcol = 16 * (vg & 1) + 4 * (vj & 3);
-    const int vrow = 4 * hl + (vj >> 2);
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const int c = 32 * db + vcol;
-      tlo[db] = (uint32_t)(vrow * RB + (((c >> 3) ^ kv_swizzle<D>(vrow)) << 4) + ((c & 7) << 1));
-      thi[db] = (uint32_t)((vrow + 8) * RB + (((c >> 3) ^ kv_swizzle<D>(vrow + 8)) << 4) + ((c & 7) << 1));
-    }
-  }
-  const char* sQb = reinterpret_cast<const char*>(&sm.q[0][0]);
-  const char* sGb = reinterpret_cast<const char*>(&sm.g[0][0]);
   const uint16_t* qg = static_cast<const uint16_t*>(A.q);
   const uint16_t* gg = static_cast<const uint16_t*>(A.dout);
   const int nrows = S.G * S.B;
   const int ntl = (nrows + kChunk - 1) / kChunk;   // 64-row query tiles per attending block
-  const float sl2 = S.scale * kLog2e;
-
-  f32x16 dk[D / 32], dv[D / 32];
-#pragma unroll
-  for (int i = 0; i < D / 32; ++i) dk[i] = dv[i] = f32x16{};
-
   // source row (in Q / dO / LSE / D) of row ir of block bq; rows past the
   // item's read its first row (masked). B is a power of two. Rows index
   // arrays of at most 2^32 bytes (checked by the caller), so byte offsets
@@ -429,9 +405,10 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkv_kernel(BwdArgs A) {
     const int r = ir < nrows ? ir : 0;
     return (uint32_t)(h * S.G + (r >> lgB)) * (uint32_t)S.qs + (uint32_t)((bq << lgB) + (r & (S.B - 1)));
   };
-  auto issue = [&](int u) {
-    const int e = u / ntl, pt = u - e * ntl;
-    const int bq = sm.lb[e] & (kDiagBit - 1);
+  // tile u (query tile pt of attending block bq) into stage u mod kKVStages:
+  // every wave loads RPW rows of Q and dO; wave 0 loads the rows' LSE, wave 1
+  // their D
+  auto issue = [&](int u, int bq, int pt) {
     const uint32_t off = (uint32_t)((u % kKVStages) * kChunk * D * 2);
 #pragma unroll
     for (int i = 0; i < KI; ++i) {
@@ -442,32 +419,88 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkv_kernel(BwdArgs A) {
       lds_dma16_off(qg, bo, lds_addr(&sm.q[0][0]) + off + (uint32_t)(row0 * RB));
       lds_dma16_off(gg, bo, lds_addr(&sm.g[0][0]) + off + (uint32_t)(row0 * RB));
     }
-    // one word per row: LSE (wave 0), D (wave 1); waves 2 and 3 load the LSE
-    // again into a spare row so that every wave issues the same loads
-    const uint32_t wo = src_row(bq, kChunk * pt + lane) * 4u;
-    const int st = u % kKVStages;
-    float* dst = wave == 0 ? &sm.lse[st][0] : wave == 1 ? &sm.dd[st][0] : &sm.spare[st][0];
-    lds_dma4_off(wave == 1 ? A.dd : A.lse, wo, lds_addr(dst));
+    if (wave < 2) {
+      const int st = u % kKVStages;
+      lds_dma4_off(wave == 1 ? A.dd : A.lse, src_row(bq, kChunk * pt + lane) * 4u,
+                   lds_addr(wave == 1 ? &sm.dd[st][0] : &sm.lse[st][0]));
+    }
   };
+  auto issue_listed = [&](int u) {
+    const int e = u / ntl;
+    issue(u, sm.lb[e] & (kDiagBit - 1), u - e * ntl);
+  };
+  // The first attending block is known before the list: the first block of
+  // the call starting in chunk m (blocks lie within one chunk; every earlier
+  // block ends before the chunk). Its first tile loads while the list is built.
+  const int b_first = (int)(((t0 > S.q0 ? t0 : S.q0) - S.q0) >> lgB);
+  // The passes over the attending blocks, kKV16ListCap at a time: step u
+  // (0 .. T) waits for tile u, starts tile u + 1 into the stage tile u - 2
+  // left, and runs the role's work of the step. Both roles run the same
+  // barriers.
+  auto passes = [&](auto&& step) {
+    for (int b0 = 0; b0 < S.nb; b0 += kKV16ListCap) {
+      const bool pre = b0 <= b_first && b_first < b0 + kKV16ListCap;
+      if (pre) issue(0, b_first, 0);
+      const int tot = list_compact(b0 == 0 ? first : attending(A, h, m, b0 + tid), sm.lb, sm.lmask, sm.scan);
+      const int T = tot * ntl;
+      if (!pre && T > 0) issue_listed(0);
+      for (int u = 0; T > 0 && u <= T; ++u) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // this thread's loads of tile u
+        __syncthreads();   // every wave's; steps u - 1 done (tile u - 2's stage, the P/dS buffer of u - 2)
+        if (u + 1 < T) issue_listed(u + 1);
+        step(u, T);
+      }
+      __syncthreads();   // the list and the stages are reused by the next pass
+    }
+  };
+  // Transposing-read offsets: rows vrow and vrow + 8 (+ 32 rw + 16 mm),
+  // columns vcol (+ 32 db).
+  auto tr_offsets = [&](uint32_t* tlo, uint32_t* thi) {
+    const int vj = lane & 15, vg = lane >> 4;
+    const int vcol = 16 * (vg & 1) + 4 * (vj & 3);
+    const int vrow = 4 * hl + (vj >> 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int c = 32 * db + vcol;
+      tlo[db] = (uint32_t)(vrow * RB + (((c >> 3) ^ kv_swizzle<D>(vrow)) << 4) + ((c & 7) << 1));
+      thi[db] = (uint32_t)((vrow + 8) * RB + (((c >> 3) ^ kv_swizzle<D>(vrow + 8)) << 4) + ((c & 7) << 1));
+    }
+  };
+  const char* sQb = reinterpret_cast<const char*>(&sm.q[0][0]);
+  const char* sGb = reinterpret_cast<const char*>(&sm.g[0][0]);
+  // the row-half partial sums (row half 1 of both token halves, a lane's 16
+  // accumulators as four lane-contiguous 16-byte pieces), then the output
+  // tiles, in the stage ring once both roles have left the passes
+  constexpr size_t kRed = sizeof(float) * 2 * 2 * (D / 32) * 16 * 64;
+  static_assert(kRed + 2 * kChunk * RB <= sizeof(sm.q) + sizeof(sm.g),
+                "the row-half buffer and the output tiles fit in the stage ring");
+  float4* red = reinterpret_cast<float4*>(&sm.q[0][0]);
+  char* otile = reinterpret_cast<char*>(&sm.q[0][0]) + kRed;
 
-  for (int b0 = 0; b0 < S.nb; b0 += kKVListCap) {
-    const int tot = list_attending(A, h, m, b0, sm.lb, sm.lmask, sm.scan);
-    const int T = tot * ntl;
-    // tiles 0 .. kKVStages - 2 in flight first; at iteration u, once tile u
-    // has landed (every newer issued tile may still be pending), tile
-    // u + kKVStages - 1 goes into the stage tile u - 1 left
-    constexpr int kPerTile = 2 * KI + 1;   // loads per thread per tile
-    for (int u = 0; u < kKVStages - 1 && u < T; ++u) issue(u);
-    for (int u = 0; u < T; ++u) {
-      const int ahead = T - 1 - u < kKVStages - 2 ? T - 1 - u : kKVStages - 2;
-      if (ahead >= 2)
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPerTile));
-      else if (ahead == 1)
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPerTile));
-      else
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      __syncthreads();   // tile u landed everywhere; the stage of tile u - 1 is free
-      if (u + kKVStages - 1 < T) issue(u + kKVStages - 1);
+  if (role == 0) {
+    // scoring: K and V of this lane's token as MFMA B operands
+    // (d = 16 ks + 8 hl + e); zero past lq, where rows may hold anything
+    bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) kf[ks] = vf[ks] = bf16x8{};
+    if (tpos < lq) {   // the call's positions lie in the device rows (split <= 64 m0)
+      const int64_t drow = (int64_t)h * (S.kvs - A.kv.split) + (tpos - A.kv.split);
+      const uint16_t* kp = static_cast<const uint16_t*>(A.kv.k_dev) + drow * D + 8 * hl;
+      const uint16_t* vp = static_cast<const uint16_t*>(A.kv.v_dev) + drow * D + 8 * hl;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        kf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kp + 16 * ks));
+        vf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vp + 16 * ks));
+      }
+    }
+    // row reads of a Q or dO tile: lane (col, hl) reads piece 2 ks + hl of
+    // row col (+ 32 rw)
+    uint32_t qoff[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) qoff[ks] = (uint32_t)(col * RB + (((2 * ks + hl) ^ kv_swizzle<D>(col)) << 4));
+    const float sl2 = S.scale * kLog2e;
+    passes([&](int u, int T) {
+      if (u >= T) return;
       const int e = u / ntl, pt = u - e * ntl;
       const int code_e = sm.lb[e];
       const bool diag = (code_e & kDiagBit) != 0;
@@ -512,69 +545,87 @@ __global__ __launch_bounds__(kKVThreads) void bwd_dkv_kernel(BwdArgs A) {
         pf[r >> 3][r & 7] = (__bf16)p;
         sf[r >> 3][r & 7] = (__bf16)ds;
       }
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) {
+        sm.pds[u & 1][pair][0][mm][lane] = __builtin_bit_cast(u32x4, pf[mm]);
+        sm.pds[u & 1][pair][1][mm][lane] = __builtin_bit_cast(u32x4, sf[mm]);
+      }
+    });
+    __syncthreads();   // the summing waves' row-half exchange
+    __syncthreads();   // ... and their output tiles
+  } else {
+    // summing: dK^T and dV^T of the wave's tokens over its row half
+    uint32_t tlo[D / 32], thi[D / 32];
+    tr_offsets(tlo, thi);
+    f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) dk[i] = dv[i] = f32x16{};
+    passes([&](int u, int T) {
+      if (u == 0) return;
+      const int t = u - 1;
+      const uint32_t stage = (uint32_t)((t % kKVStages) * kChunk * RB);
+      const char* qt = sQb + stage + 32 * rw * RB;
+      const char* gt = sGb + stage + 32 * rw * RB;
       // dV^T += dO^T P and dK^T += Q^T dS: A operands of lane (half hl,
       // column kd) hold dO / Q at tile rows 32 rw + 16 mm + 4 hl + {0..3, 8..11}
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int mm = 0; mm < 2; ++mm) {
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, sm.pds[t & 1][pair][0][mm][lane]);
+        const bf16x8 sf = __builtin_bit_cast(bf16x8, sm.pds[t & 1][pair][1][mm][lane]);
+        const char* gb = gt + 16 * mm * RB;
+        const char* qb = qt + 16 * mm * RB;
 #pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {
-          const char* gb = gt + 16 * mm * RB;
-          const char* qb = qt + 16 * mm * RB;
+        for (int db = 0; db < D / 32; ++db) {
           const s16x4 glo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(gb + tlo[db]));
           const s16x4 ghi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(gb + thi[db]));
           const s16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(qb + tlo[db]));
           const s16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(qb + thi[db]));
           const s16x8 wg = {glo[0], glo[1], glo[2], glo[3], ghi[0], ghi[1], ghi[2], ghi[3]};
           const s16x8 wq = {qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
-          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wg), pf[mm], dv[db], 0, 0, 0);
-          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wq), sf[mm], dk[db], 0, 0, 0);
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wg), pf, dv[db], 0, 0, 0);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wq), sf, dk[db], 0, 0, 0);
+        }
+      }
+    });
+    auto slot = [&](int which, int db, int a4) { return (((th * 2 + which) * (D / 32) + db) * 4 + a4) * 64 + lane; };
+    if (rw == 1) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          red[slot(0, db, a4)] = float4{dk[db][4 * a4], dk[db][4 * a4 + 1], dk[db][4 * a4 + 2], dk[db][4 * a4 + 3]};
+          red[slot(1, db, a4)] = float4{dv[db][4 * a4], dv[db][4 * a4 + 1], dv[db][4 * a4 + 2], dv[db][4 * a4 + 3]};
         }
     }
-    __syncthreads();   // the list and the stages are reused by the next pass
-  }
-
-  // sum the two row halves (row half 1 through LDS), then write the keys of
-  // the call's positions: rows tpos - q0 of dk / dv
-  float* red = reinterpret_cast<float*>(&sm.q[0][0]);   // [th][dk, dv][D/32][16][64 lanes]
-  auto slot = [&](int which, int db, int i) { return (((th * 2 + which) * (D / 32) + db) * 16 + i) * 64 + lane; };
-  if (rw == 1) {
+    __syncthreads();
+    // the sums, as bfloat16 rows of the chunk's 64 tokens, into LDS after the
+    // reduction buffer (16-byte pieces XOR-swizzled by token)
+    if (rw == 0) {
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        red[slot(0, db, i)] = dk[db][i];
-        red[slot(1, db, i)] = dv[db][i];
-      }
-  }
-  __syncthreads();
-  // the sums, as bfloat16 rows of the chunk's 64 tokens, into LDS after the
-  // reduction buffer (16-byte pieces XOR-swizzled by token), then stored as
-  // whole rows by every wave: dK at rows tpos - q0 of dk, dV of dv
-  static_assert(sizeof(float) * 2 * 2 * (D / 32) * 16 * 64 + 2 * kChunk * RB <= sizeof(sm.q) + sizeof(sm.g),
-                "the output tiles fit after the reduction buffer");
-  char* otile = reinterpret_cast<char*>(&sm.q[0][0]) + sizeof(float) * 2 * 2 * (D / 32) * 16 * 64;
-  if (rw == 0) {
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const float4 rk = red[slot(0, db, a4)], rv = red[slot(1, db, a4)];
+          const float ak[4] = {rk.x, rk.y, rk.z, rk.w}, av[4] = {rv.x, rv.y, rv.z, rv.w};
+          bf16x4 k4, v4;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        bf16x4 k4, v4;
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int i = 4 * jj + ii;
-          k4[ii] = (__bf16)((dk[db][i] + red[slot(0, db, i)]) * S.scale);
-          v4[ii] = (__bf16)(dv[db][i] + red[slot(1, db, i)]);
+          for (int ii = 0; ii < 4; ++ii) {
+            k4[ii] = (__bf16)((dk[db][4 * a4 + ii] + ak[ii]) * S.scale);
+            v4[ii] = (__bf16)(dv[db][4 * a4 + ii] + av[ii]);
+          }
+          const int off = tok * RB + (((4 * db + a4) ^ (tok & (NP - 1))) << 4) + 8 * hl;
+          *reinterpret_cast<u32x2*>(otile + off) = __builtin_bit_cast(u32x2, k4);
+          *reinterpret_cast<u32x2*>(otile + kChunk * RB + off) = __builtin_bit_cast(u32x2, v4);
         }
-        const int off = tok * RB + (((4 * db + jj) ^ (tok & (NP - 1))) << 4) + 8 * hl;
-        *reinterpret_cast<u32x2*>(otile + off) = __builtin_bit_cast(u32x2, k4);
-        *reinterpret_cast<u32x2*>(otile + kChunk * RB + off) = __builtin_bit_cast(u32x2, v4);
-      }
+    }
+    __syncthreads();
   }
-  __syncthreads();
+  // every wave stores whole rows: dK at rows tpos - q0 of dk, dV of dv
   constexpr int RPR = 64 / NP;   // token rows per store instruction
+  static_assert((2 * kChunk) % (kKV16Waves * RPR) == 0, "the output rows split evenly over the waves");
 #pragma unroll
-  for (int i = 0; i < 2 * kChunk / (kKVWaves * RPR); ++i) {
-    const int rowi = (i * kKVWaves + wave) * RPR + lane / NP;   // 0 .. 127: dK rows, then dV rows
+  for (int i = 0; i < 2 * kChunk / (kKV16Waves * RPR); ++i) {
+    const int rowi = (i * kKV16Waves + wave) * RPR + lane / NP;   // 0 .. 127: dK rows, then dV rows
     const int tk = rowi & (kChunk - 1), pc = lane % NP;
     const int64_t p = t0 + tk;
     if (p < S.q0 || p >= lq) continue;
@@ -836,11 +887,11 @@ hipError_t launch_attend_backward(const Shape& s, const void* q, const KVSrc& kv
   if (s.d == 128) {
     if (tiered) bwd_dq_kernel<128, true><<<gq, dim3(kAttnThreads), 0, st>>>(A);
     else bwd_dq_kernel<128, false><<<gq, dim3(kAttnThreads), 0, st>>>(A);
-    bwd_dkv_kernel<128><<<gkv, dim3(kKVThreads), 0, st>>>(A);
+    bwd_dkv_kernel<128><<<gkv, dim3(kKV16Threads), 0, st>>>(A);
   } else if (s.d == 64) {
     if (tiered) bwd_dq_kernel<64, true><<<gq, dim3(kAttnThreads), 0, st>>>(A);
     else bwd_dq_kernel<64, false><<<gq, dim3(kAttnThreads), 0, st>>>(A);
-    bwd_dkv_kernel<64><<<gkv, dim3(kKVThreads), 0, st>>>(A);
+    bwd_dkv_kernel<64><<<gkv, dim3(kKV16Threads), 0, st>>>(A);
   } else {
     return hipErrorInvalidValue;
   }
