@@ -536,14 +536,25 @@ __global__ __launch_bounds__(kKV16Threads) void bwd_dkv_kernel(BwdArgs A) {
       const int rlim = tok_ok ? nrows - base : 0;
       const int dpos = diag ? (int)(tpos - sq) : INT_MIN;
       bf16x8 pf[2], sf[2];
+      // (the accumulators' slots cr reach 27: with rlim >= 28 off the own
+      // chunk every pair of the lane is visible, and the wave takes the
+      // plain form when that holds in every lane)
+      if (__all(!diag && rlim >= 28)) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int cr = 8 * (r >> 2) + (r & 3);
-        const bool vis = cr < rlim && ((base + cr) & (S.B - 1)) >= dpos;
-        const float p = __builtin_amdgcn_exp2f(fmaf(vis ? sacc[r] : -INFINITY, sl2, -lr[r] * kLog2e));
-        const float ds = p * (pacc[r] - dr[r]);
-        pf[r >> 3][r & 7] = (__bf16)p;
-        sf[r >> 3][r & 7] = (__bf16)ds;
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[r], sl2, -lr[r] * kLog2e));
+          pf[r >> 3][r & 7] = (__bf16)p;
+          sf[r >> 3][r & 7] = (__bf16)(p * (pacc[r] - dr[r]));
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int cr = 8 * (r >> 2) + (r & 3);
+          const bool vis = cr < rlim && ((base + cr) & (S.B - 1)) >= dpos;
+          const float p = __builtin_amdgcn_exp2f(fmaf(vis ? sacc[r] : -INFINITY, sl2, -lr[r] * kLog2e));
+          pf[r >> 3][r & 7] = (__bf16)p;
+          sf[r >> 3][r & 7] = (__bf16)(p * (pacc[r] - dr[r]));
+        }
       }
 #pragma unroll
       for (int mm = 0; mm < 2; ++mm) {
