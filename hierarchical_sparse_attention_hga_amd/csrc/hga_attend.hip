@@ -364,18 +364,23 @@ __global__ __launch_bounds__(kAttnThreads) void route_attend_bf16_kernel(FusedAr
   item_of_block(S, F.a.wg_per_item, &b, &h, &z);
   Plan P;
   plan_windows(S, b, &P);
-  // fixed tiles need no routing: the first two (one per stage) load while
-  // the router runs
-  const int pre = P.nfix < kAttnStages ? P.nfix : kAttnStages;
-  for (int t = 0; t < pre; ++t) {
-    const int m = t < P.a ? t : (int)(P.bb + (t - P.a));   // chunk of fixed tile t
-    const uint32_t off = (uint32_t)(t * kChunk * D * 2);
-    issue_tile<D, false>(kv_rows<D, false>(F.a, h), lds_addr(&sm.k[0][0]) + off, lds_addr(&sm.v[0][0]) + off,
-                  [&](int, int sl) -> int { return m * kChunk + sl; });
-  }
   // the attention's query operands load while the router runs
   bf16x8 qf[D / 16];
   load_q_operands<D>(F.a, b, h, z, qf);
+  // fixed tiles need no routing: the first two (one per stage) load while
+  // the router runs, once its block query is formed (issued earlier, the
+  // tiles' bytes delayed the router's first loads)
+  const int pre = P.nfix < kAttnStages ? P.nfix : kAttnStages;
+  // (captures by value: captured references would keep the locals in
+  // scratch memory)
+  auto prefetch = [pre, pa = (int)P.a, pbb = (int)P.bb, kvr = kv_rows<D, false>(F.a, h),
+                   kl = lds_addr(&sm.k[0][0]), vl = lds_addr(&sm.v[0][0])]() {
+    for (int t = 0; t < pre; ++t) {
+      const int m = t < pa ? t : pbb + (t - pa);   // chunk of fixed tile t
+      const uint32_t off = (uint32_t)(t * kChunk * D * 2);
+      issue_tile<D, false>(kvr, kl + off, vl + off, [m](int, int sl) -> int { return m * kChunk + sl; });
+    }
+  };
   const bool wr = z == 0;
   int32_t* gout = F.r.group_idx + ((int64_t)b * S.hkv + h) * S.kg;
   const int g = S.g;
@@ -383,7 +388,7 @@ __global__ __launch_bounds__(kAttnThreads) void route_attend_bf16_kernel(FusedAr
   const int nsg = route::route_item<uint16_t, false>(F.r, b, h, rsm, wr, [runs, wr, gout, g](int rank, int group) {
     runs[rank] = group * g;
     if (wr) gout[rank] = group;
-  });
+  }, prefetch);
   __syncthreads();
   P.nrouted = nsg;
   P.nrt = (nsg + kChunk / g - 1) / (kChunk / g);

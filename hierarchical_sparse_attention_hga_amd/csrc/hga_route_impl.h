@@ -273,9 +273,16 @@ struct RouteArgs {
 // ascending groups), by wave 0 or spread over the workgroup; the caller
 // synchronises before reading what it stored. With write_out the item's rows
 // of chunk_idx, group_idx (-1 padding; the kept entries are left to emit) and
-// n_sel are written. Returns the number of kept groups.
-template <typename T, bool kPipelined, typename GroupEmit>
-__device__ int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm, bool write_out, GroupEmit emit) {
+// n_sel are written. Returns the number of kept groups. after_query() is
+// called by every thread once the block query is formed (the fused kernel
+// starts its first key/value tile loads there, behind the router's first
+// loads).
+struct NoHook {
+  __device__ void operator()() const {}
+};
+template <typename T, bool kPipelined, typename GroupEmit, typename AfterQuery = NoHook>
+__device__ int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm, bool write_out, GroupEmit emit,
+                          AfterQuery after_query = {}) {
   constexpr int E = Slice<T>::E;
   constexpr int kRowsPerThread = 8;   // block-query rows loaded per thread per round
   const Shape& S = a.s;
@@ -339,6 +346,7 @@ __device__ int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm, bool 
     }
     __syncthreads();
   }
+  after_query();
 
   const int64_t orow = (int64_t)b * S.hkv + h;
   // ---- 2-3. chunk stage
