@@ -127,7 +127,11 @@ CASES = {
     "no_budget": dict(top_chunks=0, top_groups=0),
     "d64": dict(d=64),
     "group4": dict(group=4, top_groups=20),
-    "block4_320_blocks": dict(q_block=4, L=2048, n_q=1280),   # attending lists in two passes of 256 blocks
+    "block4_320_blocks": dict(q_block=4, L=2048, n_q=1280),
+    # more blocks than one dK/dV list pass holds (512 per pass in the bf16
+    # kernel): chunks whose first block lies in the second pass
+    "block2_640_blocks": dict(q_block=2, L=2048, n_q=1280),
+    "f32_block4_320_blocks": dict(dtype="f32", d=64, rope_theta=None, q_block=4, L=2048, n_q=1280),   # 256 per pass
     "f32": dict(dtype="f32", d=64, rope_theta=None),
     "f32_block16_d32": dict(dtype="f32", d=32, q_block=16, n_q=496, rope_theta=None),
 }
