@@ -639,7 +639,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(the path shards by KV head with no exchange; see DESIGN.md)", file=sys.stderr)
+              "(the path would shard by KV head, each GPU running its heads' items with no exchange)", file=sys.stderr)
         sys.exit(2)
     import torch
     torch.cuda.init()
