@@ -406,7 +406,9 @@ def decode_line(cfg_id, batch, steps, warmup):
     """One-token decoding steps over a batch of sequences at the end of
     workload cfg_id's sequence (position L - 1, history L - 1 tokens): per
     step, hga_route_attend with q_block 1 over the resident summaries of the
-    closed chunks. The batch is folded into the heads (sequence-major
+    closed chunks, given the workspace hga_workspace_size asks for (nonzero
+    for few items: the attention then spreads each item over several
+    workgroups). The batch is folded into the heads (sequence-major
     [batch x heads]); every sequence repeats the workload's K/V and last query
     at its own addresses. Summaries are built before timing (each closes once
     per 64 generated tokens). Timed with HIP events around one launch in eight on the
@@ -435,9 +437,11 @@ def decode_line(cfg_id, batch, steps, warmup):
     lse = torch.empty(hq, 1, device=DEV)
     pos = L - 1
     hga.hga_build_summaries_range(c, k, L, 0, pos // 64, gs, cs)
+    wsb = hga.hga_workspace_size(c, L, 1, hga.HGA_WS_ATTEND)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=DEV)
 
     def one():
-        hga.hga_route_attend(c, q, pos, 1, L, cs, gs, k, v, ci, gi, ns, out, lse)
+        hga.hga_route_attend(c, q, pos, 1, L, cs, gs, k, v, ci, gi, ns, out, lse, ws, wsb)
     for _ in range(warmup):
         one()
     torch.cuda.synchronize()
@@ -456,11 +460,14 @@ def decode_line(cfg_id, batch, steps, warmup):
     nsel = ns.cpu().numpy().reshape(hkv, 2)
     byts = float(sum(decode_bytes(base, pos, nsel[h]) for h in range(hkv)))
     # one kernel unless the block has more than two scoring rounds of chunk
-    # candidates (then the router kernel, then the attention kernel)
-    fused = pos // 64 - base["sink"] // 64 - base["local"] // 64 <= 512 and base["hq"] // base["hkv"] <= 256
-    kname = "route_attend_bf16" if fused else "route_kernel + attend_bf16"
+    # candidates (then the router kernel, then the attention kernel) or the
+    # attention spreads the items (router, ranges, merge)
+    fused = (pos // 64 - base["sink"] // 64 - base["local"] // 64 <= 512 and base["hq"] // base["hkv"] <= 256
+             and wsb == 0)
+    kname = ("route_attend_bf16" if fused else
+             "route_kernel + attend_split_bf16 + attend_combine" if wsb else "route_kernel + attend_bf16")
     traffic = measured_traffic(f"{base['name']}-decode-b{batch}", "route_attend_bf16") if fused else None
-    del k, v, gs, cs
+    del k, v, gs, cs, ws
     torch.cuda.empty_cache()
     return {"value": steps * batch / wall, "unit": "generated tokens/s", "kernel_us_mean": us,
             "ms_per_step": wall / steps * 1e3,

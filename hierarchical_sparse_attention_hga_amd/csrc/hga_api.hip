@@ -134,7 +134,7 @@ size_t hga_workspace_size(const hga_config* cfg, int64_t seq_len, int64_t n_q, i
   if (make_shape(cfg, seq_len, seq_len - n_q, n_q, &s) != HGA_OK) return (size_t)-1;
   switch (which) {
     case HGA_WS_ROUTE: return 0;
-    case HGA_WS_ATTEND: return 0;
+    case HGA_WS_ATTEND: return hga::attend_split_bytes(s);
     case HGA_WS_ATTEND_TIERED: return hga::tier_cache_bytes(s, seq_len - n_q);
     case HGA_WS_BACKWARD: return hga::backward_workspace_bytes(s);
     case HGA_WS_BACKWARD_TIERED:
@@ -211,7 +211,7 @@ hga_status hga_stream_forward(const hga_config* cfg, const void* q, const void* 
       st = device_status(hga::launch_route(seg, qs, chunk_sum, nullptr, group_sum, 0, ci, gi, ns, hs),
                          "hga_stream_forward routing launch");
       if (st == HGA_OK)
-        st = device_status(hga::launch_attend(seg, qs, kv, gi, ns, os, ls, nullptr, hs),
+        st = device_status(hga::launch_attend(seg, qs, kv, gi, ns, os, ls, nullptr, 0, hs),
                            "hga_stream_forward attention launch");
     }
     if (st != HGA_OK) return st;
@@ -252,7 +252,7 @@ hga_status hga_attend(const hga_config* cfg, const void* q, int64_t q_start, int
   if ((st = check_tier(v, "v", seq_len, q_start)) != HGA_OK) return st;
   if ((st = check_kv_tier(s, k, v, workspace, ws_bytes)) != HGA_OK) return st;
   hga::KVSrc kv{k->host, k->dev, v->host, v->dev, k->split};
-  return device_status(hga::launch_attend(s, q, kv, group_idx, n_sel, out, lse, workspace, (hipStream_t)stream),
+  return device_status(hga::launch_attend(s, q, kv, group_idx, n_sel, out, lse, workspace, ws_bytes, (hipStream_t)stream),
                        "hga_attend launch");
 }
 
@@ -275,7 +275,11 @@ hga_status hga_route_attend(const hga_config* cfg, const void* q, int64_t q_star
   const float* gs_host = static_cast<const float*>(group_sum->host);
   const float* gs_dev = static_cast<const float*>(group_sum->dev);
   hga::KVSrc kv{k->host, k->dev, v->host, v->dev, k->split};
-  if (hga::fused_route_attend_supported(s, k->split))
+  // the fused kernel, unless the workspace lets the attention spread few
+  // items over more workgroups
+  const bool split = k->split == 0 && hga::attend_split_count(s) > 1 && workspace &&
+                     ws_bytes >= hga::attend_split_bytes(s);
+  if (!split && hga::fused_route_attend_supported(s, k->split))
     return device_status(hga::launch_route_attend(s, q, chunk_sum, gs_host, gs_dev, group_sum->split, kv,
                                                   chunk_idx, group_idx, n_sel, out, lse, hs),
                          "hga_route_attend launch");
@@ -283,7 +287,7 @@ hga_status hga_route_attend(const hga_config* cfg, const void* q, int64_t q_star
                                        n_sel, hs),
                      "hga_route_attend routing launch");
   if (st != HGA_OK) return st;
-  return device_status(hga::launch_attend(s, q, kv, group_idx, n_sel, out, lse, workspace, hs),
+  return device_status(hga::launch_attend(s, q, kv, group_idx, n_sel, out, lse, workspace, ws_bytes, hs),
                        "hga_route_attend attention launch");
 }
 
@@ -329,6 +333,6 @@ const char* hga_status_string(hga_status status) {
 
 const char* hga_last_error(void) { return g_err; }
 
-int32_t hga_version(void) { return 105; }
+int32_t hga_version(void) { return 106; }
 
 }  // extern "C"

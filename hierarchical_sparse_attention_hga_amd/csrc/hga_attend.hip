@@ -60,14 +60,27 @@ __device__ inline void load_q_operands(const AttnArgs& A, int b, int h, int z, b
   }
 }
 
-// Attention of item (b, h), workgroup slot z, over the token set of plan P
-// (runs in sm.runs). The caller has loaded the queries (qpre) and already
-// issued the loads of the first pre_tiles tiles (at most kAttnStages), tile t
-// into stage t.
+// Per wave of a split workgroup, the partial state of its 32 query columns:
+// the unnormalized O^T accumulators (D / 2 per lane), the running maximum
+// (log2 units) and the row sum, each as 64 lane-contiguous floats.
+template <int D>
+constexpr int kPartFloats = (D / 2 + 2) * 64;
+
+template <int D>
+__device__ __attribute__((always_inline)) void store_output(const AttnArgs& A, int b, int h, int z, AttnSmem<D>& sm,
+                                                            const f32x16* o, float m_run, float l_tot);
+
+// Attention of item (b, h), workgroup slot z, over tiles [ta, te) of the
+// token set of plan P (runs in sm.runs). The caller has loaded the queries
+// (qpre) and already issued the loads of the range's first pre_tiles tiles
+// (at most kAttnStages), the range's tile i into stage i. With part == NULL
+// the range is the whole set and the output is stored; otherwise each wave
+// leaves its partial state at part + wave * kPartFloats<D>.
 template <int D, bool kTiered>
 __device__ __attribute__((always_inline)) void attend_bf16_body(const AttnArgs& A, int b, int h, int z,
                                                                 const Plan& P, AttnSmem<D>& sm, int pre_tiles,
-                                                                const bf16x8* qpre) {
+                                                                const bf16x8* qpre, int ta, int te,
+                                                                float* part) {
   constexpr int NP = D / 8;
   constexpr int RPI = 64 / NP;
   constexpr int RPW = kChunk / kAttnWaves;
@@ -77,6 +90,7 @@ __device__ __attribute__((always_inline)) void attend_bf16_body(const AttnArgs& 
   static_assert(KI >= 1 && kAttnStages >= 2 && kAttnStages <= 4 && kPerTile * kAhead <= 63, "tile shape");
   const Shape& S = A.s;
   const int nt = P.ntiles;
+  const int nl = te - ta;                    // tiles of the range
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5;                  // lane half
@@ -87,11 +101,7 @@ __device__ __attribute__((always_inline)) void attend_bf16_body(const AttnArgs& 
   const int rb = z * kAttnWaves + wave;      // 32-row block of the item
   const bool active = 32 * rb < nrows;       // the wave has rows of the item
   const int row = 32 * rb + col;
-  const bool live = row < nrows;             // this lane's column is a query row
-  const int lgB = __ffs(S.B) - 1;
-  const int head = h * S.G + (row >> lgB);
   const int qi = row & (S.B - 1);            // position within the block
-  const int64_t qrow = (int64_t)b * S.B + qi;  // row of Q / O
 
   // queries of this lane's column, loaded by the caller (load_q_operands)
   bf16x8 qf[D / 16];
@@ -121,7 +131,7 @@ __device__ __attribute__((always_inline)) void attend_bf16_body(const AttnArgs& 
   const int diag0 = (int)(kTiered ? P.c0 - A.kv.split : P.c0);   // source row of the last tile's first slot
   const int dlim = P.dlim;
   auto issue = [&](int t) {
-    const uint32_t off = (uint32_t)((t % kAttnStages) * kChunk * D * 2);
+    const uint32_t off = (uint32_t)(((t - ta) % kAttnStages) * kChunk * D * 2);
     issue_tile<D, kTiered>(kv, lds_addr(&sm.k[0][0]) + off, lds_addr(&sm.v[0][0]) + off, [&](int i, int sl) -> int {
       if (t < P.nfix) return kTiered ? raw[i] + sl : (int)((t < P.a ? t : P.bb + (t - P.a)) * kChunk) + sl;
       if (t < P.nfix + P.nrt) return run_of(t, sl) < P.nrouted ? raw[i] + (sl & ((1 << lg) - 1)) : 0;
@@ -164,18 +174,19 @@ __device__ __attribute__((always_inline)) void attend_bf16_body(const AttnArgs& 
   // pre_tiles among them). At iteration t, once tile t has landed, tile
   // t + kAttnStages - 1 goes into the stage tile t - 1 left; the run-table
   // entries of the next tile to issue are always read one issue ahead.
-  for (int u = 0; u < kAttnStages - 1 && u < nt; ++u)
+  for (int u = 0; u < kAttnStages - 1 && u < nl; ++u)
     if (u >= pre_tiles) {
-      fetch(u);
-      issue(u);
+      fetch(ta + u);
+      issue(ta + u);
     }
-  fetch(kAttnStages - 1);
+  fetch(ta + kAttnStages - 1);
   // One tile per call; the stage is a compile-time constant (the loop below
   // takes the tiles two at a time), so it folds into the LDS reads' offsets.
   static_assert(kAttnStages == 2, "the tile loop alternates two stages");
-  auto step = [&](int t, auto stage_c) __attribute__((always_inline)) {
+  auto step = [&](int i, auto stage_c) __attribute__((always_inline)) {
+    const int t = ta + i;   // tile i of the range
     // this thread's loads of tile t are done once only newer tiles are pending
-    const int ahead = nt - 1 - t < kAhead ? nt - 1 - t : kAhead;
+    const int ahead = nl - 1 - i < kAhead ? nl - 1 - i : kAhead;
     if (kAhead >= 2 && ahead >= 2)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPerTile));
     else if (kAhead >= 1 && ahead >= 1)
@@ -183,8 +194,8 @@ __device__ __attribute__((always_inline)) void attend_bf16_body(const AttnArgs& 
     else
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();   // every wave's loads of tile t landed; tile t - 1 is free
-    if (t + kAttnStages - 1 < nt) {
-      if (t + kAttnStages - 1 >= pre_tiles) issue(t + kAttnStages - 1);
+    if (i + kAttnStages - 1 < nl) {
+      if (i + kAttnStages - 1 >= pre_tiles) issue(t + kAttnStages - 1);
       fetch(t + kAttnStages);
     }
     if (!active) return;
@@ -274,10 +285,43 @@ __device__ __attribute__((always_inline)) void attend_bf16_body(const AttnArgs& 
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfa[tb][db][mm], pf[mm], o[db], 0, 0, 0);
     }
   };
-  for (int t = 0; t < nt; t += 2) {
-    step(t, std::integral_constant<int, 0>{});
-    if (t + 1 < nt) step(t + 1, std::integral_constant<int, 1>{});
+  for (int i = 0; i < nl; i += 2) {
+    step(i, std::integral_constant<int, 0>{});
+    if (i + 1 < nl) step(i + 1, std::integral_constant<int, 1>{});
   }
+  if (part) {
+    if (active) {
+      float* pw = part + (size_t)wave * kPartFloats<D>;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pw[(db * 16 + r) * 64 + lane] = o[db][r];
+      pw[(D / 2) * 64 + lane] = m_run;
+      pw[(D / 2 + 1) * 64 + lane] = pair_sum(l_run);
+    }
+    return;
+  }
+  store_output<D>(A, b, h, z, sm, o, m_run, active ? pair_sum(l_run) : 0.0f);
+}
+
+// Normalize and store the output rows of item (b, h), slot z, from each
+// wave's O^T accumulators, running maximum and row sum.
+template <int D>
+__device__ __attribute__((always_inline)) void store_output(const AttnArgs& A, int b, int h, int z, AttnSmem<D>& sm,
+                                                            const f32x16* o, float m_run, float l_tot) {
+  constexpr int NP = D / 8;
+  constexpr int RB = D * 2;
+  const Shape& S = A.s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5, col = lane & 31;
+  const int nrows = S.G * S.B;
+  const int rb = z * kAttnWaves + wave;
+  const bool active = 32 * rb < nrows;
+  const int row = 32 * rb + col;
+  const bool live = row < nrows;
+  const int lgB = __ffs(S.B) - 1;
+  const int head = h * S.G + (row >> lgB);
+  const int64_t qrow = (int64_t)b * S.B + (row & (S.B - 1));
 
   // Output: each wave writes its normalized 32 x D tile to LDS (the stage
   // ring is free once every wave has left the loop), then stores it back
@@ -287,7 +331,6 @@ __device__ __attribute__((always_inline)) void attend_bf16_body(const AttnArgs& 
   static_assert(kAttnWaves * 32 * RB <= sizeof(sm.k) + sizeof(sm.v), "output tiles fit in the stage ring");
   __syncthreads();
   if (active) {
-    const float l_tot = pair_sum(l_run);
     const float inv = 1.0f / l_tot;   // columns past the item's rows are never stored
     char* tile = reinterpret_cast<char*>(&sm.k[0][0]) + wave * (32 * RB);
 #pragma unroll
@@ -341,7 +384,7 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(AttnArgs A) {
   load_q_operands<D>(A, b, h, z, qf);
   const Plan P = make_plan(A.s, b, h, A.gidx, A.nsel, sm.runs, sm.scan, kMaxRoutedAttn);
   if (kTiered) translate_plan(A.kv.split, A.nch, A.slot, h, P, sm.runs, sm.runs + kMaxRoutedAttn);
-  attend_bf16_body<D, kTiered>(A, b, h, z, P, sm, pre, qf);
+  attend_bf16_body<D, kTiered>(A, b, h, z, P, sm, pre, qf, 0, P.ntiles, nullptr);
 }
 
 // Route, then attend, in one workgroup per (item, slot): the router's kept
@@ -393,7 +436,72 @@ __global__ __launch_bounds__(kAttnThreads) void route_attend_bf16_kernel(FusedAr
   P.nrouted = nsg;
   P.nrt = (nsg + kChunk / g - 1) / (kChunk / g);
   P.ntiles = P.nfix + P.nrt + 1;
-  attend_bf16_body<D, false>(F.a, b, h, z, P, sm, pre, qf);
+  attend_bf16_body<D, false>(F.a, b, h, z, P, sm, pre, qf, 0, P.ntiles, nullptr);
+}
+
+// ------------------------------------------------------------ split items
+constexpr int kSplitMax = 32;   // ranges per item at most
+// For calls with few items (decoding a few sequences), each item's tile list
+// is cut into nsplit contiguous ranges, one workgroup each; every workgroup
+// leaves its waves' partial softmax states (relative to their own running
+// maxima) in the workspace, and attend_combine_kernel merges them per query
+// row: m = max m_s, O = sum O_s 2^(m_s - m), l = sum l_s 2^(m_s - m).
+template <int D>
+__global__ __launch_bounds__(kAttnThreads) void attend_split_bf16_kernel(AttnArgs A, float* part, int nsplit) {
+  __shared__ AttnSmem<D> sm;
+  const int nwg = (int)(A.s.nb * A.s.hkv) * A.wg_per_item;
+  const int lid = xcd_index(nwg * nsplit);   // the ranges of one item stay on one XCD
+  const int wgi = lid / nsplit, sidx = lid % nsplit;
+  int b, h, z;
+  item_of_index(A.s, A.wg_per_item, wgi, &b, &h, &z);
+  bf16x8 qf[D / 16];
+  load_q_operands<D>(A, b, h, z, qf);
+  const Plan P = make_plan(A.s, b, h, A.gidx, A.nsel, sm.runs, sm.scan, kMaxRoutedAttn);
+  const int per = (P.ntiles + nsplit - 1) / nsplit;
+  const int ta = sidx * per < P.ntiles ? sidx * per : P.ntiles;
+  const int te = ta + per < P.ntiles ? ta + per : P.ntiles;
+  attend_bf16_body<D, false>(A, b, h, z, P, sm, 0, qf, ta, te,
+                             part + ((size_t)wgi * nsplit + sidx) * kAttnWaves * kPartFloats<D>);
+}
+
+template <int D>
+__global__ __launch_bounds__(kAttnThreads) void attend_combine_kernel(AttnArgs A, const float* part, int nsplit) {
+  __shared__ AttnSmem<D> sm;
+  int b, h, z;
+  item_of_block(A.s, A.wg_per_item, &b, &h, &z);
+  const int nwg = (int)(A.s.nb * A.s.hkv) * A.wg_per_item;
+  const int wgi = xcd_index(nwg);
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const bool active = 32 * (z * kAttnWaves + wave) < A.s.G * A.s.B;
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
+  float m = -INFINITY, l = 0.0f;
+  if (active) {
+    const float* pw = part + (size_t)wgi * nsplit * kAttnWaves * kPartFloats<D> + (size_t)wave * kPartFloats<D>;
+    const size_t stride = (size_t)kAttnWaves * kPartFloats<D>;   // from one range to the next
+    float mv[kSplitMax];   // the ranges' maxima, all loads in flight at once
+#pragma unroll
+    for (int sp = 0; sp < kSplitMax; ++sp)
+      mv[sp] = sp < nsplit ? __builtin_nontemporal_load(pw + sp * stride + (D / 2) * 64 + lane) : -INFINITY;
+#pragma unroll
+    for (int sp = 0; sp < kSplitMax; ++sp) m = __builtin_fmaxf(m, mv[sp]);
+    // every row sees the first slot of the item's first tile, so m is finite
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float* ps = pw + sp * stride;
+      float v[D / 2 + 2];   // all of the range's loads in flight at once
+#pragma unroll
+      for (int j = 0; j < D / 2 + 2; ++j) v[j] = __builtin_nontemporal_load(ps + j * 64 + lane);
+      const float ms = v[D / 2];
+      const float w = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - m);   // ranges with no tile
+      l = fmaf(v[D / 2 + 1], w, l);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] = fmaf(v[db * 16 + r], w, o[db][r]);
+    }
+  }
+  store_output<D>(A, b, h, z, sm, o, m, l);
 }
 
 // ------------------------------------------------------------ float32 SIMT kernel
@@ -649,13 +757,53 @@ hipError_t prepare_tier_cache(const Shape& s, const KVSrc& kv, const int32_t* gr
   return hipGetLastError();
 }
 
+// Ranges per item of the split attention: with at most kSplitMaxWgs
+// workgroups the items alone leave most of the 256 compute units idle, so
+// each item's tiles are cut into ranges of about kSplitTiles tiles, up to
+// about 256 workgroups in all. 1 = no split. The tile count is bounded by
+// the fixed chunks, the kept groups' tiles and the block's own chunk.
+constexpr int64_t kSplitMaxWgs = 128;
+constexpr int kSplitTiles = 2;
+int attend_split_count(const Shape& s) {
+  if (s.dtype != HGA_BF16 || (s.d != 128 && s.d != 64)) return 1;
+  const int64_t wgs = s.nb * s.hkv * bf16_wg_per_item(s);
+  if (wgs == 0 || wgs > kSplitMaxWgs) return 1;
+  const int64_t max_tiles = s.sink_chunks + s.local_chunks + ((int64_t)s.kg * s.g + kChunk - 1) / kChunk + 1;
+  int64_t n = (max_tiles + kSplitTiles - 1) / kSplitTiles;
+  if (n > 256 / wgs) n = 256 / wgs;
+  if (n > kSplitMax) n = kSplitMax;
+  return n >= 2 ? (int)n : 1;
+}
+
+size_t attend_split_bytes(const Shape& s) {
+  const int n = attend_split_count(s);
+  if (n == 1) return 0;
+  const size_t per = (size_t)kAttnWaves * (s.d / 2 + 2) * 64 * sizeof(float);
+  return (size_t)(s.nb * s.hkv * bf16_wg_per_item(s)) * n * per;
+}
+
 hipError_t launch_attend(const Shape& s, const void* q, const KVSrc& kv, const int32_t* group_idx,
-                         const int32_t* n_sel, void* out, float* lse, void* workspace, hipStream_t st) {
+                         const int32_t* n_sel, void* out, float* lse, void* workspace, size_t ws_bytes,
+                         hipStream_t st) {
   const int64_t items = s.nb * s.hkv;
   if (items == 0) return hipSuccess;
   AttnArgs a{};
   a.q = q; a.kv = kv; a.gidx = group_idx; a.nsel = n_sel; a.out = out; a.lse = lse; a.s = s;
   const bool tiered = kv.split > 0;
+  const int nsplit = tiered ? 1 : attend_split_count(s);
+  if (nsplit > 1 && workspace && ws_bytes >= attend_split_bytes(s)) {
+    a.wg_per_item = bf16_wg_per_item(s);
+    float* part = static_cast<float*>(workspace);
+    const unsigned nwg = (unsigned)(items * a.wg_per_item);
+    if (s.d == 128) {
+      attend_split_bf16_kernel<128><<<dim3(nwg * nsplit), dim3(kAttnThreads), 0, st>>>(a, part, nsplit);
+      attend_combine_kernel<128><<<dim3(nwg), dim3(kAttnThreads), 0, st>>>(a, part, nsplit);
+    } else {
+      attend_split_bf16_kernel<64><<<dim3(nwg * nsplit), dim3(kAttnThreads), 0, st>>>(a, part, nsplit);
+      attend_combine_kernel<64><<<dim3(nwg), dim3(kAttnThreads), 0, st>>>(a, part, nsplit);
+    }
+    return hipGetLastError();
+  }
   if (tiered) {
     TierCache tc;
     const hipError_t e = prepare_tier_cache(s, kv, group_idx, n_sel, workspace, &tc, st);

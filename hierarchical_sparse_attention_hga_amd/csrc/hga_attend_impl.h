@@ -197,14 +197,19 @@ __device__ inline const T* src_ptr(const T* dev_head, const T* cache, int src, i
 // (neighbouring query blocks, which share sink, local and often routed
 // chunks) are kept on the same XCD: the dispatcher deals workgroups to the 8
 // XCDs round-robin, so block id x runs on XCD x % 8.
-__device__ inline void item_of_block(const Shape& S, int wpi, int* b, int* h, int* z) {
-  const int nwg = (int)(S.nb * S.hkv) * wpi;
+__device__ inline int xcd_index(int n) {
   int lid = blockIdx.x;
-  if (nwg % 8 == 0) lid = (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8;
+  if (n % 8 == 0) lid = (blockIdx.x % 8) * (n / 8) + blockIdx.x / 8;
+  return lid;
+}
+__device__ inline void item_of_index(const Shape& S, int wpi, int lid, int* b, int* h, int* z) {
   *z = lid % wpi;
   const int item = lid / wpi;       // head-major: item = h * nb + b
   *h = item / (int)S.nb;
   *b = item % (int)S.nb;
+}
+__device__ inline void item_of_block(const Shape& S, int wpi, int* b, int* h, int* z) {
+  item_of_index(S, wpi, xcd_index((int)(S.nb * S.hkv) * wpi), b, h, z);
 }
 
 // ------------------------------------------------------------ bf16 MFMA kernel

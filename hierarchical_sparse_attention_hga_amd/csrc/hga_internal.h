@@ -85,7 +85,12 @@ hipError_t prepare_tier_cache(const Shape& s, const KVSrc& kv, const int32_t* gr
                               void* workspace, TierCache* tc, hipStream_t st);
 
 hipError_t launch_attend(const Shape& s, const void* q, const KVSrc& kv, const int32_t* group_idx,
-                         const int32_t* n_sel, void* out, float* lse, void* workspace, hipStream_t st);
+                         const int32_t* n_sel, void* out, float* lse, void* workspace, size_t ws_bytes,
+                         hipStream_t st);
+// Ranges per item when launch_attend spreads each item's tiles over several
+// workgroups (1: one workgroup per item), and the workspace that takes.
+int attend_split_count(const Shape& s);
+size_t attend_split_bytes(const Shape& s);
 
 // Routing and attention in one kernel (bfloat16, K/V all on the device).
 bool fused_route_attend_supported(const Shape& s, int64_t kv_split);

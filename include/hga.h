@@ -107,6 +107,12 @@ enum {
 /* Bytes of device workspace that hga_route (which = HGA_WS_ROUTE) or
  * hga_attend / hga_route_attend (HGA_WS_ATTEND with everything on the device,
  * HGA_WS_ATTEND_TIERED with K/V split at a token > 0) needs for this shape.
+ * HGA_WS_ATTEND is 0 unless the call has few (block, KV head) items (bf16, at
+ * most 128 attention workgroups, as when decoding a few sequences): then it
+ * is the room for each item's tiles to be cut into ranges attended by
+ * separate workgroups, whose partial softmax states are merged per query row
+ * (the outputs then differ from the one-workgroup result by float32 rounding
+ * order only). Given less, the calls attend each item in one workgroup.
  * The tiered figure holds for every split <= seq_len - n_q: it covers chunk
  * flags and slots and an HBM cache as large as the whole host part of K and V
  * (the attention copies each history chunk any query block needs into it once
@@ -191,7 +197,9 @@ hga_status hga_route(const hga_config* cfg, const void* q, int64_t q_start, int6
  *              [0, top_groups]) is how many entries of the row to read.
  *   out        device, [Hq][n_q][d] of cfg->dtype.
  *   lse        device, [Hq][n_q] float32, or NULL.
- *   workspace  device, at least hga_workspace_size(...) bytes. */
+ *   workspace  device, at least hga_workspace_size(...) bytes (with split 0,
+ *              NULL or fewer bytes than HGA_WS_ATTEND asks for is accepted:
+ *              each item is then attended by one workgroup). */
 hga_status hga_attend(const hga_config* cfg, const void* q, int64_t q_start, int64_t n_q,
                       int64_t seq_len, const hga_tiered* k, const hga_tiered* v,
                       const int32_t* group_idx, const int32_t* n_sel,
@@ -209,7 +217,10 @@ hga_status hga_attend(const hga_config* cfg, const void* q, int64_t q_start, int
  * 32K tokens), both steps run in one kernel, each workgroup routing its own
  * query block before attending over the groups it kept; otherwise the call
  * runs the two steps one after the other (the results are the same either
- * way). Errors are those of either call. */
+ * way). When the workspace holds what HGA_WS_ATTEND asks for (nonzero only
+ * for few items) the two steps run one after the other and the attention
+ * spreads each item over several workgroups. Errors are those of either
+ * call. */
 hga_status hga_route_attend(const hga_config* cfg, const void* q, int64_t q_start, int64_t n_q,
                             int64_t seq_len, const float* chunk_sum, const hga_tiered* group_sum,
                             const hga_tiered* k, const hga_tiered* v,

@@ -35,7 +35,7 @@ def hga_cfg(cfg):
 
 
 def gpu_run(cfg, x, split=0, group_idx=None, n_sel=None, q_start=None, seq_len=None, fused=False,
-            capacity=None):
+            capacity=None, spread=False):
     """Run summaries, routing and attention through the C ABI.
 
     ``group_idx``/``n_sel`` (numpy, [nb][hkv][kg] / [nb][hkv][2]) replace the
@@ -43,7 +43,10 @@ def gpu_run(cfg, x, split=0, group_idx=None, n_sel=None, q_start=None, seq_len=N
     and attention run through hga_route_attend. With ``capacity`` (a multiple
     of 64 above the sequence, as a decoding cache is), K/V and the summary
     buffers hold that many tokens, every row past the sequence is NaN, and only
-    the summaries of the sequence's whole chunks are built. Returns numpy arrays.
+    the summaries of the sequence's whole chunks are built. With ``spread`` the
+    call gets the workspace hga_workspace_size(HGA_WS_ATTEND) asks for (asserted
+    nonzero), with which calls of few items spread each item's tiles over
+    several workgroups. Returns numpy arrays.
     """
     assert not (fused and group_idx is not None)
     c = hga_cfg(cfg)
@@ -83,6 +86,10 @@ def gpu_run(cfg, x, split=0, group_idx=None, n_sel=None, q_start=None, seq_len=N
     wsb = 0
     if split > 0:
         wsb = hga.hga_workspace_size(c, L, nq, hga.HGA_WS_ATTEND_TIERED)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    elif spread:
+        wsb = hga.hga_workspace_size(c, L, nq, hga.HGA_WS_ATTEND)
+        assert wsb > 0
         ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
     if fused:
         hga.hga_route_attend(c, q, q0, nq, L, cs, gs_t, k_t, v_t, ci, gi, ns, out, lse, ws, wsb)
