@@ -160,3 +160,10 @@ def test_small_blocks_spread():
     end = 4096 - 48
     cfg, x, f, cap = prefix_case(1, end, 16, 256)
     check_spread(cfg, x, f, cap, fused=False)
+
+
+def test_block64_spread_two_workgroups_per_item():
+    """G = 8 and blocks of 64: 512 rows, two workgroups per item; one block of
+    the 64K workload (4 items, 8 workgroups, each item's 36 tiles in 18 ranges)."""
+    cfg, x, f, cap = prefix_case(3, 65536, 64, 64)
+    check_spread(cfg, x, f, cap, fused=False)
