@@ -763,7 +763,7 @@ hipError_t prepare_tier_cache(const Shape& s, const KVSrc& kv, const int32_t* gr
 // about 256 workgroups in all. 1 = no split. The tile count is bounded by
 // the fixed chunks, the kept groups' tiles and the block's own chunk.
 constexpr int64_t kSplitMaxWgs = 128;
-constexpr int kSplitTiles = 2;
+constexpr int kSplitTiles = 4;
 int attend_split_count(const Shape& s) {
   if (s.dtype != HGA_BF16 || (s.d != 128 && s.d != 64)) return 1;
   const int64_t wgs = s.nb * s.hkv * bf16_wg_per_item(s);

@@ -45,11 +45,11 @@ def test_workspace_sizes():
     assert hga.hga_workspace_size(c, 16384, 2048, hga.HGA_WS_ROUTE) == 0
     assert hga.hga_workspace_size(c, 16384, 2048, hga.HGA_WS_ATTEND) == 0
     # few items (one decoded token: 8 items, 8 workgroups): each item's tiles
-    # in ranges of two, at most 12 tiles (1 sink + 2 local chunks, 64 groups
-    # of 8 in 8 tiles, the own chunk), so 6 ranges; per range 8 waves of
+    # in ranges of four, at most 12 tiles (1 sink + 2 local chunks, 64 groups
+    # of 8 in 8 tiles, the own chunk), so 3 ranges; per range 8 waves of
     # (d / 2 + 2) floats per lane
     dec = cfg(q_block=1)
-    assert hga.hga_workspace_size(dec, 16384, 1, hga.HGA_WS_ATTEND) == 8 * 6 * 8 * (64 + 2) * 64 * 4
+    assert hga.hga_workspace_size(dec, 16384, 1, hga.HGA_WS_ATTEND) == 8 * 3 * 8 * (64 + 2) * 64 * 4
     # 64 sequences decoded together: 512 items fill the chip, no split
     assert hga.hga_workspace_size(cfg(q_block=1, n_q_heads=32 * 64, n_kv_heads=8 * 64), 16384, 1,
                                   hga.HGA_WS_ATTEND) == 0

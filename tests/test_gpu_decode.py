@@ -148,7 +148,7 @@ def test_decode_token_spread_qwen3_8b_4k(pos, fused):
 
 
 def test_decode_token_spread_16k_and_64k():
-    """16K: 12 tiles in 6 ranges; 64K (G = 8, 256 kept groups): 36 tiles in 18
+    """16K: 12 tiles in 3 ranges; 64K (G = 8, 256 kept groups): 36 tiles in 9
     ranges of 4 items."""
     for cfg_id, pos in ((2, 16383), (3, 65000)):
         cfg, x, f, cap = prefix_case(cfg_id, pos + 1, 1, 1)
@@ -156,7 +156,7 @@ def test_decode_token_spread_16k_and_64k():
 
 
 def test_small_blocks_spread():
-    """16 blocks of 16 tokens (128 workgroups, two ranges each)."""
+    """16 blocks of 16 tokens (128 workgroups, two ranges each: 5 tiles at most)."""
     end = 4096 - 48
     cfg, x, f, cap = prefix_case(1, end, 16, 256)
     check_spread(cfg, x, f, cap, fused=False)
@@ -164,6 +164,6 @@ def test_small_blocks_spread():
 
 def test_block64_spread_two_workgroups_per_item():
     """G = 8 and blocks of 64: 512 rows, two workgroups per item; one block of
-    the 64K workload (4 items, 8 workgroups, each item's 36 tiles in 18 ranges)."""
+    the 64K workload (4 items, 8 workgroups, each item's 36 tiles in 9 ranges)."""
     cfg, x, f, cap = prefix_case(3, 65536, 64, 64)
     check_spread(cfg, x, f, cap, fused=False)
