@@ -278,7 +278,7 @@ hga_status hga_route_attend(const hga_config* cfg, const void* q, int64_t q_star
   // the fused kernel, unless the workspace lets the attention spread few
   // items over more workgroups
   const bool split = k->split == 0 && hga::attend_split_count(s) > 1 && workspace &&
-                     ws_bytes >= hga::attend_split_bytes(s);
+                     ((uintptr_t)workspace & 15) == 0 && ws_bytes >= hga::attend_split_bytes(s);
   if (!split && hga::fused_route_attend_supported(s, k->split))
     return device_status(hga::launch_route_attend(s, q, chunk_sum, gs_host, gs_dev, group_sum->split, kv,
                                                   chunk_idx, group_idx, n_sel, out, lse, hs),

@@ -791,7 +791,7 @@ hipError_t launch_attend(const Shape& s, const void* q, const KVSrc& kv, const i
   a.q = q; a.kv = kv; a.gidx = group_idx; a.nsel = n_sel; a.out = out; a.lse = lse; a.s = s;
   const bool tiered = kv.split > 0;
   const int nsplit = tiered ? 1 : attend_split_count(s);
-  if (nsplit > 1 && workspace && ws_bytes >= attend_split_bytes(s)) {
+  if (nsplit > 1 && workspace && ((uintptr_t)workspace & 15) == 0 && ws_bytes >= attend_split_bytes(s)) {
     a.wg_per_item = bf16_wg_per_item(s);
     float* part = static_cast<float*>(workspace);
     const unsigned nwg = (unsigned)(items * a.wg_per_item);

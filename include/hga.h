@@ -198,8 +198,9 @@ hga_status hga_route(const hga_config* cfg, const void* q, int64_t q_start, int6
  *   out        device, [Hq][n_q][d] of cfg->dtype.
  *   lse        device, [Hq][n_q] float32, or NULL.
  *   workspace  device, at least hga_workspace_size(...) bytes (with split 0,
- *              NULL or fewer bytes than HGA_WS_ATTEND asks for is accepted:
- *              each item is then attended by one workgroup). */
+ *              NULL, fewer bytes than HGA_WS_ATTEND asks for, or an address
+ *              that is not 16-byte aligned is accepted: each item is then
+ *              attended by one workgroup). */
 hga_status hga_attend(const hga_config* cfg, const void* q, int64_t q_start, int64_t n_q,
                       int64_t seq_len, const hga_tiered* k, const hga_tiered* v,
                       const int32_t* group_idx, const int32_t* n_sel,
