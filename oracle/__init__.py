@@ -60,6 +60,8 @@ def _load():
         lib.orc_token_set.restype = C.c_int64
         assert lib.orc_diag_width() == 8
         lib.orc_threads.restype = C.c_int
+        lib.orc_set_threads.argtypes = [C.c_int]
+        lib.orc_route_scores.argtypes = [C.POINTER(_Cfg), P, P, P, P, P, C.c_int, P, P, P, P]
         _lib = lib
     return _lib
 
@@ -129,6 +131,27 @@ def route(cfg, q64, k64, items=None, sums=None):
     return ci, gi, ns, dg
 
 
+def route_scores(cfg, q64, k64, items, sums=None):
+    """Decision scores of every candidate of both stages, for each (block,
+    KV head) item: chunk_sc [n][L/chunk] (NaN where a chunk is not a
+    candidate of the item), group_sc [n][L/group] (every group of every
+    candidate chunk; NaN elsewhere) and eps [n][2], the error bounds of the
+    two stages over all of these scores. Used where a boundary is not
+    certified and several selections are correct."""
+    lib = _load()
+    it = np.ascontiguousarray(np.asarray(items, dtype=np.int32).reshape(-1, 2))
+    n = it.shape[0]
+    if sums is None:
+        sums = (summaries(cfg, k64), abs_summaries(cfg, k64))
+    (gs, cs), (ga, ca) = sums
+    csc = np.empty((n, cfg["L"] // cfg["chunk"]))
+    gsc = np.empty((n, cfg["L"] // cfg["group"]))
+    eps = np.empty((n, 2))
+    lib.orc_route_scores(C.byref(make_cfg(cfg)), _ptr(_f64(q64)), _ptr(ga), _ptr(ca), _ptr(gs), _ptr(cs),
+                         n, _ptr(it), _ptr(csc), _ptr(gsc), _ptr(eps))
+    return csc, gsc, eps
+
+
 def attend(cfg, q64, k64, v64, items, group_idx, n_groups):
     """Steps 6-7: exact causal attention over each item's token set.
 
@@ -184,6 +207,31 @@ def token_set(cfg, b, group_idx, n_groups):
 def threads() -> int:
     """OpenMP threads the oracle runs on."""
     return int(_load().orc_threads())
+
+
+def set_threads(n: int) -> None:
+    """Run the oracle's loops on n OpenMP threads from now on."""
+    _load().orc_set_threads(int(n))
+
+
+def valid_selection(scores, kept, k, eps) -> bool:
+    """Several selections are correct at a boundary that is not certified:
+    with v the k-th largest of the candidates' scores (NaN entries are not
+    candidates), a kept set is correct when it holds min(k, candidates)
+    distinct candidates, every candidate scoring above v + 2 eps, and none
+    scoring below v - 2 eps (any evaluation order within the bound eps could
+    have produced it)."""
+    cand = np.flatnonzero(~np.isnan(scores))
+    kept = np.asarray(kept, dtype=np.int64)
+    kk = min(k, cand.size)
+    if kept.size != kk or np.unique(kept).size != kk or not np.isin(kept, cand).all():
+        return False
+    if kk == 0 or kk == cand.size:
+        return True
+    v = np.sort(scores[cand])[::-1][kk - 1]
+    must = cand[scores[cand] > v + 2.0 * eps]
+    never = cand[scores[cand] < v - 2.0 * eps]
+    return bool(np.isin(must, kept).all() and not np.isin(never, kept).any())
 
 
 def certified(diag_row, stage: str) -> bool:

@@ -181,6 +181,22 @@ static int select_topk(cand_t* cand, int n, int k, int32_t* sel, double* gap, in
   return kk;
 }
 
+/* Step 2: the block query of (block b, KV head h): the float64 mean of the
+ * block's B queries over the G query heads of the KV head, and the mean |Q|
+ * per dimension for the error bound. Both arrays hold d values. */
+static void block_query(const orc_cfg* c, const double* q, int b, int h, double* qb, double* qabs) {
+  const int64_t d = c->d, q0 = q_start(c);
+  const int G = c->hq / c->hkv, B = c->q_block, N = G * B;
+  const int64_t s = q0 + (int64_t)b * B;
+  for (int64_t e = 0; e < d; ++e) { qb[e] = 0.0; qabs[e] = 0.0; }
+  for (int r = 0; r < G; ++r)
+    for (int i = 0; i < B; ++i) {
+      const double* row = q + ((int64_t)(h * G + r) * c->n_q + (s - q0) + i) * d;
+      for (int64_t e = 0; e < d; ++e) { qb[e] += row[e]; qabs[e] += fabs(row[e]); }
+    }
+  for (int64_t e = 0; e < d; ++e) { qb[e] /= N; qabs[e] /= N; }
+}
+
 /* Route one (block b, KV head h) item. */
 static void route_item(const orc_cfg* c, const double* q, const double* ga, const double* ca,
                        const double* gs, const double* cs, int b, int h, int32_t* chunk_idx, int32_t* group_idx,
@@ -190,15 +206,9 @@ static void route_item(const orc_cfg* c, const double* q, const double* ga, cons
   const int64_t s = q0 + (int64_t)b * B, ms = s / c->chunk;
   const int64_t ng = L / c->group, nc = L / c->chunk, gpc = c->chunk / c->group;
 
-  /* step 2: block query (float64 mean) and mean |Q| per dim for the bound */
   double* qb = (double*)calloc((size_t)d, sizeof(double));
   double* qabs = (double*)calloc((size_t)d, sizeof(double));
-  for (int r = 0; r < G; ++r)
-    for (int i = 0; i < B; ++i) {
-      const double* row = q + ((int64_t)(h * G + r) * c->n_q + (s - q0) + i) * d;
-      for (int64_t e = 0; e < d; ++e) { qb[e] += row[e]; qabs[e] += fabs(row[e]); }
-    }
-  for (int64_t e = 0; e < d; ++e) { qb[e] /= N; qabs[e] /= N; }
+  block_query(c, q, b, h, qb, qabs);
 
   /* steps 3, 4: chunk candidates and chunk stage */
   cand_t* cand = (cand_t*)malloc(sizeof(cand_t) * (size_t)(ms > 0 ? ms : 1));
@@ -238,6 +248,50 @@ static void route_item(const orc_cfg* c, const double* q, const double* ga, cons
   for (int i = 0; i < c->top_groups; ++i) group_idx[i] = i < nsg ? selg[i] : -1;
   n_sel[0] = nsc; n_sel[1] = nsg;
   free(gc); free(selc); free(selg); free(qb); free(qabs);
+}
+
+/* Decision scores of every candidate of both stages of (block b, KV head h),
+ * for checking a selection at a boundary that is not certified (where
+ * several selections are correct): chunk_sc[m] for every closed chunk m
+ * before the block that is not fixed (NaN for every other chunk), group_sc[j]
+ * for every group j of those chunks (NaN otherwise), and the error bounds of
+ * the two stages over all of these scores (eps[0]: chunks, eps[1]: groups).
+ * chunk_sc holds seq_len / chunk values, group_sc seq_len / group. */
+static void score_item(const orc_cfg* c, const double* q, const double* ga, const double* ca, const double* gs,
+                       const double* cs, int b, int h, double* chunk_sc, double* group_sc, double* eps) {
+  const int64_t L = c->seq_len, d = c->d, q0 = q_start(c);
+  const int G = c->hq / c->hkv, B = c->q_block, N = G * B;
+  const int64_t s = q0 + (int64_t)b * B, ms = s / c->chunk;
+  const int64_t ng = L / c->group, nc = L / c->chunk, gpc = c->chunk / c->group;
+  double* qb = (double*)calloc((size_t)d, sizeof(double));
+  double* qabs = (double*)calloc((size_t)d, sizeof(double));
+  block_query(c, q, b, h, qb, qabs);
+  for (int64_t m = 0; m < nc; ++m) chunk_sc[m] = NAN;
+  for (int64_t j = 0; j < ng; ++j) group_sc[j] = NAN;
+  eps[0] = eps[1] = 0.0;
+  for (int64_t m = 0; m < ms; ++m) {
+    if (is_fixed(c, m, ms)) continue;
+    double exact;
+    score(c, qb, qabs, cs + ((int64_t)h * nc + m) * d, ca + ((int64_t)h * nc + m) * d, N, c->chunk,
+          &chunk_sc[m], &exact, &eps[0]);
+    for (int64_t u = 0; u < gpc; ++u) {
+      const int64_t j = m * gpc + u;
+      score(c, qb, qabs, gs + ((int64_t)h * ng + j) * d, ga + ((int64_t)h * ng + j) * d, N, c->group,
+            &group_sc[j], &exact, &eps[1]);
+    }
+  }
+  free(qb); free(qabs);
+}
+
+int orc_route_scores(const orc_cfg* c, const double* q, const double* ga, const double* ca,
+                     const double* gs, const double* cs, int n_items, const int32_t* items,
+                     double* chunk_sc, double* group_sc, double* eps) {
+  const int64_t nc = c->seq_len / c->chunk, ng = c->seq_len / c->group;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int it = 0; it < n_items; ++it)
+    score_item(c, q, ga, ca, gs, cs, items[2 * it], items[2 * it + 1], chunk_sc + (int64_t)it * nc,
+               group_sc + (int64_t)it * ng, eps + 2 * (int64_t)it);
+  return 0;
 }
 
 int orc_route(const orc_cfg* c, const double* q, const double* ga, const double* ca,
@@ -454,6 +508,9 @@ int orc_diag_width(void) { return DG_NUM; }
 #ifdef _OPENMP
 #include <omp.h>
 int orc_threads(void) { return omp_get_max_threads(); }
+/* Threads of the following OpenMP loops (n >= 1). */
+void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 #else
 int orc_threads(void) { return 1; }
+void orc_set_threads(int n) { (void)n; }
 #endif

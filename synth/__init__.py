@@ -115,6 +115,29 @@ def _rope(x, pos, theta):
     return x
 
 
+def _integer_inputs(cfg: dict) -> dict:
+    """Inputs with exact ties: Q and K entries are integers drawn uniformly from
+    ``integer_values`` = (lo, hi) (inclusive), and the keys repeat with a period
+    of ``chunk_period`` chunks (chunk m holds the keys of chunk m mod period),
+    so summaries, and every score built from them, repeat exactly. Small
+    integers are exact in bfloat16, and their means over power-of-two counts
+    and the dot products of such means are exact in float64, so equal scores
+    are equal on every evaluation order. V ~ N(0, 1). No RoPE, no planting."""
+    L, nq, hq, hkv, d, c = cfg["L"], cfg["n_q"], cfg["hq"], cfg["hkv"], cfg["d"], cfg["chunk"]
+    lo, hi = cfg["integer_values"]
+    per = int(cfg.get("chunk_period", 0)) or L // c
+    q = _rng(cfg, _T_Q).integers(lo, hi + 1, size=(hq, nq, d)).astype(np.float64)
+    base = _rng(cfg, _T_K).integers(lo, hi + 1, size=(hkv, per * c, d)).astype(np.float64)
+    reps = -(-L // (per * c))
+    k = np.tile(base, (1, reps, 1))[:, :L]
+    v = _rng(cfg, _T_V).standard_normal((hkv, L, d))
+    out = {"planted": [[] for _ in range(hkv)]}
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        x32 = x.astype(np.float32)
+        out[name] = f32_to_bf16_bits(x32) if cfg["dtype"] == "bf16" else x32
+    return out
+
+
 def make_inputs(cfg: dict) -> dict:
     """Generate Q, K, V for workload ``cfg``.
 
@@ -125,6 +148,8 @@ def make_inputs(cfg: dict) -> dict:
     L, nq, hq, hkv, d = cfg["L"], cfg["n_q"], cfg["hq"], cfg["hkv"], cfg["d"]
     G = hq // hkv
     q0 = L - nq
+    if cfg.get("integer_values"):
+        return _integer_inputs(cfg)
     q = _rng(cfg, _T_Q).standard_normal((hq, nq, d))
     k = _rng(cfg, _T_K).standard_normal((hkv, L, d))
     v = _rng(cfg, _T_V).standard_normal((hkv, L, d))

@@ -122,27 +122,58 @@ def oracle_route(cfg, f):
     return oracle.route(cfg, f["q"], f["k"], sums=sums)
 
 
-def check_routing(cfg, gpu, ref):
-    """Certified boundaries must match exactly. Returns (items, uncertified, mismatches)."""
+def check_routing(cfg, gpu, ref, f):
+    """The GPU's routing of every item against the oracle's ``ref`` (from
+    oracle_route on the float64 inputs ``f``).
+
+    A certified boundary (gap above twice the bound eps) has one correct
+    answer: the GPU's kept set must equal the oracle's. Where a boundary is
+    not certified several selections are correct, and the GPU's must be one of
+    them: oracle.valid_selection over the oracle's scores of every candidate
+    (for the group stage, the groups of the chunks the GPU kept). Exact ties
+    are uncertified boundaries too (gap 0); the callers assert that the GPU's
+    sets equal the oracle's there as well, which is the lower-index rule.
+    Returns (items, uncertified boundaries, items whose kept sets differ from
+    the oracle's)."""
     ci_r, gi_r, ns_r, dg = ref
     kc, kg = cfg["top_chunks"], cfg["top_groups"]
     n_items = ci_r.shape[0]
     ci_g = gpu["chunk_idx"].reshape(n_items, kc)
     gi_g = gpu["group_idx"].reshape(n_items, kg)
     ns_g = gpu["n_sel"].reshape(n_items, 2)
-    uncert = mism = 0
-    for n in range(ci_r.shape[0]):
-        cc, cg = oracle.certified(dg[n], "chunk"), oracle.certified(dg[n], "group")
-        same_c = np.array_equal(ci_g[n], ci_r[n]) and ns_g[n, 0] == ns_r[n, 0]
-        same_g = np.array_equal(gi_g[n], gi_r[n]) and ns_g[n, 1] == ns_r[n, 1]
-        if not (cc and cg):
-            uncert += 1
+    cert = [(oracle.certified(dg[n], "chunk"), oracle.certified(dg[n], "group")) for n in range(n_items)]
+    loose = [n for n in range(n_items) if not (cert[n][0] and cert[n][1])]
+    uncert = sum((not cc) + (not cg) for cc, cg in cert)
+    tables = {}
+    if loose:
+        items = oracle.all_items(cfg)
+        csc, gsc, eps = oracle.route_scores(cfg, f["q"], f["k"], [items[n] for n in loose])
+        tables = {n: (csc[i], gsc[i], eps[i]) for i, n in enumerate(loose)}
+    gpc = cfg["chunk"] // cfg["group"]
+    mism = 0
+    for n in range(n_items):
+        cc, cg = cert[n]
+        nsc, nsg = int(ns_g[n, 0]), int(ns_g[n, 1])
+        same_c = np.array_equal(ci_g[n], ci_r[n]) and nsc == ns_r[n, 0]
+        same_g = np.array_equal(gi_g[n], gi_r[n]) and nsg == ns_r[n, 1]
+        mism += int(not (same_c and same_g))
         if cc:
             assert same_c, f"item {n}: certified chunk set differs: {ci_g[n]} vs {ci_r[n]}"
-            if cg:
-                assert same_g, f"item {n}: certified group set differs: {gi_g[n]} vs {gi_r[n]}"
-        mism += int(not (same_c and same_g))
-    return ci_r.shape[0], uncert, mism
+        if cc and cg:
+            assert same_g, f"item {n}: certified group set differs: {gi_g[n]} vs {gi_r[n]}"
+        if n in tables:
+            csc, gsc, eps = tables[n]
+            kept_c = ci_g[n][:nsc]
+            assert np.all(ci_g[n][nsc:] == -1) and np.all(gi_g[n][nsg:] == -1), f"item {n}: padding"
+            assert np.all(np.diff(kept_c) > 0) and np.all(np.diff(gi_g[n][:nsg]) > 0), f"item {n}: not ascending"
+            assert oracle.valid_selection(csc, kept_c, kc, eps[0]), \
+                f"item {n}: chunk set {kept_c} is not a correct selection at its uncertified boundary"
+            mask = np.full(gsc.shape, np.nan)
+            for m in kept_c:
+                mask[m * gpc:(m + 1) * gpc] = gsc[m * gpc:(m + 1) * gpc]
+            assert oracle.valid_selection(mask, gi_g[n][:nsg], kg, eps[1]), \
+                f"item {n}: group set {gi_g[n][:nsg]} is not a correct selection at its uncertified boundary"
+    return n_items, uncert, mism
 
 
 def item_rows(cfg, out, items):

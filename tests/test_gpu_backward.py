@@ -6,7 +6,8 @@ gradients, the history is detached).
 Each case runs the GPU forward (hga_route_attend) for its kept groups, output
 and LSE, draws a seeded output gradient, runs hga_attend_backward, and compares
 dQ (every query row) and dK, dV (the call's own positions) with the float64
-oracle on the same bf16 inputs and the same kept groups.
+oracle on the same bf16 inputs and the oracle's own routing, which the GPU's
+kept groups must equal on every item.
 
 Tolerance (bf16 gradients; float32 below), derived from the arithmetic: the kernels round P
 and dS to bfloat16 as MFMA operands (relative 2^-9 each), take D = dO . O from
@@ -29,7 +30,7 @@ import torch
 import hierarchical_sparse_attention_hga_amd as hga
 import oracle
 import synth
-from harness import DEV, bf16_half_spacing, hga_cfg, inputs, to_dev
+from harness import DEV, bf16_half_spacing, check_routing, hga_cfg, inputs, oracle_route, to_dev
 from hierarchical_sparse_attention_hga_amd.memory import split_to_host
 from test_gpu_edges import small
 
@@ -77,7 +78,7 @@ def gpu_forward_backward(cfg, x, dout_bits, q_start=None, seq_len=None, split=0)
         p.free()
     f = lambda t: t.float().cpu().numpy().astype(np.float64)
     iv = torch.int16 if dt == "bf16" else torch.int32
-    return dict(gi=gi.cpu().numpy(), ns=ns.cpu().numpy(), dq=f(dq), dk=f(dk), dv=f(dv),
+    return dict(ci=ci.cpu().numpy(), gi=gi.cpu().numpy(), ns=ns.cpu().numpy(), dq=f(dq), dk=f(dk), dv=f(dv),
                 raw=(dq.view(iv).cpu().numpy(), dk.view(iv).cpu().numpy(), dv.view(iv).cpu().numpy()))
 
 
@@ -95,11 +96,19 @@ def check_grads(cfg, x, gpu, dout_bits, q_start=None):
     dt = cfg["dtype"]
     f = {n: synth.to_f64(x[n], dt) for n in ("q", "k", "v")}
     k64, v64 = f["k"][:, :q0 + nq], f["v"][:, :q0 + nq]
-    kg = max(cfg["top_groups"], 1)
     max_rel, mean_rel, mean_rms = BARS[dt]
+    # the oracle's own routing; the GPU's (which fixed the GPU's token sets)
+    # must equal it on every item
+    ref = oracle_route(sub, {"q": f["q"], "k": k64})
+    kc = cfg["top_chunks"]
+    routed = {"chunk_idx": gpu["ci"][..., :kc], "group_idx": gpu["gi"][..., :cfg["top_groups"]], "n_sel": gpu["ns"]}
+    n_items, uncert, mism = check_routing(sub, routed, ref, {"q": f["q"], "k": k64})
+    print(f"  items={n_items} uncertified boundaries={uncert} differing sets={mism}", flush=True)
+    assert mism == 0, f"{mism} items route differently from the oracle"
+    nb, hkv = nq // cfg["q_block"], cfg["hkv"]
     dq, dk, dv, qa, ka, va = oracle.attend_backward(
-        sub, f["q"], k64, v64, synth.to_f64(dout_bits, dt),
-        gpu["gi"][..., :kg] if cfg["top_groups"] else gpu["gi"][..., :0], gpu["ns"][..., 1], with_abs=True)
+        sub, f["q"], k64, v64, synth.to_f64(dout_bits, dt), ref[1].reshape(nb, hkv, -1),
+        ref[2][:, 1].reshape(nb, hkv), with_abs=True)
     sl = slice(q0, q0 + nq)
     res = {}
     for name, got, ref, comp in (("dq", gpu["dq"], dq, qa), ("dk", gpu["dk"], dk[:, sl], ka[:, sl]),

@@ -49,7 +49,8 @@ def test_routing_and_attention_end_to_end(cfg_id):
     print(f"[end-to-end] {cfg['name']}", flush=True)
     gpu = gpu_run(cfg, x)
     ref = oracle_route(cfg, f)
-    n, uncert, mism = check_routing(cfg, gpu, ref)
+    n, uncert, mism = check_routing(cfg, gpu, ref, f)
+    print(f"  items={n} uncertified boundaries={uncert} differing sets={mism}", flush=True)
     assert uncert == 0, f"{uncert} uncertified boundaries in a planted workload"
     assert mism == 0
     items = sampled_items(cfg, cfg_id)

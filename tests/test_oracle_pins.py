@@ -484,3 +484,158 @@ def test_backward_invariants():
         np.testing.assert_allclose(dv[h].sum(axis=0), dout[h * G:(h + 1) * G].sum(axis=(0, 1)), atol=1e-11)
     # keys after the last query and outside every token set get nothing
     assert np.abs(dq).max() > 0
+
+
+# ------------------------------------------------------------------ certification bound
+def test_abs_summaries_closed_form_sign_alternating():
+    """Keys K[0][t][e] = (-1)^t (t + 1 + e): the mean of |K| over group j is
+    g j + (g + 1) / 2 + e (likewise per chunk), while the plain mean of every
+    group and chunk (of even size, starting at an even token) is -1/2: each
+    pair of neighbours sums to -1."""
+    cfg = tiny_cfg(L=128, n_q=64)
+    L, d, g, c = cfg["L"], cfg["d"], cfg["group"], cfg["chunk"]
+    t = np.arange(L)[None, :, None]
+    e = np.arange(d)[None, None, :]
+    k = np.where(t % 2 == 0, 1.0, -1.0) * (t + 1 + e)
+    ga, ca = oracle.abs_summaries(cfg, k)
+    gs, cs = oracle.summaries(cfg, k)
+    j = np.arange(L // g)[None, :, None]
+    m = np.arange(L // c)[None, :, None]
+    np.testing.assert_array_equal(ga, g * j + (g + 1) / 2 + e + 0.0 * j)
+    np.testing.assert_array_equal(ca, c * m + (c + 1) / 2 + e + 0.0 * m)
+    assert np.all(gs == -0.5) and np.all(cs == -0.5)
+
+
+def _alt_score(rng, qrows, krows, adversarial):
+    """One decision score evaluated in another order: the block mean and the
+    summary summed sequentially in a random order, the summary rounded to
+    float32 (and, with adversarial = +1 / -1, moved one float32 step in the
+    direction that raises / lowers the score), the dot summed in a random
+    order."""
+    qb = np.cumsum(qrows[rng.permutation(len(qrows))], axis=0)[-1] / len(qrows)
+    s = (np.cumsum(krows[rng.permutation(len(krows))], axis=0)[-1] / len(krows)).astype(np.float32)
+    if adversarial:
+        s = np.nextafter(s, np.where(adversarial * qb > 0, np.float32(np.inf), np.float32(-np.inf))).astype(np.float32)
+    prod = qb * s.astype(np.float64)
+    return np.cumsum(prod[rng.permutation(len(prod))])[-1]
+
+
+@pytest.mark.parametrize("dtype,seed", [("f32", 0), ("f32", 1), ("bf16", 2), ("bf16", 3)])
+def test_eps_bounds_every_evaluation_order(dtype, seed):
+    """The bound eps must cover every evaluation order of the block mean, the
+    summary mean and the dot, and a float32 summary landing one step away:
+    for every candidate of both stages, scores recomputed in random orders and
+    with adversarially rounded summaries stay within eps of the oracle's. It
+    must also not be vacuous: the adversarial one-step moves reach at least
+    1/64 of it."""
+    cfg = tiny_cfg(L=512, n_q=64, hq=4, hkv=2, d=16, chunk=64, group=8, q_block=64, top_chunks=2, top_groups=5,
+                   sink=64, local=64)
+    rng = np.random.default_rng(100 + seed)
+    q, k, _ = rand_qkv(cfg, seed)
+    if dtype == "bf16":
+        q = synth.bf16_bits_to_f64(synth.f32_to_bf16_bits(q.astype(np.float32)))
+        k = synth.bf16_bits_to_f64(synth.f32_to_bf16_bits(k.astype(np.float32)))
+    else:
+        q, k = q.astype(np.float32).astype(np.float64), k.astype(np.float32).astype(np.float64)
+    items = oracle.all_items(cfg)
+    csc, gsc, eps = oracle.route_scores(cfg, q, k, items)
+    _, _, _, dg = oracle.route(cfg, q, k, items)
+    G, B, c, g = cfg["hq"] // cfg["hkv"], cfg["q_block"], cfg["chunk"], cfg["group"]
+    q0 = cfg["L"] - cfg["n_q"]
+    for n, (b, h) in enumerate(items):
+        assert eps[n, 0] >= dg[n, oracle.DG_EPS_C] and eps[n, 1] >= dg[n, oracle.DG_EPS_G]
+        s = q0 + b * B
+        qrows = q[h * G:(h + 1) * G, s - q0:s - q0 + B].reshape(-1, cfg["d"])
+        for sc, size, e in ((csc[n], c, eps[n, 0]), (gsc[n], g, eps[n, 1])):
+            idx = np.flatnonzero(~np.isnan(sc))
+            assert idx.size > 0
+            worst_adv = 0.0
+            for i in idx:
+                krows = k[h, i * size:(i + 1) * size]
+                for adversarial in (0, 0, 1, -1):
+                    dev = abs(_alt_score(rng, qrows, krows, adversarial) - sc[i])
+                    assert dev <= e, f"item {n} candidate {i}: order moved the score by {dev} > eps {e}"
+                    if adversarial:
+                        worst_adv = max(worst_adv, dev)
+            assert worst_adv >= e / 64, f"item {n}: eps {e} is far above any reachable move {worst_adv}"
+
+
+def test_route_scores_agree_with_the_selection():
+    """The score tables give the oracle's own selection back: the kept chunks
+    are the top-kc candidates by (score desc, index asc), the kept groups the
+    top-kg groups of the kept chunks, and the reported gaps are the gaps of
+    the tables."""
+    cfg = tiny_cfg(L=512, n_q=128, hq=4, hkv=2, d=16, chunk=32, group=8, q_block=32, top_chunks=3,
+                   top_groups=5, sink=32, local=32)
+    q, k, _ = rand_qkv(cfg, 11)
+    items = oracle.all_items(cfg)
+    ci, gi, ns, dg = oracle.route(cfg, q, k, items)
+    csc, gsc, _ = oracle.route_scores(cfg, q, k, items)
+    gpc = cfg["chunk"] // cfg["group"]
+    for n in range(len(items)):
+        cand = np.flatnonzero(~np.isnan(csc[n]))
+        order = sorted(cand, key=lambda m: (-csc[n][m], m))
+        kc = min(cfg["top_chunks"], cand.size)
+        assert ci[n][:kc].tolist() == sorted(order[:kc]) and ns[n, 0] == kc
+        if 0 < kc < cand.size:
+            assert dg[n, oracle.DG_GAP_C] == csc[n][order[kc - 1]] - csc[n][order[kc]]
+        groups = [m * gpc + u for m in ci[n][:kc] for u in range(gpc)]
+        gorder = sorted(groups, key=lambda j: (-gsc[n][j], j))
+        kg = min(cfg["top_groups"], len(groups))
+        assert gi[n][:kg].tolist() == sorted(gorder[:kg]) and ns[n, 1] == kg
+
+
+def test_valid_selection_rule():
+    """Several selections are correct only inside the band of 2 eps around the
+    k-th score; outside it, and for the count, the choice is forced."""
+    nan = np.nan
+    sc = np.array([5.0, nan, 3.0, 3.0 + 1e-9, 2.0, 1.0])
+    assert oracle.valid_selection(sc, [0, 2], 2, eps=1e-6)          # within the band: either tie member
+    assert oracle.valid_selection(sc, [0, 3], 2, eps=1e-6)
+    assert not oracle.valid_selection(sc, [0, 2], 2, eps=1e-12)     # outside the band the order decides
+    assert not oracle.valid_selection(sc, [0, 4], 2, eps=1e-6)      # 2.0 is below the band
+    assert not oracle.valid_selection(sc, [2, 3], 2, eps=1e-6)      # 5.0 is above it and must be kept
+    assert not oracle.valid_selection(sc, [0], 2, eps=1e-6)         # count
+    assert not oracle.valid_selection(sc, [0, 1], 2, eps=1e-6)      # not a candidate
+    assert not oracle.valid_selection(sc, [0, 0], 2, eps=1e-6)      # not distinct
+    assert oracle.valid_selection(sc, [0, 2, 3, 4, 5], 9, eps=0.0)  # the budget covers all
+
+
+def test_exact_ties_on_periodic_integer_keys():
+    """Integer queries and keys that repeat every 3 chunks make many scores
+    exactly equal (exact in float64): the kept sets must be the first in
+    (score desc, index asc) order, which a brute force over exact rational
+    scores (fractions, no floating point) gives independently."""
+    from fractions import Fraction
+    cfg = tiny_cfg(L=1024, n_q=128, hq=2, hkv=1, d=8, chunk=64, group=8, q_block=64, top_chunks=4,
+                   top_groups=9, sink=64, local=64, dtype="f32", integer_values=(-2, 2), chunk_period=3)
+    x = synth.make_inputs(cfg)
+    q, k = synth.to_f64(x["q"], "f32"), synth.to_f64(x["k"], "f32")
+    items = oracle.all_items(cfg)
+    ci, gi, ns, dg = oracle.route(cfg, q, k, items)
+    G, B, c, g, d = 2, 64, 64, 8, cfg["d"]
+    ki = k.astype(np.int64)
+    ties = 0
+    for n, (b, h) in enumerate(items):
+        s = cfg["L"] - cfg["n_q"] + b * B
+        rows = q[h * G:(h + 1) * G, b * B:(b + 1) * B].reshape(-1, d).astype(np.int64)
+        qbar = [Fraction(int(rows[:, e].sum()), len(rows)) for e in range(d)]
+
+        def exact(lo, size):
+            return sum(qbar[e] * Fraction(int(ki[h, lo:lo + size, e].sum()), size) for e in range(d))
+        ms = s // c
+        cand = [m for m in range(ms) if m >= cfg["sink"] // c and m < ms - cfg["local"] // c]
+        sc = {m: exact(m * c, c) for m in cand}
+        order = sorted(cand, key=lambda m: (-sc[m], m))
+        kc = min(cfg["top_chunks"], len(cand))
+        if kc < len(cand) and sc[order[kc - 1]] == sc[order[kc]]:
+            ties += 1
+        assert ci[n][:kc].tolist() == sorted(order[:kc])
+        groups = [m * (c // g) + u for m in sorted(order[:kc]) for u in range(c // g)]
+        gsc = {j: exact(j * g, g) for j in groups}
+        gorder = sorted(groups, key=lambda j: (-gsc[j], j))
+        kg = min(cfg["top_groups"], len(groups))
+        if kg < len(groups) and gsc[gorder[kg - 1]] == gsc[gorder[kg]]:
+            ties += 1
+        assert gi[n][:kg].tolist() == sorted(gorder[:kg])
+    assert ties > 0, "the periodic keys should put exact ties on some boundary"
