@@ -5,6 +5,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <initializer_list>
+
 #include "hga_internal.h"
 
 namespace {
@@ -100,8 +102,20 @@ hga_status make_shape(const hga_config* cfg, int64_t seq_len, int64_t q_start, i
   return HGA_OK;
 }
 
+// The kernels move rows 16 bytes at a time: every tensor and workspace
+// address must be a multiple of 16.
+bool misaligned(const void* p) { return ((uintptr_t)p & 15) != 0; }
+
+hga_status check_aligned(const char* names, std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (misaligned(p)) return fail(HGA_ERR_INVALID_ARGUMENT, "%s must be 16-byte aligned", names);
+  return HGA_OK;
+}
+
 hga_status check_tier(const hga_tiered* t, const char* name, int64_t seq_len, int64_t q_start) {
   if (!t) return fail(HGA_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (misaligned(t->host) || misaligned(t->dev))
+    return fail(HGA_ERR_INVALID_ARGUMENT, "%s.host and %s.dev must be 16-byte aligned", name, name);
   if (t->split < 0 || t->split > q_start)
     return fail(HGA_ERR_INVALID_ARGUMENT, "%s.split must be in [0, q_start]", name);
   if (t->split % hga::kChunk) return fail(HGA_ERR_UNSUPPORTED, "%s.split must be a multiple of 64", name);
@@ -151,6 +165,7 @@ hga_status hga_build_summaries(const hga_config* cfg, const void* k, int64_t seq
   if (seq_len == 0) return ok();
   if (!k || !group_sum || !chunk_sum)
     return fail(HGA_ERR_INVALID_ARGUMENT, "k, group_sum and chunk_sum must be non-NULL");
+  if ((st = check_aligned("k, group_sum and chunk_sum", {k, group_sum, chunk_sum})) != HGA_OK) return st;
   return device_status(hga::launch_summaries(s, k, group_sum, chunk_sum, 0, seq_len / hga::kChunk,
                                              (hipStream_t)stream),
                        "hga_build_summaries launch");
@@ -166,6 +181,7 @@ hga_status hga_build_summaries_range(const hga_config* cfg, const void* k, int64
   if (chunk_begin == chunk_end) return ok();
   if (!k || !group_sum || !chunk_sum)
     return fail(HGA_ERR_INVALID_ARGUMENT, "k, group_sum and chunk_sum must be non-NULL");
+  if ((st = check_aligned("k, group_sum and chunk_sum", {k, group_sum, chunk_sum})) != HGA_OK) return st;
   return device_status(hga::launch_summaries(s, k, group_sum, chunk_sum, chunk_begin, chunk_end, (hipStream_t)stream),
                        "hga_build_summaries_range launch");
 }
@@ -183,6 +199,8 @@ hga_status hga_stream_forward(const hga_config* cfg, const void* q, const void* 
       (full.kg > 0 && !group_idx))
     return fail(HGA_ERR_INVALID_ARGUMENT,
                 "q, k, v, chunk_sum, group_sum, n_sel, out, chunk_idx and group_idx must be non-NULL");
+  if ((st = check_aligned("q, k, v, chunk_sum, group_sum and out", {q, k, v, chunk_sum, group_sum, out})) != HGA_OK)
+    return st;
   const hipStream_t hs = (hipStream_t)stream;
   const size_t esz = full.dtype == HGA_BF16 ? 2 : 4;
   const hga::KVSrc kv{nullptr, k, nullptr, v, 0};
@@ -230,6 +248,7 @@ hga_status hga_route(const hga_config* cfg, const void* q, int64_t q_start, int6
   if (n_q == 0) return ok();
   if (!q || !chunk_sum || !n_sel || (s.kc > 0 && !chunk_idx) || (s.kg > 0 && !group_idx))
     return fail(HGA_ERR_INVALID_ARGUMENT, "q, chunk_sum, n_sel, chunk_idx and group_idx must be non-NULL");
+  if ((st = check_aligned("q and chunk_sum", {q, chunk_sum})) != HGA_OK) return st;
   if ((st = check_tier(group_sum, "group_sum", seq_len, q_start)) != HGA_OK) return st;
   return device_status(
       hga::launch_route(s, q, chunk_sum, static_cast<const float*>(group_sum->host),
@@ -248,6 +267,7 @@ hga_status hga_attend(const hga_config* cfg, const void* q, int64_t q_start, int
   if (n_q == 0) return ok();
   if (!q || !out || !n_sel || (s.kg > 0 && !group_idx))
     return fail(HGA_ERR_INVALID_ARGUMENT, "q, out, n_sel and group_idx must be non-NULL");
+  if ((st = check_aligned("q, out and workspace", {q, out, workspace})) != HGA_OK) return st;
   if ((st = check_tier(k, "k", seq_len, q_start)) != HGA_OK) return st;
   if ((st = check_tier(v, "v", seq_len, q_start)) != HGA_OK) return st;
   if ((st = check_kv_tier(s, k, v, workspace, ws_bytes)) != HGA_OK) return st;
@@ -267,6 +287,7 @@ hga_status hga_route_attend(const hga_config* cfg, const void* q, int64_t q_star
   if (!q || !chunk_sum || !n_sel || !out || (s.kc > 0 && !chunk_idx) || (s.kg > 0 && !group_idx))
     return fail(HGA_ERR_INVALID_ARGUMENT,
                 "q, chunk_sum, n_sel, out, chunk_idx and group_idx must be non-NULL");
+  if ((st = check_aligned("q, chunk_sum, out and workspace", {q, chunk_sum, out, workspace})) != HGA_OK) return st;
   if ((st = check_tier(group_sum, "group_sum", seq_len, q_start)) != HGA_OK) return st;
   if ((st = check_tier(k, "k", seq_len, q_start)) != HGA_OK) return st;
   if ((st = check_tier(v, "v", seq_len, q_start)) != HGA_OK) return st;
@@ -278,7 +299,7 @@ hga_status hga_route_attend(const hga_config* cfg, const void* q, int64_t q_star
   // the fused kernel, unless the workspace lets the attention spread few
   // items over more workgroups
   const bool split = k->split == 0 && hga::attend_split_count(s) > 1 && workspace &&
-                     ((uintptr_t)workspace & 15) == 0 && ws_bytes >= hga::attend_split_bytes(s);
+                     ws_bytes >= hga::attend_split_bytes(s);
   if (!split && hga::fused_route_attend_supported(s, k->split))
     return device_status(hga::launch_route_attend(s, q, chunk_sum, gs_host, gs_dev, group_sum->split, kv,
                                                   chunk_idx, group_idx, n_sel, out, lse, hs),
@@ -302,6 +323,8 @@ hga_status hga_attend_backward(const hga_config* cfg, const void* q, int64_t q_s
   if (n_q == 0) return ok();
   if (!q || !n_sel || !out || !lse || !dout || !dq || !dk || !dv || (s.kg > 0 && !group_idx))
     return fail(HGA_ERR_INVALID_ARGUMENT, "q, group_idx, n_sel, out, lse, dout, dq, dk and dv must be non-NULL");
+  if ((st = check_aligned("q, out, dout, dq, dk, dv and workspace", {q, out, dout, dq, dk, dv, workspace})) != HGA_OK)
+    return st;
   if ((st = check_tier(k, "k", seq_len, q_start)) != HGA_OK) return st;
   if ((st = check_tier(v, "v", seq_len, q_start)) != HGA_OK) return st;
   if (k->split != v->split) return fail(HGA_ERR_INVALID_ARGUMENT, "k.split and v.split differ");
@@ -333,6 +356,6 @@ const char* hga_status_string(hga_status status) {
 
 const char* hga_last_error(void) { return g_err; }
 
-int32_t hga_version(void) { return 106; }
+int32_t hga_version(void) { return 107; }
 
 }  // extern "C"

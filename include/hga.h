@@ -33,6 +33,12 @@
  *   Memory     "device" pointers are GPU memory of the current HIP device;
  *              "host" pointers of an hga_tiered are pinned host memory
  *              allocated with hipHostMalloc (mapped, readable by kernels).
+ *   Alignment  the kernels move rows 16 bytes at a time: every tensor
+ *              pointer (Q, K, V, O, the summaries, the gradients, both parts
+ *              of an hga_tiered) and the workspace must be 16-byte aligned
+ *              (index, count and LSE arrays need only their element's
+ *              alignment); otherwise HGA_ERR_INVALID_ARGUMENT before any
+ *              launch.
  *   Streams    `stream` is a hipStream_t (NULL = the default stream). All work
  *              is enqueued on it; nothing synchronizes.
  *   Errors     arguments are validated on the host before any launch; on an
@@ -110,9 +116,12 @@ enum {
  * HGA_WS_ATTEND is 0 unless the call has few (block, KV head) items (bf16, at
  * most 128 attention workgroups, as when decoding a few sequences): then it
  * is the room for each item's tiles to be cut into ranges attended by
- * separate workgroups, whose partial softmax states are merged per query row
- * (the outputs then differ from the one-workgroup result by float32 rounding
- * order only). Given less, the calls attend each item in one workgroup.
+ * separate workgroups, whose partial softmax states are merged per query row.
+ * The outputs then differ from the one-workgroup result by the rounding of
+ * the probabilities to bfloat16 before the PV product, which each range takes
+ * against its own running maximum (about 2^-9 relative, within the output
+ * tolerance); the LSE differs by float32 rounding order only. Given less, the
+ * calls attend each item in one workgroup.
  * The tiered figure holds for every split <= seq_len - n_q: it covers chunk
  * flags and slots and an HBM cache as large as the whole host part of K and V
  * (the attention copies each history chunk any query block needs into it once
@@ -198,9 +207,8 @@ hga_status hga_route(const hga_config* cfg, const void* q, int64_t q_start, int6
  *   out        device, [Hq][n_q][d] of cfg->dtype.
  *   lse        device, [Hq][n_q] float32, or NULL.
  *   workspace  device, at least hga_workspace_size(...) bytes (with split 0,
- *              NULL, fewer bytes than HGA_WS_ATTEND asks for, or an address
- *              that is not 16-byte aligned is accepted: each item is then
- *              attended by one workgroup). */
+ *              NULL or fewer bytes than HGA_WS_ATTEND asks for is accepted:
+ *              each item is then attended by one workgroup). */
 hga_status hga_attend(const hga_config* cfg, const void* q, int64_t q_start, int64_t n_q,
                       int64_t seq_len, const hga_tiered* k, const hga_tiered* v,
                       const int32_t* group_idx, const int32_t* n_sel,

@@ -31,7 +31,7 @@ def test_every_declared_entry_point_is_exported(lib):
     assert declared == set(B.EXPORTS)
     for name in declared:
         assert hasattr(lib, name)
-    assert hga.hga_version() == 106
+    assert hga.hga_version() == 107
 
 
 def test_status_strings(lib):
@@ -132,6 +132,27 @@ def test_null_pointers():
         args[[0, 1, 3, 4, 5, 6, 7, 8][i]] = None
         q, cs, gs, k, v, ci, gi, ns, out = args
         assert _status(hga.hga_route_attend, c, q, 14336, 2048, 16384, cs, gs, k, v, ci, gi, ns, out) == E
+
+
+def test_misaligned_pointers_are_rejected():
+    """The kernels move rows 16 bytes at a time: a tensor or workspace address
+    off a 16-byte boundary is refused before any launch."""
+    c = cfg()
+    E = hga.HGA_ERR_INVALID_ARGUMENT
+    odd = FAKE + 8
+    assert _status(hga.hga_build_summaries, c, odd, 16384, FAKE, FAKE) == E
+    assert _status(hga.hga_build_summaries, c, FAKE, 16384, FAKE, odd) == E
+    assert _status(hga.hga_route, c, odd, 14336, 2048, 16384, FAKE, FAKE, FAKE, FAKE, FAKE) == E
+    assert _status(hga.hga_route, c, FAKE, 14336, 2048, 16384, FAKE, (odd, FAKE, 1024), FAKE, FAKE, FAKE) == E
+    assert _status(hga.hga_attend, c, FAKE, 14336, 2048, 16384, FAKE, FAKE, FAKE, FAKE, odd) == E
+    assert _status(hga.hga_attend, c, FAKE, 14336, 2048, 16384, (FAKE, odd, 1024), FAKE, FAKE, FAKE, FAKE) == E
+    assert _status(hga.hga_attend, c, FAKE, 14336, 2048, 16384, FAKE, FAKE, FAKE, FAKE, FAKE, None, odd, 1 << 30) == E
+    assert _status(hga.hga_route_attend, c, FAKE, 14336, 2048, 16384, odd, *[FAKE] * 7) == E
+    assert _status(hga.hga_route_attend, c, FAKE, 14336, 2048, 16384, *[FAKE] * 8, None, odd, 1 << 30) == E
+    assert "16-byte aligned" in hga.hga_last_error()
+    assert _status(hga.hga_stream_forward, c, FAKE, FAKE, odd, 4096, 1024, *[FAKE] * 7) == E
+    assert _status(hga.hga_attend_backward, c, FAKE, 14336, 2048, 16384, *[FAKE] * 8, odd, FAKE, FAKE,
+                   1 << 30) == E
 
 
 def test_tier_validation():
