@@ -8,6 +8,6 @@ from ._binding import (  # noqa: F401
     HGA_ERR_WORKSPACE, HGA_F32, HGA_OK, HGA_SUMMARY_MEAN, HGA_WS_ATTEND, HGA_WS_ATTEND_TIERED,
     HGA_WS_BACKWARD, HGA_WS_BACKWARD_TIERED, HGA_WS_ROUTE, LIB_PATH, HgaError, hga_attend, hga_attend_backward, hga_build_summaries,
     hga_build_summaries_range,
-    hga_config, hga_last_error, hga_route, hga_route_attend, hga_status_string, hga_stream_forward,
+    hga_config, hga_last_error, hga_route, hga_route_attend, hga_route_attend_noalloc, hga_status_string, hga_stream_forward,
     hga_tiered, hga_version, hga_workspace_size, load, make_config,
 )

@@ -21,7 +21,7 @@ HGA_WS_ROUTE, HGA_WS_ATTEND, HGA_WS_ATTEND_TIERED, HGA_WS_BACKWARD, HGA_WS_BACKW
 
 # Every exported entry point of include/hga.h.
 EXPORTS = ("hga_workspace_size", "hga_build_summaries", "hga_build_summaries_range", "hga_route", "hga_attend",
-           "hga_route_attend", "hga_stream_forward", "hga_attend_backward", "hga_status_string", "hga_last_error",
+           "hga_route_attend", "hga_route_attend_noalloc", "hga_stream_forward", "hga_attend_backward", "hga_status_string", "hga_last_error",
            "hga_version")
 
 
@@ -61,11 +61,12 @@ def load():
         lib.hga_route.argtypes = [cfgp, P, I64, I64, I64, P, tierp, P, P, P, P, SZ, P]
         lib.hga_attend.argtypes = [cfgp, P, I64, I64, I64, tierp, tierp, P, P, P, P, P, SZ, P]
         lib.hga_route_attend.argtypes = [cfgp, P, I64, I64, I64, P, tierp, tierp, tierp, P, P, P, P, P, P, SZ, P]
+        lib.hga_route_attend_noalloc.argtypes = [cfgp, P, I64, I64, I64, P, tierp, tierp, tierp, P, P, P, P, P, P]
         lib.hga_build_summaries_range.argtypes = [cfgp, P, I64, I64, I64, P, P, P]
         lib.hga_stream_forward.argtypes = [cfgp, P, P, P, I64, I64, P, P, P, P, P, P, P, P]
         lib.hga_attend_backward.argtypes = [cfgp, P, I64, I64, I64, tierp, tierp, P, P, P, P, P, P, P, P, P, SZ, P]
         for f in ("hga_build_summaries", "hga_build_summaries_range", "hga_route", "hga_attend",
-                  "hga_route_attend", "hga_stream_forward", "hga_attend_backward"):
+                  "hga_route_attend", "hga_route_attend_noalloc", "hga_stream_forward", "hga_attend_backward"):
             getattr(lib, f).restype = C.c_int
         lib.hga_status_string.argtypes = [C.c_int]
         lib.hga_status_string.restype = C.c_char_p
@@ -153,6 +154,14 @@ def hga_route_attend(cfg, q, q_start, n_q, seq_len, chunk_sum, group_sum, k, v, 
     _check(load().hga_route_attend(C.byref(cfg), _ptr(q), q_start, n_q, seq_len, _ptr(chunk_sum), C.byref(gt),
                                    C.byref(kt), C.byref(vt), _ptr(chunk_idx), _ptr(group_idx), _ptr(n_sel),
                                    _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def hga_route_attend_noalloc(cfg, q, q_start, n_q, seq_len, chunk_sum, group_sum, k, v, chunk_idx, group_idx,
+                             n_sel, out, lse=None, stream=None):
+    gt, kt, vt = _tier(group_sum), _tier(k), _tier(v)
+    _check(load().hga_route_attend_noalloc(C.byref(cfg), _ptr(q), q_start, n_q, seq_len, _ptr(chunk_sum),
+                                           C.byref(gt), C.byref(kt), C.byref(vt), _ptr(chunk_idx), _ptr(group_idx),
+                                           _ptr(n_sel), _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def hga_build_summaries_range(cfg, k, seq_len, chunk_begin, chunk_end, group_sum, chunk_sum, stream=None):

@@ -6,6 +6,7 @@
 #include <stdio.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "hga_internal.h"
 
@@ -136,6 +137,40 @@ hga_status check_kv_tier(const hga::Shape& s, const hga_tiered* k, const hga_tie
   const size_t need = hga::tier_cache_bytes(s, k->split);
   if (!workspace || ws_bytes < need)
     return fail(HGA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : (size_t)0);
+  return HGA_OK;
+}
+
+// ---------------------------------------------------------------- static scratch
+// Scratch memory of hga_route_attend_noalloc: the partial softmax states of
+// the spread attention (attend_split_bytes), at most 256 ranges of 8 waves x
+// (d / 2 + 2) x 64 floats at d = 128, i.e. 33 MiB. Each device the library
+// runs on holds its own copy until the process ends. Its device address is
+// taken once per device with hipGetSymbolAddress; host code passes that
+// address (never the array's name, which is a host-side stand-in) to the
+// kernels.
+constexpr size_t kScratchBytes = (size_t)256 * 8 * (128 / 2 + 2) * 64 * sizeof(float);
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device, with that device current).
+hga_status scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(HGA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return device_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(HGA_ERR_DEVICE, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
   return HGA_OK;
 }
 
@@ -310,6 +345,27 @@ hga_status hga_route_attend(const hga_config* cfg, const void* q, int64_t q_star
   if (st != HGA_OK) return st;
   return device_status(hga::launch_attend(s, q, kv, group_idx, n_sel, out, lse, workspace, ws_bytes, hs),
                        "hga_route_attend attention launch");
+}
+
+hga_status hga_route_attend_noalloc(const hga_config* cfg, const void* q, int64_t q_start, int64_t n_q,
+                                    int64_t seq_len, const float* chunk_sum, const hga_tiered* group_sum,
+                                    const hga_tiered* k, const hga_tiered* v, int32_t* chunk_idx, int32_t* group_idx,
+                                    int32_t* n_sel, void* out, float* lse, void* stream) {
+  hga::Shape s;
+  hga_status st = make_shape(cfg, seq_len, q_start, n_q, &s);
+  if (st != HGA_OK) return st;
+  if (n_q == 0) return ok();
+  if (!k || !v) return fail(HGA_ERR_INVALID_ARGUMENT, "k and v must be non-NULL");
+  if (k->split != 0 || v->split != 0)
+    return fail(HGA_ERR_UNSUPPORTED, "hga_route_attend_noalloc needs K and V on the device (split 0)");
+  const size_t need = hga::attend_split_bytes(s);
+  if (need > kScratchBytes)
+    return fail(HGA_ERR_UNSUPPORTED, "the call needs %zu bytes of scratch; the static scratch holds %zu", need,
+                kScratchBytes);
+  void* ptr = nullptr;
+  if ((st = scratch_of_current_device(&ptr)) != HGA_OK) return st;
+  return hga_route_attend(cfg, q, q_start, n_q, seq_len, chunk_sum, group_sum, k, v, chunk_idx, group_idx, n_sel,
+                          out, lse, need > 0 ? ptr : nullptr, need, stream);
 }
 
 hga_status hga_attend_backward(const hga_config* cfg, const void* q, int64_t q_start, int64_t n_q,

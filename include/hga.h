@@ -29,7 +29,8 @@
  *              summaries are float32; indices are int32.
  *   Ownership  the caller allocates every buffer and the workspace and keeps
  *              them alive until the work on `stream` has finished. The library
- *              allocates nothing and keeps no state between calls.
+ *              allocates nothing and keeps no state between calls, except the
+ *              static scratch array of hga_route_attend_noalloc (see there).
  *   Memory     "device" pointers are GPU memory of the current HIP device;
  *              "host" pointers of an hga_tiered are pinned host memory
  *              allocated with hipHostMalloc (mapped, readable by kernels).
@@ -235,6 +236,29 @@ hga_status hga_route_attend(const hga_config* cfg, const void* q, int64_t q_star
                             const hga_tiered* k, const hga_tiered* v,
                             int32_t* chunk_idx, int32_t* group_idx, int32_t* n_sel,
                             void* out, float* lse, void* workspace, size_t ws_bytes, void* stream);
+
+/* hga_route_attend for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same routing and attention, with the same results, taking
+ * no workspace. Where hga_route_attend would spread few items over several
+ * workgroups given its HGA_WS_ATTEND workspace (decoding a few sequences), the
+ * partial softmax states go to a static device array of the library instead:
+ * at most 33 MiB (256 ranges of 8 waves x (head_dim / 2 + 2) x 64 floats at
+ * head_dim 128), held by each device the library runs on until the process
+ * ends; shapes that would need more return HGA_ERR_UNSUPPORTED. The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine);
+ * on its first call on a device it looks the array's device address up once.
+ * Every call on one device shares that device's array, which keeps the last
+ * call's contents (each range writes its partial state before the merge reads
+ * it, so nothing needs clearing): calls that overlap on one device, on
+ * different streams or from different threads, race and must be ordered by
+ * the caller. K and V must be entirely on the device (split 0, else
+ * HGA_ERR_UNSUPPORTED). Other arguments, layouts and errors are those of
+ * hga_route_attend. */
+hga_status hga_route_attend_noalloc(const hga_config* cfg, const void* q, int64_t q_start, int64_t n_q,
+                                    int64_t seq_len, const float* chunk_sum, const hga_tiered* group_sum,
+                                    const hga_tiered* k, const hga_tiered* v, int32_t* chunk_idx, int32_t* group_idx,
+                                    int32_t* n_sel, void* out, float* lse, void* stream);
 
 /* Forward pass over a whole sequence in segments, in the pages' execution
  * order (section 2.1 with the segment-by-segment processing of section 2.2):
