@@ -5,34 +5,35 @@ hga_build_summaries_range (group and chunk summaries of the chunks the step's
 own positions close; the history's summaries are resident, built when their
 chunks closed, as the pages keep them), then hga_route_attend (block queries,
 chunk stage, group stage and exact routed attention), all on one stream with
-every input already in HBM. The rate with every chunk's summaries rebuilt
-each step is reported alongside. With at most
-4 query heads per KV head hga_route_attend is one kernel; with more (the 64K
-layer's 8) the step runs the router and the attention kernels, timed apart.
-The 16K step through the separate hga_route and hga_attend calls is reported
-alongside.
+every input already in HBM. With at most 4 query heads per KV head
+hga_route_attend is one kernel; with more (the 64K layer's 8) the step runs
+the router and the attention kernels, timed apart.
+
+`value` is the workload's query tokens over the wall-clock time of the timed
+steps, run back to back between two device synchronizations. Then every
+stage, and the whole step, is timed call by call with HIP event pairs on the
+launch stream: warm (back to back) and with the caches flushed (a 512 MiB
+buffer written before each call, outside the pair: the L2 caches and the
+256 MB Infinity Cache then hold none of the step's data). Each reports mean,
+median, p10 and p90; `value_flushed` is n_q over the median flushed step.
 
 The workload is the 16,384-token training-segment shape (Qwen3-8B heads:
 32 query / 8 KV heads, head_dim 128, bf16, 2,048 active queries over a
 14,336-token history, top-16 chunks, top-64 groups, sink 64, local 128).
-The same line also reports the 65,536-token Qwen3-30B-A3B-shaped layer with
-its history in HBM and, separately, with its history in pinned host memory
-(that rate includes the PCIe transfer of the routed set), and the
-131,072-token long-evaluation layer with its history in pinned host memory.
+`also` reports the same figures for the tiny float32 1K workload, the
+Qwen3-8B 4K layer and the 65,536-token Qwen3-30B-A3B-shaped layer with its
+history in HBM; the 64K and 131,072-token layers with their history in
+pinned host memory (PCIe-inclusive, with the bytes they move over the host
+link and the box's measured pinned host-to-device rate); the summary build
+and the router against HBM; the 16K step through the separate calls; the 16K
+sequence streamed in segments; the backward of the attention over the 16K
+segment; and one-token decoding at the end of the 16K and 64K sequences.
 
-It also reports the backward of the attention over the 16K workload's
-2,048-query active segment (hga_attend_backward: dQ, and dK, dV of the
-segment's keys; the history is detached) against bf16 MFMA peak, and one-token decoding (query block of one token, routing over
-the resident summaries of the closed chunks, then attention) at the end of the
-16K and 64K sequences for batches of sequences, as generated tokens per
-second with the fused kernel's HBM roofline.
-
-Output: one JSON line (see the keys below). ``roofline`` covers the kernel
-that does the attention (the route-and-attend kernel, or the attention kernel
-where routing runs apart): the attention's algorithmic flops or bytes over
-that kernel's mean duration, measured with HIP events on the launch stream
-over the timed steps; ``cpu_baseline`` is the CPU oracle on a bounded sample
-of the same workload.
+``roofline`` covers the kernel that does the attention (the route-and-attend
+kernel, or the attention kernel where routing runs apart): the attention's
+algorithmic flops or bytes over that kernel's mean warm duration;
+``cpu_baseline`` is the CPU oracle on the same workload, per stage, on all
+host threads and on one.
 """
 from __future__ import annotations
 
@@ -49,7 +50,8 @@ import numpy as np  # noqa: E402
 
 PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
 PEAK_BF16 = 2.5e15         # flop/s, MI355X dense bf16 MFMA
-PEAK_F32_MFMA = 157.3e12
+PEAK_F32 = 157.3e12        # flop/s, MI355X float32 vector
+PEAK_HOST_LINK = 64e9      # B/s, PCIe 5.0 x16 per direction (nominal)
 
 METRIC = "routed-attn query-tokens/sec per layer at 16K/64K; % of HBM or MFMA peak"
 
@@ -123,6 +125,63 @@ def to_dev(a, dtype, dev):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
 
 
+_FLUSH = []
+
+
+def cache_flusher(mib=512):
+    """A call that writes `mib` MiB of device memory: more than the 256 MB
+    Infinity Cache and every L2, so the next call finds none of its data
+    cached (the buffer is allocated once)."""
+    import torch
+    if not _FLUSH:
+        _FLUSH.append(torch.empty(mib << 20, dtype=torch.uint8, device="cuda:0"))
+    buf = _FLUSH[0]
+    return lambda: buf.fill_(1)
+
+
+def event_us(call, n, flush=None, warm=2):
+    """Durations (us) of n calls, each bracketed by a pair of HIP events on
+    the current stream (the stream the library launches on), after `warm`
+    untimed calls; with flush, it runs before each call, outside the pair."""
+    import torch
+    for _ in range(warm):
+        call()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for e0, e1 in evs:
+        if flush is not None:
+            flush()
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) * 1e3 for e0, e1 in evs]
+
+
+def stats(us):
+    """Mean, median, p10 and p90 of a list of durations (us)."""
+    a = np.asarray(us, dtype=np.float64)
+    assert a.size > 0 and np.isfinite(a).all()
+    return {"mean": float(a.mean()), "median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "n": int(a.size)}
+
+
+def timed_calls(call, steps, warmup, samples=None):
+    """Wall-clock time of `steps` calls back to back, then event statistics
+    of `samples` (default max(steps, 20)) warm calls and as many with the
+    caches flushed before each."""
+    import torch
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    n = samples or max(steps, 20)
+    return wall, stats(event_us(call, n)), stats(event_us(call, n, cache_flusher()))
+
+
 class Workload:
     """Device buffers and one step of the path for one configuration."""
 
@@ -158,7 +217,6 @@ class Workload:
         if fused is None:
             fused = cfg["dtype"] == "bf16" and split == 0 and cfg["hq"] // hkv <= 4
         self.fused = fused
-        self.n_stages = 2 if fused else 3
         self.pins = []
         self.ws, self.wsb = None, 0
         # the history's summaries are resident before the step (built when
@@ -178,56 +236,51 @@ class Workload:
         else:
             self.gs_t, self.k_t, self.v_t = self.gs, k, v
 
-    def step(self, ev=None, timed=-1):
-        """One step; with ev, HIP events on the launch stream bracket stage
-        `timed` (0 summaries, 1 routing or routing + attention, 2 attention)."""
+    def stage_calls(self):
+        """The step's stages in order, as (name, call) pairs: the summaries of
+        the chunks the step's positions close, then routing and attention in
+        one call (one kernel) or in two."""
         hga, c = self.hga, self.c
-
-        def mark(stage, k):
-            if ev is not None and stage == timed:
-                ev[k].record()
-        mark(0, 0)
+        calls = []
         if self.split == 0:
-            hga.hga_build_summaries_range(c, self.k_full, self.L, *self.seg_chunks, self.gs, self.cs)
-        mark(0, 1)
-        mark(1, 0)
+            calls.append(("summaries", lambda: hga.hga_build_summaries_range(c, self.k_full, self.L, *self.seg_chunks,
+                                                                             self.gs, self.cs)))
         if self.fused:
-            hga.hga_route_attend(c, self.q, self.q0, self.nq, self.L, self.cs, self.gs_t, self.k_t, self.v_t,
-                                 self.ci, self.gi, self.ns, self.out, self.lse, self.ws, self.wsb)
-            mark(1, 1)
+            calls.append(("route_attend", lambda: hga.hga_route_attend(
+                c, self.q, self.q0, self.nq, self.L, self.cs, self.gs_t, self.k_t, self.v_t, self.ci, self.gi,
+                self.ns, self.out, self.lse, self.ws, self.wsb)))
         else:
-            hga.hga_route(c, self.q, self.q0, self.nq, self.L, self.cs, self.gs_t, self.ci, self.gi, self.ns)
-            mark(1, 1)
-            mark(2, 0)
-            hga.hga_attend(c, self.q, self.q0, self.nq, self.L, self.k_t, self.v_t, self.gi, self.ns,
-                           self.out, self.lse, self.ws, self.wsb)
-            mark(2, 1)
+            calls.append(("route", lambda: hga.hga_route(c, self.q, self.q0, self.nq, self.L, self.cs, self.gs_t,
+                                                         self.ci, self.gi, self.ns)))
+            calls.append(("attend", lambda: hga.hga_attend(c, self.q, self.q0, self.nq, self.L, self.k_t, self.v_t,
+                                                           self.gi, self.ns, self.out, self.lse, self.ws, self.wsb)))
+        return calls
 
-    # one step in SAMPLE_PERIOD carries a pair of timing events (measured: a
-    # pair on every second step costs about 5% of the step, on every eighth
-    # nothing measurable)
-    SAMPLE_PERIOD = 8
+    def step(self):
+        for _, call in self.stage_calls():
+            call()
 
-    def run(self, steps, warmup):
-        """Time `steps` steps. Every SAMPLE_PERIOD-th step brackets one stage
-        with HIP events on the launch stream, the stages in turn; stage times
-        are means over their own samples."""
+    def run(self, steps, warmup, samples):
+        """Time `steps` steps back to back (wall clock between two device
+        synchronizations), then every stage and the whole step with HIP event
+        pairs on the launch stream: `samples` calls back to back (warm), and
+        as many with a 512 MiB buffer written before each (the L2 caches and
+        the 256 MB Infinity Cache then hold none of the step's data)."""
         torch = self.torch
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
-        per = self.SAMPLE_PERIOD
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-        which = [(i // per) % self.n_stages if i % per == 0 else -1 for i in range(steps)]
-        torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(steps):
-            self.step(evs[i], which[i])
+        for _ in range(steps):
+            self.step()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        stage = [[evs[i][0].elapsed_time(evs[i][1]) * 1e3 for i in range(steps) if which[i] == j]
-                 for j in range(self.n_stages)]   # us
-        return wall, stage
+        stages = {"warm": {}, "flushed": {}}
+        flush = cache_flusher()
+        for name, call in self.stage_calls() + [("step", self.step)]:
+            stages["warm"][name] = event_us(call, samples)
+            stages["flushed"][name] = event_us(call, samples, flush)
+        return wall, stages
 
     def free(self):
         for p in self.pins:
@@ -260,18 +313,22 @@ def measured_traffic(workload, kernel):
 
 
 def roofline(cfg, n_sel, attend_us, kernel, with_traffic=True):
+    """The attention's algorithmic flops and bytes over the mean launch
+    duration of the kernel that runs it, against whichever MI355X peak binds
+    (bf16 MFMA or HBM; the float32 path against the float32 peak)."""
     flops, byts, _ = algorithmic(cfg, n_sel)
     traffic = measured_traffic(cfg["name"], kernel) if with_traffic else None
-    t_mfma = flops / PEAK_BF16
+    peak_flops = PEAK_BF16 if cfg["dtype"] == "bf16" else PEAK_F32
+    t_mfma = flops / peak_flops
     t_hbm = byts / PEAK_HBM
     t = attend_us * 1e-6
+    base = {"kernel": kernel, "traffic": traffic, "traffic_unit": "HBM bytes per launch",
+            "algorithmic_flops": flops, "algorithmic_bytes": byts, "kernel_us_mean": attend_us}
     if t_mfma >= t_hbm:
-        return {"kernel": kernel, "bound": "mfma", "achieved": flops / t / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
-                "frac": flops / t / PEAK_BF16, "traffic": traffic, "traffic_unit": "HBM bytes per launch",
-                "algorithmic_flops": flops, "algorithmic_bytes": byts}
-    return {"kernel": kernel, "bound": "hbm", "achieved": byts / t / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-            "frac": byts / t / PEAK_HBM, "traffic": traffic, "traffic_unit": "HBM bytes per launch",
-            "algorithmic_flops": flops, "algorithmic_bytes": byts}
+        return {"bound": "mfma" if cfg["dtype"] == "bf16" else "alu", "achieved": flops / t / 1e12,
+                "peak": peak_flops / 1e12, "unit": "TFLOP/s", "frac": flops / t / peak_flops, **base}
+    return {"bound": "hbm", "achieved": byts / t / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+            "frac": byts / t / PEAK_HBM, **base}
 
 
 def host_link_bytes(cfg, n_sel, group_idx, split):
@@ -294,52 +351,103 @@ def host_link_bytes(cfg, n_sel, group_idx, split):
     return sum(len(n) for n in need) * 64 * cfg["d"] * esz * 2
 
 
-def cpu_baseline(cfg_id, min_seconds=10.0):
-    """The oracle timed on the host cores: summaries, routing and attention of
-    every (block, KV head) of the layer, repeated until at least min_seconds
-    of CPU work have run."""
+def cpu_baseline(cfg_id, seconds=10.0, sample_blocks=4):
+    """The oracle timed on the host cores, per stage: summaries of every chunk
+    of the sequence, routing and attention of the (block, KV head) items.
+
+    All threads: the whole layer, repeated for about `seconds`. One thread: the
+    summaries once, routing and attention of the items of `sample_blocks`
+    blocks spread over the layer (all KV heads), scaled to the layer by item
+    count. query-tokens/s = n_q / (summaries + routing + attention)."""
     import oracle
     import synth
     cfg = synth.config(cfg_id)
     x = synth.make_inputs(cfg)
     f = {n: synth.to_f64(x[n], cfg["dtype"]) for n in ("q", "k", "v")}
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        sums = (oracle.summaries(cfg, f["k"]), oracle.abs_summaries(cfg, f["k"]))
-        ci, gi, ns, dg = oracle.route(cfg, f["q"], f["k"], sums=sums)
-        oracle.attend(cfg, f["q"], f["k"], f["v"], oracle.all_items(cfg), gi, ns[:, 1])
-        reps += 1
-        if time.perf_counter() - t0 >= min_seconds:
-            break
-    el = time.perf_counter() - t0
-    return {"value": reps * cfg["n_q"] / el, "unit": "query-tokens/s", "cores": oracle.threads(),
-            "kind": "oracle",
-            "sample": f"float64 C oracle, whole layer ({cfg['n_q']} queries, all {cfg['hkv']} KV heads: "
-                      f"summaries, routing, attention) repeated {reps}x in {el:.1f} s"}
+    items = oracle.all_items(cfg)
+    nthreads = oracle.threads()
+
+    def stages(its, reps_for=None):
+        t = {"summaries": 0.0, "routing": 0.0, "attention": 0.0}
+        reps = 0
+        t_end = time.perf_counter() + (reps_for or 0.0)
+        while True:
+            t0 = time.perf_counter()
+            sums = (oracle.summaries(cfg, f["k"]), oracle.abs_summaries(cfg, f["k"]))
+            t1 = time.perf_counter()
+            ci, gi, ns, _ = oracle.route(cfg, f["q"], f["k"], items=its, sums=sums)
+            t2 = time.perf_counter()
+            oracle.attend(cfg, f["q"], f["k"], f["v"], its, gi, ns[:, 1])
+            t3 = time.perf_counter()
+            t["summaries"] += t1 - t0
+            t["routing"] += t2 - t1
+            t["attention"] += t3 - t2
+            reps += 1
+            if reps_for is None or time.perf_counter() >= t_end:
+                break
+        return {k: v / reps for k, v in t.items()}, reps
+
+    full, reps = stages(items, seconds)
+    nb = cfg["n_q"] // cfg["q_block"]
+    blocks = sorted(set(int(round(i * (nb - 1) / max(sample_blocks - 1, 1))) for i in range(sample_blocks)))
+    sample = [(b, h) for b in blocks for h in range(cfg["hkv"])]
+    oracle.set_threads(1)
+    try:
+        one, _ = stages(sample)
+    finally:
+        oracle.set_threads(nthreads)
+    scale = len(items) / len(sample)
+    one = {"summaries": one["summaries"], "routing": one["routing"] * scale, "attention": one["attention"] * scale}
+    rate = lambda t: cfg["n_q"] / sum(t.values())
+    return {"value": rate(full), "unit": "query-tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"float64 C oracle on {cfg['name']}: the whole layer ({cfg['n_q']} queries, all "
+                      f"{cfg['hkv']} KV heads; summaries of every chunk, routing, attention) repeated {reps}x on "
+                      f"{nthreads} threads; one thread: summaries, then routing and attention of blocks {blocks} "
+                      f"(all KV heads) scaled to the layer by item count",
+            "stages_s": full,
+            "one_thread": {"value": rate(one), "unit": "query-tokens/s", "cores": 1, "stages_s": one}}
 
 
 class Result:
     """Timing of one workload: wall time of the timed steps and per-stage
-    means and medians (us)."""
+    statistics (us), warm and with the caches flushed."""
 
-    def __init__(self, w, wall, stage):
-        self.cfg, self.fused, self.wall = w.cfg, w.fused, wall
+    def __init__(self, w, wall, stages, steps):
+        self.cfg, self.fused, self.wall, self.steps = w.cfg, w.fused, wall, steps
         self.ns = w.ns.cpu().numpy()
+        self.gi = w.gi.cpu().numpy()
         self.split = w.split
-        self.host_bytes = host_link_bytes(w.cfg, self.ns, w.gi.cpu().numpy(), w.split) if w.split else 0
-        self.mean = [float(np.mean(x)) if x else float("nan") for x in stage]
-        self.med = [float(np.median(x)) if x else float("nan") for x in stage]
+        self.host_bytes = host_link_bytes(w.cfg, self.ns, self.gi, w.split) if w.split else 0
+        self.warm = {k: stats(v) for k, v in stages["warm"].items()}
+        self.flushed = {k: stats(v) for k, v in stages["flushed"].items()}
 
-    def stages(self, which):
-        v = self.mean if which == "mean" else self.med
-        if self.fused:
-            return {"summaries": v[0], "route_attend": v[1]}
-        return {"summaries": v[0], "route": v[1], "attend": v[2]}
+    @property
+    def value(self):
+        return self.steps * self.cfg["n_q"] / self.wall
 
-    def roofline(self, with_traffic=True):
-        if self.fused:
-            return roofline(self.cfg, self.ns, self.mean[1], "route_attend_bf16", with_traffic)
-        return roofline(self.cfg, self.ns, self.mean[2], "attend_bf16", with_traffic)
+    def attention_stage(self):
+        return "route_attend" if self.fused else "attend"
+
+    def kernel_name(self):
+        if self.cfg["dtype"] != "bf16":
+            return "attend_f32"
+        return "route_attend_bf16" if self.fused else "attend_bf16"
+
+    def roofline(self, flushed=False, with_traffic=True):
+        st = (self.flushed if flushed else self.warm)[self.attention_stage()]
+        return roofline(self.cfg, self.ns, st["mean"], self.kernel_name(), with_traffic and not flushed)
+
+    def line(self, with_traffic=True):
+        """The workload's measured figures as one JSON object."""
+        out = {"value": self.value, "unit": "query-tokens/s",
+               "value_flushed": self.cfg["n_q"] / (self.flushed["step"]["median"] * 1e-6),
+               "ms_per_step": self.wall / self.steps * 1e3,
+               "stages_us": self.warm, "stages_us_flushed": self.flushed,
+               "roofline": self.roofline(with_traffic=with_traffic),
+               "roofline_flushed": self.roofline(flushed=True)}
+        if self.split:
+            out["host_link_bytes_per_step"] = self.host_bytes
+        return out
 
 
 def stream_line(passes, warmup):
@@ -411,8 +519,9 @@ def decode_line(cfg_id, batch, steps, warmup):
     workgroups). The batch is folded into the heads (sequence-major
     [batch x heads]); every sequence repeats the workload's K/V and last query
     at its own addresses. Summaries are built before timing (each closes once
-    per 64 generated tokens). Timed with HIP events around one launch in eight on the
-    launch stream."""
+    per 64 generated tokens). Wall clock over the steps; each call's duration
+    from HIP event pairs on the launch stream (warm, and with the caches
+    flushed)."""
     import torch
 
     import hierarchical_sparse_attention_hga_amd as hga
@@ -442,21 +551,8 @@ def decode_line(cfg_id, batch, steps, warmup):
 
     def one():
         hga.hga_route_attend(c, q, pos, 1, L, cs, gs, k, v, ci, gi, ns, out, lse, ws, wsb)
-    for _ in range(warmup):
-        one()
-    torch.cuda.synchronize()
-    per = Workload.SAMPLE_PERIOD
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
-        if i % per == 0:
-            evs[i][0].record()
-        one()
-        if i % per == 0:
-            evs[i][1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    us = float(np.mean([evs[i][0].elapsed_time(evs[i][1]) * 1e3 for i in range(0, steps, per)]))
+    wall, warm, flushed = timed_calls(one, steps, warmup)
+    us = warm["mean"]
     nsel = ns.cpu().numpy().reshape(hkv, 2)
     byts = float(sum(decode_bytes(base, pos, nsel[h]) for h in range(hkv)))
     # one kernel unless the block has more than two scoring rounds of chunk
@@ -469,7 +565,7 @@ def decode_line(cfg_id, batch, steps, warmup):
     traffic = measured_traffic(f"{base['name']}-decode-b{batch}", "route_attend_bf16") if fused else None
     del k, v, gs, cs, ws
     torch.cuda.empty_cache()
-    return {"value": steps * batch / wall, "unit": "generated tokens/s", "kernel_us_mean": us,
+    return {"value": steps * batch / wall, "unit": "generated tokens/s", "call_us": warm, "call_us_flushed": flushed,
             "ms_per_step": wall / steps * 1e3,
             "config": {"workload": f"{base['name']}-decode", "batch": batch, "history": pos,
                        "q_heads": base["hq"], "kv_heads": base["hkv"], "q_block": 1},
@@ -508,8 +604,8 @@ def backward_flops(cfg, n_sel, group_idx):
 def backward_line(cfg_id, steps, warmup):
     """hga_attend_backward over the active segment of workload cfg_id (its n_q
     queries; keys before q_start are detached history), after one forward
-    that provides the kept groups, output and LSE; timed with HIP events on
-    the launch stream around one call in Workload.SAMPLE_PERIOD."""
+    that provides the kept groups, output and LSE; wall clock over the calls,
+    and each call's duration from HIP event pairs on the launch stream."""
     import torch
 
     hga = __import__("hierarchical_sparse_attention_hga_amd")
@@ -529,24 +625,11 @@ def backward_line(cfg_id, steps, warmup):
     def one():
         hga.hga_attend_backward(w.c, w.q, w.q0, w.nq, w.L, w.k_full, w.v_t, w.gi, w.ns, w.out, w.lse, dout,
                                 dq, dk, dv, ws, wsb)
-    for _ in range(warmup):
-        one()
-    torch.cuda.synchronize()
-    per = Workload.SAMPLE_PERIOD
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
-        if i % per == 0:
-            evs[i][0].record()
-        one()
-        if i % per == 0:
-            evs[i][1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    us = float(np.mean([evs[i][0].elapsed_time(evs[i][1]) * 1e3 for i in range(0, steps, per)]))
+    wall, warm, flushed = timed_calls(one, steps, warmup)
+    us = warm["mean"]
     flops = backward_flops(cfg, w.ns.cpu().numpy(), w.gi.cpu().numpy())
     w.free()
-    return {"value": steps * cfg["n_q"] / wall, "unit": "query-tokens/s", "call_us_mean": us,
+    return {"value": steps * cfg["n_q"] / wall, "unit": "query-tokens/s", "call_us": warm, "call_us_flushed": flushed,
             "ms_per_step": wall / steps * 1e3,
             "config": {"workload": f"{cfg['name']}-backward", "n_q": cfg["n_q"], "history": w.q0},
             "roofline": {"kernel": "hga_attend_backward (bwd_dq_kernel, then bwd_dkv_kernel)", "bound": "mfma",
@@ -557,76 +640,68 @@ def backward_line(cfg_id, steps, warmup):
 
 
 def route_bytes(cfg, n_sel):
-    """HBM bytes of hga_route over every (block, KV head) of the workload: the
-    block's G x 64 query rows, the chunk summaries it scores (all candidates,
-    when the chunk stage selects), the group summaries of its kept chunks
-    (when the group stage selects), and its index rows."""
+    """Algorithmic HBM bytes of hga_route over every (block, KV head) of the
+    workload: each KV head's chunk summaries once (every chunk that some block
+    scores, when the chunk stage selects), the group summaries of each item's
+    kept chunks (when its group stage selects), the query rows once, and the
+    index rows written."""
     d, G, hkv, g = cfg["d"], cfg["hq"] // cfg["hkv"], cfg["hkv"], cfg["group"]
     esz = 2 if cfg["dtype"] == "bf16" else 4
     nb = cfg["n_q"] // 64
     q0 = cfg["L"] - cfg["n_q"]
     ns = n_sel.reshape(nb, hkv, 2)
-    rows = 0
+    scored = [set() for _ in range(hkv)]
+    gs_rows = 0
     for b in range(nb):
         ms = (q0 + 64 * b) // 64
         a = min(cfg["sink"] // 64, ms)
         bb = max(ms - cfg["local"] // 64, a)
         for h in range(hkv):
             nsc, nsg = int(ns[b, h, 0]), int(ns[b, h, 1])
-            rows += (bb - a if 0 < nsc < bb - a else 0) + (64 // g * nsc if 0 < nsg < 64 // g * nsc else 0)
-    return (nb * hkv * G * 64 * d * esz + 4.0 * d * rows
+            if 0 < nsc < bb - a:
+                scored[h].update(range(a, bb))
+            if 0 < nsg < 64 // g * nsc:
+                gs_rows += 64 // g * nsc
+    cs_rows = sum(len(x) for x in scored)
+    return (cfg["hq"] * cfg["n_q"] * d * esz + 4.0 * d * (cs_rows + gs_rows)
             + 4 * nb * hkv * (cfg["top_chunks"] + cfg["top_groups"] + 2))
 
 
-def stage_hbm(cfg_id, reps=20):
+def stage_hbm(cfg_id, samples=20):
     """Achieved HBM rates of the summary build (every chunk of the sequence)
-    and of the router alone: algorithmic bytes over the mean of reps
-    back-to-back calls (HIP events on the launch stream around all of them)."""
-    import torch
+    and of the router alone: algorithmic bytes over the mean duration of
+    `samples` calls, each between HIP events on the launch stream."""
     w = Workload(cfg_id)
     cfg, hga = w.cfg, w.hga
-
-    def mean_us(fn):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps * 1e3
-    sum_us = mean_us(lambda: hga.hga_build_summaries(w.c, w.k_full, w.L, w.gs, w.cs))
-    route_us = mean_us(lambda: hga.hga_route(w.c, w.q, w.q0, w.nq, w.L, w.cs, w.gs_t, w.ci, w.gi, w.ns))
+    for _ in range(3):
+        w.step()
+    sum_us = stats(event_us(lambda: hga.hga_build_summaries(w.c, w.k_full, w.L, w.gs, w.cs), samples))
+    route_us = stats(event_us(lambda: hga.hga_route(w.c, w.q, w.q0, w.nq, w.L, w.cs, w.gs_t, w.ci, w.gi, w.ns),
+                              samples))
     esz = 2 if cfg["dtype"] == "bf16" else 4
     d, hkv, L = cfg["d"], cfg["hkv"], cfg["L"]
     sum_bytes = hkv * L * d * esz + 4.0 * hkv * (L // cfg["group"] + L // 64) * d
     r_bytes = route_bytes(cfg, w.ns.cpu().numpy())
     w.free()
     out = {}
-    for name, byts, us in (("summaries_full_build", sum_bytes, sum_us), ("routing", r_bytes, route_us)):
-        out[name] = {"us": us, "algorithmic_bytes": byts, "achieved_GBps": byts / (us * 1e-6) / 1e9,
+    for name, byts, st in (("summaries_full_build", sum_bytes, sum_us), ("routing", r_bytes, route_us)):
+        us = st["mean"]
+        out[name] = {"us": st, "algorithmic_bytes": byts, "achieved_GBps": byts / (us * 1e-6) / 1e9,
                      "frac_of_hbm_peak": byts / (us * 1e-6) / PEAK_HBM}
+    out["routing"]["note"] = ("latency-bound: a chain of dependent memory round trips per item (block query, "
+                              "chunk scores, selection, group scores, selection)")
     return out
 
 
-def full_summary_us(cfg_id, reps=20):
-    """Mean time of hga_build_summaries over every chunk of workload cfg_id's
-    sequence (HIP events on the launch stream)."""
-    import torch
+def full_summary_us(cfg_id, samples=20):
+    """Duration statistics of hga_build_summaries over every chunk of
+    workload cfg_id's sequence (HIP events on the launch stream)."""
     w = Workload(cfg_id)
     for _ in range(3):
         w.hga.hga_build_summaries(w.c, w.k_full, w.L, w.gs, w.cs)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        w.hga.hga_build_summaries(w.c, w.k_full, w.L, w.gs, w.cs)
-    e1.record()
-    torch.cuda.synchronize()
+    st = stats(event_us(lambda: w.hga.hga_build_summaries(w.c, w.k_full, w.L, w.gs, w.cs), samples))
     w.free()
-    return e0.elapsed_time(e1) / reps * 1e3
+    return st
 
 
 def synth_config(cfg_id):
@@ -634,12 +709,35 @@ def synth_config(cfg_id):
     return synth.config(cfg_id)
 
 
-def measure(cfg_id, steps, warmup, split=0, fused=None):
+def measure(cfg_id, steps, warmup, split=0, fused=None, samples=None):
     w = Workload(cfg_id, split, fused)
-    wall, stage = w.run(steps, warmup)
-    r = Result(w, wall, stage)
+    wall, stages = w.run(steps, warmup, samples or max(steps, 20))
+    r = Result(w, wall, stages, steps)
     w.free()
     return r
+
+
+def host_link_rate(mib=256, samples=10):
+    """Achievable pinned host-to-device copy rate of the box (B/s): the
+    median of `samples` copies of `mib` MiB from pinned host memory."""
+    import torch
+    src = torch.empty(mib << 20, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(mib << 20, dtype=torch.uint8, device="cuda:0")
+    us = stats(event_us(lambda: dst.copy_(src, non_blocking=True), samples))
+    return (mib << 20) / (us["median"] * 1e-6)
+
+
+def host_tier_line(cfg_id, steps, warmup, link_rate, note):
+    r = measure(cfg_id, steps, warmup, split=synth_config(cfg_id)["tier_split"])
+    line = r.line()
+    t = r.warm["attend"]["mean"] * 1e-6
+    line["note"] = note
+    line["host_link"] = {"bytes_per_step": r.host_bytes, "attend_stage_GBps": r.host_bytes / t / 1e9,
+                         "frac_of_nominal_64GBps": r.host_bytes / t / PEAK_HOST_LINK,
+                         "measured_pinned_h2d_GBps": link_rate / 1e9,
+                         "note": "history bytes the step moves over the host link over the whole attention stage "
+                                 "(the copy, then the attention): a lower bound of the link's achieved rate"}
+    return line
 
 
 def main():
@@ -654,87 +752,80 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.backward:
-        print(json.dumps(backward_line(args.config, args.steps, args.warmup)), flush=True)
+        print(json.dumps(backward_line(args.config, args.steps, args.warmup), allow_nan=False), flush=True)
         return
     if args.decode_batch:
-        print(json.dumps(decode_line(args.config, args.decode_batch, args.steps, args.warmup)), flush=True)
+        print(json.dumps(decode_line(args.config, args.decode_batch, args.steps, args.warmup), allow_nan=False),
+              flush=True)
         return
     split = 0
     if args.host_tier:
-        import synth
-        split = synth.config(args.config)["tier_split"] or (synth.config(args.config)["L"] -
-                                                            synth.config(args.config)["n_q"])
+        split = synth_config(args.config)["tier_split"] or (synth_config(args.config)["L"] -
+                                                            synth_config(args.config)["n_q"])
     main_r = measure(args.config, args.steps, args.warmup, split=split)
     cfg = main_r.cfg
-    value = args.steps * cfg["n_q"] / main_r.wall
+    ml = main_r.line()
     line = {
-        "metric": METRIC, "value": value, "unit": "query-tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_r.wall / args.steps * 1e3,
+        "metric": METRIC, "value": ml["value"], "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ml["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg["dtype"],
         "data": "synthetic (seeded; Qwen3-shaped heads, rank-8 shared component, planted groups)",
         "config": {"workload": cfg["name"], "seq_len": cfg["L"], "n_q": cfg["n_q"], "q_heads": cfg["hq"],
                    "kv_heads": cfg["hkv"], "head_dim": cfg["d"], "top_chunks": cfg["top_chunks"],
                    "top_groups": cfg["top_groups"], "sink": cfg["sink"], "local": cfg["local"],
                    "kv_residency": "host-pinned history" if split else "hbm"},
-        "stages_us_mean": main_r.stages("mean"),
-        "stages_us_median": main_r.stages("median"),
-        "roofline": main_r.roofline(),
+        "value_flushed": ml["value_flushed"],
+        "stages_us": ml["stages_us"], "stages_us_flushed": ml["stages_us_flushed"],
+        "roofline": ml["roofline"], "roofline_flushed": ml["roofline_flushed"],
     }
     if split:
         line["host_link_bytes_per_step"] = main_r.host_bytes
     if not args.no_extra:
         extra = {}
-        # the rate with the summaries prebuilt (kept resident, as the pages do):
-        # query tokens over the routing + gather + attention stage times
-        rest = sum(main_r.mean[1:])
+        half = max(args.steps // 2, 10)
+        rest = sum(v["mean"] for k, v in main_r.warm.items() if k not in ("summaries", "step"))
         extra["summaries_prebuilt"] = {
             "value": cfg["n_q"] / (rest * 1e-6), "unit": "query-tokens/s",
             "note": "n_q / (mean routing + gather + attention stage time); summary build excluded"}
         if not split:
-            full_us = full_summary_us(args.config)
+            full = full_summary_us(args.config)
             extra["full_summary_rebuild"] = {
-                "value": cfg["n_q"] / ((full_us + rest) * 1e-6), "unit": "query-tokens/s",
-                "summaries_us": full_us,
+                "value": cfg["n_q"] / ((full["mean"] + rest) * 1e-6), "unit": "query-tokens/s",
+                "summaries_us": full,
                 "note": "the step with the summaries of every chunk of the sequence rebuilt (history included) "
                         "instead of only the chunks the step's positions close"}
-        half = max(args.steps // 2, 5)
         extra["stage_hbm"] = stage_hbm(args.config)
         if main_r.fused:
             sep = measure(args.config, half, args.warmup, fused=False)
+            sl = sep.line(with_traffic=False)
             extra["separate_calls"] = {
-                "value": half * sep.cfg["n_q"] / sep.wall, "unit": "query-tokens/s",
+                "value": sl["value"], "unit": "query-tokens/s", "stages_us": sl["stages_us"],
                 "note": "same step through hga_route then hga_attend; roofline of the attention kernel alone",
-                "stages_us_mean": sep.stages("mean"), "roofline": sep.roofline(with_traffic=False)}
+                "roofline": sl["roofline"]}
+        names = {0: "tiny_fp32_1k", 1: "qwen3_8b_4k", 2: "qwen3_8b_segment_16k", 3: "qwen3_30b_a3b_64k_hbm"}
+        for cid in (0, 1, 3):
+            if cid != args.config:
+                extra[names[cid]] = measure(cid, half, args.warmup).line()
+        link = host_link_rate()
+        extra["64k_host_tier_pcie_inclusive"] = host_tier_line(
+            3, max(half, 20), 2, link,
+            "history K/V and group summaries in pinned host memory; each history chunk any block needs crosses "
+            "the host link once per step into an HBM cache, then attention")
+        extra["128k_host_tier_pcie_inclusive"] = host_tier_line(
+            4, max(half, 20), 2, link,
+            "the 131,072-token long-evaluation layer (Qwen3-8B heads, top-64 chunks, top-512 groups, 64 planted "
+            "needle groups per head): history K/V and group summaries in pinned host memory, the final 2,048 "
+            "queries in HBM; each history chunk any block needs crosses the host link once per step")
         if args.config == 2:
             extra["16k_streamed_2048_segments"] = stream_line(max(args.steps // 6, 3), 2)
-        if args.config != 3:
-            r3 = measure(3, half, args.warmup)
-            extra["64k_hbm"] = {"value": half * r3.cfg["n_q"] / r3.wall, "unit": "query-tokens/s",
-                                "stages_us_mean": r3.stages("mean"), "roofline": r3.roofline()}
-            rh = measure(3, 24, 2, split=r3.cfg["tier_split"])
-            extra["64k_host_tier_pcie_inclusive"] = {
-                "value": 24 * rh.cfg["n_q"] / rh.wall, "unit": "query-tokens/s",
-                "note": "history K/V and group summaries in pinned host memory; each history chunk any block "
-                        "needs crosses the host link once per step into an HBM cache, then attention",
-                "host_link_bytes_per_step": rh.host_bytes,
-                "stages_us_mean": rh.stages("mean")}
-            r4 = measure(4, 24, 2, split=synth_config(4)["tier_split"])
-            extra["128k_host_tier_pcie_inclusive"] = {
-                "value": 24 * r4.cfg["n_q"] / r4.wall, "unit": "query-tokens/s",
-                "note": "the 131,072-token long-evaluation layer (Qwen3-8B heads, top-64 chunks, top-512 groups, "
-                        "64 planted needle groups per head): history K/V and group summaries in pinned host "
-                        "memory, the final 2,048 queries in HBM; each history chunk any block needs crosses "
-                        "the host link once per step",
-                "host_link_bytes_per_step": r4.host_bytes,
-                "stages_us_mean": r4.stages("mean")}
-        extra["backward_16k_segment"] = backward_line(2, 80, 5)
-        extra["decode_16k_batch64"] = decode_line(2, 64, 80, 5)
-        extra["decode_16k_single_sequence"] = decode_line(2, 1, 80, 5)
-        extra["decode_64k_batch32"] = decode_line(3, 32, 80, 5)
+        extra["backward_16k_segment"] = backward_line(2, half, 3)
+        extra["decode_16k_batch64"] = decode_line(2, 64, half, 3)
+        extra["decode_16k_single_sequence"] = decode_line(2, 1, half, 3)
+        extra["decode_64k_batch32"] = decode_line(3, 32, half, 3)
         line["also"] = extra
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args.config)
-    print(json.dumps(line), flush=True)
+    print(json.dumps(line, allow_nan=False), flush=True)
 
 
 if __name__ == "__main__":
