@@ -18,11 +18,18 @@ HGA_OK, HGA_ERR_INVALID_ARGUMENT, HGA_ERR_UNSUPPORTED, HGA_ERR_WORKSPACE, HGA_ER
 HGA_F32, HGA_BF16 = 0, 1
 HGA_SUMMARY_MEAN = 0
 HGA_WS_ROUTE, HGA_WS_ATTEND, HGA_WS_ATTEND_TIERED, HGA_WS_BACKWARD, HGA_WS_BACKWARD_TIERED = 0, 1, 2, 3, 4
+HGA_WS_ATTEND_CACHED = 5
+HGA_TC_KV, HGA_TC_GS = 0, 1
+# counters at the start of a tier cache's memory (int64 each)
+TC_COUNTERS = ("calls", "kv_requests", "kv_misses", "kv_bytes", "kv_evictions", "gs_requests", "gs_misses",
+               "gs_bytes", "gs_evictions")
+HGA_TC_COUNTERS = 16
 
 # Every exported entry point of include/hga.h.
 EXPORTS = ("hga_workspace_size", "hga_build_summaries", "hga_build_summaries_range", "hga_route", "hga_attend",
-           "hga_route_attend", "hga_route_attend_noalloc", "hga_stream_forward", "hga_attend_backward", "hga_status_string", "hga_last_error",
-           "hga_version")
+           "hga_route_attend", "hga_route_attend_noalloc", "hga_tier_cache_size", "hga_tier_cache_min_slots",
+           "hga_tier_cache_init", "hga_route_attend_cached", "hga_stream_forward", "hga_attend_backward",
+           "hga_status_string", "hga_last_error", "hga_version")
 
 
 class HgaError(RuntimeError):
@@ -41,6 +48,11 @@ class hga_config(C.Structure):
 
 class hga_tiered(C.Structure):
     _fields_ = [("host", C.c_void_p), ("dev", C.c_void_p), ("split", C.c_int64)]
+
+
+class hga_tier_cache(C.Structure):
+    _fields_ = [("mem", C.c_void_p), ("bytes", C.c_size_t), ("split", C.c_int64), ("kv_slots", C.c_int32),
+                ("gs_slots", C.c_int32)]
 
 
 _lib = None
@@ -62,11 +74,20 @@ def load():
         lib.hga_attend.argtypes = [cfgp, P, I64, I64, I64, tierp, tierp, P, P, P, P, P, SZ, P]
         lib.hga_route_attend.argtypes = [cfgp, P, I64, I64, I64, P, tierp, tierp, tierp, P, P, P, P, P, P, SZ, P]
         lib.hga_route_attend_noalloc.argtypes = [cfgp, P, I64, I64, I64, P, tierp, tierp, tierp, P, P, P, P, P, P]
+        cachep = C.POINTER(hga_tier_cache)
+        lib.hga_tier_cache_size.argtypes = [cfgp, I64, I32, I32]
+        lib.hga_tier_cache_size.restype = SZ
+        lib.hga_tier_cache_min_slots.argtypes = [cfgp, I64, I64, I32]
+        lib.hga_tier_cache_min_slots.restype = I32
+        lib.hga_tier_cache_init.argtypes = [cfgp, cachep, P]
+        lib.hga_route_attend_cached.argtypes = [cfgp, P, I64, I64, I64, P, tierp, tierp, tierp, cachep, P, P, P, P,
+                                                P, P, SZ, P]
         lib.hga_build_summaries_range.argtypes = [cfgp, P, I64, I64, I64, P, P, P]
         lib.hga_stream_forward.argtypes = [cfgp, P, P, P, I64, I64, P, P, P, P, P, P, P, P]
         lib.hga_attend_backward.argtypes = [cfgp, P, I64, I64, I64, tierp, tierp, P, P, P, P, P, P, P, P, P, SZ, P]
         for f in ("hga_build_summaries", "hga_build_summaries_range", "hga_route", "hga_attend",
-                  "hga_route_attend", "hga_route_attend_noalloc", "hga_stream_forward", "hga_attend_backward"):
+                  "hga_route_attend", "hga_route_attend_noalloc", "hga_tier_cache_init", "hga_route_attend_cached",
+                  "hga_stream_forward", "hga_attend_backward"):
             getattr(lib, f).restype = C.c_int
         lib.hga_status_string.argtypes = [C.c_int]
         lib.hga_status_string.restype = C.c_char_p
@@ -162,6 +183,33 @@ def hga_route_attend_noalloc(cfg, q, q_start, n_q, seq_len, chunk_sum, group_sum
     _check(load().hga_route_attend_noalloc(C.byref(cfg), _ptr(q), q_start, n_q, seq_len, _ptr(chunk_sum),
                                            C.byref(gt), C.byref(kt), C.byref(vt), _ptr(chunk_idx), _ptr(group_idx),
                                            _ptr(n_sel), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def hga_tier_cache_size(cfg, split, kv_slots, gs_slots):
+    return int(load().hga_tier_cache_size(C.byref(cfg), split, kv_slots, gs_slots))
+
+
+def hga_tier_cache_min_slots(cfg, seq_len, n_q, which):
+    return int(load().hga_tier_cache_min_slots(C.byref(cfg), seq_len, n_q, which))
+
+
+def tier_cache(mem, nbytes, split, kv_slots, gs_slots):
+    """A hga_tier_cache over device memory `mem` (a tensor or an address)."""
+    return hga_tier_cache(_ptr(mem), int(nbytes), int(split), int(kv_slots), int(gs_slots))
+
+
+def hga_tier_cache_init(cfg, cache, stream=None):
+    _check(load().hga_tier_cache_init(C.byref(cfg), C.byref(cache), _stream(stream)))
+
+
+def hga_route_attend_cached(cfg, q, q_start, n_q, seq_len, chunk_sum, group_sum, k, v, cache, chunk_idx, group_idx,
+                            n_sel, out, lse=None, workspace=None, ws_bytes=0, stream=None):
+    gt, kt, vt = _tier(group_sum), _tier(k), _tier(v)
+    _check(load().hga_route_attend_cached(C.byref(cfg), _ptr(q), q_start, n_q, seq_len, _ptr(chunk_sum), C.byref(gt),
+                                          C.byref(kt), C.byref(vt), None if cache is None else C.byref(cache),
+                                          _ptr(chunk_idx), _ptr(group_idx),
+                                          _ptr(n_sel), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                                          _stream(stream)))
 
 
 def hga_build_summaries_range(cfg, k, seq_len, chunk_begin, chunk_end, group_sum, chunk_sum, stream=None):

@@ -174,9 +174,108 @@ hga_status scratch_of_current_device(void** ptr) {
   return HGA_OK;
 }
 
+// Most distinct history chunks (below split) one call of this shape can need
+// per KV head, for K/V (the sink, local and kept chunks of every block) or
+// for group summaries (the kept chunks).
+int64_t cache_need_bound(const hga::Shape& s, int64_t split, int which) {
+  const int64_t nch = split / hga::kChunk;
+  const int64_t per = which == HGA_TC_KV ? (int64_t)s.kc + s.sink_chunks + s.local_chunks : (int64_t)s.kc;
+  const int64_t b = s.nb * per;
+  return b < nch ? b : nch;
+}
+
+// Whether the group stage of some block may choose (read group summaries).
+bool group_stage_chooses(const hga::Shape& s) { return s.kg > 0 && (int64_t)s.kg < (int64_t)s.kc * (hga::kChunk / s.g); }
+
+hga_status check_cache(const hga::Shape& s, const hga_tier_cache* c) {
+  if (!c) return fail(HGA_ERR_INVALID_ARGUMENT, "cache is NULL");
+  if (!c->mem || ((uintptr_t)c->mem & 255))
+    return fail(HGA_ERR_INVALID_ARGUMENT, "cache->mem must be non-NULL and 256-byte aligned");
+  if (c->split <= 0 || c->split % hga::kChunk)
+    return fail(HGA_ERR_INVALID_ARGUMENT, "cache->split must be a positive multiple of 64");
+  if (c->split / hga::kChunk > hga::kMaxCand)
+    return fail(HGA_ERR_UNSUPPORTED, "cache->split above %lld tokens", (long long)hga::kMaxCand * hga::kChunk);
+  if (c->kv_slots < 1 || c->kv_slots > hga::kMaxCand || c->gs_slots < 0 || c->gs_slots > hga::kMaxCand)
+    return fail(HGA_ERR_INVALID_ARGUMENT, "cache slots must be in [1, %d] (K/V) and [0, %d] (summaries)",
+                hga::kMaxCand, hga::kMaxCand);
+  hga::TierCacheLayout L;
+  const size_t need = hga::tier_cache_layout(s, c->split, c->kv_slots, c->gs_slots, &L);
+  if (c->bytes < need) return fail(HGA_ERR_WORKSPACE, "cache of %zu bytes needed, %zu given", need, c->bytes);
+  return HGA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t hga_tier_cache_size(const hga_config* cfg, int64_t split, int32_t kv_slots, int32_t gs_slots) {
+  hga::Shape s;
+  if (make_shape(cfg, split, 0, 0, &s) != HGA_OK || split <= 0 || split / hga::kChunk > hga::kMaxCand ||
+      kv_slots < 1 || kv_slots > hga::kMaxCand || gs_slots < 0 || gs_slots > hga::kMaxCand)
+    return (size_t)-1;
+  hga::TierCacheLayout L;
+  return hga::tier_cache_layout(s, split, kv_slots, gs_slots, &L);
+}
+
+int32_t hga_tier_cache_min_slots(const hga_config* cfg, int64_t seq_len, int64_t n_q, int32_t which) {
+  hga::Shape s;
+  if (make_shape(cfg, seq_len, seq_len - n_q, n_q, &s) != HGA_OK || (which != HGA_TC_KV && which != HGA_TC_GS))
+    return -1;
+  if (which == HGA_TC_GS && !group_stage_chooses(s)) return 0;
+  return (int32_t)cache_need_bound(s, seq_len - n_q, which);
+}
+
+hga_status hga_tier_cache_init(const hga_config* cfg, const hga_tier_cache* cache, void* stream) {
+  if (!cache) return fail(HGA_ERR_INVALID_ARGUMENT, "cache is NULL");
+  if (cache->split <= 0 || cache->split % hga::kChunk)
+    return fail(HGA_ERR_INVALID_ARGUMENT, "cache->split must be a positive multiple of 64");
+  hga::Shape s;
+  hga_status st = make_shape(cfg, cache->split, 0, 0, &s);
+  if (st != HGA_OK) return st;
+  if ((st = check_cache(s, cache)) != HGA_OK) return st;
+  return device_status(hga::tier_cache_init(s, cache->split, cache->kv_slots, cache->gs_slots, cache->mem,
+                                            (hipStream_t)stream),
+                       "hga_tier_cache_init launch");
+}
+
+hga_status hga_route_attend_cached(const hga_config* cfg, const void* q, int64_t q_start, int64_t n_q,
+                                   int64_t seq_len, const float* chunk_sum, const hga_tiered* group_sum,
+                                   const hga_tiered* k, const hga_tiered* v, const hga_tier_cache* cache,
+                                   int32_t* chunk_idx, int32_t* group_idx, int32_t* n_sel, void* out, float* lse,
+                                   void* workspace, size_t ws_bytes, void* stream) {
+  hga::Shape s;
+  hga_status st = make_shape(cfg, seq_len, q_start, n_q, &s);
+  if (st != HGA_OK) return st;
+  if (n_q == 0) return ok();
+  if (!q || !chunk_sum || !n_sel || !out || (s.kc > 0 && !chunk_idx) || (s.kg > 0 && !group_idx))
+    return fail(HGA_ERR_INVALID_ARGUMENT,
+                "q, chunk_sum, n_sel, out, chunk_idx and group_idx must be non-NULL");
+  if ((st = check_aligned("q, chunk_sum, out and workspace", {q, chunk_sum, out, workspace})) != HGA_OK) return st;
+  if ((st = check_tier(group_sum, "group_sum", seq_len, q_start)) != HGA_OK) return st;
+  if ((st = check_tier(k, "k", seq_len, q_start)) != HGA_OK) return st;
+  if ((st = check_tier(v, "v", seq_len, q_start)) != HGA_OK) return st;
+  if ((st = check_cache(s, cache)) != HGA_OK) return st;
+  if (k->split != cache->split || v->split != cache->split || group_sum->split != cache->split)
+    return fail(HGA_ERR_INVALID_ARGUMENT, "group_sum, k and v must be split at cache->split");
+  if (s.sink_chunks + s.local_chunks > hga::kMaxFixedTiered)
+    return fail(HGA_ERR_UNSUPPORTED, "with a host tier, sink and local windows may span at most %d chunks",
+                hga::kMaxFixedTiered);
+  if (cache->kv_slots < cache_need_bound(s, cache->split, HGA_TC_KV) ||
+      (group_stage_chooses(s) && cache->gs_slots < cache_need_bound(s, cache->split, HGA_TC_GS)))
+    return fail(HGA_ERR_UNSUPPORTED, "the cache has too few slots for calls of %lld queries (K/V %lld, summaries %lld)",
+                (long long)n_q, (long long)cache_need_bound(s, cache->split, HGA_TC_KV),
+                (long long)(group_stage_chooses(s) ? cache_need_bound(s, cache->split, HGA_TC_GS) : 0));
+  hga::TierCallLayout W;
+  const size_t need = hga::tier_call_layout(s, cache->split, &W);
+  if (!workspace || ws_bytes < need)
+    return fail(HGA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : (size_t)0);
+  const hga::KVSrc kv{k->host, k->dev, v->host, v->dev, k->split};
+  return device_status(hga::launch_route_attend_cached(s, q, chunk_sum, static_cast<const float*>(group_sum->host),
+                                                       static_cast<const float*>(group_sum->dev), group_sum->split, kv,
+                                                       cache->kv_slots, cache->gs_slots, cache->mem, chunk_idx,
+                                                       group_idx, n_sel, out, lse, workspace, (hipStream_t)stream),
+                       "hga_route_attend_cached launch");
+}
 
 size_t hga_workspace_size(const hga_config* cfg, int64_t seq_len, int64_t n_q, int32_t which) {
   hga::Shape s;
@@ -188,6 +287,10 @@ size_t hga_workspace_size(const hga_config* cfg, int64_t seq_len, int64_t n_q, i
     case HGA_WS_BACKWARD: return hga::backward_workspace_bytes(s);
     case HGA_WS_BACKWARD_TIERED:
       return hga::backward_workspace_bytes(s) + hga::tier_cache_bytes(s, seq_len - n_q);
+    case HGA_WS_ATTEND_CACHED: {
+      hga::TierCallLayout W;
+      return hga::tier_call_layout(s, seq_len - n_q, &W);
+    }
     default: fail(HGA_ERR_INVALID_ARGUMENT, "unknown workspace kind %d", which); return (size_t)-1;
   }
 }
@@ -412,6 +515,6 @@ const char* hga_status_string(hga_status status) {
 
 const char* hga_last_error(void) { return g_err; }
 
-int32_t hga_version(void) { return 107; }
+int32_t hga_version(void) { return 108; }
 
 }  // extern "C"

@@ -383,7 +383,7 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(AttnArgs A) {
   bf16x8 qf[D / 16];
   load_q_operands<D>(A, b, h, z, qf);
   const Plan P = make_plan(A.s, b, h, A.gidx, A.nsel, sm.runs, sm.scan, kMaxRoutedAttn);
-  if (kTiered) translate_plan(A.kv.split, A.nch, A.slot, h, P, sm.runs, sm.runs + kMaxRoutedAttn);
+  if (kTiered) translate_plan(A.kv.split, A.nch, A.nslots, A.slot, h, P, sm.runs, sm.runs + kMaxRoutedAttn);
   attend_bf16_body<D, kTiered>(A, b, h, z, P, sm, pre, qf, 0, P.ntiles, nullptr);
 }
 
@@ -522,7 +522,7 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttnArgs A) {
   int b, h, z;
   item_of_block(S, A.wg_per_item, &b, &h, &z);
   const Plan P = make_plan(S, b, h, A.gidx, A.nsel, sRuns, sScan, kMaxRouted);
-  if (kTiered) translate_plan(A.kv.split, A.nch, A.slot, h, P, sRuns, sRuns + kMaxRouted);
+  if (kTiered) translate_plan(A.kv.split, A.nch, A.nslots, A.slot, h, P, sRuns, sRuns + kMaxRouted);
   const int64_t per_head = kTiered ? S.kvs - A.kv.split : S.kvs;
   const float* kdev = static_cast<const float*>(A.kv.k_dev) + (int64_t)h * per_head * D;
   const float* vdev = static_cast<const float*>(A.kv.v_dev) + (int64_t)h * per_head * D;
@@ -743,9 +743,10 @@ hipError_t prepare_tier_cache(const Shape& s, const KVSrc& kv, const int32_t* gr
   char* cache = static_cast<char*>(workspace) + (((2 * (size_t)s.hkv * nch * sizeof(int32_t)) + 255) & ~(size_t)255);
   a.slot = slot;
   a.nch = nch;
+  a.nslots = nch;
   a.k_cache = cache;
   a.v_cache = cache + (size_t)s.hkv * nch * kChunk * s.d * esz;
-  *tc = TierCache{slot, nch, a.k_cache, a.v_cache};
+  *tc = TierCache{slot, nch, nch, a.k_cache, a.v_cache};
   const int64_t nflags = (int64_t)s.hkv * nch;
   fill_zero_kernel<<<dim3((unsigned)((nflags + 255) / 256)), dim3(256), 0, st>>>(need, nflags);
   mark_kernel<<<dim3((unsigned)items), dim3(256), 0, st>>>(a, need);
@@ -784,7 +785,7 @@ size_t attend_split_bytes(const Shape& s) {
 
 hipError_t launch_attend(const Shape& s, const void* q, const KVSrc& kv, const int32_t* group_idx,
                          const int32_t* n_sel, void* out, float* lse, void* workspace, size_t ws_bytes,
-                         hipStream_t st) {
+                         hipStream_t st, const TierCache* cached) {
   const int64_t items = s.nb * s.hkv;
   if (items == 0) return hipSuccess;
   AttnArgs a{};
@@ -806,10 +807,15 @@ hipError_t launch_attend(const Shape& s, const void* q, const KVSrc& kv, const i
   }
   if (tiered) {
     TierCache tc;
-    const hipError_t e = prepare_tier_cache(s, kv, group_idx, n_sel, workspace, &tc, st);
-    if (e != hipSuccess) return e;
+    if (cached) {
+      tc = *cached;
+    } else {
+      const hipError_t e = prepare_tier_cache(s, kv, group_idx, n_sel, workspace, &tc, st);
+      if (e != hipSuccess) return e;
+    }
     a.slot = tc.slot;
     a.nch = tc.nch;
+    a.nslots = tc.nslots;
     a.k_cache = tc.k_cache;
     a.v_cache = tc.v_cache;
   }

@@ -32,6 +32,7 @@ struct AttnArgs {
   const void* v_cache;
   const int32_t* slot;     // [Hkv][nch]: cache slot of history chunk m of head h (-1: not needed)
   int nch;                 // chunks in the host tier (split / 64)
+  int nslots;              // cache slots per KV head (the cache is [Hkv][nslots][64][d])
   const int32_t* gidx;
   const int32_t* nsel;
   void* out;
@@ -167,17 +168,17 @@ __device__ inline int tile_limit(const Plan& P, int g, int t) {
 // Host-tier path: rewrite the kept groups' first tokens in runs[] and the
 // fixed chunks' first tokens into encoded source rows (fixsrc[t] for fixed
 // tile t), given the cache slots (slot[h nch + m], -1: not cached) of the
-// nch history chunks below split. Every history chunk used here was marked
-// and given a slot.
-__device__ void translate_plan(int64_t split, int nch, const int32_t* slot, int h, const Plan& P, int* runs,
-                               int* fixsrc) {
+// nch history chunks below split, in a cache of nslots chunk slots per KV
+// head. Every history chunk used here was given a slot.
+__device__ void translate_plan(int64_t split, int nch, int nslots, const int32_t* slot, int h, const Plan& P,
+                               int* runs, int* fixsrc) {
   auto enc = [&](int64_t tok) -> int {
     if (tok < split) {
       const int64_t m = tok / kChunk;
       const int sl = slot[(int64_t)h * nch + m];
       // every chunk used here was marked; an unmarked one would read device
       // row 0 rather than outside the cache
-      return sl >= 0 ? kCacheFlag | (int)(((int64_t)h * nch + sl) * kChunk + tok % kChunk) : 0;
+      return sl >= 0 ? kCacheFlag | (int)(((int64_t)h * nslots + sl) * kChunk + tok % kChunk) : 0;
     }
     return (int)(tok - split);
   };

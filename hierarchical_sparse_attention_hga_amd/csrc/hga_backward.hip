@@ -145,7 +145,7 @@ __global__ __launch_bounds__(kAttnThreads) void bwd_dq_kernel(BwdArgs A) {
   if (z == 0) write_chunk_masks(A, b, h, P, sm.runs);
   if (kTiered) {   // rows of the history come from the host-tier cache
     __syncthreads();   // the masks above read the token runs
-    translate_plan(A.kv.split, A.tc.nch, A.tc.slot, h, P, sm.runs, sm.runs + kMaxRoutedAttn);
+    translate_plan(A.kv.split, A.tc.nch, A.tc.nslots, A.tc.slot, h, P, sm.runs, sm.runs + kMaxRoutedAttn);
   }
   const int nt = P.ntiles;
 
@@ -668,7 +668,7 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(BwdArgs A) {
   if (z == 0) write_chunk_masks(A, b, h, P, sRuns);
   if (kTiered) {
     __syncthreads();
-    translate_plan(A.kv.split, A.tc.nch, A.tc.slot, h, P, sRuns, sRuns + kMaxRouted);
+    translate_plan(A.kv.split, A.tc.nch, A.tc.nslots, A.tc.slot, h, P, sRuns, sRuns + kMaxRouted);
   }
   const int64_t per_head = S.kvs - A.kv.split;
   const float* kdev = static_cast<const float*>(A.kv.k_dev) + (int64_t)h * per_head * D;

@@ -76,17 +76,21 @@ size_t tier_cache_bytes(const Shape& s, int64_t split);
 // KV head (-1: not needed) and the HBM copies of the needed chunks' K and V,
 // in the workspace (tier_cache_bytes). The copy runs on st.
 struct TierCache {
-  const int32_t* slot;
+  const int32_t* slot;   // [Hkv][nch]: slot of history chunk m (-1: none)
   int nch;
+  int nslots;            // slots per KV head of k_cache / v_cache ([Hkv][nslots][64][d])
   const void* k_cache;
   const void* v_cache;
 };
 hipError_t prepare_tier_cache(const Shape& s, const KVSrc& kv, const int32_t* group_idx, const int32_t* n_sel,
                               void* workspace, TierCache* tc, hipStream_t st);
 
+// With `cached` (K/V split > 0) the history rows are read from that cache,
+// whose slots the caller has filled, instead of a per-call cache built in the
+// workspace.
 hipError_t launch_attend(const Shape& s, const void* q, const KVSrc& kv, const int32_t* group_idx,
                          const int32_t* n_sel, void* out, float* lse, void* workspace, size_t ws_bytes,
-                         hipStream_t st);
+                         hipStream_t st, const TierCache* cached = nullptr);
 // Ranges per item when launch_attend spreads each item's tiles over several
 // workgroups (1: one workgroup per item), and the workspace that takes.
 int attend_split_count(const Shape& s);
@@ -97,6 +101,46 @@ bool fused_route_attend_supported(const Shape& s, int64_t kv_split);
 hipError_t launch_route_attend(const Shape& s, const void* q, const float* cs, const float* gs_host,
                                const float* gs_dev, int64_t gs_split, const KVSrc& kv, int32_t* chunk_idx,
                                int32_t* group_idx, int32_t* n_sel, void* out, float* lse, hipStream_t st);
+
+// ---------------------------------------------------------------- persistent host-tier cache
+// Counters at the start of the cache memory (int64 each).
+enum {
+  kTcCalls = 0,         // calls made through the cache (each call's stamp)
+  kTcKvRequests,        // history groups the calls' query blocks attended (summed over blocks and KV heads)
+  kTcKvMisses,          // of those, groups copied from host memory (not resident at the call)
+  kTcKvBytes,           // K and V bytes copied from host memory
+  kTcKvEvictions,       // chunks whose K/V slots were given to other chunks
+  kTcGsRequests,        // kept history chunks whose group summaries the group stage scored
+  kTcGsMisses,          // of those, chunks whose summaries were copied from host memory
+  kTcGsBytes,           // group-summary bytes copied
+  kTcGsEvictions,       // chunks whose summary slots were given to other chunks
+  kTierCounters = 16
+};
+
+// Byte offsets of the parts of a cache (see hga_tier_cache.hip).
+struct TierCacheLayout {
+  int nch, S, Sg;
+  size_t slot, owner, used, valid, hand;        // K/V slot tables
+  size_t gslot, gowner, gused, gvalid, ghand;   // group-summary slot tables
+  size_t k, v, gs;                              // [Hkv][S][64][d], [Hkv][S][64][d], [Hkv][Sg][c/g][d]
+  size_t total;
+};
+// Byte offsets of one call's workspace of the cached path.
+struct TierCallLayout {
+  size_t need, gneed, list, count, glist, gcount, qbar, total;
+};
+// A chunk whose groups (mask) are copied into a slot.
+struct CopyEntry {
+  int32_t m, slot;
+  uint64_t mask;
+};
+size_t tier_cache_layout(const Shape& s, int64_t split, int kv_slots, int gs_slots, TierCacheLayout* L);
+size_t tier_call_layout(const Shape& s, int64_t split, TierCallLayout* W);
+hipError_t tier_cache_init(const Shape& s, int64_t split, int kv_slots, int gs_slots, void* mem, hipStream_t st);
+hipError_t launch_route_attend_cached(const Shape& s, const void* q, const float* cs, const float* gs_host,
+                                      const float* gs_dev, int64_t gs_split, const KVSrc& kv, int kv_slots,
+                                      int gs_slots, void* cache_mem, int32_t* chunk_idx, int32_t* group_idx,
+                                      int32_t* n_sel, void* out, float* lse, void* workspace, hipStream_t st);
 
 // Backward of the attention (bfloat16): workspace bytes (without the
 // host-tier cache, which follows them when kv.split > 0), and the launch of

@@ -53,9 +53,13 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
 hipError_t launch_route(const Shape& s, const void* q, const float* cs, const float* gs_host,
                         const float* gs_dev, int64_t split, int32_t* chunk_idx, int32_t* group_idx,
                         int32_t* n_sel, hipStream_t st) {
+  return launch_route_args(RouteArgs{q, cs, gs_host, gs_dev, split, chunk_idx, group_idx, n_sel, s}, st);
+}
+
+hipError_t launch_route_args(const RouteArgs& a, hipStream_t st) {
+  const Shape& s = a.s;
   const int64_t items = s.nb * s.hkv;
   if (items == 0) return hipSuccess;
-  RouteArgs a{q, cs, gs_host, gs_dev, split, chunk_idx, group_idx, n_sel, s};
   if (s.dtype == HGA_BF16)
     route_kernel<uint16_t><<<dim3((unsigned)items), dim3(kThreads), 0, st>>>(a);
   else

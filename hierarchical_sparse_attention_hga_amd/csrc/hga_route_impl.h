@@ -266,7 +266,21 @@ struct RouteArgs {
   int32_t* group_idx;
   int32_t* n_sel;
   Shape s;
+  double* qbar_out;      // if set, each item's block query is stored ([nb][Hkv][d])
+  bool chunks_only;      // stop after the chunk stage (the group stage runs later)
 };
+
+template <bool kPipelined, typename GroupEmit, typename RowFn>
+__device__ int group_stage(const RouteArgs& a, int b, int h, RouteSmem& sm, int nsc, bool write_out,
+                           GroupEmit emit, RowFn gs_row);
+
+}  // namespace route
+
+// The router kernel over every item with the given arguments (with
+// chunks_only, the chunk stage only; with qbar_out, the block queries kept).
+hipError_t launch_route_args(const route::RouteArgs& a, hipStream_t st);
+
+namespace route {
 
 // Route item (query block b, KV head h) with all kThreads threads of the
 // workgroup. emit(rank, group) is called once per kept group (ranks 0..n-1,
@@ -348,6 +362,8 @@ __device__ int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm, bool 
   }
   after_query();
 
+  if (a.qbar_out && write_out && tid < d)
+    a.qbar_out[((int64_t)b * S.hkv + h) * d + tid] = sm.qbar[tid];
   const int64_t orow = (int64_t)b * S.hkv + h;
   // ---- 2-3. chunk stage
   if (chunk_select) {
@@ -366,20 +382,39 @@ __device__ int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm, bool 
   if (write_out)
     for (int i = tid; i < S.kc; i += kThreads) a.chunk_idx[orow * S.kc + i] = i < nsc ? sm.chunks[i] : -1;
 
+  if (write_out && tid == 0) a.n_sel[orow * 2 + 0] = nsc;
   // ---- 4. group stage over the groups of the kept chunks (ascending order)
+  if (a.chunks_only) return 0;
+  const int64_t gsplit = a.split / S.g;          // groups held in host memory
+  const int64_t ngl = S.kvs / S.g;
+  return group_stage<kPipelined>(a, b, h, sm, nsc, write_out, emit, [&](int, int64_t j) -> const float* {
+    return j < gsplit ? a.gs_host + ((int64_t)h * gsplit + j) * d
+                      : a.gs_dev + ((int64_t)h * (ngl - gsplit) + (j - gsplit)) * d;
+  });
+}
+
+// Group stage of item (b, h) given its nsc kept chunks (ascending, in
+// sm.chunks) and its block query (sm.qbar), with all kThreads threads:
+// score the groups of the kept chunks, keep the top_groups (ties to the
+// lower group index), emit them ascending (see route_item), and with
+// write_out write the -1 padding and the kept count. gs_row(c, j) gives the
+// d float32 values of the summary of group j, candidate c (group c % (c/g)
+// of kept chunk c / (c/g)). Returns the number kept.
+template <bool kPipelined, typename GroupEmit, typename RowFn>
+__device__ int group_stage(const RouteArgs& a, int b, int h, RouteSmem& sm, int nsc, bool write_out,
+                           GroupEmit emit, RowFn gs_row) {
+  const Shape& S = a.s;
+  const int d = S.d;
+  const int gpc = S.c / S.g;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int64_t orow = (int64_t)b * S.hkv + h;
   const int ngc = nsc * gpc;
   const int nsg = ngc < S.kg ? ngc : S.kg;
   int32_t* gout = a.group_idx + orow * S.kg;   // written only with write_out
   const int* kept_chunks = sm.chunks;
   auto group_of = [kept_chunks, gpc](int c) { return kept_chunks[c / gpc] * gpc + c % gpc; };
   if (nsg > 0 && nsg < ngc) {
-    const int64_t gsplit = a.split / S.g;          // groups held in host memory
-    const int64_t ngl = S.kvs / S.g;
-    auto group_row = [&](int c) -> const float* {
-      const int64_t j = group_of(c);
-      return j < gsplit ? a.gs_host + ((int64_t)h * gsplit + j) * d
-                        : a.gs_dev + ((int64_t)h * (ngl - gsplit) + (j - gsplit)) * d;
-    };
+    auto group_row = [&](int c) -> const float* { return gs_row(c, (int64_t)group_of(c)); };
     ScoreRound g0;
     load_round(0, d, ngc, group_row, g0);
     score_rows<kPipelined>(sm.qbar, d, ngc, group_row, sm.key, g0, 0);
@@ -390,10 +425,7 @@ __device__ int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm, bool 
   }
   if (write_out) {
     for (int i = nsg + tid; i < S.kg; i += kThreads) gout[i] = -1;
-    if (tid == 0) {
-      a.n_sel[orow * 2 + 0] = nsc;
-      a.n_sel[orow * 2 + 1] = nsg;
-    }
+    if (tid == 0) a.n_sel[orow * 2 + 1] = nsg;
   }
   return nsg;
 }

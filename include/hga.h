@@ -108,7 +108,8 @@ typedef struct {
 } hga_tiered;
 
 enum {
-  HGA_WS_ROUTE = 0, HGA_WS_ATTEND = 1, HGA_WS_ATTEND_TIERED = 2, HGA_WS_BACKWARD = 3, HGA_WS_BACKWARD_TIERED = 4
+  HGA_WS_ROUTE = 0, HGA_WS_ATTEND = 1, HGA_WS_ATTEND_TIERED = 2, HGA_WS_BACKWARD = 3, HGA_WS_BACKWARD_TIERED = 4,
+  HGA_WS_ATTEND_CACHED = 5
 };
 
 /* Bytes of device workspace that hga_route (which = HGA_WS_ROUTE) or
@@ -128,6 +129,8 @@ enum {
  * (the attention copies each history chunk any query block needs into it once
  * per call). HGA_WS_BACKWARD is the workspace of hga_attend_backward with K/V
  * on the device, HGA_WS_BACKWARD_TIERED the same plus that cache (any split).
+ * HGA_WS_ATTEND_CACHED is the per-call workspace of hga_route_attend_cached
+ * for a host tier of seq_len - n_q tokens or fewer.
  * Returns 0 when no workspace is needed, and (size_t)-1 when the config or
  * sizes are invalid. */
 size_t hga_workspace_size(const hga_config* cfg, int64_t seq_len, int64_t n_q, int32_t which);
@@ -259,6 +262,95 @@ hga_status hga_route_attend_noalloc(const hga_config* cfg, const void* q, int64_
                                     int64_t seq_len, const float* chunk_sum, const hga_tiered* group_sum,
                                     const hga_tiered* k, const hga_tiered* v, int32_t* chunk_idx, int32_t* group_idx,
                                     int32_t* n_sel, void* out, float* lse, void* stream);
+
+/* Persistent cache in device memory of a host tier (the pages' VRAM cache:
+ * "Long-Context Fine-Tuning with Limited VRAM", section 2.1, "Group
+ * selection": group summaries are kept in a larger VRAM cache and missing
+ * ones are fetched from host memory; "Exact-token attention": only the exact
+ * token K/V of the selected groups is loaded; section 4.5, table 8: the cache
+ * hit rate). It lives across calls: a call copies from host memory only what
+ * its query blocks need and the cache does not hold. The caller owns the
+ * memory; the library keeps no state of its own.
+ *   mem        device memory of hga_tier_cache_size(...) bytes, 256-byte
+ *              aligned. Its first HGA_TC_COUNTERS int64 are the counters
+ *              below (read them with a device-to-host copy).
+ *   split      the host tier it caches: tokens [0, split) of K, V and the
+ *              group summaries, in the hga_tiered layouts of the calls (a
+ *              multiple of 64). The host memory must not change while the
+ *              cache holds its rows (call hga_tier_cache_init after a change).
+ *   kv_slots   chunk slots per KV head for K and V rows: a slot holds any of
+ *              the 64 / group_size groups of one history chunk (only needed
+ *              groups are copied). At least hga_tier_cache_min_slots(...,
+ *              HGA_TC_KV) and at most 4096.
+ *   gs_slots   chunk slots per KV head for the group summaries of one history
+ *              chunk each; at least hga_tier_cache_min_slots(..., HGA_TC_GS)
+ *              (0 when top_groups >= top_chunks * 64 / group_size: the group
+ *              stage then keeps every group and reads no summary) and at most
+ *              4096.
+ * Replacement: a chunk a call needs and the cache lacks takes the next slot
+ * in ring order (per KV head and kind) that the call itself does not use,
+ * evicting the chunk there. */
+typedef struct {
+  void* mem;
+  size_t bytes;
+  int64_t split;
+  int32_t kv_slots;
+  int32_t gs_slots;
+} hga_tier_cache;
+
+enum { HGA_TC_KV = 0, HGA_TC_GS = 1 };
+
+/* Counters (int64) at the start of the cache memory. Requests are summed
+ * over the calls' (query block, KV head) items: a group (or chunk) that
+ * several blocks use counts once per block; a miss is a group (or chunk)
+ * copied from host memory because the cache did not hold it at the call. */
+enum {
+  HGA_TC_CALLS = 0,          /* calls made through the cache */
+  HGA_TC_KV_REQUESTS = 1,    /* history groups attended */
+  HGA_TC_KV_MISSES = 2,      /* groups whose K and V rows were copied */
+  HGA_TC_KV_BYTES = 3,       /* K and V bytes copied */
+  HGA_TC_KV_EVICTIONS = 4,   /* chunks whose K/V slots were reused */
+  HGA_TC_GS_REQUESTS = 5,    /* history chunks whose group summaries the group stage scored */
+  HGA_TC_GS_MISSES = 6,      /* chunks whose group summaries were copied */
+  HGA_TC_GS_BYTES = 7,       /* group-summary bytes copied */
+  HGA_TC_GS_EVICTIONS = 8,   /* chunks whose summary slots were reused */
+  HGA_TC_COUNTERS = 16
+};
+
+/* Bytes of device memory of a cache of this shape; (size_t)-1 if invalid. */
+size_t hga_tier_cache_size(const hga_config* cfg, int64_t split, int32_t kv_slots, int32_t gs_slots);
+
+/* Fewest slots per KV head of one kind (HGA_TC_KV or HGA_TC_GS) a cache must
+ * have for calls of n_q queries against a history of seq_len - n_q tokens in
+ * host memory: the most distinct history chunks such a call can need per KV
+ * head (the sink, local and kept chunks of all its query blocks), at most the
+ * history's chunks. -1 if invalid. */
+int32_t hga_tier_cache_min_slots(const hga_config* cfg, int64_t seq_len, int64_t n_q, int32_t which);
+
+/* Empty the cache and zero its counters (kernels on `stream`). */
+hga_status hga_tier_cache_init(const hga_config* cfg, const hga_tier_cache* cache, void* stream);
+
+/* hga_route_attend with the history (tokens below cache->split) in pinned
+ * host memory, through the persistent cache: the chunk stage reads the chunk
+ * summaries in HBM; when the group stage must choose, the group summaries of
+ * the kept history chunks are brought into the cache's summary slots (those
+ * missing are copied) and scored from there; then the K and V rows of every
+ * history group a query block attends (its kept groups and its sink and local
+ * chunks) are brought into the K/V slots (those missing are copied) and the
+ * attention reads them from there. Results equal those of hga_route_attend
+ * with everything in HBM, whatever the cache held.
+ *   group_sum, k, v   tiered at cache->split (> 0, <= q_start).
+ *   cache      initialized by hga_tier_cache_init for this configuration and
+ *              split, with enough slots for calls of n_q queries (see
+ *              hga_tier_cache_min_slots); else HGA_ERR_UNSUPPORTED.
+ *   workspace  device, hga_workspace_size(..., HGA_WS_ATTEND_CACHED) bytes.
+ * Other arguments as in hga_route_attend. Calls that share a cache must be
+ * ordered (one stream, or the caller's synchronization). */
+hga_status hga_route_attend_cached(const hga_config* cfg, const void* q, int64_t q_start, int64_t n_q,
+                                   int64_t seq_len, const float* chunk_sum, const hga_tiered* group_sum,
+                                   const hga_tiered* k, const hga_tiered* v, const hga_tier_cache* cache,
+                                   int32_t* chunk_idx, int32_t* group_idx, int32_t* n_sel, void* out, float* lse,
+                                   void* workspace, size_t ws_bytes, void* stream);
 
 /* Forward pass over a whole sequence in segments, in the pages' execution
  * order (section 2.1 with the segment-by-segment processing of section 2.2):

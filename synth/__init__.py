@@ -173,6 +173,9 @@ def make_inputs(cfg: dict) -> dict:
     npc = int(cfg.get("n_plant_chunks", 0))
     gpc = int(cfg.get("groups_per_plant_chunk", 1))
     c, g = cfg["chunk"], cfg["group"]
+    share = cfg.get("plant_block_share")
+    if npc > 0 and share:
+        return _finish(cfg, q, k, v, _plant_per_block_sets(cfg, q, k, int(share)))
     if npc > 0:
         dirs = _rng(cfg, _T_DIR).standard_normal((hkv, d))
         dirs /= np.linalg.norm(dirs, axis=1, keepdims=True)
@@ -193,8 +196,46 @@ def make_inputs(cfg: dict) -> dict:
             q[h * G:(h + 1) * G] += cfg["alpha"] * dirs[h]
     else:
         planted = [[] for _ in range(hkv)]
+    return _finish(cfg, q, k, v, planted)
+
+
+def _finish(cfg, q, k, v, planted):
+    """Round to the stored formats (float32, then bfloat16 bits)."""
     out = {"planted": planted}
     for name, x in (("q", q), ("k", k), ("v", v)):
         x32 = x.astype(np.float32)
         out[name] = f32_to_bf16_bits(x32) if cfg["dtype"] == "bf16" else x32
     return out
+
+
+def _plant_per_block_sets(cfg, q, k, share):
+    """Block-varying planting: the query blocks are taken `share` at a time
+    (consecutive blocks of q_block queries); each set s of blocks gets its own
+    unit direction u_{h,s} per KV head and its own n_plant_chunks planted
+    groups (in distinct chunks of plant_chunks, drawn per set): the set's
+    queries get +alpha u_{h,s}, the planted groups' keys +beta u_{h,s}. Blocks
+    of different sets then route to different chunks. Returns the planted
+    groups per KV head (all sets, sorted)."""
+    L, nq, hq, hkv, d = cfg["L"], cfg["n_q"], cfg["hq"], cfg["hkv"], cfg["d"]
+    G, c, g, B = hq // hkv, cfg["chunk"], cfg["group"], cfg["q_block"]
+    npc, gpc = int(cfg["n_plant_chunks"]), int(cfg.get("groups_per_plant_chunk", 1))
+    nsets = -(-(nq // B) // share)
+    dirs = _rng(cfg, _T_DIR).standard_normal((hkv, nsets, d))
+    dirs /= np.linalg.norm(dirs, axis=2, keepdims=True)
+    rch, rgr = _rng(cfg, _T_PCH), _rng(cfg, _T_PGR)
+    lo, hi = cfg["plant_chunks"]
+    hi = min(hi, L // c)
+    planted = []
+    for h in range(hkv):
+        groups = set()
+        for st in range(nsets):
+            chunks = rch.choice(np.arange(lo, hi), size=min(npc, hi - lo), replace=False)
+            for m in np.sort(chunks):
+                for u in np.sort(rgr.choice(c // g, size=gpc, replace=False)):
+                    j = int(m) * (c // g) + int(u)
+                    groups.add(j)
+                    k[h, j * g:(j + 1) * g, :] += cfg["beta"] * dirs[h, st]
+            rows = slice(st * share * B, min((st + 1) * share * B, nq))
+            q[h * G:(h + 1) * G, rows] += cfg["alpha"] * dirs[h, st]
+        planted.append(sorted(groups))
+    return planted

@@ -31,7 +31,7 @@ def test_every_declared_entry_point_is_exported(lib):
     assert declared == set(B.EXPORTS)
     for name in declared:
         assert hasattr(lib, name)
-    assert hga.hga_version() == 107
+    assert hga.hga_version() == 108
 
 
 def test_status_strings(lib):
@@ -246,3 +246,49 @@ def test_backward_validation():
     assert call(big, args, 1 << 62, (0, 262144, 262144)) == hga.HGA_ERR_UNSUPPORTED
     assert "4 GiB" in hga.hga_last_error()
     hga.hga_attend_backward(c, None, 16384, 0, 16384, *[None] * 11, 0)   # no queries: a no-op
+
+
+def test_tier_cache_sizes_and_validation():
+    """The persistent host-tier cache: size, fewest slots, and every
+    validation path of hga_tier_cache_init and hga_route_attend_cached."""
+    c = cfg()
+    E = hga.HGA_ERR_INVALID_ARGUMENT
+    split = 14336
+    nch = split // 64
+    # one call of 2,048 queries (32 blocks) can need every history chunk; one
+    # block of 64 at most top_chunks + sink + local chunks (16 + 1 + 2)
+    assert hga.hga_tier_cache_min_slots(c, 16384, 2048, hga.HGA_TC_KV) == nch
+    assert hga.hga_tier_cache_min_slots(c, 16384, 64, hga.HGA_TC_KV) == 19
+    assert hga.hga_tier_cache_min_slots(c, 16384, 64, hga.HGA_TC_GS) == 16
+    # top_groups covering every group of the kept chunks: no summary is read
+    assert hga.hga_tier_cache_min_slots(cfg(top_groups=128), 16384, 64, hga.HGA_TC_GS) == 0
+    assert hga.hga_tier_cache_min_slots(c, 16384, 64, 7) == -1
+    size = hga.hga_tier_cache_size(c, split, 64, 32)
+    # counters, K/V and summary tables, then K and V rows (64 x 128 bf16 per
+    # slot) and group summaries (8 x 128 float32 per slot) for 8 KV heads
+    assert size >= 8 * 64 * (2 * 64 * 128 * 2) + 8 * 32 * 8 * 128 * 4
+    assert size < 8 * 64 * (2 * 64 * 128 * 2) + 8 * 32 * 8 * 128 * 4 + 64 * 1024
+    assert hga.hga_tier_cache_size(c, split, 0, 32) == 2**64 - 1
+    assert hga.hga_tier_cache_size(c, split, 5000, 32) == 2**64 - 1
+    assert hga.hga_tier_cache_size(c, 100, 64, 32) == 2**64 - 1
+    ws = hga.hga_workspace_size(c, 16384, 64, hga.HGA_WS_ATTEND_CACHED)
+    assert ws >= 8 * nch * (8 + 8 + 16 + 16)
+    good = hga.tier_cache(FAKE * 16, size, split, 64, 32)
+    assert _status(hga.hga_tier_cache_init, c, hga.tier_cache(FAKE + 16, size, split, 64, 32)) == E   # alignment
+    assert _status(hga.hga_tier_cache_init, c, hga.tier_cache(FAKE * 16, size - 1, split, 64, 32)) == \
+        hga.HGA_ERR_WORKSPACE
+    assert _status(hga.hga_tier_cache_init, c, hga.tier_cache(FAKE * 16, size, 1000, 64, 32)) == E
+    tier = (FAKE, FAKE, split)
+    args = (c, FAKE, 16320, 64, 16384, FAKE, tier, tier, tier)
+    tail = (FAKE, FAKE, FAKE, FAKE, None, FAKE, ws)
+    assert _status(hga.hga_route_attend_cached, *args, None, *tail) == E
+    assert _status(hga.hga_route_attend_cached, *args, hga.tier_cache(FAKE * 16, size, split, 18, 32), *tail) == \
+        hga.HGA_ERR_UNSUPPORTED                                                 # too few K/V slots
+    assert _status(hga.hga_route_attend_cached, *args, hga.tier_cache(FAKE * 16, size, split, 64, 15), *tail) == \
+        hga.HGA_ERR_UNSUPPORTED                                                 # too few summary slots
+    assert _status(hga.hga_route_attend_cached, c, FAKE, 16320, 64, 16384, FAKE, tier, (FAKE, FAKE, 1024), tier,
+                   good, *tail) == E                                            # split differs from the cache's
+    assert _status(hga.hga_route_attend_cached, *args, good, FAKE, FAKE, FAKE, FAKE, None, None, 0) == \
+        hga.HGA_ERR_WORKSPACE
+    assert _status(hga.hga_route_attend_cached, *args, good, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1024) == \
+        hga.HGA_ERR_WORKSPACE
