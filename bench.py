@@ -69,6 +69,9 @@ def parse():
                     help="only the one-token decoding line of --config for a batch of B sequences")
     ap.add_argument("--host-tier", action="store_true",
                     help="main line with the history (tokens before the first query) in pinned host memory")
+    ap.add_argument("--cached-host-tier", action="store_true",
+                    help="only the lines of --config through the persistent host-tier cache (planted groups shared "
+                         "by all blocks, and a separate set per 4 blocks)")
     ap.add_argument("--traffic-kib", type=float, nargs=2, default=None, metavar=("FETCH", "WRITE"),
                     help="attention kernel FETCH_SIZE and WRITE_SIZE per dispatch (KiB, as rocprofv3 "
                          "reports them) for the roofline traffic field")
@@ -740,6 +743,120 @@ def host_tier_line(cfg_id, steps, warmup, link_rate, note):
     return line
 
 
+def cached_host_tier_line(cfg_id, steps, warmup, link_rate, share=None, calls_of=None):
+    """The layer with its history (tokens before the first query) in pinned
+    host memory, through a persistent HBM cache (hga_route_attend_cached).
+
+    cold: a call on an emptied cache of every history chunk (each distinct
+    history group crosses the host link once); warm: the same call
+    repeated (every group resident; the rate of `value`). With `calls_of`, a
+    rolling pass: the queries in consecutive calls of `calls_of` queries each,
+    on a cache with the fewest slots such calls allow (chunks are evicted),
+    with the hit rate of its K/V requests. `share` plants a separate set of
+    relevant groups for every `share` consecutive query blocks, so blocks of
+    different sets route to different chunks."""
+    import torch
+
+    import hierarchical_sparse_attention_hga_amd as hga
+    import synth
+    from hierarchical_sparse_attention_hga_amd.memory import split_to_host
+    over = dict(plant_block_share=share) if share else {}
+    cfg = synth.config(cfg_id, **over)
+    x = synth.make_inputs(cfg)
+    DEV = torch.device("cuda:0")
+    L, nq, hkv, d, g = cfg["L"], cfg["n_q"], cfg["hkv"], cfg["d"], cfg["group"]
+    q0, split = L - nq, cfg["tier_split"] or L - nq
+    c = hga.make_config(cfg["hq"], hkv, d, cfg["top_chunks"], cfg["top_groups"], cfg["sink"], cfg["local"],
+                        dtype=cfg["dtype"], group_size=g)
+    q, k, v = (to_dev(x[n], cfg["dtype"], DEV) for n in ("q", "k", "v"))
+    del x
+    gs = torch.empty(hkv, L // g, d, device=DEV)
+    cs = torch.empty(hkv, L // 64, d, device=DEV)
+    hga.hga_build_summaries(c, k, L, gs, cs)
+    torch.cuda.synchronize()
+    gpin, _, gs_t = split_to_host(gs, split // g)
+    kpin, _, k_t = split_to_host(k, split)
+    vpin, _, v_t = split_to_host(v, split)
+    gs_t = (gs_t[0], gs_t[1], split)
+    del k, v
+    esz = 2 if cfg["dtype"] == "bf16" else 4
+
+    def make(n_q, kv_slots, gs_slots):
+        size = hga.hga_tier_cache_size(c, split, kv_slots, gs_slots)
+        mem = torch.empty(size + 256, dtype=torch.uint8, device=DEV)
+        cache = hga.tier_cache((mem.data_ptr() + 255) // 256 * 256, size, split, kv_slots, gs_slots)
+        hga.hga_tier_cache_init(c, cache)
+        wsb = hga.hga_workspace_size(c, L, n_q, hga.HGA_WS_ATTEND_CACHED)
+        return mem, cache, torch.empty(wsb, dtype=torch.uint8, device=DEV), wsb
+
+    def counts(mem, cache):
+        off = cache.mem - mem.data_ptr()
+        raw = mem[off:off + 8 * len(hga.TC_COUNTERS)].cpu().numpy().view(np.int64)
+        return dict(zip(hga.TC_COUNTERS, (int(r) for r in raw)))
+
+    def caller(cache, ws, wsb, qs, n_q):
+        nb = n_q // 64
+        ci = torch.empty(nb, hkv, cfg["top_chunks"], dtype=torch.int32, device=DEV)
+        gi = torch.empty(nb, hkv, cfg["top_groups"], dtype=torch.int32, device=DEV)
+        ns = torch.empty(nb, hkv, 2, dtype=torch.int32, device=DEV)
+        qv = q[:, qs - q0:qs - q0 + n_q].contiguous()
+        out = torch.empty_like(qv)
+        lse = torch.empty(cfg["hq"], n_q, device=DEV)
+        return lambda: hga.hga_route_attend_cached(c, qv, qs, n_q, L, cs, gs_t, k_t, v_t, cache, ci, gi, ns, out, lse,
+                                                   ws, wsb)
+
+    nch = split // 64
+    gs_all = hga.hga_tier_cache_min_slots(c, L, nq, hga.HGA_TC_GS)
+    mem, cache, ws, wsb = make(nq, nch, gs_all)
+    call = caller(cache, ws, wsb, q0, nq)
+    call()                           # the kernels' first launches (code loading) out of the cold figure
+    hga.hga_tier_cache_init(c, cache)
+    cold_us = event_us(call, 1, warm=0)[0]
+    cold = counts(mem, cache)
+    wall, warm, flushed = timed_calls(call, steps, warmup)
+    line = {"value": steps * nq / wall, "unit": "query-tokens/s", "ms_per_step": wall / steps * 1e3,
+            "call_us": warm, "call_us_flushed": flushed,
+            "cold_call": {"us": cold_us, "host_link_bytes": cold["kv_bytes"] + cold["gs_bytes"],
+                          "host_link_GBps": (cold["kv_bytes"] + cold["gs_bytes"]) / (cold_us * 1e-6) / 1e9,
+                          "kv_requests": cold["kv_requests"], "kv_misses": cold["kv_misses"]},
+            "warm_counters_after": counts(mem, cache),
+            "measured_pinned_h2d_GBps": link_rate / 1e9,
+            "config": {"workload": cfg["name"] + (f"-plant-share{share}" if share else ""), "split": split,
+                       "kv_slots": nch, "gs_slots": gs_all}}
+    del mem, cache, ws
+    if calls_of:
+        kv_min = hga.hga_tier_cache_min_slots(c, L, calls_of, hga.HGA_TC_KV)
+        gs_min = hga.hga_tier_cache_min_slots(c, L, calls_of, hga.HGA_TC_GS)
+        mem, cache, ws, wsb = make(calls_of, kv_min, gs_min)
+        calls = [caller(cache, ws, wsb, qs, calls_of) for qs in range(q0, L, calls_of)]
+        for fn in calls:      # one pass to settle (the cache then holds the last calls' chunks)
+            fn()
+        before = counts(mem, cache)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for fn in calls:
+            fn()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        after = counts(mem, cache)
+        dlt = {k2: after[k2] - before[k2] for k2 in after}
+        line["rolling"] = {
+            "value": nq / el, "unit": "query-tokens/s", "calls": len(calls), "queries_per_call": calls_of,
+            "kv_slots": kv_min, "gs_slots": gs_min,
+            "kv_hit_rate": 1.0 - dlt["kv_misses"] / max(dlt["kv_requests"], 1),
+            "gs_hit_rate": 1.0 - dlt["gs_misses"] / max(dlt["gs_requests"], 1) if dlt["gs_requests"] else None,
+            "host_link_bytes_per_pass": dlt["kv_bytes"] + dlt["gs_bytes"],
+            "host_link_GBps": (dlt["kv_bytes"] + dlt["gs_bytes"]) / el / 1e9,
+            "counters": dlt,
+            "note": "the layer's queries in consecutive calls through one cache with the fewest slots such calls "
+                    "allow; hit rate = 1 - K/V groups copied / history groups the calls' blocks attended"}
+        del mem, cache, ws
+    for p in (gpin, kpin, vpin):
+        p.free()
+    torch.cuda.empty_cache()
+    return line
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -753,6 +870,12 @@ def main():
         return
     if args.backward:
         print(json.dumps(backward_line(args.config, args.steps, args.warmup), allow_nan=False), flush=True)
+        return
+    if args.cached_host_tier:
+        link = host_link_rate()
+        for share in (None, 4):
+            print(json.dumps(cached_host_tier_line(args.config, args.steps, args.warmup, link, share=share,
+                                                   calls_of=256), allow_nan=False), flush=True)
         return
     if args.decode_batch:
         print(json.dumps(decode_line(args.config, args.decode_batch, args.steps, args.warmup), allow_nan=False),
@@ -816,6 +939,9 @@ def main():
             "the 131,072-token long-evaluation layer (Qwen3-8B heads, top-64 chunks, top-512 groups, 64 planted "
             "needle groups per head): history K/V and group summaries in pinned host memory, the final 2,048 "
             "queries in HBM; each history chunk any block needs crosses the host link once per step")
+        extra["64k_host_tier_cached"] = cached_host_tier_line(3, max(half, 20), 2, link, calls_of=256)
+        extra["64k_host_tier_cached_block_varying"] = cached_host_tier_line(3, max(half, 20), 2, link, share=4,
+                                                                            calls_of=256)
         if args.config == 2:
             extra["16k_streamed_2048_segments"] = stream_line(max(args.steps // 6, 3), 2)
         extra["backward_16k_segment"] = backward_line(2, half, 3)
