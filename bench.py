@@ -754,7 +754,9 @@ def cached_host_tier_line(cfg_id, steps, warmup, link_rate, share=None, calls_of
     on a cache with the fewest slots such calls allow (chunks are evicted),
     with the hit rate of its K/V requests. `share` plants a separate set of
     relevant groups for every `share` consecutive query blocks, so blocks of
-    different sets route to different chunks."""
+    different sets route to different chunks. Every figure is taken with
+    everything on one stream and, as "overlap", with the copies on a second
+    stream while the blocks that need none of them are attended."""
     import torch
 
     import hierarchical_sparse_attention_hga_amd as hga
@@ -794,7 +796,9 @@ def cached_host_tier_line(cfg_id, steps, warmup, link_rate, share=None, calls_of
         raw = mem[off:off + 8 * len(hga.TC_COUNTERS)].cpu().numpy().view(np.int64)
         return dict(zip(hga.TC_COUNTERS, (int(r) for r in raw)))
 
-    def caller(cache, ws, wsb, qs, n_q):
+    side = torch.cuda.Stream()   # default priority
+
+    def caller(cache, ws, wsb, qs, n_q, overlap=True):
         nb = n_q // 64
         ci = torch.empty(nb, hkv, cfg["top_chunks"], dtype=torch.int32, device=DEV)
         gi = torch.empty(nb, hkv, cfg["top_groups"], dtype=torch.int32, device=DEV)
@@ -803,22 +807,26 @@ def cached_host_tier_line(cfg_id, steps, warmup, link_rate, share=None, calls_of
         out = torch.empty_like(qv)
         lse = torch.empty(cfg["hq"], n_q, device=DEV)
         return lambda: hga.hga_route_attend_cached(c, qv, qs, n_q, L, cs, gs_t, k_t, v_t, cache, ci, gi, ns, out, lse,
-                                                   ws, wsb)
+                                                   ws, wsb, copy_stream=side if overlap else None)
 
     nch = split // 64
     gs_all = hga.hga_tier_cache_min_slots(c, L, nq, hga.HGA_TC_GS)
     mem, cache, ws, wsb = make(nq, nch, gs_all)
-    call = caller(cache, ws, wsb, q0, nq)
-    call()                           # the kernels' first launches (code loading) out of the cold figure
-    hga.hga_tier_cache_init(c, cache)
-    cold_us = event_us(call, 1, warm=0)[0]
-    cold = counts(mem, cache)
-    wall, warm, flushed = timed_calls(call, steps, warmup)
-    line = {"value": steps * nq / wall, "unit": "query-tokens/s", "ms_per_step": wall / steps * 1e3,
-            "call_us": warm, "call_us_flushed": flushed,
-            "cold_call": {"us": cold_us, "host_link_bytes": cold["kv_bytes"] + cold["gs_bytes"],
+    colds = {}
+    for overlap in (False, True):
+        call = caller(cache, ws, wsb, q0, nq, overlap)
+        call()                       # the kernels' first launches (code loading) out of the cold figure
+        hga.hga_tier_cache_init(c, cache)
+        cold_us = event_us(call, 1, warm=0)[0]
+        cold = counts(mem, cache)
+        colds[overlap] = {"us": cold_us, "host_link_bytes": cold["kv_bytes"] + cold["gs_bytes"],
                           "host_link_GBps": (cold["kv_bytes"] + cold["gs_bytes"]) / (cold_us * 1e-6) / 1e9,
-                          "kv_requests": cold["kv_requests"], "kv_misses": cold["kv_misses"]},
+                          "kv_requests": cold["kv_requests"], "kv_misses": cold["kv_misses"]}
+    _, warm_overlap, _ = timed_calls(call, steps, warmup)
+    wall, warm, flushed = timed_calls(caller(cache, ws, wsb, q0, nq, False), steps, warmup)
+    line = {"value": steps * nq / wall, "unit": "query-tokens/s", "ms_per_step": wall / steps * 1e3,
+            "call_us": warm, "call_us_flushed": flushed, "call_us_overlap": warm_overlap,
+            "cold_call": colds[False], "cold_call_overlap": colds[True],
             "warm_counters_after": counts(mem, cache),
             "measured_pinned_h2d_GBps": link_rate / 1e9,
             "config": {"workload": cfg["name"] + (f"-plant-share{share}" if share else ""), "split": split,
@@ -828,20 +836,25 @@ def cached_host_tier_line(cfg_id, steps, warmup, link_rate, share=None, calls_of
         kv_min = hga.hga_tier_cache_min_slots(c, L, calls_of, hga.HGA_TC_KV)
         gs_min = hga.hga_tier_cache_min_slots(c, L, calls_of, hga.HGA_TC_GS)
         mem, cache, ws, wsb = make(calls_of, kv_min, gs_min)
-        calls = [caller(cache, ws, wsb, qs, calls_of) for qs in range(q0, L, calls_of)]
-        for fn in calls:      # one pass to settle (the cache then holds the last calls' chunks)
-            fn()
-        before = counts(mem, cache)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for fn in calls:
-            fn()
-        torch.cuda.synchronize()
-        el = time.perf_counter() - t0
-        after = counts(mem, cache)
-        dlt = {k2: after[k2] - before[k2] for k2 in after}
+        def rolling_pass(overlap):
+            calls = [caller(cache, ws, wsb, qs, calls_of, overlap) for qs in range(q0, L, calls_of)]
+            for fn in calls:      # one pass to settle (the cache then holds the last calls' chunks)
+                fn()
+            before = counts(mem, cache)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for fn in calls:
+                fn()
+            torch.cuda.synchronize()
+            el = time.perf_counter() - t0
+            after = counts(mem, cache)
+            return len(calls), el, {k2: after[k2] - before[k2] for k2 in after}
+
+        _, el_overlap, _ = rolling_pass(True)
+        ncalls, el, dlt = rolling_pass(False)
         line["rolling"] = {
-            "value": nq / el, "unit": "query-tokens/s", "calls": len(calls), "queries_per_call": calls_of,
+            "value": nq / el, "value_overlap": nq / el_overlap, "unit": "query-tokens/s", "calls": ncalls,
+            "queries_per_call": calls_of,
             "kv_slots": kv_min, "gs_slots": gs_min,
             "kv_hit_rate": 1.0 - dlt["kv_misses"] / max(dlt["kv_requests"], 1),
             "gs_hit_rate": 1.0 - dlt["gs_misses"] / max(dlt["gs_requests"], 1) if dlt["gs_requests"] else None,

@@ -81,7 +81,7 @@ def load():
         lib.hga_tier_cache_min_slots.restype = I32
         lib.hga_tier_cache_init.argtypes = [cfgp, cachep, P]
         lib.hga_route_attend_cached.argtypes = [cfgp, P, I64, I64, I64, P, tierp, tierp, tierp, cachep, P, P, P, P,
-                                                P, P, SZ, P]
+                                                P, P, SZ, P, P]
         lib.hga_build_summaries_range.argtypes = [cfgp, P, I64, I64, I64, P, P, P]
         lib.hga_stream_forward.argtypes = [cfgp, P, P, P, I64, I64, P, P, P, P, P, P, P, P]
         lib.hga_attend_backward.argtypes = [cfgp, P, I64, I64, I64, tierp, tierp, P, P, P, P, P, P, P, P, P, SZ, P]
@@ -203,13 +203,13 @@ def hga_tier_cache_init(cfg, cache, stream=None):
 
 
 def hga_route_attend_cached(cfg, q, q_start, n_q, seq_len, chunk_sum, group_sum, k, v, cache, chunk_idx, group_idx,
-                            n_sel, out, lse=None, workspace=None, ws_bytes=0, stream=None):
+                            n_sel, out, lse=None, workspace=None, ws_bytes=0, stream=None, copy_stream=None):
     gt, kt, vt = _tier(group_sum), _tier(k), _tier(v)
     _check(load().hga_route_attend_cached(C.byref(cfg), _ptr(q), q_start, n_q, seq_len, _ptr(chunk_sum), C.byref(gt),
                                           C.byref(kt), C.byref(vt), None if cache is None else C.byref(cache),
                                           _ptr(chunk_idx), _ptr(group_idx),
                                           _ptr(n_sel), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
-                                          _stream(stream)))
+                                          _stream(stream), None if copy_stream is None else _stream(copy_stream)))
 
 
 def hga_build_summaries_range(cfg, k, seq_len, chunk_begin, chunk_end, group_sum, chunk_sum, stream=None):

@@ -242,7 +242,7 @@ hga_status hga_route_attend_cached(const hga_config* cfg, const void* q, int64_t
                                    int64_t seq_len, const float* chunk_sum, const hga_tiered* group_sum,
                                    const hga_tiered* k, const hga_tiered* v, const hga_tier_cache* cache,
                                    int32_t* chunk_idx, int32_t* group_idx, int32_t* n_sel, void* out, float* lse,
-                                   void* workspace, size_t ws_bytes, void* stream) {
+                                   void* workspace, size_t ws_bytes, void* stream, void* copy_stream) {
   hga::Shape s;
   hga_status st = make_shape(cfg, seq_len, q_start, n_q, &s);
   if (st != HGA_OK) return st;
@@ -255,6 +255,8 @@ hga_status hga_route_attend_cached(const hga_config* cfg, const void* q, int64_t
   if ((st = check_tier(k, "k", seq_len, q_start)) != HGA_OK) return st;
   if ((st = check_tier(v, "v", seq_len, q_start)) != HGA_OK) return st;
   if ((st = check_cache(s, cache)) != HGA_OK) return st;
+  if (copy_stream && copy_stream == stream)
+    return fail(HGA_ERR_INVALID_ARGUMENT, "copy_stream must be NULL or a stream other than stream");
   if (k->split != cache->split || v->split != cache->split || group_sum->split != cache->split)
     return fail(HGA_ERR_INVALID_ARGUMENT, "group_sum, k and v must be split at cache->split");
   if (s.sink_chunks + s.local_chunks > hga::kMaxFixedTiered)
@@ -273,7 +275,8 @@ hga_status hga_route_attend_cached(const hga_config* cfg, const void* q, int64_t
   return device_status(hga::launch_route_attend_cached(s, q, chunk_sum, static_cast<const float*>(group_sum->host),
                                                        static_cast<const float*>(group_sum->dev), group_sum->split, kv,
                                                        cache->kv_slots, cache->gs_slots, cache->mem, chunk_idx,
-                                                       group_idx, n_sel, out, lse, workspace, (hipStream_t)stream),
+                                                       group_idx, n_sel, out, lse, workspace, (hipStream_t)stream,
+                                                       (hipStream_t)copy_stream),
                        "hga_route_attend_cached launch");
 }
 
@@ -515,6 +518,6 @@ const char* hga_status_string(hga_status status) {
 
 const char* hga_last_error(void) { return g_err; }
 
-int32_t hga_version(void) { return 108; }
+int32_t hga_version(void) { return 109; }
 
 }  // extern "C"

@@ -364,6 +364,7 @@ __device__ __attribute__((always_inline)) void store_output(const AttnArgs& A, i
 template <int D, bool kTiered>
 __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(AttnArgs A) {
   __shared__ AttnSmem<D> sm;
+  if (kTiered && A.pass == 2 && A.done[blockIdx.x]) return;   // attended by pass 1
   int b, h, z;
   item_of_block(A.s, A.wg_per_item, &b, &h, &z);
   // the queries and, with every row on the device, the first fixed tiles
@@ -383,7 +384,9 @@ __global__ __launch_bounds__(kAttnThreads) void attend_bf16_kernel(AttnArgs A) {
   bf16x8 qf[D / 16];
   load_q_operands<D>(A, b, h, z, qf);
   const Plan P = make_plan(A.s, b, h, A.gidx, A.nsel, sm.runs, sm.scan, kMaxRoutedAttn);
-  if (kTiered) translate_plan(A.kv.split, A.nch, A.nslots, A.slot, h, P, sm.runs, sm.runs + kMaxRoutedAttn);
+  if (kTiered && translate_plan(A.kv.split, A.nch, A.nslots, A.slot, h, P, sm.runs, sm.runs + kMaxRoutedAttn,
+                                A.s.g, A.pending, A.pass, A.done))
+    return;   // pass 2 attends this item
   attend_bf16_body<D, kTiered>(A, b, h, z, P, sm, pre, qf, 0, P.ntiles, nullptr);
 }
 
@@ -518,11 +521,14 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttnArgs A) {
   __shared__ int sRuns[kMaxRouted + kMaxFixedTiered];
   __shared__ int sScan[16];
 
+  if (kTiered && A.pass == 2 && A.done[blockIdx.x]) return;   // attended by pass 1
   const Shape& S = A.s;
   int b, h, z;
   item_of_block(S, A.wg_per_item, &b, &h, &z);
   const Plan P = make_plan(S, b, h, A.gidx, A.nsel, sRuns, sScan, kMaxRouted);
-  if (kTiered) translate_plan(A.kv.split, A.nch, A.nslots, A.slot, h, P, sRuns, sRuns + kMaxRouted);
+  if (kTiered && translate_plan(A.kv.split, A.nch, A.nslots, A.slot, h, P, sRuns, sRuns + kMaxRouted, S.g,
+                                A.pending, A.pass, A.done))
+    return;   // pass 2 attends this item
   const int64_t per_head = kTiered ? S.kvs - A.kv.split : S.kvs;
   const float* kdev = static_cast<const float*>(A.kv.k_dev) + (int64_t)h * per_head * D;
   const float* vdev = static_cast<const float*>(A.kv.v_dev) + (int64_t)h * per_head * D;
@@ -818,6 +824,9 @@ hipError_t launch_attend(const Shape& s, const void* q, const KVSrc& kv, const i
     a.nslots = tc.nslots;
     a.k_cache = tc.k_cache;
     a.v_cache = tc.v_cache;
+    a.pending = tc.pending;
+    a.pass = tc.pass;
+    a.done = tc.done;
   }
   if (s.dtype == HGA_BF16) {
     a.wg_per_item = bf16_wg_per_item(s);

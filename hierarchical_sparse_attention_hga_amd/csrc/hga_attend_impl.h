@@ -33,6 +33,9 @@ struct AttnArgs {
   const int32_t* slot;     // [Hkv][nch]: cache slot of history chunk m of head h (-1: not needed)
   int nch;                 // chunks in the host tier (split / 64)
   int nslots;              // cache slots per KV head (the cache is [Hkv][nslots][64][d])
+  const uint64_t* pending; // [Hkv][nch]: groups of history chunks copied by a concurrent kernel (null: none)
+  int pass;                // with pending: 1 attends the items that read none of them, 2 the others
+  int* done;               // [workgroups]: set by pass 1 for each workgroup that attended its item
   const int32_t* gidx;
   const int32_t* nsel;
   void* out;
@@ -102,7 +105,7 @@ __device__ int block_scan(int v, int* lds, int* total) {
 // block start and it is not inside a fixed chunk; a usable entry is used when
 // it is greater than every earlier usable entry of the row, so each token is
 // used once and ascending rows are taken whole.
-__device__ Plan make_plan(const Shape& S, int b, int h, const int32_t* gidx, const int32_t* nsel,
+__device__ inline Plan make_plan(const Shape& S, int b, int h, const int32_t* gidx, const int32_t* nsel,
                           int* runs, int* lds, int cap) {
   Plan P;
   plan_windows(S, b, &P);
@@ -169,9 +172,15 @@ __device__ inline int tile_limit(const Plan& P, int g, int t) {
 // fixed chunks' first tokens into encoded source rows (fixsrc[t] for fixed
 // tile t), given the cache slots (slot[h nch + m], -1: not cached) of the
 // nch history chunks below split, in a cache of nslots chunk slots per KV
-// head. Every history chunk used here was given a slot.
-__device__ void translate_plan(int64_t split, int nch, int nslots, const int32_t* slot, int h, const Plan& P,
-                               int* runs, int* fixsrc) {
+// head. Every history chunk used here was given a slot. With pending (the
+// groups of each history chunk still being copied, as group bits) in pass 1,
+// returns whether the item reads a pending group, so that the workgroup must
+// leave it to pass 2, and records in done[workgroup] whether it attends it
+// (pass 2 runs the workgroups pass 1 did not). The result is the same in
+// every thread.
+__device__ inline bool translate_plan(int64_t split, int nch, int nslots, const int32_t* slot, int h, const Plan& P,
+                                      int* runs, int* fixsrc, int g = 8, const uint64_t* pending = nullptr,
+                                      int pass = 0, int* done = nullptr) {
   auto enc = [&](int64_t tok) -> int {
     if (tok < split) {
       const int64_t m = tok / kChunk;
@@ -182,10 +191,21 @@ __device__ void translate_plan(int64_t split, int nch, int nslots, const int32_t
     }
     return (int)(tok - split);
   };
-  for (int i = threadIdx.x; i < P.nrouted; i += blockDim.x) runs[i] = enc(runs[i]);
-  for (int t = threadIdx.x; t < P.nfix; t += blockDim.x)
-    fixsrc[t] = enc((t < P.a ? t : P.bb + (t - P.a)) * kChunk);
-  __syncthreads();
+  const uint64_t* ph = pending && pass == 1 ? pending + (int64_t)h * nch : nullptr;
+  int busy = 0;
+  for (int i = threadIdx.x; i < P.nrouted; i += blockDim.x) {
+    const int tok = runs[i];
+    if (ph && tok < split && ((ph[tok / kChunk] >> ((tok % kChunk) / g)) & 1ull)) busy = 1;
+    runs[i] = enc(tok);
+  }
+  for (int t = threadIdx.x; t < P.nfix; t += blockDim.x) {
+    const int64_t m = t < P.a ? t : P.bb + (t - P.a);
+    if (ph && m < nch && ph[m]) busy = 1;
+    fixsrc[t] = enc(m * kChunk);
+  }
+  busy = __syncthreads_or(busy);
+  if (ph && threadIdx.x == 0) done[blockIdx.x] = busy ? 0 : 1;
+  return busy != 0;
 }
 
 // K or V row of a source row: the cache, or the head's device rows.

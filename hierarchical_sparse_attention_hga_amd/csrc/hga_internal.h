@@ -81,6 +81,12 @@ struct TierCache {
   int nslots;            // slots per KV head of k_cache / v_cache ([Hkv][nslots][64][d])
   const void* k_cache;
   const void* v_cache;
+  // [Hkv][nch]: groups of each needed history chunk that this call copies
+  // (null: none). pass 1 attends only the items that need none of them,
+  // pass 2 only the others, pass 0 every item.
+  const uint64_t* pending;
+  int pass;
+  int* done;             // [workgroups of the attention launch]: written by pass 1, read by pass 2
 };
 hipError_t prepare_tier_cache(const Shape& s, const KVSrc& kv, const int32_t* group_idx, const int32_t* n_sel,
                               void* workspace, TierCache* tc, hipStream_t st);
@@ -122,12 +128,13 @@ struct TierCacheLayout {
   int nch, S, Sg;
   size_t slot, owner, used, valid, hand;        // K/V slot tables
   size_t gslot, gowner, gused, gvalid, ghand;   // group-summary slot tables
+  size_t need, gneed;                           // [Hkv][nch] marks of the running call (zero between calls)
   size_t k, v, gs;                              // [Hkv][S][64][d], [Hkv][S][64][d], [Hkv][Sg][c/g][d]
   size_t total;
 };
 // Byte offsets of one call's workspace of the cached path.
 struct TierCallLayout {
-  size_t need, gneed, list, count, glist, gcount, qbar, total;
+  size_t pend, list, count, glist, gcount, qbar, done, total;
 };
 // A chunk whose groups (mask) are copied into a slot.
 struct CopyEntry {
@@ -140,7 +147,8 @@ hipError_t tier_cache_init(const Shape& s, int64_t split, int kv_slots, int gs_s
 hipError_t launch_route_attend_cached(const Shape& s, const void* q, const float* cs, const float* gs_host,
                                       const float* gs_dev, int64_t gs_split, const KVSrc& kv, int kv_slots,
                                       int gs_slots, void* cache_mem, int32_t* chunk_idx, int32_t* group_idx,
-                                      int32_t* n_sel, void* out, float* lse, void* workspace, hipStream_t st);
+                                      int32_t* n_sel, void* out, float* lse, void* workspace, hipStream_t st,
+                                      hipStream_t copy_st);
 
 // Backward of the attention (bfloat16): workspace bytes (without the
 // host-tier cache, which follows them when kv.split > 0), and the launch of

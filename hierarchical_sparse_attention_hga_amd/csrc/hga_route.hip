@@ -36,6 +36,7 @@ using route::kThreads;
 template <typename T>
 __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   __shared__ route::RouteSmem sm;
+  __shared__ int sMarked;   // the item's kept history groups (or chunks) marked for the cache
   const Shape& S = a.s;
   // the workgroups of one KV head stay on one XCD (block id x runs on XCD
   // x % 8), so its summaries stay in that XCD's L2
@@ -45,7 +46,21 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   const int h = lid / (int)S.nb;
   const int b = lid % (int)S.nb;
   int32_t* gout = a.group_idx + ((int64_t)b * S.hkv + h) * S.kg;
-  route::route_item<T, true>(a, b, h, sm, true, [gout](int rank, int group) { gout[rank] = group; });
+  if (!a.kv_need && !a.gs_need) {
+    route::route_item<T, true>(a, b, h, sm, true, [gout](int rank, int group) { gout[rank] = group; });
+    return;
+  }
+  // with the persistent cache's marks (route_item's first barrier orders
+  // this store before every use)
+  if (threadIdx.x == 0) sMarked = 0;
+  uint64_t* need = a.kv_need ? a.kv_need + (int64_t)h * (a.need_split / kChunk) : nullptr;
+  const int n = route::route_item<T, true>(a, b, h, sm, true, route::MarkingEmit{gout, need, S.g, a.need_split, &sMarked});
+  __syncthreads();
+  if (a.chunks_only) {
+    if (a.gs_need) route::mark_summary_chunks(a, h, sm, n, &sMarked);
+  } else if (a.kv_need) {
+    route::mark_fixed_chunks(a, b, h, sMarked);
+  }
 }
 
 }  // namespace

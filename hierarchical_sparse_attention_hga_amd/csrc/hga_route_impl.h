@@ -268,6 +268,13 @@ struct RouteArgs {
   Shape s;
   double* qbar_out;      // if set, each item's block query is stored ([nb][Hkv][d])
   bool chunks_only;      // stop after the chunk stage (the group stage runs later)
+  // Marks of the persistent host-tier cache (unused when null): the history
+  // (tokens below need_split) an item needs, OR-ed into [Hkv][need_split / 64]
+  // words, and the requests counted in counters.
+  uint64_t* kv_need;     // with the group stage: bit u of chunk m = group u of m is attended
+  uint64_t* gs_need;     // with chunks_only: bit 0 of chunk m = its group summaries are scored
+  long long* counters;
+  int64_t need_split;
 };
 
 template <bool kPipelined, typename GroupEmit, typename RowFn>
@@ -287,7 +294,8 @@ namespace route {
 // ascending groups), by wave 0 or spread over the workgroup; the caller
 // synchronises before reading what it stored. With write_out the item's rows
 // of chunk_idx, group_idx (-1 padding; the kept entries are left to emit) and
-// n_sel are written. Returns the number of kept groups. after_query() is
+// n_sel are written. Returns the number of kept groups (with chunks_only, the
+// number of kept chunks, which are then in sm.chunks). after_query() is
 // called by every thread once the block query is formed (the fused kernel
 // starts its first key/value tile loads there, behind the router's first
 // loads).
@@ -303,7 +311,6 @@ __device__ int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm, bool 
   const int d = S.d;
   const int64_t s = S.q0 + (int64_t)b * S.B;
   const int64_t ms = s / S.c;
-  const int gpc = S.c / S.g;
   const int tid = threadIdx.x, wave = tid >> 6;
 
   // chunk-stage candidates [lo, hi); the first round of their summaries is
@@ -384,7 +391,7 @@ __device__ int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm, bool 
 
   if (write_out && tid == 0) a.n_sel[orow * 2 + 0] = nsc;
   // ---- 4. group stage over the groups of the kept chunks (ascending order)
-  if (a.chunks_only) return 0;
+  if (a.chunks_only) return nsc;
   const int64_t gsplit = a.split / S.g;          // groups held in host memory
   const int64_t ngl = S.kvs / S.g;
   return group_stage<kPipelined>(a, b, h, sm, nsc, write_out, emit, [&](int, int64_t j) -> const float* {
@@ -428,6 +435,73 @@ __device__ int group_stage(const RouteArgs& a, int b, int h, RouteSmem& sm, int 
     if (tid == 0) a.n_sel[orow * 2 + 1] = nsg;
   }
   return nsg;
+}
+
+// Emit function of the router kernels: stores the kept group and, with the
+// persistent cache's marks, sets the group's bit in kv_need when it lies in
+// the history and counts it in *hist (shared memory).
+struct MarkingEmit {
+  int32_t* gout;
+  uint64_t* need;     // the KV head's row of kv_need, or null
+  int g;
+  int64_t split;
+  int* hist;
+  __device__ void operator()(int rank, int group) const {
+    gout[rank] = group;
+    const int64_t tok = (int64_t)group * g;
+    if (need && tok < split) {
+      atomicOr(reinterpret_cast<unsigned long long*>(&need[tok / kChunk]), 1ull << ((tok % kChunk) / g));
+      atomicAdd(hist, 1);
+    }
+  }
+};
+
+// After the group stage of item (b, h) (every thread, after a barrier that
+// follows the emits): mark the item's fixed chunks below need_split as whole
+// chunks in kv_need and add the item's K/V requests (hist kept history
+// groups plus the fixed chunks' groups) to the counters.
+__device__ inline void mark_fixed_chunks(const RouteArgs& a, int b, int h, int hist) {
+  const Shape& S = a.s;
+  const int64_t ms = (S.q0 + (int64_t)b * S.B) / S.c;
+  int64_t fa, fbb;
+  fixed_windows(ms, S.sink_chunks, S.local_chunks, &fa, &fbb);
+  const int64_t nch = a.need_split / kChunk;
+  const int gpc = kChunk / S.g;
+  const uint64_t full = gpc == 64 ? ~0ull : (1ull << gpc) - 1ull;
+  const int nfix = (int)(fa + (ms - fbb));
+  for (int t = threadIdx.x; t < nfix; t += blockDim.x) {
+    const int64_t m = t < fa ? t : fbb + (t - fa);
+    if (m < nch) atomicOr(reinterpret_cast<unsigned long long*>(&a.kv_need[(int64_t)h * nch + m]), full);
+  }
+  if (threadIdx.x == 0) {
+    const int64_t sink_hist = fa < nch ? fa : nch;
+    const int64_t lo = fbb > nch ? nch : fbb, hi = ms > nch ? nch : ms;
+    const long long n = hist + (long long)gpc * (sink_hist + (hi - lo));
+    if (n) atomicAdd(reinterpret_cast<unsigned long long*>(&a.counters[kTcKvRequests]), (unsigned long long)n);
+  }
+}
+
+// After the chunk stage of item h (chunks_only, every thread): when its group
+// stage will score summaries, mark its kept history chunks in gs_need and
+// count them. `count` is a shared-memory int the caller zeroed before a
+// barrier.
+__device__ inline void mark_summary_chunks(const RouteArgs& a, int h, const RouteSmem& sm, int nsc, int* count) {
+  const Shape& S = a.s;
+  const int gpc = kChunk / S.g;
+  if (!(S.kg > 0 && S.kg < nsc * gpc)) return;   // every group kept (or none): no summary is read
+  const int64_t nch = a.need_split / kChunk;
+  int n = 0;
+  for (int i = threadIdx.x; i < nsc; i += blockDim.x) {
+    const int m = sm.chunks[i];
+    if (m >= 0 && m < nch) {
+      atomicOr(reinterpret_cast<unsigned long long*>(&a.gs_need[(int64_t)h * nch + m]), 1ull);
+      ++n;
+    }
+  }
+  if (n) atomicAdd(count, n);
+  __syncthreads();
+  if (threadIdx.x == 0 && *count)
+    atomicAdd(reinterpret_cast<unsigned long long*>(&a.counters[kTcGsRequests]), (unsigned long long)*count);
 }
 
 }  // namespace route

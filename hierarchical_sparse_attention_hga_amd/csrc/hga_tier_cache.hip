@@ -13,15 +13,20 @@
 //   GS slots    the group summaries of one history chunk (all its groups),
 //               read by the group stage.
 // Each kind has a table: the slot of every history chunk (-1: absent), the
-// chunk of every slot (-1: empty), the call that last used each slot, and a
-// ring position. A call marks the chunks (and groups) its query blocks need;
-// one workgroup per KV head stamps the resident ones, gives the absent ones
-// the next slots in ring order that this call does not use (evicting their
-// chunks), and lists what to copy; copy kernels move those rows from pinned
-// host memory into the slots. Every chunk a call needs is resident before
-// its attention runs, so results do not depend on what the cache held.
-// Counters of requests, misses, bytes and evictions accumulate in the
-// cache's first bytes.
+// chunk of every slot (-1: empty), the call that last used each slot, a ring
+// position, and one word per history chunk in which the router marks what
+// the call's query blocks need (group bits for K/V, one bit for summaries).
+// One workgroup per KV head then reads and clears the marks, stamps the
+// resident chunks, gives the absent ones the next slots in ring order that
+// this call does not use (evicting their chunks), and lists what to copy;
+// copy kernels move those rows from pinned host memory into the slots. Every
+// chunk a call needs is resident before its attention reads it, so results
+// do not depend on what the cache held. Counters of requests, misses, bytes
+// and evictions accumulate in the cache's first bytes.
+//
+// With a second stream the K/V copies run there while the attention of the
+// query blocks whose history groups were all resident runs on the call's
+// stream; the other blocks are attended once the copies are done.
 #include "hga_attend_impl.h"
 
 namespace hga {
@@ -45,6 +50,8 @@ size_t tier_cache_layout(const Shape& s, int64_t split, int kv_slots, int gs_slo
   L->gused = o;  o = up(o + hkv * Sg * 4);
   L->gvalid = o; o = up(o + hkv * Sg * 8);
   L->ghand = o;  o = up(o + hkv * 4);
+  L->need = o;   o = up(o + hkv * nch * 8);
+  L->gneed = o;  o = up(o + hkv * nch * 8);
   L->k = o;      o = up(o + hkv * S * kChunk * (size_t)s.d * esz);
   L->v = o;      o = up(o + hkv * S * kChunk * (size_t)s.d * esz);
   L->gs = o;     o = up(o + hkv * Sg * gpc * (size_t)s.d * 4);
@@ -56,13 +63,14 @@ size_t tier_call_layout(const Shape& s, int64_t split, TierCallLayout* W) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t nch = (size_t)(split / kChunk), hkv = (size_t)s.hkv;
   size_t o = 0;
-  W->need = o;   o = up(o + hkv * nch * 8);
-  W->gneed = o;  o = up(o + hkv * nch * 8);
+  W->pend = o;   o = up(o + hkv * nch * 8);
   W->list = o;   o = up(o + hkv * nch * sizeof(CopyEntry));
   W->count = o;  o = up(o + hkv * 4);
   W->glist = o;  o = up(o + hkv * nch * sizeof(CopyEntry));
   W->gcount = o; o = up(o + hkv * 4);
   W->qbar = o;   o = up(o + (size_t)s.nb * hkv * (size_t)s.d * 8);
+  // one flag per attention workgroup (at least 32 query rows each)
+  W->done = o;   o = up(o + (size_t)s.nb * hkv * (size_t)((s.G * s.B + 31) / 32) * 4);
   W->total = o;
   return o;
 }
@@ -78,7 +86,8 @@ struct SlotTable {
   uint64_t* valid;     // [Hkv][S]: groups of the slot's chunk that are present
   int32_t* hand;       // [Hkv]: ring position of the next slot to give out
   int nch, S;
-  const uint64_t* need;   // [Hkv][nch]: groups of each chunk the call needs (0: chunk not needed)
+  uint64_t* need;         // [Hkv][nch]: groups of each chunk the call needs (0: chunk not needed); cleared here
+  uint64_t* pend;         // [Hkv][nch] or null: groups of each needed chunk this call copies
   CopyEntry* list;        // [Hkv][nch]
   int32_t* count;         // [Hkv]
   long long* evictions;   // counter
@@ -89,9 +98,6 @@ __global__ __launch_bounds__(256) void fill_kernel(T* p, int64_t n, T value) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     p[i] = value;
 }
-
-// The call's stamp: the call counter, raised by one.
-__global__ void begin_kernel(long long* counters) { counters[kTcCalls] += 1; }
 
 // Sum of one value per thread over the workgroup, added to *dst by thread 0.
 __device__ void block_add(long long v, long long* dst, long long* lds) {
@@ -107,64 +113,11 @@ __device__ void block_add(long long v, long long* dst, long long* lds) {
   __syncthreads();
 }
 
-// Mark the history groups item (b, h) attends (its usable kept groups and
-// its fixed chunks, below split) in need[h][chunk] as group bits, and count
-// them as requests.
-__global__ __launch_bounds__(256) void mark_kv_kernel(AttnArgs A, uint64_t* need, long long* counters) {
-  __shared__ int sRuns[kMaxRouted];
-  __shared__ int sScan[16];
-  __shared__ long long sSum[4];
-  const Shape& S = A.s;
-  const int h = (int)(blockIdx.x / S.nb), b = (int)(blockIdx.x % S.nb);
-  const Plan P = make_plan(S, b, h, A.gidx, A.nsel, sRuns, sScan, kMaxRouted);
-  uint64_t* nh = need + (int64_t)h * A.nch;
-  const int gpc = kChunk / S.g;
-  const uint64_t full = gpc == 64 ? ~0ull : (1ull << gpc) - 1ull;
-  long long cnt = 0;
-  for (int i = threadIdx.x; i < P.nrouted; i += blockDim.x) {
-    const int tok = sRuns[i];
-    if (tok < A.kv.split) {
-      atomicOr(reinterpret_cast<unsigned long long*>(&nh[tok / kChunk]), 1ull << ((tok % kChunk) / S.g));
-      ++cnt;
-    }
-  }
-  for (int t = threadIdx.x; t < P.nfix; t += blockDim.x) {
-    const int64_t m = t < P.a ? t : P.bb + (t - P.a);
-    if (m < A.nch) {
-      atomicOr(reinterpret_cast<unsigned long long*>(&nh[m]), full);
-      cnt += gpc;
-    }
-  }
-  block_add(cnt, &counters[kTcKvRequests], sSum);
-}
-
-// Mark the history chunks whose group summaries the group stage of item
-// (b, h) scores (its kept chunks below split, when the stage must choose),
-// and count them as requests.
-__global__ __launch_bounds__(64) void mark_gs_kernel(Shape S, int nch, const int32_t* chunk_idx,
-                                                     const int32_t* n_sel, uint64_t* gneed, long long* counters) {
-  const int h = (int)(blockIdx.x / S.nb), b = (int)(blockIdx.x % S.nb);
-  const int64_t row = (int64_t)b * S.hkv + h;
-  int nsc = n_sel[row * 2];
-  nsc = nsc < 0 ? 0 : (nsc > S.kc ? S.kc : nsc);
-  const int gpc = kChunk / S.g;
-  if (!(S.kg > 0 && S.kg < nsc * gpc)) return;   // no group or every group is kept: no summary is read
-  long long cnt = 0;
-  for (int i = threadIdx.x; i < nsc; i += blockDim.x) {
-    const int m = chunk_idx[row * S.kc + i];
-    if (m >= 0 && m < nch) {
-      atomicOr(reinterpret_cast<unsigned long long*>(&gneed[(int64_t)h * nch + m]), 1ull);
-      ++cnt;
-    }
-  }
-  for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
-  if (threadIdx.x == 0 && cnt) atomicAdd(reinterpret_cast<unsigned long long*>(&counters[kTcGsRequests]),
-                                         (unsigned long long)cnt);
-}
-
-// Slot assignment of one KV head (one 1024-thread workgroup per head):
-//  1. every needed chunk with a slot is stamped with this call; the groups
-//     it still lacks go to the copy list;
+// Slot assignment of one KV head (one 1024-thread workgroup per head); the
+// call's stamp is the call counter plus one (the K/V copy kernel raises the
+// counter):
+//  1. every needed chunk (its mark read and cleared) with a slot is stamped
+//     with this call; the groups it still lacks go to the copy list;
 //  2. every needed chunk without a slot takes the next slot in ring order
 //     from the head's ring position that this call does not use (an empty
 //     slot, or the slot of a chunk this call does not need, which is
@@ -178,12 +131,13 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(SlotTable T, con
   __shared__ int sVict[kMaxCand];
   __shared__ long long sSum[16];
   const int h = blockIdx.x, tid = threadIdx.x;
-  const int stamp = (int)counters[kTcCalls];
+  const int stamp = (int)counters[kTcCalls] + 1;
   int32_t* slot = T.slot + (int64_t)h * T.nch;
   int32_t* owner = T.owner + (int64_t)h * T.S;
   int32_t* used = T.used + (int64_t)h * T.S;
   uint64_t* valid = T.valid + (int64_t)h * T.S;
-  const uint64_t* need = T.need + (int64_t)h * T.nch;
+  uint64_t* need = T.need + (int64_t)h * T.nch;
+  uint64_t* pend = T.pend ? T.pend + (int64_t)h * T.nch : nullptr;
   CopyEntry* list = T.list + (int64_t)h * T.nch;
   // 1. needed chunks: hits stamped, their missing groups listed; misses counted
   uint64_t nd[kAssignPer];
@@ -193,6 +147,7 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(SlotTable T, con
   for (int k = 0; k < kAssignPer; ++k) {
     const int m = tid * kAssignPer + k;
     nd[k] = m < T.nch ? need[m] : 0ull;
+    if (nd[k]) need[m] = 0ull;   // the next call's marks start from zero
     sl[k] = nd[k] ? slot[m] : -1;
     if (nd[k] && sl[k] >= 0) {
       used[sl[k]] = stamp;
@@ -238,8 +193,10 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(SlotTable T, con
     if (!nd[k]) continue;
     if (sl[k] >= 0) {
       const uint64_t miss = nd[k] & ~valid[sl[k]];
+      if (pend) pend[m] = miss;
       if (miss) list[pos_fill++] = CopyEntry{m, sl[k], miss};
     } else if (pos_alloc < tot_free) {   // (the host sizes the cache so that this always holds)
+      if (pend) pend[m] = nd[k];
       const int v = sVict[pos_alloc];
       const int old = owner[v];
       if (old >= 0) {
@@ -260,7 +217,8 @@ __global__ __launch_bounds__(kAssignThreads) void assign_kernel(SlotTable T, con
 
 // Copy the listed groups of K and V (g rows each) from pinned host memory
 // into their slots; one workgroup per list entry (grid-stride over the
-// head's list). Every thread issues all its loads before its stores.
+// head's list). Every thread issues all its loads before its stores. The
+// first workgroup raises the call counter (the call's stamp).
 template <typename T>
 __global__ __launch_bounds__(256) void copy_kv_kernel(AttnArgs A, const CopyEntry* list, const int32_t* count,
                                                       uint64_t* valid, int S, long long* counters) {
@@ -271,6 +229,7 @@ __global__ __launch_bounds__(256) void copy_kv_kernel(AttnArgs A, const CopyEntr
   constexpr int EPV = 16 / sizeof(T);             // elements per 16-byte piece
   const int per_group = g * d / EPV;               // pieces per group and tensor
   long long groups = 0;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) counters[kTcCalls] += 1;
   for (int e = blockIdx.x; e < n; e += gridDim.x) {
     const CopyEntry ce = list[(int64_t)h * A.nch + e];
     const int ng = __popcll(ce.mask);
@@ -357,6 +316,7 @@ struct GroupArgs {
 __global__ __launch_bounds__(route::kThreads) void route_groups_kernel(GroupArgs G) {
   __shared__ route::RouteSmem sm;
   __shared__ const float* sBase[kMaxKeptChunks];   // summary row of each kept chunk's first group
+  __shared__ int sMarked;                          // kept history groups marked for the K/V slots
   const route::RouteArgs& a = G.r;
   const Shape& S = a.s;
   const int nwg = (int)(S.nb * S.hkv);
@@ -369,6 +329,7 @@ __global__ __launch_bounds__(route::kThreads) void route_groups_kernel(GroupArgs
   nsc = nsc < 0 ? 0 : (nsc > S.kc ? S.kc : nsc);
   const int64_t gsplit = a.split / S.g;
   const int64_t ngl = S.kvs / S.g;
+  if (threadIdx.x == 0) sMarked = 0;
   for (int i = threadIdx.x; i < d; i += blockDim.x) sm.qbar[i] = G.qbar[row * d + i];
   for (int i = threadIdx.x; i < nsc; i += blockDim.x) {
     const int m = a.chunk_idx[row * S.kc + i];
@@ -379,8 +340,11 @@ __global__ __launch_bounds__(route::kThreads) void route_groups_kernel(GroupArgs
   }
   __syncthreads();
   int32_t* gout = a.group_idx + row * S.kg;
-  route::group_stage<true>(a, b, h, sm, nsc, true, [gout](int rank, int group) { gout[rank] = group; },
+  uint64_t* need = a.kv_need + (int64_t)h * (a.need_split / kChunk);
+  route::group_stage<true>(a, b, h, sm, nsc, true, route::MarkingEmit{gout, need, S.g, a.need_split, &sMarked},
                            [&](int c, int64_t) -> const float* { return sBase[c / gpc] + (int64_t)(c % gpc) * d; });
+  __syncthreads();
+  route::mark_fixed_chunks(a, b, h, sMarked);
 }
 
 }  // namespace
@@ -411,15 +375,19 @@ hipError_t tier_cache_init(const Shape& s, int64_t split, int kv_slots, int gs_s
   fill32(L.gused, hkv * L.Sg, -1);
   fill64(L.gvalid, hkv * L.Sg);
   fill32(L.ghand, hkv, 0);
+  fill64(L.need, hkv * L.nch);
+  fill64(L.gneed, hkv * L.nch);
   return hipGetLastError();
 }
 
 // Routing and attention of one call through the cache (history K/V and
-// group summaries in pinned host memory, split at kv.split).
+// group summaries in pinned host memory, split at kv.split). With copy_st
+// the K/V copies overlap the attention of the items that need none.
 hipError_t launch_route_attend_cached(const Shape& s, const void* q, const float* cs, const float* gs_host,
                                       const float* gs_dev, int64_t gs_split, const KVSrc& kv, int kv_slots,
                                       int gs_slots, void* cache_mem, int32_t* chunk_idx, int32_t* group_idx,
-                                      int32_t* n_sel, void* out, float* lse, void* workspace, hipStream_t st) {
+                                      int32_t* n_sel, void* out, float* lse, void* workspace, hipStream_t st,
+                                      hipStream_t copy_st) {
   const int64_t items = s.nb * s.hkv;
   if (items == 0) return hipSuccess;
   TierCacheLayout L;
@@ -430,30 +398,30 @@ hipError_t launch_route_attend_cached(const Shape& s, const void* q, const float
   char* wb = static_cast<char*>(workspace);
   long long* counters = reinterpret_cast<long long*>(cb);
   const int nch = L.nch;
-  const int64_t nflags = (int64_t)s.hkv * nch;
-  const unsigned fill_blocks = (unsigned)((nflags + 255) / 256 < 4096 ? (nflags + 255) / 256 : 4096);
-  begin_kernel<<<1, 1, 0, st>>>(counters);
+  uint64_t* need = reinterpret_cast<uint64_t*>(cb + L.need);
+  uint64_t* gneed = reinterpret_cast<uint64_t*>(cb + L.gneed);
 
-  // ---- routing; when the group stage must choose, the group summaries of
-  // the kept history chunks go through the cache's GS slots
+  // ---- routing, marking what each item needs; when the group stage must
+  // choose, the group summaries of the kept history chunks go through the
+  // cache's GS slots
   const int gpc = kChunk / s.g;
   const bool groups_choose = s.kg < s.kc * gpc && gs_split > 0;
   route::RouteArgs ra{q, cs, gs_host, gs_dev, gs_split, chunk_idx, group_idx, n_sel, s};
+  ra.counters = counters;
+  ra.need_split = kv.split;
   if (groups_choose) {
     ra.chunks_only = true;
     ra.qbar_out = reinterpret_cast<double*>(wb + W.qbar);
+    ra.gs_need = gneed;
+  } else {
+    ra.kv_need = need;
   }
   hipError_t e = launch_route_args(ra, st);
   if (e != hipSuccess) return e;
   if (groups_choose) {
-    uint64_t* gneed = reinterpret_cast<uint64_t*>(wb + W.gneed);
-    if (nflags > 0)
-      fill_kernel<unsigned long long><<<fill_blocks, 256, 0, st>>>(reinterpret_cast<unsigned long long*>(gneed),
-                                                                   nflags, 0ull);
-    mark_gs_kernel<<<dim3((unsigned)items), dim3(64), 0, st>>>(s, nch, chunk_idx, n_sel, gneed, counters);
     SlotTable G{reinterpret_cast<int32_t*>(cb + L.gslot), reinterpret_cast<int32_t*>(cb + L.gowner),
                 reinterpret_cast<int32_t*>(cb + L.gused), reinterpret_cast<uint64_t*>(cb + L.gvalid),
-                reinterpret_cast<int32_t*>(cb + L.ghand), nch, gs_slots, gneed,
+                reinterpret_cast<int32_t*>(cb + L.ghand), nch, gs_slots, gneed, nullptr,
                 reinterpret_cast<CopyEntry*>(wb + W.glist), reinterpret_cast<int32_t*>(wb + W.gcount),
                 &counters[kTcGsEvictions]};
     assign_kernel<<<dim3((unsigned)s.hkv), dim3(kAssignThreads), 0, st>>>(G, counters);
@@ -464,35 +432,58 @@ hipError_t launch_route_attend_cached(const Shape& s, const void* q, const float
                  nch, gs_slots};
     ga.r.chunks_only = false;
     ga.r.qbar_out = nullptr;
+    ga.r.gs_need = nullptr;
+    ga.r.kv_need = need;
     route_groups_kernel<<<dim3((unsigned)items), dim3(route::kThreads), 0, st>>>(ga);
   }
 
   // ---- the history groups every item attends, through the K/V slots
-  uint64_t* need = reinterpret_cast<uint64_t*>(wb + W.need);
-  if (nflags > 0)
-    fill_kernel<unsigned long long><<<fill_blocks, 256, 0, st>>>(reinterpret_cast<unsigned long long*>(need), nflags,
-                                                                 0ull);
   AttnArgs a{};
   a.kv = kv; a.gidx = group_idx; a.nsel = n_sel; a.s = s; a.nch = nch; a.nslots = kv_slots;
   a.k_cache = cb + L.k;
   a.v_cache = cb + L.v;
-  mark_kv_kernel<<<dim3((unsigned)items), dim3(256), 0, st>>>(a, need, counters);
+  uint64_t* pend = reinterpret_cast<uint64_t*>(wb + W.pend);
   SlotTable T{reinterpret_cast<int32_t*>(cb + L.slot), reinterpret_cast<int32_t*>(cb + L.owner),
               reinterpret_cast<int32_t*>(cb + L.used), reinterpret_cast<uint64_t*>(cb + L.valid),
-              reinterpret_cast<int32_t*>(cb + L.hand), nch, kv_slots, need,
+              reinterpret_cast<int32_t*>(cb + L.hand), nch, kv_slots, need, pend,
               reinterpret_cast<CopyEntry*>(wb + W.list), reinterpret_cast<int32_t*>(wb + W.count),
               &counters[kTcKvEvictions]};
   assign_kernel<<<dim3((unsigned)s.hkv), dim3(kAssignThreads), 0, st>>>(T, counters);
-  if (s.dtype == HGA_BF16)
-    copy_kv_kernel<uint16_t><<<dim3(64, (unsigned)s.hkv), dim3(256), 0, st>>>(a, T.list, T.count, T.valid, kv_slots,
-                                                                               counters);
-  else
-    copy_kv_kernel<float><<<dim3(64, (unsigned)s.hkv), dim3(256), 0, st>>>(a, T.list, T.count, T.valid, kv_slots,
-                                                                            counters);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const TierCache tc{T.slot, nch, kv_slots, a.k_cache, a.v_cache};
-  return launch_attend(s, q, kv, group_idx, n_sel, out, lse, nullptr, 0, st, &tc);
+  auto copy = [&](hipStream_t cs_) {
+    if (s.dtype == HGA_BF16)
+      copy_kv_kernel<uint16_t><<<dim3(64, (unsigned)s.hkv), dim3(256), 0, cs_>>>(a, T.list, T.count, T.valid,
+                                                                                  kv_slots, counters);
+    else
+      copy_kv_kernel<float><<<dim3(64, (unsigned)s.hkv), dim3(256), 0, cs_>>>(a, T.list, T.count, T.valid,
+                                                                               kv_slots, counters);
+    return hipGetLastError();
+  };
+  TierCache tc{T.slot, nch, kv_slots, a.k_cache, a.v_cache, pend, 0, reinterpret_cast<int*>(wb + W.done)};
+  if (!copy_st) {
+    if ((e = copy(st)) != hipSuccess) return e;
+    return launch_attend(s, q, kv, group_idx, n_sel, out, lse, nullptr, 0, st, &tc);
+  }
+  // fork the copies onto copy_st; attend the items that need no copy (pass
+  // 1) meanwhile; join; attend the rest (pass 2)
+  hipEvent_t assigned = nullptr, copied = nullptr;
+  if ((e = hipEventCreateWithFlags(&assigned, hipEventDisableTiming)) != hipSuccess) return e;
+  if ((e = hipEventCreateWithFlags(&copied, hipEventDisableTiming)) != hipSuccess) {
+    (void)hipEventDestroy(assigned);
+    return e;
+  }
+  if ((e = hipEventRecord(assigned, st)) == hipSuccess && (e = hipStreamWaitEvent(copy_st, assigned, 0)) == hipSuccess &&
+      (e = copy(copy_st)) == hipSuccess && (e = hipEventRecord(copied, copy_st)) == hipSuccess) {
+    tc.pass = 1;
+    if ((e = launch_attend(s, q, kv, group_idx, n_sel, out, lse, nullptr, 0, st, &tc)) == hipSuccess &&
+        (e = hipStreamWaitEvent(st, copied, 0)) == hipSuccess) {
+      tc.pass = 2;
+      e = launch_attend(s, q, kv, group_idx, n_sel, out, lse, nullptr, 0, st, &tc);
+    }
+  }
+  // (an event recorded but not yet reached is released once it completes)
+  (void)hipEventDestroy(assigned);
+  (void)hipEventDestroy(copied);
+  return e;
 }
 
 }  // namespace hga

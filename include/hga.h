@@ -344,13 +344,21 @@ hga_status hga_tier_cache_init(const hga_config* cfg, const hga_tier_cache* cach
  *              split, with enough slots for calls of n_q queries (see
  *              hga_tier_cache_min_slots); else HGA_ERR_UNSUPPORTED.
  *   workspace  device, hga_workspace_size(..., HGA_WS_ATTEND_CACHED) bytes.
+ *   copy_stream  NULL, or a stream other than `stream` (default priority):
+ *              the copies of missing K/V groups then run on it while the
+ *              attention of the query blocks (per KV head) that need none of
+ *              them runs on `stream`; the rest are attended once the copies
+ *              are done. Work enqueued on `stream` after the call follows all
+ *              of it; work on copy_stream is not ordered after the call. The
+ *              call creates and destroys two HIP events (no device memory).
+ *              Results do not depend on copy_stream.
  * Other arguments as in hga_route_attend. Calls that share a cache must be
  * ordered (one stream, or the caller's synchronization). */
 hga_status hga_route_attend_cached(const hga_config* cfg, const void* q, int64_t q_start, int64_t n_q,
                                    int64_t seq_len, const float* chunk_sum, const hga_tiered* group_sum,
                                    const hga_tiered* k, const hga_tiered* v, const hga_tier_cache* cache,
                                    int32_t* chunk_idx, int32_t* group_idx, int32_t* n_sel, void* out, float* lse,
-                                   void* workspace, size_t ws_bytes, void* stream);
+                                   void* workspace, size_t ws_bytes, void* stream, void* copy_stream);
 
 /* Forward pass over a whole sequence in segments, in the pages' execution
  * order (section 2.1 with the segment-by-segment processing of section 2.2):

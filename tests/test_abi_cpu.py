@@ -31,7 +31,7 @@ def test_every_declared_entry_point_is_exported(lib):
     assert declared == set(B.EXPORTS)
     for name in declared:
         assert hasattr(lib, name)
-    assert hga.hga_version() == 108
+    assert hga.hga_version() == 109
 
 
 def test_status_strings(lib):
@@ -272,7 +272,8 @@ def test_tier_cache_sizes_and_validation():
     assert hga.hga_tier_cache_size(c, split, 5000, 32) == 2**64 - 1
     assert hga.hga_tier_cache_size(c, 100, 64, 32) == 2**64 - 1
     ws = hga.hga_workspace_size(c, 16384, 64, hga.HGA_WS_ATTEND_CACHED)
-    assert ws >= 8 * nch * (8 + 8 + 16 + 16)
+    # per history chunk and KV head: the copied-groups word and two copy-list entries
+    assert ws >= 8 * nch * (8 + 16 + 16)
     good = hga.tier_cache(FAKE * 16, size, split, 64, 32)
     assert _status(hga.hga_tier_cache_init, c, hga.tier_cache(FAKE + 16, size, split, 64, 32)) == E   # alignment
     assert _status(hga.hga_tier_cache_init, c, hga.tier_cache(FAKE * 16, size - 1, split, 64, 32)) == \
@@ -290,5 +291,6 @@ def test_tier_cache_sizes_and_validation():
                    good, *tail) == E                                            # split differs from the cache's
     assert _status(hga.hga_route_attend_cached, *args, good, FAKE, FAKE, FAKE, FAKE, None, None, 0) == \
         hga.HGA_ERR_WORKSPACE
+    assert _status(hga.hga_route_attend_cached, *args, good, *tail, FAKE * 32, FAKE * 32) == E   # one stream twice
     assert _status(hga.hga_route_attend_cached, *args, good, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1024) == \
         hga.HGA_ERR_WORKSPACE

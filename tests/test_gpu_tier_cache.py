@@ -46,6 +46,7 @@ class Setup:
         kpin, _, self.k_t = split_to_host(self.k, split)
         vpin, _, self.v_t = split_to_host(self.v, split)
         self.pins = [gpin, kpin, vpin]
+        self.side = torch.cuda.Stream()   # copy stream of the overlapped calls (default priority)
 
     def free(self):
         for p in self.pins:
@@ -71,14 +72,14 @@ class Setup:
         torch.cuda.synchronize()
         return fetch(o)
 
-    def cached(self, cache, q_start, n_q):
+    def cached(self, cache, q_start, n_q, overlap=False):
         o = self.outputs(q_start, n_q)
         L = self.cfg["L"]
         wsb = hga.hga_workspace_size(self.c, L, n_q, hga.HGA_WS_ATTEND_CACHED)
         ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
         hga.hga_route_attend_cached(self.c, self.q(q_start, n_q), q_start, n_q, L, self.cs, self.gs_t, self.k_t,
                                     self.v_t, cache, o["chunk_idx"], o["group_idx"], o["n_sel"], o["out"], o["lse"],
-                                    ws, wsb)
+                                    ws, wsb, copy_stream=self.side if overlap else None)
         torch.cuda.synchronize()
         return fetch(o)
 
@@ -158,12 +159,14 @@ def assert_same(a, b, what):
 CALLS = [(2048, 128), (2176, 128), (2048, 128), (3072, 128), (3968, 128), (2048, 128)]
 
 
-@pytest.mark.parametrize("case", ["bf16", "bf16_d64_g4", "f32"])
-def test_cache_across_calls_with_evictions(case):
+@pytest.mark.parametrize("case,overlap", [("bf16", False), ("bf16", True), ("bf16_d64_g4", True), ("f32", True)])
+def test_cache_across_calls_with_evictions(case, overlap):
     """A cache with the fewest slots the calls allow (so chunks are evicted
     between calls), the group stage choosing (its summaries go through the
     cache too): six calls over different query ranges, each bit-identical to
-    the all-HBM call; the counters add up."""
+    the all-HBM call; the counters add up. With overlap the copies run on a
+    second stream while the blocks that need none of them are attended (calls
+    mixing such blocks with others: a repeat, a neighbour)."""
     over = {"bf16": dict(),
             "bf16_d64_g4": dict(d=64, group=4, top_groups=20),
             "f32": dict(dtype="f32", d=64, rope_theta=None)}[case]
@@ -182,9 +185,9 @@ def test_cache_across_calls_with_evictions(case):
         prev = counters(mem, cache)
         assert all(v == 0 for v in prev.values())
         for i, (q0, n) in enumerate(CALLS):
-            print(f"[tier cache] {case} call {i}: queries [{q0}, {q0 + n})", flush=True)
+            print(f"[tier cache] {case} overlap={overlap} call {i}: queries [{q0}, {q0 + n})", flush=True)
             ref = st.hbm(q0, n)
-            got = st.cached(cache, q0, n)
+            got = st.cached(cache, q0, n, overlap)
             assert_same(ref, got, f"{case} call {i}")
             now = counters(mem, cache)
             req = kv_requests(cfg, ref, q0, split)
@@ -202,14 +205,15 @@ def test_cache_across_calls_with_evictions(case):
         st.free()
 
 
-@pytest.mark.parametrize("share", [None, 4])
-def test_cache_64k_layer(share):
+@pytest.mark.parametrize("share,overlap", [(None, False), (4, True)])
+def test_cache_64k_layer(share, overlap):
     """The 64K Qwen3-30B-A3B-shaped layer with its history in pinned host
     memory and a cache of every history chunk: the first call copies each
     distinct history group once (across all query blocks), the second copies
     nothing; both bit-identical to the all-HBM call. With block-varying
     planting (each set of four consecutive query blocks routes to its own
-    chunks) the first call copies more."""
+    chunks) the first call copies more. With overlap, the first call's blocks
+    all wait for the copies and the second call's need none."""
     over = dict(plant_block_share=share) if share else {}
     cfg = synth.config(3, **over)
     x = synth.make_inputs(cfg)
@@ -223,8 +227,8 @@ def test_cache_64k_layer(share):
         mem, cache = make_cache(st, nch, 0)
         ref = st.hbm(q0, n)
         for call in range(2):
-            print(f"[tier cache] 64K share={share} call {call}", flush=True)
-            got = st.cached(cache, q0, n)
+            print(f"[tier cache] 64K share={share} overlap={overlap} call {call}", flush=True)
+            got = st.cached(cache, q0, n, overlap)
             assert_same(ref, got, f"64K call {call}")
             c = counters(mem, cache)
             print(f"  {c}", flush=True)
