@@ -33,7 +33,10 @@ namespace {
 using route::RouteArgs;
 using route::kThreads;
 
-template <typename T>
+// kCache: the persistent cache's variant (block queries kept, chunk stage
+// alone, the history each item needs marked); a kernel of its own, so that
+// the plain router's code and registers are those of the plain path.
+template <typename T, bool kCache>
 __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   __shared__ route::RouteSmem sm;
   __shared__ int sMarked;   // the item's kept history groups (or chunks) marked for the cache
@@ -46,7 +49,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   const int h = lid / (int)S.nb;
   const int b = lid % (int)S.nb;
   int32_t* gout = a.group_idx + ((int64_t)b * S.hkv + h) * S.kg;
-  if (!a.kv_need && !a.gs_need) {
+  if constexpr (!kCache) {
     route::route_item<T, true>(a, b, h, sm, true, [gout](int rank, int group) { gout[rank] = group; });
     return;
   }
@@ -54,7 +57,8 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   // this store before every use)
   if (threadIdx.x == 0) sMarked = 0;
   uint64_t* need = a.kv_need ? a.kv_need + (int64_t)h * (a.need_split / kChunk) : nullptr;
-  const int n = route::route_item<T, true>(a, b, h, sm, true, route::MarkingEmit{gout, need, S.g, a.need_split, &sMarked});
+  const int n = route::route_item<T, true, true>(a, b, h, sm, true,
+                                                 route::MarkingEmit{gout, need, S.g, a.need_split, &sMarked});
   __syncthreads();
   if (a.chunks_only) {
     if (a.gs_need) route::mark_summary_chunks(a, h, sm, n, &sMarked);
@@ -75,10 +79,15 @@ hipError_t launch_route_args(const RouteArgs& a, hipStream_t st) {
   const Shape& s = a.s;
   const int64_t items = s.nb * s.hkv;
   if (items == 0) return hipSuccess;
-  if (s.dtype == HGA_BF16)
-    route_kernel<uint16_t><<<dim3((unsigned)items), dim3(kThreads), 0, st>>>(a);
-  else
-    route_kernel<float><<<dim3((unsigned)items), dim3(kThreads), 0, st>>>(a);
+  const bool cache = a.kv_need || a.gs_need || a.qbar_out || a.chunks_only;
+  const dim3 grid((unsigned)items), block(kThreads);
+  if (s.dtype == HGA_BF16) {
+    if (cache) route_kernel<uint16_t, true><<<grid, block, 0, st>>>(a);
+    else route_kernel<uint16_t, false><<<grid, block, 0, st>>>(a);
+  } else {
+    if (cache) route_kernel<float, true><<<grid, block, 0, st>>>(a);
+    else route_kernel<float, false><<<grid, block, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -278,8 +278,8 @@ struct RouteArgs {
 };
 
 template <bool kPipelined, typename GroupEmit, typename RowFn>
-__device__ int group_stage(const RouteArgs& a, int b, int h, RouteSmem& sm, int nsc, bool write_out,
-                           GroupEmit emit, RowFn gs_row);
+__device__ __attribute__((always_inline)) int group_stage(const RouteArgs& a, int b, int h, RouteSmem& sm, int nsc,
+                                                          bool write_out, GroupEmit emit, RowFn gs_row);
 
 }  // namespace route
 
@@ -294,15 +294,17 @@ namespace route {
 // ascending groups), by wave 0 or spread over the workgroup; the caller
 // synchronises before reading what it stored. With write_out the item's rows
 // of chunk_idx, group_idx (-1 padding; the kept entries are left to emit) and
-// n_sel are written. Returns the number of kept groups (with chunks_only, the
-// number of kept chunks, which are then in sm.chunks). after_query() is
+// n_sel are written. Returns the number of kept groups. kCache enables the
+// persistent cache's options of the arguments (qbar_out, chunks_only: then
+// the number of kept chunks is returned, the chunks in sm.chunks); without
+// it they are ignored and cost nothing. after_query() is
 // called by every thread once the block query is formed (the fused kernel
 // starts its first key/value tile loads there, behind the router's first
 // loads).
 struct NoHook {
   __device__ void operator()() const {}
 };
-template <typename T, bool kPipelined, typename GroupEmit, typename AfterQuery = NoHook>
+template <typename T, bool kPipelined, bool kCache = false, typename GroupEmit, typename AfterQuery = NoHook>
 __device__ int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm, bool write_out, GroupEmit emit,
                           AfterQuery after_query = {}) {
   constexpr int E = Slice<T>::E;
@@ -369,8 +371,9 @@ __device__ int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm, bool 
   }
   after_query();
 
-  if (a.qbar_out && write_out && tid < d)
-    a.qbar_out[((int64_t)b * S.hkv + h) * d + tid] = sm.qbar[tid];
+  if constexpr (kCache) {
+    if (a.qbar_out && write_out && tid < d) a.qbar_out[((int64_t)b * S.hkv + h) * d + tid] = sm.qbar[tid];
+  }
   const int64_t orow = (int64_t)b * S.hkv + h;
   // ---- 2-3. chunk stage
   if (chunk_select) {
@@ -389,18 +392,50 @@ __device__ int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm, bool 
   if (write_out)
     for (int i = tid; i < S.kc; i += kThreads) a.chunk_idx[orow * S.kc + i] = i < nsc ? sm.chunks[i] : -1;
 
-  if (write_out && tid == 0) a.n_sel[orow * 2 + 0] = nsc;
+  if constexpr (kCache) {
+    if (a.chunks_only) {
+      if (write_out && tid == 0) a.n_sel[orow * 2 + 0] = nsc;
+      return nsc;
+    }
+  }
   // ---- 4. group stage over the groups of the kept chunks (ascending order)
-  if (a.chunks_only) return nsc;
-  const int64_t gsplit = a.split / S.g;          // groups held in host memory
-  const int64_t ngl = S.kvs / S.g;
-  return group_stage<kPipelined>(a, b, h, sm, nsc, write_out, emit, [&](int, int64_t j) -> const float* {
-    return j < gsplit ? a.gs_host + ((int64_t)h * gsplit + j) * d
-                      : a.gs_dev + ((int64_t)h * (ngl - gsplit) + (j - gsplit)) * d;
-  });
+  // (written out here rather than through group_stage below: the fused
+  // kernel's registers are allocated better this way, 232 against 744 bytes
+  // of spill space)
+  const int gpc = S.c / S.g;
+  const int ngc = nsc * gpc;
+  const int nsg = ngc < S.kg ? ngc : S.kg;
+  int32_t* gout = a.group_idx + orow * S.kg;   // written only with write_out
+  const int* kept_chunks = sm.chunks;
+  auto group_of = [kept_chunks, gpc](int c) { return kept_chunks[c / gpc] * gpc + c % gpc; };
+  if (nsg > 0 && nsg < ngc) {
+    const int64_t gsplit = a.split / S.g;          // groups held in host memory
+    const int64_t ngl = S.kvs / S.g;
+    auto group_row = [&](int c) -> const float* {
+      const int64_t j = group_of(c);
+      return j < gsplit ? a.gs_host + ((int64_t)h * gsplit + j) * d
+                        : a.gs_dev + ((int64_t)h * (ngl - gsplit) + (j - gsplit)) * d;
+    };
+    ScoreRound g0;
+    load_round(0, d, ngc, group_row, g0);
+    score_rows<kPipelined>(sm.qbar, d, ngc, group_row, sm.key, g0, 0);
+    __syncthreads();
+    if (wave == 0) wave_select(sm.key, ngc, nsg, sm.hist, [emit, group_of](int rank, int pos) { emit(rank, group_of(pos)); });
+  } else {
+    for (int i = tid; i < nsg; i += kThreads) emit(i, group_of(i));
+  }
+  if (write_out) {
+    for (int i = nsg + tid; i < S.kg; i += kThreads) gout[i] = -1;
+    if (tid == 0) {
+      a.n_sel[orow * 2 + 0] = nsc;
+      a.n_sel[orow * 2 + 1] = nsg;
+    }
+  }
+  return nsg;
 }
 
-// Group stage of item (b, h) given its nsc kept chunks (ascending, in
+// Group stage of item (b, h) on its own (the persistent cache's group kernel,
+// after the chunk stage ran alone), given its nsc kept chunks (ascending, in
 // sm.chunks) and its block query (sm.qbar), with all kThreads threads:
 // score the groups of the kept chunks, keep the top_groups (ties to the
 // lower group index), emit them ascending (see route_item), and with
@@ -408,8 +443,8 @@ __device__ int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm, bool 
 // d float32 values of the summary of group j, candidate c (group c % (c/g)
 // of kept chunk c / (c/g)). Returns the number kept.
 template <bool kPipelined, typename GroupEmit, typename RowFn>
-__device__ int group_stage(const RouteArgs& a, int b, int h, RouteSmem& sm, int nsc, bool write_out,
-                           GroupEmit emit, RowFn gs_row) {
+__device__ __attribute__((always_inline)) int group_stage(const RouteArgs& a, int b, int h, RouteSmem& sm, int nsc,
+                                                          bool write_out, GroupEmit emit, RowFn gs_row) {
   const Shape& S = a.s;
   const int d = S.d;
   const int gpc = S.c / S.g;
@@ -421,7 +456,7 @@ __device__ int group_stage(const RouteArgs& a, int b, int h, RouteSmem& sm, int 
   const int* kept_chunks = sm.chunks;
   auto group_of = [kept_chunks, gpc](int c) { return kept_chunks[c / gpc] * gpc + c % gpc; };
   if (nsg > 0 && nsg < ngc) {
-    auto group_row = [&](int c) -> const float* { return gs_row(c, (int64_t)group_of(c)); };
+    auto group_row = [gs_row, group_of](int c) -> const float* { return gs_row(c, (int64_t)group_of(c)); };
     ScoreRound g0;
     load_round(0, d, ngc, group_row, g0);
     score_rows<kPipelined>(sm.qbar, d, ngc, group_row, sm.key, g0, 0);

@@ -342,7 +342,9 @@ __global__ __launch_bounds__(route::kThreads) void route_groups_kernel(GroupArgs
   int32_t* gout = a.group_idx + row * S.kg;
   uint64_t* need = a.kv_need + (int64_t)h * (a.need_split / kChunk);
   route::group_stage<true>(a, b, h, sm, nsc, true, route::MarkingEmit{gout, need, S.g, a.need_split, &sMarked},
-                           [&](int c, int64_t) -> const float* { return sBase[c / gpc] + (int64_t)(c % gpc) * d; });
+                           [gpc, d, base = &sBase[0]](int c, int64_t) -> const float* {
+                             return base[c / gpc] + (int64_t)(c % gpc) * d;
+                           });
   __syncthreads();
   route::mark_fixed_chunks(a, b, h, sMarked);
 }
