@@ -15,7 +15,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhga.so")
 
 HGA_OK, HGA_ERR_INVALID_ARGUMENT, HGA_ERR_UNSUPPORTED, HGA_ERR_WORKSPACE, HGA_ERR_DEVICE = range(5)
-HGA_F32, HGA_BF16 = 0, 1
+HGA_F32, HGA_BF16, HGA_BF16_F32OUT = 0, 1, 2
 HGA_SUMMARY_MEAN = 0
 HGA_WS_ROUTE, HGA_WS_ATTEND, HGA_WS_ATTEND_TIERED, HGA_WS_BACKWARD, HGA_WS_BACKWARD_TIERED = 0, 1, 2, 3, 4
 HGA_WS_ATTEND_CACHED = 5
@@ -139,7 +139,7 @@ def _check(status):
 def make_config(n_q_heads, n_kv_heads, head_dim, top_chunks, top_groups, sink_tokens, local_tokens,
                 dtype="bf16", chunk_size=64, group_size=8, q_block=64, summary_op=HGA_SUMMARY_MEAN,
                 softmax_scale=0.0) -> hga_config:
-    dt = {"bf16": HGA_BF16, "f32": HGA_F32}.get(dtype, dtype)
+    dt = {"bf16": HGA_BF16, "f32": HGA_F32, "bf16_f32out": HGA_BF16_F32OUT}.get(dtype, dtype)
     return hga_config(n_q_heads, n_kv_heads, head_dim, chunk_size, group_size, q_block, top_chunks,
                       top_groups, sink_tokens, local_tokens, summary_op, dt, float(softmax_scale))
 

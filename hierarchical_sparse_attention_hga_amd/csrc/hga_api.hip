@@ -40,8 +40,9 @@ hga_status make_shape(const hga_config* cfg, int64_t seq_len, int64_t q_start, i
   if (cfg->n_q_heads < 1 || cfg->n_kv_heads < 1 || cfg->n_q_heads % cfg->n_kv_heads != 0)
     return fail(HGA_ERR_INVALID_ARGUMENT, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)",
                 cfg->n_q_heads, cfg->n_kv_heads);
-  if (cfg->dtype != HGA_F32 && cfg->dtype != HGA_BF16)
+  if (cfg->dtype != HGA_F32 && cfg->dtype != HGA_BF16 && cfg->dtype != HGA_BF16_F32OUT)
     return fail(HGA_ERR_INVALID_ARGUMENT, "unknown dtype %d", cfg->dtype);
+  const int dt = cfg->dtype == HGA_BF16_F32OUT ? HGA_BF16 : cfg->dtype;   // element type of Q, K, V
   if (cfg->summary_op != HGA_SUMMARY_MEAN)
     return fail(HGA_ERR_INVALID_ARGUMENT, "unknown summary_op %d", cfg->summary_op);
   if (cfg->head_dim < 1) return fail(HGA_ERR_INVALID_ARGUMENT, "head_dim must be positive");
@@ -67,9 +68,9 @@ hga_status make_shape(const hga_config* cfg, int64_t seq_len, int64_t q_start, i
   if (q_start % cfg->q_block || n_q % cfg->q_block)
     return fail(HGA_ERR_UNSUPPORTED, "q_start and n_q must be multiples of q_block (%d)", cfg->q_block);
   const int d = cfg->head_dim;
-  if (cfg->dtype == HGA_BF16 && d != 64 && d != 128)
+  if (dt == HGA_BF16 && d != 64 && d != 128)
     return fail(HGA_ERR_UNSUPPORTED, "bfloat16 needs head_dim 64 or 128 (got %d)", d);
-  if (cfg->dtype == HGA_F32 && !(d == 4 || d == 8 || d == 16 || d == 32 || d == 64 || d == 128))
+  if (dt == HGA_F32 && !(d == 4 || d == 8 || d == 16 || d == 32 || d == 64 || d == 128))
     return fail(HGA_ERR_UNSUPPORTED, "float32 needs head_dim in {4, 8, 16, 32, 64, 128} (got %d)", d);
   if (seq_len / kChunk > kMaxCand)
     return fail(HGA_ERR_UNSUPPORTED, "seq_len above %lld", (long long)kMaxCand * kChunk);
@@ -79,7 +80,7 @@ hga_status make_shape(const hga_config* cfg, int64_t seq_len, int64_t q_start, i
                 kMaxCand);
   if (cfg->top_groups > kMaxRouted)
     return fail(HGA_ERR_UNSUPPORTED, "top_groups above %d", kMaxRouted);
-  if (cfg->dtype == HGA_BF16 && cfg->top_groups > kMaxRoutedAttn)
+  if (dt == HGA_BF16 && cfg->top_groups > kMaxRoutedAttn)
     return fail(HGA_ERR_UNSUPPORTED, "top_groups above %d for bfloat16", kMaxRoutedAttn);
   s->hq = cfg->n_q_heads;
   s->hkv = cfg->n_kv_heads;
@@ -92,7 +93,8 @@ hga_status make_shape(const hga_config* cfg, int64_t seq_len, int64_t q_start, i
   s->kg = cfg->top_groups;
   s->sink_chunks = cfg->sink_tokens / kChunk;
   s->local_chunks = cfg->local_tokens / kChunk;
-  s->dtype = cfg->dtype;
+  s->dtype = dt;
+  s->out_f32 = cfg->dtype == HGA_BF16_F32OUT;
   s->scale = cfg->softmax_scale > 0.0f ? cfg->softmax_scale : 1.0f / sqrtf((float)d);
   s->L = seq_len;
   s->q0 = q_start;
@@ -344,6 +346,7 @@ hga_status hga_stream_forward(const hga_config* cfg, const void* q, const void* 
     return st;
   const hipStream_t hs = (hipStream_t)stream;
   const size_t esz = full.dtype == HGA_BF16 ? 2 : 4;
+  const size_t oesz = full.out_f32 ? 4 : esz;   // output elements
   const hga::KVSrc kv{nullptr, k, nullptr, v, 0};
   for (int64_t s0 = 0; s0 < seq_len; s0 += segment) {
     const int64_t s1 = s0 + segment < seq_len ? s0 + segment : seq_len;
@@ -357,7 +360,7 @@ hga_status hga_stream_forward(const hga_config* cfg, const void* q, const void* 
     seg.qs = seq_len;
     seg.kvs = seq_len;
     const void* qs = static_cast<const char*>(q) + (size_t)s0 * full.d * esz;
-    void* os = static_cast<char*>(out) + (size_t)s0 * full.d * esz;
+    void* os = static_cast<char*>(out) + (size_t)s0 * full.d * oesz;
     float* ls = lse ? lse + s0 : nullptr;
     const int64_t b0 = s0 / full.B;   // first query block of the segment
     int32_t* ci = full.kc > 0 ? chunk_idx + b0 * full.hkv * full.kc : chunk_idx;
@@ -485,6 +488,7 @@ hga_status hga_attend_backward(const hga_config* cfg, const void* q, int64_t q_s
   if (n_q == 0) return ok();
   if (!q || !n_sel || !out || !lse || !dout || !dq || !dk || !dv || (s.kg > 0 && !group_idx))
     return fail(HGA_ERR_INVALID_ARGUMENT, "q, group_idx, n_sel, out, lse, dout, dq, dk and dv must be non-NULL");
+  if (s.out_f32) return fail(HGA_ERR_UNSUPPORTED, "the backward takes the forward's bfloat16 output (dtype HGA_BF16)");
   if ((st = check_aligned("q, out, dout, dq, dk, dv and workspace", {q, out, dout, dq, dk, dv, workspace})) != HGA_OK)
     return st;
   if ((st = check_tier(k, "k", seq_len, q_start)) != HGA_OK) return st;
@@ -518,6 +522,6 @@ const char* hga_status_string(hga_status status) {
 
 const char* hga_last_error(void) { return g_err; }
 
-int32_t hga_version(void) { return 109; }
+int32_t hga_version(void) { return 110; }
 
 }  // extern "C"

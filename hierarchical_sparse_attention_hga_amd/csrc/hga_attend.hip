@@ -323,6 +323,22 @@ __device__ __attribute__((always_inline)) void store_output(const AttnArgs& A, i
   const int head = h * S.G + (row >> lgB);
   const int64_t qrow = (int64_t)b * S.B + (row & (S.B - 1));
 
+  if (S.out_f32) {
+    // float32 output: each lane stores its column's four consecutive values
+    // of each accumulator quarter as they are (16-byte stores)
+    if (active && live) {
+      const float inv = 1.0f / l_tot;
+      float* op = static_cast<float*>(A.out) + ((int64_t)head * S.qs + qrow) * D + 4 * hl;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          *reinterpret_cast<float4*>(op + 32 * db + 8 * jj) =
+              float4{o[db][4 * jj] * inv, o[db][4 * jj + 1] * inv, o[db][4 * jj + 2] * inv, o[db][4 * jj + 3] * inv};
+      if (A.lse && hl == 0) A.lse[(int64_t)head * S.qs + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+    }
+    return;
+  }
   // Output: each wave writes its normalized 32 x D tile to LDS (the stage
   // ring is free once every wave has left the loop), then stores it back
   // row by row, 64 / (D / 8) whole rows per instruction, so every store

@@ -31,7 +31,8 @@ struct Shape {
   int c, g, B;          // chunk, group, query block
   int kc, kg;           // top chunks, top groups
   int sink_chunks, local_chunks;
-  int dtype;            // hga_dtype
+  int dtype;            // element type of Q, K and V (HGA_F32 or HGA_BF16)
+  bool out_f32;         // O in float32 whatever dtype is (HGA_BF16_F32OUT)
   float scale;          // softmax scale (resolved)
   int64_t L, q0, nq, nb;
   int64_t qs;           // rows per head of Q, O and LSE (n_q; more when they cover a longer sequence)

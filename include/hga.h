@@ -74,7 +74,13 @@ typedef enum {
   HGA_ERR_DEVICE = 4             /* a HIP launch or runtime call failed */
 } hga_status;
 
-typedef enum { HGA_F32 = 0, HGA_BF16 = 1 } hga_dtype;
+/* Element types. HGA_BF16_F32OUT takes bfloat16 Q, K and V like HGA_BF16 and
+ * writes the attention output O in float32 (the value before any rounding to
+ * bfloat16: the output a parity check compares with a float64 reference
+ * without the output's own storage rounding). Every entry point that writes
+ * O accepts it (O then has 4-byte elements); hga_attend_backward does not
+ * (HGA_ERR_UNSUPPORTED). The LSE is float32 in every mode. */
+typedef enum { HGA_F32 = 0, HGA_BF16 = 1, HGA_BF16_F32OUT = 2 } hga_dtype;
 
 /* Summary operator. The pages call the chunk summaries "RoPE-aware" without
  * defining them; the mean of the post-RoPE keys is the operator built here. */
@@ -208,7 +214,7 @@ hga_status hga_route(const hga_config* cfg, const void* q, int64_t q_start, int6
  *              row is taken whole.
  *   n_sel      device, [n_q/B][Hkv][2]; the second value (clamped to
  *              [0, top_groups]) is how many entries of the row to read.
- *   out        device, [Hq][n_q][d] of cfg->dtype.
+ *   out        device, [Hq][n_q][d] of cfg->dtype (float32 for HGA_BF16_F32OUT).
  *   lse        device, [Hq][n_q] float32, or NULL.
  *   workspace  device, at least hga_workspace_size(...) bytes (with split 0,
  *              NULL or fewer bytes than HGA_WS_ATTEND asks for is accepted:
@@ -368,7 +374,8 @@ hga_status hga_route_attend_cached(const hga_config* cfg, const void* q, int64_t
  * (hga_route_attend with q_start = s0 and seq_len = the segment's end). The
  * results equal one hga_build_summaries over the sequence followed by one
  * hga_route_attend over all of its queries.
- *   q, out     device, [Hq][seq_len][d] of cfg->dtype (every position queries).
+ *   q, out     device, [Hq][seq_len][d] of cfg->dtype (every position queries; out
+ *              float32 for HGA_BF16_F32OUT).
  *   k, v       device, [Hkv][seq_len][d] of cfg->dtype.
  *   chunk_sum, group_sum   device, as written by hga_build_summaries (every
  *              row is written).

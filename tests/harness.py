@@ -28,14 +28,18 @@ def to_dev(a, dtype):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
 
 
-def hga_cfg(cfg):
+def hga_cfg(cfg, out_f32=False):
+    """The library config of a workload; ``out_f32`` (bfloat16 workloads) asks
+    for the float32 output mode (HGA_BF16_F32OUT)."""
+    assert not out_f32 or cfg["dtype"] == "bf16"
     return hga.make_config(cfg["hq"], cfg["hkv"], cfg["d"], cfg["top_chunks"], cfg["top_groups"],
-                           cfg["sink"], cfg["local"], dtype=cfg["dtype"], group_size=cfg["group"],
+                           cfg["sink"], cfg["local"], dtype="bf16_f32out" if out_f32 else cfg["dtype"],
+                           group_size=cfg["group"],
                            q_block=cfg["q_block"], softmax_scale=cfg.get("softmax_scale") or 0.0)
 
 
 def gpu_run(cfg, x, split=0, group_idx=None, n_sel=None, q_start=None, seq_len=None, fused=False,
-            capacity=None, spread=False):
+            capacity=None, spread=False, out_f32=False):
     """Run summaries, routing and attention through the C ABI.
 
     ``group_idx``/``n_sel`` (numpy, [nb][hkv][kg] / [nb][hkv][2]) replace the
@@ -46,10 +50,11 @@ def gpu_run(cfg, x, split=0, group_idx=None, n_sel=None, q_start=None, seq_len=N
     the summaries of the sequence's whole chunks are built. With ``spread`` the
     call gets the workspace hga_workspace_size(HGA_WS_ATTEND) asks for (asserted
     nonzero), with which calls of few items spread each item's tiles over
-    several workgroups. Returns numpy arrays.
+    several workgroups. With ``out_f32`` the output is written in float32
+    (HGA_BF16_F32OUT). Returns numpy arrays.
     """
     assert not (fused and group_idx is not None)
-    c = hga_cfg(cfg)
+    c = hga_cfg(cfg, out_f32)
     dt = cfg["dtype"]
     L = cfg["L"] if seq_len is None else seq_len
     nq = cfg["n_q"]
@@ -67,7 +72,7 @@ def gpu_run(cfg, x, split=0, group_idx=None, n_sel=None, q_start=None, seq_len=N
     ci = torch.full((nb, hkv, cfg["top_chunks"]), -7, dtype=torch.int32, device=DEV)
     gi = torch.full((nb, hkv, cfg["top_groups"]), -7, dtype=torch.int32, device=DEV)
     ns = torch.full((nb, hkv, 2), -7, dtype=torch.int32, device=DEV)
-    out = torch.empty_like(q)
+    out = torch.empty(q.shape, dtype=torch.float32 if out_f32 else q.dtype, device=DEV)
     lse = torch.empty(cfg["hq"], nq, device=DEV)
     if capacity is not None:
         hga.hga_build_summaries_range(c, k, L, 0, L_seq // 64, gs, cs)

@@ -31,7 +31,7 @@ def test_every_declared_entry_point_is_exported(lib):
     assert declared == set(B.EXPORTS)
     for name in declared:
         assert hasattr(lib, name)
-    assert hga.hga_version() == 109
+    assert hga.hga_version() == 110
 
 
 def test_status_strings(lib):
@@ -235,6 +235,8 @@ def test_backward_validation():
     assert call(c, args[:10] + [None]) == hga.HGA_ERR_WORKSPACE
     assert call(c, args, need - 1) == hga.HGA_ERR_WORKSPACE
     assert call(c, args, need, (14300, 2048, 16384)) == hga.HGA_ERR_UNSUPPORTED
+    # the float32 output mode is forward-only
+    assert call(cfg(dtype="bf16_f32out"), args) == hga.HGA_ERR_UNSUPPORTED
     # tiers: same split for k and v, host memory present, workspace with the cache
     t1, t2 = (FAKE, FAKE, 1024), (FAKE, FAKE, 2048)
     assert call(c, [t1, t2] + args[2:]) == E
@@ -294,3 +296,16 @@ def test_tier_cache_sizes_and_validation():
     assert _status(hga.hga_route_attend_cached, *args, good, *tail, FAKE * 32, FAKE * 32) == E   # one stream twice
     assert _status(hga.hga_route_attend_cached, *args, good, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1024) == \
         hga.HGA_ERR_WORKSPACE
+
+
+def test_float32_output_mode_config():
+    """HGA_BF16_F32OUT is a bfloat16 configuration (same shapes, limits and
+    workspaces) whose output is float32."""
+    a, b = cfg(), cfg(dtype="bf16_f32out")
+    assert b.dtype == hga.HGA_BF16_F32OUT
+    for which in (hga.HGA_WS_ATTEND, hga.HGA_WS_ATTEND_TIERED, hga.HGA_WS_ATTEND_CACHED):
+        assert hga.hga_workspace_size(a, 16384, 2048, which) == hga.hga_workspace_size(b, 16384, 2048, which)
+    assert hga.hga_workspace_size(cfg(dtype=3), 16384, 2048, 0) == 2**64 - 1   # unknown dtype
+    # bfloat16's head sizes
+    assert hga.hga_workspace_size(cfg(dtype="bf16_f32out", head_dim=96), 16384, 2048, 0) == 2**64 - 1
+

@@ -17,8 +17,10 @@ kept sets must in fact equal the oracle's on every item, so attention is
 compared with the oracle's attention over the oracle's own routing. A
 token near the start of the sequence attends a handful of tokens, so its
 output is not averaged down and its own bfloat16 rounding is as large as the
-mean-abs bar: bfloat16 errors are measured beyond that rounding (see
-harness.check_outputs); the LSE, in float32, takes the bar unchanged.
+mean-abs bar: bfloat16 outputs are measured beyond that rounding (see
+harness.check_outputs), and the same cases run again in the float32 output
+mode (HGA_BF16_F32OUT: the output before that rounding), which takes the bars
+unchanged. The LSE, in float32, takes the bar unchanged in both.
 """
 import numpy as np
 import pytest
@@ -44,17 +46,18 @@ def prefix_case(cfg_id, end, B, n_q):
     return cfg, xs, fs, full["L"]
 
 
-def check_case(cfg, x, f, capacity, fused=False, split=0, spread=False):
+def check_case(cfg, x, f, capacity, fused=False, split=0, spread=False, out_f32=False):
     print(f"[decode] {cfg['name']} end={cfg['L']} n_q={cfg['n_q']} B={cfg['q_block']} fused={fused} "
-          f"split={split} spread={spread}", flush=True)
-    gpu = gpu_run(cfg, x, capacity=capacity, fused=fused, split=split, spread=spread)
+          f"split={split} spread={spread} out_f32={out_f32}", flush=True)
+    gpu = gpu_run(cfg, x, capacity=capacity, fused=fused, split=split, spread=spread, out_f32=out_f32)
     ref = oracle_route(cfg, f)
     n, uncert, mism = check_routing(cfg, gpu, ref, f)
     print(f"  items={n} uncertified boundaries={uncert} differing sets={mism}", flush=True)
     assert mism == 0
     items = oracle.all_items(cfg)
     ro, rl = oracle.attend(cfg, f["q"], f["k"], f["v"], items, ref[1], ref[2][:, 1])
-    mx, mean, lerr = check_outputs(cfg, gpu, items, ro, rl, beyond_output_rounding=cfg["dtype"] == "bf16")
+    mx, mean, lerr = check_outputs(cfg, gpu, items, ro, rl,
+                                   beyond_output_rounding=cfg["dtype"] == "bf16" and not out_f32)
     print(f"  max_abs={mx:.3g} mean_abs={mean:.3g} lse={lerr:.3g}", flush=True)
     return gpu
 
@@ -66,6 +69,14 @@ def check_case(cfg, x, f, capacity, fused=False, split=0, spread=False):
 def test_decode_token_qwen3_8b_4k(pos, fused):
     cfg, x, f, cap = prefix_case(1, pos + 1, 1, 1)
     check_case(cfg, x, f, cap, fused=fused)
+
+
+# the same tokens with the output in float32, at the bars unchanged
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("pos", [0, 1, 63, 64, 130, 2047, 4095])
+def test_decode_token_qwen3_8b_4k_f32_output(pos, fused):
+    cfg, x, f, cap = prefix_case(1, pos + 1, 1, 1)
+    check_case(cfg, x, f, cap, fused=fused, out_f32=True)
 
 
 @pytest.mark.parametrize("pos", [14336, 15000, 16383])
@@ -83,6 +94,38 @@ def test_decode_token_64k_device_and_host_tier():
     b = check_case(cfg, x, f, cap, split=64 * (64999 // 64))
     for name in ("chunk_idx", "group_idx", "n_sel", "out", "lse"):
         np.testing.assert_array_equal(a[name], b[name])
+
+
+def bf16_round(a):
+    """float32 values rounded to bfloat16 (to nearest, ties to even), as
+    float64."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+# the float32 output mode through every output path (the one-workgroup
+# kernel, the fused kernel, the spread kernels, the host tier): at the bars
+# unchanged, and each bfloat16 output is its float32 output rounded
+@pytest.mark.parametrize("path", ["attend", "fused", "spread", "host_tier", "block64_fused", "block64_g8"])
+def test_float32_output_mode(path):
+    if path == "host_tier":
+        cfg, x, f, cap = prefix_case(3, 65000, 1, 1)
+        kw = dict(split=64 * (64999 // 64))
+    elif path == "block64_fused":
+        cfg, x, f, cap = prefix_case(1, 4096, 64, 256)
+        kw = dict(fused=True)
+    elif path == "block64_g8":
+        cfg, x, f, cap = prefix_case(3, 65536, 64, 128)
+        kw = {}
+    else:
+        cfg, x, f, cap = prefix_case(1, 2048, 1, 1)
+        kw = dict(fused=path == "fused", spread=path == "spread")
+    a = check_case(cfg, x, f, cap, out_f32=True, **kw)
+    b = gpu_run(cfg, x, capacity=cap, **kw)
+    for name in ("chunk_idx", "group_idx", "n_sel", "lse"):
+        np.testing.assert_array_equal(a[name], b[name])
+    np.testing.assert_array_equal(bf16_round(a["out"]), b["out"])
 
 
 # small blocks (speculative or chunked decoding): several blocks per call,
