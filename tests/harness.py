@@ -187,6 +187,14 @@ def item_rows(cfg, out, items):
     return np.stack([np.stack([out[h * G + r, b * B:(b + 1) * B] for r in range(G)]) for b, h in items])
 
 
+def bf16_round(a):
+    """float32 values rounded to bfloat16 (to nearest, ties to even), as
+    float64."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 def bf16_half_spacing(o):
     """Half the gap from each bfloat16 value to the next one away from zero:
     the most its own round-to-nearest can have moved it."""

@@ -27,7 +27,7 @@ import pytest
 
 import oracle
 import synth
-from harness import check_outputs, check_routing, gpu_run, inputs, oracle_route
+from harness import bf16_round, check_outputs, check_routing, gpu_run, inputs, oracle_route
 
 pytestmark = pytest.mark.gpu
 
@@ -94,14 +94,6 @@ def test_decode_token_64k_device_and_host_tier():
     b = check_case(cfg, x, f, cap, split=64 * (64999 // 64))
     for name in ("chunk_idx", "group_idx", "n_sel", "out", "lse"):
         np.testing.assert_array_equal(a[name], b[name])
-
-
-def bf16_round(a):
-    """float32 values rounded to bfloat16 (to nearest, ties to even), as
-    float64."""
-    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
-    return r.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
 # the float32 output mode through every output path (the one-workgroup

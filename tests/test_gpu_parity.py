@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import synth
-from harness import check_outputs, check_routing, gpu_run, inputs, oracle_route
+from harness import bf16_round, check_outputs, check_routing, gpu_run, inputs, oracle_route
 
 pytestmark = pytest.mark.gpu
 
@@ -58,6 +58,15 @@ def test_routing_and_attention_end_to_end(cfg_id):
     ro, rl = oracle.attend(cfg, f["q"], f["k"], f["v"], items, ref[1][idx], ref[2][idx, 1])
     mx, mean, lerr = check_outputs(cfg, gpu, items, ro, rl)
     print(f"  items={n} max_abs={mx:.3g} mean_abs={mean:.3g} lse={lerr:.3g}", flush=True)
+    if cfg["dtype"] == "bf16":
+        # the float32 output mode: the same bars on the output before its
+        # rounding to bfloat16, which must give the bfloat16 output exactly
+        g32 = gpu_run(cfg, x, out_f32=True)
+        for name in ("chunk_idx", "group_idx", "n_sel", "lse"):
+            np.testing.assert_array_equal(g32[name], gpu[name])
+        mx, mean, lerr = check_outputs(cfg, g32, items, ro, rl)
+        print(f"  float32 output: max_abs={mx:.3g} mean_abs={mean:.3g}", flush=True)
+        np.testing.assert_array_equal(bf16_round(g32["out"]), gpu["out"])
 
 
 @pytest.mark.parametrize("cfg_id", [3, 4])
