@@ -447,10 +447,12 @@ __global__ __launch_bounds__(kAttnThreads) void route_attend_bf16_kernel(FusedAr
   int32_t* gout = F.r.group_idx + ((int64_t)b * S.hkv + h) * S.kg;
   const int g = S.g;
   int* runs = sm.runs;
-  const int nsg = route::route_item<uint16_t, false>(F.r, b, h, rsm, wr, [runs, wr, gout, g](int rank, int group) {
+  auto emit = [runs, wr, gout, g](int rank, int group) {
     runs[rank] = group * g;
     if (wr) gout[rank] = group;
-  }, prefetch);
+  };
+  const int nsg = route::route_item<uint16_t, false, false, decltype(emit), decltype(prefetch), true>(
+      F.r, b, h, rsm, wr, emit, prefetch);
   __syncthreads();
   P.nrouted = nsg;
   P.nrt = (nsg + kChunk / g - 1) / (kChunk / g);
@@ -863,12 +865,15 @@ hipError_t launch_attend(const Shape& s, const void* q, const KVSrc& kv, const i
 // kernel keeps two rounds in flight, the fused kernel (whose registers hold
 // the attention's state) one, and at 64K and beyond the router kernel then
 // attention kernel are faster (measured: 128K 200 -> 183 us, 64K decoding
-// 83 -> 70 us).
+// 83 -> 70 us). Both selections then take at most 512 candidates (two rounds
+// of chunk summaries; the kept chunks' groups are bounded here), which the
+// kernel's inlined selection requires.
 bool fused_route_attend_supported(const Shape& s, int64_t kv_split) {
   const int64_t last_chunk = (s.q0 + s.nq - 1) / kChunk;   // the last block's chunk
   const int64_t candidates = last_chunk - s.sink_chunks - s.local_chunks;
+  static_assert(2 * route::kRoundRows == 512, "the fused kernel's selection bound");
   return s.dtype == HGA_BF16 && kv_split == 0 && (s.d == 128 || s.d == 64) && bf16_wg_per_item(s) == 1 &&
-         candidates <= 2 * route::kRoundRows;
+         candidates <= 2 * route::kRoundRows && (int64_t)s.kc * (kChunk / s.g) <= 512;
 }
 
 hipError_t launch_route_attend(const Shape& s, const void* q, const float* cs, const float* gs_host,

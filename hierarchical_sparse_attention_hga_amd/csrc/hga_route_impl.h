@@ -159,6 +159,19 @@ __device__ void wave_select_kpl(const unsigned long long* key, int n, int k, int
   }
 }
 
+// The same for at most 512 keys (the bound of the fused route-and-attend
+// kernel), with every variant inlined: that kernel then makes no function
+// call, and holds no stack frame (a call from it kept 232 bytes per lane in
+// scratch memory).
+template <typename EmitFn>
+__device__ __attribute__((always_inline)) void wave_select_512(const unsigned long long* key, int n, int k, int* hist,
+                                                               EmitFn emit) {
+  if (n <= 64) wave_select_kpl<1>(key, n, k, hist, emit);
+  else if (n <= 128) wave_select_kpl<2>(key, n, k, hist, emit);
+  else if (n <= 256) wave_select_kpl<4>(key, n, k, hist, emit);
+  else wave_select_kpl<8>(key, n, k, hist, emit);
+}
+
 template <typename EmitFn>
 __device__ void wave_select(const unsigned long long* key, int n, int k, int* hist, EmitFn emit) {
   if (n <= 64) wave_select_kpl<1>(key, n, k, hist, emit);
@@ -181,7 +194,7 @@ struct ScoreRound {
 };
 
 template <typename RowFn>
-__device__ void load_round(int base, int d, int n, RowFn row, ScoreRound& rd) {
+__device__ __attribute__((always_inline)) void load_round(int base, int d, int n, RowFn row, ScoreRound& rd) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane / kLanesPerCand, lic = lane % kLanesPerCand;
   constexpr int per_wave = 64 / kLanesPerCand;
@@ -235,8 +248,8 @@ constexpr int kRoundRows = kRowsInFlight * kWaves * (64 / kLanesPerCand);   // r
 // registers are left to the router kernel: inside the fused kernel they
 // would push the attention's state out to scratch memory).
 template <bool kPipelined, typename RowFn>
-__device__ void score_rows(const double* qbar, int d, int n, RowFn row, unsigned long long* key, ScoreRound& cur,
-                           int from) {
+__device__ __attribute__((always_inline)) void score_rows(const double* qbar, int d, int n, RowFn row,
+                                                          unsigned long long* key, ScoreRound& cur, int from) {
   if (!kPipelined) {
     finish_round(cur, qbar, d, n, key);
     for (int base = from + kRoundRows; base < n; base += kRoundRows) {
@@ -300,13 +313,16 @@ namespace route {
 // it they are ignored and cost nothing. after_query() is
 // called by every thread once the block query is formed (the fused kernel
 // starts its first key/value tile loads there, behind the router's first
-// loads).
+// loads). kSelect512: both selections take at most 512 candidates (the
+// caller checks), so they use wave_select_512 and the item is routed with no
+// function call.
 struct NoHook {
   __device__ void operator()() const {}
 };
-template <typename T, bool kPipelined, bool kCache = false, typename GroupEmit, typename AfterQuery = NoHook>
-__device__ int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm, bool write_out, GroupEmit emit,
-                          AfterQuery after_query = {}) {
+template <typename T, bool kPipelined, bool kCache = false, typename GroupEmit, typename AfterQuery = NoHook,
+          bool kSelect512 = false>
+__device__ __attribute__((always_inline)) int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm,
+                                                         bool write_out, GroupEmit emit, AfterQuery after_query = {}) {
   constexpr int E = Slice<T>::E;
   constexpr int kRowsPerThread = 8;   // block-query rows loaded per thread per round
   const Shape& S = a.s;
@@ -383,8 +399,13 @@ __device__ int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm, bool 
     // capture would keep the captured locals in scratch memory
     int* kept = sm.chunks;
     const int first_cand = (int)lo;
-    if (wave == 0)
-      wave_select(sm.key, ncand, nsc, sm.hist, [kept, first_cand](int rank, int pos) { kept[rank] = first_cand + pos; });
+    if (wave == 0) {
+      auto keep = [kept, first_cand](int rank, int pos) { kept[rank] = first_cand + pos; };
+      if constexpr (kSelect512)
+        wave_select_512(sm.key, ncand, nsc, sm.hist, keep);
+      else
+        wave_select(sm.key, ncand, nsc, sm.hist, keep);
+    }
   } else {
     for (int i = tid; i < nsc; i += kThreads) sm.chunks[i] = (int)(lo + i);
   }
@@ -420,7 +441,13 @@ __device__ int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm, bool 
     load_round(0, d, ngc, group_row, g0);
     score_rows<kPipelined>(sm.qbar, d, ngc, group_row, sm.key, g0, 0);
     __syncthreads();
-    if (wave == 0) wave_select(sm.key, ngc, nsg, sm.hist, [emit, group_of](int rank, int pos) { emit(rank, group_of(pos)); });
+    if (wave == 0) {
+      auto keep = [emit, group_of](int rank, int pos) { emit(rank, group_of(pos)); };
+      if constexpr (kSelect512)
+        wave_select_512(sm.key, ngc, nsg, sm.hist, keep);
+      else
+        wave_select(sm.key, ngc, nsg, sm.hist, keep);
+    }
   } else {
     for (int i = tid; i < nsg; i += kThreads) emit(i, group_of(i));
   }
