@@ -866,14 +866,12 @@ hipError_t launch_attend(const Shape& s, const void* q, const KVSrc& kv, const i
 // the attention's state) one, and at 64K and beyond the router kernel then
 // attention kernel are faster (measured: 128K 200 -> 183 us, 64K decoding
 // 83 -> 70 us). Both selections then take at most 512 candidates (two rounds
-// of chunk summaries; the kept chunks' groups are bounded here), which the
+// of chunk summaries; the kept chunks' groups, bounded as well), which the
 // kernel's inlined selection requires.
 bool fused_route_attend_supported(const Shape& s, int64_t kv_split) {
-  const int64_t last_chunk = (s.q0 + s.nq - 1) / kChunk;   // the last block's chunk
-  const int64_t candidates = last_chunk - s.sink_chunks - s.local_chunks;
-  static_assert(2 * route::kRoundRows == 512, "the fused kernel's selection bound");
+  static_assert(2 * route::kRoundRows == 512, "two rounds of chunk candidates: the fused kernel's selection bound");
   return s.dtype == HGA_BF16 && kv_split == 0 && (s.d == 128 || s.d == 64) && bf16_wg_per_item(s) == 1 &&
-         candidates <= 2 * route::kRoundRows && (int64_t)s.kc * (kChunk / s.g) <= 512;
+         route::select512_fits(s);
 }
 
 hipError_t launch_route_attend(const Shape& s, const void* q, const float* cs, const float* gs_host,

@@ -159,10 +159,9 @@ __device__ void wave_select_kpl(const unsigned long long* key, int n, int k, int
   }
 }
 
-// The same for at most 512 keys (the bound of the fused route-and-attend
-// kernel), with every variant inlined: that kernel then makes no function
-// call, and holds no stack frame (a call from it kept 232 bytes per lane in
-// scratch memory).
+// The same for at most 512 keys, with every variant inlined: the caller
+// then makes no function call and holds no stack frame (a call from the
+// fused route-and-attend kernel kept 232 bytes per lane in scratch memory).
 template <typename EmitFn>
 __device__ __attribute__((always_inline)) void wave_select_512(const unsigned long long* key, int n, int k, int* hist,
                                                                EmitFn emit) {
@@ -241,6 +240,15 @@ __device__ inline void finish_round(const ScoreRound& rd, const double* qbar, in
 }
 
 constexpr int kRoundRows = kRowsInFlight * kWaves * (64 / kLanesPerCand);   // rows per round
+
+// Whether every item of the call selects among at most 512 candidates at
+// both stages (the chunk candidates of the last block, the most any block
+// has; the groups of the kept chunks), so that route_item may take
+// kSelect512.
+inline bool select512_fits(const Shape& s) {
+  const int64_t last_chunk = (s.q0 + s.nq - 1) / kChunk;   // the last block's chunk
+  return last_chunk - s.sink_chunks - s.local_chunks <= 512 && (int64_t)s.kc * (kChunk / s.g) <= 512;
+}
 
 // Rounds from row `from` on (a multiple of kRoundRows), the loads of round
 // `from` already issued into cur. With kPipelined the next round's loads are
