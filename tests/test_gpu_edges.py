@@ -51,6 +51,18 @@ CASES = {
     # 384 groups of 48 kept chunks in two rounds (also inside the fused kernel)
     "chunk_rounds3": dict(L=64 * 700, n_q=128, top_chunks=8, top_groups=24),
     "group_rounds2": dict(L=64 * 80, n_q=128, top_chunks=48, top_groups=100),
+    # the largest selections: the longest sequence the library takes (4,096
+    # chunks; 4,092 chunk candidates, 64 keys per lane in the selecting
+    # wave), 1,500 chunks (32 per lane), and the group stage over 4,096 and
+    # 1,600 groups with the bfloat16 attention's largest group budget
+    "max_seq_len": dict(L=64 * 4096, n_q=64, hq=2, hkv=1, d=64, top_chunks=8, top_groups=24,
+                        n_plant_chunks=8, plant_chunks=(1, 4090)),
+    "candidates_1500": dict(L=64 * 1500, n_q=64, hq=2, hkv=1, d=64, top_chunks=8, top_groups=24,
+                            n_plant_chunks=8, plant_chunks=(1, 1495)),
+    "max_group_candidates": dict(L=64 * 600, n_q=64, hq=2, hkv=1, d=64, top_chunks=512, top_groups=2048,
+                                 n_plant_chunks=8, plant_chunks=(1, 595)),
+    "group_candidates_1600": dict(L=64 * 600, n_q=64, hq=2, hkv=1, d=64, top_chunks=200, top_groups=700,
+                                  n_plant_chunks=8, plant_chunks=(1, 595)),
 }
 
 
