@@ -63,6 +63,13 @@ CASES = {
                                  n_plant_chunks=8, plant_chunks=(1, 595)),
     "group_candidates_1600": dict(L=64 * 600, n_q=64, hq=2, hkv=1, d=64, top_chunks=200, top_groups=700,
                                   n_plant_chunks=8, plant_chunks=(1, 595)),
+    # at the fused kernel's selection bound: 512 chunk and 512 group
+    # candidates (the fused kernel), then one chunk candidate more (the
+    # router kernel, then the attention kernel)
+    "select_bound_512": dict(L=64 * 516, n_q=64, top_chunks=64, top_groups=200, n_plant_chunks=8,
+                             plant_chunks=(1, 510)),
+    "select_bound_513": dict(L=64 * 517, n_q=64, top_chunks=64, top_groups=200, n_plant_chunks=8,
+                             plant_chunks=(1, 510)),
 }
 
 
