@@ -19,9 +19,15 @@ moves each term by at most 2^-8 of its companion term. The bar: beyond each
 value's own storage rounding (half a bf16 spacing), every element's error is
 at most 2^-6 of its companion (four times the first-order bound), and the
 mean error at most 2^-9 of the mean companion. A second bar, on the mean
-error beyond storage rounding (at most 2e-3 of the gradient's RMS; observed up
-to 1.2e-3 at head_dim 64 and 3e-4 to 9e-4 at 128), catches a systematic error
-spread thinly over many elements.
+error beyond storage rounding, catches a systematic error spread thinly over
+many elements: at most 2e-3 of the gradient's RMS. That is the mean error the
+roundings themselves give: a sum of terms c_t each moved by an independent
+relative error uniform within +-2^-8 errs by sum c_t e_t, whose standard
+deviation is 2^-8 / sqrt(3) sqrt(sum c_t^2) and whose mean absolute value is
+sqrt(2 / pi) times that; with terms of both signs sqrt(sum c_t^2) is the size
+of the sum itself in RMS, so the mean error is about 1.8e-3 of the RMS (below
+it once the storage rounding is taken off; observed up to 1.2e-3 at head_dim
+64 and 3e-4 to 9e-4 at 128).
 """
 import numpy as np
 import pytest
