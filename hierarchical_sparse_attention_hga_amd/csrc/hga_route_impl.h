@@ -192,7 +192,17 @@ struct ScoreRound {
   float4 v[kQuadsPerLane][kRowsInFlight];
 };
 
-template <typename RowFn>
+// kFlat (the single-round scoring of the fused route-and-attend kernel): no
+// load depends on a per-lane condition (slots past the last row read the
+// last row, or row 0 of the candidates when there are none; quads past d
+// read the row's first quad; finish_round uses neither; only a slot group
+// with no row for the whole wave skips its loads), and finish_round takes
+// the data through an empty asm. Otherwise the compiler converted each loaded value to float64
+// inside the load's condition, right after the load, so every load waited on
+// its own (one round trip each) and the first round waited before the block
+// query's loads could issue. The router kernel, two rounds in flight, keeps
+// the conditional loads (the flat form slowed it down).
+template <bool kFlat, typename RowFn>
 __device__ __attribute__((always_inline)) void load_round(int base, int d, int n, RowFn row, ScoreRound& rd) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane / kLanesPerCand, lic = lane % kLanesPerCand;
@@ -202,21 +212,40 @@ __device__ __attribute__((always_inline)) void load_round(int base, int d, int n
 #pragma unroll
   for (int u = 0; u < kRowsInFlight; ++u) {
     rd.c[u] = base + u * per_round + wave * per_wave + sub;
-    r[u] = rd.c[u] < n ? row(rd.c[u]) : nullptr;
+    if (kFlat)
+      r[u] = row(rd.c[u] < n ? rd.c[u] : (n > 0 ? n - 1 : 0));
+    else
+      r[u] = rd.c[u] < n ? row(rd.c[u]) : nullptr;
   }
 #pragma unroll
   for (int i = 0; i < kQuadsPerLane; ++i)
 #pragma unroll
     for (int u = 0; u < kRowsInFlight; ++u) {
       const int q4 = lic + i * kLanesPerCand;
-      rd.v[i][u] = float4{0.f, 0.f, 0.f, 0.f};
-      if (r[u] && q4 < d / 4) rd.v[i][u] = *reinterpret_cast<const float4*>(r[u] + 4 * q4);
+      if (kFlat) {
+        // a slot group with no row of the round for this wave skips its loads
+        // (a wave-uniform branch)
+        const int first_row = base + u * per_round + __builtin_amdgcn_readfirstlane(wave) * per_wave;
+        if (first_row < n) rd.v[i][u] = *reinterpret_cast<const float4*>(r[u] + 4 * (q4 < d / 4 ? q4 : 0));
+      } else {
+        rd.v[i][u] = float4{0.f, 0.f, 0.f, 0.f};
+        if (r[u] && q4 < d / 4) rd.v[i][u] = *reinterpret_cast<const float4*>(r[u] + 4 * q4);
+      }
     }
 }
 
-__device__ inline void finish_round(const ScoreRound& rd, const double* qbar, int d, int n,
+template <bool kFlat>
+__device__ inline void finish_round(const ScoreRound& rd_in, const double* qbar, int d, int n,
                                     unsigned long long* key) {
   const int lic = (threadIdx.x & 63) % kLanesPerCand;
+  ScoreRound rd = rd_in;
+  if (kFlat) {
+#pragma unroll
+    for (int i = 0; i < kQuadsPerLane; ++i)
+#pragma unroll
+      for (int u = 0; u < kRowsInFlight; ++u)
+        asm volatile("" : "+v"(rd.v[i][u].x), "+v"(rd.v[i][u].y), "+v"(rd.v[i][u].z), "+v"(rd.v[i][u].w));
+  }
   double acc[kRowsInFlight];
 #pragma unroll
   for (int u = 0; u < kRowsInFlight; ++u) acc[u] = 0.0;
@@ -259,21 +288,21 @@ template <bool kPipelined, typename RowFn>
 __device__ __attribute__((always_inline)) void score_rows(const double* qbar, int d, int n, RowFn row,
                                                           unsigned long long* key, ScoreRound& cur, int from) {
   if (!kPipelined) {
-    finish_round(cur, qbar, d, n, key);
+    finish_round<true>(cur, qbar, d, n, key);
     for (int base = from + kRoundRows; base < n; base += kRoundRows) {
-      load_round(base, d, n, row, cur);
-      finish_round(cur, qbar, d, n, key);
+      load_round<true>(base, d, n, row, cur);
+      finish_round<true>(cur, qbar, d, n, key);
     }
     return;
   }
   ScoreRound nxt;
   for (int base = from; base < n; base += 2 * kRoundRows) {
     const bool more = base + kRoundRows < n;
-    if (more) load_round(base + kRoundRows, d, n, row, nxt);
-    finish_round(cur, qbar, d, n, key);
+    if (more) load_round<false>(base + kRoundRows, d, n, row, nxt);
+    finish_round<false>(cur, qbar, d, n, key);
     if (!more) break;
-    if (base + 2 * kRoundRows < n) load_round(base + 2 * kRoundRows, d, n, row, cur);
-    finish_round(nxt, qbar, d, n, key);
+    if (base + 2 * kRoundRows < n) load_round<false>(base + 2 * kRoundRows, d, n, row, cur);
+    finish_round<false>(nxt, qbar, d, n, key);
   }
 }
 
@@ -349,7 +378,7 @@ __device__ __attribute__((always_inline)) int route_item(const RouteArgs& a, int
   const float* csh = a.cs + (int64_t)h * (S.kvs / S.c) * d;
   auto chunk_row = [&](int c) { return csh + (lo + c) * d; };
   ScoreRound first;
-  if (chunk_select) load_round(0, d, ncand, chunk_row, first);
+  if (!kPipelined || chunk_select) load_round<!kPipelined>(0, d, ncand, chunk_row, first);
 
   // ---- 1. block query (float64)
   {
@@ -446,7 +475,7 @@ __device__ __attribute__((always_inline)) int route_item(const RouteArgs& a, int
                         : a.gs_dev + ((int64_t)h * (ngl - gsplit) + (j - gsplit)) * d;
     };
     ScoreRound g0;
-    load_round(0, d, ngc, group_row, g0);
+    load_round<!kPipelined>(0, d, ngc, group_row, g0);
     score_rows<kPipelined>(sm.qbar, d, ngc, group_row, sm.key, g0, 0);
     __syncthreads();
     if (wave == 0) {
@@ -493,7 +522,7 @@ __device__ __attribute__((always_inline)) int group_stage(const RouteArgs& a, in
   if (nsg > 0 && nsg < ngc) {
     auto group_row = [gs_row, group_of](int c) -> const float* { return gs_row(c, (int64_t)group_of(c)); };
     ScoreRound g0;
-    load_round(0, d, ngc, group_row, g0);
+    load_round<!kPipelined>(0, d, ngc, group_row, g0);
     score_rows<kPipelined>(sm.qbar, d, ngc, group_row, sm.key, g0, 0);
     __syncthreads();
     if (wave == 0) wave_select(sm.key, ngc, nsg, sm.hist, [emit, group_of](int rank, int pos) { emit(rank, group_of(pos)); });
