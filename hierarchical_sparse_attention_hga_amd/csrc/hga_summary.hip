@@ -19,17 +19,18 @@ struct Slice;  // one 16-byte slice of a key row, widened to double
 template <>
 struct Slice<float> {
   static constexpr int E = 4;
-  __device__ static void add(const float* p, double* acc) {
-    const float4 v = *reinterpret_cast<const float4*>(p);
-    acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
+  __device__ static uint4 load(const float* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ static void add(uint4 v, double* acc) {
+    acc[0] += __uint_as_float(v.x); acc[1] += __uint_as_float(v.y);
+    acc[2] += __uint_as_float(v.z); acc[3] += __uint_as_float(v.w);
   }
 };
 
 template <>
 struct Slice<uint16_t> {
   static constexpr int E = 8;
-  __device__ static void add(const uint16_t* p, double* acc) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
+  __device__ static uint4 load(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ static void add(uint4 v, double* acc) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -56,8 +57,18 @@ __global__ __launch_bounds__(1024) void summary_kernel(const T* __restrict__ k, 
     double acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.0;
-#pragma unroll 8
-    for (int t = 0; t < g; ++t) Slice<T>::add(src + (int64_t)t * d, acc);
+    if (g % 8 == 0) {
+      // eight rows' loads issued together, then added in row order
+      for (int t0 = 0; t0 < g; t0 += 8) {
+        uint4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = Slice<T>::load(src + (int64_t)(t0 + j) * d);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) Slice<T>::add(v[j], acc);
+      }
+    } else {
+      for (int t = 0; t < g; ++t) Slice<T>::add(Slice<T>::load(src + (int64_t)t * d), acc);
+    }
     float* dst = gs + (h * (kvs / g) + m * gpc + u) * d + p * E;
 #pragma unroll
     for (int e = 0; e < E; e += 4) {
