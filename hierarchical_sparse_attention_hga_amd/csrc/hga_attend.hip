@@ -68,7 +68,8 @@ constexpr int kPartFloats = (D / 2 + 2) * 64;
 
 template <int D>
 __device__ __attribute__((always_inline)) void store_output(const AttnArgs& A, int b, int h, int z, AttnSmem<D>& sm,
-                                                            const f32x16* o, float m_run, float l_tot);
+                                                            const f32x16* o, float m_run, float l_tot,
+                                                            int free_stage = -1);
 
 // Attention of item (b, h), workgroup slot z, over tiles [ta, te) of the
 // token set of plan P (runs in sm.runs). The caller has loaded the queries
@@ -301,14 +302,16 @@ __device__ __attribute__((always_inline)) void attend_bf16_body(const AttnArgs& 
     }
     return;
   }
-  store_output<D>(A, b, h, z, sm, o, m_run, active ? pair_sum(l_run) : 0.0f);
+  // the stage the last tile did not use is free: no wave reads it any more
+  store_output<D>(A, b, h, z, sm, o, m_run, active ? pair_sum(l_run) : 0.0f, 1 - ((nl - 1) & 1));
 }
 
 // Normalize and store the output rows of item (b, h), slot z, from each
 // wave's O^T accumulators, running maximum and row sum.
 template <int D>
 __device__ __attribute__((always_inline)) void store_output(const AttnArgs& A, int b, int h, int z, AttnSmem<D>& sm,
-                                                            const f32x16* o, float m_run, float l_tot) {
+                                                            const f32x16* o, float m_run, float l_tot,
+                                                            int free_stage) {
   constexpr int NP = D / 8;
   constexpr int RB = D * 2;
   const Shape& S = A.s;
@@ -345,6 +348,47 @@ __device__ __attribute__((always_inline)) void store_output(const AttnArgs& A, i
   // writes contiguous rows instead of 16 bytes of each of 32 rows. Pieces of
   // 16 bytes are XOR-swizzled by row in LDS (conflict-free both ways).
   static_assert(kAttnWaves * 32 * RB <= sizeof(sm.k) + sizeof(sm.v), "output tiles fit in the stage ring");
+  if (free_stage >= 0) {
+    // With one stage known free (after the tile loop), no barrier: each wave
+    // stages its tile through its own quarter of that stage's K or V half,
+    // one half of the head dimension at a time (half rows of D bytes).
+    static_assert(kAttnWaves * 32 * D <= 2 * kChunk * D * 2, "half tiles fit in one stage");
+    if (!active) return;
+    constexpr int NH = D / 16;   // 16-byte pieces per half row
+    const float inv = 1.0f / l_tot;
+    char* tile = (wave < kAttnWaves / 2 ? reinterpret_cast<char*>(&sm.k[free_stage][0])
+                                        : reinterpret_cast<char*>(&sm.v[free_stage][0])) +
+                 (wave % (kAttnWaves / 2)) * (32 * D);
+    uint16_t* outp = static_cast<uint16_t*>(A.out);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int dq = 0; dq < D / 64; ++dq)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int db = half * (D / 64) + dq;
+          bf16x4 v4;
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) v4[ii] = (__bf16)(o[db][4 * jj + ii] * inv);
+          const int piece = 4 * dq + jj;   // of the half row
+          *reinterpret_cast<u32x2*>(tile + col * D + ((piece ^ (col & (NH - 1))) << 4) + 8 * hl) =
+              __builtin_bit_cast(u32x2, v4);
+        }
+      constexpr int RPR = 64 / NH;   // half rows per store instruction
+#pragma unroll
+      for (int i = 0; i < 32 / RPR; ++i) {
+        const int r = i * RPR + lane / NH, pc = lane % NH;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(tile + r * D + ((pc ^ (r & (NH - 1))) << 4));
+        const int R = 32 * rb + r;   // item row
+        if (R < nrows) {
+          const int64_t orow = (int64_t)(h * S.G + (R >> lgB)) * S.qs + (int64_t)b * S.B + (R & (S.B - 1));
+          *reinterpret_cast<u32x4*>(outp + orow * D + half * (D / 2) + pc * 8) = val;
+        }
+      }
+    }
+    if (A.lse && hl == 0 && live) A.lse[(int64_t)head * S.qs + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+    return;
+  }
   __syncthreads();
   if (active) {
     const float inv = 1.0f / l_tot;   // columns past the item's rows are never stored
