@@ -66,10 +66,13 @@ __device__ inline void load_q_operands(const AttnArgs& A, int b, int h, int z, b
 template <int D>
 constexpr int kPartFloats = (D / 2 + 2) * 64;
 
-template <int D>
-__device__ __attribute__((always_inline)) void store_output(const AttnArgs& A, int b, int h, int z, AttnSmem<D>& sm,
+template <int D, int NS>
+__device__ __attribute__((always_inline)) void store_output(const AttnArgs& A, int b, int h, int z, AttnSmem<D, NS>& sm,
                                                             const f32x16* o, float m_run, float l_tot,
                                                             int free_stage = -1);
+
+// No routing inside the attention body: the plan is complete.
+struct NoRoute {};
 
 // Attention of item (b, h), workgroup slot z, over tiles [ta, te) of the
 // token set of plan P (runs in sm.runs). The caller has loaded the queries
@@ -77,11 +80,25 @@ __device__ __attribute__((always_inline)) void store_output(const AttnArgs& A, i
 // (at most kAttnStages), the range's tile i into stage i. With part == NULL
 // the range is the whole set and the output is stored; otherwise each wave
 // leaves its partial state at part + wave * kPartFloats<D>.
-template <int D, bool kTiered>
+//
+// With a router (route(window) routes the item and returns its kept groups
+// after a barrier; the plan then holds only its fixed windows, te is ignored
+// and the range is the whole set): the first fixed tiles are computed while
+// the router's group selection runs (one wave selects, the others would
+// wait). route calls window.scored() before the barrier that follows the
+// group scores (each wave waits for its tile loads there, so the tiles are
+// visible after it) and window.selected() right after the selecting wave is
+// done; there every wave computes the early tiles from the LDS stages
+// without a barrier and without issuing loads. One fixed tile is kept back
+// to run while the first tile after routing loads; with three fixed tiles or
+// more it is tile 2, which loads into a third stage once the chunks are kept
+// (window.chunks_kept()). The order of the tiles is unchanged, so the
+// results equal the separate route and attention calls bit for bit.
+template <int D, bool kTiered, int NS = kAttnStages, typename Route = NoRoute>
 __device__ __attribute__((always_inline)) void attend_bf16_body(const AttnArgs& A, int b, int h, int z,
-                                                                const Plan& P, AttnSmem<D>& sm, int pre_tiles,
+                                                                Plan P, AttnSmem<D, NS>& sm, int pre_tiles,
                                                                 const bf16x8* qpre, int ta, int te,
-                                                                float* part) {
+                                                                float* part, Route route = {}) {
   constexpr int NP = D / 8;
   constexpr int RPI = 64 / NP;
   constexpr int RPW = kChunk / kAttnWaves;
@@ -89,9 +106,10 @@ __device__ __attribute__((always_inline)) void attend_bf16_body(const AttnArgs& 
   constexpr int kPerTile = 2 * KI;            // K and V
   constexpr int kAhead = kAttnStages - 2;     // most tiles in flight beyond t at the top of iteration t
   static_assert(KI >= 1 && kAttnStages >= 2 && kAttnStages <= 4 && kPerTile * kAhead <= 63, "tile shape");
+  constexpr bool kRouted = !std::is_same<Route, NoRoute>::value;
   const Shape& S = A.s;
-  const int nt = P.ntiles;
-  const int nl = te - ta;                    // tiles of the range
+  int nt = P.ntiles;
+  int nl = te - ta;                          // tiles of the range
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5;                  // lane half
@@ -131,14 +149,15 @@ __device__ __attribute__((always_inline)) void attend_bf16_body(const AttnArgs& 
   };
   const int diag0 = (int)(kTiered ? P.c0 - A.kv.split : P.c0);   // source row of the last tile's first slot
   const int dlim = P.dlim;
-  auto issue = [&](int t) {
-    const uint32_t off = (uint32_t)(((t - ta) % kAttnStages) * kChunk * D * 2);
+  auto issue_to = [&](int t, int st) {
+    const uint32_t off = (uint32_t)(st * kChunk * D * 2);
     issue_tile<D, kTiered>(kv, lds_addr(&sm.k[0][0]) + off, lds_addr(&sm.v[0][0]) + off, [&](int i, int sl) -> int {
       if (t < P.nfix) return kTiered ? raw[i] + sl : (int)((t < P.a ? t : P.bb + (t - P.a)) * kChunk) + sl;
       if (t < P.nfix + P.nrt) return run_of(t, sl) < P.nrouted ? raw[i] + (sl & ((1 << lg) - 1)) : 0;
       return diag0 + (sl < dlim ? sl : 0);   // empty slots past the block read the chunk's first row
     });
   };
+  auto issue = [&](int t) { issue_to(t, (t - ta) % kAttnStages); };
 
   const float sl2 = S.scale * kLog2e;
   float m_run = -INFINITY, l_run = 0.0f;
@@ -175,31 +194,10 @@ __device__ __attribute__((always_inline)) void attend_bf16_body(const AttnArgs& 
   // pre_tiles among them). At iteration t, once tile t has landed, tile
   // t + kAttnStages - 1 goes into the stage tile t - 1 left; the run-table
   // entries of the next tile to issue are always read one issue ahead.
-  for (int u = 0; u < kAttnStages - 1 && u < nl; ++u)
-    if (u >= pre_tiles) {
-      fetch(ta + u);
-      issue(ta + u);
-    }
-  fetch(ta + kAttnStages - 1);
   // One tile per call; the stage is a compile-time constant (the loop below
   // takes the tiles two at a time), so it folds into the LDS reads' offsets.
   static_assert(kAttnStages == 2, "the tile loop alternates two stages");
-  auto step = [&](int i, auto stage_c) __attribute__((always_inline)) {
-    const int t = ta + i;   // tile i of the range
-    // this thread's loads of tile t are done once only newer tiles are pending
-    const int ahead = nl - 1 - i < kAhead ? nl - 1 - i : kAhead;
-    if (kAhead >= 2 && ahead >= 2)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPerTile));
-    else if (kAhead >= 1 && ahead >= 1)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPerTile));
-    else
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();   // every wave's loads of tile t landed; tile t - 1 is free
-    if (i + kAttnStages - 1 < nl) {
-      if (i + kAttnStages - 1 >= pre_tiles) issue(t + kAttnStages - 1);
-      fetch(t + kAttnStages);
-    }
-    if (!active) return;
+  auto compute = [&](int t, auto stage_c) __attribute__((always_inline)) {
     constexpr uint32_t stage = (uint32_t)(decltype(stage_c)::value * kChunk * RB);
     const char* kt = sKb + stage;
     const char* vt = sVb + stage;
@@ -286,7 +284,83 @@ __device__ __attribute__((always_inline)) void attend_bf16_body(const AttnArgs& 
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfa[tb][db][mm], pf[mm], o[db], 0, 0, 0);
     }
   };
-  for (int i = 0; i < nl; i += 2) {
+
+  int i0 = 0;   // tiles of the range already computed
+  if constexpr (kRouted) {
+    static_assert(!kTiered && NS == 3, "the routing body reads device rows and has a third stage");
+    // fixed tiles [0, nearly) run in the group selection's window; the
+    // caller issued tiles [0, pre_tiles), one per stage. A fixed tile is
+    // kept back to run while the first tile after routing loads: with three
+    // fixed tiles or more, tile 2 loads into the third stage once the chunks
+    // are kept (its loads then come before the group summaries').
+    int nearly = P.nfix - 1 < pre_tiles ? P.nfix - 1 : pre_tiles;
+    nearly = nearly > 0 ? nearly : 0;
+    const bool third = nearly == 2;
+    P.nrouted = 0;
+    P.nrt = 0;
+    P.ntiles = P.nfix + 1;   // only fixed tiles are computed before routing ends
+    nt = P.ntiles;
+    auto chunks_kept = [&]() __attribute__((always_inline)) {
+      if (third) issue_to(ta + 2, 2);
+    };
+    auto scored = [nearly]() __attribute__((always_inline)) {
+      if (nearly > 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    };
+    auto selected = [&]() __attribute__((always_inline)) {
+      if (!active) return;
+      if (nearly > 0) compute(0, std::integral_constant<int, 0>{});
+      if (nearly > 1) compute(1, std::integral_constant<int, 1>{});
+    };
+    const int nsg = route(route::EarlyWindow<decltype(chunks_kept), decltype(scored), decltype(selected)>{
+        chunks_kept, scored, selected});
+    P.nrouted = nsg;
+    P.nrt = (nsg + kChunk / S.g - 1) / (kChunk / S.g);
+    P.ntiles = P.nfix + P.nrt + 1;
+    nt = P.ntiles;
+    nl = nt;
+    i0 = nearly;
+    if (third) {
+      // route returned after a barrier: stage 1 is free; tile 2 has landed
+      // (the group scores waited for it) and every wave saw it at the
+      // barrier before the group selection
+      fetch(ta + 3);
+      issue(ta + 3);
+      fetch(ta + 4);
+      if (active) compute(ta + 2, std::integral_constant<int, 2>{});
+      i0 = 3;
+      pre_tiles = 4;
+    }
+  }
+  for (int u = i0; u < i0 + kAttnStages - 1 && u < nl; ++u)
+    if (u >= pre_tiles) {
+      fetch(ta + u);
+      issue(ta + u);
+    }
+  fetch(ta + i0 + kAttnStages - 1);
+  auto step = [&](int i, auto stage_c) __attribute__((always_inline)) {
+    const int t = ta + i;   // tile i of the range
+    // this thread's loads of tile t are done once only newer tiles are pending
+    const int ahead = nl - 1 - i < kAhead ? nl - 1 - i : kAhead;
+    if (kAhead >= 2 && ahead >= 2)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPerTile));
+    else if (kAhead >= 1 && ahead >= 1)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPerTile));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();   // every wave's loads of tile t landed; tile t - 1 is free
+    if (i + kAttnStages - 1 < nl) {
+      if (i + kAttnStages - 1 >= pre_tiles) issue(t + kAttnStages - 1);
+      fetch(t + kAttnStages);
+    }
+    if (!active) return;
+    compute(t, stage_c);
+  };
+  int i = i0;
+  if (i & 1) {
+    step(i, std::integral_constant<int, 1>{});
+    ++i;
+  }
+  for (; i < nl; i += 2) {
     step(i, std::integral_constant<int, 0>{});
     if (i + 1 < nl) step(i + 1, std::integral_constant<int, 1>{});
   }
@@ -308,8 +382,8 @@ __device__ __attribute__((always_inline)) void attend_bf16_body(const AttnArgs& 
 
 // Normalize and store the output rows of item (b, h), slot z, from each
 // wave's O^T accumulators, running maximum and row sum.
-template <int D>
-__device__ __attribute__((always_inline)) void store_output(const AttnArgs& A, int b, int h, int z, AttnSmem<D>& sm,
+template <int D, int NS>
+__device__ __attribute__((always_inline)) void store_output(const AttnArgs& A, int b, int h, int z, AttnSmem<D, NS>& sm,
                                                             const f32x16* o, float m_run, float l_tot,
                                                             int free_stage) {
   constexpr int NP = D / 8;
@@ -463,7 +537,7 @@ struct FusedArgs {
 template <int D>
 __global__ __launch_bounds__(kAttnThreads) void route_attend_bf16_kernel(FusedArgs F) {
   static_assert(kAttnThreads == route::kThreads, "one workgroup size for both phases");
-  __shared__ AttnSmem<D> sm;
+  __shared__ AttnSmem<D, 3> sm;
   __shared__ route::RouteSmem rsm;
   const Shape& S = F.a.s;
   int b, h, z;
@@ -495,13 +569,13 @@ __global__ __launch_bounds__(kAttnThreads) void route_attend_bf16_kernel(FusedAr
     runs[rank] = group * g;
     if (wr) gout[rank] = group;
   };
-  const int nsg = route::route_item<uint16_t, false, false, decltype(emit), decltype(prefetch), true>(
-      F.r, b, h, rsm, wr, emit, prefetch);
-  __syncthreads();
-  P.nrouted = nsg;
-  P.nrt = (nsg + kChunk / g - 1) / (kChunk / g);
-  P.ntiles = P.nfix + P.nrt + 1;
-  attend_bf16_body<D, false>(F.a, b, h, z, P, sm, pre, qf, 0, P.ntiles, nullptr);
+  auto route = [&](auto window) __attribute__((always_inline)) -> int {
+    const int nsg = route::route_item<uint16_t, false, false, decltype(emit), decltype(prefetch), true,
+                                      decltype(window)>(F.r, b, h, rsm, wr, emit, prefetch, window);
+    __syncthreads();
+    return nsg;
+  };
+  attend_bf16_body<D, false, 3>(F.a, b, h, z, P, sm, pre, qf, 0, 0, nullptr, route);
 }
 
 // ------------------------------------------------------------ split items

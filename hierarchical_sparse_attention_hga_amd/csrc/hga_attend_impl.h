@@ -361,13 +361,14 @@ __device__ inline float pair_sum(float x) {
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
-// Shared memory of the bfloat16 attention: the K and V stage rings, the
-// item's routed run list and, after it, the fixed chunks' source rows of the
-// host-tier path.
-template <int D>
+// Shared memory of the bfloat16 attention: the K and V stage rings (NS
+// stages: the loop's two, and a third in the fused route-and-attend kernel
+// for a fixed tile that loads during routing), the item's routed run list
+// and, after it, the fixed chunks' source rows of the host-tier path.
+template <int D, int NS = kAttnStages>
 struct AttnSmem {
-  uint16_t k[kAttnStages][kChunk * D];
-  uint16_t v[kAttnStages][kChunk * D];
+  uint16_t k[NS][kChunk * D];
+  uint16_t v[NS][kChunk * D];
   int runs[kMaxRoutedAttn + kMaxFixedTiered];
   int scan[16];
 };

@@ -356,10 +356,33 @@ namespace route {
 struct NoHook {
   __device__ void operator()() const {}
 };
+// Hooks for work that needs no routing (the fused kernel's first attention
+// tiles): chunks_kept() runs after the barrier that follows the chunk
+// selection; scored() before the barrier after the group scores, and
+// selected() once the wave selecting the groups is done (every other wave
+// reaches it right after that barrier). With no group selection the window
+// still has that barrier. NoWindow has no hooks and adds no barrier.
+struct NoWindow {
+  static constexpr bool kActive = false;
+  __device__ void chunks_kept() const {}
+  __device__ void scored() const {}
+  __device__ void selected() const {}
+};
+template <typename F1, typename F2, typename F3>
+struct EarlyWindow {
+  static constexpr bool kActive = true;
+  F1 f1;
+  F2 f2;
+  F3 f3;
+  __device__ __attribute__((always_inline)) void chunks_kept() const { f1(); }
+  __device__ __attribute__((always_inline)) void scored() const { f2(); }
+  __device__ __attribute__((always_inline)) void selected() const { f3(); }
+};
 template <typename T, bool kPipelined, bool kCache = false, typename GroupEmit, typename AfterQuery = NoHook,
-          bool kSelect512 = false>
+          bool kSelect512 = false, typename Window = NoWindow>
 __device__ __attribute__((always_inline)) int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm,
-                                                         bool write_out, GroupEmit emit, AfterQuery after_query = {}) {
+                                                         bool write_out, GroupEmit emit, AfterQuery after_query = {},
+                                                         Window window = {}) {
   constexpr int E = Slice<T>::E;
   constexpr int kRowsPerThread = 8;   // block-query rows loaded per thread per round
   const Shape& S = a.s;
@@ -447,6 +470,7 @@ __device__ __attribute__((always_inline)) int route_item(const RouteArgs& a, int
     for (int i = tid; i < nsc; i += kThreads) sm.chunks[i] = (int)(lo + i);
   }
   __syncthreads();
+  window.chunks_kept();
   if (write_out)
     for (int i = tid; i < S.kc; i += kThreads) a.chunk_idx[orow * S.kc + i] = i < nsc ? sm.chunks[i] : -1;
 
@@ -477,6 +501,7 @@ __device__ __attribute__((always_inline)) int route_item(const RouteArgs& a, int
     ScoreRound g0;
     load_round<!kPipelined>(0, d, ngc, group_row, g0);
     score_rows<kPipelined>(sm.qbar, d, ngc, group_row, sm.key, g0, 0);
+    window.scored();
     __syncthreads();
     if (wave == 0) {
       auto keep = [emit, group_of](int rank, int pos) { emit(rank, group_of(pos)); };
@@ -487,7 +512,12 @@ __device__ __attribute__((always_inline)) int route_item(const RouteArgs& a, int
     }
   } else {
     for (int i = tid; i < nsg; i += kThreads) emit(i, group_of(i));
+    if constexpr (Window::kActive) {
+      window.scored();
+      __syncthreads();
+    }
   }
+  window.selected();
   if (write_out) {
     for (int i = nsg + tid; i < S.kg; i += kThreads) gout[i] = -1;
     if (tid == 0) {
