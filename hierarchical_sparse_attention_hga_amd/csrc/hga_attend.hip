@@ -122,10 +122,12 @@ __device__ __attribute__((always_inline)) void attend_bf16_body(const AttnArgs& 
   const int row = 32 * rb + col;
   const int qi = row & (S.B - 1);            // position within the block
 
-  // queries of this lane's column, loaded by the caller (load_q_operands)
+  // queries of this lane's column, loaded by the caller (load_q_operands),
+  // or with a router once the router's first loads are issued
   bf16x8 qf[D / 16];
+  if constexpr (!kRouted)
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) qf[ks] = qpre[ks];
+    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = qpre[ks];
 
   const int lg = __ffs(S.g) - 1;
   const KVRows kv = kv_rows<D, kTiered>(A, h);
@@ -311,8 +313,9 @@ __device__ __attribute__((always_inline)) void attend_bf16_body(const AttnArgs& 
       if (nearly > 0) compute(0, std::integral_constant<int, 0>{});
       if (nearly > 1) compute(1, std::integral_constant<int, 1>{});
     };
-    const int nsg = route(route::EarlyWindow<decltype(chunks_kept), decltype(scored), decltype(selected)>{
-        chunks_kept, scored, selected});
+    auto queries_issued = [&]() __attribute__((always_inline)) { load_q_operands<D>(A, b, h, z, qf); };
+    const int nsg = route(route::EarlyWindow<decltype(queries_issued), decltype(chunks_kept), decltype(scored),
+                                             decltype(selected)>{queries_issued, chunks_kept, scored, selected});
     P.nrouted = nsg;
     P.nrt = (nsg + kChunk / S.g - 1) / (kChunk / S.g);
     P.ntiles = P.nfix + P.nrt + 1;
@@ -544,9 +547,6 @@ __global__ __launch_bounds__(kAttnThreads) void route_attend_bf16_kernel(FusedAr
   item_of_block(S, F.a.wg_per_item, &b, &h, &z);
   Plan P;
   plan_windows(S, b, &P);
-  // the attention's query operands load while the router runs
-  bf16x8 qf[D / 16];
-  load_q_operands<D>(F.a, b, h, z, qf);
   // fixed tiles need no routing: the first two (one per stage) load while
   // the router runs, once its block query is formed (issued earlier, the
   // tiles' bytes delayed the router's first loads)
@@ -575,7 +575,7 @@ __global__ __launch_bounds__(kAttnThreads) void route_attend_bf16_kernel(FusedAr
     __syncthreads();
     return nsg;
   };
-  attend_bf16_body<D, false, 3>(F.a, b, h, z, P, sm, pre, qf, 0, 0, nullptr, route);
+  attend_bf16_body<D, false, 3>(F.a, b, h, z, P, sm, pre, nullptr, 0, 0, nullptr, route);
 }
 
 // ------------------------------------------------------------ split items

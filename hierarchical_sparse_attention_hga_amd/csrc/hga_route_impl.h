@@ -202,7 +202,7 @@ struct ScoreRound {
 // its own (one round trip each) and the first round waited before the block
 // query's loads could issue. The router kernel, two rounds in flight, keeps
 // the conditional loads (the flat form slowed it down).
-template <bool kFlat, typename RowFn>
+template <bool kFlat, bool kSkipEmpty = true, typename RowFn>
 __device__ __attribute__((always_inline)) void load_round(int base, int d, int n, RowFn row, ScoreRound& rd) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane / kLanesPerCand, lic = lane % kLanesPerCand;
@@ -226,7 +226,8 @@ __device__ __attribute__((always_inline)) void load_round(int base, int d, int n
         // a slot group with no row of the round for this wave skips its loads
         // (a wave-uniform branch)
         const int first_row = base + u * per_round + __builtin_amdgcn_readfirstlane(wave) * per_wave;
-        if (first_row < n) rd.v[i][u] = *reinterpret_cast<const float4*>(r[u] + 4 * (q4 < d / 4 ? q4 : 0));
+        if (!kSkipEmpty || first_row < n)
+          rd.v[i][u] = *reinterpret_cast<const float4*>(r[u] + 4 * (q4 < d / 4 ? q4 : 0));
       } else {
         rd.v[i][u] = float4{0.f, 0.f, 0.f, 0.f};
         if (r[u] && q4 < d / 4) rd.v[i][u] = *reinterpret_cast<const float4*>(r[u] + 4 * q4);
@@ -356,24 +357,29 @@ namespace route {
 struct NoHook {
   __device__ void operator()() const {}
 };
-// Hooks for work that needs no routing (the fused kernel's first attention
-// tiles): chunks_kept() runs after the barrier that follows the chunk
+// Hooks for work that needs no routing (the fused kernel's query operands
+// and first attention tiles): queries_issued() runs once the block query's
+// first rows and the first round of chunk summaries are requested;
+// chunks_kept() runs after the barrier that follows the chunk
 // selection; scored() before the barrier after the group scores, and
 // selected() once the wave selecting the groups is done (every other wave
 // reaches it right after that barrier). With no group selection the window
 // still has that barrier. NoWindow has no hooks and adds no barrier.
 struct NoWindow {
   static constexpr bool kActive = false;
+  __device__ void queries_issued() const {}
   __device__ void chunks_kept() const {}
   __device__ void scored() const {}
   __device__ void selected() const {}
 };
-template <typename F1, typename F2, typename F3>
+template <typename F0, typename F1, typename F2, typename F3>
 struct EarlyWindow {
   static constexpr bool kActive = true;
+  F0 f0;
   F1 f1;
   F2 f2;
   F3 f3;
+  __device__ __attribute__((always_inline)) void queries_issued() const { f0(); }
   __device__ __attribute__((always_inline)) void chunks_kept() const { f1(); }
   __device__ __attribute__((always_inline)) void scored() const { f2(); }
   __device__ __attribute__((always_inline)) void selected() const { f3(); }
@@ -400,30 +406,59 @@ __device__ __attribute__((always_inline)) int route_item(const RouteArgs& a, int
   const bool chunk_select = nsc > 0 && nsc < ncand;
   const float* csh = a.cs + (int64_t)h * (S.kvs / S.c) * d;
   auto chunk_row = [&](int c) { return csh + (lo + c) * d; };
+  // block-query rows: thread (p, ph) sums 16-byte slice p of rows ph,
+  // ph + phases, ...; with a window the first kRowsPerThread of them load
+  // before the first round of chunk summaries, unconditionally (rows past
+  // the item read its last row and count as zero), so the block query waits
+  // for its own rows only
+  const int P = d / E;                       // 16-byte slices per row
+  const int phases = kThreads / P;
+  const int p = tid % P, ph = tid / P;
+  const int nrows = S.G * S.B;
+  const T* qbase = static_cast<const T*>(a.q);
+  auto q_slice = [&](int rr) {
+    const int64_t row = (int64_t)(h * S.G + rr / S.B) * S.qs + (s - S.q0) + rr % S.B;
+    return reinterpret_cast<const uint4*>(qbase + row * d + p * E);
+  };
+  uint4 v0[kRowsPerThread];
+  if constexpr (Window::kActive) {
+#pragma unroll
+    for (int u = 0; u < kRowsPerThread; ++u) {
+      const int rr = ph + u * phases;
+      v0[u] = *q_slice(rr < nrows ? rr : nrows - 1);
+    }
+  }
   ScoreRound first;
-  if (!kPipelined || chunk_select) load_round<!kPipelined>(0, d, ncand, chunk_row, first);
+  // (with a window, no branch around them either: the compiler's waits for
+  // the block query's rows would then count every later load as pending)
+  if (!kPipelined || chunk_select) load_round<!kPipelined, !Window::kActive>(0, d, ncand, chunk_row, first);
+  window.queries_issued();
 
   // ---- 1. block query (float64)
   {
-    const int P = d / E;                       // 16-byte slices per row
-    const int phases = kThreads / P;
-    const int p = tid % P, ph = tid / P;
     double* part = reinterpret_cast<double*>(sm.key);   // [waves][d]
-    const int nrows = S.G * S.B;
-    const T* qbase = static_cast<const T*>(a.q);
     double acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.0;
-    for (int r = ph; r < nrows; r += kRowsPerThread * phases) {
+    int r0 = ph;
+    if constexpr (Window::kActive) {
+#pragma unroll
+      for (int u = 0; u < kRowsPerThread; ++u) {
+        // the rows in registers as loaded (otherwise the compiler copies
+        // them under the row condition and waits for every later load too)
+        asm volatile("" : "+v"(v0[u].x), "+v"(v0[u].y), "+v"(v0[u].z), "+v"(v0[u].w));
+        const unsigned keep = ph + u * phases < nrows ? 0xffffffffu : 0u;
+        Slice<T>::add(uint4{v0[u].x & keep, v0[u].y & keep, v0[u].z & keep, v0[u].w & keep}, acc);
+      }
+      r0 += kRowsPerThread * phases;
+    }
+    for (int r = r0; r < nrows; r += kRowsPerThread * phases) {
       uint4 v[kRowsPerThread];
 #pragma unroll
       for (int u = 0; u < kRowsPerThread; ++u) {
         const int rr = r + u * phases;
         v[u] = uint4{0u, 0u, 0u, 0u};
-        if (rr < nrows) {
-          const int64_t row = (int64_t)(h * S.G + rr / S.B) * S.qs + (s - S.q0) + rr % S.B;
-          v[u] = *reinterpret_cast<const uint4*>(qbase + row * d + p * E);
-        }
+        if (rr < nrows) v[u] = *q_slice(rr);
       }
 #pragma unroll
       for (int u = 0; u < kRowsPerThread; ++u) Slice<T>::add(v[u], acc);
