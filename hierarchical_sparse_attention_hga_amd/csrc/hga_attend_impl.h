@@ -181,27 +181,36 @@ __device__ inline int tile_limit(const Plan& P, int g, int t) {
 __device__ inline bool translate_plan(int64_t split, int nch, int nslots, const int32_t* slot, int h, const Plan& P,
                                       int* runs, int* fixsrc, int g = 8, const uint64_t* pending = nullptr,
                                       int pass = 0, int* done = nullptr) {
-  auto enc = [&](int64_t tok) -> int {
-    if (tok < split) {
-      const int64_t m = tok / kChunk;
-      const int sl = slot[(int64_t)h * nch + m];
-      // every chunk used here was marked; an unmarked one would read device
-      // row 0 rather than outside the cache
-      return sl >= 0 ? kCacheFlag | (int)(((int64_t)h * nslots + sl) * kChunk + tok % kChunk) : 0;
-    }
+  // Each token's table entries are read unconditionally at a clamped chunk
+  // (history chunk 0 for rows above the split; every table holds nch >= 1
+  // entries per head), all of a thread's reads before any is used: with the
+  // reads under their conditions the compiler waited for each on its own.
+  const uint64_t* ph = pending && pass == 1 ? pending + (int64_t)h * nch : nullptr;
+  const int32_t* sh = slot + (int64_t)h * nch;
+  auto enc = [&](int64_t tok, int sl) -> int {
+    // every chunk used here was marked; an unmarked one would read device
+    // row 0 rather than outside the cache
+    if (tok < split) return sl >= 0 ? kCacheFlag | (int)(((int64_t)h * nslots + sl) * kChunk + tok % kChunk) : 0;
     return (int)(tok - split);
   };
-  const uint64_t* ph = pending && pass == 1 ? pending + (int64_t)h * nch : nullptr;
   int busy = 0;
-  for (int i = threadIdx.x; i < P.nrouted; i += blockDim.x) {
-    const int tok = runs[i];
-    if (ph && tok < split && ((ph[tok / kChunk] >> ((tok % kChunk) / g)) & 1ull)) busy = 1;
-    runs[i] = enc(tok);
-  }
-  for (int t = threadIdx.x; t < P.nfix; t += blockDim.x) {
-    const int64_t m = t < P.a ? t : P.bb + (t - P.a);
-    if (ph && m < nch && ph[m]) busy = 1;
-    fixsrc[t] = enc(m * kChunk);
+  for (int base = 0; base < P.nrouted || base < P.nfix; base += blockDim.x) {
+    const int i = base + threadIdx.x;
+    const bool rt = i < P.nrouted, fx = i < P.nfix;
+    const int64_t tok = rt ? runs[i] : 0;
+    const int64_t mf = fx ? (i < P.a ? i : P.bb + (i - P.a)) : 0;
+    const int64_t mr = tok < split ? tok / kChunk : 0;
+    const int64_t mfc = mf < nch ? mf : 0;
+    const int sr = sh[mr], sf = sh[mfc];
+    const uint64_t pr = ph ? ph[mr] : 0ull, pf = ph ? ph[mfc] : 0ull;
+    if (rt) {
+      if (tok < split && ((pr >> ((tok % kChunk) / g)) & 1ull)) busy = 1;
+      runs[i] = enc(tok, sr);
+    }
+    if (fx) {
+      if (mf < nch && pf) busy = 1;
+      fixsrc[i] = enc(mf * kChunk, sf);
+    }
   }
   busy = __syncthreads_or(busy);
   if (ph && threadIdx.x == 0) done[blockIdx.x] = busy ? 0 : 1;
