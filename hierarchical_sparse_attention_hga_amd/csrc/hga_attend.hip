@@ -308,14 +308,19 @@ __device__ __attribute__((always_inline)) void attend_bf16_body(const AttnArgs& 
     auto scored = [nearly]() __attribute__((always_inline)) {
       if (nearly > 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     };
+    auto chunks_selected = [nearly]() __attribute__((always_inline)) {
+      if (nearly > 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    };
+    auto groups_issued = [&]() __attribute__((always_inline)) {
+      if (active && nearly > 0) compute(0, std::integral_constant<int, 0>{});
+    };
     auto selected = [&]() __attribute__((always_inline)) {
-      if (!active) return;
-      if (nearly > 0) compute(0, std::integral_constant<int, 0>{});
-      if (nearly > 1) compute(1, std::integral_constant<int, 1>{});
+      if (active && nearly > 1) compute(1, std::integral_constant<int, 1>{});
     };
     auto queries_issued = [&]() __attribute__((always_inline)) { load_q_operands<D>(A, b, h, z, qf); };
     const int nsg = route(route::EarlyWindow<decltype(queries_issued), decltype(chunks_kept), decltype(scored),
-                                             decltype(selected)>{queries_issued, chunks_kept, scored, selected});
+                                             decltype(selected), decltype(chunks_selected), decltype(groups_issued)>{
+        queries_issued, chunks_kept, scored, selected, chunks_selected, groups_issued});
     P.nrouted = nsg;
     P.nrt = (nsg + kChunk / S.g - 1) / (kChunk / S.g);
     P.ntiles = P.nfix + P.nrt + 1;

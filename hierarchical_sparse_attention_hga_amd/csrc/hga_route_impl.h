@@ -36,6 +36,7 @@ constexpr int kThreads = 512;   // threads of a routing workgroup
 constexpr int kWaves = kThreads / 64;
 constexpr int kLanesPerCand = 8;
 constexpr int kRowsInFlight = 4;   // summary rows per lane group per round
+constexpr int kGroupRowsWindow = 2;   // the same for the group stage with a window
 constexpr int kQuadsPerLane = 128 / 4 / kLanesPerCand;   // float4s per lane and row (d <= 128)
 
 template <typename T>
@@ -187,10 +188,13 @@ __device__ void wave_select(const unsigned long long* key, int n, int k, int* hi
 // kRowsInFlight rows per lane group per round; a round's loads are all
 // issued before any is used, and the first round's may be issued early
 // (before the block query exists) by load_round.
+template <int R = kRowsInFlight>
 struct ScoreRound {
-  int c[kRowsInFlight];
-  float4 v[kQuadsPerLane][kRowsInFlight];
+  int c[R];
+  float4 v[kQuadsPerLane][R];
 };
+template <int R>
+constexpr int round_rows() { return R * kWaves * (64 / kLanesPerCand); }
 
 // kFlat (the single-round scoring of the fused route-and-attend kernel): no
 // load depends on a per-lane condition (slots past the last row read the
@@ -202,15 +206,15 @@ struct ScoreRound {
 // its own (one round trip each) and the first round waited before the block
 // query's loads could issue. The router kernel, two rounds in flight, keeps
 // the conditional loads (the flat form slowed it down).
-template <bool kFlat, bool kSkipEmpty = true, typename RowFn>
-__device__ __attribute__((always_inline)) void load_round(int base, int d, int n, RowFn row, ScoreRound& rd) {
+template <bool kFlat, bool kSkipEmpty = true, typename RowFn, int R>
+__device__ __attribute__((always_inline)) void load_round(int base, int d, int n, RowFn row, ScoreRound<R>& rd) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane / kLanesPerCand, lic = lane % kLanesPerCand;
   constexpr int per_wave = 64 / kLanesPerCand;
   constexpr int per_round = kWaves * per_wave;
-  const float* r[kRowsInFlight];
+  const float* r[R];
 #pragma unroll
-  for (int u = 0; u < kRowsInFlight; ++u) {
+  for (int u = 0; u < R; ++u) {
     rd.c[u] = base + u * per_round + wave * per_wave + sub;
     if (kFlat)
       r[u] = row(rd.c[u] < n ? rd.c[u] : (n > 0 ? n - 1 : 0));
@@ -220,7 +224,7 @@ __device__ __attribute__((always_inline)) void load_round(int base, int d, int n
 #pragma unroll
   for (int i = 0; i < kQuadsPerLane; ++i)
 #pragma unroll
-    for (int u = 0; u < kRowsInFlight; ++u) {
+    for (int u = 0; u < R; ++u) {
       const int q4 = lic + i * kLanesPerCand;
       if (kFlat) {
         // a slot group with no row of the round for this wave skips its loads
@@ -235,41 +239,41 @@ __device__ __attribute__((always_inline)) void load_round(int base, int d, int n
     }
 }
 
-template <bool kFlat>
-__device__ inline void finish_round(const ScoreRound& rd_in, const double* qbar, int d, int n,
+template <bool kFlat, int R>
+__device__ inline void finish_round(const ScoreRound<R>& rd_in, const double* qbar, int d, int n,
                                     unsigned long long* key) {
   const int lic = (threadIdx.x & 63) % kLanesPerCand;
-  ScoreRound rd = rd_in;
+  ScoreRound<R> rd = rd_in;
   if (kFlat) {
 #pragma unroll
     for (int i = 0; i < kQuadsPerLane; ++i)
 #pragma unroll
-      for (int u = 0; u < kRowsInFlight; ++u)
+      for (int u = 0; u < R; ++u)
         asm volatile("" : "+v"(rd.v[i][u].x), "+v"(rd.v[i][u].y), "+v"(rd.v[i][u].z), "+v"(rd.v[i][u].w));
   }
-  double acc[kRowsInFlight];
+  double acc[R];
 #pragma unroll
-  for (int u = 0; u < kRowsInFlight; ++u) acc[u] = 0.0;
+  for (int u = 0; u < R; ++u) acc[u] = 0.0;
 #pragma unroll
   for (int i = 0; i < kQuadsPerLane; ++i) {
     const int q4 = lic + i * kLanesPerCand;
     if (q4 >= d / 4) break;
     const double q0 = qbar[4 * q4], q1 = qbar[4 * q4 + 1], q2 = qbar[4 * q4 + 2], q3 = qbar[4 * q4 + 3];
 #pragma unroll
-    for (int u = 0; u < kRowsInFlight; ++u) {
+    for (int u = 0; u < R; ++u) {
       acc[u] += q0 * (double)rd.v[i][u].x; acc[u] += q1 * (double)rd.v[i][u].y;
       acc[u] += q2 * (double)rd.v[i][u].z; acc[u] += q3 * (double)rd.v[i][u].w;
     }
   }
 #pragma unroll
-  for (int u = 0; u < kRowsInFlight; ++u) {
+  for (int u = 0; u < R; ++u) {
 #pragma unroll
     for (int off = kLanesPerCand / 2; off > 0; off >>= 1) acc[u] += __shfl_xor(acc[u], off, kLanesPerCand);
     if (lic == 0 && rd.c[u] < n) key[rd.c[u]] = order_key(acc[u]);
   }
 }
 
-constexpr int kRoundRows = kRowsInFlight * kWaves * (64 / kLanesPerCand);   // rows per round
+constexpr int kRoundRows = round_rows<kRowsInFlight>();   // rows per round
 
 // Whether every item of the call selects among at most 512 candidates at
 // both stages (the chunk candidates of the last block, the most any block
@@ -285,24 +289,25 @@ inline bool select512_fits(const Shape& s) {
 // issued before a round is scored, so two rounds are in flight (their
 // registers are left to the router kernel: inside the fused kernel they
 // would push the attention's state out to scratch memory).
-template <bool kPipelined, typename RowFn>
+template <bool kPipelined, typename RowFn, int R>
 __device__ __attribute__((always_inline)) void score_rows(const double* qbar, int d, int n, RowFn row,
-                                                          unsigned long long* key, ScoreRound& cur, int from) {
+                                                          unsigned long long* key, ScoreRound<R>& cur, int from) {
+  constexpr int RR = round_rows<R>();
   if (!kPipelined) {
     finish_round<true>(cur, qbar, d, n, key);
-    for (int base = from + kRoundRows; base < n; base += kRoundRows) {
+    for (int base = from + RR; base < n; base += RR) {
       load_round<true>(base, d, n, row, cur);
       finish_round<true>(cur, qbar, d, n, key);
     }
     return;
   }
-  ScoreRound nxt;
-  for (int base = from; base < n; base += 2 * kRoundRows) {
-    const bool more = base + kRoundRows < n;
-    if (more) load_round<false>(base + kRoundRows, d, n, row, nxt);
+  ScoreRound<R> nxt;
+  for (int base = from; base < n; base += 2 * RR) {
+    const bool more = base + RR < n;
+    if (more) load_round<false>(base + RR, d, n, row, nxt);
     finish_round<false>(cur, qbar, d, n, key);
     if (!more) break;
-    if (base + 2 * kRoundRows < n) load_round<false>(base + 2 * kRoundRows, d, n, row, cur);
+    if (base + 2 * RR < n) load_round<false>(base + 2 * RR, d, n, row, cur);
     finish_round<false>(nxt, qbar, d, n, key);
   }
 }
@@ -368,19 +373,25 @@ struct NoHook {
 struct NoWindow {
   static constexpr bool kActive = false;
   __device__ void queries_issued() const {}
+  __device__ void chunks_selected() const {}
   __device__ void chunks_kept() const {}
+  __device__ void groups_issued() const {}
   __device__ void scored() const {}
   __device__ void selected() const {}
 };
-template <typename F0, typename F1, typename F2, typename F3>
+template <typename F0, typename F1, typename F2, typename F3, typename F4, typename F5>
 struct EarlyWindow {
   static constexpr bool kActive = true;
   F0 f0;
   F1 f1;
   F2 f2;
   F3 f3;
+  F4 f4;
+  F5 f5;
   __device__ __attribute__((always_inline)) void queries_issued() const { f0(); }
+  __device__ __attribute__((always_inline)) void chunks_selected() const { f4(); }
   __device__ __attribute__((always_inline)) void chunks_kept() const { f1(); }
+  __device__ __attribute__((always_inline)) void groups_issued() const { f5(); }
   __device__ __attribute__((always_inline)) void scored() const { f2(); }
   __device__ __attribute__((always_inline)) void selected() const { f3(); }
 };
@@ -428,7 +439,7 @@ __device__ __attribute__((always_inline)) int route_item(const RouteArgs& a, int
       v0[u] = *q_slice(rr < nrows ? rr : nrows - 1);
     }
   }
-  ScoreRound first;
+  ScoreRound<> first;
   // (with a window, no branch around them either: the compiler's waits for
   // the block query's rows would then count every later load as pending)
   if (!kPipelined || chunk_select) load_round<!kPipelined, !Window::kActive>(0, d, ncand, chunk_row, first);
@@ -504,9 +515,13 @@ __device__ __attribute__((always_inline)) int route_item(const RouteArgs& a, int
   } else {
     for (int i = tid; i < nsc; i += kThreads) sm.chunks[i] = (int)(lo + i);
   }
+  window.chunks_selected();
   __syncthreads();
   window.chunks_kept();
-  if (write_out)
+  // (with a window the kept chunks are written at the end: a store in flight
+  // here holds its registers, and the compiler's wait before reusing them
+  // would wait for the group summaries too)
+  if (write_out && !Window::kActive)
     for (int i = tid; i < S.kc; i += kThreads) a.chunk_idx[orow * S.kc + i] = i < nsc ? sm.chunks[i] : -1;
 
   if constexpr (kCache) {
@@ -533,8 +548,11 @@ __device__ __attribute__((always_inline)) int route_item(const RouteArgs& a, int
       return j < gsplit ? a.gs_host + ((int64_t)h * gsplit + j) * d
                         : a.gs_dev + ((int64_t)h * (ngl - gsplit) + (j - gsplit)) * d;
     };
-    ScoreRound g0;
-    load_round<!kPipelined>(0, d, ngc, group_row, g0);
+    // with a window an attention tile runs while these rows load: fewer
+    // rows per round leave it its registers
+    ScoreRound<Window::kActive ? kGroupRowsWindow : kRowsInFlight> g0;
+    load_round<!kPipelined, !Window::kActive>(0, d, ngc, group_row, g0);
+    window.groups_issued();
     score_rows<kPipelined>(sm.qbar, d, ngc, group_row, sm.key, g0, 0);
     window.scored();
     __syncthreads();
@@ -548,12 +566,15 @@ __device__ __attribute__((always_inline)) int route_item(const RouteArgs& a, int
   } else {
     for (int i = tid; i < nsg; i += kThreads) emit(i, group_of(i));
     if constexpr (Window::kActive) {
+      window.groups_issued();
       window.scored();
       __syncthreads();
     }
   }
   window.selected();
   if (write_out) {
+    if (Window::kActive)
+      for (int i = tid; i < S.kc; i += kThreads) a.chunk_idx[orow * S.kc + i] = i < nsc ? sm.chunks[i] : -1;
     for (int i = nsg + tid; i < S.kg; i += kThreads) gout[i] = -1;
     if (tid == 0) {
       a.n_sel[orow * 2 + 0] = nsc;
@@ -586,7 +607,7 @@ __device__ __attribute__((always_inline)) int group_stage(const RouteArgs& a, in
   auto group_of = [kept_chunks, gpc](int c) { return kept_chunks[c / gpc] * gpc + c % gpc; };
   if (nsg > 0 && nsg < ngc) {
     auto group_row = [gs_row, group_of](int c) -> const float* { return gs_row(c, (int64_t)group_of(c)); };
-    ScoreRound g0;
+    ScoreRound<> g0;
     load_round<!kPipelined>(0, d, ngc, group_row, g0);
     score_rows<kPipelined>(sm.qbar, d, ngc, group_row, sm.key, g0, 0);
     __syncthreads();
