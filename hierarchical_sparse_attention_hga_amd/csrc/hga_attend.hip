@@ -575,7 +575,7 @@ __global__ __launch_bounds__(kAttnThreads) void route_attend_bf16_kernel(FusedAr
     if (wr) gout[rank] = group;
   };
   auto route = [&](auto window) __attribute__((always_inline)) -> int {
-    const int nsg = route::route_item<uint16_t, false, false, decltype(emit), decltype(prefetch), true,
+    const int nsg = route::route_item<uint16_t, false, false, decltype(emit), decltype(prefetch), 512,
                                       decltype(window)>(F.r, b, h, rsm, wr, emit, prefetch, window);
     __syncthreads();
     return nsg;

@@ -36,9 +36,10 @@ using route::kThreads;
 // kCache: the persistent cache's variant (block queries kept, chunk stage
 // alone, the history each item needs marked); a kernel of its own, so that
 // the plain router's code and registers are those of the plain path.
-// kSelect512: both selections take at most 512 candidates (see
-// select512_fits), and the selection is inlined.
-template <typename T, bool kCache, bool kSelect512 = false>
+// kSelectMax: both selections take at most that many candidates (512 or
+// 1024, see select_fits), and the selection is inlined (0: any number, the
+// selection is a function call).
+template <typename T, bool kCache, int kSelectMax = 0>
 __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   __shared__ route::RouteSmem sm;
   __shared__ int sMarked;   // the item's kept history groups (or chunks) marked for the cache
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(kThreads) void route_kernel(RouteArgs a) {
   int32_t* gout = a.group_idx + ((int64_t)b * S.hkv + h) * S.kg;
   if constexpr (!kCache) {
     auto emit = [gout](int rank, int group) { gout[rank] = group; };
-    route::route_item<T, true, false, decltype(emit), route::NoHook, kSelect512>(a, b, h, sm, true, emit);
+    route::route_item<T, true, false, decltype(emit), route::NoHook, kSelectMax>(a, b, h, sm, true, emit);
     return;
   }
   // with the persistent cache's marks (route_item's first barrier orders
@@ -83,15 +84,16 @@ hipError_t launch_route_args(const RouteArgs& a, hipStream_t st) {
   const int64_t items = s.nb * s.hkv;
   if (items == 0) return hipSuccess;
   const bool cache = a.kv_need || a.gs_need || a.qbar_out || a.chunks_only;
-  const bool small = route::select512_fits(s);
+  const int sel = route::select_fits(s, 512) ? 512 : route::select_fits(s, 1024) ? 1024 : 0;
   const dim3 grid((unsigned)items), block(kThreads);
   if (s.dtype == HGA_BF16) {
     if (cache) route_kernel<uint16_t, true><<<grid, block, 0, st>>>(a);
-    else if (small) route_kernel<uint16_t, false, true><<<grid, block, 0, st>>>(a);
+    else if (sel == 512) route_kernel<uint16_t, false, 512><<<grid, block, 0, st>>>(a);
+    else if (sel == 1024) route_kernel<uint16_t, false, 1024><<<grid, block, 0, st>>>(a);
     else route_kernel<uint16_t, false><<<grid, block, 0, st>>>(a);
   } else {
     if (cache) route_kernel<float, true><<<grid, block, 0, st>>>(a);
-    else if (small) route_kernel<float, false, true><<<grid, block, 0, st>>>(a);
+    else if (sel == 512) route_kernel<float, false, 512><<<grid, block, 0, st>>>(a);
     else route_kernel<float, false><<<grid, block, 0, st>>>(a);
   }
   return hipGetLastError();

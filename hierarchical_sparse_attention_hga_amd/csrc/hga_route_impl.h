@@ -160,16 +160,19 @@ __device__ void wave_select_kpl(const unsigned long long* key, int n, int k, int
   }
 }
 
-// The same for at most 512 keys, with every variant inlined: the caller
-// then makes no function call and holds no stack frame (a call from the
-// fused route-and-attend kernel kept 232 bytes per lane in scratch memory).
-template <typename EmitFn>
-__device__ __attribute__((always_inline)) void wave_select_512(const unsigned long long* key, int n, int k, int* hist,
-                                                               EmitFn emit) {
+// The same for at most kMax keys (512 or 1024), with every variant inlined:
+// the caller then makes no function call and holds no stack frame (a call
+// from the fused route-and-attend kernel kept 232 bytes per lane in scratch
+// memory).
+template <int kMax, typename EmitFn>
+__device__ __attribute__((always_inline)) void wave_select_inline(const unsigned long long* key, int n, int k,
+                                                                  int* hist, EmitFn emit) {
+  static_assert(kMax == 512 || kMax == 1024, "inlined selections");
   if (n <= 64) wave_select_kpl<1>(key, n, k, hist, emit);
   else if (n <= 128) wave_select_kpl<2>(key, n, k, hist, emit);
   else if (n <= 256) wave_select_kpl<4>(key, n, k, hist, emit);
-  else wave_select_kpl<8>(key, n, k, hist, emit);
+  else if (kMax == 512 || n <= 512) wave_select_kpl<8>(key, n, k, hist, emit);
+  else wave_select_kpl<16>(key, n, k, hist, emit);
 }
 
 template <typename EmitFn>
@@ -275,14 +278,15 @@ __device__ inline void finish_round(const ScoreRound<R>& rd_in, const double* qb
 
 constexpr int kRoundRows = round_rows<kRowsInFlight>();   // rows per round
 
-// Whether every item of the call selects among at most 512 candidates at
-// both stages (the chunk candidates of the last block, the most any block
-// has; the groups of the kept chunks), so that route_item may take
-// kSelect512.
-inline bool select512_fits(const Shape& s) {
+// Whether every item of the call selects among at most m candidates at both
+// stages (the chunk candidates of the last block, the most any block has;
+// the groups of the kept chunks), so that route_item may inline its
+// selections (kSelectMax = m).
+inline bool select_fits(const Shape& s, int m) {
   const int64_t last_chunk = (s.q0 + s.nq - 1) / kChunk;   // the last block's chunk
-  return last_chunk - s.sink_chunks - s.local_chunks <= 512 && (int64_t)s.kc * (kChunk / s.g) <= 512;
+  return last_chunk - s.sink_chunks - s.local_chunks <= m && (int64_t)s.kc * (kChunk / s.g) <= m;
 }
+inline bool select512_fits(const Shape& s) { return select_fits(s, 512); }
 
 // Rounds from row `from` on (a multiple of kRoundRows), the loads of round
 // `from` already issued into cur. With kPipelined the next round's loads are
@@ -356,9 +360,9 @@ namespace route {
 // it they are ignored and cost nothing. after_query() is
 // called by every thread once the block query is formed (the fused kernel
 // starts its first key/value tile loads there, behind the router's first
-// loads). kSelect512: both selections take at most 512 candidates (the
-// caller checks), so they use wave_select_512 and the item is routed with no
-// function call.
+// loads). kSelectMax (512 or 1024; 0: any number): both selections take at
+// most that many candidates (the caller checks), so they are inlined and the
+// item is routed with no function call.
 struct NoHook {
   __device__ void operator()() const {}
 };
@@ -396,7 +400,7 @@ struct EarlyWindow {
   __device__ __attribute__((always_inline)) void selected() const { f3(); }
 };
 template <typename T, bool kPipelined, bool kCache = false, typename GroupEmit, typename AfterQuery = NoHook,
-          bool kSelect512 = false, typename Window = NoWindow>
+          int kSelectMax = 0, typename Window = NoWindow>
 __device__ __attribute__((always_inline)) int route_item(const RouteArgs& a, int b, int h, RouteSmem& sm,
                                                          bool write_out, GroupEmit emit, AfterQuery after_query = {},
                                                          Window window = {}) {
@@ -507,8 +511,8 @@ __device__ __attribute__((always_inline)) int route_item(const RouteArgs& a, int
     const int first_cand = (int)lo;
     if (wave == 0) {
       auto keep = [kept, first_cand](int rank, int pos) { kept[rank] = first_cand + pos; };
-      if constexpr (kSelect512)
-        wave_select_512(sm.key, ncand, nsc, sm.hist, keep);
+      if constexpr (kSelectMax > 0)
+        wave_select_inline<kSelectMax>(sm.key, ncand, nsc, sm.hist, keep);
       else
         wave_select(sm.key, ncand, nsc, sm.hist, keep);
     }
@@ -558,8 +562,8 @@ __device__ __attribute__((always_inline)) int route_item(const RouteArgs& a, int
     __syncthreads();
     if (wave == 0) {
       auto keep = [emit, group_of](int rank, int pos) { emit(rank, group_of(pos)); };
-      if constexpr (kSelect512)
-        wave_select_512(sm.key, ngc, nsg, sm.hist, keep);
+      if constexpr (kSelectMax > 0)
+        wave_select_inline<kSelectMax>(sm.key, ngc, nsg, sm.hist, keep);
       else
         wave_select(sm.key, ngc, nsg, sm.hist, keep);
     }
