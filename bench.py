@@ -9,13 +9,16 @@ every input already in HBM. With at most 4 query heads per KV head
 hga_route_attend is one kernel; with more (the 64K layer's 8) the step runs
 the router and the attention kernels, timed apart.
 
-`value` is the workload's query tokens over the wall-clock time of the timed
-steps, run back to back between two device synchronizations. Then every
-stage, and the whole step, is timed call by call with HIP event pairs on the
-launch stream: warm (back to back) and with the caches flushed (a 512 MiB
-buffer written before each call, outside the pair: the L2 caches and the
-256 MB Infinity Cache then hold none of the step's data). Each reports mean,
-median, p10 and p90; `value_flushed` is n_q over the median flushed step.
+`value` is the workload's query tokens over the mean duration of the timed
+steps with the caches flushed: each of the timed steps runs after a 512 MiB
+buffer is written (outside its pair of HIP events on the launch stream), so
+the L2 caches and the 256 MB Infinity Cache hold none of the step's data, as
+in a model where the other layers' weights and activations pass through the
+caches between two calls of this layer. `value_warm` is the same steps run
+back to back (wall clock between two device synchronizations), with the
+layer's data left in the caches by the previous step. Then every stage is
+timed call by call with HIP event pairs, warm and flushed; each reports mean,
+median, p10 and p90.
 
 The workload is the 16,384-token training-segment shape (Qwen3-8B heads:
 32 query / 8 KV heads, head_dim 128, bf16, 2,048 active queries over a
@@ -282,7 +285,8 @@ class Workload:
         flush = cache_flusher()
         for name, call in self.stage_calls() + [("step", self.step)]:
             stages["warm"][name] = event_us(call, samples)
-            stages["flushed"][name] = event_us(call, samples, flush)
+            # the timed steps of the headline rate: exactly `steps` of them
+            stages["flushed"][name] = event_us(call, steps if name == "step" else samples, flush)
         return wall, stages
 
     def free(self):
@@ -300,7 +304,7 @@ def source_sha256():
     return hashlib.sha256(b"".join(open(f, "rb").read() for f in files)).hexdigest()
 
 
-def measured_traffic(workload, kernel):
+def measured_traffic(workload, kernel, flushed=False):
     """HBM bytes per launch of `kernel` ("route_attend_bf16", "attend_bf16" or
     "attend_backward", the latter summed over its kernels) from the committed
     rocprofv3 counter runs
@@ -312,15 +316,16 @@ def measured_traffic(workload, kernel):
     rec = json.load(open(path))
     if source_sha256() != rec["source_sha256"]:
         return None
-    return 1024.0 * (rec["fetch_kib"] * rec["fetch_factor"] + rec["write_kib"] * rec["write_factor"])
+    sfx = "_after_flush" if flushed else ""
+    return 1024.0 * (rec["fetch_kib" + sfx] * rec["fetch_factor"] + rec["write_kib" + sfx] * rec["write_factor"])
 
 
-def roofline(cfg, n_sel, attend_us, kernel, with_traffic=True):
+def roofline(cfg, n_sel, attend_us, kernel, with_traffic=True, flushed=False):
     """The attention's algorithmic flops and bytes over the mean launch
     duration of the kernel that runs it, against whichever MI355X peak binds
     (bf16 MFMA or HBM; the float32 path against the float32 peak)."""
     flops, byts, _ = algorithmic(cfg, n_sel)
-    traffic = measured_traffic(cfg["name"], kernel) if with_traffic else None
+    traffic = measured_traffic(cfg["name"], kernel, flushed) if with_traffic else None
     peak_flops = PEAK_BF16 if cfg["dtype"] == "bf16" else PEAK_F32
     t_mfma = flops / peak_flops
     t_hbm = byts / PEAK_HBM
@@ -426,6 +431,12 @@ class Result:
 
     @property
     def value(self):
+        """n_q over the mean flushed step (the timed steps)."""
+        return self.cfg["n_q"] / (self.flushed["step"]["mean"] * 1e-6)
+
+    @property
+    def value_warm(self):
+        """n_q x steps over the wall clock of the warm steps, back to back."""
         return self.steps * self.cfg["n_q"] / self.wall
 
     def attention_stage(self):
@@ -436,18 +447,18 @@ class Result:
             return "attend_f32"
         return "route_attend_bf16" if self.fused else "attend_bf16"
 
-    def roofline(self, flushed=False, with_traffic=True):
+    def roofline(self, flushed=True, with_traffic=True):
         st = (self.flushed if flushed else self.warm)[self.attention_stage()]
-        return roofline(self.cfg, self.ns, st["mean"], self.kernel_name(), with_traffic and not flushed)
+        return roofline(self.cfg, self.ns, st["mean"], self.kernel_name(), with_traffic, flushed)
 
     def line(self, with_traffic=True):
         """The workload's measured figures as one JSON object."""
-        out = {"value": self.value, "unit": "query-tokens/s",
-               "value_flushed": self.cfg["n_q"] / (self.flushed["step"]["median"] * 1e-6),
-               "ms_per_step": self.wall / self.steps * 1e3,
-               "stages_us": self.warm, "stages_us_flushed": self.flushed,
+        out = {"value": self.value, "unit": "query-tokens/s", "value_warm": self.value_warm,
+               "ms_per_step": self.flushed["step"]["mean"] * 1e-3,
+               "ms_per_step_warm": self.wall / self.steps * 1e3,
+               "stages_us_flushed": self.flushed, "stages_us": self.warm,
                "roofline": self.roofline(with_traffic=with_traffic),
-               "roofline_flushed": self.roofline(flushed=True)}
+               "roofline_warm": self.roofline(flushed=False, with_traffic=with_traffic)}
         if self.split:
             out["host_link_bytes_per_step"] = self.host_bytes
         return out
@@ -733,7 +744,7 @@ def host_link_rate(mib=256, samples=10):
 def host_tier_line(cfg_id, steps, warmup, link_rate, note):
     r = measure(cfg_id, steps, warmup, split=synth_config(cfg_id)["tier_split"])
     line = r.line()
-    t = r.warm["attend"]["mean"] * 1e-6
+    t = r.flushed["attend"]["mean"] * 1e-6
     line["note"] = note
     line["host_link"] = {"bytes_per_step": r.host_bytes, "attend_stage_GBps": r.host_bytes / t / 1e9,
                          "frac_of_nominal_64GBps": r.host_bytes / t / PEAK_HOST_LINK,
@@ -910,19 +921,19 @@ def main():
                    "kv_heads": cfg["hkv"], "head_dim": cfg["d"], "top_chunks": cfg["top_chunks"],
                    "top_groups": cfg["top_groups"], "sink": cfg["sink"], "local": cfg["local"],
                    "kv_residency": "host-pinned history" if split else "hbm"},
-        "value_flushed": ml["value_flushed"],
-        "stages_us": ml["stages_us"], "stages_us_flushed": ml["stages_us_flushed"],
-        "roofline": ml["roofline"], "roofline_flushed": ml["roofline_flushed"],
+        "value_warm": ml["value_warm"], "ms_per_step_warm": ml["ms_per_step_warm"],
+        "stages_us_flushed": ml["stages_us_flushed"], "stages_us": ml["stages_us"],
+        "roofline": ml["roofline"], "roofline_warm": ml["roofline_warm"],
     }
     if split:
         line["host_link_bytes_per_step"] = main_r.host_bytes
     if not args.no_extra:
         extra = {}
         half = max(args.steps // 2, 10)
-        rest = sum(v["mean"] for k, v in main_r.warm.items() if k not in ("summaries", "step"))
+        rest = sum(v["mean"] for k, v in main_r.flushed.items() if k not in ("summaries", "step"))
         extra["summaries_prebuilt"] = {
             "value": cfg["n_q"] / (rest * 1e-6), "unit": "query-tokens/s",
-            "note": "n_q / (mean routing + gather + attention stage time); summary build excluded"}
+            "note": "n_q / (mean flushed routing + gather + attention stage time); summary build excluded"}
         if not split:
             full = full_summary_us(args.config)
             extra["full_summary_rebuild"] = {
