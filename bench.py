@@ -449,7 +449,8 @@ class Result:
 
     def roofline(self, flushed=True, with_traffic=True):
         st = (self.flushed if flushed else self.warm)[self.attention_stage()]
-        return roofline(self.cfg, self.ns, st["mean"], self.kernel_name(), with_traffic, flushed)
+        # the counters are of the all-HBM kernels; the host-tier path runs another instantiation
+        return roofline(self.cfg, self.ns, st["mean"], self.kernel_name(), with_traffic and not self.split, flushed)
 
     def line(self, with_traffic=True):
         """The workload's measured figures as one JSON object."""
